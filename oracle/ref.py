@@ -1,0 +1,314 @@
+"""fp64 CPU oracle of the ButterflyMoE expert-layer forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module: only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+It shares no code with the HIP library; both sides only read the arrays made by
+``compressed_mixture_experts_amd.workloads``.
+
+Sources (web summaries of the papers; cited by page and section):
+  [MoE-zh]  "ButterflyMoE: Sub-Linear Ternary Experts via Structured Butterfly
+            Orbits", gist.science/zh/paper/2601.13563, technical summary:
+            §2.1 (formal definition of an expert), §2.2 (ternary substrate,
+            butterfly = hierarchical Givens rotations + permutations),
+            §4.4 (inference cost).
+  [MoE-pt]  same paper, gist.science/pt/paper/2601.13563, technical summary
+            §2 "Metodologia" (expert formula, O(d log d) angles, memory
+            O(d^2 + N d log d)) and §4 "Resultados" (4.70 MB at 256 experts).
+  [MoE-nl]  same paper, gist.science/nl/paper/2601.13563, §2 "Methodologie",
+            "Drie Fasen van de Methode" (standard top-k gating network;
+            experts never materialised during inference).
+  [ViT-pt]  "ButterflyViT", gist.science/pt/paper/2603.06746, §2 "Metodologia"
+            (block-diagonal Givens parameterisation, rotations before and after
+            the shared substrate in the FFN) and §3 (per-expert cost n_l * d).
+
+What the pages leave open is read as follows (each choice is a convention that
+every statement on the pages still satisfies):
+  * stage s of a butterfly of size n = 2^L rotates the index pair (i, i + 2^s)
+    (bit s of i clear) by the angle with pair number p = i with bit s deleted;
+    the rotation acts as [[c, -s], [s, c]] on (v_i, v_j);
+    B = S_{L-1} ... S_1 S_0, so B v applies the stride-1 stage first;
+  * angles are stored [log2 n][n/2] per butterfly, fp32, and are used exactly
+    (their cos/sin are taken in fp64);
+  * B(theta) has the input width, B(phi) the output width; an FFN expert has an
+    up substrate (d_ff x d) and a down substrate (d x d_ff), each with its own
+    pair of rotations, and an exact-erf GELU between them;
+  * the router is a bias-free linear map x -> logits, top-k on the logits
+    (larger first, ties to the lower expert index), gate = softmax probability
+    of the chosen expert over all N logits (optionally renormalised over the k);
+  * the combine is y_t = sum_j gate_{t,j} * E_{e_j}(x_t), no capacity limit;
+  * an optional scalar alpha multiplies each substrate (default 1).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "stored_to_f64", "pair_index", "stage_matrix", "butterfly_dense",
+    "butterfly_apply", "expert_matrix", "expert_apply", "gelu", "route",
+    "forward", "forward_tokens", "param_counts",
+]
+
+
+# ---------------------------------------------------------------------------
+# stored values -> float64
+# ---------------------------------------------------------------------------
+def stored_to_f64(a: np.ndarray, act: str) -> np.ndarray:
+    """Exact float64 value of stored activations (float32, or bf16 bit patterns)."""
+    if act == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if act == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(act)
+
+
+# ---------------------------------------------------------------------------
+# butterfly matrices  ([MoE-zh] §2.2, [ViT-pt] §2)
+# ---------------------------------------------------------------------------
+def pair_index(i: int, s: int) -> int:
+    """Pair number of index i (bit s clear) in stage s: i with bit s deleted."""
+    low = i & ((1 << s) - 1)
+    return ((i >> (s + 1)) << s) | low
+
+
+def stage_matrix(angles_s: np.ndarray, s: int, n: int) -> np.ndarray:
+    """Dense n x n matrix of butterfly stage s (small n only)."""
+    S = np.zeros((n, n))
+    ang = np.asarray(angles_s, dtype=np.float64)
+    for i in range(n):
+        if i & (1 << s):
+            continue
+        j = i + (1 << s)
+        t = ang[pair_index(i, s)]
+        c, sn = math.cos(t), math.sin(t)
+        S[i, i] = c
+        S[i, j] = -sn
+        S[j, i] = sn
+        S[j, j] = c
+    return S
+
+
+def butterfly_dense(angles: np.ndarray) -> np.ndarray:
+    """B = S_{L-1} ... S_0 as an explicit dense product (small n only)."""
+    angles = np.asarray(angles)
+    L = angles.shape[0]
+    n = 1 << L
+    B = np.eye(n)
+    for s in range(L):
+        B = stage_matrix(angles[s], s, n) @ B
+    return B
+
+
+def butterfly_apply(angles: np.ndarray, M: np.ndarray, transpose: bool = False) -> np.ndarray:
+    """B(angles) @ M, or B(angles)^T @ M, one Givens stage at a time.
+
+    M has shape (n, m) (or (n,)).  B @ M applies S_0 first; B^T @ M applies
+    S_{L-1}^T first.  Each stage rotates the rows i and i + 2^s of M.
+    """
+    ang = np.asarray(angles, dtype=np.float64)
+    L = ang.shape[0]
+    n = 1 << L
+    V = np.array(M, dtype=np.float64, copy=True)
+    vec = V.ndim == 1
+    if vec:
+        V = V[:, None]
+    if V.shape[0] != n:
+        raise ValueError(f"butterfly of size {n} applied to {V.shape[0]} rows")
+    order = range(L - 1, -1, -1) if transpose else range(L)
+    for s in order:
+        h = 1 << s
+        c = np.cos(ang[s]).reshape(n // (2 * h), h, 1)
+        sn = np.sin(ang[s]).reshape(n // (2 * h), h, 1)
+        W = V.reshape(n // (2 * h), 2, h, V.shape[1])
+        a = W[:, 0].copy()
+        b = W[:, 1].copy()
+        if not transpose:
+            W[:, 0] = c * a - sn * b
+            W[:, 1] = sn * a + c * b
+        else:
+            W[:, 0] = c * a + sn * b
+            W[:, 1] = -sn * a + c * b
+        V = W.reshape(n, -1)
+    return V[:, 0] if vec else V
+
+
+# ---------------------------------------------------------------------------
+# experts  ([MoE-zh] §2.1: W_i = B(phi_i) W_base B(theta_i)^T)
+# ---------------------------------------------------------------------------
+def expert_matrix(theta: np.ndarray, phi: np.ndarray, w_base: np.ndarray,
+                  alpha: float = 1.0) -> np.ndarray:
+    """Materialise W_e = B(phi) (alpha W_base) B(theta)^T as a float64 array."""
+    W = alpha * np.asarray(w_base, dtype=np.float64)
+    P = butterfly_apply(phi, W)                     # B(phi) @ W
+    return butterfly_apply(theta, P.T).T            # (B(theta) @ P^T)^T = P B(theta)^T
+
+
+def expert_apply(theta: np.ndarray, phi: np.ndarray, w_base: np.ndarray, X: np.ndarray,
+                 alpha: float = 1.0) -> np.ndarray:
+    """W_e @ X evaluated right to left: B(phi) (alpha W_base (B(theta)^T X)).
+
+    Same value as ``expert_matrix(...) @ X`` by associativity; used where
+    materialising every expert is too slow (sampled tokens of large layers).
+    X has shape (d_in, m).
+    """
+    U = butterfly_apply(theta, X, transpose=True)
+    Z = alpha * (np.asarray(w_base, dtype=np.float64) @ U)
+    return butterfly_apply(phi, Z)
+
+
+def gelu(h: np.ndarray) -> np.ndarray:
+    """Exact GELU, h * Phi(h) = h * (1 + erf(h / sqrt 2)) / 2."""
+    return h * 0.5 * (1.0 + _erf(h / math.sqrt(2.0)))
+
+
+# ---------------------------------------------------------------------------
+# routing  ([MoE-nl] §2 "Gated Routing": standard top-k gating network)
+# ---------------------------------------------------------------------------
+class Routing:
+    def __init__(self, logits, idx, gates, probs, ambiguous, gap_eps):
+        self.logits = logits          # [T][N] float64
+        self.idx = idx                # [T][k] int64
+        self.gates = gates            # [T][k] float64
+        self.probs = probs            # [T][N] float64
+        self.ambiguous = ambiguous    # [T] bool: a decisive gap is within fp64 noise
+        self.gap_eps = gap_eps        # [T] float64
+
+
+def route(x64: np.ndarray, wg64: np.ndarray, k: int, renorm: bool = False) -> Routing:
+    """Top-k softmax gating on logits l = W_g x (no bias, no noise).
+
+    Experts are ordered by logit, larger first, equal logits by lower index.
+    gate = softmax(l)[e] for each chosen e (divided by the sum of the k chosen
+    gates when ``renorm``).  A token is flagged ambiguous when one of the k
+    decisive gaps (between consecutive chosen experts, and between the k-th and
+    the (k+1)-th) is below 4 d 2^-53 |x| max|w| (fp64 rounding level).
+    """
+    T, d = x64.shape
+    N = wg64.shape[0]
+    logits = x64 @ wg64.T
+    order = np.argsort(-logits, axis=1, kind="stable")
+    idx = order[:, :k]
+    m = logits.max(axis=1, keepdims=True)
+    ex = np.exp(logits - m)
+    probs = ex / ex.sum(axis=1, keepdims=True)
+    gates = np.take_along_axis(probs, idx, axis=1)
+    if renorm:
+        gates = gates / gates.sum(axis=1, keepdims=True)
+    srt = np.take_along_axis(logits, order, axis=1)
+    n_gaps = min(k, N - 1)
+    eps = 4.0 * d * 2.0 ** -53 * np.linalg.norm(x64, axis=1) * np.linalg.norm(wg64, axis=1).max()
+    if n_gaps > 0:
+        gaps = srt[:, :n_gaps] - srt[:, 1:n_gaps + 1]
+        ambiguous = (gaps < eps[:, None]).any(axis=1)
+    else:
+        ambiguous = np.zeros(T, dtype=bool)
+    return Routing(logits, idx, gates, probs, ambiguous, eps)
+
+
+# ---------------------------------------------------------------------------
+# layer forward
+# ---------------------------------------------------------------------------
+def _inputs_f64(inp):
+    cfg = inp.cfg
+    x = stored_to_f64(inp.x, cfg.act)
+    wg = stored_to_f64(inp.w_gate, cfg.act)
+    return cfg, x, wg
+
+
+def forward(inp, routing: Optional[Routing] = None, idx_override: Optional[np.ndarray] = None):
+    """Full layer forward by materialising every used expert (the definition).
+
+    y_t = sum_j g_{t,j} W_{e_j} x_t for square experts, and
+    y_t = sum_j g_{t,j} W_dn,e GELU(W_up,e x_t) for FFN experts, where each
+    W_e = B(phi_e) W_base B(theta_e)^T ([MoE-zh] §2.1, [ViT-pt] §2).
+    ``idx_override`` evaluates the layer at given expert choices (gates are then
+    the softmax probabilities of those experts).
+    Returns (y float64 [T][d], routing).
+    """
+    cfg, x, wg = _inputs_f64(inp)
+    if routing is None:
+        routing = route(x, wg, cfg.top_k, cfg.renorm_gates)
+    idx, gates = routing.idx, routing.gates
+    if idx_override is not None:
+        idx = np.asarray(idx_override)
+        gates = np.take_along_axis(routing.probs, idx, axis=1)
+        if cfg.renorm_gates:
+            gates = gates / gates.sum(axis=1, keepdims=True)
+    T = x.shape[0]
+    y = np.zeros((T, cfg.d_model))
+    for e in np.unique(idx):
+        tok, slot = np.nonzero(idx == e)
+        Xe = x[tok]                                     # rows = tokens
+        if cfg.is_ffn:
+            Wup = expert_matrix(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], cfg.w_scale)
+            Wdn = expert_matrix(inp.theta[1][e], inp.phi[1][e], inp.w_base[1], cfg.w_scale)
+            Ye = gelu(Xe @ Wup.T) @ Wdn.T
+        else:
+            We = expert_matrix(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], cfg.w_scale)
+            Ye = Xe @ We.T
+        np.add.at(y, tok, gates[tok, slot][:, None] * Ye)
+    return y, routing
+
+
+def forward_tokens(inp, tokens: Sequence[int], routing: Optional[Routing] = None,
+                   idx_override: Optional[np.ndarray] = None):
+    """Layer output for a subset of tokens, one token at a time, without
+    materialising experts (right-to-left evaluation of the same products).
+
+    Used for sampled checks of layers too large to materialise.  Routing is
+    computed for the requested tokens only unless ``routing`` is given.
+    Returns (y float64 [len(tokens)][d], idx [len][k], gates [len][k]).
+    """
+    cfg = inp.cfg
+    tokens = np.asarray(tokens, dtype=np.int64)
+    x = stored_to_f64(inp.x[tokens], cfg.act)
+    if routing is None:
+        wg = stored_to_f64(inp.w_gate, cfg.act)
+        r = route(x, wg, cfg.top_k, cfg.renorm_gates)
+        idx, gates, probs = r.idx, r.gates, r.probs
+    else:
+        idx, gates, probs = routing.idx[tokens], routing.gates[tokens], routing.probs[tokens]
+    if idx_override is not None:
+        idx = np.asarray(idx_override)
+        gates = np.take_along_axis(probs, idx, axis=1)
+        if cfg.renorm_gates:
+            gates = gates / gates.sum(axis=1, keepdims=True)
+    y = np.zeros((len(tokens), cfg.d_model))
+    for t in range(len(tokens)):
+        for j in range(idx.shape[1]):
+            e = int(idx[t, j])
+            v = x[t][:, None]
+            if cfg.is_ffn:
+                h = expert_apply(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], v, cfg.w_scale)
+                z = expert_apply(inp.theta[1][e], inp.phi[1][e], inp.w_base[1], gelu(h), cfg.w_scale)
+            else:
+                z = expert_apply(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], v, cfg.w_scale)
+            y[t] += gates[t, j] * z[:, 0]
+    return y, idx, gates
+
+
+# ---------------------------------------------------------------------------
+# parameter counts  ([MoE-pt] §2 memory O(d^2 + N d log d); [ViT-pt] §3)
+# ---------------------------------------------------------------------------
+def param_counts(d_model: int, n_experts: int, d_ff: int = 0, angle_bytes: int = 4,
+                 dense_bytes: int = 4) -> dict:
+    """Storage of one layer: shared ternary substrate(s) + per-expert angles,
+    against N independent dense experts of the same shapes."""
+    shapes = [(d_ff, d_model), (d_model, d_ff)] if d_ff else [(d_model, d_model)]
+    angles_per_expert = 0
+    substrate_weights = 0
+    for d_out, d_in in shapes:
+        angles_per_expert += (d_in // 2) * int(math.log2(d_in)) + (d_out // 2) * int(math.log2(d_out))
+        substrate_weights += d_out * d_in
+    return {
+        "angles_per_expert": angles_per_expert,
+        "angle_bytes_total": n_experts * angles_per_expert * angle_bytes,
+        "substrate_weights": substrate_weights,
+        "substrate_bytes_2bit": substrate_weights * 2 // 8,
+        "ternary_entropy_bits": math.log2(3.0),
+        "dense_expert_bytes_total": n_experts * substrate_weights * dense_bytes,
+    }

@@ -1,0 +1,288 @@
+"""Pins of the fp64 oracle against mathematics and the pages' figures.
+
+Each test checks the oracle against something other than itself: a textbook
+matrix, a hand-expanded product, closed forms, invariants that any correct
+implementation satisfies, brute force on tiny inputs, or a figure the pages
+print.  A plausible slip (dropped stage, wrong sign, transposed operand, wrong
+pair wiring, wrong stage order, dropped gate) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from compressed_mixture_experts_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def rand_angles(n, seed=0):
+    r = np.random.default_rng(seed)
+    L = int(math.log2(n))
+    return r.uniform(-math.pi, math.pi, size=(L, n // 2))
+
+
+# ---------------------------------------------------------------- butterfly
+def test_d2_is_textbook_givens():
+    t = 0.7
+    B = ref.butterfly_dense(np.array([[t]]))
+    G = np.array([[math.cos(t), -math.sin(t)], [math.sin(t), math.cos(t)]])
+    assert np.allclose(B, G, atol=1e-15, rtol=0)
+    Bv = ref.butterfly_apply(np.array([[t]]), np.array([1.0, 0.0]))
+    assert np.allclose(Bv, [math.cos(t), math.sin(t)], atol=1e-15)
+
+
+def test_d4_hand_expanded():
+    a0, a1, b0, b1 = 0.3, -1.1, 2.0, 0.45
+    A = np.array([[a0, a1], [b0, b1]])  # stage 0 angles (a0,a1), stage 1 (b0,b1)
+    ca0, sa0, ca1, sa1 = math.cos(a0), math.sin(a0), math.cos(a1), math.sin(a1)
+    cb0, sb0, cb1, sb1 = math.cos(b0), math.sin(b0), math.cos(b1), math.sin(b1)
+    expect = np.array([
+        [cb0 * ca0, -cb0 * sa0, -sb0 * ca1, sb0 * sa1],
+        [cb1 * sa0, cb1 * ca0, -sb1 * sa1, -sb1 * ca1],
+        [sb0 * ca0, -sb0 * sa0, cb0 * ca1, -cb0 * sa1],
+        [sb1 * sa0, sb1 * ca0, cb1 * sa1, cb1 * ca1],
+    ])
+    assert np.allclose(ref.butterfly_dense(A), expect, atol=1e-15, rtol=0)
+    assert np.allclose(ref.butterfly_apply(A, np.eye(4)), expect, atol=1e-15, rtol=0)
+    assert np.allclose(ref.butterfly_apply(A, np.eye(4), transpose=True), expect.T, atol=1e-15, rtol=0)
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 64])
+def test_applied_equals_dense(n):
+    A = rand_angles(n, n)
+    B = ref.butterfly_dense(A)
+    M = rng.standard_normal((n, 5))
+    assert np.allclose(ref.butterfly_apply(A, M), B @ M, atol=1e-12, rtol=0)
+    assert np.allclose(ref.butterfly_apply(A, M, transpose=True), B.T @ M, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 256])
+def test_orthogonal_det_norm(n):
+    A = rand_angles(n, 7 + n)
+    B = ref.butterfly_apply(A, np.eye(n))
+    assert np.abs(B @ B.T - np.eye(n)).max() < 1e-12
+    assert abs(np.linalg.det(B) - 1.0) < 1e-9
+    v = rng.standard_normal(n)
+    assert abs(np.linalg.norm(ref.butterfly_apply(A, v)) - np.linalg.norm(v)) < 1e-12 * np.linalg.norm(v)
+    back = ref.butterfly_apply(A, ref.butterfly_apply(A, v), transpose=True)
+    assert np.abs(back - v).max() < 1e-12
+
+
+@pytest.mark.parametrize("n", [2, 8, 64])
+def test_closed_forms(n):
+    L = int(math.log2(n))
+    eye = np.eye(n)
+    zero = np.zeros((L, n // 2))
+    assert np.array_equal(ref.butterfly_apply(zero, eye), eye)
+    Bpi = ref.butterfly_apply(np.full((L, n // 2), math.pi), eye)
+    assert np.abs(Bpi - (-1) ** L * eye).max() < 1e-14
+    # all angles pi/2: (B x)_i = (-1)^(L - popcount i) x_{n-1-i}
+    Bh = ref.butterfly_apply(np.full((L, n // 2), math.pi / 2), eye)
+    P = np.zeros((n, n))
+    for i in range(n):
+        P[i, n - 1 - i] = (-1) ** (L - bin(i).count("1"))
+    assert np.abs(Bh - P).max() < 1e-14
+    # all angles pi/4: Walsh-Hadamard up to signs, B_ij = 2^(-L/2) (-1)^popcount(~i & j)
+    Bq = ref.butterfly_apply(np.full((L, n // 2), math.pi / 4), eye)
+    H = np.array([[(-1) ** bin((~i) & j & (n - 1)).count("1") for j in range(n)] for i in range(n)])
+    assert np.abs(Bq - H * 2.0 ** (-L / 2)).max() < 1e-14
+
+
+def test_stage_order_matters_and_is_pinned():
+    # applying the stages in the opposite order gives a different matrix: the
+    # d=4 hand expansion above fixes which one the oracle uses.
+    A = rand_angles(8, 3)
+    B = ref.butterfly_dense(A)
+    Brev = np.eye(8)
+    for s in range(3):  # S_0 S_1 S_2: stride-n/2 stage applied first
+        Brev = Brev @ ref.stage_matrix(A[s], s, 8)
+    assert np.abs(B - Brev).max() > 1e-3
+
+
+def test_pair_index_bit_deletion():
+    for s in range(4):
+        seen = set()
+        for i in range(16):
+            if i & (1 << s):
+                continue
+            p = ref.pair_index(i, s)
+            seen.add(p)
+            # brute force: rank of i among indices with bit s clear
+            assert p == sum(1 for q in range(i) if not q & (1 << s))
+        assert seen == set(range(8))
+
+
+# ---------------------------------------------------------------- experts
+def test_orbit_invariants():
+    d = 16
+    r = np.random.default_rng(5)
+    W = r.integers(-1, 2, size=(d, d)).astype(np.int8)
+    We = ref.expert_matrix(rand_angles(d, 1), rand_angles(d, 2), W)
+    assert abs(np.linalg.norm(We) - np.linalg.norm(W.astype(float))) < 1e-12
+    sv = np.linalg.svd(We, compute_uv=False)
+    sv0 = np.linalg.svd(W.astype(float), compute_uv=False)
+    assert np.abs(sv - sv0).max() < 1e-12
+
+
+def test_expert_matrix_explicit_products():
+    d_out, d_in = 8, 4
+    r = np.random.default_rng(9)
+    W = r.integers(-1, 2, size=(d_out, d_in)).astype(np.int8)
+    th, ph = rand_angles(d_in, 4), rand_angles(d_out, 5)
+    expect = ref.butterfly_dense(ph) @ (2.5 * W) @ ref.butterfly_dense(th).T
+    assert np.abs(ref.expert_matrix(th, ph, W, 2.5) - expect).max() < 1e-12
+    X = r.standard_normal((d_in, 3))
+    assert np.abs(ref.expert_apply(th, ph, W, X, 2.5) - expect @ X).max() < 1e-12
+
+
+def test_identity_expert_all_angles_zero():
+    cfg = wl.small_config(d_model=16, n_experts=3, top_k=2, tokens=9, act="f32")
+    inp = wl.generate(cfg, angle_mode="zero")
+    y, r = ref.forward(inp)
+    x = inp.x.astype(np.float64)
+    W = inp.w_base[0].astype(np.float64)
+    expect = (r.gates.sum(axis=1)[:, None]) * (x @ W.T)
+    assert np.abs(y - expect).max() < 1e-12
+
+
+def test_gelu_against_normal_cdf_table():
+    tab = json.load(open(os.path.join(GOLDEN, "normal_cdf.json")))["values"]
+    for x, phi in tab:
+        assert abs(ref.gelu(np.array(x)) - x * phi) < 1e-15
+
+
+# ---------------------------------------------------------------- routing
+def test_route_brute_force_small_n():
+    r = np.random.default_rng(77)
+    for N in (2, 3, 5, 8):
+        for k in range(1, N + 1):
+            x = r.standard_normal((6, 4))
+            wg = r.standard_normal((N, 4))
+            R = ref.route(x, wg, k)
+            for t in range(6):
+                l = [float(np.dot(x[t], wg[e])) for e in range(N)]
+                best = max(itertools.permutations(range(N), k),
+                           key=lambda p: tuple(l[e] for e in p) + tuple(-e for e in p))
+                assert tuple(R.idx[t]) == best
+                z = sum(math.exp(v - max(l)) for v in l)
+                for j, e in enumerate(best):
+                    assert abs(R.gates[t, j] - math.exp(l[e] - max(l)) / z) < 1e-14
+
+
+def test_route_ties_go_to_lower_index_and_softmax_sums_to_one():
+    x = np.array([[1.0, 0.0]])
+    wg = np.array([[0.5, 0.0], [2.0, 0.0], [2.0, 1.0], [0.5, 3.0]])  # experts 1 and 2 tie
+    R = ref.route(x, wg, 3)
+    assert list(R.idx[0]) == [1, 2, 0]
+    assert abs(R.probs.sum() - 1.0) < 1e-15
+    assert R.ambiguous[0]  # the tie is a decisive gap of 0
+    Rn = ref.route(x, wg, 2, renorm=True)
+    assert abs(Rn.gates.sum() - 1.0) < 1e-15
+
+
+def test_route_one_hot_gate_columns():
+    d, N = 8, 8
+    wg = np.eye(N, d) * np.arange(1, N + 1)[:, None]  # expert e reads channel e
+    x = np.zeros((3, d))
+    x[0, 5] = 1.0
+    x[1, 2] = 1.0
+    x[2, 7] = -1.0
+    R = ref.route(x, wg, 1)
+    assert list(R.idx[:, 0]) == [5, 2, 0]  # token 2: all logits <= 0, ties -> expert 0...
+
+
+# ---------------------------------------------------------------- layer
+def _brute_forward(inp):
+    """Pure-Python loop forward with dense butterflies (tiny sizes only)."""
+    cfg = inp.cfg
+    x = ref.stored_to_f64(inp.x, cfg.act)
+    wg = ref.stored_to_f64(inp.w_gate, cfg.act)
+    T, d = x.shape
+    out = np.zeros((T, d))
+    for t in range(T):
+        l = [sum(x[t, i] * wg[e, i] for i in range(d)) for e in range(cfg.n_experts)]
+        order = sorted(range(cfg.n_experts), key=lambda e: (-l[e], e))[:cfg.top_k]
+        m = max(l)
+        z = sum(math.exp(v - m) for v in l)
+        g = [math.exp(l[e] - m) / z for e in order]
+        if cfg.renorm_gates:
+            sg = sum(g)
+            g = [v / sg for v in g]
+        for gj, e in zip(g, order):
+            def apply(mi, v):
+                B_th = ref.butterfly_dense(inp.theta[mi][e])
+                B_ph = ref.butterfly_dense(inp.phi[mi][e])
+                W = cfg.w_scale * inp.w_base[mi].astype(np.float64)
+                u = [sum(B_th[i, r] * v[i] for i in range(len(v))) for r in range(B_th.shape[0])]
+                h = [sum(W[o, r] * u[r] for r in range(len(u))) for o in range(W.shape[0])]
+                return [sum(B_ph[o, p] * h[p] for p in range(len(h))) for o in range(len(h))]
+            if cfg.is_ffn:
+                h = apply(0, x[t])
+                a = [hv * 0.5 * (1 + math.erf(hv / math.sqrt(2))) for hv in h]
+                zz = apply(1, a)
+            else:
+                zz = apply(0, x[t])
+            for o in range(d):
+                out[t, o] += gj * zz[o]
+    return out
+
+
+@pytest.mark.parametrize("ffn", [False, True])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_forward_against_brute_loops(ffn, renorm):
+    cfg = wl.small_config(d_model=8, d_ff=16 if ffn else 0, n_experts=3, top_k=2, tokens=5,
+                          act="f32", renorm_gates=renorm, w_scale=1.5, seed_index=21)
+    inp = wl.generate(cfg)
+    y, _ = ref.forward(inp)
+    yb = _brute_forward(inp)
+    assert np.abs(y - yb).max() < 1e-12 * max(1.0, np.abs(yb).max())
+
+
+@pytest.mark.parametrize("ffn", [False, True])
+def test_forward_tokens_equals_materialised(ffn):
+    cfg = wl.small_config(d_model=32, d_ff=64 if ffn else 0, n_experts=5, top_k=2, tokens=23,
+                          act="bf16", seed_index=33)
+    inp = wl.generate(cfg)
+    y, r = ref.forward(inp)
+    toks = [0, 4, 17, 22]
+    ys, idx, g = ref.forward_tokens(inp, toks)
+    assert np.array_equal(idx, r.idx[toks])
+    assert np.abs(ys - y[toks]).max() < 1e-11 * np.abs(y).max()
+
+
+# ---------------------------------------------------------------- page figures
+def test_page_parameter_figures():
+    figs = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+    assert round(math.log2(3), 2) == figs["ternary_bits_per_weight"]["value"]
+    m = figs["memory_256_experts_d512_MB"]
+    pc = ref.param_counts(m["d_model"], m["n_experts"])
+    assert pc["angles_per_expert"] == 512 * 9  # two butterflies of 256 * 9 angles
+    mb = pc["angle_bytes_total"] / 1e6
+    assert abs(mb - m["value"]) / m["value"] < 0.005
+    # n_l * d per expert with n_l = log2 d (ViT page, contributions section)
+    for d in (64, 256, 1024):
+        assert ref.param_counts(d, 1)["angles_per_expert"] == int(math.log2(d)) * d
+    # sub-linear: dense storage grows ~N d^2, angles ~N d log d
+    a = ref.param_counts(512, 256)
+    assert a["dense_expert_bytes_total"] / (a["angle_bytes_total"] + a["substrate_bytes_2bit"]) > 50
+
+
+def test_generator_stored_values():
+    cfg = wl.CONFIGS[1]
+    inp = wl.generate(cfg.with_tokens(64))
+    assert inp.x.dtype == np.uint16 and inp.x.shape == (64, 512)
+    assert inp.w_gate.shape == (64, 512)
+    assert set(np.unique(inp.w_base[0])) <= {-1, 0, 1}
+    assert inp.theta[0].shape == (64, 9, 256) and inp.phi[0].shape == (64, 9, 256)
+    # round trip: bf16 bits widen exactly
+    x64 = ref.stored_to_f64(inp.x, "bf16")
+    assert np.array_equal(wl.round_to_bf16_bits(x64), inp.x)
+    c4 = wl.CONFIGS[4]
+    i4 = wl.generate(c4.with_tokens(8))
+    assert len(i4.outlier_channels) == round(0.01 * 2048)
