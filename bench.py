@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Routed tokens/s of one ButterflyMoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+
+One step = one bmoe_forward over a batch of synthetic tokens (router,
+bucketing, input rotation, ternary substrate product(s), FFN middle when
+present, output rotation and combine), inputs resident in HBM.  Prints one
+JSON line.  The dominant kernel's duration is measured live with HIP events
+recorded around that kernel's launch inside the timed steps; the CPU baseline
+is the fp64 oracle timed on this host over a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+VALU_FP32_PEAK_TFLOPS = 157.3
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime (timing plumbing only)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float(0.0)
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_work(cfg):
+    """Algorithmic bytes and flops of each kernel of one forward.
+
+    Bytes count what the step must move at least once (activations in and out
+    of each kernel, the packed substrate, the angles of every expert, the
+    router weights); flops count multiply-adds as 2.  Returns
+    {name: (bytes, flops, bound)}."""
+    s = 2 if cfg.act == "bf16" else 4
+    T, d, f, N, k = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k
+    R = T * k
+    Ld = int(math.log2(d))
+    ang_d = N * Ld * (d // 2) * 4
+    w = {}
+    w["prep"] = (N * d * s + 8 * N, 2 * N * d, "hbm")
+    w["route"] = (T * d * s + N * d * s + 8 * R, 2 * T * d * N, "hbm")
+    w["bucket"] = (4 * R + 4 * R + 4 * (N + 1), 0, "hbm")
+    w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
+
+    def gemm(din, dout):
+        fl = 2 * R * din * dout
+        by = R * din * s + R * dout * s + dout * din // 4
+        return (by, fl, "mfma" if fl / by > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm")
+
+    if f == 0:
+        w["gemm"] = gemm(d, d)
+    else:
+        Lf = int(math.log2(f))
+        w["gemm_up"] = gemm(d, f)
+        w["bfly_mid"] = (2 * R * f * s + 2 * N * Lf * (f // 2) * 4, 2 * 6 * R * (f // 2) * Lf, "hbm")
+        w["gemm_down"] = gemm(f, d)
+    w["bfly_out"] = (2 * R * d * s + ang_d + 8 * R, 6 * R * (d // 2) * Ld, "hbm")
+    if k > 1:
+        w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
+    return w
+
+
+def roofline_entry(by, fl, bound, seconds, traffic=None):
+    if bound == "mfma":
+        ach = fl / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    ach = by / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def cpu_baseline(inp, y_gpu, seconds_target: float):
+    """fp64 oracle on this host: full-batch forwards until ~seconds_target."""
+    import numpy as np
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    cfg = inp.cfg
+    t0 = time.perf_counter()
+    reps = 0
+    y_ref = None
+    while True:
+        y_ref, _ = ref.forward(inp)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds_target:
+            break
+    dt = time.perf_counter() - t0
+    err = None
+    if y_gpu is not None:
+        num = np.linalg.norm(y_gpu - y_ref, axis=1)
+        den = np.maximum(np.linalg.norm(y_ref, axis=1), 1e-30)
+        err = float((num / den).max())
+    return {"value": round(cfg.tokens * reps / dt, 1), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{reps} full-batch forward(s) of {cfg.tokens} tokens ({cfg.name}), "
+                      f"materialising every used expert in fp64, {dt:.1f} s",
+            "max_rel_err_gpu_vs_oracle": err}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=None,
+                    help="workload index (default: the d=512, 64-expert layer)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the ButterflyMoE "
+              "forward shards over tokens with no exchange, so N GPUs each run this same step "
+              "on T/N tokens; multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import compressed_mixture_experts_amd as bm
+    from compressed_mixture_experts_amd import workloads as wl
+
+    ci = wl.BENCH_CONFIG_INDEX if args.config is None else args.config
+    cfg = wl.CONFIGS[ci]
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = wl.generate(cfg)
+    layer = bm.Layer.from_inputs(inp, device="cuda")
+    if cfg.act == "bf16":
+        x = torch.from_numpy(inp.x.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        x = torch.from_numpy(inp.x).cuda()
+    y = torch.empty_like(x)
+    names = layer.kernel_names()
+    nk = len(names)
+    ev = HipEvents()
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        layer.forward(x, y)
+    torch.cuda.synchronize()
+
+    # calibration (outside the timed region): every kernel bracketed
+    cal_steps = 10
+    marks = [ev.create(nk + 1) for _ in range(cal_steps)]
+    for i in range(cal_steps):
+        layer.forward_marked(x, y, marks[i])
+    torch.cuda.synchronize()
+    per_kernel = {n: 0.0 for n in names}
+    for i in range(cal_steps):
+        for j, n in enumerate(names):
+            per_kernel[n] += ev.elapsed_ms(marks[i][j], marks[i][j + 1]) / cal_steps
+    for m in marks:
+        ev.destroy(m)
+    dom = max(per_kernel, key=per_kernel.get)
+    dj = names.index(dom)
+
+    # timed region: K steps, HIP events around the dominant kernel's launch
+    K = args.steps
+    starts, stops = ev.create(K), ev.create(K)
+    step_marks = []
+    for i in range(K):
+        m = [None] * (nk + 1)
+        m[dj], m[dj + 1] = starts[i], stops[i]
+        step_marks.append(m)
+    print(f"[bench] timing {K} steps (dominant kernel {dom})", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        layer.forward_marked(x, y, step_marks[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom_ms = sum(ev.elapsed_ms(starts[i], stops[i]) for i in range(K)) / K
+    ev.destroy(starts)
+    ev.destroy(stops)
+    elapsed = t1 - t0
+    ms_per_step = elapsed / K * 1e3
+    value = cfg.tokens * K / elapsed
+
+    work = kernel_work(cfg)
+    by, fl, bound = work[dom]
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tj = json.load(open(tfile)).get(f"{cfg.name}:{dom}")
+            if tj and tj.get("kernel_source_sha") == bm_kernel_sha(dom):
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roof = roofline_entry(by, fl, bound, dom_ms / 1e3, traffic)
+    roof["kernel"] = dom
+    roof["avg_us"] = round(dom_ms * 1e3, 2)
+
+    kernels = {}
+    for n in names:
+        b_, f_, bd_ = work[n]
+        e = roofline_entry(b_, f_, bd_, per_kernel[n] / 1e3)
+        kernels[n] = {"us": round(per_kernel[n] * 1e3, 2), "bound": bd_, "frac": e["frac"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        y64 = y.float().cpu().numpy().astype(np.float64)
+        cpu = cpu_baseline(inp, y64, args.cpu_seconds)
+
+    out = {
+        "metric": "routed tokens/sec per ButterflyMoE layer",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act,
+        "data": "synthetic (seeded Gaussian activations, uniform ternary substrate, uniform angles)",
+        "config": {"workload": cfg.name, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k, "tokens": cfg.tokens,
+                   "routed_rows": cfg.tokens * cfg.top_k, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def bm_kernel_sha(kernel: str) -> str:
+    """Hash of the HIP source that holds `kernel` (to invalidate stale counters)."""
+    import hashlib
+    src = {"gemm": "gemm.hip", "gemm_up": "gemm.hip", "gemm_down": "gemm.hip", "combine": "gemm.hip",
+           "route": "route.hip", "prep": "route.hip", "bucket": "route.hip"}.get(kernel, "butterfly.hip")
+    p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

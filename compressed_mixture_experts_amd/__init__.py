@@ -1,0 +1,288 @@
+"""ButterflyMoE expert layer on AMD MI355X (gfx950): Python binding.
+
+The computation runs in ``libbmoe.so`` (hand-written HIP kernels behind the C
+ABI of ``include/bmoe.h``).  This module only marshals arguments: torch
+tensors provide device memory and the current HIP stream.  There is no
+fallback path; if the library is missing, loading it raises.
+
+    import compressed_mixture_experts_amd as bmoe
+    layer = bmoe.Layer.from_inputs(inputs, device="cuda")   # uploads + packs
+    y = layer.forward(x)                                     # x: [T][d] on the GPU
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
+    "dbg_butterfly", "dbg_ternary_gemm", "STATUS", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libbmoe.so")
+
+STATUS = {
+    0: "BMOE_OK", 1: "BMOE_ERR_NULL", 2: "BMOE_ERR_SHAPE", 3: "BMOE_ERR_DTYPE",
+    4: "BMOE_ERR_ALIGN", 5: "BMOE_ERR_ALIAS", 6: "BMOE_ERR_WORKSPACE",
+    7: "BMOE_ERR_TERNARY", 8: "BMOE_ERR_HIP", 9: "BMOE_ERR_DEVICE",
+}
+F32, BF16 = 0, 1
+ACT_NONE, ACT_GELU_ERF = 0, 1
+
+EXPORTED_SYMBOLS = [
+    "bmoe_packed_words", "bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_route",
+    "bmoe_forward", "bmoe_status_string", "bmoe_last_error",
+    "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_forward_kernels",
+    "bmoe_dbg_forward_marked",
+]
+
+
+class BmoeError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+class LayerStruct(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32), ("ffn_act", ctypes.c_int32),
+        ("renorm_gates", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("w_gate", ctypes.c_void_p),
+        ("w_base", ctypes.c_void_p * 2),
+        ("theta", ctypes.c_void_p * 2),
+        ("phi", ctypes.c_void_p * 2),
+        ("w_scale", ctypes.c_float * 2),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbmoe.so (built in-tree by compressed_mixture_experts_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m compressed_mixture_experts_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    c_i32, c_sz, c_vp, c_f = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    pL = ctypes.POINTER(LayerStruct)
+    L.bmoe_packed_words.argtypes = [c_i32, c_i32]
+    L.bmoe_packed_words.restype = c_sz
+    L.bmoe_pack_ternary.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz]
+    L.bmoe_workspace_size.argtypes = [pL, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_route.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+    L.bmoe_forward.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+    L.bmoe_status_string.argtypes = [c_i32]
+    L.bmoe_status_string.restype = ctypes.c_char_p
+    L.bmoe_last_error.argtypes = []
+    L.bmoe_last_error.restype = ctypes.c_char_p
+    L.bmoe_dbg_butterfly.argtypes = [c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
+    L.bmoe_dbg_ternary_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
+    L.bmoe_dbg_forward_kernels.argtypes = [pL, ctypes.POINTER(c_i32), ctypes.c_char_p, c_sz]
+    L.bmoe_dbg_forward_marked.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_i32]
+    for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_route", "bmoe_forward",
+                 "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_forward_kernels",
+                 "bmoe_dbg_forward_marked"):
+        getattr(L, name).restype = c_i32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        detail = lib().bmoe_last_error().decode(errors="replace")
+        raise BmoeError(status, detail)
+
+
+def packed_words(rows: int, cols: int) -> int:
+    return int(lib().bmoe_packed_words(rows, cols))
+
+
+def pack_ternary(w: np.ndarray) -> np.ndarray:
+    """int8 [rows][cols] in {-1,0,1} -> uint32 [rows][cols/16] (host, via the C ABI)."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    if w.ndim != 2:
+        raise ValueError("pack_ternary expects a 2-D array")
+    rows, cols = w.shape
+    nw = packed_words(rows, cols)
+    out = np.zeros(max(nw, 1), dtype=np.uint32)
+    _check(lib().bmoe_pack_ternary(w.ctypes.data, rows, cols, out.ctypes.data, nw))
+    return out[:nw].reshape(rows, cols // 16)
+
+
+# --------------------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _to_device_act(a: np.ndarray, act: str, device):
+    torch = _torch()
+    if act == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device).contiguous()
+
+
+class Layer:
+    """A ButterflyMoE layer resident on one GPU (weights packed and uploaded)."""
+
+    def __init__(self, *, d_model: int, d_ff: int, n_experts: int, top_k: int, act: str,
+                 ffn_act: str, renorm_gates: bool, w_gate, w_base_packed: Sequence,
+                 theta: Sequence, phi: Sequence, w_scale: Sequence[float]):
+        self.d_model, self.d_ff, self.n_experts, self.top_k = d_model, d_ff, n_experts, top_k
+        self.act = act
+        self.w_gate = w_gate
+        self.w_base = list(w_base_packed)
+        self.theta = list(theta)
+        self.phi = list(phi)
+        s = LayerStruct()
+        s.d_model, s.d_ff, s.n_experts, s.top_k = d_model, d_ff, n_experts, top_k
+        s.act_dtype = BF16 if act == "bf16" else F32
+        s.ffn_act = ACT_GELU_ERF if ffn_act == "gelu" else ACT_NONE
+        s.renorm_gates = 1 if renorm_gates else 0
+        s.reserved = 0
+        s.w_gate = _ptr(w_gate)
+        for m in range(2):
+            s.w_base[m] = _ptr(self.w_base[m]) if m < len(self.w_base) else None
+            s.theta[m] = _ptr(self.theta[m]) if m < len(self.theta) else None
+            s.phi[m] = _ptr(self.phi[m]) if m < len(self.phi) else None
+            s.w_scale[m] = float(w_scale[m]) if m < len(w_scale) else 1.0
+        self.struct = s
+        self._ws = None
+
+    @classmethod
+    def from_inputs(cls, inp, device="cuda") -> "Layer":
+        """Pack and upload the arrays of a workloads.LayerInputs."""
+        torch = _torch()
+        cfg = inp.cfg
+        packed = [torch.from_numpy(pack_ternary(w).view(np.int32)).to(device).contiguous()
+                  for w in inp.w_base]
+        th = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device) for a in inp.theta]
+        ph = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device) for a in inp.phi]
+        wg = _to_device_act(inp.w_gate, cfg.act, device)
+        nsub = len(inp.w_base)
+        return cls(d_model=cfg.d_model, d_ff=cfg.d_ff, n_experts=cfg.n_experts, top_k=cfg.top_k,
+                   act=cfg.act, ffn_act=cfg.ffn_act, renorm_gates=cfg.renorm_gates, w_gate=wg,
+                   w_base_packed=packed, theta=th, phi=ph, w_scale=[cfg.w_scale] * nsub)
+
+    # ---------------------------------------------------------------- workspace
+    def workspace_size(self, T: int) -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib().bmoe_workspace_size(ctypes.byref(self.struct), int(T), ctypes.byref(n)))
+        return int(n.value)
+
+    def workspace(self, T: int, device=None):
+        """A cached device workspace large enough for T tokens."""
+        torch = _torch()
+        need = self.workspace_size(T)
+        if self._ws is None or self._ws.numel() < need:
+            dev = device if device is not None else self.w_gate.device
+            self._ws = torch.empty(max(need, 256) + 256, dtype=torch.uint8, device=dev)
+        ws = self._ws
+        off = (-int(ws.data_ptr())) % 256
+        return ws[off:], need
+
+    # ---------------------------------------------------------------- calls
+    def route(self, x, with_buckets: bool = False):
+        """Top-k routing of x [T][d_model].  Returns (idx [T][k] int32, gate [T][k]
+        fp32[, offsets [N+1], bucket_slots [T*k]])."""
+        torch = _torch()
+        T = int(x.shape[0])
+        dev = x.device
+        idx = torch.empty((T, self.top_k), dtype=torch.int32, device=dev)
+        gate = torch.empty((T, self.top_k), dtype=torch.float32, device=dev)
+        off = slots = None
+        if with_buckets:
+            off = torch.empty(self.n_experts + 1, dtype=torch.int32, device=dev)
+            slots = torch.empty(max(T * self.top_k, 1), dtype=torch.int32, device=dev)
+        ws, nbytes = self.workspace(T, dev)
+        _check(lib().bmoe_route(ctypes.byref(self.struct), _ptr(x), T, _ptr(idx), _ptr(gate),
+                                _ptr(off), _ptr(slots), _ptr(ws), nbytes, _stream_handle()))
+        if with_buckets:
+            return idx, gate, off, slots[:T * self.top_k]
+        return idx, gate
+
+    def forward(self, x, y=None, return_routing: bool = False):
+        """y [T][d_model] = ButterflyMoE layer(x)."""
+        torch = _torch()
+        T = int(x.shape[0])
+        if y is None:
+            y = torch.empty_like(x)
+        idx = gate = None
+        if return_routing:
+            idx = torch.empty((T, self.top_k), dtype=torch.int32, device=x.device)
+            gate = torch.empty((T, self.top_k), dtype=torch.float32, device=x.device)
+        ws, nbytes = self.workspace(T, x.device)
+        _check(lib().bmoe_forward(ctypes.byref(self.struct), _ptr(x), T, _ptr(y), _ptr(idx),
+                                  _ptr(gate), _ptr(ws), nbytes, _stream_handle()))
+        if return_routing:
+            return y, idx, gate
+        return y
+
+
+    def kernel_names(self) -> List[str]:
+        """Names of the kernel launches of one forward, in order."""
+        n = ctypes.c_int32(0)
+        buf = ctypes.create_string_buffer(512)
+        _check(lib().bmoe_dbg_forward_kernels(ctypes.byref(self.struct), ctypes.byref(n), buf, 512))
+        return buf.value.decode().split(",")[: n.value]
+
+    def forward_marked(self, x, y, marks):
+        """Forward into y, recording the raw hipEvent_t handles in `marks`
+        (list of ints or None) before the first and after each kernel launch."""
+        T = int(x.shape[0])
+        ws, nbytes = self.workspace(T, x.device)
+        arr = (ctypes.c_void_p * max(len(marks), 1))(*[m if m else None for m in marks])
+        _check(lib().bmoe_dbg_forward_marked(ctypes.byref(self.struct), _ptr(x), T, _ptr(y),
+                                             _ptr(ws), nbytes, _stream_handle(), arr, len(marks)))
+        return y
+
+
+def dbg_butterfly(angles, x, transpose: bool = False, out=None):
+    """Rows of x [rows][n] -> B(angles) row (or B^T row); angles [log2 n][n/2] fp32."""
+    torch = _torch()
+    rows, n = int(x.shape[0]), int(x.shape[1])
+    log2n = n.bit_length() - 1
+    dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().bmoe_dbg_butterfly(log2n, rows, _ptr(angles), 1 if transpose else 0, dtype,
+                                    _ptr(x), _ptr(out), _stream_handle()))
+    return out
+
+
+def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):
+    """z [M][n_out] = alpha * a [M][K] @ W^T with W packed [n_out][K/16]."""
+    torch = _torch()
+    M, K = int(a.shape[0]), int(a.shape[1])
+    dtype = BF16 if a.dtype == torch.bfloat16 else F32
+    z = torch.empty((M, n_out), dtype=a.dtype, device=a.device)
+    _check(lib().bmoe_dbg_ternary_gemm(M, n_out, K, dtype, _ptr(a), _ptr(w_packed), float(alpha),
+                                       _ptr(z), _stream_handle()))
+    return z

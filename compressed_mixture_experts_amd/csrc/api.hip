@@ -1,0 +1,463 @@
+// Host side of the C ABI declared in include/bmoe.h and include/bmoe_debug.h:
+// argument validation (all before any enqueue), workspace planning, and the
+// launch sequence of the forward pass on the caller's stream.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/bmoe.h"
+#include "../../include/bmoe_debug.h"
+#include "common.hpp"
+
+using namespace bmoe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bmoe_status fail(bmoe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bmoe_status fail(bmoe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bmoe_status ok() {
+  g_last_error.clear();
+  return BMOE_OK;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+size_t act_size(int act) { return act == BMOE_BF16 ? 2 : 4; }
+
+constexpr int32_t kMaxTokens = 1 << 24;
+
+// Per-device gfx950 check, cached.
+std::atomic<int> g_dev_state[64];
+
+bmoe_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BMOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64) {
+    const int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return BMOE_OK;
+    if (st == 2) return fail(BMOE_ERR_DEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(BMOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) g_dev_state[dev].store(good ? 1 : 2, std::memory_order_relaxed);
+  if (!good) return fail(BMOE_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  return BMOE_OK;
+}
+
+bmoe_status check_layer(const bmoe_layer* L) {
+  if (!L) return fail(BMOE_ERR_NULL, "layer is NULL");
+  if (!is_pow2(L->d_model) || L->d_model < 64 || L->d_model > 8192)
+    return fail(BMOE_ERR_SHAPE, "d_model=%d must be a power of two in [64, 8192]", L->d_model);
+  if (L->d_ff != 0 && (!is_pow2(L->d_ff) || L->d_ff < 64 || L->d_ff > 8192))
+    return fail(BMOE_ERR_SHAPE, "d_ff=%d must be 0 or a power of two in [64, 8192]", L->d_ff);
+  if (L->n_experts < 1 || L->n_experts > 256)
+    return fail(BMOE_ERR_SHAPE, "n_experts=%d must be in [1, 256]", L->n_experts);
+  const int kmax = L->n_experts < 8 ? L->n_experts : 8;
+  if (L->top_k < 1 || L->top_k > kmax)
+    return fail(BMOE_ERR_SHAPE, "top_k=%d must be in [1, %d]", L->top_k, kmax);
+  if (L->act_dtype != BMOE_F32 && L->act_dtype != BMOE_BF16)
+    return fail(BMOE_ERR_DTYPE, "act_dtype=%d is not BMOE_F32 or BMOE_BF16", L->act_dtype);
+  if (L->ffn_act != BMOE_ACT_NONE && L->ffn_act != BMOE_ACT_GELU_ERF)
+    return fail(BMOE_ERR_DTYPE, "ffn_act=%d is unknown", L->ffn_act);
+  if (L->d_ff == 0 && L->ffn_act != BMOE_ACT_NONE)
+    return fail(BMOE_ERR_DTYPE, "ffn_act must be BMOE_ACT_NONE for a square layer");
+  if (L->renorm_gates != 0 && L->renorm_gates != 1)
+    return fail(BMOE_ERR_SHAPE, "renorm_gates=%d must be 0 or 1", L->renorm_gates);
+  if (L->reserved != 0) return fail(BMOE_ERR_SHAPE, "reserved field must be 0");
+  const int nsub = L->d_ff ? 2 : 1;
+  if (!L->w_gate) return fail(BMOE_ERR_NULL, "w_gate is NULL");
+  if (!aligned(L->w_gate, 16)) return fail(BMOE_ERR_ALIGN, "w_gate is not 16-byte aligned");
+  for (int m = 0; m < nsub; ++m) {
+    if (!L->w_base[m]) return fail(BMOE_ERR_NULL, "w_base[%d] is NULL", m);
+    if (!L->theta[m]) return fail(BMOE_ERR_NULL, "theta[%d] is NULL", m);
+    if (!L->phi[m]) return fail(BMOE_ERR_NULL, "phi[%d] is NULL", m);
+    if (!aligned(L->w_base[m], 16)) return fail(BMOE_ERR_ALIGN, "w_base[%d] is not 16-byte aligned", m);
+    if (!aligned(L->theta[m], 4) || !aligned(L->phi[m], 4))
+      return fail(BMOE_ERR_ALIGN, "angles of substrate %d are not 4-byte aligned", m);
+  }
+  return BMOE_OK;
+}
+
+// Workspace layout (offsets in bytes, each 256-byte aligned).
+struct Plan {
+  size_t counts, wnorm2, offsets, perm, idx, gate, bufU, bufZ, total;
+  int64_t R;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Plan make_plan(const bmoe_layer* L, int32_t T) {
+  Plan p{};
+  const int64_t R = int64_t(T) * L->top_k;
+  const size_t s = act_size(L->act_dtype);
+  const int64_t d = L->d_model, f = L->d_ff;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  p.counts = take(size_t(L->n_experts) * 4);
+  p.wnorm2 = take(size_t(L->n_experts) * 4);
+  p.offsets = take(size_t(L->n_experts + 1) * 4);
+  p.perm = take(size_t(R) * 4);
+  p.idx = take(size_t(R) * 4);
+  p.gate = take(size_t(R) * 4);
+  p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
+  p.bufZ = take(size_t(R) * (f > d ? f : d) * s);    // Z / H / A, then per-slot Y (FFN)
+  p.total = o;
+  p.R = R;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+#define BMOE_HIP(call)                                                                 \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess) return fail(BMOE_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+bmoe_status validate_call(const bmoe_layer* L, const void* x, int32_t T, void* ws, size_t ws_bytes,
+                          Plan& plan) {
+  bmoe_status st = check_layer(L);
+  if (st != BMOE_OK) return st;
+  if (T < 0 || T > kMaxTokens) return fail(BMOE_ERR_SHAPE, "T=%d must be in [0, %d]", T, kMaxTokens);
+  plan = make_plan(L, T);
+  if (T == 0) return BMOE_OK;
+  if (!x) return fail(BMOE_ERR_NULL, "x is NULL");
+  if (!ws) return fail(BMOE_ERR_NULL, "workspace is NULL");
+  if (!aligned(x, 16)) return fail(BMOE_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned(ws, 256)) return fail(BMOE_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if (ws_bytes < plan.total)
+    return fail(BMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, plan.total);
+  const Range rx{x, size_t(T) * L->d_model * act_size(L->act_dtype)};
+  if (overlap(rx, Range{ws, plan.total})) return fail(BMOE_ERR_ALIAS, "x overlaps the workspace");
+  return BMOE_OK;
+}
+
+bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* idx, float* gate,
+                      void* ws, const Plan& p, hipStream_t s) {
+  const int act = L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
+  int32_t* counts = at<int32_t>(ws, p.counts);
+  float* wn2 = at<float>(ws, p.wnorm2);
+  BMOE_HIP(launch_prep(L->w_gate, act, L->n_experts, L->d_model, wn2, counts, s));
+  RouteArgs ra{x, L->w_gate, wn2, idx, gate, counts, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates};
+  BMOE_HIP(launch_route(ra, act, s));
+  BucketArgs ba{idx, counts, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts};
+  BMOE_HIP(launch_bucket(ba, s));
+  return BMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bmoe_packed_words(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 16 || cols % 16) return 0;
+  return size_t(rows) * size_t(cols / 16);
+}
+
+bmoe_status bmoe_pack_ternary(const int8_t* w, int32_t rows, int32_t cols, uint32_t* out,
+                              size_t out_words) {
+  if (!w) return fail(BMOE_ERR_NULL, "w is NULL");
+  if (!out) return fail(BMOE_ERR_NULL, "out is NULL");
+  const size_t need = bmoe_packed_words(rows, cols);
+  if (need == 0) return fail(BMOE_ERR_SHAPE, "rows=%d cols=%d: need rows >= 1 and cols a positive multiple of 16", rows, cols);
+  if (out_words < need) return fail(BMOE_ERR_SHAPE, "out has %zu words, %zu needed", out_words, need);
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t wd = 0; wd < cols / 16; ++wd) {
+      uint32_t word = 0;
+      for (int c = 0; c < 16; ++c) {
+        const int64_t i = r * cols + wd * 16 + c;
+        const int8_t v = w[i];
+        if (v < -1 || v > 1)
+          return fail(BMOE_ERR_TERNARY, "w[%lld] = %d (row %lld, column %lld) is not in {-1, 0, 1}",
+                      (long long)i, int(v), (long long)r, (long long)(wd * 16 + c));
+        const int j = c >> 1, h = c & 1;
+        if (v != 0) word |= 1u << (16 * h + j);
+        if (v < 0) word |= 1u << (16 * h + 8 + j);
+      }
+      out[r * (cols / 16) + wd] = word;
+    }
+  }
+  return ok();
+}
+
+bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* bytes) {
+  if (!bytes) return fail(BMOE_ERR_NULL, "bytes is NULL");
+  bmoe_status st = check_layer(layer);
+  if (st != BMOE_OK) return st;
+  if (T < 0 || T > kMaxTokens) return fail(BMOE_ERR_SHAPE, "T=%d must be in [0, %d]", T, kMaxTokens);
+  *bytes = make_plan(layer, T).total;
+  return ok();
+}
+
+bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T, int32_t* topk_idx,
+                       float* topk_gate, int32_t* expert_offsets, int32_t* bucket_slots,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  bmoe_status st = validate_call(layer, x, T, workspace, workspace_bytes, p);
+  if (st != BMOE_OK) return st;
+  if (T == 0) return ok();
+  if (!topk_idx || !topk_gate) return fail(BMOE_ERR_NULL, "topk_idx / topk_gate is NULL");
+  const size_t rb = size_t(p.R) * 4;
+  const Range ri{topk_idx, rb}, rg{topk_gate, rb}, rw{workspace, p.total};
+  const Range ro{expert_offsets, size_t(layer->n_experts + 1) * 4}, rs{bucket_slots, rb};
+  if (overlap(ri, rw) || overlap(rg, rw) || overlap(ri, rg) || overlap(ro, rw) || overlap(rs, rw) ||
+      overlap(ro, ri) || overlap(ro, rg) || overlap(rs, ri) || overlap(rs, rg) || overlap(ro, rs))
+    return fail(BMOE_ERR_ALIAS, "route outputs overlap each other or the workspace");
+  if (!aligned(topk_idx, 16) || !aligned(topk_gate, 4))
+    return fail(BMOE_ERR_ALIGN, "topk_idx must be 16-byte aligned, topk_gate 4-byte aligned");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+  st = run_route(layer, x, T, topk_idx, topk_gate, workspace, p, stream);
+  if (st != BMOE_OK) return st;
+  if (expert_offsets)
+    BMOE_HIP(hipMemcpyAsync(expert_offsets, at<int32_t>(workspace, p.offsets),
+                            size_t(layer->n_experts + 1) * 4, hipMemcpyDeviceToDevice, stream));
+  if (bucket_slots)
+    BMOE_HIP(hipMemcpyAsync(bucket_slots, at<int32_t>(workspace, p.perm), rb, hipMemcpyDeviceToDevice, stream));
+  return ok();
+}
+
+// Kernel launches of one forward, in order (marks[i] follows launch i-1).
+static int forward_kernel_names(const bmoe_layer* L, const char** names) {
+  int n = 0;
+  names[n++] = "prep";
+  names[n++] = "route";
+  names[n++] = "bucket";
+  names[n++] = "bfly_in";
+  if (L->d_ff == 0) {
+    names[n++] = "gemm";
+  } else {
+    names[n++] = "gemm_up";
+    names[n++] = "bfly_mid";
+    names[n++] = "gemm_down";
+  }
+  names[n++] = "bfly_out";
+  if (L->top_k > 1) names[n++] = "combine";
+  return n;
+}
+
+static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+                                int32_t* topk_idx, float* topk_gate, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks,
+                                int32_t n_marks) {
+  Plan p;
+  bmoe_status st = validate_call(layer, x, T, workspace, workspace_bytes, p);
+  if (st != BMOE_OK) return st;
+  if (T == 0) return ok();
+  if (!y) return fail(BMOE_ERR_NULL, "y is NULL");
+  if (!aligned(y, 16)) return fail(BMOE_ERR_ALIGN, "y is not 16-byte aligned");
+  const size_t s = act_size(layer->act_dtype);
+  const Range ry{y, size_t(T) * layer->d_model * s}, rx{x, size_t(T) * layer->d_model * s};
+  const Range rw{workspace, p.total};
+  const size_t rb = size_t(p.R) * 4;
+  const Range ri{topk_idx, rb}, rg{topk_gate, rb};
+  if (overlap(ry, rx)) return fail(BMOE_ERR_ALIAS, "y overlaps x");
+  if (overlap(ry, rw)) return fail(BMOE_ERR_ALIAS, "y overlaps the workspace");
+  if (overlap(ri, ry) || overlap(rg, ry) || overlap(ri, rw) || overlap(rg, rw) || overlap(ri, rg) ||
+      overlap(ri, rx) || overlap(rg, rx))
+    return fail(BMOE_ERR_ALIAS, "topk outputs overlap x, y, each other or the workspace");
+  if ((topk_idx && !aligned(topk_idx, 16)) || (topk_gate && !aligned(topk_gate, 4)))
+    return fail(BMOE_ERR_ALIGN, "topk_idx must be 16-byte aligned, topk_gate 4-byte aligned");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+
+  int launch = 0;
+  auto mark = [&]() -> hipError_t {
+    if (marks && launch < n_marks && marks[launch]) return hipEventRecord(marks[launch], stream);
+    return hipSuccess;
+  };
+  BMOE_HIP(mark());
+#define BMOE_LAUNCH(call) \
+  do {                    \
+    BMOE_HIP(call);       \
+    ++launch;             \
+    BMOE_HIP(mark());     \
+  } while (0)
+
+  const int act = layer->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(workspace, p.idx);
+  float* gate = topk_gate ? topk_gate : at<float>(workspace, p.gate);
+  const int32_t R = int32_t(p.R);
+  const int32_t N = layer->n_experts, k = layer->top_k, d = layer->d_model, f = layer->d_ff;
+  int32_t* counts = at<int32_t>(workspace, p.counts);
+  float* wn2 = at<float>(workspace, p.wnorm2);
+  int32_t* offsets = at<int32_t>(workspace, p.offsets);
+  int32_t* perm = at<int32_t>(workspace, p.perm);
+  void* bufU = at<char>(workspace, p.bufU);
+  void* bufZ = at<char>(workspace, p.bufZ);
+  const int Ld = ilog2(d);
+
+  // router and bucketing
+  BMOE_LAUNCH(launch_prep(layer->w_gate, act, N, d, wn2, counts, stream));
+  RouteArgs ra{x, layer->w_gate, wn2, idx, gate, counts, T, d, N, k, layer->renorm_gates};
+  BMOE_LAUNCH(launch_route(ra, act, stream));
+  BucketArgs ba{idx, counts, offsets, perm, R, N};
+  BMOE_LAUNCH(launch_bucket(ba, stream));
+  // input rotation: U[q] = B(theta_e)^T x_t
+  BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+  BMOE_LAUNCH(launch_butterfly(bi, BFLY_IN, act, Ld, stream));
+  void* yslot = nullptr;  // per-slot outputs (k > 1)
+  const void* zlast = nullptr;
+  const float* phi_last = nullptr;
+  if (f == 0) {
+    GemmArgs g{bufU, layer->w_base[0], bufZ, layer->w_scale[0], R, d, d};
+    BMOE_LAUNCH(launch_gemm(g, act, stream));
+    zlast = bufZ;
+    yslot = bufU;
+    phi_last = layer->phi[0];
+  } else {
+    GemmArgs g0{bufU, layer->w_base[0], bufZ, layer->w_scale[0], R, f, d};
+    BMOE_LAUNCH(launch_gemm(g0, act, stream));
+    BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0,
+                layer->ffn_act == BMOE_ACT_GELU_ERF ? 1 : 0};
+    BMOE_LAUNCH(launch_butterfly(bm, BFLY_MID, act, ilog2(f), stream));
+    GemmArgs g1{bufZ, layer->w_base[1], bufU, layer->w_scale[1], R, d, f};
+    BMOE_LAUNCH(launch_gemm(g1, act, stream));
+    zlast = bufU;
+    yslot = bufZ;
+    phi_last = layer->phi[1];
+  }
+  // output rotation, gate, per-slot rows (or y directly when k == 1)
+  BflyArgs bo{zlast, k == 1 ? y : yslot, phi_last, nullptr, offsets, perm, gate, R, N, k, 0, 0};
+  BMOE_LAUNCH(launch_butterfly(bo, BFLY_OUT, act, Ld, stream));
+  if (k > 1) {
+    CombineArgs c{yslot, y, T, d, k};
+    BMOE_LAUNCH(launch_combine(c, act, stream));
+  }
+#undef BMOE_LAUNCH
+  return ok();
+}
+
+bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+                         int32_t* topk_idx, float* topk_gate, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(layer, x, T, y, topk_idx, topk_gate, workspace, workspace_bytes, stream,
+                      nullptr, 0);
+}
+
+bmoe_status bmoe_dbg_forward_kernels(const bmoe_layer* layer, int32_t* n_kernels, char* names,
+                                     size_t names_len) {
+  bmoe_status st = check_layer(layer);
+  if (st != BMOE_OK) return st;
+  if (!n_kernels) return fail(BMOE_ERR_NULL, "n_kernels is NULL");
+  const char* nm[16];
+  const int n = forward_kernel_names(layer, nm);
+  *n_kernels = n;
+  if (names && names_len) {
+    std::string all;
+    for (int i = 0; i < n; ++i) {
+      if (i) all += ",";
+      all += nm[i];
+    }
+    std::snprintf(names, names_len, "%s", all.c_str());
+  }
+  return ok();
+}
+
+bmoe_status bmoe_dbg_forward_marked(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* marks, int32_t n_marks) {
+  if (n_marks < 0) return fail(BMOE_ERR_SHAPE, "n_marks is negative");
+  return forward_impl(layer, x, T, y, nullptr, nullptr, workspace, workspace_bytes, stream, marks,
+                      n_marks);
+}
+
+bmoe_status bmoe_dbg_butterfly(int32_t log2n, int32_t rows, const float* angles, int32_t transpose,
+                               int32_t dtype, const void* in, void* out, hipStream_t stream) {
+  if (log2n < 3 || log2n > 13) return fail(BMOE_ERR_SHAPE, "log2n=%d must be in [3, 13]", log2n);
+  if (rows < 0) return fail(BMOE_ERR_SHAPE, "rows=%d is negative", rows);
+  if (transpose != 0 && transpose != 1) return fail(BMOE_ERR_SHAPE, "transpose must be 0 or 1");
+  if (dtype != BMOE_F32 && dtype != BMOE_BF16) return fail(BMOE_ERR_DTYPE, "dtype=%d is unknown", dtype);
+  if (rows == 0) return ok();
+  if (!angles || !in || !out) return fail(BMOE_ERR_NULL, "angles / in / out is NULL");
+  if (!aligned(in, 16) || !aligned(out, 16) || !aligned(angles, 4))
+    return fail(BMOE_ERR_ALIGN, "in/out must be 16-byte aligned, angles 4-byte aligned");
+  const size_t bytes = size_t(rows) << log2n;
+  const size_t s = dtype == BMOE_BF16 ? 2 : 4;
+  if (in != out && overlap(Range{in, bytes * s}, Range{out, bytes * s}))
+    return fail(BMOE_ERR_ALIAS, "in and out overlap without being the same buffer");
+  bmoe_status st = check_device();
+  if (st != BMOE_OK) return st;
+  BflyArgs a{in, out, angles, nullptr, nullptr, nullptr, nullptr, rows, 1, 1, transpose, 0};
+  BMOE_HIP(launch_butterfly(a, BFLY_DBG, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, log2n, stream));
+  return ok();
+}
+
+bmoe_status bmoe_dbg_ternary_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype, const void* a,
+                                  const uint32_t* w_packed, float alpha, void* z, hipStream_t stream) {
+  if (dtype != BMOE_F32 && dtype != BMOE_BF16) return fail(BMOE_ERR_DTYPE, "dtype=%d is unknown", dtype);
+  const int q = dtype == BMOE_BF16 ? 64 : 16;
+  if (M < 0 || N < q || K < q || N % q || K % q)
+    return fail(BMOE_ERR_SHAPE, "M=%d N=%d K=%d: N and K must be positive multiples of %d", M, N, K, q);
+  if (M == 0) return ok();
+  if (!a || !w_packed || !z) return fail(BMOE_ERR_NULL, "a / w_packed / z is NULL");
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(z, 16))
+    return fail(BMOE_ERR_ALIGN, "a, w_packed and z must be 16-byte aligned");
+  const size_t s = dtype == BMOE_BF16 ? 2 : 4;
+  if (overlap(Range{a, size_t(M) * K * s}, Range{z, size_t(M) * N * s}))
+    return fail(BMOE_ERR_ALIAS, "z overlaps a");
+  bmoe_status st = check_device();
+  if (st != BMOE_OK) return st;
+  GemmArgs g{a, w_packed, z, alpha, M, N, K};
+  BMOE_HIP(launch_gemm(g, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
+  return ok();
+}
+
+const char* bmoe_status_string(bmoe_status s) {
+  switch (s) {
+    case BMOE_OK: return "BMOE_OK";
+    case BMOE_ERR_NULL: return "BMOE_ERR_NULL: a required pointer is NULL";
+    case BMOE_ERR_SHAPE: return "BMOE_ERR_SHAPE: a size is outside the supported limits";
+    case BMOE_ERR_DTYPE: return "BMOE_ERR_DTYPE: unknown dtype or activation";
+    case BMOE_ERR_ALIGN: return "BMOE_ERR_ALIGN: a pointer is misaligned";
+    case BMOE_ERR_ALIAS: return "BMOE_ERR_ALIAS: an output overlaps an input or the workspace";
+    case BMOE_ERR_WORKSPACE: return "BMOE_ERR_WORKSPACE: workspace too small";
+    case BMOE_ERR_TERNARY: return "BMOE_ERR_TERNARY: a substrate value is not in {-1, 0, 1}";
+    case BMOE_ERR_HIP: return "BMOE_ERR_HIP: a HIP call or kernel launch failed";
+    case BMOE_ERR_DEVICE: return "BMOE_ERR_DEVICE: the current device is not gfx950";
+  }
+  return "unknown bmoe_status";
+}
+
+const char* bmoe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

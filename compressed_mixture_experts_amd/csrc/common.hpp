@@ -1,0 +1,150 @@
+// Shared device helpers and launcher declarations of the ButterflyMoE HIP
+// library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bmoe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+enum Act { ACT_F32 = 0, ACT_BF16 = 1 };
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round two floats to bf16 (nearest-even; one v_cvt_pk_bf16_f32) and pack.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v.x = (__bf16)a;
+  v.y = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Load 8 consecutive activations starting at element `i` of `p` as floats.
+template <int ACT>
+__device__ __forceinline__ void load8(const void* p, size_t i, float v[8]) {
+  if constexpr (ACT == ACT_BF16) {
+    uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    v[0] = bf16lo(u.x); v[1] = bf16hi(u.x);
+    v[2] = bf16lo(u.y); v[3] = bf16hi(u.y);
+    v[4] = bf16lo(u.z); v[5] = bf16hi(u.z);
+    v[6] = bf16lo(u.w); v[7] = bf16hi(u.w);
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// Store 8 consecutive activations (rounded to the activation dtype).
+template <int ACT>
+__device__ __forceinline__ void store8(void* p, size_t i, const float v[8]) {
+  if constexpr (ACT == ACT_BF16) {
+    uint4 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p) + i) = u;
+  } else {
+    float4* q = reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i);
+    q[0] = make_float4(v[0], v[1], v[2], v[3]);
+    q[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <int ACT>
+__device__ __forceinline__ float load1(const void* p, size_t i) {
+  if constexpr (ACT == ACT_BF16) {
+    return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+// ---------------------------------------------------------------- ternary code
+// Substrate word layout (one 32-bit word per 16 consecutive columns): column
+// 2j+h has its nonzero bit at 16h+j and its sign bit at 16h+8+j.  The pair of
+// columns (2j, 2j+1) becomes two bf16 values (+1 = 0x3F80, -1 = 0xBF80) in one
+// 32-bit word with a shift, two masks and a 24-bit multiply.
+__device__ __forceinline__ uint32_t ternary_pair_bf16(uint32_t w, int j) {
+  const uint32_t sign = (w << (7 - j)) & 0x80008000u;
+  const uint32_t mag = __umul24((w >> j) & 0x00010001u, 0x3F80u);
+  return sign | mag;
+}
+
+__device__ __forceinline__ float ternary_value(uint32_t w, int c) {
+  const int j = c >> 1, h = c & 1;
+  const uint32_t nz = (w >> (16 * h + j)) & 1u;
+  const uint32_t sg = (w >> (16 * h + 8 + j)) & 1u;
+  return nz ? (sg ? -1.0f : 1.0f) : 0.0f;
+}
+
+// ---------------------------------------------------------------- launchers
+struct RouteArgs {
+  const void* x;            // [T][d]
+  const void* w_gate;       // [N][d]
+  const float* wnorm2;      // [N] squared row norms of w_gate (fp32)
+  int32_t* topk_idx;        // [T][k]
+  float* topk_gate;         // [T][k]
+  int32_t* counts;          // [N], zeroed before, incremented per routed slot
+  int32_t T, d, N, k, renorm;
+};
+
+struct BucketArgs {
+  const int32_t* topk_idx;  // [R] flat slots
+  const int32_t* counts;    // [N]
+  int32_t* offsets;         // [N+1]
+  int32_t* perm;            // [R] bucket position -> flat slot
+  int32_t R, N;
+};
+
+enum BflyMode { BFLY_DBG = 0, BFLY_IN = 1, BFLY_MID = 2, BFLY_OUT = 3 };
+
+struct BflyArgs {
+  const void* in;           // source rows
+  void* out;                // destination rows
+  const float* ang0;        // first rotation's angles  [N][L0][n/2]
+  const float* ang1;        // second rotation's angles (MID only)
+  const int32_t* offsets;   // [N+1] bucket offsets (bucketed modes)
+  const int32_t* perm;      // [R] bucket position -> flat slot
+  const float* gate;        // [R] gate per flat slot (OUT)
+  int32_t rows;             // R (number of rows)
+  int32_t n_experts;
+  int32_t top_k;            // IN: token = slot / top_k;  OUT: token when k == 1
+  int32_t transpose;        // DBG only
+  int32_t gelu;             // MID: apply GELU between the two rotations
+};
+
+struct GemmArgs {
+  const void* a;            // [M][K]
+  const uint32_t* w;        // [N][K/16]
+  void* z;                  // [M][N]
+  float alpha;
+  int32_t M, N, K;
+};
+
+struct CombineArgs {
+  const void* yp;           // [T*k][d] per-slot gated outputs
+  void* y;                  // [T][d]
+  int32_t T, d, k;
+};
+
+hipError_t launch_prep(const void* w_gate, int act, int32_t N, int32_t d, float* wnorm2,
+                       int32_t* counts, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s);
+hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
+hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
+
+// Rows per butterfly tile for width 2^log2n (shared by launcher and planner).
+int bfly_rows_per_tile(int log2n);
+
+}  // namespace bmoe

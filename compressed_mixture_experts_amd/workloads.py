@@ -150,8 +150,8 @@ def generate(cfg: LayerConfig, *, angle_mode: str = "uniform", x_mode: str = "no
     x_mode:    "normal"  x ~ N(0, 1)
                "integer" x uniform integers in [-8, 8] (exact in bf16)
     gate_mode: "normal"  w_gate ~ N(0, 1/d_model)
-               "skewed"  normal plus a per-expert bias direction that makes a few
-                         experts far more popular (Zipf-like load)
+               "skewed"  row e scaled by 4/(e+1)^0.75: a few experts take most of
+                         the load, many get few or no tokens
     angle_mode: "uniform" U[-pi, pi); or the closed-form cases "zero", "pi",
                "half_pi", "quarter_pi", "small".
     """
@@ -174,9 +174,10 @@ def generate(cfg: LayerConfig, *, angle_mode: str = "uniform", x_mode: str = "no
 
     g64 = r_g.standard_normal((N, d)) / math.sqrt(d)
     if gate_mode == "skewed":
-        # popularity bias: expert e gets a shared direction with weight ~ 1/(e+1)
-        direction = r_g.standard_normal(d) / math.sqrt(d)
-        g64 = g64 + (2.0 / (np.arange(N)[:, None] + 1.0)) * direction[None, :]
+        # popularity skew: wider logits win the top-k more often, so scaling
+        # expert e's gate row by 4 / (e+1)^0.75 gives the low experts most of
+        # the load and leaves high ones with few or no tokens
+        g64 = g64 * (4.0 / (np.arange(N)[:, None] + 1.0) ** 0.75)
     elif gate_mode != "normal":
         raise ValueError(gate_mode)
 

@@ -1,0 +1,159 @@
+/*
+ * bmoe.h - ButterflyMoE expert-layer forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (ButterflyMoE: Sub-Linear Ternary Experts via Structured Butterfly
+ * Orbits; gist.science/zh/paper/2601.13563, technical summary §2.1 and §2.2):
+ *   - N experts share one ternary substrate W_base with entries in {-1, 0, +1};
+ *   - expert e is W_e = B(phi_e) * W_base * B(theta_e)^T, where each B is an
+ *     orthogonal butterfly of log2(n) stages of Givens rotations, (n/2) angles
+ *     per stage, n the width it acts on;
+ *   - experts are never materialised: a routed token is rotated by
+ *     B(theta_e)^T, multiplied by the ternary substrate, rotated by B(phi_e);
+ *   - a standard top-k gating network picks the experts of each token
+ *     (gist.science/nl/paper/2601.13563, §2 "Drie Fasen van de Methode").
+ * The FFN form (ButterflyViT, gist.science/pt/paper/2603.06746, §2) has an up
+ * substrate (d_ff x d_model) and a down substrate (d_model x d_ff), each with
+ * its own pair of rotations, and an exact-erf GELU between them.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   Butterfly B(a) of width n = 2^L, angles a[L][n/2] (fp32, row-major):
+ *     stage s rotates the pair (i, j = i + 2^s), bit s of i clear, by the angle
+ *     a[s][p], p = i with bit s deleted:  v_i' = c v_i - s v_j,
+ *     v_j' = s v_i + c v_j  (c = cos a, s = sin a);  B = S_{L-1} ... S_1 S_0.
+ *   Router: logits l = W_g x (W_g row-major [n_experts][d_model], no bias);
+ *     top-k by logit, larger first, equal logits to the lower expert index;
+ *     gate = softmax(l) of the chosen expert over all N logits, divided by the
+ *     sum of the k gates when renorm_gates is 1.
+ *   Combine: y_t = sum_j gate_{t,j} * E_{e_{t,j}}(x_t); no capacity limit.
+ *   Ternary storage: bmoe_pack_ternary's 2-bit format (see below).
+ *
+ * Memory and streams.  Every pointer argument of bmoe_route and bmoe_forward
+ * is device memory owned by the caller; all arrays are row-major and dense.
+ * x, y, w_gate, the workspace and the packed substrates must be 16-byte
+ * aligned; angle arrays 4-byte aligned.  The library allocates and frees
+ * nothing, never synchronises the device, and enqueues all work on the given
+ * stream (0 = default stream).  Inputs must stay valid until the stream has
+ * passed the call.  Calls on different streams must use different workspaces
+ * and outputs.
+ *
+ * Errors.  Argument errors are detected on the host before anything is
+ * enqueued (no partial launch); bmoe_last_error() then holds a description.
+ * BMOE_ERR_HIP reports a failed HIP call or kernel launch.  bmoe_last_error()
+ * is per host thread.
+ *
+ * Limits.  d_model and d_ff (when nonzero) are powers of two in [64, 8192];
+ * 1 <= n_experts <= 256; 1 <= top_k <= min(8, n_experts); 0 <= T.
+ */
+#ifndef BMOE_H
+#define BMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bmoe_status {
+  BMOE_OK = 0,
+  BMOE_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  BMOE_ERR_SHAPE = 2,       /* a size is outside the limits above              */
+  BMOE_ERR_DTYPE = 3,       /* unknown dtype / activation code                 */
+  BMOE_ERR_ALIGN = 4,       /* a pointer is not aligned as required            */
+  BMOE_ERR_ALIAS = 5,       /* an output overlaps an input or the workspace    */
+  BMOE_ERR_WORKSPACE = 6,   /* workspace smaller than bmoe_workspace_size()    */
+  BMOE_ERR_TERNARY = 7,     /* a substrate value is not in {-1, 0, +1}         */
+  BMOE_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed      */
+  BMOE_ERR_DEVICE = 9       /* the current device is not a gfx950 GPU          */
+} bmoe_status;
+
+typedef enum bmoe_dtype {
+  BMOE_F32 = 0,             /* IEEE binary32                                   */
+  BMOE_BF16 = 1             /* bfloat16 (upper half of binary32)               */
+} bmoe_dtype;
+
+typedef enum bmoe_act {
+  BMOE_ACT_NONE = 0,
+  BMOE_ACT_GELU_ERF = 1     /* h * (1 + erf(h / sqrt 2)) / 2                   */
+} bmoe_act;
+
+/* One ButterflyMoE layer.  Substrate m (m = 0, or m = 0 and 1 for the FFN
+ * form) has shape d_out(m) x d_in(m):
+ *   square layer (d_ff == 0): m=0 is d_model x d_model;
+ *   FFN layer    (d_ff  > 0): m=0 (up) is d_ff x d_model, m=1 (down) is
+ *                             d_model x d_ff.
+ * All pointers are device memory. */
+typedef struct bmoe_layer {
+  int32_t d_model;          /* width of x and y                                 */
+  int32_t d_ff;             /* 0: square experts; else FFN hidden width         */
+  int32_t n_experts;        /* N                                                */
+  int32_t top_k;            /* k                                                */
+  int32_t act_dtype;        /* bmoe_dtype of x, y and w_gate                    */
+  int32_t ffn_act;          /* bmoe_act between the FFN substrates (FFN only)   */
+  int32_t renorm_gates;     /* 0: gate = softmax probability; 1: renormalised   */
+  int32_t reserved;         /* must be 0                                        */
+  const void* w_gate;       /* [n_experts][d_model], act_dtype                  */
+  const uint32_t* w_base[2];/* packed substrate m: [d_out][d_in/16] words       */
+  const float* theta[2];    /* input-side angles of substrate m:
+                               [n_experts][log2 d_in][d_in/2]                   */
+  const float* phi[2];      /* output-side angles of substrate m:
+                               [n_experts][log2 d_out][d_out/2]                 */
+  float w_scale[2];         /* scalar multiplying substrate m (normally 1.0)    */
+} bmoe_layer;
+
+/* Number of 32-bit words bmoe_pack_ternary writes for a rows x cols matrix
+ * (rows * cols / 16), or 0 when cols is not a positive multiple of 16. */
+size_t bmoe_packed_words(int32_t rows, int32_t cols);
+
+/* Pack a ternary matrix (HOST memory, int8 row-major [rows][cols], values in
+ * {-1, 0, +1}) into the 2-bit substrate format, synchronously on the host.
+ * Word w of row r holds columns 16w .. 16w+15.  For a column c = 16w + 2j + h
+ * (j = 0..7, h = 0 or 1) the word holds a nonzero bit at position 16h + j and
+ * a sign bit (1 = negative) at position 16h + 8 + j; a zero entry has both
+ * bits clear.  Errors: BMOE_ERR_NULL, BMOE_ERR_SHAPE (cols not a multiple of
+ * 16, rows < 1, out_words too small), BMOE_ERR_TERNARY (first bad index in
+ * bmoe_last_error()).  ButterflyMoE zh §2.2: substrate values are ternary. */
+bmoe_status bmoe_pack_ternary(const int8_t* w, int32_t rows, int32_t cols,
+                              uint32_t* out, size_t out_words);
+
+/* Bytes of device workspace bmoe_route / bmoe_forward need for T tokens.
+ * Depends only on the layer's sizes and T. */
+bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* bytes);
+
+/* Router and per-expert bucketing only.
+ *   x              [T][d_model] act_dtype
+ *   topk_idx       [T][top_k] int32 out: chosen experts, larger logit first
+ *   topk_gate      [T][top_k] fp32  out: their gates
+ *   expert_offsets [n_experts+1] int32 out (may be NULL): rows of expert e are
+ *                  bucket positions offsets[e] .. offsets[e+1]-1
+ *   bucket_slots   [T*top_k] int32 out (may be NULL): bucket position q holds
+ *                  the flat slot t*top_k + j; within an expert, slots ascend
+ * Expert indices equal those of an exact-arithmetic top-k: logits are computed
+ * in fp32 and every token whose decisive gaps fall within the fp32 error bound
+ * is recomputed in fp64. */
+bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T,
+                       int32_t* topk_idx, float* topk_gate,
+                       int32_t* expert_offsets, int32_t* bucket_slots,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Full layer forward: y[t] = sum_j gate_{t,j} * E_{e_{t,j}}(x_t).
+ *   x  [T][d_model] act_dtype;  y [T][d_model] act_dtype (must not overlap x,
+ *   the workspace or the optional outputs);
+ *   topk_idx / topk_gate: optional [T][top_k] outputs as in bmoe_route.
+ * Intermediates between the steps are kept in act_dtype; rotations, GELU and
+ * accumulation run in fp32. */
+bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+                         int32_t* topk_idx, float* topk_gate,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* bmoe_status_string(bmoe_status status);
+
+/* Detail of the last error on this host thread ("" if none). */
+const char* bmoe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BMOE_H */

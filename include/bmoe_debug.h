@@ -1,0 +1,53 @@
+/*
+ * bmoe_debug.h - single steps of the ButterflyMoE forward path, exported so
+ * that each kernel can be checked on its own against a reference.  They run
+ * the same kernels bmoe_forward runs, on caller-given device buffers, enqueued
+ * on `stream`, with the same validation rules and error codes as bmoe.h.
+ */
+#ifndef BMOE_DEBUG_H
+#define BMOE_DEBUG_H
+
+#include "bmoe.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Apply one butterfly to every row: out[r] = B(angles) in[r], or
+ * B(angles)^T in[r] when transpose is 1 (ButterflyMoE zh §2.2: hierarchical
+ * Givens rotations; wiring as documented in bmoe.h).
+ *   log2n in [1, 13]; rows >= 0; angles [log2n][2^log2n / 2] fp32 (device);
+ *   in, out [rows][2^log2n] of dtype (bmoe_dtype), 16-byte aligned, may be
+ *   the same buffer.  Rotations run in fp32. */
+bmoe_status bmoe_dbg_butterfly(int32_t log2n, int32_t rows, const float* angles,
+                               int32_t transpose, int32_t dtype,
+                               const void* in, void* out, hipStream_t stream);
+
+/* Ternary substrate product z = alpha * a * W^T (ButterflyMoE zh §2.2:
+ * ternary substrate).
+ *   a [M][K] of dtype; w_packed [N][K/16] words (bmoe_pack_ternary format);
+ *   z [M][N] of dtype; fp32 accumulation.  K and N are multiples of 64
+ *   (bf16) or 16 (fp32); M >= 0. */
+bmoe_status bmoe_dbg_ternary_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype,
+                                  const void* a, const uint32_t* w_packed, float alpha,
+                                  void* z, hipStream_t stream);
+
+/* Names of the kernel launches one bmoe_forward makes for this layer, in
+ * launch order, comma-separated into `names` (truncated to names_len), and
+ * their number in *n_kernels. */
+bmoe_status bmoe_dbg_forward_kernels(const bmoe_layer* layer, int32_t* n_kernels, char* names,
+                                     size_t names_len);
+
+/* bmoe_forward (without the optional routing outputs) that also records
+ * marks[0] on `stream` before its first kernel launch and marks[i] after its
+ * i-th launch (i = 1 .. n_kernels); NULL entries and entries at or beyond
+ * n_marks are skipped.  The events are created and owned by the caller; the
+ * call never synchronises.  Used to time single kernels of a live forward. */
+bmoe_status bmoe_dbg_forward_marked(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* marks, int32_t n_marks);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BMOE_DEBUG_H */

@@ -49,7 +49,7 @@ from scipy.special import erf as _erf
 __all__ = [
     "stored_to_f64", "pair_index", "stage_matrix", "butterfly_dense",
     "butterfly_apply", "expert_matrix", "expert_apply", "gelu", "route",
-    "forward", "forward_tokens", "param_counts",
+    "forward", "forward_tokens", "param_counts", "ternary_product",
 ]
 
 
@@ -223,7 +223,8 @@ def forward(inp, routing: Optional[Routing] = None, idx_override: Optional[np.nd
     """Full layer forward by materialising every used expert (the definition).
 
     y_t = sum_j g_{t,j} W_{e_j} x_t for square experts, and
-    y_t = sum_j g_{t,j} W_dn,e GELU(W_up,e x_t) for FFN experts, where each
+    y_t = sum_j g_{t,j} W_dn,e GELU(W_up,e x_t) for FFN experts (GELU replaced
+    by the identity when the layer's FFN activation is "none"), where each
     W_e = B(phi_e) W_base B(theta_e)^T ([MoE-zh] §2.1, [ViT-pt] §2).
     ``idx_override`` evaluates the layer at given expert choices (gates are then
     the softmax probabilities of those experts).
@@ -246,7 +247,8 @@ def forward(inp, routing: Optional[Routing] = None, idx_override: Optional[np.nd
         if cfg.is_ffn:
             Wup = expert_matrix(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], cfg.w_scale)
             Wdn = expert_matrix(inp.theta[1][e], inp.phi[1][e], inp.w_base[1], cfg.w_scale)
-            Ye = gelu(Xe @ Wup.T) @ Wdn.T
+            H = Xe @ Wup.T
+            Ye = (gelu(H) if cfg.ffn_act == "gelu" else H) @ Wdn.T
         else:
             We = expert_matrix(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], cfg.w_scale)
             Ye = Xe @ We.T
@@ -284,7 +286,8 @@ def forward_tokens(inp, tokens: Sequence[int], routing: Optional[Routing] = None
             v = x[t][:, None]
             if cfg.is_ffn:
                 h = expert_apply(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], v, cfg.w_scale)
-                z = expert_apply(inp.theta[1][e], inp.phi[1][e], inp.w_base[1], gelu(h), cfg.w_scale)
+                a = gelu(h) if cfg.ffn_act == "gelu" else h
+                z = expert_apply(inp.theta[1][e], inp.phi[1][e], inp.w_base[1], a, cfg.w_scale)
             else:
                 z = expert_apply(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], v, cfg.w_scale)
             y[t] += gates[t, j] * z[:, 0]
@@ -312,3 +315,10 @@ def param_counts(d_model: int, n_experts: int, d_ff: int = 0, angle_bytes: int =
         "ternary_entropy_bits": math.log2(3.0),
         "dense_expert_bytes_total": n_experts * substrate_weights * dense_bytes,
     }
+
+
+def ternary_product(U: np.ndarray, w_base: np.ndarray, alpha: float = 1.0) -> np.ndarray:
+    """Z = alpha * U @ W_base^T in fp64: the shared-substrate product every
+    routed row goes through ([MoE-zh] §2.1: rotated input times the ternary
+    substrate).  U [M][d_in], W_base [d_out][d_in]."""
+    return alpha * (np.asarray(U, dtype=np.float64) @ np.asarray(w_base, dtype=np.float64).T)

@@ -1,0 +1,48 @@
+"""Shared helpers of the GPU parity tests (upload, download, error metrics)."""
+import sys
+
+import numpy as np
+
+import compressed_mixture_experts_amd as bm
+from compressed_mixture_experts_amd import workloads as wl
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, act):
+    import torch
+    if act == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def to_f64(t):
+    """Exact float64 value of a device tensor (bf16 or fp32)."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.float().numpy().astype(np.float64)
+    return t.numpy().astype(np.float64)
+
+
+def row_rel_err(y, ref):
+    """Per-row relative L2 error ||y - ref|| / ||ref||."""
+    num = np.linalg.norm(y - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    return num / den
+
+
+def tol_for(act):
+    return 1e-4 if act == "f32" else 2e-2
+
+
+def run_layer(inp, return_routing=True):
+    import torch
+    layer = bm.Layer.from_inputs(inp, device="cuda")
+    x = to_dev(inp.x, inp.cfg.act)
+    out = layer.forward(x, return_routing=return_routing)
+    torch.cuda.synchronize()
+    return layer, x, out

@@ -1,0 +1,204 @@
+"""C-ABI checks that need no GPU: exports, the 2-bit packing format, and every
+argument error (all detected on the host before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_mixture_experts_amd as bm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(bmoe_\w+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    L = bm.lib()
+    declared = header_functions()
+    assert declared == set(bm.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def decode_packed(words: np.ndarray, cols: int) -> np.ndarray:
+    """Independent decoder of the documented word layout (bmoe.h)."""
+    rows = words.shape[0]
+    out = np.zeros((rows, cols), dtype=np.int8)
+    for r in range(rows):
+        for c in range(cols):
+            w = int(words[r, c // 16])
+            cc = c % 16
+            j, h = cc >> 1, cc & 1
+            nz = (w >> (16 * h + j)) & 1
+            sg = (w >> (16 * h + 8 + j)) & 1
+            assert not (sg and not nz), "negative zero code"
+            out[r, c] = (-1 if sg else 1) if nz else 0
+    return out
+
+
+def test_pack_roundtrip_and_format():
+    r = np.random.default_rng(0)
+    w = r.integers(-1, 2, size=(7, 48)).astype(np.int8)
+    p = bm.pack_ternary(w)
+    assert p.shape == (7, 3) and p.dtype == np.uint32
+    assert np.array_equal(decode_packed(p, 48), w)
+    # single entries land on the documented bits
+    one = np.zeros((1, 16), np.int8)
+    one[0, 5] = -1  # column 5 = 2*2 + 1 -> nonzero bit 16+2, sign bit 16+8+2
+    assert int(bm.pack_ternary(one)[0, 0]) == (1 << 18) | (1 << 26)
+    one[0, 5] = 0
+    one[0, 14] = 1  # column 14 = 2*7 + 0 -> nonzero bit 7
+    assert int(bm.pack_ternary(one)[0, 0]) == 1 << 7
+
+
+def test_pack_errors():
+    with pytest.raises(bm.BmoeError) as e:
+        bm.pack_ternary(np.full((2, 16), 2, np.int8))
+    assert e.value.name == "BMOE_ERR_TERNARY" and "w[0]" in str(e.value)
+    w = np.zeros((3, 32), np.int8)
+    w[2, 17] = -2
+    with pytest.raises(bm.BmoeError) as e:
+        bm.pack_ternary(w)
+    assert "w[81]" in str(e.value)
+    with pytest.raises(bm.BmoeError) as e:
+        bm.pack_ternary(np.zeros((2, 24), np.int8))
+    assert e.value.name == "BMOE_ERR_SHAPE"
+    assert bm.packed_words(4, 24) == 0 and bm.packed_words(4, 32) == 8
+    L = bm.lib()
+    assert L.bmoe_pack_ternary(None, 1, 16, None, 1) == 1
+    buf = np.zeros(1, np.uint32)
+    w = np.zeros((2, 16), np.int8)
+    assert L.bmoe_pack_ternary(w.ctypes.data, 2, 16, buf.ctypes.data, 1) == 2  # out too small
+
+
+FAKE = 0x7F0000000000  # never dereferenced: validation fails before any device call
+
+
+def make_struct(**kw):
+    s = bm.LayerStruct()
+    s.d_model, s.d_ff, s.n_experts, s.top_k = 512, 0, 64, 2
+    s.act_dtype, s.ffn_act, s.renorm_gates, s.reserved = bm.BF16, bm.ACT_NONE, 0, 0
+    s.w_gate = FAKE
+    s.w_base[0], s.theta[0], s.phi[0] = FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    s.w_base[1], s.theta[1], s.phi[1] = FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000
+    s.w_scale[0] = s.w_scale[1] = 1.0
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def ws_size(s, T):
+    n = ctypes.c_size_t(0)
+    st = bm.lib().bmoe_workspace_size(ctypes.byref(s), T, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_model", 500, 2), ("d_model", 32, 2), ("d_model", 16384, 2), ("d_ff", 100, 2),
+    ("n_experts", 0, 2), ("n_experts", 257, 2), ("top_k", 0, 2), ("top_k", 9, 2),
+    ("act_dtype", 2, 3), ("ffn_act", 1, 3), ("renorm_gates", 2, 2), ("reserved", 1, 2),
+    ("w_gate", None, 1), ("w_gate", FAKE + 8, 4),
+])
+def test_layer_validation(field, value, status):
+    s = make_struct(**{field: value})
+    assert ws_size(s, 16)[0] == status
+    assert bm.lib().bmoe_last_error() != b""
+
+
+def test_topk_limited_by_experts_and_ffn_pointers():
+    assert ws_size(make_struct(n_experts=3, top_k=4), 8)[0] == 2
+    s = make_struct(d_ff=2048, ffn_act=bm.ACT_GELU_ERF)
+    s.phi[1] = None
+    assert ws_size(s, 8)[0] == 1
+    s = make_struct(d_ff=2048, ffn_act=bm.ACT_GELU_ERF)
+    s.theta[1] = FAKE + 2  # misaligned angles
+    assert ws_size(s, 8)[0] == 4
+    s = make_struct()
+    s.w_base[0] = FAKE + 4
+    assert ws_size(s, 8)[0] == 4
+    assert bm.lib().bmoe_workspace_size(None, 8, ctypes.byref(ctypes.c_size_t())) == 1
+
+
+def test_workspace_size_monotone_and_layout():
+    s = make_struct()
+    prev = -1
+    for T in (0, 1, 7, 64, 4096, 16384):
+        st, n = ws_size(s, T)
+        assert st == 0 and n > prev
+        prev = n
+    # dominated by two [T*k][d] bf16 row buffers
+    st, n = ws_size(s, 4096)
+    assert n >= 2 * 4096 * 2 * 512 * 2
+    sf = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
+    st, nf = ws_size(sf, 8192)
+    assert st == 0 and nf >= 8192 * 2 * (1024 + 4096) * 2
+    assert ws_size(s, -1)[0] == 2
+
+
+def call_forward(s, x=FAKE + 0x800000, T=16, y=FAKE + 0x900000, idx=None, gate=None,
+                 ws=FAKE + 0x1000000, nbytes=None):
+    if nbytes is None:
+        nbytes = ws_size(s, T)[1]
+    return bm.lib().bmoe_forward(ctypes.byref(s), x, T, y, idx, gate, ws, nbytes, None)
+
+
+def test_forward_argument_errors():
+    s = make_struct()
+    assert call_forward(s, x=None) == 1
+    assert call_forward(s, y=None) == 1
+    assert call_forward(s, ws=None) == 1
+    assert call_forward(s, x=FAKE + 0x800008) == 4
+    assert call_forward(s, y=FAKE + 0x900004) == 4
+    assert call_forward(s, ws=FAKE + 0x1000010) == 4
+    need = ws_size(s, 16)[1]
+    assert call_forward(s, nbytes=need - 1) == 6
+    # y overlapping x, y overlapping the workspace, x overlapping the workspace
+    assert call_forward(s, y=FAKE + 0x800000 + 256) == 5
+    assert call_forward(s, y=FAKE + 0x1000000 + 512) == 5
+    assert call_forward(s, x=FAKE + 0x1000000 + 1024) == 5
+    assert call_forward(s, idx=FAKE + 0x900000) == 5          # topk output on y
+    assert call_forward(s, idx=FAKE + 0x2000004) == 4         # misaligned idx
+    assert call_forward(s, T=-3) == 2
+    assert call_forward(s, T=0, x=None, y=None, ws=None) == 0  # empty batch: no-op
+    assert b"overlap" not in bm.lib().bmoe_last_error()
+
+
+def test_route_argument_errors():
+    s = make_struct()
+    L = bm.lib()
+    n = ws_size(s, 16)[1]
+    ws = FAKE + 0x1000000
+    assert L.bmoe_route(ctypes.byref(s), FAKE, 16, None, FAKE + 0x200000000, None, None, ws, n, None) == 1
+    assert L.bmoe_route(ctypes.byref(s), FAKE, 16, ws + 256, FAKE + 0x200000000, None, None, ws, n, None) == 5
+    assert L.bmoe_route(ctypes.byref(s), FAKE, 16, FAKE + 0x200000000, FAKE + 0x200000000, None, None, ws, n, None) == 5
+
+
+def test_debug_hook_argument_errors():
+    L = bm.lib()
+    assert L.bmoe_dbg_butterfly(2, 4, FAKE, 0, 0, FAKE, FAKE, None) == 2
+    assert L.bmoe_dbg_butterfly(14, 4, FAKE, 0, 0, FAKE, FAKE, None) == 2
+    assert L.bmoe_dbg_butterfly(8, 4, FAKE, 3, 0, FAKE, FAKE, None) == 2
+    assert L.bmoe_dbg_butterfly(8, 4, FAKE, 0, 5, FAKE, FAKE, None) == 3
+    assert L.bmoe_dbg_butterfly(8, 4, None, 0, 0, FAKE, FAKE, None) == 1
+    assert L.bmoe_dbg_butterfly(8, 4, FAKE, 0, 0, FAKE + 4, FAKE + 0x100000, None) == 4
+    assert L.bmoe_dbg_butterfly(8, 4, FAKE, 0, 0, FAKE, FAKE + 64, None) == 5
+    assert L.bmoe_dbg_butterfly(8, 0, None, 0, 0, None, None, None) == 0
+    assert L.bmoe_dbg_ternary_gemm(8, 96, 64, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE + 0x100000, None) == 2
+    assert L.bmoe_dbg_ternary_gemm(8, 64, 64, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE + 16, None) == 5
+    assert L.bmoe_dbg_ternary_gemm(8, 64, 64, 7, FAKE, FAKE, ctypes.c_float(1.0), FAKE + 0x100000, None) == 3
+
+
+def test_status_strings():
+    L = bm.lib()
+    for code, name in bm.STATUS.items():
+        assert L.bmoe_status_string(code).decode().startswith(name)

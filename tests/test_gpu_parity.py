@@ -1,0 +1,276 @@
+"""GPU parity: every step of the HIP path against the fp64 oracle.
+
+Per-kernel checks go through the debug hooks of include/bmoe_debug.h; routing
+and the whole layer through bmoe_route / bmoe_forward.  Bars:
+  * expert indices and bucket layout: bit-exact (tokens the oracle flags as
+    within fp64 rounding of a tie may take either choice);
+  * layer output: per-token relative L2 error <= 1e-4 (fp32 activations) and
+    <= 2e-2 (bf16 activations);
+  * integer-valued substrate products: bit-exact after the output rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import compressed_mixture_experts_amd as bm
+from compressed_mixture_experts_amd import workloads as wl
+from oracle import ref
+from gpu_helpers import log, row_rel_err, run_layer, to_dev, to_f64, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bm.lib()
+    yield
+
+
+# ------------------------------------------------------------------ butterfly
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("log2n,rows", [(3, 5), (6, 37), (9, 100), (10, 33), (11, 9), (13, 7)])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_butterfly_kernel(act, log2n, rows, transpose):
+    import torch
+    n = 1 << log2n
+    r = np.random.default_rng(1000 + log2n)
+    ang = r.uniform(-math.pi, math.pi, size=(log2n, n // 2)).astype(np.float32)
+    x64 = r.standard_normal((rows, n))
+    xs = wl.round_to_bf16_bits(x64) if act == "bf16" else x64.astype(np.float32)
+    log(f"butterfly act={act} n={n} rows={rows} transpose={transpose}")
+    out = bm.dbg_butterfly(torch.from_numpy(ang).cuda(), to_dev(xs, act), transpose=transpose)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    want = ref.butterfly_apply(ang, ref.stored_to_f64(xs, act).T, transpose=transpose).T
+    err = row_rel_err(got, want).max()
+    # fp32: a few ulp per stage plus the sin/cos unit; bf16: one output rounding
+    assert err <= (2e-5 if act == "f32" else 4e-3), err
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_butterfly_zero_angles_is_identity_and_inplace(act):
+    import torch
+    n, rows = 512, 40
+    x = wl.round_to_bf16_bits(np.random.default_rng(3).standard_normal((rows, n))) if act == "bf16" \
+        else np.random.default_rng(3).standard_normal((rows, n)).astype(np.float32)
+    xd = to_dev(x, act)
+    x0 = xd.clone()
+    ang = torch.zeros((9, n // 2), dtype=torch.float32, device="cuda")
+    log(f"butterfly identity act={act}")
+    bm.dbg_butterfly(ang, xd, transpose=False, out=xd)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(xd, x0)
+
+
+# ------------------------------------------------------------------ substrate product
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (37, 128, 512), (300, 192, 256), (515, 512, 2048), (130, 4096, 1024)])
+def test_ternary_gemm_integer_exact(act, M, N, K):
+    import torch
+    r = np.random.default_rng(M + N + K)
+    w = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    a = r.integers(-8, 9, size=(M, K)).astype(np.float64)
+    a_st = wl.round_to_bf16_bits(a) if act == "bf16" else a.astype(np.float32)
+    wp = torch.from_numpy(bm.pack_ternary(w).view(np.int32)).cuda()
+    log(f"gemm exact act={act} M={M} N={N} K={K}")
+    z = bm.dbg_ternary_gemm(to_dev(a_st, act), wp, N, 1.0)
+    torch.cuda.synchronize()
+    exact = ref.ternary_product(a, w)           # integers, |.| <= 8 K < 2^24
+    want = wl.round_to_bf16_bits(exact) if act == "bf16" else exact.astype(np.float32)
+    got = z.cpu().view(torch.int16).numpy().view(np.uint16) if act == "bf16" else z.cpu().numpy()
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_ternary_gemm_random_bound(act):
+    import torch
+    M, N, K = 333, 256, 1024
+    r = np.random.default_rng(9)
+    w = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    a64 = r.standard_normal((M, K))
+    a_st = wl.round_to_bf16_bits(a64) if act == "bf16" else a64.astype(np.float32)
+    a = ref.stored_to_f64(a_st, act)
+    wp = torch.from_numpy(bm.pack_ternary(w).view(np.int32)).cuda()
+    log(f"gemm bound act={act}")
+    z = to_f64(bm.dbg_ternary_gemm(to_dev(a_st, act), wp, N, 0.75))
+    torch.cuda.synchronize()
+    exact = ref.ternary_product(a, w, 0.75)
+    u = 2.0 ** -23
+    gam = K * u / (1 - K * u)
+    bound = gam * 0.75 * (np.abs(a) @ np.abs(w.astype(np.float64)).T)
+    if act == "bf16":
+        bound += np.abs(exact) * 2.0 ** -8   # output rounding to bf16 (one half ulp, doubled)
+    assert np.all(np.abs(z - exact) <= bound + 1e-30)
+
+
+# ------------------------------------------------------------------ routing
+def check_routing(inp, idx, gate, offsets=None, slots=None):
+    cfg = inp.cfg
+    x = ref.stored_to_f64(inp.x, cfg.act)
+    wg = ref.stored_to_f64(inp.w_gate, cfg.act)
+    R = ref.route(x, wg, cfg.top_k, cfg.renorm_gates)
+    idx = np.asarray(idx)
+    same = (idx == R.idx).all(axis=1)
+    bad = ~same & ~R.ambiguous
+    assert not bad.any(), f"{bad.sum()} tokens routed differently, e.g. {np.nonzero(bad)[0][:5]}"
+    # gates: fp32 softmax of fp32 logits; relative error bound from the logit bound
+    d = cfg.d_model
+    depth = d / 32 + 32 if cfg.act == "bf16" else d
+    g = depth * 2.0 ** -22
+    lerr = 2 * g / (1 - g) * np.linalg.norm(x, axis=1) * np.linalg.norm(wg, axis=1).max()
+    tol = (2 * lerr + 3e-5 + cfg.n_experts * 2.0 ** -23)[:, None] * R.gates
+    ok = same[:, None]
+    assert np.all(~ok | (np.abs(np.asarray(gate, np.float64) - R.gates) <= tol))
+    if offsets is not None:
+        counts = np.bincount(np.asarray(idx).ravel(), minlength=cfg.n_experts)
+        assert np.array_equal(np.asarray(offsets), np.concatenate([[0], np.cumsum(counts)]))
+        flat = np.asarray(idx).ravel()
+        want = np.concatenate([np.nonzero(flat == e)[0] for e in range(cfg.n_experts)])
+        assert np.array_equal(np.asarray(slots), want)
+    return R
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
+def test_route_configs(ci):
+    import torch
+    cfg = wl.CONFIGS[ci]
+    log(f"route config {cfg.name}")
+    inp = wl.generate(cfg)
+    layer = bm.Layer.from_inputs(inp)
+    idx, gate, off, slots = layer.route(to_dev(inp.x, cfg.act), with_buckets=True)
+    torch.cuda.synchronize()
+    check_routing(inp, idx.cpu().numpy(), gate.cpu().numpy(), off.cpu().numpy(), slots.cpu().numpy())
+
+
+def test_route_skewed_and_tied():
+    import torch
+    cfg = wl.small_config(d_model=128, n_experts=16, top_k=4, tokens=777, act="bf16", seed_index=5)
+    inp = wl.generate(cfg, gate_mode="skewed")
+    # duplicate two experts' gate rows: exact ties in every token's logits
+    inp.w_gate[7] = inp.w_gate[3]
+    layer = bm.Layer.from_inputs(inp)
+    log("route skewed/tied")
+    idx, gate, off, slots = layer.route(to_dev(inp.x, cfg.act), with_buckets=True)
+    torch.cuda.synchronize()
+    R = check_routing(inp, idx.cpu().numpy(), gate.cpu().numpy(), off.cpu().numpy(), slots.cpu().numpy())
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=16)
+    assert counts.max() > 1.5 * counts.mean()  # the load really is skewed
+
+
+# ------------------------------------------------------------------ layer forward
+def check_forward(inp, y, idx, gate, tokens=None):
+    cfg = inp.cfg
+    y = to_f64(y)
+    idx = idx.cpu().numpy()
+    if tokens is None:
+        x = ref.stored_to_f64(inp.x, cfg.act)
+        wg = ref.stored_to_f64(inp.w_gate, cfg.act)
+        R = ref.route(x, wg, cfg.top_k, cfg.renorm_gates)
+        mism = ~(idx == R.idx).all(axis=1)
+        assert not (mism & ~R.ambiguous).any()
+        yref, _ = ref.forward(inp, routing=R, idx_override=idx if mism.any() else None)
+        err = row_rel_err(y, yref)
+    else:
+        yref, ridx, _ = ref.forward_tokens(inp, tokens)
+        assert np.array_equal(idx[tokens], ridx)
+        err = row_rel_err(y[tokens], yref)
+    log(f"  max rel err {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= tol_for(cfg.act), err.max()
+    return err
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2])
+def test_forward_configs_full(ci):
+    cfg = wl.CONFIGS[ci]
+    log(f"forward config {cfg.name}")
+    inp = wl.generate(cfg)
+    _, _, (y, idx, gate) = run_layer(inp)
+    check_forward(inp, y, idx, gate)
+
+
+@pytest.mark.parametrize("ci", [3, 4])
+def test_forward_configs_sampled(ci):
+    cfg = wl.CONFIGS[ci]
+    log(f"forward config {cfg.name} (full run, sampled check)")
+    inp = wl.generate(cfg)
+    _, _, (y, idx, gate) = run_layer(inp)
+    r = np.random.default_rng(ci)
+    toks = np.sort(r.choice(cfg.tokens, size=24, replace=False))
+    toks = np.unique(np.concatenate([toks, [0, cfg.tokens - 1]]))
+    check_forward(inp, y, idx, gate, tokens=toks)
+    # every output row finite
+    import torch
+    assert bool(torch.isfinite(y.float()).all())
+
+
+SMALL_CASES = [
+    dict(d_model=64, n_experts=5, top_k=2, tokens=37, act="bf16"),
+    dict(d_model=64, n_experts=5, top_k=2, tokens=37, act="f32"),
+    dict(d_model=128, n_experts=1, top_k=1, tokens=1, act="bf16"),
+    dict(d_model=256, n_experts=8, top_k=8, tokens=300, act="bf16"),
+    dict(d_model=64, n_experts=3, top_k=1, tokens=129, act="bf16"),
+    dict(d_model=128, n_experts=6, top_k=3, tokens=200, act="f32", renorm_gates=True, w_scale=0.5),
+    dict(d_model=64, d_ff=256, n_experts=3, top_k=2, tokens=50, act="bf16"),
+    dict(d_model=64, d_ff=128, n_experts=4, top_k=2, tokens=65, act="f32"),
+    dict(d_model=128, d_ff=64, n_experts=7, top_k=2, tokens=333, act="bf16", renorm_gates=True),
+    dict(d_model=256, d_ff=1024, n_experts=16, top_k=2, tokens=1000, act="bf16", ffn_act="none"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_forward_small(case):
+    kw = SMALL_CASES[case]
+    cfg = wl.small_config(seed_index=200 + case, **kw)
+    log(f"forward small {cfg.name} {kw}")
+    inp = wl.generate(cfg)
+    _, _, (y, idx, gate) = run_layer(inp)
+    check_forward(inp, y, idx, gate)
+
+
+def test_forward_identity_experts_and_skew():
+    cfg = wl.small_config(d_model=512, n_experts=32, top_k=2, tokens=2048, act="bf16", seed_index=77)
+    inp = wl.generate(cfg, angle_mode="zero", gate_mode="skewed")
+    log("forward identity experts, skewed routing")
+    _, _, (y, idx, gate) = run_layer(inp)
+    check_forward(inp, y, idx, gate)
+
+
+def test_forward_outliers_small():
+    cfg = wl.small_config(d_model=256, d_ff=512, n_experts=8, top_k=2, tokens=300, act="bf16",
+                          outlier_frac=0.02, outlier_scale=50.0, seed_index=31)
+    inp = wl.generate(cfg)
+    log("forward outliers small")
+    _, _, (y, idx, gate) = run_layer(inp)
+    check_forward(inp, y, idx, gate)
+
+
+def test_forward_deterministic_and_empty():
+    import torch
+    cfg = wl.CONFIGS[1]
+    inp = wl.generate(cfg)
+    layer = bm.Layer.from_inputs(inp)
+    x = to_dev(inp.x, cfg.act)
+    log("forward determinism")
+    y1 = layer.forward(x)
+    y2 = layer.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y0 = layer.forward(x[:0])
+    torch.cuda.synchronize()
+    assert y0.shape == (0, cfg.d_model)
+
+
+def test_route_matches_forward_routing():
+    import torch
+    cfg = wl.CONFIGS[2]
+    inp = wl.generate(cfg)
+    layer = bm.Layer.from_inputs(inp)
+    x = to_dev(inp.x, cfg.act)
+    log("route vs forward routing")
+    i1, g1 = layer.route(x)
+    _, i2, g2 = layer.forward(x, return_routing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(g1, g2)
