@@ -74,7 +74,6 @@ def kernel_work(cfg):
     Ld = int(math.log2(d))
     ang_d = N * Ld * (d // 2) * 4
     w = {}
-    w["prep"] = (N * d * s + 8 * N, 2 * N * d, "hbm")
     w["route"] = (T * d * s + N * d * s + 8 * R, 2 * T * d * N, "hbm")
     w["bucket"] = (4 * R + 4 * R + 4 * (N + 1), 0, "hbm")
     w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
@@ -270,7 +269,7 @@ def bm_kernel_sha(kernel: str) -> str:
     """Hash of the HIP source that holds `kernel` (to invalidate stale counters)."""
     import hashlib
     src = {"gemm": "gemm.hip", "gemm_up": "gemm.hip", "gemm_down": "gemm.hip", "combine": "gemm.hip",
-           "route": "route.hip", "prep": "route.hip", "bucket": "route.hip"}.get(kernel, "butterfly.hip")
+           "route": "route.hip", "bucket": "route.hip"}.get(kernel, "butterfly.hip")
     p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 

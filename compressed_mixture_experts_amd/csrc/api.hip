@@ -7,8 +7,8 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/bmoe.h"
-#include "../../include/bmoe_debug.h"
+#include "bmoe.h"
+#include "bmoe_debug.h"
 #include "common.hpp"
 
 using namespace bmoe;
@@ -112,7 +112,7 @@ bmoe_status check_layer(const bmoe_layer* L) {
 
 // Workspace layout (offsets in bytes, each 256-byte aligned).
 struct Plan {
-  size_t counts, wnorm2, offsets, perm, idx, gate, bufU, bufZ, total;
+  size_t offsets, perm, idx, gate, bufU, bufZ, total;
   int64_t R;
 };
 
@@ -129,8 +129,6 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
     o = align256(o + bytes);
     return at;
   };
-  p.counts = take(size_t(L->n_experts) * 4);
-  p.wnorm2 = take(size_t(L->n_experts) * 4);
   p.offsets = take(size_t(L->n_experts + 1) * 4);
   p.perm = take(size_t(R) * 4);
   p.idx = take(size_t(R) * 4);
@@ -174,12 +172,9 @@ bmoe_status validate_call(const bmoe_layer* L, const void* x, int32_t T, void* w
 bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* idx, float* gate,
                       void* ws, const Plan& p, hipStream_t s) {
   const int act = L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
-  int32_t* counts = at<int32_t>(ws, p.counts);
-  float* wn2 = at<float>(ws, p.wnorm2);
-  BMOE_HIP(launch_prep(L->w_gate, act, L->n_experts, L->d_model, wn2, counts, s));
-  RouteArgs ra{x, L->w_gate, wn2, idx, gate, counts, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates};
+  RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates};
   BMOE_HIP(launch_route(ra, act, s));
-  BucketArgs ba{idx, counts, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts};
+  BucketArgs ba{idx, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -259,7 +254,6 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T, int32_
 // Kernel launches of one forward, in order (marks[i] follows launch i-1).
 static int forward_kernel_names(const bmoe_layer* L, const char** names) {
   int n = 0;
-  names[n++] = "prep";
   names[n++] = "route";
   names[n++] = "bucket";
   names[n++] = "bfly_in";
@@ -318,8 +312,6 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   float* gate = topk_gate ? topk_gate : at<float>(workspace, p.gate);
   const int32_t R = int32_t(p.R);
   const int32_t N = layer->n_experts, k = layer->top_k, d = layer->d_model, f = layer->d_ff;
-  int32_t* counts = at<int32_t>(workspace, p.counts);
-  float* wn2 = at<float>(workspace, p.wnorm2);
   int32_t* offsets = at<int32_t>(workspace, p.offsets);
   int32_t* perm = at<int32_t>(workspace, p.perm);
   void* bufU = at<char>(workspace, p.bufU);
@@ -327,10 +319,9 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   const int Ld = ilog2(d);
 
   // router and bucketing
-  BMOE_LAUNCH(launch_prep(layer->w_gate, act, N, d, wn2, counts, stream));
-  RouteArgs ra{x, layer->w_gate, wn2, idx, gate, counts, T, d, N, k, layer->renorm_gates};
+  RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates};
   BMOE_LAUNCH(launch_route(ra, act, stream));
-  BucketArgs ba{idx, counts, offsets, perm, R, N};
+  BucketArgs ba{idx, offsets, perm, R, N};
   BMOE_LAUNCH(launch_bucket(ba, stream));
   // input rotation: U[q] = B(theta_e)^T x_t
   BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};

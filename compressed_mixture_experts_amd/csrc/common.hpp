@@ -90,16 +90,13 @@ __device__ __forceinline__ float ternary_value(uint32_t w, int c) {
 struct RouteArgs {
   const void* x;            // [T][d]
   const void* w_gate;       // [N][d]
-  const float* wnorm2;      // [N] squared row norms of w_gate (fp32)
   int32_t* topk_idx;        // [T][k]
   float* topk_gate;         // [T][k]
-  int32_t* counts;          // [N], zeroed before, incremented per routed slot
   int32_t T, d, N, k, renorm;
 };
 
 struct BucketArgs {
   const int32_t* topk_idx;  // [R] flat slots
-  const int32_t* counts;    // [N]
   int32_t* offsets;         // [N+1]
   int32_t* perm;            // [R] bucket position -> flat slot
   int32_t R, N;
@@ -136,8 +133,6 @@ struct CombineArgs {
   int32_t T, d, k;
 };
 
-hipError_t launch_prep(const void* w_gate, int act, int32_t N, int32_t d, float* wnorm2,
-                       int32_t* counts, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);

@@ -2,56 +2,34 @@
 // gist.science/nl/paper/2601.13563, §2 "Drie Fasen van de Methode": a standard
 // top-k gating network selects the active experts).
 //
-// Logits l = W_g x are computed in fp32 (bf16 activations: MFMA
-// 16x16x32 bf16 -> fp32; fp32 activations: one FMA chain per logit).  Each
-// token's top-k order is then decided in fp32 unless one of its decisive gaps
-// (between consecutive chosen logits, and between the k-th and the (k+1)-th)
-// is within twice the worst-case fp32 error of a logit,
-//     gamma_D * |x| * max_e |w_e|,  gamma_D = D u / (1 - D u),
-// where D bounds the rounding depth of the sum (K/32 MFMA accumulations plus
-// 32 adds inside one MFMA; or d for an FMA chain) and u = 2^-22 (twice the fp32
-// unit roundoff, as the MFMA's internal rounding mode is not documented).
-// Such tokens are recomputed in fp64 (bf16 x bf16 products are exact), so the
-// chosen experts equal those of exact arithmetic except for gaps below fp64
-// rounding.
+// Logits l = W_g x are computed in fp32: bf16 activations on MFMA
+// (v_mfma_f32_16x16x32_bf16, exact bf16 products, fp32 accumulation), fp32
+// activations with one FMA chain per logit.  Every fp32 logit is within
+//     eps_t = gamma_D * |x_t| * max_e |w_e|,   gamma_D = D u / (1 - D u)
+// of its exact value, where D bounds the rounding depth of the sum (K/32 MFMA
+// accumulations plus 32 adds inside one MFMA, or d for an FMA chain) and
+// u = 2^-22 (twice the fp32 unit roundoff, as the MFMA's internal rounding is
+// not documented).  A token's top-k is taken from the fp32 logits unless one
+// of its decisive gaps (between consecutive chosen logits, or between the k-th
+// and the (k+1)-th) is below 2 eps_t.  Then every expert whose fp32 logit is
+// at least (k-th fp32 logit - 2 eps_t) - the only experts that can belong to
+// the exact top-k - is recomputed in fp64 (exact bf16 products) and the top-k
+// is taken among those.  Gates are the fp32 softmax probabilities.
 #include "common.hpp"
 #include <float.h>
 
 namespace bmoe {
 
 constexpr int RT_THREADS = 256;
-constexpr int RT_TOK = 32;     // tokens per workgroup
-constexpr int RT_KMAX = 8;     // largest supported top_k
+constexpr int RT_BT = 64;            // tokens per workgroup
+constexpr int RT_BK = 64;            // K per pipeline step (two MFMA k-steps)
+constexpr int RT_XLD = RT_BK + 8;    // padded LDS row of the token tile (bf16)
+constexpr int RT_KMAX = 8;           // largest supported top_k
 
-// ------------------------------------------------------------------ prep
-// Squared row norms of W_g (for the error bound) and zeroed expert counters.
-__global__ __launch_bounds__(64) void prep_kernel(const void* w_gate, int act, int d,
-                                                  float* wnorm2, int32_t* counts) {
-  const int e = blockIdx.x;
-  float s = 0.f;
-  for (int i = threadIdx.x; i < d; i += 64) {
-    const float v = act == ACT_BF16 ? load1<ACT_BF16>(w_gate, size_t(e) * d + i)
-                                    : load1<ACT_F32>(w_gate, size_t(e) * d + i);
-    s = fmaf(v, v, s);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (threadIdx.x == 0) {
-    wnorm2[e] = s;
-    counts[e] = 0;
-  }
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
 }
-
-hipError_t launch_prep(const void* w_gate, int act, int32_t N, int32_t d, float* wnorm2,
-                       int32_t* counts, hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel, dim3(N), dim3(64), 0, s, w_gate, act, d, wnorm2, counts);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ wave top-k
-// Better = larger value, or equal value and lower index.
-template <typename T>
-__device__ __forceinline__ bool better(T v, int i, T bv, int bi) {
+__device__ __forceinline__ bool better(double v, int i, double bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
@@ -62,255 +40,377 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
-// Top-kk of the N values a wave holds (lane owns indices lane + 64 j).
-// Results are uniform over the wave.
-template <typename T>
-__device__ __forceinline__ void wave_topk(T v[4], int N, int kk, T* tv, int* ti) {
-  const int lane = threadIdx.x & 63;
-  for (int j = 0; j < kk; ++j) {
-    T bv = v[0];
-    int bi = lane;
+// Insert (v, i) into the sorted list (tv, ti) of length KK, branch-free.
+template <int KK, typename T>
+__device__ __forceinline__ void topk_insert(T* tv, int* ti, T v, int i) {
 #pragma unroll
-    for (int u = 1; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      if (i < N && better(v[u], i, bv, bi)) { bv = v[u]; bi = i; }
-    }
-    if (lane >= N) bi = 0x7fffffff;
+  for (int j = 0; j < KK; ++j) {
+    const bool sw = better(v, i, tv[j], ti[j]);
+    const T a = tv[j];
+    const int b = ti[j];
+    tv[j] = sw ? v : a;
+    ti[j] = sw ? i : b;
+    v = sw ? a : v;
+    i = sw ? b : i;
+  }
+}
+
+// Per-token decision: 4 threads per token (q = lane & 3) each scan every 4th
+// expert.  Round j picks the best entry strictly below the pick of round j-1
+// in the order (larger value, then lower index), so kk rounds give the sorted
+// top-kk.  Writes idx/gates of the fp32 decision and flags tokens whose
+// decisive gaps are within the error bound.
+__device__ void decide(const float* Lrow, int N, int k, int kk, int renorm, float tau, int q,
+                       int* out_idx, float* out_gate, float* out_thr, float* out_max,
+                       float* out_sum, bool* flag) {
+  float tv[RT_KMAX + 1];
+  int ti[RT_KMAX + 1];
+  float pv = INFINITY;
+  int pi = -1;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const T ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  for (int j = 0; j < RT_KMAX + 1; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (j < kk) {
+      for (int e = q; e < N; e += 4) {
+        const float v = Lrow[e];
+        const bool below = v < pv || (v == pv && e > pi);
+        if (below && better(v, e, bv, bi)) { bv = v; bi = e; }
+      }
+#pragma unroll
+      for (int o = 1; o <= 2; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
     }
     tv[j] = bv;
     ti[j] = bi;
-    // remove the winner
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (lane + 64 * u == bi) v[u] = -(T)INFINITY;
+    pv = bv;
+    pi = bi;
   }
-}
-
-// Decide one token from its N logits held in LDS (fp32 or fp64).  Writes the
-// chosen experts and gates to the per-token slots; returns true (uniform) if a
-// decisive gap is below `tau`.
-template <typename T>
-__device__ bool decide_token(const T* logits, int N, int k, int renorm, T tau, int* out_idx,
-                             float* out_gate) {
-  const int lane = threadIdx.x & 63;
-  T v[4], orig[4];
+  const float mx = tv[0];
+  float s = 0.f;
+  for (int e = q; e < N; e += 4) s += __expf(Lrow[e] - mx);
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  if (q == 0) {
+    bool f = false;
+    const int ngap = min(k, N - 1);
+    float g[RT_KMAX];
+    float gs = 0.f;
+    float kth = tv[0];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = lane + 64 * u;
-    v[u] = i < N ? logits[i] : -(T)INFINITY;
-    orig[u] = v[u];
-  }
-  const int kk = min(k + 1, N);
-  T tv[RT_KMAX + 1];
-  int ti[RT_KMAX + 1];
-  wave_topk<T>(v, N, kk, tv, ti);
-  const T mx = tv[0];
-  T se = 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = lane + 64 * u;
-    if (i < N) se += (sizeof(T) == 8) ? (T)exp((double)(orig[u] - mx)) : (T)expf((float)(orig[u] - mx));
-  }
-  se = wave_sum(se);
-  bool flag = false;
-  const int ngap = min(k, N - 1);
-  for (int j = 0; j < ngap; ++j)
-    if (tv[j] - tv[j + 1] < tau) flag = true;
-  if (lane == 0) {
-    T g[RT_KMAX];
-    T gs = 0;
-    for (int j = 0; j < k; ++j) {
-      g[j] = ((sizeof(T) == 8) ? (T)exp((double)(tv[j] - mx)) : (T)expf((float)(tv[j] - mx))) / se;
+    for (int j = 0; j < RT_KMAX; ++j) {
+      if (j < ngap && tv[j] - tv[j + 1] < tau) f = true;
+      g[j] = (j < k) ? __expf(tv[j] - mx) / s : 0.f;
       gs += g[j];
+      if (j == k - 1) kth = tv[j];
     }
-    for (int j = 0; j < k; ++j) {
-      out_idx[j] = ti[j];
-      out_gate[j] = (float)(renorm ? g[j] / gs : g[j]);
+#pragma unroll
+    for (int j = 0; j < RT_KMAX; ++j) {
+      if (j < k) {
+        out_idx[j] = ti[j];
+        out_gate[j] = renorm ? g[j] / gs : g[j];
+      }
     }
+    *out_thr = kth - tau;
+    *out_max = mx;
+    *out_sum = s;
+    *flag = f;
   }
-  return flag;
 }
 
-// ------------------------------------------------------------------ router
 template <int ACT>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
-  // LDS: logits [RT_TOK][257] fp32, gate-weight chunk [256][40] bf16 (bf16 path)
-  __shared__ float sL[RT_TOK][257];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[256 * 40];
-  __shared__ float sX2[RT_TOK];
-  __shared__ double sL64[256];
-  __shared__ int sIdx[RT_TOK][RT_KMAX];
-  __shared__ float sGate[RT_TOK][RT_KMAX];
-  __shared__ int sFlag[RT_TOK];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* sx = reinterpret_cast<uint16_t*>(smem);  // [2][RT_BT][RT_XLD] token tile (bf16)
+  float* sL = reinterpret_cast<float*>(smem);         // [RT_BT][LS] logits (after the K loop)
+  __shared__ float sX2[RT_BT];
+  __shared__ int sIdx[RT_BT][RT_KMAX];
+  __shared__ float sGate[RT_BT][RT_KMAX];
+  __shared__ float sThr[RT_BT], sMax[RT_BT], sSum[RT_BT];
+  __shared__ int sFlag[RT_BT];
   __shared__ int sNF;
-  __shared__ float sWmax;
+  __shared__ float sWmax[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RT_TOK;
+  const int t0 = blockIdx.x * RT_BT;
   const int N = a.N, d = a.d, k = a.k;
+  const int NB = (N + 15) >> 4;
+  const int LS = NB * 16 + 4;  // logit row stride (conflict-free quarter reads)
   if (tid == 0) sNF = 0;
-
-  // max_e |w_e|^2 (wave 0)
-  if (wave == 0) {
-    float m = 0.f;
-    for (int i = lane; i < N; i += 64) m = fmaxf(m, a.wnorm2[i]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    if (lane == 0) sWmax = m;
-  }
 
   int depth;
   if constexpr (ACT == ACT_BF16) {
-    // wave (tg, eg): tokens 16*tg .. +15, expert blocks eg, eg+2, ...
-    const int tg = wave & 1, eg = wave >> 1;
-    const int NB = (N + 15) >> 4;
-    f32x4_t acc[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float x2 = 0.f;
-    const int tok = t0 + 16 * tg + (lane & 15);
-    const bool tok_ok = tok < a.T;
     const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
     const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w_gate);
-    const int Npad = NB * 16;
-    for (int k0 = 0; k0 < d; k0 += 32) {
-      // gate-weight chunk [Npad][32] -> LDS (row stride 40 bf16)
-      for (int c = tid; c < Npad * 4; c += RT_THREADS) {
-        const int row = c >> 2, ch = c & 3;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < N) v = *reinterpret_cast<const uint4*>(wg + size_t(row) * d + k0 + 8 * ch);
-        *reinterpret_cast<uint4*>(&sG[row * 40 + 8 * ch]) = v;
-      }
-      uint4 xv = make_uint4(0, 0, 0, 0);
-      if (tok_ok) xv = *reinterpret_cast<const uint4*>(xg + size_t(tok) * d + k0 + 8 * (lane >> 4));
-      {
-        const float f[8] = {bf16lo(xv.x), bf16hi(xv.x), bf16lo(xv.y), bf16hi(xv.y),
-                            bf16lo(xv.z), bf16hi(xv.z), bf16lo(xv.w), bf16hi(xv.w)};
+    // wave w owns expert blocks b = w + 4 i (i < 4) and all four token blocks
+    f32x4_t acc[4][4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x2 = fmaf(f[j], f[j], x2);
-      }
-      const bf16x8_t xf = __builtin_bit_cast(bf16x8_t, xv);
-      __syncthreads();
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const int b = eg + 2 * bb;
-        if (b < NB) {
-          const bf16x8_t gf = *reinterpret_cast<const bf16x8_t*>(&sG[(16 * b + (lane & 15)) * 40 + 8 * (lane >> 4)]);
-          acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf, xf, acc[bb], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float wsq[4] = {0.f, 0.f, 0.f, 0.f};
+    float xsq[2] = {0.f, 0.f};
+    uint4 afr[4][2], anx[4][2];
+    uint4 xr[2];
+
+    auto load_a = [&](int k0, uint4 (&dst)[4][2]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 16 * (wave + 4 * i) + (lane & 15);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          dst[i][s] = (e < N) ? *reinterpret_cast<const uint4*>(wg + size_t(e) * d + k0 + 32 * s + 8 * (lane >> 4))
+                              : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto load_x = [&](int k0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int c = tid + RT_THREADS * r;
+        const int tok = t0 + (c >> 3);
+        xr[r] = (tok < a.T) ? *reinterpret_cast<const uint4*>(xg + size_t(tok) * d + k0 + 8 * (c & 7))
+                            : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int c = tid + RT_THREADS * r;
+        const uint4 v = xr[r];
+        const float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                            bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xsq[r] = fmaf(f[j], f[j], xsq[r]);
+        *reinterpret_cast<uint4*>(sx + (buf * RT_BT + (c >> 3)) * RT_XLD + 8 * (c & 7)) = v;
+      }
+    };
+
+    const int nk = d / RT_BK;
+    load_x(0);
+    load_a(0, afr);
+    store_x(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) {
+        load_x((kt + 1) * RT_BK);
+        load_a((kt + 1) * RT_BK, anx);
+      }
+      const uint16_t* xb = sx + buf * RT_BT * RT_XLD;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8_t bx[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bx[j] = *reinterpret_cast<const bf16x8_t*>(xb + (16 * j + (lane & 15)) * RT_XLD + 32 * s + 8 * (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (wave + 4 * i < NB) {
+            const uint4 av = afr[i][s];
+            const float f[8] = {bf16lo(av.x), bf16hi(av.x), bf16lo(av.y), bf16hi(av.y),
+                                bf16lo(av.z), bf16hi(av.z), bf16lo(av.w), bf16hi(av.w)};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wsq[i] = fmaf(f[j], f[j], wsq[i]);
+            const bf16x8_t ab = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bx[j], acc[i][j], 0, 0, 0);
+          }
         }
+      }
+      if (kt + 1 < nk) {
+        store_x(buf ^ 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) afr[i][s] = anx[i][s];
       }
       __syncthreads();
     }
-    // D[expert][token]: lane holds experts 16b + 4(lane>>4) + r, token lane & 15
+    // |x_t|^2: 8 threads share a token row per pipeline step
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      const int b = eg + 2 * bb;
+    for (int r = 0; r < 2; ++r) {
+      float v = xsq[r];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      if ((tid & 7) == 0) sX2[(tid + RT_THREADS * r) >> 3] = v;
+    }
+    // max_e |w_e|^2: lanes l, l^16, l^32, l^48 hold the same expert
+    float wm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = wsq[i];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      wm = fmaxf(wm, v);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+    if (lane == 0) sWmax[wave] = wm;
+    // logits -> LDS (the token tile is dead after the last barrier)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave + 4 * i;
       if (b < NB) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 16 * b + 4 * (lane >> 4) + r;
-          if (e < N) sL[16 * tg + (lane & 15)][e] = acc[bb][r];
-        }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sL[(16 * j + (lane & 15)) * LS + 16 * b + 4 * (lane >> 4) + r] = acc[i][j][r];
       }
     }
-    x2 += __shfl_xor(x2, 16, 64);
-    x2 += __shfl_xor(x2, 32, 64);
-    if (eg == 0 && lane < 16) sX2[16 * tg + lane] = x2;
     depth = d / 32 + 32;
   } else {
-    // fp32: one sequential FMA chain per (token, expert)
+    // fp32 activations: one sequential FMA chain per (token, expert)
     const float* xf = reinterpret_cast<const float*>(a.x);
     const float* wf = reinterpret_cast<const float*>(a.w_gate);
-    for (int p = tid; p < RT_TOK * N; p += RT_THREADS) {
+    for (int p = tid; p < RT_BT * N; p += RT_THREADS) {
       const int tl = p / N, e = p - tl * N;
       const int tok = t0 + tl;
       float s = 0.f;
       if (tok < a.T) {
-        const float* xr = xf + size_t(tok) * d;
-        const float* wr = wf + size_t(e) * d;
-        for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+        const float* xrow = xf + size_t(tok) * d;
+        const float* wrow = wf + size_t(e) * d;
+        for (int i = 0; i < d; ++i) s = fmaf(xrow[i], wrow[i], s);
       }
-      sL[tl][e] = s;
+      sL[tl * LS + e] = s;
     }
-    for (int tl = tid; tl < RT_TOK; tl += RT_THREADS) {
+    for (int tl = tid; tl < RT_BT; tl += RT_THREADS) {
       const int tok = t0 + tl;
       float s = 0.f;
       if (tok < a.T) {
-        const float* xr = xf + size_t(tok) * d;
-        for (int i = 0; i < d; ++i) s = fmaf(xr[i], xr[i], s);
+        const float* xrow = xf + size_t(tok) * d;
+        for (int i = 0; i < d; ++i) s = fmaf(xrow[i], xrow[i], s);
       }
       sX2[tl] = s;
     }
+    float wm = 0.f;
+    for (int e = tid; e < N; e += RT_THREADS) {
+      const float* wrow = wf + size_t(e) * d;
+      float s = 0.f;
+      for (int i = 0; i < d; ++i) s = fmaf(wrow[i], wrow[i], s);
+      wm = fmaxf(wm, s);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+    if (lane == 0) sWmax[wave] = wm;
     depth = d;
   }
   __syncthreads();
 
-  // ---- fp32 decision, one wave per token
-  const float u = 2.384185791015625e-07f;  // 2^-22
-  const float Du = depth * u;
-  const float gamma = Du / (1.f - Du);
-  const float wmax = sqrtf(sWmax);
-  for (int tl = wave; tl < RT_TOK; tl += RT_THREADS / 64) {
-    if (t0 + tl >= a.T) break;
+  // ---- fp32 decision: 4 threads per token
+  {
+    const float u = 2.384185791015625e-07f;  // 2^-22
+    const float Du = depth * u;
+    const float gamma = Du / (1.f - Du);
+    const float wmax = sqrtf(fmaxf(fmaxf(sWmax[0], sWmax[1]), fmaxf(sWmax[2], sWmax[3])));
+    const int tl = tid >> 2, q = tid & 3;
     const float tau = 2.02f * gamma * sqrtf(sX2[tl]) * wmax;
-    const bool flag = decide_token<float>(sL[tl], N, k, a.renorm, tau, sIdx[tl], sGate[tl]);
-    if (flag && lane == 0) sFlag[atomicAdd(&sNF, 1)] = tl;
+    const int kk = min(k + 1, N);
+    bool flag = false;
+    const float* Lrow = sL + tl * LS;
+decide(Lrow, N, k, kk, a.renorm, tau, q, sIdx[tl], sGate[tl], &sThr[tl], &sMax[tl], &sSum[tl], &flag);
+    if (q == 0 && flag && t0 + tl < a.T) sFlag[atomicAdd(&sNF, 1)] = tl;
   }
   __syncthreads();
 
-  // ---- fp64 recheck of flagged tokens (whole workgroup per token)
+  // ---- exact order of the near-tied tokens: candidates recomputed in fp64
   const int nf = sNF;
-  for (int f = 0; f < nf; ++f) {
+  for (int f = wave; f < nf; f += RT_THREADS / 64) {
     const int tl = sFlag[f];
+    const float thr = sThr[tl];
+    const float* Lrow = sL + tl * LS;
     const size_t xo = size_t(t0 + tl) * d;
-    for (int e = wave; e < N; e += RT_THREADS / 64) {
-      double s = 0.0;
-      for (int i = lane; i < d; i += 64) {
-        const double xv = ACT == ACT_BF16 ? (double)load1<ACT_BF16>(a.x, xo + i) : (double)load1<ACT_F32>(a.x, xo + i);
-        const double wv = ACT == ACT_BF16 ? (double)load1<ACT_BF16>(a.w_gate, size_t(e) * d + i)
-                                          : (double)load1<ACT_F32>(a.w_gate, size_t(e) * d + i);
-        s = fma(xv, wv, s);
+    double cv[RT_KMAX];
+    int ci[RT_KMAX];
+#pragma unroll
+    for (int j = 0; j < RT_KMAX; ++j) { cv[j] = -INFINITY; ci[j] = 0x7fffffff; }
+    for (int u = 0; u < 4; ++u) {
+      const int e0 = lane + 64 * u;
+      const bool cand = e0 < N && Lrow[e0] >= thr;
+      uint64_t m = __ballot(cand);
+      while (m) {
+        const int bit = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const int e = 64 * u + bit;
+        double s = 0.0;
+        for (int i = lane; i < d; i += 64) {
+          const double xv = (double)load1<ACT>(a.x, xo + i);
+          const double wv = (double)load1<ACT>(a.w_gate, size_t(e) * d + i);
+          s = fma(xv, wv, s);
+        }
+        s = wave_sum(s);
+        topk_insert<RT_KMAX>(cv, ci, s, e);
       }
-      s = wave_sum(s);
-      if (lane == 0) sL64[e] = s;
     }
-    __syncthreads();
-    if (wave == 0) decide_token<double>(sL64, N, k, a.renorm, 0.0, sIdx[tl], sGate[tl]);
-    __syncthreads();
+    if (lane == 0) {
+      const float mx = sMax[tl], se = sSum[tl];
+      float g[RT_KMAX];
+      float gs = 0.f;
+#pragma unroll
+      for (int j = 0; j < RT_KMAX; ++j) {
+        g[j] = (j < k) ? __expf(Lrow[ci[j] < N ? ci[j] : 0] - mx) / se : 0.f;
+        gs += g[j];
+      }
+#pragma unroll
+      for (int j = 0; j < RT_KMAX; ++j)
+        if (j < k) {
+          sIdx[tl][j] = ci[j] < N ? ci[j] : 0;
+          sGate[tl][j] = a.renorm ? g[j] / gs : g[j];
+        }
+    }
   }
+  __syncthreads();
 
-  // ---- outputs and expert counts
-  for (int p = tid; p < RT_TOK * k; p += RT_THREADS) {
+  for (int p = tid; p < RT_BT * k; p += RT_THREADS) {
     const int tl = p / k, j = p - tl * k;
     const int tok = t0 + tl;
     if (tok < a.T) {
-      const int e = sIdx[tl][j];
-      a.topk_idx[size_t(tok) * k + j] = e;
+      a.topk_idx[size_t(tok) * k + j] = sIdx[tl][j];
       a.topk_gate[size_t(tok) * k + j] = sGate[tl][j];
-      atomicAdd(&a.counts[e], 1);
     }
   }
+}
+
+size_t route_lds_bytes(int N) {
+  const int NB = (N + 15) >> 4;
+  const size_t logits = size_t(RT_BT) * (NB * 16 + 4) * sizeof(float);
+  const size_t tiles = size_t(2) * RT_BT * RT_XLD * sizeof(uint16_t);
+  return logits > tiles ? logits : tiles;
 }
 
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  const int grid = (a.T + RT_TOK - 1) / RT_TOK;
+  const int grid = (a.T + RT_BT - 1) / RT_BT;
+  const size_t lds = route_lds_bytes(a.N);
+  static int attr_done[64] = {0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  auto kb = route_kernel<ACT_BF16>;
+  auto kf = route_kernel<ACT_F32>;
+  if (dev < 0 || dev >= 64 || !attr_done[dev]) {
+    const int mx = int(route_lds_bytes(256));
+    err = hipFuncSetAttribute((const void*)kb, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+    if (err == hipSuccess) err = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+    if (err != hipSuccess) return err;
+    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
+  }
   if (act == ACT_BF16)
-    hipLaunchKernelGGL(route_kernel<ACT_BF16>, dim3(grid), dim3(RT_THREADS), 0, s, a);
+    hipLaunchKernelGGL(kb, dim3(grid), dim3(RT_THREADS), lds, s, a);
   else
-    hipLaunchKernelGGL(route_kernel<ACT_F32>, dim3(grid), dim3(RT_THREADS), 0, s, a);
+    hipLaunchKernelGGL(kf, dim3(grid), dim3(RT_THREADS), lds, s, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ bucketing
-// One workgroup per expert: its first bucket position is the sum of the
-// counts of the lower experts; it then walks all routed slots in order and
-// appends the ones routed to it, so within an expert slots ascend.
+// One workgroup per expert e.  Pass 1 counts the routed slots of experts below
+// e (its first bucket position); pass 2 walks all slots in order and appends
+// the ones routed to e, so within an expert slots ascend.
 constexpr int BK_THREADS = 1024;
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
@@ -318,9 +418,31 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   __shared__ int s_off;
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int part = (tid < e) ? a.counts[tid] : 0;  // e < 256 <= BK_THREADS
-  part = wave_sum(part);
-  if (lane == 0) s_w[wave] = part;
+
+  auto load4 = [&](int f0) -> int4 {
+    if (f0 + 3 < a.R) return *reinterpret_cast<const int4*>(a.topk_idx + f0);
+    int4 q;
+    q.x = (f0 + 0 < a.R) ? a.topk_idx[f0 + 0] : 0x7fffffff;
+    q.y = (f0 + 1 < a.R) ? a.topk_idx[f0 + 1] : 0x7fffffff;
+    q.z = (f0 + 2 < a.R) ? a.topk_idx[f0 + 2] : 0x7fffffff;
+    q.w = (f0 + 3 < a.R) ? a.topk_idx[f0 + 3] : 0x7fffffff;
+    return q;
+  };
+
+  // The routed slots are read in blocks of BK_BATCH int4 per thread, all
+  // loads of a block issued before any is used.
+  constexpr int BK_BATCH = 8;
+  const int span = 4 * BK_THREADS * BK_BATCH;
+  int lt = 0;
+  for (int b0 = 0; b0 < a.R; b0 += span) {
+    int4 q[BK_BATCH];
+#pragma unroll
+    for (int b = 0; b < BK_BATCH; ++b) q[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
+#pragma unroll
+    for (int b = 0; b < BK_BATCH; ++b) lt += (q[b].x < e) + (q[b].y < e) + (q[b].z < e) + (q[b].w < e);
+  }
+  lt = wave_sum(lt);
+  if (lane == 0) s_w[wave] = lt;
   __syncthreads();
   if (tid == 0) {
     int o = 0;
@@ -331,38 +453,40 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   }
   __syncthreads();
   const int off = s_off;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int running = 0;
-  for (int base = 0; base < a.R; base += 4 * BK_THREADS) {
-    const int f0 = base + 4 * tid;
-    int v[4];
-    if (f0 + 3 < a.R) {
-      const int4 q = *reinterpret_cast<const int4*>(a.topk_idx + f0);
-      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-    } else {
+  for (int b0 = 0; b0 < a.R; b0 += span) {
+    int4 qb[BK_BATCH];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = (f0 + j < a.R) ? a.topk_idx[f0 + j] : -1;
+    for (int b = 0; b < BK_BATCH; ++b) qb[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
+#pragma unroll
+    for (int b = 0; b < BK_BATCH; ++b) {
+      const int f0 = b0 + 4 * (b * BK_THREADS + tid);
+      if (b0 + 4 * b * BK_THREADS >= a.R) break;  // uniform
+      const int v[4] = {qb[b].x, qb[b].y, qb[b].z, qb[b].w};
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c += (v[j] == e);
+      const uint64_t m0 = __ballot(c & 1), m1 = __ballot(c & 2), m2 = __ballot(c & 4);
+      const int lpre = __popcll(m0 & ltmask) + 2 * __popcll(m1 & ltmask) + 4 * __popcll(m2 & ltmask);
+      const int wtot = __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2);
+      __syncthreads();
+      if (lane == 0) s_w[wave] = wtot;
+      __syncthreads();
+      int wpre = 0, tot = 0;
+      for (int w = 0; w < BK_THREADS / 64; ++w) {
+        const int x = s_w[w];
+        wpre += (w < wave) ? x : 0;
+        tot += x;
+      }
+      if (c) {
+        int qq = off + running + wpre + lpre;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (v[j] == e) a.perm[qq++] = f0 + j;
+      }
+      running += tot;
     }
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c += (v[j] == e);
-    const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
-    const int lpre = __popcll(b0 & lt) + 2 * __popcll(b1 & lt) + 4 * __popcll(b2 & lt);
-    const int wtot = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-    __syncthreads();
-    if (lane == 0) s_w[wave] = wtot;
-    __syncthreads();
-    int wpre = 0, tot = 0;
-    for (int w = 0; w < BK_THREADS / 64; ++w) {
-      const int x = s_w[w];
-      wpre += (w < wave) ? x : 0;
-      tot += x;
-    }
-    int q = off + running + wpre + lpre;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (v[j] == e) a.perm[q++] = f0 + j;
-    running += tot;
   }
 }
 
