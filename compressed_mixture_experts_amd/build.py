@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbmoe.so")
-SOURCES = ["api.hip", "route.hip", "butterfly.hip", "gemm.hip"]
+SOURCES = ["api.hip", "route.hip", "gemm.hip", "butterfly.hip", "butterfly_dbg.hip",
+           "butterfly_in.hip", "butterfly_mid.hip", "butterfly_out.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -37,7 +38,7 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
+def build(jobs: int = 8, verbose: bool = False) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)

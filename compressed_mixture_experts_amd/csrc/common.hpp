@@ -139,7 +139,5 @@ hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hip
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 
-// Rows per butterfly tile for width 2^log2n (shared by launcher and planner).
-int bfly_rows_per_tile(int log2n);
 
 }  // namespace bmoe
