@@ -12,13 +12,12 @@
 // columns of one row and stores them as one 8-byte write.
 // fp32 path: a plain fp32 FMA loop (small layers and tests).
 #include "common.hpp"
+#include <type_traits>
 
 namespace bmoe {
 
 constexpr int GM_THREADS = 256;
-constexpr int GT_N = 128;     // substrate rows per workgroup tile
-constexpr int GT_M = 128;     // activation rows per workgroup tile
-constexpr int GBK = 64;       // K per stage
+constexpr int GBK = 64;       // K per pipeline step
 constexpr int GLDK = GBK + 8; // padded LDS row (bf16 elements): conflict-free fragment reads
 
 // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -30,53 +29,66 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+// Workgroup tile: TN substrate rows (output columns) x TM activation rows,
+// four waves in a 2 x 2 arrangement.  NS register sets keep the global loads
+// of the next NS K-steps in flight (NS >= K/64 issues every load of the tile
+// at once); two LDS buffers, one barrier per step.
+template <int TM, int TN, int NS>
 __global__ __launch_bounds__(GM_THREADS) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int WN = TN / 2, WM = TM / 2;            // wave tile
+  constexpr int NI = WN / 16, MJ = WM / 16;          // MFMA blocks per wave
+  constexpr int UCH = TM * (GBK / 8);                // 16-byte chunks of the U tile per step
+  constexpr int UPT = UCH / GM_THREADS;
+  constexpr int WWD = TN * (GBK / 16);               // packed words of the W tile per step
+  constexpr int WPT = WWD / GM_THREADS;
+  static_assert(UPT >= 1 && WPT >= 1, "tile too small");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* sW = smem;                       // [2][GT_N][GLDK]
-  uint16_t* sU = smem + 2 * GT_N * GLDK;     // [2][GT_M][GLDK]
+  uint16_t* sW = smem;                       // [2][TN][GLDK]
+  uint16_t* sU = smem + 2 * TN * GLDK;       // [2][TM][GLDK]
 
-  const int ntn = (a.N + GT_N - 1) / GT_N;
+  const int ntn = (a.N + TN - 1) / TN;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int tn = logical % ntn, tm = logical / ntn;
-  const int n0 = tn * GT_N, m0 = tm * GT_M;
+  const int n0 = tn * TN, m0 = tm * TM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int K = a.K, KW = a.K >> 4;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(a.a);
 
-  uint4 ureg[4];
-  uint32_t wreg[2];
-  auto gload = [&](int k0) {
+  uint4 ureg[NS][UPT];
+  uint32_t wreg[NS][WPT];
+  // (all set indices below are compile-time constants after unrolling)
+  auto gload = [&](int k0, uint4 (&ur)[UPT], uint32_t (&wr)[WPT]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < UPT; ++i) {
       const int c = tid + GM_THREADS * i;
       const int row = c >> 3, ch = c & 7;
       const int m = m0 + row;
-      ureg[i] = (m < a.M) ? *reinterpret_cast<const uint4*>(A + size_t(m) * K + k0 + 8 * ch)
-                          : make_uint4(0, 0, 0, 0);
+      ur[i] = (m < a.M) ? *reinterpret_cast<const uint4*>(A + size_t(m) * K + k0 + 8 * ch)
+                        : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WPT; ++i) {
       const int w = tid + GM_THREADS * i;
       const int row = w >> 2, kw = w & 3;
       const int n = n0 + row;
-      wreg[i] = (n < a.N) ? a.w[size_t(n) * KW + (k0 >> 4) + kw] : 0u;
+      wr[i] = (n < a.N) ? a.w[size_t(n) * KW + (k0 >> 4) + kw] : 0u;
     }
   };
-  auto lstore = [&](int buf) {
-    uint16_t* su = sU + buf * GT_M * GLDK;
-    uint16_t* sw = sW + buf * GT_N * GLDK;
+  auto lstore = [&](int buf, const uint4 (&ur)[UPT], const uint32_t (&wr)[WPT]) {
+    uint16_t* su = sU + buf * TM * GLDK;
+    uint16_t* sw = sW + buf * TN * GLDK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < UPT; ++i) {
       const int c = tid + GM_THREADS * i;
       const int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4*>(su + row * GLDK + 8 * ch) = ureg[i];
+      *reinterpret_cast<uint4*>(su + row * GLDK + 8 * ch) = ur[i];
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WPT; ++i) {
       const int w = tid + GM_THREADS * i;
       const int row = w >> 2, kw = w & 3;
-      const uint32_t P = wreg[i];
+      const uint32_t P = wr[i];
       uint4 lo, hi;
       lo.x = ternary_pair_bf16(P, 0); lo.y = ternary_pair_bf16(P, 1);
       lo.z = ternary_pair_bf16(P, 2); lo.w = ternary_pair_bf16(P, 3);
@@ -88,47 +100,54 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_bf16_kernel(GemmArgs a) {
     }
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[NI][MJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int nk = K / GBK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GBK);
-    const uint16_t* sw = sW + buf * GT_N * GLDK;
-    const uint16_t* su = sU + buf * GT_M * GLDK;
 #pragma unroll
-    for (int kk = 0; kk < GBK; kk += 32) {
-      bf16x8_t wf[4], uf[4];
+  for (int s = 0; s < NS; ++s)
+    if (s < nk) gload(s * GBK, ureg[s], wreg[s]);
+
+  for (int kb = 0; kb < nk; kb += NS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wf[i] = *reinterpret_cast<const bf16x8_t*>(sw + (wn * 64 + 16 * i + (lane & 15)) * GLDK + kk + 8 * (lane >> 4));
+    for (int s = 0; s < NS; ++s) {
+      const int kt = kb + s;
+      if (kt < nk) {
+        const int buf = kt & 1;
+        lstore(buf, ureg[s], wreg[s]);
+        __syncthreads();
+        if (kt + NS < nk) gload((kt + NS) * GBK, ureg[s], wreg[s]);  // refill this set
+        const uint16_t* sw = sW + buf * TN * GLDK;
+        const uint16_t* su = sU + buf * TM * GLDK;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        uf[j] = *reinterpret_cast<const bf16x8_t*>(su + (wm * 64 + 16 * j + (lane & 15)) * GLDK + kk + 8 * (lane >> 4));
+        for (int kk = 0; kk < GBK; kk += 32) {
+          bf16x8_t wf[NI], uf[MJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < NI; ++i)
+            wf[i] = *reinterpret_cast<const bf16x8_t*>(sw + (wn * WN + 16 * i + (lane & 15)) * GLDK + kk + 8 * (lane >> 4));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], uf[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < MJ; ++j)
+            uf[j] = *reinterpret_cast<const bf16x8_t*>(su + (wm * WM + 16 * j + (lane & 15)) * GLDK + kk + 8 * (lane >> 4));
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < MJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], uf[j], acc[i][j], 0, 0, 0);
+        }
+      }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   uint16_t* Z = reinterpret_cast<uint16_t*>(a.z);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + wn * 64 + 16 * i + 4 * (lane >> 4);
+  for (int i = 0; i < NI; ++i) {
+    const int n = n0 + wn * WN + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 64 + 16 * j + (lane & 15);
+    for (int j = 0; j < MJ; ++j) {
+      const int m = m0 + wm * WM + 16 * j + (lane & 15);
       if (m < a.M && n < a.N) {
         uint2 o;
         o.x = pack_bf16x2(a.alpha * acc[i][j][0], a.alpha * acc[i][j][1]);
@@ -155,25 +174,36 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   reinterpret_cast<float*>(a.z)[size_t(m) * a.N + n] = a.alpha * s;
 }
 
+template <int TM, int TN, int NS>
+static hipError_t launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
+  const int ntn = (a.N + TN - 1) / TN, ntm = (a.M + TM - 1) / TM;
+  const size_t lds = size_t(2) * (TN + TM) * GLDK * sizeof(uint16_t);
+  static int attr_done[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
+    e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<TM, TN, NS>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
+  }
+  auto kern = gemm_bf16_kernel<TM, TN, NS>;
+  hipLaunchKernelGGL(kern, dim3(ntn * ntm), dim3(GM_THREADS), lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (act == ACT_BF16) {
-    const int ntn = (a.N + GT_N - 1) / GT_N, ntm = (a.M + GT_M - 1) / GT_M;
-    const size_t lds = size_t(2) * (GT_N + GT_M) * GLDK * sizeof(uint16_t);
-    static int attr_done[64] = {0};
-    int dev = 0;
-    hipGetDevice(&dev);
-    if (dev < 64 && !attr_done[dev]) {
-      hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-      if (e != hipSuccess) return e;
-      attr_done[dev] = 1;
-    }
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(ntn * ntm), dim3(GM_THREADS), lds, s, a);
-  } else {
-    const size_t total = size_t(a.M) * a.N;
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a);
+    // 128-row tiles once they give every CU two workgroups, 64-row tiles below
+    const long tiles128 = long((a.M + 127) / 128) * ((a.N + 127) / 128);
+    if (tiles128 >= 512) return launch_gemm_tile<128, 128, 1>(a, s);
+    if (a.K <= 8 * GBK) return launch_gemm_tile<64, 128, 8>(a, s);
+    return launch_gemm_tile<64, 128, 2>(a, s);
   }
+  const size_t total = size_t(a.M) * a.N;
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

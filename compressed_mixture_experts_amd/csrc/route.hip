@@ -17,11 +17,11 @@
 // is taken among those.  Gates are the fp32 softmax probabilities.
 #include "common.hpp"
 #include <float.h>
+#include <type_traits>
 
 namespace bmoe {
 
 constexpr int RT_THREADS = 256;
-constexpr int RT_BT = 64;            // tokens per workgroup
 constexpr int RT_BK = 64;            // K per pipeline step (two MFMA k-steps)
 constexpr int RT_XLD = RT_BK + 8;    // padded LDS row of the token tile (bf16)
 constexpr int RT_KMAX = 8;           // largest supported top_k
@@ -121,21 +121,24 @@ __device__ void decide(const float* Lrow, int N, int k, int kk, int renorm, floa
   }
 }
 
-template <int ACT>
+template <int ACT, int BT>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
+  constexpr int TB = BT / 16;                 // token blocks of 16
+  constexpr int XCH = BT * (RT_BK / 8);       // 16-byte chunks of the token tile per step
+  constexpr int XPT = (XCH + RT_THREADS - 1) / RT_THREADS;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* sx = reinterpret_cast<uint16_t*>(smem);  // [2][RT_BT][RT_XLD] token tile (bf16)
-  float* sL = reinterpret_cast<float*>(smem);         // [RT_BT][LS] logits (after the K loop)
-  __shared__ float sX2[RT_BT];
-  __shared__ int sIdx[RT_BT][RT_KMAX];
-  __shared__ float sGate[RT_BT][RT_KMAX];
-  __shared__ float sThr[RT_BT], sMax[RT_BT], sSum[RT_BT];
-  __shared__ int sFlag[RT_BT];
+  uint16_t* sx = reinterpret_cast<uint16_t*>(smem);  // [2][BT][RT_XLD] token tile (bf16)
+  float* sL = reinterpret_cast<float*>(smem);         // [BT][LS] logits (after the K loop)
+  __shared__ float sX2[BT];
+  __shared__ int sIdx[BT][RT_KMAX];
+  __shared__ float sGate[BT][RT_KMAX];
+  __shared__ float sThr[BT], sMax[BT], sSum[BT];
+  __shared__ int sFlag[BT];
   __shared__ int sNF;
   __shared__ float sWmax[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RT_BT;
+  const int t0 = blockIdx.x * BT;
   const int N = a.N, d = a.d, k = a.k;
   const int NB = (N + 15) >> 4;
   const int LS = NB * 16 + 4;  // logit row stride (conflict-free quarter reads)
@@ -145,16 +148,20 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   if constexpr (ACT == ACT_BF16) {
     const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
     const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w_gate);
-    // wave w owns expert blocks b = w + 4 i (i < 4) and all four token blocks
-    f32x4_t acc[4][4];
+    // wave w owns expert blocks b = w + 4 i (i < 4) and all token blocks
+    f32x4_t acc[4][TB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float wsq[4] = {0.f, 0.f, 0.f, 0.f};
-    float xsq[2] = {0.f, 0.f};
-    uint4 afr[4][2], anx[4][2];
-    uint4 xr[2];
+    float xsq[XPT];
+#pragma unroll
+    for (int r = 0; r < XPT; ++r) xsq[r] = 0.f;
+    // two register sets (compile-time indexed): gate-weight fragments and
+    // token chunks two steps ahead
+    uint4 afr0[4][2], afr1[4][2];
+    uint4 xr0[XPT], xr1[XPT];
 
     auto load_a = [&](int k0, uint4 (&dst)[4][2]) {
 #pragma unroll
@@ -166,78 +173,86 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
                               : make_uint4(0, 0, 0, 0);
       }
     };
-    auto load_x = [&](int k0) {
+    auto load_x = [&](int k0, uint4 (&dst)[XPT]) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < XPT; ++r) {
         const int c = tid + RT_THREADS * r;
         const int tok = t0 + (c >> 3);
-        xr[r] = (tok < a.T) ? *reinterpret_cast<const uint4*>(xg + size_t(tok) * d + k0 + 8 * (c & 7))
-                            : make_uint4(0, 0, 0, 0);
+        dst[r] = (c < XCH && tok < a.T) ? *reinterpret_cast<const uint4*>(xg + size_t(tok) * d + k0 + 8 * (c & 7))
+                                        : make_uint4(0, 0, 0, 0);
       }
     };
-    auto store_x = [&](int buf) {
+    auto store_x = [&](int buf, const uint4 (&src)[XPT]) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < XPT; ++r) {
         const int c = tid + RT_THREADS * r;
-        const uint4 v = xr[r];
-        const float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
-                            bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+        if (c < XCH) {
+          const uint4 v = src[r];
+          const float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                              bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xsq[r] = fmaf(f[j], f[j], xsq[r]);
-        *reinterpret_cast<uint4*>(sx + (buf * RT_BT + (c >> 3)) * RT_XLD + 8 * (c & 7)) = v;
+          for (int j = 0; j < 8; ++j) xsq[r] = fmaf(f[j], f[j], xsq[r]);
+          *reinterpret_cast<uint4*>(sx + (buf * BT + (c >> 3)) * RT_XLD + 8 * (c & 7)) = v;
+        }
       }
     };
 
     const int nk = d / RT_BK;
-    load_x(0);
-    load_a(0, afr);
-    store_x(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) {
-        load_x((kt + 1) * RT_BK);
-        load_a((kt + 1) * RT_BK, anx);
-      }
-      const uint16_t* xb = sx + buf * RT_BT * RT_XLD;
+    auto step = [&](auto bufc, int kt, uint4 (&acur)[4][2], uint4 (&xcur)[XPT], uint4 (&xnext)[XPT]) {
+      constexpr int buf = decltype(bufc)::value;
+      const uint16_t* xb = sx + buf * BT * RT_XLD;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        bf16x8_t bx[4];
+        bf16x8_t bx[TB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TB; ++j)
           bx[j] = *reinterpret_cast<const bf16x8_t*>(xb + (16 * j + (lane & 15)) * RT_XLD + 32 * s + 8 * (lane >> 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (wave + 4 * i < NB) {
-            const uint4 av = afr[i][s];
+            const uint4 av = acur[i][s];
             const float f[8] = {bf16lo(av.x), bf16hi(av.x), bf16lo(av.y), bf16hi(av.y),
                                 bf16lo(av.z), bf16hi(av.z), bf16lo(av.w), bf16hi(av.w)};
 #pragma unroll
             for (int j = 0; j < 8; ++j) wsq[i] = fmaf(f[j], f[j], wsq[i]);
             const bf16x8_t ab = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < TB; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bx[j], acc[i][j], 0, 0, 0);
           }
         }
       }
-      if (kt + 1 < nk) {
-        store_x(buf ^ 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) afr[i][s] = anx[i][s];
+      // the gate fragments and token chunks of step kt are consumed: fetch
+      // step kt+2 into their registers, then publish step kt+1 to LDS
+      if (kt + 2 < nk) {
+        load_a((kt + 2) * RT_BK, acur);
+        load_x((kt + 2) * RT_BK, xcur);
       }
+      if (kt + 1 < nk) store_x(buf ^ 1, xnext);
       __syncthreads();
+    };
+
+    load_x(0, xr0);
+    load_a(0, afr0);
+    if (nk > 1) {
+      load_x(RT_BK, xr1);
+      load_a(RT_BK, afr1);
+    }
+    store_x(0, xr0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(std::integral_constant<int, 0>{}, kt, afr0, xr0, xr1);
+      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1, afr1, xr1, xr0);
     }
     // |x_t|^2: 8 threads share a token row per pipeline step
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < XPT; ++r) {
       float v = xsq[r];
       v += __shfl_xor(v, 1, 64);
       v += __shfl_xor(v, 2, 64);
       v += __shfl_xor(v, 4, 64);
-      if ((tid & 7) == 0) sX2[(tid + RT_THREADS * r) >> 3] = v;
+      const int c = tid + RT_THREADS * r;
+      if ((tid & 7) == 0 && c < XCH) sX2[c >> 3] = v;
     }
     // max_e |w_e|^2: lanes l, l^16, l^32, l^48 hold the same expert
     float wm = 0.f;
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       const int b = wave + 4 * i;
       if (b < NB) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TB; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             sL[(16 * j + (lane & 15)) * LS + 16 * b + 4 * (lane >> 4) + r] = acc[i][j][r];
@@ -268,7 +283,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     // fp32 activations: one sequential FMA chain per (token, expert)
     const float* xf = reinterpret_cast<const float*>(a.x);
     const float* wf = reinterpret_cast<const float*>(a.w_gate);
-    for (int p = tid; p < RT_BT * N; p += RT_THREADS) {
+    for (int p = tid; p < BT * N; p += RT_THREADS) {
       const int tl = p / N, e = p - tl * N;
       const int tok = t0 + tl;
       float s = 0.f;
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       }
       sL[tl * LS + e] = s;
     }
-    for (int tl = tid; tl < RT_BT; tl += RT_THREADS) {
+    for (int tl = tid; tl < BT; tl += RT_THREADS) {
       const int tok = t0 + tl;
       float s = 0.f;
       if (tok < a.T) {
@@ -309,12 +324,14 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     const float gamma = Du / (1.f - Du);
     const float wmax = sqrtf(fmaxf(fmaxf(sWmax[0], sWmax[1]), fmaxf(sWmax[2], sWmax[3])));
     const int tl = tid >> 2, q = tid & 3;
-    const float tau = 2.02f * gamma * sqrtf(sX2[tl]) * wmax;
-    const int kk = min(k + 1, N);
-    bool flag = false;
-    const float* Lrow = sL + tl * LS;
-decide(Lrow, N, k, kk, a.renorm, tau, q, sIdx[tl], sGate[tl], &sThr[tl], &sMax[tl], &sSum[tl], &flag);
-    if (q == 0 && flag && t0 + tl < a.T) sFlag[atomicAdd(&sNF, 1)] = tl;
+    if (tl < BT) {  // whole waves
+      const float tau = 2.02f * gamma * sqrtf(sX2[tl]) * wmax;
+      const int kk = min(k + 1, N);
+      bool flag = false;
+      const float* Lrow = sL + tl * LS;
+      decide(Lrow, N, k, kk, a.renorm, tau, q, sIdx[tl], sGate[tl], &sThr[tl], &sMax[tl], &sSum[tl], &flag);
+      if (q == 0 && flag && t0 + tl < a.T) sFlag[atomicAdd(&sNF, 1)] = tl;
+    }
   }
   __syncthreads();
 
@@ -337,11 +354,26 @@ decide(Lrow, N, k, kk, a.renorm, tau, q, sIdx[tl], sGate[tl], &sThr[tl], &sMax[t
         const int bit = __ffsll((unsigned long long)m) - 1;
         m &= m - 1;
         const int e = 64 * u + bit;
+        // lane owns elements 8*lane .. 8*lane+7 of each 512-wide chunk; the
+        // chunks' loads are issued four at a time before they are used
         double s = 0.0;
-        for (int i = lane; i < d; i += 64) {
-          const double xv = (double)load1<ACT>(a.x, xo + i);
-          const double wv = (double)load1<ACT>(a.w_gate, size_t(e) * d + i);
-          s = fma(xv, wv, s);
+        for (int i0 = 0; i0 < d; i0 += 4 * 512) {
+          float xv[4][8], wv[4][8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 512 * u + 8 * lane;
+            if (i < d) {
+              load8<ACT>(a.x, xo + i, xv[u]);
+              load8<ACT>(a.w_gate, size_t(e) * d + i, wv[u]);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (i0 + 512 * u + 8 * lane < d) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) s = fma((double)xv[u][j], (double)wv[u][j], s);
+            }
+          }
         }
         s = wave_sum(s);
         topk_insert<RT_KMAX>(cv, ci, s, e);
@@ -366,7 +398,7 @@ decide(Lrow, N, k, kk, a.renorm, tau, q, sIdx[tl], sGate[tl], &sThr[tl], &sMax[t
   }
   __syncthreads();
 
-  for (int p = tid; p < RT_BT * k; p += RT_THREADS) {
+  for (int p = tid; p < BT * k; p += RT_THREADS) {
     const int tl = p / k, j = p - tl * k;
     const int tok = t0 + tl;
     if (tok < a.T) {
@@ -376,25 +408,26 @@ decide(Lrow, N, k, kk, a.renorm, tau, q, sIdx[tl], sGate[tl], &sThr[tl], &sMax[t
   }
 }
 
-size_t route_lds_bytes(int N) {
+template <int BT>
+static size_t route_lds_bytes(int N) {
   const int NB = (N + 15) >> 4;
-  const size_t logits = size_t(RT_BT) * (NB * 16 + 4) * sizeof(float);
-  const size_t tiles = size_t(2) * RT_BT * RT_XLD * sizeof(uint16_t);
+  const size_t logits = size_t(BT) * (NB * 16 + 4) * sizeof(float);
+  const size_t tiles = size_t(2) * BT * RT_XLD * sizeof(uint16_t);
   return logits > tiles ? logits : tiles;
 }
 
-hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
-  if (a.T <= 0) return hipSuccess;
-  const int grid = (a.T + RT_BT - 1) / RT_BT;
-  const size_t lds = route_lds_bytes(a.N);
+template <int BT>
+static hipError_t launch_route_bt(const RouteArgs& a, int act, hipStream_t s) {
+  const int grid = (a.T + BT - 1) / BT;
+  const size_t lds = route_lds_bytes<BT>(a.N);
   static int attr_done[64] = {0};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  auto kb = route_kernel<ACT_BF16>;
-  auto kf = route_kernel<ACT_F32>;
+  auto kb = route_kernel<ACT_BF16, BT>;
+  auto kf = route_kernel<ACT_F32, BT>;
   if (dev < 0 || dev >= 64 || !attr_done[dev]) {
-    const int mx = int(route_lds_bytes(256));
+    const int mx = int(route_lds_bytes<BT>(256));
     err = hipFuncSetAttribute((const void*)kb, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
     if (err == hipSuccess) err = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
     if (err != hipSuccess) return err;
@@ -405,6 +438,13 @@ hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
   else
     hipLaunchKernelGGL(kf, dim3(grid), dim3(RT_THREADS), lds, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  // 64-token tiles once they give every CU a workgroup, 16-token tiles below
+  if (a.T >= 64 * 256) return launch_route_bt<64>(a, act, s);
+  return launch_route_bt<16>(a, act, s);
 }
 
 // ------------------------------------------------------------------ bucketing
