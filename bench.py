@@ -85,6 +85,9 @@ def kernel_work(cfg):
 
     if f == 0:
         w["gemm"] = gemm(d, d)
+        fb = 2 * R * d * s + 2 * ang_d + d * d // 4 + 8 * R
+        ff = 2 * R * d * d + 2 * 6 * R * (d // 2) * Ld
+        w["fused"] = (fb, ff, "mfma" if ff / fb > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm")
     else:
         Lf = int(math.log2(f))
         w["gemm_up"] = gemm(d, f)

@@ -112,11 +112,17 @@ bmoe_status check_layer(const bmoe_layer* L) {
 
 // Workspace layout (offsets in bytes, each 256-byte aligned).
 struct Plan {
-  size_t offsets, perm, idx, gate, bufU, bufZ, total;
+  size_t offsets, perm, idx, gate, bufU, bufZ, wbytes, total;
+  bool fused;
   int64_t R;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Square bf16 layers of width <= 512 run rotations and substrate product in one kernel.
+bool use_fused(const bmoe_layer* L) {
+  return L->act_dtype == BMOE_BF16 && L->d_ff == 0 && fused_square_supported(ilog2(L->d_model));
+}
 
 Plan make_plan(const bmoe_layer* L, int32_t T) {
   Plan p{};
@@ -133,8 +139,10 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.perm = take(size_t(R) * 4);
   p.idx = take(size_t(R) * 4);
   p.gate = take(size_t(R) * 4);
+  p.fused = use_fused(L);
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
-  p.bufZ = take(size_t(R) * (f > d ? f : d) * s);    // Z / H / A, then per-slot Y (FFN)
+  p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
+  p.wbytes = take(p.fused ? size_t(d) * d : 0);      // substrate, one byte per weight
   p.total = o;
   p.R = R;
   return p;
@@ -174,7 +182,8 @@ bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* id
   const int act = L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
   RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates};
   BMOE_HIP(launch_route(ra, act, s));
-  BucketArgs ba{idx, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts};
+  BucketArgs ba{idx, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts,
+                nullptr, nullptr, 0};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -256,6 +265,11 @@ static int forward_kernel_names(const bmoe_layer* L, const char** names) {
   int n = 0;
   names[n++] = "route";
   names[n++] = "bucket";
+  if (use_fused(L)) {
+    names[n++] = "fused";
+    if (L->top_k > 1) names[n++] = "combine";
+    return n;
+  }
   names[n++] = "bfly_in";
   if (L->d_ff == 0) {
     names[n++] = "gemm";
@@ -321,8 +335,22 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   // router and bucketing
   RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates};
   BMOE_LAUNCH(launch_route(ra, act, stream));
-  BucketArgs ba{idx, offsets, perm, R, N};
+  const bool fused = p.fused;
+  unsigned char* wbytes = fused ? at<unsigned char>(workspace, p.wbytes) : nullptr;
+  BucketArgs ba{idx, offsets, perm, R, N, fused ? layer->w_base[0] : nullptr, wbytes,
+                fused ? int32_t(int64_t(d) * d / 16) : 0};
   BMOE_LAUNCH(launch_bucket(ba, stream));
+  if (fused) {
+    void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);
+    FusedArgs fa{x, yslot_f, layer->theta[0], layer->phi[0], wbytes, offsets, perm, gate,
+                 layer->w_scale[0], R, N, k};
+    BMOE_LAUNCH(launch_fused_square(fa, ilog2(d), stream));
+    if (k > 1) {
+      CombineArgs c{yslot_f, y, T, d, k};
+      BMOE_LAUNCH(launch_combine(c, act, stream));
+    }
+    return ok();
+  }
   // input rotation: U[q] = B(theta_e)^T x_t
   BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
   BMOE_LAUNCH(launch_butterfly(bi, BFLY_IN, act, Ld, stream));

@@ -114,8 +114,9 @@ __device__ __forceinline__ void rotate_group(float* v, const float2* cs) {
   }
 }
 
-// One pass (stages 3P .. 3P+M-1) over rows [0, nr) of the tile.
-template <int L, int P, bool TRANS, bool POST_GELU>
+// One pass (stages 3P .. 3P+M-1) over rows [0, nr) of the tile.  TMODE picks
+// where (cos, sin) come from (default: the width's own table mode).
+template <int L, int P, bool TRANS, bool POST_GELU, int TMODE = BflyCfg<L>::TM>
 __device__ __forceinline__ void bfly_pass(float* __restrict__ tile, int nr, const float2* __restrict__ tab,
                                           const float* __restrict__ ang) {
   using C = BflyCfg<L>;
@@ -135,8 +136,8 @@ __device__ __forceinline__ void bfly_pass(float* __restrict__ tile, int nr, cons
     const int g = gsub + gi * BF_THREADS;
     const int base = group_base(g, S0, M);
     float2 cs[NCS];
-    if constexpr (C::TM != TAB_NONE) {
-      const float2* t = tab + (C::TM == TAB_FULL ? S0 * C::half : 0) + g * NCS;
+    if constexpr (TMODE != TAB_NONE) {
+      const float2* t = tab + (TMODE == TAB_FULL ? S0 * C::half : 0) + g * NCS;
       if constexpr ((NCS % 2) == 0) {
 #pragma unroll
         for (int j = 0; j < NCS / 2; ++j) {
@@ -210,13 +211,13 @@ __device__ __forceinline__ void fill_full_table(float2* tab, const float* __rest
 }
 
 // Angles of one butterfly held in registers (one-pass-table mode).
-template <int L>
+template <int L, int TMODE = BflyCfg<L>::TM>
 struct AngleRegs {
-  float a[BflyCfg<L>::TM == TAB_PASS ? (L * BflyCfg<L>::half + BF_THREADS - 1) / BF_THREADS : 1];
+  float a[TMODE == TAB_PASS ? (L * BflyCfg<L>::half + BF_THREADS - 1) / BF_THREADS : 1];
 };
 
-template <int L>
-__device__ __forceinline__ void load_angle_regs(AngleRegs<L>& R, const float* __restrict__ ang) {
+template <int L, int TMODE>
+__device__ __forceinline__ void load_angle_regs(AngleRegs<L, TMODE>& R, const float* __restrict__ ang) {
   constexpr int TOTAL = L * BflyCfg<L>::half;
   constexpr int PER = (TOTAL + BF_THREADS - 1) / BF_THREADS;
 #pragma unroll
@@ -226,8 +227,8 @@ __device__ __forceinline__ void load_angle_regs(AngleRegs<L>& R, const float* __
   }
 }
 
-template <int L>
-__device__ __forceinline__ void fill_pass_table(float2* tab, const AngleRegs<L>& R, int P) {
+template <int L, int TMODE>
+__device__ __forceinline__ void fill_pass_table(float2* tab, const AngleRegs<L, TMODE>& R, int P) {
   constexpr int TOTAL = L * BflyCfg<L>::half;
   constexpr int PER = (TOTAL + BF_THREADS - 1) / BF_THREADS;
   const int s_lo = 3 * P, s_hi = min(3 * P + 3, L);
@@ -241,19 +242,19 @@ __device__ __forceinline__ void fill_pass_table(float2* tab, const AngleRegs<L>&
 }
 
 // Passes T = 0 .. NP-1 of one butterfly (forward: P = T; transposed: P = NP-1-T).
-template <int L, bool TRANS, bool GELU_LAST, int T = 0>
+template <int L, bool TRANS, bool GELU_LAST, int T = 0, int TMODE = BflyCfg<L>::TM>
 __device__ __forceinline__ void run_passes(float* tile, int nr, float2* tab, const float* ang,
-                                           const AngleRegs<L>& R) {
+                                           const AngleRegs<L, TMODE>& R) {
   using C = BflyCfg<L>;
   if constexpr (T < C::NP) {
     constexpr int P = TRANS ? C::NP - 1 - T : T;
-    if constexpr (C::TM == TAB_PASS) {
-      fill_pass_table<L>(tab, R, P);
+    if constexpr (TMODE == TAB_PASS) {
+      fill_pass_table<L, TMODE>(tab, R, P);
       __syncthreads();
     }
-    bfly_pass<L, P, TRANS, GELU_LAST && (T == C::NP - 1)>(tile, nr, tab, ang);
+    bfly_pass<L, P, TRANS, GELU_LAST && (T == C::NP - 1), TMODE>(tile, nr, tab, ang);
     __syncthreads();
-    run_passes<L, TRANS, GELU_LAST, T + 1>(tile, nr, tab, ang, R);
+    run_passes<L, TRANS, GELU_LAST, T + 1, TMODE>(tile, nr, tab, ang, R);
   }
 }
 

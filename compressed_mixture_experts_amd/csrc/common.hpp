@@ -100,6 +100,22 @@ struct BucketArgs {
   int32_t* offsets;         // [N+1]
   int32_t* perm;            // [R] bucket position -> flat slot
   int32_t R, N;
+  const uint32_t* w_packed; // optional: 2-bit substrate words to unpack
+  unsigned char* w_bytes;   //   into one byte per weight (bf16 high byte)
+  int32_t w_words;          //   number of words (0: nothing to unpack)
+};
+
+struct FusedArgs {
+  const void* x;            // [T][d] bf16
+  void* out;                // per-slot rows [R][d] (or y when k == 1)
+  const float* theta;       // [N][L][d/2]
+  const float* phi;         // [N][L][d/2]
+  const unsigned char* wb;  // [d][d] substrate bytes (bf16 high byte: +-0.5 / 0)
+  const int32_t* offsets;   // [N+1]
+  const int32_t* perm;      // [R]
+  const float* gate;        // [R]
+  float alpha;              // substrate scale
+  int32_t rows, n_experts, top_k;
 };
 
 enum BflyMode { BFLY_DBG = 0, BFLY_IN = 1, BFLY_MID = 2, BFLY_OUT = 3 };
@@ -138,6 +154,8 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
+bool fused_square_supported(int log2n);
+hipError_t launch_fused_square(const FusedArgs& a, int log2n, hipStream_t s);
 
 
 }  // namespace bmoe

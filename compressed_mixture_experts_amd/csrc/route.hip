@@ -459,6 +459,25 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  // optional: unpack the 2-bit substrate into one byte per weight holding the
+  // high byte of its bf16 value scaled by 1/2 (+1 -> 0x3F, -1 -> 0xBF, 0 -> 0)
+  for (int w = e * BK_THREADS + tid; w < a.w_words; w += gridDim.x * BK_THREADS) {
+    const uint32_t P = a.w_packed[w];
+    uint32_t out[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c = 4 * q + b, j = c >> 1, h = c & 1;
+        const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = (P >> (16 * h + 8 + j)) & 1u;
+        v |= (nz * (0x3Fu | (sg << 7))) << (8 * b);
+      }
+      out[q] = v;
+    }
+    reinterpret_cast<uint4*>(a.w_bytes)[w] = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+
   auto load4 = [&](int f0) -> int4 {
     if (f0 + 3 < a.R) return *reinterpret_cast<const int4*>(a.topk_idx + f0);
     int4 q;

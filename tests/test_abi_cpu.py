@@ -136,9 +136,13 @@ def test_workspace_size_monotone_and_layout():
         st, n = ws_size(s, T)
         assert st == 0 and n > prev
         prev = n
-    # dominated by two [T*k][d] bf16 row buffers
+    # square bf16 layer of width 512 (single fused expert kernel): one [T*k][d]
+    # bf16 row buffer plus the substrate at one byte per weight
     st, n = ws_size(s, 4096)
-    assert n >= 2 * 4096 * 2 * 512 * 2
+    assert n >= 4096 * 2 * 512 * 2 + 512 * 512
+    # fp32 square layer (separate kernels): two [T*k][d] row buffers
+    st, n32 = ws_size(make_struct(act_dtype=bm.F32), 4096)
+    assert st == 0 and n32 >= 2 * 4096 * 2 * 512 * 4
     sf = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
     st, nf = ws_size(sf, 8192)
     assert st == 0 and nf >= 8192 * 2 * (1024 + 4096) * 2
