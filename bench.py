@@ -85,8 +85,18 @@ def kernel_work(cfg):
 
     if f == 0:
         w["gemm"] = gemm(d, d)
-        fb = 2 * R * d * s + 2 * ang_d + d * d // 4 + 8 * R
-        ff = 2 * R * d * d + 2 * 6 * R * (d // 2) * Ld
+        if cfg.act == "bf16" and Ld in (8, 9):
+            # rotations as block factors on the matrix cores: per rotation one
+            # P x P and one 16 x 16 product per 32-wide / 16-wide block of a row
+            P = 32 if Ld == 9 else 16
+            fac = N * 2 * (P * 64 * 4 * 2 + 16 * (P // 16) * 64 * (P // 4) * 2)
+            w["bucket"] = (w["bucket"][0] + d * d // 4 + d * d, 0, "hbm")
+            w["factors"] = (2 * ang_d + fac, 0, "hbm")
+            fb = 2 * R * d * s + fac + d * d + 8 * R
+            ff = 2 * R * d * d + 2 * 2 * R * d * (P + 16)
+        else:
+            fb = 2 * R * d * s + 2 * ang_d + d * d // 4 + 8 * R
+            ff = 2 * R * d * d + 2 * 6 * R * (d // 2) * Ld
         w["fused"] = (fb, ff, "mfma" if ff / fb > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm")
     else:
         Lf = int(math.log2(f))
@@ -272,7 +282,8 @@ def bm_kernel_sha(kernel: str) -> str:
     """Hash of the HIP source that holds `kernel` (to invalidate stale counters)."""
     import hashlib
     src = {"gemm": "gemm.hip", "gemm_up": "gemm.hip", "gemm_down": "gemm.hip", "combine": "gemm.hip",
-           "route": "route.hip", "bucket": "route.hip"}.get(kernel, "butterfly.hip")
+           "route": "route.hip", "bucket": "route.hip", "factors": "fused_mfma.hip",
+           "fused": "fused_mfma.hip"}.get(kernel, "butterfly.hip")
     p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 

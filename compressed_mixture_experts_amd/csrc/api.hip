@@ -112,8 +112,8 @@ bmoe_status check_layer(const bmoe_layer* L) {
 
 // Workspace layout (offsets in bytes, each 256-byte aligned).
 struct Plan {
-  size_t offsets, perm, idx, gate, bufU, bufZ, wbytes, total;
-  bool fused;
+  size_t offsets, perm, idx, gate, bufU, bufZ, wbytes, fac, total;
+  bool fused, mfma;
   int64_t R;
 };
 
@@ -121,8 +121,11 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Square bf16 layers of width <= 512 run rotations and substrate product in one kernel.
 bool use_fused(const bmoe_layer* L) {
-  return L->act_dtype == BMOE_BF16 && L->d_ff == 0 && fused_square_supported(ilog2(L->d_model));
+  return L->act_dtype == BMOE_BF16 && L->d_ff == 0 &&
+         (fused_square_supported(ilog2(L->d_model)) || fused_mfma_supported(ilog2(L->d_model)));
 }
+// ... with the rotations as block factors on the matrix cores (widths 256, 512)
+bool use_fused_mfma(const bmoe_layer* L) { return use_fused(L) && fused_mfma_supported(ilog2(L->d_model)); }
 
 Plan make_plan(const bmoe_layer* L, int32_t T) {
   Plan p{};
@@ -143,6 +146,8 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
   p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
   p.wbytes = take(p.fused ? size_t(d) * d : 0);      // substrate, one byte per weight
+  p.mfma = use_fused_mfma(L);
+  p.fac = take(p.mfma ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(d)) : 0);
   p.total = o;
   p.R = R;
   return p;
@@ -266,6 +271,7 @@ static int forward_kernel_names(const bmoe_layer* L, const char** names) {
   names[n++] = "route";
   names[n++] = "bucket";
   if (use_fused(L)) {
+    if (use_fused_mfma(L)) names[n++] = "factors";
     names[n++] = "fused";
     if (L->top_k > 1) names[n++] = "combine";
     return n;
@@ -342,9 +348,16 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
     void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);
-    FusedArgs fa{x, yslot_f, layer->theta[0], layer->phi[0], wbytes, offsets, perm, gate,
+    unsigned char* fac = p.mfma ? at<unsigned char>(workspace, p.fac) : nullptr;
+    FusedArgs fa{x, yslot_f, layer->theta[0], layer->phi[0], wbytes, fac, offsets, perm, gate,
                  layer->w_scale[0], R, N, k};
-    BMOE_LAUNCH(launch_fused_square(fa, ilog2(d), stream));
+    if (p.mfma) {
+      FactorArgs fc{layer->theta[0], layer->phi[0], fac, N};
+      BMOE_LAUNCH(launch_factors(fc, ilog2(d), stream));
+      BMOE_LAUNCH(launch_fused_mfma(fa, ilog2(d), stream));
+    } else {
+      BMOE_LAUNCH(launch_fused_square(fa, ilog2(d), stream));
+    }
     if (k > 1) {
       CombineArgs c{yslot_f, y, T, d, k};
       BMOE_LAUNCH(launch_combine(c, act, stream));

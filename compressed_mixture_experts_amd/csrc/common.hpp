@@ -111,6 +111,7 @@ struct FusedArgs {
   const float* theta;       // [N][L][d/2]
   const float* phi;         // [N][L][d/2]
   const unsigned char* wb;  // [d][d] substrate bytes (bf16 high byte: +-0.5 / 0)
+  const unsigned char* fac; // per-expert rotation block factors (matrix-core path)
   const int32_t* offsets;   // [N+1]
   const int32_t* perm;      // [R]
   const float* gate;        // [R]
@@ -154,7 +155,18 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
+struct FactorArgs {
+  const float* theta;       // [N][L][n/2]
+  const float* phi;         // [N][L][n/2]
+  unsigned char* fac;       // [N][factor_bytes_per_expert]
+  int32_t n_experts;
+};
+
 bool fused_square_supported(int log2n);
+bool fused_mfma_supported(int log2n);
+size_t factor_bytes_per_expert(int log2n);
+hipError_t launch_factors(const FactorArgs& a, int log2n, hipStream_t s);
+hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s);
 hipError_t launch_fused_square(const FusedArgs& a, int log2n, hipStream_t s);
 
 

@@ -1,0 +1,509 @@
+// Square-expert step with every product on the matrix cores (ButterflyMoE,
+// gist.science/zh/paper/2601.13563, technical summary §2.1 and §2.2: the expert
+// B(phi) W_base B(theta)^T is applied as input rotation, ternary substrate
+// product and output rotation, never formed).
+//
+// Rotations as two block-diagonal factors.  For width n = 2^L write an index as
+// i = p + P m with p < P = 2^LA (LA = 5 at width 512, 4 at width 256) and
+// m < 16.  Stages 0 .. LA-1 only mix indices of equal m, stages LA .. L-1 only
+// indices of equal p, so
+//     B = G_B G_A,   G_A = diag over m of A_m (P x P),   G_B = diag over p of B_p (16 x 16),
+// each block the product of its stages' Givens rotations.  A tile of 32 rows
+// then needs 16 + P small dense products per rotation, done on MFMA in bf16
+// with fp32 accumulation, instead of (n/2) L scalar rotations per row.
+//
+// factor_kernel builds, per expert, the blocks in the exact per-lane order of
+// the MFMA operands (bf16): the transposed blocks of theta (input rotation
+// B(theta)^T = G_A^T G_B^T) and the blocks of phi (output rotation G_B G_A).
+//
+// fused_mfma_kernel, one workgroup (4 waves) per tile of 32 bucketed rows of one
+// expert.  Two bf16 LDS buffers of 32 rows alternate:
+//   gather   x rows -> buf0 as [row][p][m]                 (transposed per row)
+//   G_B^T    wave (tb, h): token block tb, classes p of half h   -> buf1 [row][m][p]
+//   G_A^T    wave (tb, h): blocks m of half h                    -> buf0 [row][i]  (= U)
+//   W        wave w: outputs [w n/4, (w+1) n/4) of all rows, accumulators kept
+//   G_A      on the accumulators of the wave's own blocks        -> buf1 [row][p][m]
+//   G_B      wave (tb, h): classes p of half h, * gate * 2 alpha -> buf0 [row][i]
+//   store    buf0 rows -> per-slot rows
+// LDS is 2 x 32 rows (~66 KiB), so two workgroups share a CU.
+#include "common.hpp"
+
+namespace bmoe {
+
+constexpr int FM_RT = 32;        // rows per tile
+constexpr int FM_THREADS = 256;  // four waves
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+template <int L>
+struct MfCfg {
+  static constexpr int n = 1 << L;
+  static constexpr int LA = L == 9 ? 5 : 4;    // stages in G_A
+  static constexpr int PA = 1 << LA;           // G_A block width
+  static constexpr int NM = n / PA;            // G_A blocks = G_B block width
+  static constexpr int NP = PA;                // G_B blocks (classes)
+  static constexpr int HA = PA / 16;           // 16-row halves of a G_A block
+  static constexpr int KA = PA / 4;            // contraction values per lane in a G_A MFMA
+  static constexpr int TS = 2 * n + 16;        // LDS row stride in bytes
+  static constexpr size_t buf_bytes = size_t(FM_RT) * TS;
+  static constexpr size_t lds_bytes = 2 * buf_bytes;
+  static constexpr size_t gb_bytes = size_t(NP) * 64 * 4 * 2;        // one G_B set
+  static constexpr size_t ga_bytes = size_t(NM) * HA * 64 * KA * 2;  // one G_A set
+  // per expert: [G_B^T(theta) | G_A^T(theta) | G_A(phi) | G_B(phi)]
+  static constexpr size_t off_bt = 0, off_at = gb_bytes, off_ap = gb_bytes + ga_bytes,
+                          off_bp = gb_bytes + 2 * ga_bytes;
+  static constexpr size_t per_expert = 2 * (gb_bytes + ga_bytes);
+  static_assert(NM == 16, "G_B blocks are 16 wide");
+};
+
+size_t factor_bytes_per_expert(int log2n) {
+  switch (log2n) {
+    case 8: return MfCfg<8>::per_expert;
+    case 9: return MfCfg<9>::per_expert;
+    default: return 0;
+  }
+}
+
+__device__ __forceinline__ int stage_pair_index(int i, int s) {
+  return ((i >> (s + 1)) << s) | (i & ((1 << s) - 1));
+}
+
+// Apply stages [S_LO, S_HI) (local bit = s - S_LO) to a W-vector whose entry b
+// sits at global index base + stride * b.  FWD: stages in increasing order with
+// [[c, -s], [s, c]]; otherwise decreasing order with the transposed rotation.
+template <int W, int S_LO, int S_HI, bool FWD>
+__device__ __forceinline__ void rotate_vec(float (&v)[W], const float2* cs, int half, int base, int stride) {
+#pragma unroll
+  for (int k = 0; k < S_HI - S_LO; ++k) {
+    const int s = FWD ? S_LO + k : S_HI - 1 - k;
+    const int sl = s - S_LO;
+#pragma unroll
+    for (int q = 0; q < W / 2; ++q) {
+      const int b = ((q >> sl) << (sl + 1)) | (q & ((1 << sl) - 1));
+      const int i = base + stride * b;
+      const float2 r = cs[s * half + stage_pair_index(i, s)];
+      const float x = v[b], y = v[b + (1 << sl)];
+      if (FWD) {
+        v[b] = r.x * x - r.y * y;
+        v[b + (1 << sl)] = r.y * x + r.x * y;
+      } else {
+        v[b] = r.x * x + r.y * y;
+        v[b + (1 << sl)] = r.x * y - r.y * x;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// grid (N, 2): blockIdx.y = 0 builds the theta set, 1 the phi set.
+template <int L>
+__global__ __launch_bounds__(FM_THREADS) void factor_kernel(FactorArgs a) {
+  using C = MfCfg<L>;
+  constexpr int n = C::n, half = n / 2, PA = C::PA, KA = C::KA, HA = C::HA;
+  __shared__ float2 cs[L * half];
+  const int e = blockIdx.x;
+  const bool th = blockIdx.y == 0;
+  const float* ang = (th ? a.theta : a.phi) + size_t(e) * L * half;
+  for (int i = threadIdx.x; i < L * half; i += FM_THREADS) {
+    float sn, c;
+    sincosf(ang[i], &sn, &c);
+    cs[i] = make_float2(c, sn);
+  }
+  __syncthreads();
+  unsigned char* fe = a.fac + size_t(e) * C::per_expert;
+
+  // G_A: theta -> column j of A_m (operand row j of A_m^T); phi -> row j of A_m
+  for (int job = threadIdx.x; job < C::NM * PA; job += FM_THREADS) {
+    const int m = job / PA, j = job % PA;
+    float v[PA];
+#pragma unroll
+    for (int q = 0; q < PA; ++q) v[q] = q == j ? 1.0f : 0.0f;
+    if (th) rotate_vec<PA, 0, C::LA, true>(v, cs, half, PA * m, 1);
+    else rotate_vec<PA, 0, C::LA, false>(v, cs, half, PA * m, 1);
+    const int hq = j / 16, row = j % 16;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint16_t h[KA];
+#pragma unroll
+      for (int i = 0; i < KA; ++i) {
+        // contraction index held by lane group g, slot i: 4g+i (PA 16);
+        // theta: 8g+i; phi (accumulator order of the substrate product): 4g+i, then 16+4g+i
+        const int k = KA == 4 ? 4 * g + i : th ? 8 * g + i : (i < 4 ? 4 * g + i : 12 + 4 * g + i);
+        h[i] = bf16_bits(v[k]);
+      }
+      uint16_t* dst = reinterpret_cast<uint16_t*>(fe + (th ? C::off_at : C::off_ap)) +
+                      ((size_t(m) * HA + hq) * 64 + 16 * g + row) * KA;
+#pragma unroll
+      for (int i = 0; i < KA; ++i) dst[i] = h[i];
+    }
+  }
+  // G_B: theta -> column j of B_p (operand row j of B_p^T); phi -> row j of B_p
+  for (int job = threadIdx.x; job < C::NP * 16; job += FM_THREADS) {
+    const int p = job / 16, j = job % 16;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = q == j ? 1.0f : 0.0f;
+    if (th) rotate_vec<16, C::LA, L, true>(v, cs, half, p, PA);
+    else rotate_vec<16, C::LA, L, false>(v, cs, half, p, PA);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(fe + (th ? C::off_bt : C::off_bp)) +
+                      (size_t(p) * 64 + 16 * g + j) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = bf16_bits(v[4 * g + i]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// four substrate bytes (weights k..k+3) -> two bf16 pairs (low bytes zero)
+__device__ __forceinline__ void wb_to_bf16(uint32_t w, uint32_t& p0, uint32_t& p1) {
+  p0 = __builtin_amdgcn_perm(0u, w, 0x010C000Cu);
+  p1 = __builtin_amdgcn_perm(0u, w, 0x030C020Cu);
+}
+
+__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int KA> struct AFragT { using type = uint2; };
+template <> struct AFragT<8> { using type = uint4; };
+
+// exclusive scan over the 256 threads; `total` gets the sum
+__device__ __forceinline__ int fm_block_scan(int v, int* s_tmp, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_tmp[w] = x;
+  __syncthreads();
+  int pre = 0;
+  for (int i = 0; i < w; ++i) pre += s_tmp[i];
+  total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  return pre + x - v;
+}
+
+template <int L>
+__global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) {
+  using C = MfCfg<L>;
+  using AF = typename AFragT<C::KA>::type;
+  constexpr int n = C::n, PA = C::PA, NP = C::NP, HA = C::HA, TS = C::TS;
+  constexpr int OB = n / 64;          // substrate: 16-output blocks per wave
+  constexpr int DS = n / 64;          // substrate: double steps of 64 contraction indices
+  constexpr int PF = DS < 2 ? DS : 2; // double steps of W in flight
+  constexpr int NCW = NP / 2;         // G_B classes per wave
+  constexpr int NBW = (n / 4) / PA;   // G_A blocks inside one wave's substrate outputs
+  static_assert(NBW == 4 && NCW % 4 == 0 && DS % PF == 0, "tile shape");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* buf0 = lds;
+  unsigned char* buf1 = lds + C::buf_bytes;
+  __shared__ int s_info[3];
+  __shared__ int s_tmp[4];
+  __shared__ size_t s_src[FM_RT], s_dst[FM_RT];
+  __shared__ float s_gate[FM_RT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int tb = wave >> 1, hh = wave & 1;
+
+  // ---- tile of one expert
+  if (tid == 0) s_info[0] = -1;
+  {
+    int nt = 0, cnt = 0, off = 0;
+    if (tid < a.n_experts) {
+      off = a.offsets[tid];
+      cnt = a.offsets[tid + 1] - off;
+      nt = (cnt + FM_RT - 1) / FM_RT;
+    }
+    int total;
+    const int excl = fm_block_scan(nt, s_tmp, total);
+    if (tid < a.n_experts && int(blockIdx.x) >= excl && int(blockIdx.x) < excl + nt) {
+      const int j = blockIdx.x - excl;
+      s_info[0] = tid;
+      s_info[1] = off + j * FM_RT;
+      s_info[2] = min(FM_RT, cnt - j * FM_RT);
+    }
+  }
+  __syncthreads();
+  const int e = s_info[0];
+  if (e < 0) return;
+  const int r0 = s_info[1], nr = s_info[2];
+  if (tid < nr) {
+    const int slot = a.perm[r0 + tid];
+    s_src[tid] = size_t(slot / a.top_k) * n;
+    s_dst[tid] = size_t(slot) * n;
+    s_gate[tid] = a.gate[slot] * 2.0f * a.alpha;
+  }
+
+  // ---- input-rotation factor fragments of this expert
+  const unsigned char* fe = a.fac + size_t(e) * C::per_expert;
+  uint2 fbt[NCW];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c)
+    fbt[c] = *reinterpret_cast<const uint2*>(fe + C::off_bt + (size_t(hh * NCW + c) * 64 + lane) * 8);
+  __syncthreads();
+
+  // ---- gather x rows into buf0 as [row][p][m]: item (row, m-quad, 8 p's)
+  constexpr int PG = PA / 8;
+  constexpr int ITEMS = FM_RT * 4 * PG;
+  constexpr int IPT = ITEMS / FM_THREADS;
+  static_assert(ITEMS % FM_THREADS == 0, "gather items");
+  const unsigned char* wrow = a.wb + size_t(wave * (n / 4) + l16) * n + 16 * g;
+  uint4 W[PF][OB];
+  {
+    uint4 ch[IPT][4];
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = it * FM_THREADS + tid;
+      const int pg = item % PG, mq = (item / PG) % 4, t = item / (PG * 4);
+      if (t < nr) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.x) + s_src[t] + 8 * pg;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          ch[it][mi] = *reinterpret_cast<const uint4*>(src + PA * (4 * mq + mi));
+      }
+    }
+    // substrate prefetch, after the gather loads
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+      for (int i = 0; i < OB; ++i)
+        W[u][i] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * n + 64 * u);
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = it * FM_THREADS + tid;
+      const int pg = item % PG, mq = (item / PG) % 4, t = item / (PG * 4);
+      if (t < nr) {
+        unsigned char* dst = buf0 + t * TS + ((8 * pg) * 16 + 4 * mq) * 2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t lo = __builtin_amdgcn_perm(u4get(ch[it][1], j >> 1), u4get(ch[it][0], j >> 1), sel);
+          const uint32_t hi = __builtin_amdgcn_perm(u4get(ch[it][3], j >> 1), u4get(ch[it][2], j >> 1), sel);
+          *reinterpret_cast<uint2*>(dst + j * 32) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+  AF fat[8][HA];  // second input-rotation factor, used after the next barrier
+#pragma unroll
+  for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+    for (int hq = 0; hq < HA; ++hq)
+      fat[jb][hq] = *reinterpret_cast<const AF*>(
+          fe + C::off_at + ((size_t(8 * hh + jb) * HA + hq) * 64 + lane) * sizeof(AF));
+  __syncthreads();
+
+  const int trow = 16 * tb + l16;  // this lane's row in the butterfly phases
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- G_B^T (theta): classes hh*NCW .. +NCW of token block tb  -> buf1 [row][m][p]
+  {
+    const unsigned char* xr = buf0 + trow * TS;
+    unsigned char* yr = buf1 + trow * TS;
+#pragma unroll
+    for (int cg = 0; cg < NCW / 4; ++cg) {
+      f32x4_t d[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = hh * NCW + 4 * cg + c;
+        const uint2 b = *reinterpret_cast<const uint2*>(xr + (p * 16 + 4 * g) * 2);
+        d[c] = mfma16(fbt[4 * cg + c], b, zero4);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint2*>(yr + ((4 * g + i) * PA + hh * NCW + 4 * cg) * 2) =
+            make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i]));
+    }
+  }
+  __syncthreads();
+
+  // ---- G_A^T (theta): blocks 8hh .. 8hh+7 of token block tb  -> buf0 [row][i] (U)
+  {
+    const unsigned char* yr = buf1 + trow * TS;
+    unsigned char* ur = buf0 + trow * TS;
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      const int mb = 8 * hh + jb;
+#pragma unroll
+      for (int hq = 0; hq < HA; ++hq) {
+        f32x4_t d;
+        if constexpr (C::KA == 8) {
+          const uint4 b = *reinterpret_cast<const uint4*>(yr + (mb * PA + 8 * g) * 2);
+          d = mfma32(fat[jb][hq], b, zero4);
+        } else {
+          const uint2 b = *reinterpret_cast<const uint2*>(yr + (mb * PA + 4 * g) * 2);
+          d = mfma16(fat[jb][hq], b, zero4);
+        }
+        *reinterpret_cast<uint2*>(ur + (PA * mb + 16 * hq + 4 * g) * 2) =
+            make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- first output-rotation factor (in flight during the substrate product)
+  AF fa[NBW][HA];
+#pragma unroll
+  for (int jm = 0; jm < NBW; ++jm)
+#pragma unroll
+    for (int hq = 0; hq < HA; ++hq)
+      fa[jm][hq] = *reinterpret_cast<const AF*>(
+          fe + C::off_ap + ((size_t(NBW * wave + jm) * HA + hq) * 64 + lane) * sizeof(AF));
+
+  // ---- Z = U W^T: wave owns outputs [wave n/4, (wave+1) n/4) of all 32 rows.
+  // Double step u: lanes 16g.. hold the 16 weights k = 64u + 16g .. +15 of their
+  // output row (first 8 -> first MFMA, last 8 -> second); U follows that order.
+  f32x4_t acc[OB][2];
+#pragma unroll
+  for (int i = 0; i < OB; ++i) acc[i][0] = acc[i][1] = zero4;
+  const uint16_t* urow = reinterpret_cast<const uint16_t*>(buf0) + l16 * (TS / 2) + 16 * g;
+#pragma unroll 1
+  for (int u0 = 0; u0 < DS; u0 += PF) {
+#pragma unroll
+    for (int pq = 0; pq < PF; ++pq) {
+      const int u = u0 + pq;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4 uf[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          uf[j] = *reinterpret_cast<const uint4*>(urow + 16 * j * (TS / 2) + 64 * u + 8 * h);
+#pragma unroll
+        for (int i = 0; i < OB; ++i) {
+          uint4 wv;
+          wb_to_bf16(h ? W[pq][i].z : W[pq][i].x, wv.x, wv.y);
+          wb_to_bf16(h ? W[pq][i].w : W[pq][i].y, wv.z, wv.w);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wv, uf[j], acc[i][j]);
+        }
+      }
+      if (u + PF < DS) {
+#pragma unroll
+        for (int i = 0; i < OB; ++i)
+          W[pq][i] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * n + 64 * (u + PF));
+      }
+    }
+  }
+
+  uint2 fb[NCW];  // last factor, used after the next barrier
+#pragma unroll
+  for (int c = 0; c < NCW; ++c)
+    fb[c] = *reinterpret_cast<const uint2*>(fe + C::off_bp + (size_t(hh * NCW + c) * 64 + lane) * 8);
+
+  // ---- G_A (phi) on the accumulators: blocks NBW*wave .. +3  -> buf1 [row][p][m]
+  // (buf1 was last read before the barrier above; buf0 still holds U for the
+  // other waves, so it is not touched here)
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    f32x4_t d[NBW][HA];
+#pragma unroll
+    for (int jm = 0; jm < NBW; ++jm) {
+      if constexpr (C::KA == 8) {
+        const f32x4_t z0 = acc[2 * jm][rb], z1 = acc[2 * jm + 1][rb];
+        const uint4 b = make_uint4(pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]),
+                                   pack_bf16x2(z1[0], z1[1]), pack_bf16x2(z1[2], z1[3]));
+#pragma unroll
+        for (int hq = 0; hq < HA; ++hq) d[jm][hq] = mfma32(fa[jm][hq], b, zero4);
+      } else {
+        const f32x4_t z0 = acc[jm][rb];
+        const uint2 b = make_uint2(pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]));
+        d[jm][0] = mfma16(fa[jm][0], b, zero4);
+      }
+    }
+    unsigned char* yr = buf1 + (16 * rb + l16) * TS;
+#pragma unroll
+    for (int hq = 0; hq < HA; ++hq)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = 16 * hq + 4 * g + i;
+        *reinterpret_cast<uint2*>(yr + (p * 16 + NBW * wave) * 2) =
+            make_uint2(pack_bf16x2(d[0][hq][i], d[1][hq][i]), pack_bf16x2(d[2][hq][i], d[3][hq][i]));
+      }
+  }
+  __syncthreads();
+
+  // ---- G_B (phi), * gate * 2 alpha: classes hh*NCW .. of token block tb -> buf0 [row][i]
+  {
+    const unsigned char* yr = buf1 + trow * TS;
+    unsigned char* orow = buf0 + trow * TS;
+    const float gs = s_gate[trow];
+#pragma unroll
+    for (int cg = 0; cg < NCW / 4; ++cg) {
+      f32x4_t d[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int p = hh * NCW + 4 * cg + c;
+        const uint2 b = *reinterpret_cast<const uint2*>(yr + (p * 16 + 4 * g) * 2);
+        d[c] = mfma16(fb[4 * cg + c], b, zero4);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint2*>(orow + (hh * NCW + 4 * cg + PA * (4 * g + i)) * 2) =
+            make_uint2(pack_bf16x2(gs * d[0][i], gs * d[1][i]), pack_bf16x2(gs * d[2][i], gs * d[3][i]));
+    }
+  }
+  __syncthreads();
+
+  // ---- per-slot rows
+  constexpr int CPR = n / 8;
+#pragma unroll
+  for (int c = tid; c < FM_RT * CPR; c += FM_THREADS) {
+    const int r = c / CPR;
+    if (r < nr)
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + s_dst[r] + 8 * (c % CPR)) =
+          *reinterpret_cast<const uint4*>(buf0 + r * TS + 16 * (c % CPR));
+  }
+}
+
+template <int L>
+static hipError_t launch_fused_mfma_L(const FusedArgs& a, hipStream_t s) {
+  using C = MfCfg<L>;
+  const int grid = (a.rows + FM_RT - 1) / FM_RT + a.n_experts;
+  auto k = fused_mfma_kernel<L>;
+  static int attr_done[64] = {0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (C::lds_bytes > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
+    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(C::lds_bytes));
+    if (err != hipSuccess) return err;
+    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
+  }
+  hipLaunchKernelGGL(k, dim3(grid), dim3(FM_THREADS), C::lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+bool fused_mfma_supported(int log2n) { return log2n == 8 || log2n == 9; }
+
+hipError_t launch_factors(const FactorArgs& a, int log2n, hipStream_t s) {
+  if (a.n_experts <= 0) return hipSuccess;
+  switch (log2n) {
+    case 8: hipLaunchKernelGGL(factor_kernel<8>, dim3(a.n_experts, 2), dim3(FM_THREADS), 0, s, a); break;
+    case 9: hipLaunchKernelGGL(factor_kernel<9>, dim3(a.n_experts, 2), dim3(FM_THREADS), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  switch (log2n) {
+    case 8: return launch_fused_mfma_L<8>(a, s);
+    case 9: return launch_fused_mfma_L<9>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bmoe
