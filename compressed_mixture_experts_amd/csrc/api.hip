@@ -145,8 +145,8 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.fused = use_fused(L);
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
   p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
-  p.wbytes = take(p.fused ? size_t(d) * d : 0);      // substrate, one byte per weight
   p.mfma = use_fused_mfma(L);
+  p.wbytes = take(p.fused ? size_t(d) * d / (p.mfma ? 2 : 1) : 0);  // substrate: byte or fp4 per weight
   p.fac = take(p.mfma ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(d)) : 0);
   p.total = o;
   p.R = R;
@@ -188,7 +188,7 @@ bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* id
   RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates};
   BMOE_HIP(launch_route(ra, act, s));
   BucketArgs ba{idx, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts,
-                nullptr, nullptr, 0};
+                nullptr, nullptr, 0, 0};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -344,7 +344,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   const bool fused = p.fused;
   unsigned char* wbytes = fused ? at<unsigned char>(workspace, p.wbytes) : nullptr;
   BucketArgs ba{idx, offsets, perm, R, N, fused ? layer->w_base[0] : nullptr, wbytes,
-                fused ? int32_t(int64_t(d) * d / 16) : 0};
+                fused ? int32_t(int64_t(d) * d / 16) : 0, p.mfma ? 1 : 0};
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
     void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);

@@ -100,9 +100,13 @@ struct BucketArgs {
   int32_t* offsets;         // [N+1]
   int32_t* perm;            // [R] bucket position -> flat slot
   int32_t R, N;
-  const uint32_t* w_packed; // optional: 2-bit substrate words to unpack
-  unsigned char* w_bytes;   //   into one byte per weight (bf16 high byte)
-  int32_t w_words;          //   number of words (0: nothing to unpack)
+  // optional substrate unpack of w_words 2-bit words (16 weights each) into
+  // w_bytes: one byte per weight (bf16 high byte of +-0.5 / 0) when w_fp4 == 0,
+  // one fp4 e2m1 nibble per weight (low nibble first) when w_fp4 == 1
+  const uint32_t* w_packed;
+  unsigned char* w_bytes;
+  int32_t w_words;
+  int32_t w_fp4;
 };
 
 struct FusedArgs {
@@ -110,7 +114,8 @@ struct FusedArgs {
   void* out;                // per-slot rows [R][d] (or y when k == 1)
   const float* theta;       // [N][L][d/2]
   const float* phi;         // [N][L][d/2]
-  const unsigned char* wb;  // [d][d] substrate bytes (bf16 high byte: +-0.5 / 0)
+  const unsigned char* wb;  // substrate: [d][d] bytes (bf16 high byte of +-0.5 / 0) for the
+                            // scalar-rotation kernel, [d][d/2] fp4 e2m1 for the matrix-core one
   const unsigned char* fac; // per-expert rotation block factors (matrix-core path)
   const int32_t* offsets;   // [N+1]
   const int32_t* perm;      // [R]

@@ -23,7 +23,7 @@
 //   G_A^T    wave (tb, h): blocks m of half h                    -> buf0 [row][i]  (= U)
 //   W        wave w: outputs [w n/4, (w+1) n/4) of all rows, accumulators kept
 //   G_A      on the accumulators of the wave's own blocks        -> buf1 [row][p][m]
-//   G_B      wave (tb, h): classes p of half h, * gate * 2 alpha -> buf0 [row][i]
+//   G_B      wave (tb, h): classes p of half h, * gate * alpha   -> buf0 [row][i]
 //   store    buf0 rows -> per-slot rows
 // LDS is 2 x 32 rows (~66 KiB), so two workgroups share a CU.
 #include "common.hpp"
@@ -94,9 +94,12 @@ __device__ __forceinline__ void rotate_vec(float (&v)[W], const float2* cs, int 
   }
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+constexpr int FAC_SPLIT = 4;  // workgroups per (expert, angle set)
 
-// grid (N, 2): blockIdx.y = 0 builds the theta set, 1 the phi set.
+// grid (N, 2, FAC_SPLIT): blockIdx.y = 0 builds the theta set, 1 the phi set;
+// blockIdx.z takes every FAC_SPLIT-th job.  (cos, sin) come from the hardware
+// transcendental unit: their error (~1e-6) is far below the bf16 rounding of
+// the factors.
 template <int L>
 __global__ __launch_bounds__(FM_THREADS) void factor_kernel(FactorArgs a) {
   using C = MfCfg<L>;
@@ -105,16 +108,17 @@ __global__ __launch_bounds__(FM_THREADS) void factor_kernel(FactorArgs a) {
   const int e = blockIdx.x;
   const bool th = blockIdx.y == 0;
   const float* ang = (th ? a.theta : a.phi) + size_t(e) * L * half;
+  constexpr float inv2pi = 0.15915494309189535f;
   for (int i = threadIdx.x; i < L * half; i += FM_THREADS) {
-    float sn, c;
-    sincosf(ang[i], &sn, &c);
-    cs[i] = make_float2(c, sn);
+    const float r = ang[i] * inv2pi;
+    cs[i] = make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
   }
   __syncthreads();
   unsigned char* fe = a.fac + size_t(e) * C::per_expert;
+  const int j0 = blockIdx.z * FM_THREADS + threadIdx.x, js = FAC_SPLIT * FM_THREADS;
 
   // G_A: theta -> column j of A_m (operand row j of A_m^T); phi -> row j of A_m
-  for (int job = threadIdx.x; job < C::NM * PA; job += FM_THREADS) {
+  for (int job = j0; job < C::NM * PA; job += js) {
     const int m = job / PA, j = job % PA;
     float v[PA];
 #pragma unroll
@@ -124,22 +128,21 @@ __global__ __launch_bounds__(FM_THREADS) void factor_kernel(FactorArgs a) {
     const int hq = j / 16, row = j % 16;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      uint16_t h[KA];
+      uint32_t h[KA / 2];
 #pragma unroll
-      for (int i = 0; i < KA; ++i) {
+      for (int i = 0; i < KA; i += 2) {
         // contraction index held by lane group g, slot i: 4g+i (PA 16);
         // theta: 8g+i; phi (accumulator order of the substrate product): 4g+i, then 16+4g+i
-        const int k = KA == 4 ? 4 * g + i : th ? 8 * g + i : (i < 4 ? 4 * g + i : 12 + 4 * g + i);
-        h[i] = bf16_bits(v[k]);
+        auto kidx = [&](int ii) { return KA == 4 ? 4 * g + ii : th ? 8 * g + ii : (ii < 4 ? 4 * g + ii : 12 + 4 * g + ii); };
+        h[i / 2] = pack_bf16x2(v[kidx(i)], v[kidx(i + 1)]);
       }
-      uint16_t* dst = reinterpret_cast<uint16_t*>(fe + (th ? C::off_at : C::off_ap)) +
-                      ((size_t(m) * HA + hq) * 64 + 16 * g + row) * KA;
-#pragma unroll
-      for (int i = 0; i < KA; ++i) dst[i] = h[i];
+      unsigned char* dst = fe + (th ? C::off_at : C::off_ap) + ((size_t(m) * HA + hq) * 64 + 16 * g + row) * KA * 2;
+      if constexpr (KA == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
+      else *reinterpret_cast<uint2*>(dst) = make_uint2(h[0], h[1]);
     }
   }
   // G_B: theta -> column j of B_p (operand row j of B_p^T); phi -> row j of B_p
-  for (int job = threadIdx.x; job < C::NP * 16; job += FM_THREADS) {
+  for (int job = j0; job < C::NP * 16; job += js) {
     const int p = job / 16, j = job % 16;
     float v[16];
 #pragma unroll
@@ -147,12 +150,9 @@ __global__ __launch_bounds__(FM_THREADS) void factor_kernel(FactorArgs a) {
     if (th) rotate_vec<16, C::LA, L, true>(v, cs, half, p, PA);
     else rotate_vec<16, C::LA, L, false>(v, cs, half, p, PA);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(fe + (th ? C::off_bt : C::off_bp)) +
-                      (size_t(p) * 64 + 16 * g + j) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = bf16_bits(v[4 * g + i]);
-    }
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint2*>(fe + (th ? C::off_bt : C::off_bp) + (size_t(p) * 64 + 16 * g + j) * 8) =
+          make_uint2(pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
   }
 }
 
@@ -160,10 +160,16 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, int k) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
-// four substrate bytes (weights k..k+3) -> two bf16 pairs (low bytes zero)
-__device__ __forceinline__ void wb_to_bf16(uint32_t w, uint32_t& p0, uint32_t& p1) {
-  p0 = __builtin_amdgcn_perm(0u, w, 0x010C000Cu);
-  p1 = __builtin_amdgcn_perm(0u, w, 0x030C020Cu);
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// eight fp4 (e2m1) substrate weights k..k+7 -> eight bf16 (exact: +-1 and 0)
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+  return r;
 }
 
 __device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
@@ -201,11 +207,10 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   using AF = typename AFragT<C::KA>::type;
   constexpr int n = C::n, PA = C::PA, NP = C::NP, HA = C::HA, TS = C::TS;
   constexpr int OB = n / 64;          // substrate: 16-output blocks per wave
-  constexpr int DS = n / 64;          // substrate: double steps of 64 contraction indices
-  constexpr int PF = DS < 2 ? DS : 2; // double steps of W in flight
+  constexpr int NU = n / 256;         // substrate: units of 256 contraction indices
   constexpr int NCW = NP / 2;         // G_B classes per wave
   constexpr int NBW = (n / 4) / PA;   // G_A blocks inside one wave's substrate outputs
-  static_assert(NBW == 4 && NCW % 4 == 0 && DS % PF == 0, "tile shape");
+  static_assert(NBW == 4 && NCW % 4 == 0 && (NU == 1 || NU == 2), "tile shape");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* buf0 = lds;
   unsigned char* buf1 = lds + C::buf_bytes;
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
     const int slot = a.perm[r0 + tid];
     s_src[tid] = size_t(slot / a.top_k) * n;
     s_dst[tid] = size_t(slot) * n;
-    s_gate[tid] = a.gate[slot] * 2.0f * a.alpha;
+    s_gate[tid] = a.gate[slot] * a.alpha;
   }
 
   // ---- input-rotation factor fragments of this expert
@@ -259,8 +264,11 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   constexpr int ITEMS = FM_RT * 4 * PG;
   constexpr int IPT = ITEMS / FM_THREADS;
   static_assert(ITEMS % FM_THREADS == 0, "gather items");
-  const unsigned char* wrow = a.wb + size_t(wave * (n / 4) + l16) * n + 16 * g;
-  uint4 W[PF][OB];
+  // substrate rows: n/2 bytes of fp4.  Unit v covers contraction indices
+  // [256v, 256v+256) = bytes [128v, 128v+128) of a row; lane group g takes
+  // bytes 16g..16g+15 of each 64-byte half (two loads that fill one line).
+  const unsigned char* wrow = a.wb + size_t(wave * (n / 4) + l16) * (n / 2) + 16 * g;
+  uint4 W0[OB][2];
   {
     uint4 ch[IPT][4];
 #pragma unroll
@@ -274,12 +282,12 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
           ch[it][mi] = *reinterpret_cast<const uint4*>(src + PA * (4 * mq + mi));
       }
     }
-    // substrate prefetch, after the gather loads
+    // first substrate unit, after the gather loads
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
+    for (int i = 0; i < OB; ++i)
 #pragma unroll
-      for (int i = 0; i < OB; ++i)
-        W[u][i] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * n + 64 * u);
+      for (int hf = 0; hf < 2; ++hf)
+        W0[i][hf] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * (n / 2) + 64 * hf);
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int item = it * FM_THREADS + tid;
@@ -351,9 +359,42 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
       }
     }
   }
+  uint4 W1[OB][2];  // second substrate unit (width 512)
+  if constexpr (NU == 2) {
+#pragma unroll
+    for (int i = 0; i < OB; ++i)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        W1[i][hf] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * (n / 2) + 128 + 64 * hf);
+  }
   __syncthreads();
 
-  // ---- first output-rotation factor (in flight during the substrate product)
+  // ---- Z = U W^T: wave owns outputs [wave n/4, (wave+1) n/4) of all 32 rows.
+  // In unit v, MFMA step s (8 contraction indices) of lane group g uses dword
+  // s % 4 of half s / 4: indices 256v + 128(s/4) + 32g + 8(s%4) .. +7; the U
+  // operand is read in the same order.
+  f32x4_t acc[OB][2];
+#pragma unroll
+  for (int i = 0; i < OB; ++i) acc[i][0] = acc[i][1] = zero4;
+  const uint16_t* urow = reinterpret_cast<const uint16_t*>(buf0) + l16 * (TS / 2) + 32 * g;
+  auto unit = [&](const uint4 (&Wu)[OB][2], int v) {
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int kk = 256 * v + 128 * (st >> 2) + 8 * (st & 3);
+      uint4 uf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) uf[j] = *reinterpret_cast<const uint4*>(urow + 16 * j * (TS / 2) + kk);
+#pragma unroll
+      for (int i = 0; i < OB; ++i) {
+        const uint4 wv = fp4x8_to_bf16(u4get(Wu[i][st >> 2], st & 3));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wv, uf[j], acc[i][j]);
+      }
+    }
+  };
+  unit(W0, 0);
+  if constexpr (NU == 2) unit(W1, 1);
+  // output-rotation factors
   AF fa[NBW][HA];
 #pragma unroll
   for (int jm = 0; jm < NBW; ++jm)
@@ -361,41 +402,6 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
     for (int hq = 0; hq < HA; ++hq)
       fa[jm][hq] = *reinterpret_cast<const AF*>(
           fe + C::off_ap + ((size_t(NBW * wave + jm) * HA + hq) * 64 + lane) * sizeof(AF));
-
-  // ---- Z = U W^T: wave owns outputs [wave n/4, (wave+1) n/4) of all 32 rows.
-  // Double step u: lanes 16g.. hold the 16 weights k = 64u + 16g .. +15 of their
-  // output row (first 8 -> first MFMA, last 8 -> second); U follows that order.
-  f32x4_t acc[OB][2];
-#pragma unroll
-  for (int i = 0; i < OB; ++i) acc[i][0] = acc[i][1] = zero4;
-  const uint16_t* urow = reinterpret_cast<const uint16_t*>(buf0) + l16 * (TS / 2) + 16 * g;
-#pragma unroll 1
-  for (int u0 = 0; u0 < DS; u0 += PF) {
-#pragma unroll
-    for (int pq = 0; pq < PF; ++pq) {
-      const int u = u0 + pq;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint4 uf[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          uf[j] = *reinterpret_cast<const uint4*>(urow + 16 * j * (TS / 2) + 64 * u + 8 * h);
-#pragma unroll
-        for (int i = 0; i < OB; ++i) {
-          uint4 wv;
-          wb_to_bf16(h ? W[pq][i].z : W[pq][i].x, wv.x, wv.y);
-          wb_to_bf16(h ? W[pq][i].w : W[pq][i].y, wv.z, wv.w);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wv, uf[j], acc[i][j]);
-        }
-      }
-      if (u + PF < DS) {
-#pragma unroll
-        for (int i = 0; i < OB; ++i)
-          W[pq][i] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * n + 64 * (u + PF));
-      }
-    }
-  }
 
   uint2 fb[NCW];  // last factor, used after the next barrier
 #pragma unroll
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   }
   __syncthreads();
 
-  // ---- G_B (phi), * gate * 2 alpha: classes hh*NCW .. of token block tb -> buf0 [row][i]
+  // ---- G_B (phi), * gate * alpha: classes hh*NCW .. of token block tb -> buf0 [row][i]
   {
     const unsigned char* yr = buf1 + trow * TS;
     unsigned char* orow = buf0 + trow * TS;
@@ -490,8 +496,8 @@ bool fused_mfma_supported(int log2n) { return log2n == 8 || log2n == 9; }
 hipError_t launch_factors(const FactorArgs& a, int log2n, hipStream_t s) {
   if (a.n_experts <= 0) return hipSuccess;
   switch (log2n) {
-    case 8: hipLaunchKernelGGL(factor_kernel<8>, dim3(a.n_experts, 2), dim3(FM_THREADS), 0, s, a); break;
-    case 9: hipLaunchKernelGGL(factor_kernel<9>, dim3(a.n_experts, 2), dim3(FM_THREADS), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(factor_kernel<8>, dim3(a.n_experts, 2, FAC_SPLIT), dim3(FM_THREADS), 0, s, a); break;
+    case 9: hipLaunchKernelGGL(factor_kernel<9>, dim3(a.n_experts, 2, FAC_SPLIT), dim3(FM_THREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -459,23 +459,30 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // optional: unpack the 2-bit substrate into one byte per weight holding the
-  // high byte of its bf16 value scaled by 1/2 (+1 -> 0x3F, -1 -> 0xBF, 0 -> 0)
+  // optional: unpack the 2-bit substrate (16 weights per word) into one byte
+  // per weight holding the high byte of its bf16 value scaled by 1/2
+  // (+1 -> 0x3F, -1 -> 0xBF, 0 -> 0), or into fp4 e2m1 nibbles (+1 -> 0x2,
+  // -1 -> 0xA, 0 -> 0; weight 2b in the low nibble of byte b)
   for (int w = e * BK_THREADS + tid; w < a.w_words; w += gridDim.x * BK_THREADS) {
     const uint32_t P = a.w_packed[w];
-    uint32_t out[4];
+    uint32_t code[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int c = 4 * q + b, j = c >> 1, h = c & 1;
-        const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = (P >> (16 * h + 8 + j)) & 1u;
-        v |= (nz * (0x3Fu | (sg << 7))) << (8 * b);
-      }
-      out[q] = v;
+    for (int c = 0; c < 16; ++c) {
+      const int j = c >> 1, h = c & 1;
+      const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = (P >> (16 * h + 8 + j)) & 1u;
+      code[c] = a.w_fp4 ? nz * (0x2u | (sg << 3)) : nz * (0x3Fu | (sg << 7));
     }
-    reinterpret_cast<uint4*>(a.w_bytes)[w] = make_uint4(out[0], out[1], out[2], out[3]);
+    if (a.w_fp4) {
+      uint32_t o[2] = {0u, 0u};
+#pragma unroll
+      for (int c = 0; c < 16; ++c) o[c >> 3] |= code[c] << (4 * (c & 7));
+      reinterpret_cast<uint2*>(a.w_bytes)[w] = make_uint2(o[0], o[1]);
+    } else {
+      uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int c = 0; c < 16; ++c) o[c >> 2] |= code[c] << (8 * (c & 3));
+      reinterpret_cast<uint4*>(a.w_bytes)[w] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
 
   auto load4 = [&](int f0) -> int4 {
