@@ -27,10 +27,10 @@ constexpr int RT_XLD = RT_BK + 8;    // padded LDS row of the token tile (bf16)
 constexpr int RT_KMAX = 8;           // largest supported top_k
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+  return (v > bv) | ((v == bv) & (i < bi));
 }
 __device__ __forceinline__ bool better(double v, int i, double bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+  return (v > bv) | ((v == bv) & (i < bi));
 }
 
 template <typename T>
@@ -55,72 +55,274 @@ __device__ __forceinline__ void topk_insert(T* tv, int* ti, T v, int i) {
   }
 }
 
-// Per-token decision: 4 threads per token (q = lane & 3) each scan every 4th
-// expert.  Round j picks the best entry strictly below the pick of round j-1
-// in the order (larger value, then lower index), so kk rounds give the sorted
-// top-kk.  Writes idx/gates of the fp32 decision and flags tokens whose
-// decisive gaps are within the error bound.
-__device__ void decide(const float* Lrow, int N, int k, int kk, int renorm, float tau, int q,
-                       int* out_idx, float* out_gate, float* out_thr, float* out_max,
-                       float* out_sum, bool* flag) {
+// Per-workgroup state of the decision phase.
+template <int BT>
+struct RouteSh {
+  float X2[BT];               // |x_t|^2
+  int Idx[BT][RT_KMAX];
+  float Gate[BT][RT_KMAX];
+  float Thr[BT], Max[BT], Sum[BT];
+  int Flag[BT];
+  int NF;
+  float Wmax[8];              // max_e |w_e|^2 seen by each wave (unused entries 0)
+};
+
+// Per-token decision, 16 lanes per token (four tokens per wave at a time):
+// lane j of the token's group holds the logits of experts j, j+16, ...,
+// j+16(NR-1) in registers.  Round r takes the best remaining entry (larger
+// value, then lower index) over the group in four shuffle steps and its owner
+// marks it taken, so kk rounds give the sorted top-kk.  The group's lane 0
+// writes idx/gates of the fp32 decision; returns whether a decisive gap is
+// within the error bound.
+template <int NR>
+__device__ __forceinline__ bool decide16(const float* Lrow, bool valid, int N, int k, int kk, int renorm,
+                                         float tau, int j, int* out_idx, float* out_gate, float* out_thr,
+                                         float* out_max, float* out_sum) {
+  float v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int e = j + 16 * r;
+    v[r] = (valid && e < N) ? Lrow[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
   float tv[RT_KMAX + 1];
   int ti[RT_KMAX + 1];
-  float pv = INFINITY;
-  int pi = -1;
 #pragma unroll
-  for (int j = 0; j < RT_KMAX + 1; ++j) {
+  for (int rr = 0; rr < RT_KMAX + 1; ++rr) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    if (j < kk) {
-      for (int e = q; e < N; e += 4) {
-        const float v = Lrow[e];
-        const bool below = v < pv || (v == pv && e > pi);
-        if (below && better(v, e, bv, bi)) { bv = v; bi = e; }
+    if (rr < kk) {  // uniform
+      int br = 0;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int e = j + 16 * r;
+        const bool c = (e < N) & (((taken >> r) & 1u) == 0u) & better(v[r], e, bv, bi);
+        bv = c ? v[r] : bv;
+        bi = c ? e : bi;
+        br = c ? r : br;
       }
 #pragma unroll
-      for (int o = 1; o <= 2; o <<= 1) {
+      for (int o = 1; o < 16; o <<= 1) {
         const float ov = __shfl_xor(bv, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        const bool c = better(ov, oi, bv, bi);
+        bv = c ? ov : bv;
+        bi = c ? oi : bi;
       }
+      taken |= (j + 16 * br == bi) ? (1u << br) : 0u;
     }
-    tv[j] = bv;
-    ti[j] = bi;
-    pv = bv;
-    pi = bi;
+    tv[rr] = bv;
+    ti[rr] = bi;
   }
   const float mx = tv[0];
   float s = 0.f;
-  for (int e = q; e < N; e += 4) s += __expf(Lrow[e] - mx);
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  if (q == 0) {
-    bool f = false;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) s += (j + 16 * r < N) ? __expf(v[r] - mx) : 0.f;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+  bool f = false;
+  if (j == 0 && valid) {
     const int ngap = min(k, N - 1);
     float g[RT_KMAX];
     float gs = 0.f;
     float kth = tv[0];
 #pragma unroll
-    for (int j = 0; j < RT_KMAX; ++j) {
-      if (j < ngap && tv[j] - tv[j + 1] < tau) f = true;
-      g[j] = (j < k) ? __expf(tv[j] - mx) / s : 0.f;
-      gs += g[j];
-      if (j == k - 1) kth = tv[j];
+    for (int q = 0; q < RT_KMAX; ++q) {
+      f |= (q < ngap) & (tv[q] - tv[q + 1] < tau);
+      g[q] = (q < k) ? __expf(tv[q] - mx) / s : 0.f;
+      gs += g[q];
+      kth = (q == k - 1) ? tv[q] : kth;
     }
 #pragma unroll
-    for (int j = 0; j < RT_KMAX; ++j) {
-      if (j < k) {
-        out_idx[j] = ti[j];
-        out_gate[j] = renorm ? g[j] / gs : g[j];
+    for (int q = 0; q < RT_KMAX; ++q) {
+      if (q < k) {
+        out_idx[q] = ti[q];
+        out_gate[q] = renorm ? g[q] / gs : g[q];
       }
     }
     *out_thr = kth - tau;
     *out_max = mx;
     *out_sum = s;
-    *flag = f;
+  }
+  return f;
+}
+
+template <int BT, int NR, int NT>
+__device__ __forceinline__ void decide_all(const RouteArgs& a, RouteSh<BT>& sh, const float* sL, int LS,
+                                           float gamma, float wmax, int t0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kk = min(a.k + 1, a.N);
+  const int j = lane & 15;
+#pragma unroll
+  for (int tl0 = 0; tl0 < BT; tl0 += NT / 16) {
+    const int tl = tl0 + 4 * wave + (lane >> 4);
+    if (tl < BT) {  // whole 16-lane groups
+      const bool valid = t0 + tl < a.T;
+      const float tau = 2.02f * gamma * sqrtf(sh.X2[tl]) * wmax;
+      const bool flag = decide16<NR>(sL + tl * LS, valid, a.N, a.k, kk, a.renorm, tau, j, sh.Idx[tl],
+                                     sh.Gate[tl], &sh.Thr[tl], &sh.Max[tl], &sh.Sum[tl]);
+      if (j == 0 && flag && valid) sh.Flag[atomicAdd(&sh.NF, 1)] = tl;
+    }
   }
 }
 
+__device__ __forceinline__ float route_gamma(int depth) {
+  const float u = 2.384185791015625e-07f;  // 2^-22
+  const float Du = depth * u;
+  return Du / (1.f - Du);
+}
+
+template <int BT>
+__device__ __forceinline__ float route_wmax(const RouteSh<BT>& sh) {
+  float w = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w = fmaxf(w, sh.Wmax[i]);
+  return sqrtf(w);
+}
+
+// Decision from the logits in LDS (row stride LS), after X2 / Wmax are set.
+// Starts and ends with a barrier.
+template <int BT, int NT>
+__device__ __forceinline__ void route_decide(const RouteArgs& a, RouteSh<BT>& sh, const float* sL, int LS,
+                                             int depth, int t0) {
+  const int N = a.N;
+  __syncthreads();
+  const float gamma = route_gamma(depth), wmax = route_wmax(sh);
+  if (N <= 16) decide_all<BT, 1, NT>(a, sh, sL, LS, gamma, wmax, t0);
+  else if (N <= 32) decide_all<BT, 2, NT>(a, sh, sL, LS, gamma, wmax, t0);
+  else if (N <= 64) decide_all<BT, 4, NT>(a, sh, sL, LS, gamma, wmax, t0);
+  else if (N <= 128) decide_all<BT, 8, NT>(a, sh, sL, LS, gamma, wmax, t0);
+  else decide_all<BT, 16, NT>(a, sh, sL, LS, gamma, wmax, t0);
+  __syncthreads();
+}
+
+// Exact re-ranking of the flagged (near-tied) tokens and output of the tile.
+// Expects the decision state and the logits in LDS, synchronised.
+template <int ACT, int BT, int NT>
+__device__ __forceinline__ void route_recheck_store(const RouteArgs& a, RouteSh<BT>& sh, const float* sL, int LS,
+                                                    int t0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.N, d = a.d, k = a.k;
+  const int nf = sh.NF;
+  for (int f = wave; f < nf; f += NT / 64) {
+    const int tl = sh.Flag[f];
+    const float thr = sh.Thr[tl];
+    const float* Lrow = sL + tl * LS;
+    const size_t xo = size_t(t0 + tl) * d;
+    double cv[RT_KMAX];
+    int ci[RT_KMAX];
+#pragma unroll
+    for (int j = 0; j < RT_KMAX; ++j) { cv[j] = -INFINITY; ci[j] = 0x7fffffff; }
+    for (int u = 0; u < 4; ++u) {
+      const int e0 = lane + 64 * u;
+      const bool cand = e0 < N && Lrow[e0] >= thr;
+      uint64_t m = __ballot(cand);
+      while (m) {
+        const int bit = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const int e = 64 * u + bit;
+        // lane owns elements 8*lane .. 8*lane+7 of each 512-wide chunk; the
+        // chunks' loads are issued four at a time before they are used
+        double s = 0.0;
+        for (int i0 = 0; i0 < d; i0 += 4 * 512) {
+          float xv[4][8], wv[4][8];
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            const int i = i0 + 512 * uu + 8 * lane;
+            if (i < d) {
+              load8<ACT>(a.x, xo + i, xv[uu]);
+              load8<ACT>(a.w_gate, size_t(e) * d + i, wv[uu]);
+            }
+          }
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            if (i0 + 512 * uu + 8 * lane < d) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) s = fma((double)xv[uu][j], (double)wv[uu][j], s);
+            }
+          }
+        }
+        s = wave_sum(s);
+        topk_insert<RT_KMAX>(cv, ci, s, e);
+      }
+    }
+    if (lane == 0) {
+      const float mx = sh.Max[tl], se = sh.Sum[tl];
+      float g[RT_KMAX];
+      float gs = 0.f;
+#pragma unroll
+      for (int j = 0; j < RT_KMAX; ++j) {
+        g[j] = (j < k) ? __expf(Lrow[ci[j] < N ? ci[j] : 0] - mx) / se : 0.f;
+        gs += g[j];
+      }
+#pragma unroll
+      for (int j = 0; j < RT_KMAX; ++j)
+        if (j < k) {
+          sh.Idx[tl][j] = ci[j] < N ? ci[j] : 0;
+          sh.Gate[tl][j] = a.renorm ? g[j] / gs : g[j];
+        }
+    }
+  }
+  __syncthreads();
+
+  for (int p = tid; p < BT * k; p += NT) {
+    const int tl = p / k, j = p - tl * k;
+    const int tok = t0 + tl;
+    if (tok < a.T) {
+      a.topk_idx[size_t(tok) * k + j] = sh.Idx[tl][j];
+      a.topk_gate[size_t(tok) * k + j] = sh.Gate[tl][j];
+    }
+  }
+}
+
+// max over the workgroup's gate rows of |w_e|^2 from per-lane partial sums:
+// lanes l, l^16, l^32, l^48 hold the same expert
+template <int NI>
+__device__ __forceinline__ void publish_wmax(const float (&wsq)[NI], float* Wmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float wm = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float v = wsq[i];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    wm = fmaxf(wm, v);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+  if (lane == 0) Wmax[wave] = wm;
+}
+
+// Order-preserving 64-bit key of (logit, expert): larger logit first, then
+// lower expert index.  Key 0 lies below every real logit.
+__device__ __forceinline__ uint64_t rkey(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t(u) << 32) | uint32_t(0xFFFFFFFFu - uint32_t(e));
+}
+__device__ __forceinline__ float rkey_val(uint64_t k) {
+  uint32_t u = uint32_t(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ int rkey_idx(uint64_t k) { return int(0xFFFFFFFFu - uint32_t(k)); }
+
+// insert into a descending list of three distinct keys
+__device__ __forceinline__ void top3_insert(uint64_t (&t)[3], uint64_t k) {
+  const bool c0 = k > t[0], c1 = k > t[1], c2 = k > t[2];
+  t[2] = c1 ? t[1] : (c2 ? k : t[2]);
+  t[1] = c0 ? t[0] : (c1 ? k : t[1]);
+  t[0] = c0 ? k : t[0];
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor(uint32_t(v), o, 64), hi = __shfl_xor(uint32_t(v >> 32), o, 64);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// ----------------------------------------------------------------------------
+// Any width: bf16 tokens stream through two LDS steps of 64 contraction
+// indices (pipelined), fp32 tokens use one FMA chain per logit.
 template <int ACT, int BT>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   constexpr int TB = BT / 16;                 // token blocks of 16
@@ -129,20 +331,14 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sx = reinterpret_cast<uint16_t*>(smem);  // [2][BT][RT_XLD] token tile (bf16)
   float* sL = reinterpret_cast<float*>(smem);         // [BT][LS] logits (after the K loop)
-  __shared__ float sX2[BT];
-  __shared__ int sIdx[BT][RT_KMAX];
-  __shared__ float sGate[BT][RT_KMAX];
-  __shared__ float sThr[BT], sMax[BT], sSum[BT];
-  __shared__ int sFlag[BT];
-  __shared__ int sNF;
-  __shared__ float sWmax[4];
+  __shared__ RouteSh<BT> sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * BT;
-  const int N = a.N, d = a.d, k = a.k;
+  const int N = a.N, d = a.d;
   const int NB = (N + 15) >> 4;
-  const int LS = NB * 16 + 4;  // logit row stride (conflict-free quarter reads)
-  if (tid == 0) sNF = 0;
+  const int LS = NB * 16 + 4;  // logit row stride
+  if (tid == 0) sh.NF = 0;
 
   int depth;
   if constexpr (ACT == ACT_BF16) {
@@ -252,20 +448,9 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       v += __shfl_xor(v, 2, 64);
       v += __shfl_xor(v, 4, 64);
       const int c = tid + RT_THREADS * r;
-      if ((tid & 7) == 0 && c < XCH) sX2[c >> 3] = v;
+      if ((tid & 7) == 0 && c < XCH) sh.X2[c >> 3] = v;
     }
-    // max_e |w_e|^2: lanes l, l^16, l^32, l^48 hold the same expert
-    float wm = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = wsq[i];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      wm = fmaxf(wm, v);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
-    if (lane == 0) sWmax[wave] = wm;
+    publish_wmax(wsq, sh.Wmax);
     // logits -> LDS (the token tile is dead after the last barrier)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -301,7 +486,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
         const float* xrow = xf + size_t(tok) * d;
         for (int i = 0; i < d; ++i) s = fmaf(xrow[i], xrow[i], s);
       }
-      sX2[tl] = s;
+      sh.X2[tl] = s;
     }
     float wm = 0.f;
     for (int e = tid; e < N; e += RT_THREADS) {
@@ -312,132 +497,310 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
-    if (lane == 0) sWmax[wave] = wm;
+    if (lane == 0) sh.Wmax[wave] = wm;
     depth = d;
   }
-  __syncthreads();
+  if (tid < 4) sh.Wmax[4 + tid] = 0.f;
+  route_decide<BT, RT_THREADS>(a, sh, sL, LS, depth, t0);
+  route_recheck_store<ACT, BT, RT_THREADS>(a, sh, sL, LS, t0);
+}
 
-  // ---- fp32 decision: 4 threads per token
-  {
-    const float u = 2.384185791015625e-07f;  // 2^-22
-    const float Du = depth * u;
-    const float gamma = Du / (1.f - Du);
-    const float wmax = sqrtf(fmaxf(fmaxf(sWmax[0], sWmax[1]), fmaxf(sWmax[2], sWmax[3])));
-    const int tl = tid >> 2, q = tid & 3;
-    if (tl < BT) {  // whole waves
-      const float tau = 2.02f * gamma * sqrtf(sX2[tl]) * wmax;
-      const int kk = min(k + 1, N);
-      bool flag = false;
-      const float* Lrow = sL + tl * LS;
-      decide(Lrow, N, k, kk, a.renorm, tau, q, sIdx[tl], sGate[tl], &sThr[tl], &sMax[tl], &sSum[tl], &flag);
-      if (q == 0 && flag && t0 + tl < a.T) sFlag[atomicAdd(&sNF, 1)] = tl;
-    }
+// ----------------------------------------------------------------------------
+// bf16 tokens, width d = 64 NK, the whole token tile in LDS.  Eight waves:
+// wave w owns expert blocks w (and w + 8 when NI = 2; 16 experts each) and
+// holds its whole share of the gate matrix in registers (at most 128 per
+// lane), loaded at the start together with the
+// token tile; the contraction loop is unrolled at compile time.  For k <= 2
+// the top-(k+1) is taken from the accumulators: each lane keeps the three best
+// (logit, expert) keys of its experts per token, the four lanes of a token
+// merge theirs by shuffles, the waves' lists meet in LDS.  Larger k uses the
+// decision over the logits in LDS.
+constexpr int RW_THREADS = 512;
+constexpr int RW_WAVES = RW_THREADS / 64;
+
+template <int BT, int NK, int NI>
+__global__ __launch_bounds__(RW_THREADS) void route_whole_kernel(RouteArgs a) {
+  constexpr int TB = BT / 16;
+  constexpr int D = NK * RT_BK;
+  constexpr int KS = D / 32;                          // MFMA k-steps
+  constexpr int XST = D + 8;                          // LDS row stride (bf16)
+  constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  constexpr int NCH = BT * CPR;
+  constexpr int CPT = (NCH + RW_THREADS - 1) / RW_THREADS;
+  constexpr int G = CPR < 64 ? CPR : 64;              // lanes sharing a row in one load
+  static_assert(NI == 1 || NI == 2, "expert blocks per wave");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* sx = reinterpret_cast<uint16_t*>(smem);  // [BT][XST] token tile
+  float* sL = reinterpret_cast<float*>(smem);         // [BT][LS] logits (after the contraction)
+  __shared__ RouteSh<BT> sh;
+  __shared__ uint64_t sTop[BT][RW_WAVES][3];
+  __shared__ float sPart[BT][RW_WAVES];
+  __shared__ int sTflag[BT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * BT;
+  const int N = a.N, k = a.k;
+  const int NB = (N + 15) >> 4;
+  const int LS = NB * 16 + 4;
+  const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
+  const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w_gate);
+  if (tid == 0) sh.NF = 0;
+  if (tid < BT) sh.X2[tid] = 0.f;
+
+  // token tile: all loads first
+  uint4 xv[CPT];
+#pragma unroll
+  for (int r = 0; r < CPT; ++r) {
+    const int c = r * RW_THREADS + tid;
+    const int tl = c / CPR;
+    xv[r] = (c < NCH && t0 + tl < a.T) ? *reinterpret_cast<const uint4*>(xg + size_t(t0 + tl) * D + 8 * (c % CPR))
+                                       : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
+  // this wave's gate rows: block b = wave + 8 i, k-step s, 8 values per lane
+  bool bval[NI];
+  uint4 A[NI][KS];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int b = wave + RW_WAVES * i;
+    const int e = 16 * b + l16;
+    bval[i] = b < NB;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      A[i][st] = (bval[i] && e < N) ? *reinterpret_cast<const uint4*>(wg + size_t(e) * D + 32 * st + 8 * g)
+                                    : make_uint4(0, 0, 0, 0);
+  }
+  // tile -> LDS; |x|^2 partial sums reduced over the lanes sharing a row
+  float xs[CPT];
+#pragma unroll
+  for (int r = 0; r < CPT; ++r) {
+    const int c = r * RW_THREADS + tid;
+    const uint4 q = xv[r];
+    float ss = 0.f;
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x), __builtin_bit_cast(bf16x2_t, q.x), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y), __builtin_bit_cast(bf16x2_t, q.y), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z), __builtin_bit_cast(bf16x2_t, q.z), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w), __builtin_bit_cast(bf16x2_t, q.w), ss, false);
+    xs[r] = ss;
+    if (c < NCH) *reinterpret_cast<uint4*>(sx + (c / CPR) * XST + 8 * (c % CPR)) = q;
+  }
+#pragma unroll
+  for (int r = 0; r < CPT; ++r)
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) xs[r] += __shfl_xor(xs[r], o, 64);
+  __syncthreads();  // tile in LDS, X2 cleared
+#pragma unroll
+  for (int r = 0; r < CPT; ++r) {
+    const int c = r * RW_THREADS + tid;
+    if (c < NCH && (lane % G) == 0) atomicAdd(&sh.X2[c / CPR], xs[r]);
+  }
 
-  // ---- exact order of the near-tied tokens: candidates recomputed in fp64
-  const int nf = sNF;
-  for (int f = wave; f < nf; f += RT_THREADS / 64) {
-    const int tl = sFlag[f];
-    const float thr = sThr[tl];
-    const float* Lrow = sL + tl * LS;
-    const size_t xo = size_t(t0 + tl) * d;
-    double cv[RT_KMAX];
-    int ci[RT_KMAX];
+  f32x4_t acc[NI][TB];
 #pragma unroll
-    for (int j = 0; j < RT_KMAX; ++j) { cv[j] = -INFINITY; ci[j] = 0x7fffffff; }
-    for (int u = 0; u < 4; ++u) {
-      const int e0 = lane + 64 * u;
-      const bool cand = e0 < N && Lrow[e0] >= thr;
-      uint64_t m = __ballot(cand);
-      while (m) {
-        const int bit = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const int e = 64 * u + bit;
-        // lane owns elements 8*lane .. 8*lane+7 of each 512-wide chunk; the
-        // chunks' loads are issued four at a time before they are used
-        double s = 0.0;
-        for (int i0 = 0; i0 < d; i0 += 4 * 512) {
-          float xv[4][8], wv[4][8];
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = i0 + 512 * u + 8 * lane;
-            if (i < d) {
-              load8<ACT>(a.x, xo + i, xv[u]);
-              load8<ACT>(a.w_gate, size_t(e) * d + i, wv[u]);
-            }
-          }
+    for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (i0 + 512 * u + 8 * lane < d) {
+  for (int st = 0; st < KS; ++st) {
+    bf16x8_t bx[TB];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) s = fma((double)xv[u][j], (double)wv[u][j], s);
-            }
-          }
+    for (int j = 0; j < TB; ++j)
+      bx[j] = *reinterpret_cast<const bf16x8_t*>(sx + (16 * j + l16) * XST + 32 * st + 8 * g);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (bval[i]) {
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[i][st]), bx[j],
+                                                              acc[i][j], 0, 0, 0);
+      }
+  }
+  // max_e |w_e|^2 of the wave's rows (two-term dot products of the bf16 pairs)
+  float wsq[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float ss = 0.f;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const uint4 q = A[i][st];
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x), __builtin_bit_cast(bf16x2_t, q.x), ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y), __builtin_bit_cast(bf16x2_t, q.y), ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z), __builtin_bit_cast(bf16x2_t, q.z), ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w), __builtin_bit_cast(bf16x2_t, q.w), ss, false);
+    }
+    wsq[i] = ss;
+  }
+  publish_wmax(wsq, sh.Wmax);
+
+  if (k <= 2) {
+    // lane's best three (logit, expert) keys per token block, merged over the
+    // four lanes of each token, published per wave
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      uint64_t t3[3] = {0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 16 * (wave + RW_WAVES * i) + 4 * g + r;
+          if (bval[i] && e < N) top3_insert(t3, rkey(acc[i][j][r], e));
         }
-        s = wave_sum(s);
-        topk_insert<RT_KMAX>(cv, ci, s, e);
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const uint64_t p0 = shfl_xor_u64(t3[0], o), p1 = shfl_xor_u64(t3[1], o), p2 = shfl_xor_u64(t3[2], o);
+        top3_insert(t3, p0);
+        top3_insert(t3, p1);
+        top3_insert(t3, p2);
+      }
+      if (g == 0) {
+        sTop[16 * j + l16][wave][0] = t3[0];
+        sTop[16 * j + l16][wave][1] = t3[1];
+        sTop[16 * j + l16][wave][2] = t3[2];
       }
     }
-    if (lane == 0) {
-      const float mx = sMax[tl], se = sSum[tl];
-      float g[RT_KMAX];
-      float gs = 0.f;
-#pragma unroll
-      for (int j = 0; j < RT_KMAX; ++j) {
-        g[j] = (j < k) ? __expf(Lrow[ci[j] < N ? ci[j] : 0] - mx) / se : 0.f;
-        gs += g[j];
-      }
-#pragma unroll
-      for (int j = 0; j < RT_KMAX; ++j)
-        if (j < k) {
-          sIdx[tl][j] = ci[j] < N ? ci[j] : 0;
-          sGate[tl][j] = a.renorm ? g[j] / gs : g[j];
-        }
-    }
   }
-  __syncthreads();
+  __syncthreads();  // token tile dead; wave lists and Wmax published
+  // logits -> LDS (fp64 re-ranking of near-tied tokens reads them)
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if (bval[i]) {
+#pragma unroll
+      for (int j = 0; j < TB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sL[(16 * j + l16) * LS + 16 * (wave + RW_WAVES * i) + 4 * g + r] = acc[i][j][r];
+    }
 
-  for (int p = tid; p < BT * k; p += RT_THREADS) {
-    const int tl = p / k, j = p - tl * k;
-    const int tok = t0 + tl;
-    if (tok < a.T) {
-      a.topk_idx[size_t(tok) * k + j] = sIdx[tl][j];
-      a.topk_gate[size_t(tok) * k + j] = sGate[tl][j];
+  if (k <= 2) {
+    const int kk = min(k + 1, N);
+    if (tid < BT) {
+      uint64_t t3[3] = {0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < RW_WAVES; ++w)
+        if (w < NB) {
+          top3_insert(t3, sTop[tid][w][0]);
+          top3_insert(t3, sTop[tid][w][1]);
+          top3_insert(t3, sTop[tid][w][2]);
+        }
+      float tv[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) tv[q] = rkey_val(t3[q]);
+      const float tau = 2.02f * route_gamma(D / 32 + 32) * sqrtf(sh.X2[tid]) * route_wmax(sh);
+      const int ngap = min(k, N - 1);
+      bool f = false;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) f |= (q < ngap) & (q + 1 < kk) & (tv[q] - tv[q + 1] < tau);
+      sh.Max[tid] = tv[0];
+      sh.Thr[tid] = tv[k - 1] - tau;
+      sh.Idx[tid][0] = rkey_idx(t3[0]);
+      sh.Idx[tid][1] = rkey_idx(t3[1]);
+      sh.Gate[tid][0] = tv[0];
+      sh.Gate[tid][1] = tv[1];
+      sTflag[tid] = f;
     }
+    __syncthreads();
+    // softmax denominators: per lane over its experts, then the token's lanes and waves
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const float mx = sh.Max[16 * j + l16];
+      float se = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 16 * (wave + RW_WAVES * i) + 4 * g + r;
+          se += (bval[i] && e < N) ? __expf(acc[i][j][r] - mx) : 0.f;
+        }
+      se += __shfl_xor(se, 16, 64);
+      se += __shfl_xor(se, 32, 64);
+      if (g == 0) sPart[16 * j + l16][wave] = se;
+    }
+    __syncthreads();
+    if (tid < BT) {
+      float se = 0.f;
+#pragma unroll
+      for (int w = 0; w < RW_WAVES; ++w) se += sPart[tid][w];
+      const float mx = sh.Max[tid];
+      float g0 = __expf(sh.Gate[tid][0] - mx) / se;
+      float g1 = k > 1 ? __expf(sh.Gate[tid][1] - mx) / se : 0.f;
+      if (a.renorm) {
+        const float gs = g0 + g1;
+        g0 /= gs;
+        g1 /= gs;
+      }
+      sh.Gate[tid][0] = g0;
+      sh.Gate[tid][1] = g1;
+      sh.Sum[tid] = se;
+      if (sTflag[tid] && t0 + tid < a.T) sh.Flag[atomicAdd(&sh.NF, 1)] = tid;
+    }
+    __syncthreads();
+  } else {
+    route_decide<BT, RW_THREADS>(a, sh, sL, LS, D / 32 + 32, t0);
   }
+  route_recheck_store<ACT_BF16, BT, RW_THREADS>(a, sh, sL, LS, t0);
 }
 
 template <int BT>
-static size_t route_lds_bytes(int N) {
+static size_t route_lds_bytes(int N, size_t tiles) {
   const int NB = (N + 15) >> 4;
   const size_t logits = size_t(BT) * (NB * 16 + 4) * sizeof(float);
-  const size_t tiles = size_t(2) * BT * RT_XLD * sizeof(uint16_t);
   return logits > tiles ? logits : tiles;
 }
 
-template <int BT>
-static hipError_t launch_route_bt(const RouteArgs& a, int act, hipStream_t s) {
-  const int grid = (a.T + BT - 1) / BT;
-  const size_t lds = route_lds_bytes<BT>(a.N);
-  static int attr_done[64] = {0};
+constexpr size_t RT_WHOLE_MAX = 72 * 1024;  // whole token tile in LDS up to this size
+
+// `opted`: per-device flags of one kernel (dynamic LDS above 64 KiB allowed once)
+template <typename K>
+static hipError_t route_launch(K kern, int* opted, int grid, int threads, size_t lds, hipStream_t s,
+                               const RouteArgs& a) {
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  auto kb = route_kernel<ACT_BF16, BT>;
-  auto kf = route_kernel<ACT_F32, BT>;
-  if (dev < 0 || dev >= 64 || !attr_done[dev]) {
-    const int mx = int(route_lds_bytes<BT>(256));
-    err = hipFuncSetAttribute((const void*)kb, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-    if (err == hipSuccess) err = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+  if (dev < 0 || dev >= 64 || !opted[dev]) {
+    err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
+    if (dev >= 0 && dev < 64) opted[dev] = 1;
   }
-  if (act == ACT_BF16)
-    hipLaunchKernelGGL(kb, dim3(grid), dim3(RT_THREADS), lds, s, a);
-  else
-    hipLaunchKernelGGL(kf, dim3(grid), dim3(RT_THREADS), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, a);
   return hipGetLastError();
+}
+
+template <int BT, int NK, int NI>
+static hipError_t launch_whole(const RouteArgs& a, hipStream_t s) {
+  static int opted[64] = {0};
+  const size_t lds = route_lds_bytes<BT>(a.N, size_t(BT) * (NK * RT_BK + 8) * sizeof(uint16_t));
+  return route_launch(route_whole_kernel<BT, NK, NI>, opted, (a.T + BT - 1) / BT, RW_THREADS, lds, s, a);
+}
+
+// whole-tile kernel when the tile fits LDS and a wave's gate rows fit 128
+// registers per lane (width <= 1024 with one 16-expert block per wave, <= 512 with two)
+template <int BT>
+static hipError_t launch_route_bt(const RouteArgs& a, int act, hipStream_t s) {
+  if (act == ACT_BF16 && size_t(BT) * (a.d + 8) * sizeof(uint16_t) <= RT_WHOLE_MAX) {
+    if (a.N <= 128) {
+      switch (a.d / RT_BK) {
+        case 1: return launch_whole<BT, 1, 1>(a, s);
+        case 2: return launch_whole<BT, 2, 1>(a, s);
+        case 4: return launch_whole<BT, 4, 1>(a, s);
+        case 8: return launch_whole<BT, 8, 1>(a, s);
+        case 16: if constexpr (BT <= 32) return launch_whole<BT, 16, 1>(a, s); break;
+        default: break;
+      }
+    } else {
+      switch (a.d / RT_BK) {
+        case 1: return launch_whole<BT, 1, 2>(a, s);
+        case 2: return launch_whole<BT, 2, 2>(a, s);
+        case 4: return launch_whole<BT, 4, 2>(a, s);
+        case 8: return launch_whole<BT, 8, 2>(a, s);
+        default: break;
+      }
+    }
+  }
+  static int opted_b[64] = {0}, opted_f[64] = {0};
+  const size_t lds = route_lds_bytes<BT>(a.N, size_t(2) * BT * RT_XLD * sizeof(uint16_t));
+  const int grid = (a.T + BT - 1) / BT;
+  if (act == ACT_BF16) return route_launch(route_kernel<ACT_BF16, BT>, opted_b, grid, RT_THREADS, lds, s, a);
+  return route_launch(route_kernel<ACT_F32, BT>, opted_f, grid, RT_THREADS, lds, s, a);
 }
 
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
