@@ -34,8 +34,8 @@ F32, BF16 = 0, 1
 ACT_NONE, ACT_GELU_ERF = 0, 1
 
 EXPORTED_SYMBOLS = [
-    "bmoe_packed_words", "bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_route",
-    "bmoe_forward", "bmoe_status_string", "bmoe_last_error",
+    "bmoe_packed_words", "bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepared_bytes",
+    "bmoe_prepare", "bmoe_route", "bmoe_forward", "bmoe_status_string", "bmoe_last_error",
     "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_forward_kernels",
     "bmoe_dbg_forward_marked",
 ]
@@ -59,6 +59,8 @@ class LayerStruct(ctypes.Structure):
         ("theta", ctypes.c_void_p * 2),
         ("phi", ctypes.c_void_p * 2),
         ("w_scale", ctypes.c_float * 2),
+        ("prepared", ctypes.c_void_p),
+        ("prepared_bytes", ctypes.c_size_t),
     ]
 
 
@@ -84,6 +86,9 @@ def lib() -> ctypes.CDLL:
     L.bmoe_packed_words.restype = c_sz
     L.bmoe_pack_ternary.argtypes = [c_vp, c_i32, c_i32, c_vp, c_sz]
     L.bmoe_workspace_size.argtypes = [pL, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_prepared_bytes.argtypes = [pL]
+    L.bmoe_prepared_bytes.restype = c_sz
+    L.bmoe_prepare.argtypes = [pL, c_vp, c_sz, c_vp]
     L.bmoe_route.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
     L.bmoe_forward.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
     L.bmoe_status_string.argtypes = [c_i32]
@@ -94,7 +99,7 @@ def lib() -> ctypes.CDLL:
     L.bmoe_dbg_ternary_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
     L.bmoe_dbg_forward_kernels.argtypes = [pL, ctypes.POINTER(c_i32), ctypes.c_char_p, c_sz]
     L.bmoe_dbg_forward_marked.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_i32]
-    for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_route", "bmoe_forward",
+    for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
                  "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_forward_kernels",
                  "bmoe_dbg_forward_marked"):
         getattr(L, name).restype = c_i32
@@ -173,8 +178,10 @@ class Layer:
             s.theta[m] = _ptr(self.theta[m]) if m < len(self.theta) else None
             s.phi[m] = _ptr(self.phi[m]) if m < len(self.phi) else None
             s.w_scale[m] = float(w_scale[m]) if m < len(w_scale) else 1.0
+        s.prepared, s.prepared_bytes = None, 0
         self.struct = s
         self._ws = None
+        self._prep = None
 
     @classmethod
     def from_inputs(cls, inp, device="cuda") -> "Layer":
@@ -190,6 +197,33 @@ class Layer:
         return cls(d_model=cfg.d_model, d_ff=cfg.d_ff, n_experts=cfg.n_experts, top_k=cfg.top_k,
                    act=cfg.act, ffn_act=cfg.ffn_act, renorm_gates=cfg.renorm_gates, w_gate=wg,
                    w_base_packed=packed, theta=th, phi=ph, w_scale=[cfg.w_scale] * nsub)
+
+    # ---------------------------------------------------------------- prepared weights
+    def prepared_bytes(self) -> int:
+        return int(lib().bmoe_prepared_bytes(ctypes.byref(self.struct)))
+
+    def prepare(self):
+        """Build the prepared weights once (bmoe_prepare) and use them from now
+        on; a no-op for layers whose forward uses none."""
+        torch = _torch()
+        need = self.prepared_bytes()
+        self.struct.prepared, self.struct.prepared_bytes = None, 0
+        if need == 0:
+            self._prep = None
+            return self
+        buf = torch.empty(need + 256, dtype=torch.uint8, device=self.w_gate.device)
+        off = (-int(buf.data_ptr())) % 256
+        view = buf[off:off + need]
+        _check(lib().bmoe_prepare(ctypes.byref(self.struct), _ptr(view), need, _stream_handle()))
+        self._prep = buf
+        self.struct.prepared, self.struct.prepared_bytes = _ptr(view), need
+        return self
+
+    def unprepare(self):
+        """Go back to building the prepared data inside every forward."""
+        self.struct.prepared, self.struct.prepared_bytes = None, 0
+        self._prep = None
+        return self
 
     # ---------------------------------------------------------------- workspace
     def workspace_size(self, T: int) -> int:

@@ -110,9 +110,17 @@ bmoe_status check_layer(const bmoe_layer* L) {
   return BMOE_OK;
 }
 
+bmoe_status check_prepared(const bmoe_layer* L, size_t need) {
+  if (!L->prepared || need == 0) return BMOE_OK;
+  if (!aligned(L->prepared, 256)) return fail(BMOE_ERR_ALIGN, "prepared is not 256-byte aligned");
+  if (L->prepared_bytes < need)
+    return fail(BMOE_ERR_WORKSPACE, "prepared buffer has %zu bytes, %zu needed", L->prepared_bytes, need);
+  return BMOE_OK;
+}
+
 // Workspace layout (offsets in bytes, each 256-byte aligned).
 struct Plan {
-  size_t offsets, perm, idx, gate, bufU, bufZ, wbytes, fac, total;
+  size_t offsets, perm, idx, gate, bufU, bufZ, prep, total;
   bool fused, mfma;
   int64_t R;
 };
@@ -126,6 +134,24 @@ bool use_fused(const bmoe_layer* L) {
 }
 // ... with the rotations as block factors on the matrix cores (widths 256, 512)
 bool use_fused_mfma(const bmoe_layer* L) { return use_fused(L) && fused_mfma_supported(ilog2(L->d_model)); }
+
+// Prepared-weights buffer: [substrate re-encoded | rotation factors], 256-aligned.
+struct PrepLayout {
+  size_t w_off, w_len, fac_off, fac_len, total;
+  bool fp4;
+};
+
+PrepLayout prep_layout(const bmoe_layer* L) {
+  PrepLayout q{};
+  if (!use_fused(L)) return q;
+  const size_t d = size_t(L->d_model);
+  q.fp4 = use_fused_mfma(L);
+  q.w_len = d * d / (q.fp4 ? 2 : 1);
+  q.fac_off = align256(q.w_len);
+  q.fac_len = q.fp4 ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(L->d_model)) : 0;
+  q.total = align256(q.fac_off + q.fac_len);
+  return q;
+}
 
 Plan make_plan(const bmoe_layer* L, int32_t T) {
   Plan p{};
@@ -146,8 +172,7 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
   p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
   p.mfma = use_fused_mfma(L);
-  p.wbytes = take(p.fused ? size_t(d) * d / (p.mfma ? 2 : 1) : 0);  // substrate: byte or fp4 per weight
-  p.fac = take(p.mfma ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(d)) : 0);
+  p.prep = (p.fused && !L->prepared) ? take(prep_layout(L).total) : 0;  // prepared data built per call
   p.total = o;
   p.R = R;
   return p;
@@ -169,6 +194,8 @@ bmoe_status validate_call(const bmoe_layer* L, const void* x, int32_t T, void* w
   bmoe_status st = check_layer(L);
   if (st != BMOE_OK) return st;
   if (T < 0 || T > kMaxTokens) return fail(BMOE_ERR_SHAPE, "T=%d must be in [0, %d]", T, kMaxTokens);
+  st = check_prepared(L, prep_layout(L).total);
+  if (st != BMOE_OK) return st;
   plan = make_plan(L, T);
   if (T == 0) return BMOE_OK;
   if (!x) return fail(BMOE_ERR_NULL, "x is NULL");
@@ -187,8 +214,7 @@ bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* id
   const int act = L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
   RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates};
   BMOE_HIP(launch_route(ra, act, s));
-  BucketArgs ba{idx, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts,
-                nullptr, nullptr, 0, 0};
+  BucketArgs ba{idx, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -233,7 +259,37 @@ bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* byte
   bmoe_status st = check_layer(layer);
   if (st != BMOE_OK) return st;
   if (T < 0 || T > kMaxTokens) return fail(BMOE_ERR_SHAPE, "T=%d must be in [0, %d]", T, kMaxTokens);
+  st = check_prepared(layer, prep_layout(layer).total);
+  if (st != BMOE_OK) return st;
   *bytes = make_plan(layer, T).total;
+  return ok();
+}
+
+size_t bmoe_prepared_bytes(const bmoe_layer* layer) {
+  if (check_layer(layer) != BMOE_OK) return 0;
+  return prep_layout(layer).total;
+}
+
+bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, hipStream_t stream) {
+  bmoe_status st = check_layer(layer);
+  if (st != BMOE_OK) return st;
+  const PrepLayout q = prep_layout(layer);
+  if (q.total == 0) return ok();
+  if (!prepared) return fail(BMOE_ERR_NULL, "prepared is NULL");
+  if (!aligned(prepared, 256)) return fail(BMOE_ERR_ALIGN, "prepared is not 256-byte aligned");
+  if (bytes < q.total) return fail(BMOE_ERR_WORKSPACE, "prepared buffer has %zu bytes, %zu needed", bytes, q.total);
+  const int64_t d = layer->d_model, N = layer->n_experts;
+  const Range rp{prepared, q.total};
+  const size_t angle_bytes = size_t(N) * ilog2(d) * (d / 2) * 4;
+  if (overlap(rp, Range{layer->w_base[0], size_t(d) * d / 4}) || overlap(rp, Range{layer->theta[0], angle_bytes}) ||
+      overlap(rp, Range{layer->phi[0], angle_bytes}))
+    return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+  unsigned char* buf = static_cast<unsigned char*>(prepared);
+  PrepArgs pa{layer->w_base[0], buf + q.w_off, int32_t(d * d / 16), q.fp4 ? 1 : 0, layer->theta[0],
+              layer->phi[0], buf + q.fac_off, q.fp4 ? ilog2(d) : 0, int32_t(N)};
+  BMOE_HIP(launch_prep(pa, stream));
   return ok();
 }
 
@@ -268,10 +324,10 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T, int32_
 // Kernel launches of one forward, in order (marks[i] follows launch i-1).
 static int forward_kernel_names(const bmoe_layer* L, const char** names) {
   int n = 0;
+  if (use_fused(L) && !L->prepared) names[n++] = "prep";
   names[n++] = "route";
   names[n++] = "bucket";
   if (use_fused(L)) {
-    if (use_fused_mfma(L)) names[n++] = "factors";
     names[n++] = "fused";
     if (L->top_k > 1) names[n++] = "combine";
     return n;
@@ -338,22 +394,33 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   void* bufZ = at<char>(workspace, p.bufZ);
   const int Ld = ilog2(d);
 
+  // prepared weights (fused square experts): given, or built here
+  const bool fused = p.fused;
+  const unsigned char* wbytes = nullptr;
+  const unsigned char* fac = nullptr;
+  if (fused) {
+    const PrepLayout q = prep_layout(layer);
+    const unsigned char* base = static_cast<const unsigned char*>(layer->prepared);
+    if (!base) {
+      unsigned char* buf = at<unsigned char>(workspace, p.prep);
+      PrepArgs pa{layer->w_base[0], buf + q.w_off, int32_t(int64_t(d) * d / 16), q.fp4 ? 1 : 0,
+                  layer->theta[0], layer->phi[0], buf + q.fac_off, p.mfma ? Ld : 0, N};
+      BMOE_LAUNCH(launch_prep(pa, stream));
+      base = buf;
+    }
+    wbytes = base + q.w_off;
+    fac = p.mfma ? base + q.fac_off : nullptr;
+  }
   // router and bucketing
   RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates};
   BMOE_LAUNCH(launch_route(ra, act, stream));
-  const bool fused = p.fused;
-  unsigned char* wbytes = fused ? at<unsigned char>(workspace, p.wbytes) : nullptr;
-  BucketArgs ba{idx, offsets, perm, R, N, fused ? layer->w_base[0] : nullptr, wbytes,
-                fused ? int32_t(int64_t(d) * d / 16) : 0, p.mfma ? 1 : 0};
+  BucketArgs ba{idx, offsets, perm, R, N};
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
     void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);
-    unsigned char* fac = p.mfma ? at<unsigned char>(workspace, p.fac) : nullptr;
     FusedArgs fa{x, yslot_f, layer->theta[0], layer->phi[0], wbytes, fac, offsets, perm, gate,
                  layer->w_scale[0], R, N, k};
     if (p.mfma) {
-      FactorArgs fc{layer->theta[0], layer->phi[0], fac, N};
-      BMOE_LAUNCH(launch_factors(fc, ilog2(d), stream));
       BMOE_LAUNCH(launch_fused_mfma(fa, ilog2(d), stream));
     } else {
       BMOE_LAUNCH(launch_fused_square(fa, ilog2(d), stream));

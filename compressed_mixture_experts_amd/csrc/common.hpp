@@ -100,13 +100,21 @@ struct BucketArgs {
   int32_t* offsets;         // [N+1]
   int32_t* perm;            // [R] bucket position -> flat slot
   int32_t R, N;
-  // optional substrate unpack of w_words 2-bit words (16 weights each) into
-  // w_bytes: one byte per weight (bf16 high byte of +-0.5 / 0) when w_fp4 == 0,
-  // one fp4 e2m1 nibble per weight (low nibble first) when w_fp4 == 1
-  const uint32_t* w_packed;
-  unsigned char* w_bytes;
+};
+
+// Weight preparation for the fused square-expert kernels (once per weight set,
+// or per call when no prepared buffer is given).
+struct PrepArgs {
+  const uint32_t* w_packed; // 2-bit substrate, d*d/16 words (16 weights each)
+  unsigned char* w_out;     // w_fp4 == 0: [d][d] bytes (bf16 high byte of +-0.5 / 0);
+                            // w_fp4 == 1: [d][d/2] fp4 e2m1 nibbles, low nibble first
   int32_t w_words;
   int32_t w_fp4;
+  const float* theta;       // [N][L][n/2]
+  const float* phi;         // [N][L][n/2]
+  unsigned char* fac;       // [N][factor_bytes_per_expert] (matrix-core kernel only)
+  int32_t fac_log2n;        // 8 or 9 (0: no factors)
+  int32_t n_experts;
 };
 
 struct FusedArgs {
@@ -157,20 +165,14 @@ struct CombineArgs {
 
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
-struct FactorArgs {
-  const float* theta;       // [N][L][n/2]
-  const float* phi;         // [N][L][n/2]
-  unsigned char* fac;       // [N][factor_bytes_per_expert]
-  int32_t n_experts;
-};
 
 bool fused_square_supported(int log2n);
 bool fused_mfma_supported(int log2n);
 size_t factor_bytes_per_expert(int log2n);
-hipError_t launch_factors(const FactorArgs& a, int log2n, hipStream_t s);
 hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s);
 hipError_t launch_fused_square(const FusedArgs& a, int log2n, hipStream_t s);
 

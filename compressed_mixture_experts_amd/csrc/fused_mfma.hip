@@ -12,9 +12,10 @@
 // then needs 16 + P small dense products per rotation, done on MFMA in bf16
 // with fp32 accumulation, instead of (n/2) L scalar rotations per row.
 //
-// factor_kernel builds, per expert, the blocks in the exact per-lane order of
-// the MFMA operands (bf16): the transposed blocks of theta (input rotation
-// B(theta)^T = G_A^T G_B^T) and the blocks of phi (output rotation G_B G_A).
+// The blocks come from the bucketing kernel (mfma_factors.hpp), in the exact
+// per-lane order of the MFMA operands (bf16): the transposed blocks of theta
+// (input rotation B(theta)^T = G_A^T G_B^T) and the blocks of phi (output
+// rotation G_B G_A).
 //
 // fused_mfma_kernel, one workgroup (4 waves) per tile of 32 bucketed rows of one
 // expert.  Two bf16 LDS buffers of 32 rows alternate:
@@ -26,135 +27,13 @@
 //   G_B      wave (tb, h): classes p of half h, * gate * alpha   -> buf0 [row][i]
 //   store    buf0 rows -> per-slot rows
 // LDS is 2 x 32 rows (~66 KiB), so two workgroups share a CU.
-#include "common.hpp"
+#include "mfma_factors.hpp"
 
 namespace bmoe {
 
-constexpr int FM_RT = 32;        // rows per tile
 constexpr int FM_THREADS = 256;  // four waves
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-template <int L>
-struct MfCfg {
-  static constexpr int n = 1 << L;
-  static constexpr int LA = L == 9 ? 5 : 4;    // stages in G_A
-  static constexpr int PA = 1 << LA;           // G_A block width
-  static constexpr int NM = n / PA;            // G_A blocks = G_B block width
-  static constexpr int NP = PA;                // G_B blocks (classes)
-  static constexpr int HA = PA / 16;           // 16-row halves of a G_A block
-  static constexpr int KA = PA / 4;            // contraction values per lane in a G_A MFMA
-  static constexpr int TS = 2 * n + 16;        // LDS row stride in bytes
-  static constexpr size_t buf_bytes = size_t(FM_RT) * TS;
-  static constexpr size_t lds_bytes = 2 * buf_bytes;
-  static constexpr size_t gb_bytes = size_t(NP) * 64 * 4 * 2;        // one G_B set
-  static constexpr size_t ga_bytes = size_t(NM) * HA * 64 * KA * 2;  // one G_A set
-  // per expert: [G_B^T(theta) | G_A^T(theta) | G_A(phi) | G_B(phi)]
-  static constexpr size_t off_bt = 0, off_at = gb_bytes, off_ap = gb_bytes + ga_bytes,
-                          off_bp = gb_bytes + 2 * ga_bytes;
-  static constexpr size_t per_expert = 2 * (gb_bytes + ga_bytes);
-  static_assert(NM == 16, "G_B blocks are 16 wide");
-};
-
-size_t factor_bytes_per_expert(int log2n) {
-  switch (log2n) {
-    case 8: return MfCfg<8>::per_expert;
-    case 9: return MfCfg<9>::per_expert;
-    default: return 0;
-  }
-}
-
-__device__ __forceinline__ int stage_pair_index(int i, int s) {
-  return ((i >> (s + 1)) << s) | (i & ((1 << s) - 1));
-}
-
-// Apply stages [S_LO, S_HI) (local bit = s - S_LO) to a W-vector whose entry b
-// sits at global index base + stride * b.  FWD: stages in increasing order with
-// [[c, -s], [s, c]]; otherwise decreasing order with the transposed rotation.
-template <int W, int S_LO, int S_HI, bool FWD>
-__device__ __forceinline__ void rotate_vec(float (&v)[W], const float2* cs, int half, int base, int stride) {
-#pragma unroll
-  for (int k = 0; k < S_HI - S_LO; ++k) {
-    const int s = FWD ? S_LO + k : S_HI - 1 - k;
-    const int sl = s - S_LO;
-#pragma unroll
-    for (int q = 0; q < W / 2; ++q) {
-      const int b = ((q >> sl) << (sl + 1)) | (q & ((1 << sl) - 1));
-      const int i = base + stride * b;
-      const float2 r = cs[s * half + stage_pair_index(i, s)];
-      const float x = v[b], y = v[b + (1 << sl)];
-      if (FWD) {
-        v[b] = r.x * x - r.y * y;
-        v[b + (1 << sl)] = r.y * x + r.x * y;
-      } else {
-        v[b] = r.x * x + r.y * y;
-        v[b + (1 << sl)] = r.x * y - r.y * x;
-      }
-    }
-  }
-}
-
-constexpr int FAC_SPLIT = 4;  // workgroups per (expert, angle set)
-
-// grid (N, 2, FAC_SPLIT): blockIdx.y = 0 builds the theta set, 1 the phi set;
-// blockIdx.z takes every FAC_SPLIT-th job.  (cos, sin) come from the hardware
-// transcendental unit: their error (~1e-6) is far below the bf16 rounding of
-// the factors.
-template <int L>
-__global__ __launch_bounds__(FM_THREADS) void factor_kernel(FactorArgs a) {
-  using C = MfCfg<L>;
-  constexpr int n = C::n, half = n / 2, PA = C::PA, KA = C::KA, HA = C::HA;
-  __shared__ float2 cs[L * half];
-  const int e = blockIdx.x;
-  const bool th = blockIdx.y == 0;
-  const float* ang = (th ? a.theta : a.phi) + size_t(e) * L * half;
-  constexpr float inv2pi = 0.15915494309189535f;
-  for (int i = threadIdx.x; i < L * half; i += FM_THREADS) {
-    const float r = ang[i] * inv2pi;
-    cs[i] = make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
-  }
-  __syncthreads();
-  unsigned char* fe = a.fac + size_t(e) * C::per_expert;
-  const int j0 = blockIdx.z * FM_THREADS + threadIdx.x, js = FAC_SPLIT * FM_THREADS;
-
-  // G_A: theta -> column j of A_m (operand row j of A_m^T); phi -> row j of A_m
-  for (int job = j0; job < C::NM * PA; job += js) {
-    const int m = job / PA, j = job % PA;
-    float v[PA];
-#pragma unroll
-    for (int q = 0; q < PA; ++q) v[q] = q == j ? 1.0f : 0.0f;
-    if (th) rotate_vec<PA, 0, C::LA, true>(v, cs, half, PA * m, 1);
-    else rotate_vec<PA, 0, C::LA, false>(v, cs, half, PA * m, 1);
-    const int hq = j / 16, row = j % 16;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t h[KA / 2];
-#pragma unroll
-      for (int i = 0; i < KA; i += 2) {
-        // contraction index held by lane group g, slot i: 4g+i (PA 16);
-        // theta: 8g+i; phi (accumulator order of the substrate product): 4g+i, then 16+4g+i
-        auto kidx = [&](int ii) { return KA == 4 ? 4 * g + ii : th ? 8 * g + ii : (ii < 4 ? 4 * g + ii : 12 + 4 * g + ii); };
-        h[i / 2] = pack_bf16x2(v[kidx(i)], v[kidx(i + 1)]);
-      }
-      unsigned char* dst = fe + (th ? C::off_at : C::off_ap) + ((size_t(m) * HA + hq) * 64 + 16 * g + row) * KA * 2;
-      if constexpr (KA == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
-      else *reinterpret_cast<uint2*>(dst) = make_uint2(h[0], h[1]);
-    }
-  }
-  // G_B: theta -> column j of B_p (operand row j of B_p^T); phi -> row j of B_p
-  for (int job = j0; job < C::NP * 16; job += js) {
-    const int p = job / 16, j = job % 16;
-    float v[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = q == j ? 1.0f : 0.0f;
-    if (th) rotate_vec<16, C::LA, L, true>(v, cs, half, p, PA);
-    else rotate_vec<16, C::LA, L, false>(v, cs, half, p, PA);
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<uint2*>(fe + (th ? C::off_bt : C::off_bp) + (size_t(p) * 64 + 16 * g + j) * 8) =
-          make_uint2(pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
-  }
-}
 
 __device__ __forceinline__ uint32_t u4get(const uint4& v, int k) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
@@ -493,15 +372,7 @@ static hipError_t launch_fused_mfma_L(const FusedArgs& a, hipStream_t s) {
 
 bool fused_mfma_supported(int log2n) { return log2n == 8 || log2n == 9; }
 
-hipError_t launch_factors(const FactorArgs& a, int log2n, hipStream_t s) {
-  if (a.n_experts <= 0) return hipSuccess;
-  switch (log2n) {
-    case 8: hipLaunchKernelGGL(factor_kernel<8>, dim3(a.n_experts, 2, FAC_SPLIT), dim3(FM_THREADS), 0, s, a); break;
-    case 9: hipLaunchKernelGGL(factor_kernel<9>, dim3(a.n_experts, 2, FAC_SPLIT), dim3(FM_THREADS), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
+size_t factor_bytes_per_expert(int log2n) { return mf_factor_bytes(log2n); }
 
 hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;

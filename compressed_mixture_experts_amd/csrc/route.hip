@@ -811,42 +811,54 @@ hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ bucketing
-// One workgroup per expert e.  Pass 1 counts the routed slots of experts below
-// e (its first bucket position); pass 2 walks all slots in order and appends
-// the ones routed to e, so within an expert slots ascend.
+// One workgroup per expert e.  Every thread holds a contiguous range of routed
+// slots in registers (one load round per 64K slots); the count of slots routed
+// below e gives the first bucket position of e, an exclusive scan of the
+// threads' counts of slots routed to e gives each thread's positions, so within
+// an expert slots ascend.
 constexpr int BK_THREADS = 1024;
+constexpr int BK_Q = 16;  // int4 of slots per thread per round
+constexpr int BK_ROUND = 4 * BK_Q * BK_THREADS;
+
+__device__ __forceinline__ int bk_block_sum(int v, int* s_w) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) s_w[wave] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < BK_THREADS / 64; ++w) t += s_w[w];
+  return t;
+}
+
+// exclusive prefix of v over the threads in order; `total` gets the sum
+__device__ __forceinline__ int bk_block_scan(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  int pre = 0, t = 0;
+#pragma unroll
+  for (int w = 0; w < BK_THREADS / 64; ++w) {
+    const int y = s_w[w];
+    pre += (w < wave) ? y : 0;
+    t += y;
+  }
+  total = t;
+  return pre + x - v;
+}
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   __shared__ int s_w[BK_THREADS / 64];
-  __shared__ int s_off;
   const int e = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // optional: unpack the 2-bit substrate (16 weights per word) into one byte
-  // per weight holding the high byte of its bf16 value scaled by 1/2
-  // (+1 -> 0x3F, -1 -> 0xBF, 0 -> 0), or into fp4 e2m1 nibbles (+1 -> 0x2,
-  // -1 -> 0xA, 0 -> 0; weight 2b in the low nibble of byte b)
-  for (int w = e * BK_THREADS + tid; w < a.w_words; w += gridDim.x * BK_THREADS) {
-    const uint32_t P = a.w_packed[w];
-    uint32_t code[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int j = c >> 1, h = c & 1;
-      const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = (P >> (16 * h + 8 + j)) & 1u;
-      code[c] = a.w_fp4 ? nz * (0x2u | (sg << 3)) : nz * (0x3Fu | (sg << 7));
-    }
-    if (a.w_fp4) {
-      uint32_t o[2] = {0u, 0u};
-#pragma unroll
-      for (int c = 0; c < 16; ++c) o[c >> 3] |= code[c] << (4 * (c & 7));
-      reinterpret_cast<uint2*>(a.w_bytes)[w] = make_uint2(o[0], o[1]);
-    } else {
-      uint32_t o[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int c = 0; c < 16; ++c) o[c >> 2] |= code[c] << (8 * (c & 3));
-      reinterpret_cast<uint4*>(a.w_bytes)[w] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  }
+  const int tid = threadIdx.x;
 
   auto load4 = [&](int f0) -> int4 {
     if (f0 + 3 < a.R) return *reinterpret_cast<const int4*>(a.topk_idx + f0);
@@ -857,70 +869,46 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
     q.w = (f0 + 3 < a.R) ? a.topk_idx[f0 + 3] : 0x7fffffff;
     return q;
   };
-
-  // The routed slots are read in blocks of BK_BATCH int4 per thread, all
-  // loads of a block issued before any is used.
-  constexpr int BK_BATCH = 8;
-  const int span = 4 * BK_THREADS * BK_BATCH;
-  int lt = 0;
-  for (int b0 = 0; b0 < a.R; b0 += span) {
-    int4 q[BK_BATCH];
+  int base = 0;     // slots routed below e
+  int running = 0;  // slots routed to e in earlier rounds
+  for (int r0 = 0; r0 < a.R; r0 += BK_ROUND) {
+    // thread t holds slots [r0 + 4 nq t, r0 + 4 nq (t+1))
+    const int nq = (min(a.R - r0, BK_ROUND) + 4 * BK_THREADS - 1) / (4 * BK_THREADS);
+    int4 q[BK_Q];
 #pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) q[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
-#pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) lt += (q[b].x < e) + (q[b].y < e) + (q[b].z < e) + (q[b].w < e);
-  }
-  lt = wave_sum(lt);
-  if (lane == 0) s_w[wave] = lt;
-  __syncthreads();
-  if (tid == 0) {
-    int o = 0;
-    for (int w = 0; w < BK_THREADS / 64; ++w) o += s_w[w];
-    s_off = o;
-    a.offsets[e] = o;
-    if (e == a.N - 1) a.offsets[a.N] = a.R;
-  }
-  __syncthreads();
-  const int off = s_off;
-  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int running = 0;
-  for (int b0 = 0; b0 < a.R; b0 += span) {
-    int4 qb[BK_BATCH];
-#pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) qb[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
-#pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) {
-      const int f0 = b0 + 4 * (b * BK_THREADS + tid);
-      if (b0 + 4 * b * BK_THREADS >= a.R) break;  // uniform
-      const int v[4] = {qb[b].x, qb[b].y, qb[b].z, qb[b].w};
-      int c = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c += (v[j] == e);
-      const uint64_t m0 = __ballot(c & 1), m1 = __ballot(c & 2), m2 = __ballot(c & 4);
-      const int lpre = __popcll(m0 & ltmask) + 2 * __popcll(m1 & ltmask) + 4 * __popcll(m2 & ltmask);
-      const int wtot = __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2);
-      __syncthreads();
-      if (lane == 0) s_w[wave] = wtot;
-      __syncthreads();
-      int wpre = 0, tot = 0;
-      for (int w = 0; w < BK_THREADS / 64; ++w) {
-        const int x = s_w[w];
-        wpre += (w < wave) ? x : 0;
-        tot += x;
-      }
-      if (c) {
-        int qq = off + running + wpre + lpre;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (v[j] == e) a.perm[qq++] = f0 + j;
-      }
-      running += tot;
+    for (int i = 0; i < BK_Q; ++i) {
+      const int f0 = r0 + 4 * (nq * tid + i);
+      q[i] = (i < nq && f0 < a.R) ? load4(f0) : make_int4(0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff);
     }
+    int lt = 0, ce = 0;
+#pragma unroll
+    for (int i = 0; i < BK_Q; ++i) {
+      lt += (q[i].x < e) + (q[i].y < e) + (q[i].z < e) + (q[i].w < e);
+      ce += (q[i].x == e) + (q[i].y == e) + (q[i].z == e) + (q[i].w == e);
+    }
+    base += bk_block_sum(lt, s_w);
+    int tot;
+    const int pre = bk_block_scan(ce, s_w, tot);
+    if (ce) {
+      int pos = running + pre;
+#pragma unroll
+      for (int i = 0; i < BK_Q; ++i) {
+        const int f0 = r0 + 4 * (nq * tid + i);
+        if (q[i].x == e) a.perm[base + pos++] = f0;
+        if (q[i].y == e) a.perm[base + pos++] = f0 + 1;
+        if (q[i].z == e) a.perm[base + pos++] = f0 + 2;
+        if (q[i].w == e) a.perm[base + pos++] = f0 + 3;
+      }
+    }
+    running += tot;
+  }
+  if (tid == 0) {
+    a.offsets[e] = base;
+    if (e == a.N - 1) a.offsets[a.N] = a.R;
   }
 }
 
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
-  if (a.R <= 0) return hipSuccess;
   hipLaunchKernelGGL(bucket_kernel, dim3(a.N), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }

@@ -62,7 +62,7 @@ typedef enum bmoe_status {
   BMOE_ERR_DTYPE = 3,       /* unknown dtype / activation code                 */
   BMOE_ERR_ALIGN = 4,       /* a pointer is not aligned as required            */
   BMOE_ERR_ALIAS = 5,       /* an output overlaps an input or the workspace    */
-  BMOE_ERR_WORKSPACE = 6,   /* workspace smaller than bmoe_workspace_size()    */
+  BMOE_ERR_WORKSPACE = 6,   /* workspace / prepared buffer smaller than needed */
   BMOE_ERR_TERNARY = 7,     /* a substrate value is not in {-1, 0, +1}         */
   BMOE_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed      */
   BMOE_ERR_DEVICE = 9       /* the current device is not a gfx950 GPU          */
@@ -100,6 +100,9 @@ typedef struct bmoe_layer {
   const float* phi[2];      /* output-side angles of substrate m:
                                [n_experts][log2 d_out][d_out/2]                 */
   float w_scale[2];         /* scalar multiplying substrate m (normally 1.0)    */
+  const void* prepared;     /* NULL, or a buffer filled by bmoe_prepare for these
+                               weights (256-byte aligned, device memory)       */
+  size_t prepared_bytes;    /* its size (ignored when prepared is NULL)         */
 } bmoe_layer;
 
 /* Number of 32-bit words bmoe_pack_ternary writes for a rows x cols matrix
@@ -118,8 +121,29 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int32_t rows, int32_t cols,
                               uint32_t* out, size_t out_words);
 
 /* Bytes of device workspace bmoe_route / bmoe_forward need for T tokens.
- * Depends only on the layer's sizes and T. */
+ * Depends on the layer's sizes, T and whether layer->prepared is set. */
 bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* bytes);
+
+/* Size of the prepared-weights buffer of this layer, 0 when its forward path
+ * uses none (or the layer is invalid).  Square bf16 layers of width 64..512
+ * use one: the substrate re-encoded for the expert kernel (one byte per weight
+ * at widths 64 and 128, one fp4 e2m1 nibble per weight at 256 and 512) and, at
+ * widths 256 and 512, every expert's rotations as block-diagonal factors in
+ * bf16 (stages below bit 5 at width 512 / bit 4 at width 256 as one block per
+ * group of 32 / 16 consecutive indices, the stages above as 16 x 16 blocks).
+ * These depend on the weights only (ButterflyMoE zh §2.1-§2.2: ternary
+ * substrate, per-expert Givens angles). */
+size_t bmoe_prepared_bytes(const bmoe_layer* layer);
+
+/* Fill `prepared` (device, 256-byte aligned, at least bmoe_prepared_bytes) for
+ * the weights of `layer` (layer->prepared itself is ignored), enqueued on
+ * `stream`.  Afterwards set layer->prepared / prepared_bytes to skip this work
+ * in every bmoe_forward; it stays valid while the weights are unchanged.
+ * A layer that uses no prepared buffer returns BMOE_OK and writes nothing.
+ * Errors: those of the layer checks, BMOE_ERR_NULL, BMOE_ERR_ALIGN,
+ * BMOE_ERR_WORKSPACE (buffer too small), BMOE_ERR_ALIAS (buffer overlaps a
+ * weight array), BMOE_ERR_DEVICE, BMOE_ERR_HIP. */
+bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, hipStream_t stream);
 
 /* Router and per-expert bucketing only.
  *   x              [T][d_model] act_dtype
@@ -141,8 +165,12 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T,
  *   x  [T][d_model] act_dtype;  y [T][d_model] act_dtype (must not overlap x,
  *   the workspace or the optional outputs);
  *   topk_idx / topk_gate: optional [T][top_k] outputs as in bmoe_route.
- * Intermediates between the steps are kept in act_dtype; rotations, GELU and
- * accumulation run in fp32. */
+ * Intermediates between the steps are kept in act_dtype; GELU and
+ * accumulation run in fp32.  Rotations run in fp32, except in square bf16
+ * layers of width 256 and 512, whose rotations are products with the bf16
+ * block factors described at bmoe_prepared_bytes (fp32 accumulation, bf16
+ * rounding between the two factors).  Without layer->prepared the call
+ * builds the prepared data in the workspace first. */
 bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void* y,
                          int32_t* topk_idx, float* topk_gate,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);

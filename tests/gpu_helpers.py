@@ -39,9 +39,11 @@ def tol_for(act):
     return 1e-4 if act == "f32" else 2e-2
 
 
-def run_layer(inp, return_routing=True):
+def run_layer(inp, return_routing=True, prepared=False):
     import torch
     layer = bm.Layer.from_inputs(inp, device="cuda")
+    if prepared:
+        layer.prepare()
     x = to_dev(inp.x, inp.cfg.act)
     out = layer.forward(x, return_routing=return_routing)
     torch.cuda.synchronize()

@@ -206,3 +206,51 @@ def test_status_strings():
     L = bm.lib()
     for code, name in bm.STATUS.items():
         assert L.bmoe_status_string(code).decode().startswith(name)
+
+
+def test_prepared_bytes_layout():
+    L = bm.lib()
+    # square bf16 width 512: fp4 substrate d*d/2 plus 98304 factor bytes per expert
+    s = make_struct()
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 512 * 512 // 2 + 64 * 98304
+    s = make_struct(d_model=256)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 256 * 256 // 2 + 64 * 32768
+    # widths 64 / 128: one byte per weight, no factors (rounded up to 256 bytes)
+    s = make_struct(d_model=128)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 128 * 128
+    # fp32 activations, FFN layers and invalid layers use none
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(act_dtype=bm.F32))) == 0
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF))) == 0
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=100))) == 0
+
+
+def test_prepare_argument_errors():
+    L = bm.lib()
+    s = make_struct()
+    need = L.bmoe_prepared_bytes(ctypes.byref(s))
+    buf = FAKE + 0x10000000
+    assert L.bmoe_prepare(ctypes.byref(s), None, need, None) == 1
+    assert L.bmoe_prepare(ctypes.byref(s), buf + 128, need, None) == 4
+    assert L.bmoe_prepare(ctypes.byref(s), buf, need - 1, None) == 6
+    assert L.bmoe_prepare(ctypes.byref(s), FAKE + 0x100000 - 256, need, None) == 5   # over w_base[0]
+    assert L.bmoe_prepare(ctypes.byref(make_struct(d_model=100)), buf, need, None) == 2
+    # a layer without prepared data: nothing to do
+    assert L.bmoe_prepare(ctypes.byref(make_struct(act_dtype=bm.F32)), None, 0, None) == 0
+    # valid arguments reach the device check (no GPU here)
+    assert L.bmoe_prepare(ctypes.byref(s), buf, need, None) in (8, 9)
+
+
+def test_forward_checks_prepared_buffer():
+    L = bm.lib()
+    s = make_struct()
+    need = L.bmoe_prepared_bytes(ctypes.byref(s))
+    n_plain = ws_size(s, 4096)[1]
+    s.prepared, s.prepared_bytes = FAKE + 0x10000000, need
+    st, n_prep = ws_size(s, 4096)
+    # prepared data no longer needs room in the workspace
+    assert st == 0 and n_plain - n_prep >= need - 256
+    assert call_forward(s) in (8, 9)
+    s.prepared_bytes = need - 1
+    assert call_forward(s) == 6 and ws_size(s, 16)[0] == 6
+    s.prepared, s.prepared_bytes = FAKE + 0x10000000 + 64, need
+    assert call_forward(s) == 4

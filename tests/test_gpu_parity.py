@@ -274,3 +274,43 @@ def test_route_matches_forward_routing():
     _, i2, g2 = layer.forward(x, return_routing=True)
     torch.cuda.synchronize()
     assert torch.equal(i1, i2) and torch.equal(g1, g2)
+
+
+# Prepared weights (bmoe_prepare, done once per weight set) must give exactly the
+# results of the per-call preparation: same kernels on the same bytes.
+PREP_CASES = [
+    dict(d_model=512, n_experts=64, top_k=2, tokens=700),   # matrix-core expert kernel
+    dict(d_model=256, n_experts=9, top_k=3, tokens=333),
+    dict(d_model=128, n_experts=5, top_k=2, tokens=200),    # fp32-rotation expert kernel
+    dict(d_model=64, n_experts=3, top_k=1, tokens=65),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREP_CASES)))
+def test_prepared_matches_per_call(case):
+    import torch
+    kw = PREP_CASES[case]
+    cfg = wl.small_config(seed_index=400 + case, act="bf16", **kw)
+    log(f"prepared vs per call {cfg.name}")
+    inp = wl.generate(cfg)
+    layer = bm.Layer.from_inputs(inp, device="cuda")
+    x = to_dev(inp.x, cfg.act)
+    assert "prep" in layer.kernel_names()
+    y0, i0, g0 = layer.forward(x, return_routing=True)
+    layer.prepare()
+    assert layer.struct.prepared and layer.prepared_bytes() > 0
+    assert "prep" not in layer.kernel_names()
+    y1, i1, g1 = layer.forward(x, return_routing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1) and torch.equal(g0, g1)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    check_forward(inp, y1, i1, g1)
+
+
+@pytest.mark.parametrize("ci", [1, 2])
+def test_forward_configs_prepared(ci):
+    cfg = wl.CONFIGS[ci]
+    log(f"forward config {cfg.name} with prepared weights")
+    inp = wl.generate(cfg)
+    _, _, (y, idx, gate) = run_layer(inp, prepared=True)
+    check_forward(inp, y, idx, gate)
