@@ -160,6 +160,19 @@ def test_route_skewed_and_tied():
     assert counts.max() > 1.5 * counts.mean()  # the load really is skewed
 
 
+def test_route_buckets_beyond_one_round():
+    # more routed slots than one bucketing round (65536): bucket bases must
+    # count the slots of lower experts in every round
+    import torch
+    cfg = wl.small_config(d_model=64, n_experts=8, top_k=2, tokens=40000, act="bf16", seed_index=6)
+    inp = wl.generate(cfg, gate_mode="skewed")
+    layer = bm.Layer.from_inputs(inp)
+    log("route 80000 slots")
+    idx, gate, off, slots = layer.route(to_dev(inp.x, cfg.act), with_buckets=True)
+    torch.cuda.synchronize()
+    check_routing(inp, idx.cpu().numpy(), gate.cpu().numpy(), off.cpu().numpy(), slots.cpu().numpy())
+
+
 # ------------------------------------------------------------------ layer forward
 def check_forward(inp, y, idx, gate, tokens=None):
     cfg = inp.cfg
