@@ -811,27 +811,14 @@ hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ bucketing
-// One workgroup per expert e; the routed slots are read in rounds of up to 64K
-// (each thread holds 16 int4, wave-contiguous, so every load instruction reads
-// 1 KiB in one piece).  The first bucket position of e is the number of slots
-// routed below e (counted in a first pass when there is more than one round).
-// A slot routed to e goes to that base plus the number of slots routed to e
-// before it, from ballots inside each wave and a table of per-(load, wave)
-// counts scanned once per round, so within an expert slots ascend.
+// One workgroup per expert e.  Pass 1 counts the routed slots of experts below
+// e (its first bucket position); pass 2 walks all slots in order and appends
+// the ones routed to e, so within an expert slots ascend.
 constexpr int BK_THREADS = 1024;
-constexpr int BK_WAVES = BK_THREADS / 64;
-constexpr int BK_Q = 16;  // int4 of slots per thread per round
-constexpr int BK_ROUND = 4 * BK_Q * BK_THREADS;
-
-// set bits of a wave mask below this lane
-__device__ __forceinline__ int mbcnt64(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-}
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
-  __shared__ int s_c[BK_Q * BK_WAVES];  // counts, then exclusive prefixes, in (load, wave) order
-  __shared__ int s_lt[BK_WAVES];
-  __shared__ int s_tot;
+  __shared__ int s_w[BK_THREADS / 64];
+  __shared__ int s_off;
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -844,112 +831,70 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
     q.w = (f0 + 3 < a.R) ? a.topk_idx[f0 + 3] : 0x7fffffff;
     return q;
   };
-  // load i of a round starting at r0: slots r0 + 4 (i BK_THREADS + tid) .. +3
-  auto load_round = [&](int r0, int4 (&q)[BK_Q]) {
-#pragma unroll
-    for (int i = 0; i < BK_Q; ++i) {
-      const int f0 = r0 + 4 * (i * BK_THREADS + tid);
-      q[i] = f0 < a.R ? load4(f0) : make_int4(0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff);
-    }
-  };
-  auto count_below = [&](const int4 (&q)[BK_Q]) {
-    int lt = 0;
-#pragma unroll
-    for (int i = 0; i < BK_Q; ++i) lt += (q[i].x < e) + (q[i].y < e) + (q[i].z < e) + (q[i].w < e);
-    return lt;
-  };
-  auto block_sum = [&](int v) {
-    v = wave_sum(v);
-    __syncthreads();
-    if (lane == 0) s_lt[wave] = v;
-    __syncthreads();
-    int t = 0;
-#pragma unroll
-    for (int w = 0; w < BK_WAVES; ++w) t += s_lt[w];
-    return t;
-  };
 
-  int base = 0;
-  const bool multi = a.R > BK_ROUND;
-  if (multi) {
-    int lt = 0;
-    for (int r0 = 0; r0 < a.R; r0 += BK_ROUND) {
-      int4 q[BK_Q];
-      load_round(r0, q);
-      lt += count_below(q);
-    }
-    base = block_sum(lt);
+  // The routed slots are read in blocks of BK_BATCH int4 per thread, all
+  // loads of a block issued before any is used.
+  constexpr int BK_BATCH = 8;
+  const int span = 4 * BK_THREADS * BK_BATCH;
+  int lt = 0;
+  for (int b0 = 0; b0 < a.R; b0 += span) {
+    int4 q[BK_BATCH];
+#pragma unroll
+    for (int b = 0; b < BK_BATCH; ++b) q[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
+#pragma unroll
+    for (int b = 0; b < BK_BATCH; ++b) lt += (q[b].x < e) + (q[b].y < e) + (q[b].z < e) + (q[b].w < e);
   }
-  int running = 0;  // slots routed to e in earlier rounds
-  for (int r0 = 0; r0 < a.R; r0 += BK_ROUND) {
-    int4 q[BK_Q];
-    load_round(r0, q);
-    const int lt = multi ? 0 : count_below(q);
-    // loads of this round that hold slots (uniform)
-    const int nq = min(BK_Q, (a.R - r0 + 4 * BK_THREADS - 1) / (4 * BK_THREADS));
-    int lpre[BK_Q];
-#pragma unroll
-    for (int i = 0; i < BK_Q; ++i) {
-      lpre[i] = 0;
-      if (i < nq) {
-        const int c = (q[i].x == e) + (q[i].y == e) + (q[i].z == e) + (q[i].w == e);
-        const uint64_t m0 = __ballot(c & 1), m1 = __ballot(c & 2), m2 = __ballot(c & 4);
-        lpre[i] = mbcnt64(m0) + 2 * mbcnt64(m1) + 4 * mbcnt64(m2);
-        if (lane == 0) s_c[i * BK_WAVES + wave] = __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2);
-      } else if (lane == 0) {
-        s_c[i * BK_WAVES + wave] = 0;
-      }
-    }
-    const int ltw = wave_sum(lt);
-    if (lane == 0) s_lt[wave] = ltw;
-    __syncthreads();
-    if (wave == 0) {
-      // exclusive scan of the BK_Q x BK_WAVES counts (lane l: entries 4l .. 4l+3)
-      int v[4], sum = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[j] = s_c[4 * lane + j];
-        sum += v[j];
-      }
-      int x = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
-      int pre = x - sum;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s_c[4 * lane + j] = pre;
-        pre += v[j];
-      }
-      if (lane == 63) s_tot = x;
-    }
-    __syncthreads();
-    if (!multi) {
-#pragma unroll
-      for (int w = 0; w < BK_WAVES; ++w) base += s_lt[w];
-    }
-#pragma unroll
-    for (int i = 0; i < BK_Q; ++i) {
-      if (i >= nq) break;
-      const int f0 = r0 + 4 * (i * BK_THREADS + tid);
-      int pos = base + running + s_c[i * BK_WAVES + wave] + lpre[i];
-      if (q[i].x == e) a.perm[pos++] = f0;
-      if (q[i].y == e) a.perm[pos++] = f0 + 1;
-      if (q[i].z == e) a.perm[pos++] = f0 + 2;
-      if (q[i].w == e) a.perm[pos++] = f0 + 3;
-    }
-    running += s_tot;
-    __syncthreads();  // s_c / s_lt / s_tot reused by the next round
-  }
+  lt = wave_sum(lt);
+  if (lane == 0) s_w[wave] = lt;
+  __syncthreads();
   if (tid == 0) {
-    a.offsets[e] = base;
+    int o = 0;
+    for (int w = 0; w < BK_THREADS / 64; ++w) o += s_w[w];
+    s_off = o;
+    a.offsets[e] = o;
     if (e == a.N - 1) a.offsets[a.N] = a.R;
+  }
+  __syncthreads();
+  const int off = s_off;
+  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int running = 0;
+  for (int b0 = 0; b0 < a.R; b0 += span) {
+    int4 qb[BK_BATCH];
+#pragma unroll
+    for (int b = 0; b < BK_BATCH; ++b) qb[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
+#pragma unroll
+    for (int b = 0; b < BK_BATCH; ++b) {
+      const int f0 = b0 + 4 * (b * BK_THREADS + tid);
+      if (b0 + 4 * b * BK_THREADS >= a.R) break;  // uniform
+      const int v[4] = {qb[b].x, qb[b].y, qb[b].z, qb[b].w};
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c += (v[j] == e);
+      const uint64_t m0 = __ballot(c & 1), m1 = __ballot(c & 2), m2 = __ballot(c & 4);
+      const int lpre = __popcll(m0 & ltmask) + 2 * __popcll(m1 & ltmask) + 4 * __popcll(m2 & ltmask);
+      const int wtot = __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2);
+      __syncthreads();
+      if (lane == 0) s_w[wave] = wtot;
+      __syncthreads();
+      int wpre = 0, tot = 0;
+      for (int w = 0; w < BK_THREADS / 64; ++w) {
+        const int x = s_w[w];
+        wpre += (w < wave) ? x : 0;
+        tot += x;
+      }
+      if (c) {
+        int qq = off + running + wpre + lpre;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (v[j] == e) a.perm[qq++] = f0 + j;
+      }
+      running += tot;
+    }
   }
 }
 
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
+  if (a.R <= 0) return hipSuccess;
   hipLaunchKernelGGL(bucket_kernel, dim3(a.N), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }
