@@ -159,17 +159,28 @@ def main() -> int:
                     help="workload index (default: the d=512, 64-expert layer)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 5 times (HBM counter calibration) and exit")
     ap.add_argument("--per-call-prep", action="store_true",
                     help="re-encode the weights inside every forward instead of once")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the ButterflyMoE "
-              "forward shards over tokens with no exchange, so N GPUs each run this same step "
-              "on T/N tokens; multi-GPU runs are not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}): the ButterflyMoE forward "
+              "shards over tokens with no exchange between GPUs, so N GPUs would each run this "
+              "same step on their own T/N tokens.", file=sys.stderr)
         return 2
 
     import numpy as np
     import torch
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_mib": args.copy_probe, "copies": 5}))
+        return 0
     import compressed_mixture_experts_amd as bm
     from compressed_mixture_experts_amd import workloads as wl
 

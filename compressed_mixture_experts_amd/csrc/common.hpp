@@ -132,6 +132,15 @@ struct FusedArgs {
   int32_t rows, n_experts, top_k;
 };
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
+// map launch index bid (< nb) to a logical index so that each XCD gets one
+// contiguous range of logical indices (neighbouring tiles share its L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
 enum BflyMode { BFLY_DBG = 0, BFLY_IN = 1, BFLY_MID = 2, BFLY_OUT = 3 };
 
 struct BflyArgs {

@@ -97,8 +97,10 @@ __global__ __launch_bounds__(BF_THREADS, 2) void fused_square_kernel(FusedArgs a
     }
     int total;
     const int excl = block_excl_scan(nt, s_tmp, total);
-    if (tid < a.n_experts && t >= excl && t < excl + nt) {
-      const int j = t - excl;
+    // tiles of one expert are consecutive: keep them on one XCD
+    const int tl = t < total ? xcd_remap(t, total) : -1;
+    if (tid < a.n_experts && tl >= excl && tl < excl + nt) {
+      const int j = tl - excl;
       s_info[0] = tid;
       s_info[1] = off + j * FZ_RT;
       s_info[2] = min(FZ_RT, cnt - j * FZ_RT);

@@ -112,8 +112,10 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
     }
     int total;
     const int excl = fm_block_scan(nt, s_tmp, total);
-    if (tid < a.n_experts && int(blockIdx.x) >= excl && int(blockIdx.x) < excl + nt) {
-      const int j = blockIdx.x - excl;
+    // tiles of one expert are consecutive: keep them on one XCD
+    const int t = int(blockIdx.x) < total ? xcd_remap(blockIdx.x, total) : -1;
+    if (tid < a.n_experts && t >= excl && t < excl + nt) {
+      const int j = t - excl;
       s_info[0] = tid;
       s_info[1] = off + j * FM_RT;
       s_info[2] = min(FM_RT, cnt - j * FM_RT);

@@ -20,14 +20,6 @@ constexpr int GM_THREADS = 256;
 constexpr int GBK = 64;       // K per pipeline step
 constexpr int GLDK = GBK + 8; // padded LDS row (bf16 elements): conflict-free fragment reads
 
-// Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
-// contiguous range of logical tiles so tiles sharing an activation row-block
-// share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-}
 
 // Workgroup tile: TN substrate rows (output columns) x TM activation rows,
 // four waves in a 2 x 2 arrangement.  NS register sets keep the global loads
