@@ -78,13 +78,20 @@ def kernel_work(cfg):
     w["bucket"] = (4 * R + 4 * R + 4 * (N + 1), 0, "hbm")
     w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
 
+    def fp4_gemm(din, dout):
+        # bf16 products whose shape the fp4 matrix-core GEMM covers read the
+        # substrate prepared as fp4 (half a byte per weight)
+        return cfg.act == "bf16" and dout % 256 == 0 and din % 128 == 0
+
     def gemm(din, dout):
         fl = 2 * R * din * dout
-        by = R * din * s + R * dout * s + dout * din // 4
+        by = R * din * s + R * dout * s + dout * din // (2 if fp4_gemm(din, dout) else 4)
         return (by, fl, "mfma" if fl / by > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm")
 
     if f == 0:
         w["gemm"] = gemm(d, d)
+        if fp4_gemm(d, d) and Ld > 9:
+            w["prep"] = (d * d // 4 + d * d // 2, 0, "hbm")
         if cfg.act == "bf16" and Ld in (8, 9):
             # rotations as block factors on the matrix cores: per rotation one
             # P x P and one 16 x 16 product per 32-wide / 16-wide block of a row
@@ -103,6 +110,9 @@ def kernel_work(cfg):
         w["gemm_up"] = gemm(d, f)
         w["bfly_mid"] = (2 * R * f * s + 2 * N * Lf * (f // 2) * 4, 2 * 6 * R * (f // 2) * Lf, "hbm")
         w["gemm_down"] = gemm(f, d)
+        pw = sum(a * b // 4 + a * b // 2 for a, b in ((d, f), (f, d)) if fp4_gemm(a, b))
+        if pw:
+            w["prep"] = (pw, 0, "hbm")
     w["bfly_out"] = (2 * R * d * s + ang_d + 8 * R, 6 * R * (d // 2) * Ld, "hbm")
     if k > 1:
         w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
@@ -257,7 +267,7 @@ def main() -> int:
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile)).get(f"{cfg.name}:{dom}")
-            if tj and tj.get("kernel_source_sha") == bm_kernel_sha(dom):
+            if tj and tj.get("kernel_source_sha") == bm_kernel_sha(dom, cfg):
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -303,10 +313,11 @@ def main() -> int:
     return 0
 
 
-def bm_kernel_sha(kernel: str) -> str:
+def bm_kernel_sha(kernel: str, cfg) -> str:
     """Hash of the HIP source that holds `kernel` (to invalidate stale counters)."""
     import hashlib
-    src = {"gemm": "gemm.hip", "gemm_up": "gemm.hip", "gemm_down": "gemm.hip", "combine": "gemm.hip",
+    g = "gemm_fp4.hip" if cfg.act == "bf16" and cfg.d_model >= 256 else "gemm.hip"
+    src = {"gemm": g, "gemm_up": g, "gemm_down": g, "combine": "gemm.hip",
            "route": "route.hip", "bucket": "route.hip", "prep": "prep.hip",
            "fused": "fused_mfma.hip"}.get(kernel, "butterfly.hip")
     p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)

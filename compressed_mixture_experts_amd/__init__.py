@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
-    "dbg_butterfly", "dbg_ternary_gemm", "STATUS", "EXPORTED_SYMBOLS",
+    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "STATUS", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,8 +36,8 @@ ACT_NONE, ACT_GELU_ERF = 0, 1
 EXPORTED_SYMBOLS = [
     "bmoe_packed_words", "bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepared_bytes",
     "bmoe_prepare", "bmoe_route", "bmoe_forward", "bmoe_status_string", "bmoe_last_error",
-    "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_forward_kernels",
-    "bmoe_dbg_forward_marked",
+    "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
+    "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
 ]
 
 
@@ -97,11 +97,12 @@ def lib() -> ctypes.CDLL:
     L.bmoe_last_error.restype = ctypes.c_char_p
     L.bmoe_dbg_butterfly.argtypes = [c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
     L.bmoe_dbg_ternary_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
+    L.bmoe_dbg_ternary_gemm_fp4.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_f, c_vp, c_vp]
     L.bmoe_dbg_forward_kernels.argtypes = [pL, ctypes.POINTER(c_i32), ctypes.c_char_p, c_sz]
     L.bmoe_dbg_forward_marked.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_i32]
     for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
-                 "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_forward_kernels",
-                 "bmoe_dbg_forward_marked"):
+                 "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
+                 "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked"):
         getattr(L, name).restype = c_i32
     _lib = L
     return L
@@ -319,4 +320,15 @@ def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):
     z = torch.empty((M, n_out), dtype=a.dtype, device=a.device)
     _check(lib().bmoe_dbg_ternary_gemm(M, n_out, K, dtype, _ptr(a), _ptr(w_packed), float(alpha),
                                        _ptr(z), _stream_handle()))
+    return z
+
+
+def dbg_ternary_gemm_fp4(a, w_packed, n_out: int, alpha: float = 1.0):
+    """Matrix-core form of dbg_ternary_gemm for bf16 `a` (substrate re-encoded as fp4)."""
+    torch = _torch()
+    M, K = int(a.shape[0]), int(a.shape[1])
+    z = torch.empty((M, n_out), dtype=a.dtype, device=a.device)
+    scratch = torch.empty((n_out * K // 2,), dtype=torch.uint8, device=a.device)
+    _check(lib().bmoe_dbg_ternary_gemm_fp4(M, n_out, K, _ptr(a), _ptr(w_packed), _ptr(scratch),
+                                           float(alpha), _ptr(z), _stream_handle()))
     return z

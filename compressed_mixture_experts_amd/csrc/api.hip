@@ -135,22 +135,72 @@ bool use_fused(const bmoe_layer* L) {
 // ... with the rotations as block factors on the matrix cores (widths 256, 512)
 bool use_fused_mfma(const bmoe_layer* L) { return use_fused(L) && fused_mfma_supported(ilog2(L->d_model)); }
 
-// Prepared-weights buffer: [substrate re-encoded | rotation factors], 256-aligned.
+// Substrate m's product as a GEMM Z = U W_m^T: output columns and contraction length.
+void sub_shape(const bmoe_layer* L, int m, int32_t& n_out, int32_t& k_in) {
+  const int32_t d = L->d_model, f = L->d_ff;
+  n_out = f == 0 ? d : m == 0 ? f : d;
+  k_in = f == 0 ? d : m == 0 ? d : f;
+}
+
+// Prepared-weights buffer, 256-aligned sections: [substrate 0 re-encoded |
+// substrate 1 re-encoded (FFN) | rotation factors].  Fused square layers: the
+// substrate as bytes (widths 64, 128) or fp4 (256, 512) plus block factors
+// (256, 512).  Other bf16 layers: each substrate whose product the fp4 GEMM
+// covers, as fp4.  fp32 layers: nothing.
 struct PrepLayout {
-  size_t w_off, w_len, fac_off, fac_len, total;
-  bool fp4;
+  size_t w_off[2], w_len[2], fac_off, fac_len, total;
+  bool fp4[2];
 };
 
 PrepLayout prep_layout(const bmoe_layer* L) {
   PrepLayout q{};
-  if (!use_fused(L)) return q;
-  const size_t d = size_t(L->d_model);
-  q.fp4 = use_fused_mfma(L);
-  q.w_len = d * d / (q.fp4 ? 2 : 1);
-  q.fac_off = align256(q.w_len);
-  q.fac_len = q.fp4 ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(L->d_model)) : 0;
-  q.total = align256(q.fac_off + q.fac_len);
+  size_t o = 0;
+  if (use_fused(L)) {
+    const size_t d = size_t(L->d_model);
+    q.fp4[0] = use_fused_mfma(L);
+    q.w_len[0] = d * d / (q.fp4[0] ? 2 : 1);
+    o = align256(q.w_len[0]);
+    q.fac_off = o;
+    q.fac_len = q.fp4[0] ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(L->d_model)) : 0;
+    q.total = align256(o + q.fac_len);
+    return q;
+  }
+  if (L->act_dtype != BMOE_BF16) return q;
+  for (int m = 0; m < (L->d_ff ? 2 : 1); ++m) {
+    int32_t n_out, k_in;
+    sub_shape(L, m, n_out, k_in);
+    if (!gemm_fp4_supported(n_out, k_in)) continue;
+    q.fp4[m] = true;
+    q.w_off[m] = o;
+    q.w_len[m] = size_t(n_out) * size_t(k_in) / 2;
+    o = align256(o + q.w_len[m]);
+  }
+  q.fac_off = o;
+  q.total = o;
   return q;
+}
+
+// Arguments of the prep kernel that fills `buf` (layout q) for layer L.
+PrepArgs prep_args(const bmoe_layer* L, const PrepLayout& q, unsigned char* buf) {
+  PrepArgs pa{};
+  int32_t n_out, k_in;
+  sub_shape(L, 0, n_out, k_in);
+  pa.w_packed = L->w_base[0];
+  pa.w_out = buf + q.w_off[0];
+  pa.w_words = q.w_len[0] ? int32_t(int64_t(n_out) * k_in / 16) : 0;
+  pa.w_fp4 = q.fp4[0] ? 1 : 0;
+  if (L->d_ff && q.w_len[1]) {
+    sub_shape(L, 1, n_out, k_in);
+    pa.w_packed1 = L->w_base[1];
+    pa.w_out1 = buf + q.w_off[1];
+    pa.w_words1 = int32_t(int64_t(n_out) * k_in / 16);
+  }
+  pa.theta = L->theta[0];
+  pa.phi = L->phi[0];
+  pa.fac = buf + q.fac_off;
+  pa.fac_log2n = q.fac_len ? ilog2(L->d_model) : 0;
+  pa.n_experts = L->n_experts;
+  return pa;
 }
 
 Plan make_plan(const bmoe_layer* L, int32_t T) {
@@ -172,7 +222,7 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
   p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
   p.mfma = use_fused_mfma(L);
-  p.prep = (p.fused && !L->prepared) ? take(prep_layout(L).total) : 0;  // prepared data built per call
+  p.prep = L->prepared ? 0 : take(prep_layout(L).total);  // prepared data built per call
   p.total = o;
   p.R = R;
   return p;
@@ -278,17 +328,22 @@ bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, 
   if (!prepared) return fail(BMOE_ERR_NULL, "prepared is NULL");
   if (!aligned(prepared, 256)) return fail(BMOE_ERR_ALIGN, "prepared is not 256-byte aligned");
   if (bytes < q.total) return fail(BMOE_ERR_WORKSPACE, "prepared buffer has %zu bytes, %zu needed", bytes, q.total);
-  const int64_t d = layer->d_model, N = layer->n_experts;
   const Range rp{prepared, q.total};
-  const size_t angle_bytes = size_t(N) * ilog2(d) * (d / 2) * 4;
-  if (overlap(rp, Range{layer->w_base[0], size_t(d) * d / 4}) || overlap(rp, Range{layer->theta[0], angle_bytes}) ||
-      overlap(rp, Range{layer->phi[0], angle_bytes}))
-    return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
+  for (int m = 0; m < (layer->d_ff ? 2 : 1); ++m) {
+    int32_t n_out, k_in;
+    sub_shape(layer, m, n_out, k_in);
+    if (q.w_len[m] && overlap(rp, Range{layer->w_base[m], size_t(n_out) * k_in / 4}))
+      return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
+  }
+  if (q.fac_len) {
+    const int64_t d = layer->d_model;
+    const size_t angle_bytes = size_t(layer->n_experts) * ilog2(d) * (d / 2) * 4;
+    if (overlap(rp, Range{layer->theta[0], angle_bytes}) || overlap(rp, Range{layer->phi[0], angle_bytes}))
+      return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
+  }
   st = check_device();
   if (st != BMOE_OK) return st;
-  unsigned char* buf = static_cast<unsigned char*>(prepared);
-  PrepArgs pa{layer->w_base[0], buf + q.w_off, int32_t(d * d / 16), q.fp4 ? 1 : 0, layer->theta[0],
-              layer->phi[0], buf + q.fac_off, q.fp4 ? ilog2(d) : 0, int32_t(N)};
+  const PrepArgs pa = prep_args(layer, q, static_cast<unsigned char*>(prepared));
   BMOE_HIP(launch_prep(pa, stream));
   return ok();
 }
@@ -324,7 +379,7 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T, int32_
 // Kernel launches of one forward, in order (marks[i] follows launch i-1).
 static int forward_kernel_names(const bmoe_layer* L, const char** names) {
   int n = 0;
-  if (use_fused(L) && !L->prepared) names[n++] = "prep";
+  if (prep_layout(L).total && !L->prepared) names[n++] = "prep";
   names[n++] = "route";
   names[n++] = "bucket";
   if (use_fused(L)) {
@@ -394,23 +449,24 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   void* bufZ = at<char>(workspace, p.bufZ);
   const int Ld = ilog2(d);
 
-  // prepared weights (fused square experts): given, or built here
+  // prepared weights: given, or built here
+  const PrepLayout q = prep_layout(layer);
   const bool fused = p.fused;
-  const unsigned char* wbytes = nullptr;
-  const unsigned char* fac = nullptr;
-  if (fused) {
-    const PrepLayout q = prep_layout(layer);
-    const unsigned char* base = static_cast<const unsigned char*>(layer->prepared);
-    if (!base) {
-      unsigned char* buf = at<unsigned char>(workspace, p.prep);
-      PrepArgs pa{layer->w_base[0], buf + q.w_off, int32_t(int64_t(d) * d / 16), q.fp4 ? 1 : 0,
-                  layer->theta[0], layer->phi[0], buf + q.fac_off, p.mfma ? Ld : 0, N};
-      BMOE_LAUNCH(launch_prep(pa, stream));
-      base = buf;
-    }
-    wbytes = base + q.w_off;
-    fac = p.mfma ? base + q.fac_off : nullptr;
+  const unsigned char* pbase = static_cast<const unsigned char*>(layer->prepared);
+  if (q.total && !pbase) {
+    unsigned char* buf = at<unsigned char>(workspace, p.prep);
+    BMOE_LAUNCH(launch_prep(prep_args(layer, q, buf), stream));
+    pbase = buf;
   }
+  const unsigned char* wbytes = q.w_len[0] ? pbase + q.w_off[0] : nullptr;
+  const unsigned char* wbytes1 = q.w_len[1] ? pbase + q.w_off[1] : nullptr;
+  const unsigned char* fac = q.fac_len ? pbase + q.fac_off : nullptr;
+  // substrate product: fp4 matrix-core GEMM on a prepared substrate, else the 2-bit one
+  auto substrate_gemm = [&](int m, const void* a_in, void* z_out, int32_t n_out, int32_t k_in) -> hipError_t {
+    const unsigned char* wq = m == 0 ? wbytes : wbytes1;
+    if (wq) return launch_gemm_fp4(GemmFp4Args{a_in, wq, z_out, layer->w_scale[m], R, n_out, k_in}, stream);
+    return launch_gemm(GemmArgs{a_in, layer->w_base[m], z_out, layer->w_scale[m], R, n_out, k_in}, act, stream);
+  };
   // router and bucketing
   RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates};
   BMOE_LAUNCH(launch_route(ra, act, stream));
@@ -438,19 +494,16 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   const void* zlast = nullptr;
   const float* phi_last = nullptr;
   if (f == 0) {
-    GemmArgs g{bufU, layer->w_base[0], bufZ, layer->w_scale[0], R, d, d};
-    BMOE_LAUNCH(launch_gemm(g, act, stream));
+    BMOE_LAUNCH(substrate_gemm(0, bufU, bufZ, d, d));
     zlast = bufZ;
     yslot = bufU;
     phi_last = layer->phi[0];
   } else {
-    GemmArgs g0{bufU, layer->w_base[0], bufZ, layer->w_scale[0], R, f, d};
-    BMOE_LAUNCH(launch_gemm(g0, act, stream));
+    BMOE_LAUNCH(substrate_gemm(0, bufU, bufZ, f, d));
     BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0,
                 layer->ffn_act == BMOE_ACT_GELU_ERF ? 1 : 0};
     BMOE_LAUNCH(launch_butterfly(bm, BFLY_MID, act, ilog2(f), stream));
-    GemmArgs g1{bufZ, layer->w_base[1], bufU, layer->w_scale[1], R, d, f};
-    BMOE_LAUNCH(launch_gemm(g1, act, stream));
+    BMOE_LAUNCH(substrate_gemm(1, bufZ, bufU, d, f));
     zlast = bufU;
     yslot = bufZ;
     phi_last = layer->phi[1];
@@ -538,6 +591,32 @@ bmoe_status bmoe_dbg_ternary_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype
   if (st != BMOE_OK) return st;
   GemmArgs g{a, w_packed, z, alpha, M, N, K};
   BMOE_HIP(launch_gemm(g, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
+  return ok();
+}
+
+bmoe_status bmoe_dbg_ternary_gemm_fp4(int32_t M, int32_t N, int32_t K, const void* a,
+                                      const uint32_t* w_packed, void* w_fp4, float alpha, void* z,
+                                      hipStream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0 || !gemm_fp4_supported(N, K))
+    return fail(BMOE_ERR_SHAPE, "M=%d N=%d K=%d: N must be a positive multiple of 256, K of 128", M, N, K);
+  if (M == 0) return ok();
+  if (!a || !w_packed || !w_fp4 || !z) return fail(BMOE_ERR_NULL, "a / w_packed / w_fp4 / z is NULL");
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_fp4, 16) || !aligned(z, 16))
+    return fail(BMOE_ERR_ALIGN, "a, w_packed, w_fp4 and z must be 16-byte aligned");
+  const Range ra{a, size_t(M) * K * 2}, rz{z, size_t(M) * N * 2}, rq{w_fp4, size_t(N) * K / 2},
+      rw{w_packed, size_t(N) * K / 4};
+  if (overlap(ra, rz) || overlap(rq, ra) || overlap(rq, rz) || overlap(rq, rw))
+    return fail(BMOE_ERR_ALIAS, "z / w_fp4 overlap an operand");
+  bmoe_status st = check_device();
+  if (st != BMOE_OK) return st;
+  PrepArgs pa{};
+  pa.w_packed = w_packed;
+  pa.w_out = static_cast<unsigned char*>(w_fp4);
+  pa.w_words = int32_t(int64_t(N) * K / 16);
+  pa.w_fp4 = 1;
+  BMOE_HIP(launch_prep(pa, stream));
+  GemmFp4Args g{a, static_cast<const unsigned char*>(w_fp4), z, alpha, M, N, K};
+  BMOE_HIP(launch_gemm_fp4(g, stream));
   return ok();
 }
 

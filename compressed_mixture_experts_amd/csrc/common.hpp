@@ -102,14 +102,17 @@ struct BucketArgs {
   int32_t R, N;
 };
 
-// Weight preparation for the fused square-expert kernels (once per weight set,
+// Weight preparation for the expert kernels (once per weight set,
 // or per call when no prepared buffer is given).
 struct PrepArgs {
-  const uint32_t* w_packed; // 2-bit substrate, d*d/16 words (16 weights each)
-  unsigned char* w_out;     // w_fp4 == 0: [d][d] bytes (bf16 high byte of +-0.5 / 0);
-                            // w_fp4 == 1: [d][d/2] fp4 e2m1 nibbles, low nibble first
+  const uint32_t* w_packed; // substrate 0, 2-bit packed, w_words words (16 weights each)
+  unsigned char* w_out;     // w_fp4 == 0: one byte per weight (bf16 high byte of +-0.5 / 0);
+                            // w_fp4 == 1: fp4 e2m1 nibbles, two per byte, low nibble first
   int32_t w_words;
   int32_t w_fp4;
+  const uint32_t* w_packed1; // substrate 1 (FFN down), always fp4; w_words1 may be 0
+  unsigned char* w_out1;
+  int32_t w_words1;
   const float* theta;       // [N][L][n/2]
   const float* phi;         // [N][L][n/2]
   unsigned char* fac;       // [N][factor_bytes_per_expert] (matrix-core kernel only)
@@ -166,6 +169,14 @@ struct GemmArgs {
   int32_t M, N, K;
 };
 
+struct GemmFp4Args {
+  const void* a;            // [M][K] bf16
+  const unsigned char* w;   // [N][K/2] fp4 e2m1 substrate (weight 2b in the low nibble of byte b)
+  void* z;                  // [M][N] bf16
+  float alpha;
+  int32_t M, N, K;
+};
+
 struct CombineArgs {
   const void* yp;           // [T*k][d] per-slot gated outputs
   void* y;                  // [T][d]
@@ -177,6 +188,8 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
+bool gemm_fp4_supported(int N, int K);
+hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 
 bool fused_square_supported(int log2n);

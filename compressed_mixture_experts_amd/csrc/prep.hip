@@ -1,11 +1,12 @@
-// Weight preparation for the fused square-expert kernels: re-encodings of the
+// Weight preparation for the expert kernels: re-encodings of the
 // shared ternary substrate and of each expert's rotations that depend on the
 // weights only (ButterflyMoE, gist.science/zh/paper/2601.13563, technical
 // summary §2.1-§2.2: the substrate is ternary, every expert rotates with its
 // own Givens angles).  Done once per weight set (bmoe_prepare) or per call.
 //
-// Grid: PR_FS workgroups per expert.  Every workgroup unpacks a grid-stride
-// share of the 2-bit words; for the matrix-core kernel each builds a share of
+// Grid: PR_FS workgroups per expert (matrix-core square layers), else enough
+// workgroups to cover the words.  Every workgroup unpacks a grid-stride share
+// of the 2-bit words of one or two substrates; for the matrix-core kernel each builds a share of
 // its expert's rotation block factors (mfma_factors.hpp).
 #include "mfma_factors.hpp"
 
@@ -22,25 +23,30 @@ __global__ __launch_bounds__(PR_THREADS) void prep_kernel(PrepArgs a) {
   // substrate: 16 weights per word, column 2j+h of the word's 16: nonzero bit
   // 16h+j, sign bit 16h+8+j.  Bytes: +1 -> 0x3F, -1 -> 0xBF, 0 -> 0 (bf16 high
   // byte of +-0.5); fp4 e2m1: +1 -> 0x2, -1 -> 0xA, 0 -> 0
-  for (int w = blockIdx.x * PR_THREADS + tid; w < a.w_words; w += gridDim.x * PR_THREADS) {
-    const uint32_t P = a.w_packed[w];
+  const int nw = a.w_words + a.w_words1;
+  for (int i = blockIdx.x * PR_THREADS + tid; i < nw; i += gridDim.x * PR_THREADS) {
+    const bool s1 = i >= a.w_words;
+    const int w = s1 ? i - a.w_words : i;
+    const bool fp4 = s1 || a.w_fp4;
+    const uint32_t P = s1 ? a.w_packed1[w] : a.w_packed[w];
+    unsigned char* out = s1 ? a.w_out1 : a.w_out;
     uint32_t code[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const int j = c >> 1, h = c & 1;
       const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = (P >> (16 * h + 8 + j)) & 1u;
-      code[c] = a.w_fp4 ? nz * (0x2u | (sg << 3)) : nz * (0x3Fu | (sg << 7));
+      code[c] = fp4 ? nz * (0x2u | (sg << 3)) : nz * (0x3Fu | (sg << 7));
     }
-    if (a.w_fp4) {
+    if (fp4) {
       uint32_t o[2] = {0u, 0u};
 #pragma unroll
       for (int c = 0; c < 16; ++c) o[c >> 3] |= code[c] << (4 * (c & 7));
-      reinterpret_cast<uint2*>(a.w_out)[w] = make_uint2(o[0], o[1]);
+      reinterpret_cast<uint2*>(out)[w] = make_uint2(o[0], o[1]);
     } else {
       uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int c = 0; c < 16; ++c) o[c >> 2] |= code[c] << (8 * (c & 3));
-      reinterpret_cast<uint4*>(a.w_out)[w] = make_uint4(o[0], o[1], o[2], o[3]);
+      reinterpret_cast<uint4*>(out)[w] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
   if constexpr (LF > 0) {
@@ -56,7 +62,8 @@ __global__ __launch_bounds__(PR_THREADS) void prep_kernel(PrepArgs a) {
 }
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
-  const int grid = a.fac_log2n ? a.n_experts * PR_FS : (a.w_words + PR_THREADS - 1) / PR_THREADS;
+  const int64_t nw = int64_t(a.w_words) + a.w_words1;
+  const int grid = a.fac_log2n ? a.n_experts * PR_FS : int((nw + PR_THREADS - 1) / PR_THREADS < 8192 ? (nw + PR_THREADS - 1) / PR_THREADS : 8192);
   if (grid <= 0) return hipSuccess;
   switch (a.fac_log2n) {
     case 8: hipLaunchKernelGGL(prep_kernel<8>, dim3(grid), dim3(PR_THREADS), 0, s, a); break;

@@ -200,6 +200,16 @@ def test_debug_hook_argument_errors():
     assert L.bmoe_dbg_ternary_gemm(8, 96, 64, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE + 0x100000, None) == 2
     assert L.bmoe_dbg_ternary_gemm(8, 64, 64, 1, FAKE, FAKE, ctypes.c_float(1.0), FAKE + 16, None) == 5
     assert L.bmoe_dbg_ternary_gemm(8, 64, 64, 7, FAKE, FAKE, ctypes.c_float(1.0), FAKE + 0x100000, None) == 3
+    # fp4 form: N a multiple of 256, K of 128; scratch must not alias an operand
+    g = L.bmoe_dbg_ternary_gemm_fp4
+    one = ctypes.c_float(1.0)
+    assert g(8, 128, 128, FAKE, FAKE + 0x1000, FAKE + 0x2000, one, FAKE + 0x100000, None) == 2
+    assert g(8, 256, 64, FAKE, FAKE + 0x1000, FAKE + 0x2000, one, FAKE + 0x100000, None) == 2
+    assert g(0, 256, 128, None, None, None, one, None, None) == 0
+    assert g(8, 256, 128, FAKE, FAKE + 0x10000, None, one, FAKE + 0x100000, None) == 1
+    assert g(8, 256, 128, FAKE, FAKE + 0x10000, FAKE + 0x20008, one, FAKE + 0x100000, None) == 4
+    assert g(8, 256, 128, FAKE, FAKE + 0x10000, FAKE + 0x10000, one, FAKE + 0x100000, None) == 5
+    assert g(8, 256, 128, FAKE, FAKE + 0x10000, FAKE + 0x20000, one, FAKE + 0x100000, None) in (8, 9)
 
 
 def test_status_strings():
@@ -218,9 +228,20 @@ def test_prepared_bytes_layout():
     # widths 64 / 128: one byte per weight, no factors (rounded up to 256 bytes)
     s = make_struct(d_model=128)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 128 * 128
-    # fp32 activations, FFN layers and invalid layers use none
+    # wider bf16 layers: each substrate whose product the fp4 GEMM covers
+    # (output width a multiple of 256, contraction a multiple of 128), as fp4
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 2
+    s = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 2 * (4096 * 1024 // 2)
+    # d_ff = 128: the up product (128 outputs) keeps the 2-bit GEMM, the down one is fp4
+    s = make_struct(d_model=1024, d_ff=128, ffn_act=bm.ACT_GELU_ERF)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 2
+    s = make_struct(d_model=128, d_ff=64, ffn_act=bm.ACT_GELU_ERF)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 0
+    # fp32 activations and invalid layers use none
     assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(act_dtype=bm.F32))) == 0
-    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF))) == 0
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(act_dtype=bm.F32, d_model=1024, d_ff=4096,
+                                                          ffn_act=bm.ACT_GELU_ERF))) == 0
     assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=100))) == 0
 
 
@@ -234,6 +255,11 @@ def test_prepare_argument_errors():
     assert L.bmoe_prepare(ctypes.byref(s), buf, need - 1, None) == 6
     assert L.bmoe_prepare(ctypes.byref(s), FAKE + 0x100000 - 256, need, None) == 5   # over w_base[0]
     assert L.bmoe_prepare(ctypes.byref(make_struct(d_model=100)), buf, need, None) == 2
+    # FFN: the buffer must not overlap the down substrate either
+    f = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
+    fneed = L.bmoe_prepared_bytes(ctypes.byref(f))
+    assert L.bmoe_prepare(ctypes.byref(f), FAKE + 0x400000 - 256, fneed, None) == 5
+    assert L.bmoe_prepare(ctypes.byref(f), buf, fneed, None) in (8, 9)
     # a layer without prepared data: nothing to do
     assert L.bmoe_prepare(ctypes.byref(make_struct(act_dtype=bm.F32)), None, 0, None) == 0
     # valid arguments reach the device check (no GPU here)

@@ -84,6 +84,41 @@ def test_ternary_gemm_integer_exact(act, M, N, K):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (129, 512, 256), (300, 768, 384), (515, 1024, 2048),
+                                   (1000, 4096, 1024)])
+def test_ternary_gemm_fp4_integer_exact(M, N, K):
+    # integer operands: every partial sum is an exact fp32 integer (|.| <= 8 K < 2^24),
+    # so the matrix-core product must round to exactly the bf16 of the true result
+    import torch
+    r = np.random.default_rng(7 * M + N + K)
+    w = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    a = r.integers(-8, 9, size=(M, K)).astype(np.float64)
+    a_st = wl.round_to_bf16_bits(a)
+    wp = torch.from_numpy(bm.pack_ternary(w).view(np.int32)).cuda()
+    log(f"gemm fp4 exact M={M} N={N} K={K}")
+    z = bm.dbg_ternary_gemm_fp4(to_dev(a_st, "bf16"), wp, N, 1.0)
+    torch.cuda.synchronize()
+    want = wl.round_to_bf16_bits(ref.ternary_product(a, w))
+    assert np.array_equal(z.cpu().view(torch.int16).numpy().view(np.uint16), want)
+
+
+def test_ternary_gemm_fp4_random_bound():
+    import torch
+    M, N, K = 333, 512, 1024
+    r = np.random.default_rng(10)
+    w = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    a_st = wl.round_to_bf16_bits(r.standard_normal((M, K)))
+    a = ref.stored_to_f64(a_st, "bf16")
+    wp = torch.from_numpy(bm.pack_ternary(w).view(np.int32)).cuda()
+    log("gemm fp4 bound")
+    z = to_f64(bm.dbg_ternary_gemm_fp4(to_dev(a_st, "bf16"), wp, N, 0.75))
+    torch.cuda.synchronize()
+    exact = ref.ternary_product(a, w, 0.75)
+    # fp32 accumulation of K terms (error <= K u32 sum|a|) plus one bf16 rounding
+    bound = K * 2.0 ** -24 * 0.75 * np.abs(a) @ np.abs(w.T).astype(np.float64) + 2.0 ** -8 * np.abs(exact)
+    assert np.all(np.abs(z - exact) <= bound + 1e-30)
+
+
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_ternary_gemm_random_bound(act):
     import torch
