@@ -76,7 +76,21 @@ def kernel_work(cfg):
     w = {}
     w["route"] = (T * d * s + N * d * s + 8 * R, 2 * T * d * N, "hbm")
     w["bucket"] = (4 * R + 4 * R + 4 * (N + 1), 0, "hbm")
-    w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
+
+    def split(L):
+        # bf16 rows of width 1024 .. 8192: butterflies as low / high parts
+        return cfg.act == "bf16" and 10 <= L <= 13
+
+    def part(n, stages, nbfly=1, extra=0):
+        # one pass over R rows of width n applying `stages` stages of nbfly butterflies
+        return (2 * R * n * s + nbfly * N * stages * (n // 2) * 4 + extra,
+                6 * R * (n // 2) * stages * nbfly, "hbm")
+
+    if split(Ld):
+        w["bfly_in_hi"] = part(d, 4, extra=4 * R)
+        w["bfly_in_lo"] = part(d, Ld - 4)
+    else:
+        w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
 
     def fp4_gemm(din, dout):
         # bf16 products whose shape the fp4 matrix-core GEMM covers read the
@@ -108,12 +122,21 @@ def kernel_work(cfg):
     else:
         Lf = int(math.log2(f))
         w["gemm_up"] = gemm(d, f)
-        w["bfly_mid"] = (2 * R * f * s + 2 * N * Lf * (f // 2) * 4, 2 * 6 * R * (f // 2) * Lf, "hbm")
+        if split(Lf):
+            w["bfly_mid_lo"] = part(f, Lf - 4)
+            w["bfly_mid_hi"] = part(f, 4, nbfly=2)
+            w["bfly_mid_lo_t"] = part(f, Lf - 4)
+        else:
+            w["bfly_mid"] = (2 * R * f * s + 2 * N * Lf * (f // 2) * 4, 2 * 6 * R * (f // 2) * Lf, "hbm")
         w["gemm_down"] = gemm(f, d)
         pw = sum(a * b // 4 + a * b // 2 for a, b in ((d, f), (f, d)) if fp4_gemm(a, b))
         if pw:
             w["prep"] = (pw, 0, "hbm")
-    w["bfly_out"] = (2 * R * d * s + ang_d + 8 * R, 6 * R * (d // 2) * Ld, "hbm")
+    if split(Ld):
+        w["bfly_out_lo"] = part(d, Ld - 4)
+        w["bfly_out_hi"] = part(d, 4, extra=8 * R)
+    else:
+        w["bfly_out"] = (2 * R * d * s + ang_d + 8 * R, 6 * R * (d // 2) * Ld, "hbm")
     if k > 1:
         w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
     return w
@@ -319,7 +342,8 @@ def bm_kernel_sha(kernel: str, cfg) -> str:
     g = "gemm_fp4.hip" if cfg.act == "bf16" and cfg.d_model >= 256 else "gemm.hip"
     src = {"gemm": g, "gemm_up": g, "gemm_down": g, "combine": "gemm.hip",
            "route": "route.hip", "bucket": "route.hip", "prep": "prep.hip",
-           "fused": "fused_mfma.hip"}.get(kernel, "butterfly.hip")
+           "fused": "fused_mfma.hip"}.get(kernel, "butterfly_split.hip" if kernel.endswith(("_hi", "_lo", "_lo_t"))
+                                          else "butterfly.hip")
     p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 

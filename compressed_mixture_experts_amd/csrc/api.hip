@@ -142,6 +142,12 @@ void sub_shape(const bmoe_layer* L, int m, int32_t& n_out, int32_t& k_in) {
   k_in = f == 0 ? d : m == 0 ? d : f;
 }
 
+// bf16 rows of width 2^log2n (1024 .. 8192): each butterfly runs as a low and
+// a high part, each part over many rows of one expert per workgroup.
+bool use_split(const bmoe_layer* L, int log2n) {
+  return L->act_dtype == BMOE_BF16 && bfly_split_supported(log2n);
+}
+
 // Prepared-weights buffer, 256-aligned sections: [substrate 0 re-encoded |
 // substrate 1 re-encoded (FFN) | rotation factors].  Fused square layers: the
 // substrate as bytes (widths 64, 128) or fp4 (256, 512) plus block factors
@@ -387,15 +393,32 @@ static int forward_kernel_names(const bmoe_layer* L, const char** names) {
     if (L->top_k > 1) names[n++] = "combine";
     return n;
   }
-  names[n++] = "bfly_in";
+  const bool split_d = use_split(L, ilog2(L->d_model));
+  if (split_d) {
+    names[n++] = "bfly_in_hi";
+    names[n++] = "bfly_in_lo";
+  } else {
+    names[n++] = "bfly_in";
+  }
   if (L->d_ff == 0) {
     names[n++] = "gemm";
   } else {
     names[n++] = "gemm_up";
-    names[n++] = "bfly_mid";
+    if (use_split(L, ilog2(L->d_ff))) {
+      names[n++] = "bfly_mid_lo";
+      names[n++] = "bfly_mid_hi";
+      names[n++] = "bfly_mid_lo_t";
+    } else {
+      names[n++] = "bfly_mid";
+    }
     names[n++] = "gemm_down";
   }
-  names[n++] = "bfly_out";
+  if (split_d) {
+    names[n++] = "bfly_out_lo";
+    names[n++] = "bfly_out_hi";
+  } else {
+    names[n++] = "bfly_out";
+  }
   if (L->top_k > 1) names[n++] = "combine";
   return n;
 }
@@ -488,10 +511,17 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
     return ok();
   }
   // input rotation: U[q] = B(theta_e)^T x_t
+  const bool split_d = use_split(layer, Ld);
   BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
-  BMOE_LAUNCH(launch_butterfly(bi, BFLY_IN, act, Ld, stream));
+  if (split_d) {
+    BMOE_LAUNCH(launch_bfly_split(bi, SPLIT_HIGH_IN, Ld, stream));
+    BflyArgs bl{bufU, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+    BMOE_LAUNCH(launch_bfly_split(bl, SPLIT_LOW_T, Ld, stream));
+  } else {
+    BMOE_LAUNCH(launch_butterfly(bi, BFLY_IN, act, Ld, stream));
+  }
   void* yslot = nullptr;  // per-slot outputs (k > 1)
-  const void* zlast = nullptr;
+  void* zlast = nullptr;
   const float* phi_last = nullptr;
   if (f == 0) {
     BMOE_LAUNCH(substrate_gemm(0, bufU, bufZ, d, d));
@@ -500,9 +530,18 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
     phi_last = layer->phi[0];
   } else {
     BMOE_LAUNCH(substrate_gemm(0, bufU, bufZ, f, d));
-    BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0,
-                layer->ffn_act == BMOE_ACT_GELU_ERF ? 1 : 0};
-    BMOE_LAUNCH(launch_butterfly(bm, BFLY_MID, act, ilog2(f), stream));
+    const int gelu = layer->ffn_act == BMOE_ACT_GELU_ERF ? 1 : 0;
+    BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0, gelu};
+    if (use_split(layer, ilog2(f))) {
+      // B(theta_dn)^T GELU(B(phi_up) h) = low^T(theta) high^T(theta) GELU high(phi) low(phi) h
+      BflyArgs b1{bufZ, bufZ, layer->phi[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+      BMOE_LAUNCH(launch_bfly_split(b1, SPLIT_LOW, ilog2(f), stream));
+      BMOE_LAUNCH(launch_bfly_split(bm, SPLIT_HIGH_MID, ilog2(f), stream));
+      BflyArgs b3{bufZ, bufZ, layer->theta[1], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+      BMOE_LAUNCH(launch_bfly_split(b3, SPLIT_LOW_T, ilog2(f), stream));
+    } else {
+      BMOE_LAUNCH(launch_butterfly(bm, BFLY_MID, act, ilog2(f), stream));
+    }
     BMOE_LAUNCH(substrate_gemm(1, bufZ, bufU, d, f));
     zlast = bufU;
     yslot = bufZ;
@@ -510,7 +549,13 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   }
   // output rotation, gate, per-slot rows (or y directly when k == 1)
   BflyArgs bo{zlast, k == 1 ? y : yslot, phi_last, nullptr, offsets, perm, gate, R, N, k, 0, 0};
-  BMOE_LAUNCH(launch_butterfly(bo, BFLY_OUT, act, Ld, stream));
+  if (split_d) {
+    BflyArgs bl{zlast, zlast, phi_last, nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+    BMOE_LAUNCH(launch_bfly_split(bl, SPLIT_LOW, Ld, stream));
+    BMOE_LAUNCH(launch_bfly_split(bo, SPLIT_HIGH_OUT, Ld, stream));
+  } else {
+    BMOE_LAUNCH(launch_butterfly(bo, BFLY_OUT, act, Ld, stream));
+  }
   if (k > 1) {
     CombineArgs c{yslot, y, T, d, k};
     BMOE_LAUNCH(launch_combine(c, act, stream));

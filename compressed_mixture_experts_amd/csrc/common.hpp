@@ -161,6 +161,15 @@ struct BflyArgs {
   int32_t gelu;             // MID: apply GELU between the two rotations
 };
 
+// Parts of a wide butterfly run as separate passes (butterfly_split.hip).
+enum SplitPart {
+  SPLIT_LOW = 0,       // stages 0 .. L-5 (in place)
+  SPLIT_LOW_T = 1,     // the same, transposed
+  SPLIT_HIGH_IN = 2,   // gather x rows, top 4 stages transposed
+  SPLIT_HIGH_MID = 3,  // top 4 stages of ang0, GELU, top 4 of ang1 transposed (in place)
+  SPLIT_HIGH_OUT = 4,  // top 4 stages, gate, scatter to slot rows
+};
+
 struct GemmArgs {
   const void* a;            // [M][K]
   const uint32_t* w;        // [N][K/16]
@@ -188,6 +197,8 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
+bool bfly_split_supported(int log2n);
+hipError_t launch_bfly_split(const BflyArgs& a, int part, int log2n, hipStream_t s);
 bool gemm_fp4_supported(int N, int K);
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);

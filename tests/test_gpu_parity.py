@@ -265,6 +265,11 @@ SMALL_CASES = [
     dict(d_model=64, d_ff=128, n_experts=4, top_k=2, tokens=65, act="f32"),
     dict(d_model=128, d_ff=64, n_experts=7, top_k=2, tokens=333, act="bf16", renorm_gates=True),
     dict(d_model=256, d_ff=1024, n_experts=16, top_k=2, tokens=1000, act="bf16", ffn_act="none"),
+    # wide bf16 rows: butterflies as low / high parts, several 64-row blocks per expert
+    dict(d_model=1024, n_experts=6, top_k=2, tokens=400, act="bf16"),
+    dict(d_model=2048, n_experts=3, top_k=1, tokens=50, act="bf16"),
+    dict(d_model=256, d_ff=4096, n_experts=5, top_k=2, tokens=120, act="bf16"),
+    dict(d_model=128, d_ff=8192, n_experts=3, top_k=2, tokens=40, act="bf16"),
 ]
 
 
@@ -328,6 +333,7 @@ def test_route_matches_forward_routing():
 # results of the per-call preparation: same kernels on the same bytes.
 PREP_CASES = [
     dict(d_model=512, n_experts=64, top_k=2, tokens=700),   # matrix-core expert kernel
+    dict(d_model=256, d_ff=1024, n_experts=6, top_k=2, tokens=300),   # fp4 substrates of both GEMMs
     dict(d_model=256, n_experts=9, top_k=3, tokens=333),
     dict(d_model=128, n_experts=5, top_k=2, tokens=200),    # fp32-rotation expert kernel
     dict(d_model=64, n_experts=3, top_k=1, tokens=65),
