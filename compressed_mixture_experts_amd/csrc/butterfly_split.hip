@@ -17,8 +17,9 @@
 // bytes than activation bytes per row.  Rows are read and written as bf16; the
 // rotations of a part run in fp32.
 //
-// Low part: the chunk rows go through an fp32 LDS tile and the passes of
-// butterfly_impl.hpp (three stages per pass, table of the chunk's (cos, sin)).
+// Low part: the chunk rows go through an fp32 LDS tile in passes of three
+// stages (groups and (cos, sin) table as in butterfly_impl.hpp); every pass
+// covers the whole sub-tile with all its LDS reads issued first.
 // High part: thread (column v, row lane) keeps the (cos, sin) of its column in
 // registers and holds the 16 elements of one row's column at a time (stride
 // 2^S; 64 lanes read 64 consecutive bf16), so all four stages, the GELU
@@ -67,7 +68,72 @@ __device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_exper
   nr = s_info[2];
 }
 
+// One pass (stages 3P .. 3P+M-1) of the chunk butterfly over all RT rows of
+// the sub-tile: each thread owns one group of 2^M elements in RT * G / 256
+// rows, whose reads are all issued before any rotation (rows past the valid
+// ones repeat the last valid row and are not stored).
+template <int S, int P, bool TRANS>
+__device__ __forceinline__ void low_pass(float* __restrict__ tile, const float2* __restrict__ tab) {
+  using C = BflyCfg<S>;
+  constexpr int RT = LowCfg<S>::RT;
+  constexpr int S0 = 3 * P;
+  constexpr int M = (S - S0) < 3 ? (S - S0) : 3;
+  constexpr int E = 1 << M, NCS = M * (E / 2);
+  constexpr int G = C::n >> M;                 // groups per row
+  constexpr int RPT = RT * G / BF_THREADS;     // rows per thread
+  constexpr int TPG = BF_THREADS / G;          // row stride between a thread's rows
+  constexpr int OFF = elem_off<S0>();
+  constexpr bool VEC = (S0 == 0 && M == 3);
+  static_assert(G <= BF_THREADS && RPT >= 1, "tile shape");
+  const int tid = threadIdx.x;
+  const int g = tid & (G - 1), r0 = tid / G;
+  float2 cs[NCS];
+  const float2* t = tab + S0 * C::half + g * NCS;
+#pragma unroll
+  for (int j = 0; j < NCS; ++j) cs[j] = t[j];
+  float* gp = tile + pos(group_base(g, S0, M)) + r0 * C::stride;
+  float v[RPT][E];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const float* rp = gp + k * TPG * C::stride;
+    if constexpr (VEC) {
+      const float4 x0 = reinterpret_cast<const float4*>(rp)[0];
+      const float4 x1 = reinterpret_cast<const float4*>(rp)[1];
+      v[k][0] = x0.x; v[k][1] = x0.y; v[k][2] = x0.z; v[k][3] = x0.w;
+      v[k][4] = x1.x; v[k][5] = x1.y; v[k][6] = x1.z; v[k][7] = x1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[k][e] = rp[e * OFF];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) rotate_group<M, TRANS>(v[k], cs);
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    float* rp = gp + k * TPG * C::stride;
+    if constexpr (VEC) {
+      reinterpret_cast<float4*>(rp)[0] = make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
+      reinterpret_cast<float4*>(rp)[1] = make_float4(v[k][4], v[k][5], v[k][6], v[k][7]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) rp[e * OFF] = v[k][e];
+    }
+  }
+}
+
+template <int S, bool TRANS, int T = 0>
+__device__ __forceinline__ void low_passes(float* tile, const float2* tab) {
+  constexpr int NP = BflyCfg<S>::NP;
+  if constexpr (T < NP) {
+    low_pass<S, TRANS ? NP - 1 - T : T, TRANS>(tile, tab);
+    __syncthreads();
+    low_passes<S, TRANS, T + 1>(tile, tab);
+  }
+}
+
 // Low part of the butterfly of every row, in place allowed (a.in may equal a.out).
+// Sub-tiles of RT rows: the bf16 rows of sub-tile k + 1 are loaded into
+// registers while sub-tile k runs its passes.
 template <int S, bool TRANS>
 __global__ __launch_bounds__(BF_THREADS) void bsplit_low_kernel(BflyArgs a) {
   using C = BflyCfg<S>;
@@ -75,6 +141,9 @@ __global__ __launch_bounds__(BF_THREADS) void bsplit_low_kernel(BflyArgs a) {
   constexpr int L = S + 4;
   constexpr int n = 1 << L, half = n / 2;
   constexpr int nch = n >> S;
+  constexpr int CPR = C::n / 8;                       // 8-element pieces per row
+  constexpr int PPT = LC::RT * CPR / BF_THREADS;      // pieces per thread
+  static_assert(PPT * BF_THREADS == LC::RT * CPR, "sub-tile shape");
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* tile = smem;
   float2* tab = reinterpret_cast<float2*>(smem + LC::tile_floats);
@@ -90,31 +159,44 @@ __global__ __launch_bounds__(BF_THREADS) void bsplit_low_kernel(BflyArgs a) {
     const int s = idx >> (S - 1), p = idx & (C::half - 1);
     tab[table_slot(s, p, S, true)] = sincos_rev(ang[s * half + p]);
   }
-  AngleRegs<S, TAB_FULL> none;
 
-  constexpr int CPR = C::n / 8;  // 8-element chunks per row
-  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in) + size_t(r0) * n + c * C::n;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + size_t(r0) * n + c * C::n;
+  auto load_raw = [&](int rs, uint4 (&raw)[PPT]) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int q = k * BF_THREADS + tid, r = q / CPR, j = q % CPR;
+      raw[k] = *reinterpret_cast<const uint4*>(in + size_t(min(rs + r, nr - 1)) * n + 8 * j);
+    }
+  };
+  uint4 raw[PPT];
+  load_raw(0, raw);
   for (int rs = 0; rs < nr; rs += LC::RT) {
-    const int m = min(LC::RT, nr - rs);
     __syncthreads();  // table written / previous sub-tile stored
-    for (int k = tid; k < m * CPR; k += BF_THREADS) {
-      const int r = k / CPR, j = k % CPR;
-      float v[8];
-      load8<ACT_BF16>(in, size_t(r0 + rs + r) * n + c * C::n + 8 * j, v);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int q = k * BF_THREADS + tid, r = q / CPR, j = q % CPR;
       float* d = tile + r * C::stride + pos(8 * j);
-      reinterpret_cast<float4*>(d)[0] = make_float4(v[0], v[1], v[2], v[3]);
-      reinterpret_cast<float4*>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      reinterpret_cast<float4*>(d)[0] = make_float4(bf16lo(raw[k].x), bf16hi(raw[k].x), bf16lo(raw[k].y), bf16hi(raw[k].y));
+      reinterpret_cast<float4*>(d)[1] = make_float4(bf16lo(raw[k].z), bf16hi(raw[k].z), bf16lo(raw[k].w), bf16hi(raw[k].w));
     }
     __syncthreads();
-    run_passes<S, TRANS, false, 0, TAB_FULL>(tile, m, tab, nullptr, none);
-    for (int k = tid; k < m * CPR; k += BF_THREADS) {
-      const int r = k / CPR, j = k % CPR;
-      const float* sp = tile + r * C::stride + pos(8 * j);
-      const float4 x0 = reinterpret_cast<const float4*>(sp)[0];
-      const float4 x1 = reinterpret_cast<const float4*>(sp)[1];
-      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      store8<ACT_BF16>(out, size_t(r0 + rs + r) * n + c * C::n + 8 * j, v);
+    if (rs + LC::RT < nr) load_raw(rs + LC::RT, raw);
+    low_passes<S, TRANS>(tile, tab);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int q = k * BF_THREADS + tid, r = q / CPR, j = q % CPR;
+      if (rs + r < nr) {
+        const float* sp = tile + r * C::stride + pos(8 * j);
+        const float4 x0 = reinterpret_cast<const float4*>(sp)[0];
+        const float4 x1 = reinterpret_cast<const float4*>(sp)[1];
+        uint4 o;
+        o.x = pack_bf16x2(x0.x, x0.y);
+        o.y = pack_bf16x2(x0.z, x0.w);
+        o.z = pack_bf16x2(x1.x, x1.y);
+        o.w = pack_bf16x2(x1.z, x1.w);
+        *reinterpret_cast<uint4*>(out + size_t(rs + r) * n + 8 * j) = o;
+      }
     }
   }
 }
