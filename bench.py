@@ -86,9 +86,25 @@ def kernel_work(cfg):
         return (2 * R * n * s + nbfly * N * stages * (n // 2) * 4 + extra,
                 6 * R * (n // 2) * stages * nbfly, "hbm")
 
+    def lowfac_bytes(L):
+        # low-part block factors per expert (widths 4096 / 8192, bf16 layers)
+        return {12: 16 * 16384, 13: 16 * 49152}.get(L, 0) if cfg.act == "bf16" else 0
+
+    def low(n):
+        # low part of width n: block factors on the matrix cores where prepared
+        L = int(math.log2(n))
+        fb = lowfac_bytes(L)
+        if not fb:
+            return part(n, L - 4)
+        P0 = 1 << (L - 8)
+        return (2 * R * n * s + N * fb, 2 * R * n * (P0 + 16), "hbm")
+
+    prep_lo = 0
+
     if split(Ld):
         w["bfly_in_hi"] = part(d, 4, extra=4 * R)
-        w["bfly_in_lo"] = part(d, Ld - 4)
+        w["bfly_in_lo"] = low(d)
+        prep_lo += N * (Ld * (d // 2) * 4 + lowfac_bytes(Ld)) if lowfac_bytes(Ld) else 0
     else:
         w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
 
@@ -123,9 +139,10 @@ def kernel_work(cfg):
         Lf = int(math.log2(f))
         w["gemm_up"] = gemm(d, f)
         if split(Lf):
-            w["bfly_mid_lo"] = part(f, Lf - 4)
+            w["bfly_mid_lo"] = low(f)
             w["bfly_mid_hi"] = part(f, 4, nbfly=2)
-            w["bfly_mid_lo_t"] = part(f, Lf - 4)
+            w["bfly_mid_lo_t"] = low(f)
+            prep_lo += 2 * N * (Lf * (f // 2) * 4 + lowfac_bytes(Lf)) if lowfac_bytes(Lf) else 0
         else:
             w["bfly_mid"] = (2 * R * f * s + 2 * N * Lf * (f // 2) * 4, 2 * 6 * R * (f // 2) * Lf, "hbm")
         w["gemm_down"] = gemm(f, d)
@@ -133,10 +150,13 @@ def kernel_work(cfg):
         if pw:
             w["prep"] = (pw, 0, "hbm")
     if split(Ld):
-        w["bfly_out_lo"] = part(d, Ld - 4)
+        w["bfly_out_lo"] = low(d)
+        prep_lo += N * (Ld * (d // 2) * 4 + lowfac_bytes(Ld)) if lowfac_bytes(Ld) else 0
         w["bfly_out_hi"] = part(d, 4, extra=8 * R)
     else:
         w["bfly_out"] = (2 * R * d * s + ang_d + 8 * R, 6 * R * (d // 2) * Ld, "hbm")
+    if prep_lo:
+        w["prep_lo"] = (prep_lo, 0, "hbm")
     if k > 1:
         w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
     return w
@@ -341,7 +361,7 @@ def bm_kernel_sha(kernel: str, cfg) -> str:
     import hashlib
     g = "gemm_fp4.hip" if cfg.act == "bf16" and cfg.d_model >= 256 else "gemm.hip"
     src = {"gemm": g, "gemm_up": g, "gemm_down": g, "combine": "gemm.hip",
-           "route": "route.hip", "bucket": "route.hip", "prep": "prep.hip",
+           "route": "route.hip", "bucket": "route.hip", "prep": "prep.hip", "prep_lo": "butterfly_split.hip",
            "fused": "fused_mfma.hip"}.get(kernel, "butterfly_split.hip" if kernel.endswith(("_hi", "_lo", "_lo_t"))
                                           else "butterfly.hip")
     p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)

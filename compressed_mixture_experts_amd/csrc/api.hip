@@ -153,10 +153,27 @@ bool use_split(const bmoe_layer* L, int log2n) {
 // substrate as bytes (widths 64, 128) or fp4 (256, 512) plus block factors
 // (256, 512).  Other bf16 layers: each substrate whose product the fp4 GEMM
 // covers, as fp4.  fp32 layers: nothing.
+// Low-part block factors of the butterflies of width 4096 / 8192 (bf16 layers):
+// input rotation theta (transposed), output rotation phi, FFN phi_up, FFN
+// theta_dn (transposed).
+enum LowSet { LF_IN = 0, LF_OUT = 1, LF_UP = 2, LF_DN = 3, LF_SETS = 4 };
+
 struct PrepLayout {
   size_t w_off[2], w_len[2], fac_off, fac_len, total;
+  size_t lf_off[LF_SETS], lf_len[LF_SETS];
   bool fp4[2];
 };
+
+// Angles, width and orientation of low-factor set k.
+void low_set(const bmoe_layer* L, int k, const float*& ang, int& log2n, bool& trans) {
+  const bool ffn = L->d_ff != 0;
+  switch (k) {
+    case LF_IN: ang = L->theta[0]; log2n = ilog2(L->d_model); trans = true; break;
+    case LF_OUT: ang = L->phi[ffn ? 1 : 0]; log2n = ilog2(L->d_model); trans = false; break;
+    case LF_UP: ang = L->phi[0]; log2n = ffn ? ilog2(L->d_ff) : 0; trans = false; break;
+    default: ang = L->theta[1]; log2n = ffn ? ilog2(L->d_ff) : 0; trans = true; break;
+  }
+}
 
 PrepLayout prep_layout(const bmoe_layer* L) {
   PrepLayout q{};
@@ -182,9 +199,23 @@ PrepLayout prep_layout(const bmoe_layer* L) {
     o = align256(o + q.w_len[m]);
   }
   q.fac_off = o;
+  for (int k = 0; k < LF_SETS; ++k) {
+    const float* ang;
+    int ln;
+    bool tr;
+    low_set(L, k, ang, ln, tr);
+    if (!ln || !use_split(L, ln) || !low_factor_bytes(ln)) continue;
+    q.lf_off[k] = o;
+    q.lf_len[k] = low_factor_bytes(ln) * size_t(L->n_experts);
+    o = align256(o + q.lf_len[k]);
+  }
   q.total = o;
   return q;
 }
+
+// Launches of the preparation: the substrate / fused-factor kernel when it has
+// work, then one builder per low-factor set.
+bool prep_has_sub(const PrepLayout& q) { return q.w_len[0] || q.w_len[1] || q.fac_len; }
 
 // Arguments of the prep kernel that fills `buf` (layout q) for layer L.
 PrepArgs prep_args(const bmoe_layer* L, const PrepLayout& q, unsigned char* buf) {
@@ -347,10 +378,25 @@ bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, 
     if (overlap(rp, Range{layer->theta[0], angle_bytes}) || overlap(rp, Range{layer->phi[0], angle_bytes}))
       return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
   }
+  for (int k = 0; k < LF_SETS; ++k) {
+    const float* ang;
+    int ln;
+    bool tr;
+    low_set(layer, k, ang, ln, tr);
+    if (q.lf_len[k] && overlap(rp, Range{ang, size_t(layer->n_experts) * ln * (size_t(1) << (ln - 1)) * 4}))
+      return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
+  }
   st = check_device();
   if (st != BMOE_OK) return st;
-  const PrepArgs pa = prep_args(layer, q, static_cast<unsigned char*>(prepared));
-  BMOE_HIP(launch_prep(pa, stream));
+  unsigned char* buf = static_cast<unsigned char*>(prepared);
+  if (prep_has_sub(q)) BMOE_HIP(launch_prep(prep_args(layer, q, buf), stream));
+  for (int k = 0; k < LF_SETS; ++k) {
+    const float* ang;
+    int ln;
+    bool tr;
+    low_set(layer, k, ang, ln, tr);
+    if (q.lf_len[k]) BMOE_HIP(launch_low_factor_prep(ang, buf + q.lf_off[k], layer->n_experts, ln, tr, stream));
+  }
   return ok();
 }
 
@@ -385,7 +431,12 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T, int32_
 // Kernel launches of one forward, in order (marks[i] follows launch i-1).
 static int forward_kernel_names(const bmoe_layer* L, const char** names) {
   int n = 0;
-  if (prep_layout(L).total && !L->prepared) names[n++] = "prep";
+  if (!L->prepared) {
+    const PrepLayout q = prep_layout(L);
+    if (prep_has_sub(q)) names[n++] = "prep";
+    for (int k = 0; k < LF_SETS; ++k)
+      if (q.lf_len[k]) names[n++] = "prep_lo";
+  }
   names[n++] = "route";
   names[n++] = "bucket";
   if (use_fused(L)) {
@@ -478,9 +529,17 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   const unsigned char* pbase = static_cast<const unsigned char*>(layer->prepared);
   if (q.total && !pbase) {
     unsigned char* buf = at<unsigned char>(workspace, p.prep);
-    BMOE_LAUNCH(launch_prep(prep_args(layer, q, buf), stream));
+    if (prep_has_sub(q)) BMOE_LAUNCH(launch_prep(prep_args(layer, q, buf), stream));
+    for (int k = 0; k < LF_SETS; ++k) {
+      const float* ang;
+      int ln;
+      bool tr;
+      low_set(layer, k, ang, ln, tr);
+      if (q.lf_len[k]) BMOE_LAUNCH(launch_low_factor_prep(ang, buf + q.lf_off[k], N, ln, tr, stream));
+    }
     pbase = buf;
   }
+  auto lowfac = [&](int k) -> const unsigned char* { return q.lf_len[k] ? pbase + q.lf_off[k] : nullptr; };
   const unsigned char* wbytes = q.w_len[0] ? pbase + q.w_off[0] : nullptr;
   const unsigned char* wbytes1 = q.w_len[1] ? pbase + q.w_off[1] : nullptr;
   const unsigned char* fac = q.fac_len ? pbase + q.fac_off : nullptr;
@@ -515,7 +574,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
   if (split_d) {
     BMOE_LAUNCH(launch_bfly_split(bi, SPLIT_HIGH_IN, Ld, stream));
-    BflyArgs bl{bufU, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+    BflyArgs bl{bufU, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_IN)};
     BMOE_LAUNCH(launch_bfly_split(bl, SPLIT_LOW_T, Ld, stream));
   } else {
     BMOE_LAUNCH(launch_butterfly(bi, BFLY_IN, act, Ld, stream));
@@ -534,10 +593,10 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
     BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0, gelu};
     if (use_split(layer, ilog2(f))) {
       // B(theta_dn)^T GELU(B(phi_up) h) = low^T(theta) high^T(theta) GELU high(phi) low(phi) h
-      BflyArgs b1{bufZ, bufZ, layer->phi[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+      BflyArgs b1{bufZ, bufZ, layer->phi[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_UP)};
       BMOE_LAUNCH(launch_bfly_split(b1, SPLIT_LOW, ilog2(f), stream));
       BMOE_LAUNCH(launch_bfly_split(bm, SPLIT_HIGH_MID, ilog2(f), stream));
-      BflyArgs b3{bufZ, bufZ, layer->theta[1], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+      BflyArgs b3{bufZ, bufZ, layer->theta[1], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_DN)};
       BMOE_LAUNCH(launch_bfly_split(b3, SPLIT_LOW_T, ilog2(f), stream));
     } else {
       BMOE_LAUNCH(launch_butterfly(bm, BFLY_MID, act, ilog2(f), stream));
@@ -550,7 +609,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   // output rotation, gate, per-slot rows (or y directly when k == 1)
   BflyArgs bo{zlast, k == 1 ? y : yslot, phi_last, nullptr, offsets, perm, gate, R, N, k, 0, 0};
   if (split_d) {
-    BflyArgs bl{zlast, zlast, phi_last, nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+    BflyArgs bl{zlast, zlast, phi_last, nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_OUT)};
     BMOE_LAUNCH(launch_bfly_split(bl, SPLIT_LOW, Ld, stream));
     BMOE_LAUNCH(launch_bfly_split(bo, SPLIT_HIGH_OUT, Ld, stream));
   } else {

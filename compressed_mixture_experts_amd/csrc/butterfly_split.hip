@@ -25,6 +25,7 @@
 // 2^S; 64 lanes read 64 consecutive bf16), so all four stages, the GELU
 // between the FFN's two butterflies and the gate run in registers.
 #include "butterfly_impl.hpp"
+#include "mfma_factors.hpp"
 
 namespace bmoe {
 
@@ -201,6 +202,268 @@ __global__ __launch_bounds__(BF_THREADS) void bsplit_low_kernel(BflyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- matrix-core low part
+// Widths 4096 (S = 8) and 8192 (S = 9).  The low part of a chunk is G1 G0 with
+//   G0 = stages 0 .. S-5: block-diagonal over runs of P0 = 2^(S-4) consecutive
+//        indices (P0 x P0 blocks: 32 at S = 9, 16 at S = 8),
+//   G1 = stages S-4 .. S-1: block-diagonal over the 16 indices u + P0 j (j < 16)
+//        of each u < P0 (16 x 16 blocks),
+// every block the product of its stages' rotations (the pair structure of each
+// stage stays inside one block).  The blocks depend on the angles only, so they
+// are built once per weight set, in bf16 and in the per-lane order of the MFMA
+// operands; a workgroup then multiplies its 64-row tile (bf16, in LDS) by both
+// factors: B x = G1 (G0 x), B^T x = G0^T (G1^T x).
+
+template <int S>
+struct LowMCfg {
+  static constexpr int P0 = 1 << (S - 4);    // G0 block width = number of G1 blocks
+  static constexpr int NB0 = (1 << S) / P0;  // G0 blocks per chunk (16)
+  static constexpr int H0 = P0 / 16;         // 16-row halves of a G0 block
+  static constexpr int RS = (1 << S) + 4;    // LDS row stride in bf16 (8-byte aligned rows)
+  static constexpr int ROWS = SP_RB;
+  static constexpr size_t g0_bytes = size_t(NB0) * P0 * P0 * 2;
+  static constexpr size_t g1_bytes = size_t(P0) * 256 * 2;
+  static constexpr size_t chunk_bytes = g0_bytes + g1_bytes;
+  static constexpr size_t per_expert = 16 * chunk_bytes;
+  static constexpr size_t lds_bytes = size_t(ROWS) * RS * 2;
+  // G1 contraction slot 4g+i holds j = (g&1) DJ + (g>>1) (6-DJ) + (i&1) + 8 (i>>1):
+  // lane groups 0 and 1 then read LDS words 32 banks apart
+  static constexpr int DJ = S == 9 ? 2 : 4;
+};
+
+template <int S>
+__host__ __device__ constexpr int g1_slot(int g, int i) {
+  return (g & 1) * LowMCfg<S>::DJ + (g >> 1) * (6 - LowMCfg<S>::DJ) + (i & 1) + 8 * (i >> 1);
+}
+
+typedef short lm_s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t lm_mfma16(uint2 a, uint2 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(lm_s16x4_t, a),
+                                                    __builtin_bit_cast(lm_s16x4_t, b),
+                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t lm_mfma32(uint4 a, uint4 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+__device__ __forceinline__ uint2 lm_pack4(const f32x4_t& d) {
+  return make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+}
+__device__ __forceinline__ uint2 lm_ld64(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void lm_st64(uint16_t* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+// Factor fragments one wave keeps: G0 blocks 4w .. 4w+3, G1 blocks (u) P0/4 w ..
+template <int S> struct LowFrag;
+template <> struct LowFrag<9> { uint4 g0[4][2]; uint2 g1[8]; };
+template <> struct LowFrag<8> { uint4 g0_unused; uint2 g0[4][1]; uint2 g1[4]; };
+
+// G0 on the tile: wave w owns blocks 4w .. 4w+3 in all 64 rows.  Operand B of
+// row r: the block's contraction values held by lane group g (S = 9: inputs
+// 8g .. 8g+7; S = 8: 4g .. 4g+3); the products overwrite the same elements.
+template <int S>
+__device__ __forceinline__ void lowm_g0(uint16_t* tile, const LowFrag<S>& F, int wave, int g, int l16) {
+  using C = LowMCfg<S>;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    const int b = 4 * wave + bb;
+#pragma unroll
+    for (int rg = 0; rg < C::ROWS / 16; ++rg) {
+      uint16_t* rp = tile + (16 * rg + l16) * C::RS + C::P0 * b;
+      if constexpr (S == 9) {
+        const uint2 x0 = lm_ld64(rp + 8 * g), x1 = lm_ld64(rp + 8 * g + 4);
+        const uint4 bx = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        const f32x4_t d0 = lm_mfma32(F.g0[bb][0], bx), d1 = lm_mfma32(F.g0[bb][1], bx);
+        lm_st64(rp + 4 * g, lm_pack4(d0));
+        lm_st64(rp + 16 + 4 * g, lm_pack4(d1));
+      } else {
+        const f32x4_t d = lm_mfma16(F.g0[bb][0], lm_ld64(rp + 4 * g));
+        lm_st64(rp + 4 * g, lm_pack4(d));
+      }
+    }
+  }
+}
+
+// G1 on the tile: wave w owns u = P0/4 w .. in groups of 4 consecutive u; lane
+// group g reads, for each of its 4 slots, the 4 u's of one j at once (8 bytes)
+// and regroups them per u.
+template <int S>
+__device__ __forceinline__ void lowm_g1(uint16_t* tile, const LowFrag<S>& F, int wave, int g, int l16) {
+  using C = LowMCfg<S>;
+  constexpr int UW = C::P0 / 4;  // u per wave
+#pragma unroll
+  for (int uq = 0; uq < UW / 4; ++uq) {
+    const int u0 = UW * wave + 4 * uq;
+#pragma unroll
+    for (int rg = 0; rg < C::ROWS / 16; ++rg) {
+      uint16_t* rp = tile + (16 * rg + l16) * C::RS + u0;
+      uint2 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + C::P0 * g1_slot<S>(g, i));
+      f32x4_t d[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+        const uint2 bq = (q < 2) ? make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, sel), __builtin_amdgcn_perm(r[3].x, r[2].x, sel))
+                                 : make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, sel), __builtin_amdgcn_perm(r[3].y, r[2].y, sel));
+        d[q] = lm_mfma16(F.g1[4 * uq + q], bq);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lm_st64(rp + C::P0 * g1_slot<S>(g, i),
+                make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
+    }
+  }
+}
+
+// Low part on the matrix cores (in place allowed): WG = (tile of <= 64 rows of
+// one expert, chunk).  Rows past the tile's last repeat it and are not stored.
+template <int S, bool TRANS>
+__global__ __launch_bounds__(BF_THREADS) void lowm_kernel(BflyArgs a) {
+  using C = LowMCfg<S>;
+  constexpr int L = S + 4, n = 1 << L;
+  constexpr int PPR = (1 << S) / 8;                 // 16-byte pieces per row
+  constexpr int PPT = C::ROWS * PPR / BF_THREADS;   // per thread
+  constexpr int BATCH = PPT < 8 ? PPT : 8;
+  extern __shared__ __attribute__((aligned(16))) uint16_t tile[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int t = blockIdx.x / 16, c = blockIdx.x % 16;
+  int e, r0, nr;
+  sp_find_tile(a.offsets, a.n_experts, t, e, r0, nr);
+  if (e < 0) return;
+
+  const unsigned char* fc = a.fac + (size_t(e) * 16 + c) * C::chunk_bytes;
+  LowFrag<S> F;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    if constexpr (S == 9) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        F.g0[bb][h] = *reinterpret_cast<const uint4*>(fc + ((size_t(4 * wave + bb) * 2 + h) * 64 + lane) * 16);
+    } else {
+      F.g0[bb][0] = *reinterpret_cast<const uint2*>(fc + (size_t(4 * wave + bb) * 64 + lane) * 8);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < C::P0 / 4; ++q)
+    F.g1[q] = *reinterpret_cast<const uint2*>(fc + C::g0_bytes + (size_t(C::P0 / 4 * wave + q) * 64 + lane) * 8);
+
+  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in) + size_t(r0) * n + c * (1 << S);
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + size_t(r0) * n + c * (1 << S);
+#pragma unroll
+  for (int k0 = 0; k0 < PPT; k0 += BATCH) {
+    uint4 v[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int q = (k0 + k) * BF_THREADS + tid, r = q / PPR, j = q % PPR;
+      v[k] = *reinterpret_cast<const uint4*>(in + size_t(min(r, nr - 1)) * n + 8 * j);
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int q = (k0 + k) * BF_THREADS + tid, r = q / PPR, j = q % PPR;
+      uint16_t* d = tile + r * C::RS + 8 * j;
+      lm_st64(d, make_uint2(v[k].x, v[k].y));
+      lm_st64(d + 4, make_uint2(v[k].z, v[k].w));
+    }
+  }
+  __syncthreads();
+  if constexpr (!TRANS) {
+    lowm_g0<S>(tile, F, wave, g, l16);
+    __syncthreads();
+    lowm_g1<S>(tile, F, wave, g, l16);
+  } else {
+    lowm_g1<S>(tile, F, wave, g, l16);
+    __syncthreads();
+    lowm_g0<S>(tile, F, wave, g, l16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int q = k * BF_THREADS + tid, r = q / PPR, j = q % PPR;
+    if (r < nr) {
+      const uint16_t* sp = tile + r * C::RS + 8 * j;
+      const uint2 x0 = lm_ld64(sp), x1 = lm_ld64(sp + 4);
+      *reinterpret_cast<uint4*>(out + size_t(r) * n + 8 * j) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+    }
+  }
+}
+
+// Builder: one workgroup per (expert, chunk).  (cos, sin) of the chunk's S
+// stages into LDS, then one job per operand row: G0 (block b, output o), G1
+// (u, output slot).  Operand row o of M is M^T e_o (stages in decreasing order,
+// transposed rotations); of M^T it is M e_o.
+template <int S, bool TRANS>
+__global__ __launch_bounds__(BF_THREADS) void lowfac_kernel(const float* __restrict__ ang, unsigned char* __restrict__ out) {
+  using C = LowMCfg<S>;
+  constexpr int L = S + 4, half = 1 << (L - 1), hc = 1 << (S - 1);
+  constexpr int P0 = C::P0;
+  __shared__ float2 cs[S * hc];
+  const int tid = threadIdx.x;
+  const int e = blockIdx.x / 16, c = blockIdx.x % 16;
+  const float* ae = ang + size_t(e) * L * half + size_t(c) * hc;
+  for (int idx = tid; idx < S * hc; idx += BF_THREADS) cs[idx] = sincos_rev(ae[(idx / hc) * half + idx % hc]);
+  __syncthreads();
+  unsigned char* fc = out + (size_t(e) * 16 + c) * C::chunk_bytes;
+  constexpr int J0 = C::NB0 * P0, J1 = P0 * 16;
+  for (int job = tid; job < J0 + J1; job += BF_THREADS) {
+    if (job < J0) {
+      const int b = job / P0, o = job % P0;
+      float v[P0];
+#pragma unroll
+      for (int q = 0; q < P0; ++q) v[q] = q == o ? 1.0f : 0.0f;
+      rotate_vec<P0, 0, S - 4, TRANS>(v, cs, hc, P0 * b, 1);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        if constexpr (S == 9) {
+          uint4 w;
+          w.x = pack_bf16x2(v[8 * gq + 0], v[8 * gq + 1]);
+          w.y = pack_bf16x2(v[8 * gq + 2], v[8 * gq + 3]);
+          w.z = pack_bf16x2(v[8 * gq + 4], v[8 * gq + 5]);
+          w.w = pack_bf16x2(v[8 * gq + 6], v[8 * gq + 7]);
+          *reinterpret_cast<uint4*>(fc + ((size_t(b) * 2 + o / 16) * 64 + 16 * gq + o % 16) * 16) = w;
+        } else {
+          *reinterpret_cast<uint2*>(fc + (size_t(b) * 64 + 16 * gq + o) * 8) =
+              make_uint2(pack_bf16x2(v[4 * gq], v[4 * gq + 1]), pack_bf16x2(v[4 * gq + 2], v[4 * gq + 3]));
+        }
+      }
+    } else {
+      const int jj = job - J0, u = jj / 16, l = jj % 16;
+      const int jo = g1_slot<S>(l >> 2, l & 3);
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = q == jo ? 1.0f : 0.0f;
+      rotate_vec<16, S - 4, S, TRANS>(v, cs, hc, u, P0);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        *reinterpret_cast<uint2*>(fc + C::g0_bytes + (size_t(u) * 64 + 16 * gq + l) * 8) =
+            make_uint2(pack_bf16x2(v[g1_slot<S>(gq, 0)], v[g1_slot<S>(gq, 1)]),
+                       pack_bf16x2(v[g1_slot<S>(gq, 2)], v[g1_slot<S>(gq, 3)]));
+    }
+  }
+}
+
+size_t low_factor_bytes(int log2n) {
+  return log2n == 12 ? LowMCfg<8>::per_expert : log2n == 13 ? LowMCfg<9>::per_expert : 0;
+}
+
+hipError_t launch_low_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n, bool trans,
+                                  hipStream_t s) {
+  if (n_experts <= 0) return hipSuccess;
+  const dim3 grid(n_experts * 16), block(BF_THREADS);
+  switch (log2n) {
+    case 12:
+      if (trans) hipLaunchKernelGGL((lowfac_kernel<8, true>), grid, block, 0, s, ang, out);
+      else hipLaunchKernelGGL((lowfac_kernel<8, false>), grid, block, 0, s, ang, out);
+      break;
+    case 13:
+      if (trans) hipLaunchKernelGGL((lowfac_kernel<9, true>), grid, block, 0, s, ang, out);
+      else hipLaunchKernelGGL((lowfac_kernel<9, false>), grid, block, 0, s, ang, out);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 enum SplitHigh { SH_IN = 0, SH_MID = 1, SH_OUT = 2 };
 
 // (cos, sin) of the four high stages of column v: cs[t * 8 + q] for stage S+t, local pair q.
@@ -297,6 +560,13 @@ template <int S>
 static hipError_t launch_low_S(const BflyArgs& a, bool trans, hipStream_t s) {
   static int done[2][64] = {{0}};
   const int grid = sp_tiles(a) * 16;
+  if constexpr (S == 8 || S == 9) {
+    if (a.fac) {
+      static int mdone[2][64] = {{0}};
+      if (trans) return sp_launch(lowm_kernel<S, true>, grid, LowMCfg<S>::lds_bytes, a, s, mdone[1]);
+      return sp_launch(lowm_kernel<S, false>, grid, LowMCfg<S>::lds_bytes, a, s, mdone[0]);
+    }
+  }
   if (trans) return sp_launch(bsplit_low_kernel<S, true>, grid, LowCfg<S>::lds_bytes, a, s, done[1]);
   return sp_launch(bsplit_low_kernel<S, false>, grid, LowCfg<S>::lds_bytes, a, s, done[0]);
 }

@@ -159,6 +159,8 @@ struct BflyArgs {
   int32_t top_k;            // IN: token = slot / top_k;  OUT: token when k == 1
   int32_t transpose;        // DBG only
   int32_t gelu;             // MID: apply GELU between the two rotations
+  const unsigned char* fac; // low part of widths 4096 / 8192: prepared block factors
+                            // of ang0 (butterfly_split.hip), or null
 };
 
 // Parts of a wide butterfly run as separate passes (butterfly_split.hip).
@@ -198,6 +200,11 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 bool bfly_split_supported(int log2n);
+// Low-part block factors (matrix-core low part, widths 4096 and 8192): bytes per
+// expert, and the launch that builds them from one butterfly's angles.
+size_t low_factor_bytes(int log2n);
+hipError_t launch_low_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n,
+                                  bool trans, hipStream_t s);
 hipError_t launch_bfly_split(const BflyArgs& a, int part, int log2n, hipStream_t s);
 bool gemm_fp4_supported(int N, int K);
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s);

@@ -231,8 +231,13 @@ def test_prepared_bytes_layout():
     # wider bf16 layers: each substrate whose product the fp4 GEMM covers
     # (output width a multiple of 256, contraction a multiple of 128), as fp4
     assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 2
+    # ... and, at FFN width 4096, the low-part block factors of phi_up and theta_dn:
+    # per expert 16 chunks x (16 blocks 16 x 16 + 16 blocks 16 x 16) bf16
     s = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 2 * (4096 * 1024 // 2)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 2 * (4096 * 1024 // 2) + 2 * 64 * 16 * 16384
+    # width 8192: 16 chunks x (16 blocks 32 x 32 + 32 blocks 16 x 16)
+    s = make_struct(d_model=2048, d_ff=8192, ffn_act=bm.ACT_GELU_ERF)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 2 * (8192 * 2048 // 2) + 2 * 64 * 16 * (32768 + 16384)
     # d_ff = 128: the up product (128 outputs) keeps the 2-bit GEMM, the down one is fp4
     s = make_struct(d_model=1024, d_ff=128, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 2

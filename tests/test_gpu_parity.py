@@ -334,6 +334,7 @@ def test_route_matches_forward_routing():
 PREP_CASES = [
     dict(d_model=512, n_experts=64, top_k=2, tokens=700),   # matrix-core expert kernel
     dict(d_model=256, d_ff=1024, n_experts=6, top_k=2, tokens=300),   # fp4 substrates of both GEMMs
+    dict(d_model=128, d_ff=4096, n_experts=4, top_k=2, tokens=150),   # + low-part block factors
     dict(d_model=256, n_experts=9, top_k=3, tokens=333),
     dict(d_model=128, n_experts=5, top_k=2, tokens=200),    # fp32-rotation expert kernel
     dict(d_model=64, n_experts=3, top_k=1, tokens=65),
