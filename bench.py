@@ -216,6 +216,8 @@ def main() -> int:
                     help="only copy a MIB-MiB device buffer 5 times (HBM counter calibration) and exit")
     ap.add_argument("--per-call-prep", action="store_true",
                     help="re-encode the weights inside every forward instead of once")
+    ap.add_argument("--eager", action="store_true",
+                    help="time launch-by-launch forwards instead of captured-graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU (asked for --gpus {args.gpus}): the ButterflyMoE forward "
@@ -289,11 +291,48 @@ def main() -> int:
         m = [None] * (nk + 1)
         m[dj], m[dj + 1] = starts[i], stops[i]
         step_marks.append(m)
-    print(f"[bench] timing {K} steps (dominant kernel {dom})", file=sys.stderr, flush=True)
+    # eager reference result and eager step time (launch by launch from the host)
+    y_eager = layer.forward(x).clone()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    te0 = time.perf_counter()
     for i in range(K):
         layer.forward_marked(x, y, step_marks[i])
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - te0) / K * 1e3
+
+    # each timed step replays a captured HIP graph of one forward (the same kernel
+    # launches and event records, replayed without host launch gaps); eager
+    # launches when capture is unavailable
+    graphs = []
+    graph_note = None
+    if not args.eager:
+        try:
+            cs = torch.cuda.Stream()
+            for i in range(K):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    layer.forward_marked(x, y, step_marks[i])
+                graphs.append(g)
+            torch.cuda.synchronize()
+            for g in graphs[:3]:  # replays must reproduce the eager result exactly
+                y.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
+                                   y_eager.view(torch.int16) if y.dtype == torch.bfloat16 else y_eager):
+                    raise RuntimeError("graph replay differs from the eager forward")
+        except Exception as ex:  # pragma: no cover - depends on the runtime
+            graphs, graph_note = [], f"graph capture unavailable: {ex}"[:200]
+    print(f"[bench] timing {K} steps (dominant kernel {dom}, "
+          f"{'graph replay' if graphs else 'eager'})", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graphs:
+        for g in graphs:
+            g.replay()
+    else:
+        for i in range(K):
+            layer.forward_marked(x, y, step_marks[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dom_ms = sum(ev.elapsed_ms(starts[i], stops[i]) for i in range(K)) / K
@@ -345,6 +384,8 @@ def main() -> int:
         "data": "synthetic (seeded Gaussian activations, uniform ternary substrate, uniform angles)",
         "weight_prep": ({"once_ms": round(prep_ms, 3), "in_timed_steps": False} if prep_ms is not None
                         else {"in_timed_steps": layer.prepared_bytes() > 0}),
+        "launch": ({"mode": "graph replay", "eager_ms_per_step": round(eager_ms, 5)} if graphs
+                   else {"mode": "eager", "note": graph_note}),
         "config": {"workload": cfg.name, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k, "tokens": cfg.tokens,
                    "routed_rows": cfg.tokens * cfg.top_k, "parallelism": "single GPU"},

@@ -369,3 +369,31 @@ def test_forward_configs_prepared(ci):
     inp = wl.generate(cfg)
     _, _, (y, idx, gate) = run_layer(inp, prepared=True)
     check_forward(inp, y, idx, gate)
+
+
+@pytest.mark.parametrize("ci", [1, 3])
+def test_graph_replay_matches_eager(ci):
+    # a captured HIP graph of one forward, replayed several times with eager
+    # forwards and synchronisations in between, reproduces the eager result
+    import torch
+    cfg = wl.CONFIGS[ci]
+    inp = wl.generate(cfg)
+    layer = bm.Layer.from_inputs(inp, device="cuda")
+    layer.prepare()
+    x = to_dev(inp.x, cfg.act)
+    log(f"graph replay {cfg.name}")
+    y_eager = layer.forward(x).clone()
+    y = torch.empty_like(x)
+    layer.forward(x, y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        layer.forward(x, y)
+    for rep in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), rep
+        y_other = layer.forward(x)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y_other.view(torch.int16), y_eager.view(torch.int16))
