@@ -13,7 +13,9 @@
 // In a K step, lanes 16g .. 16g+15 supply contraction indices 32g .. 32g+31 of
 // the step (8 per MFMA); the activation operand follows the same order.  The
 // loads of step k+1 are issued before the products of step k.
-// Accumulators (up to 256 per lane) live in AGPRs; one workgroup per CU.
+// TN = 256: 64 columns per wave, 128 accumulators per lane, two workgroups
+// per CU (LDS 64 KiB each), so one workgroup's products cover the other's
+// load waits.
 //
 // Tile order: groups of 4 row tiles sweep all column tiles, so a substrate
 // slice is reused by 4 row tiles and an activation tile by every column tile
@@ -46,7 +48,7 @@ __device__ __forceinline__ uint4 gf_fp4x8_to_bf16(uint32_t w) {
 // tile is filled by direct global->LDS loads: one 16-byte load per lane, each
 // wave-wide load filling 4 consecutive rows.
 template <int TN>
-__global__ __launch_bounds__(GF_THREADS, 1) void gemm_fp4_kernel(GemmFp4Args a) {
+__global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) {
   constexpr int WN = TN / 4;                  // output columns per wave
   constexpr int OB = WN / 16;                 // 16-column blocks per wave
   constexpr int MB = GF_TM / 16;              // 16-row blocks
@@ -185,7 +187,6 @@ bool gemm_fp4_supported(int N, int K) { return N % 256 == 0 && K % GF_KS == 0; }
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (!gemm_fp4_supported(a.N, a.K)) return hipErrorInvalidValue;
-  if (a.N % 512 == 0) return launch_gemm_fp4_tn<512>(a, s);
   return launch_gemm_fp4_tn<256>(a, s);
 }
 
