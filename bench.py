@@ -90,6 +90,14 @@ def kernel_work(cfg):
         # low-part block factors per expert (widths 4096 / 8192, bf16 layers)
         return {12: 16 * 16384, 13: 16 * 49152}.get(L, 0) if cfg.act == "bf16" else 0
 
+    def highfac_bytes(L):
+        # high-part block factors per expert (one 16 x 16 bf16 block per column)
+        return (1 << (L - 4)) * 512 if cfg.act == "bf16" and 10 <= L <= 13 else 0
+
+    def high(n, nbfly=1, extra=0):
+        L = int(math.log2(n))
+        return (2 * R * n * s + nbfly * N * highfac_bytes(L) + extra, 2 * R * n * 16 * nbfly, "hbm")
+
     def low(n):
         # low part of width n: block factors on the matrix cores where prepared
         L = int(math.log2(n))
@@ -99,12 +107,13 @@ def kernel_work(cfg):
         P0 = 1 << (L - 8)
         return (2 * R * n * s + N * fb, 2 * R * n * (P0 + 16), "hbm")
 
-    prep_lo = 0
+    prep_lo = prep_hi = 0
 
     if split(Ld):
-        w["bfly_in_hi"] = part(d, 4, extra=4 * R)
+        w["bfly_in_hi"] = high(d, extra=4 * R)
         w["bfly_in_lo"] = low(d)
         prep_lo += N * (Ld * (d // 2) * 4 + lowfac_bytes(Ld)) if lowfac_bytes(Ld) else 0
+        prep_hi += 2 * N * (4 * (d // 2) * 4 + highfac_bytes(Ld))
     else:
         w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
 
@@ -140,9 +149,10 @@ def kernel_work(cfg):
         w["gemm_up"] = gemm(d, f)
         if split(Lf):
             w["bfly_mid_lo"] = low(f)
-            w["bfly_mid_hi"] = part(f, 4, nbfly=2)
+            w["bfly_mid_hi"] = high(f, nbfly=2)
             w["bfly_mid_lo_t"] = low(f)
             prep_lo += 2 * N * (Lf * (f // 2) * 4 + lowfac_bytes(Lf)) if lowfac_bytes(Lf) else 0
+            prep_hi += 2 * N * (4 * (f // 2) * 4 + highfac_bytes(Lf))
         else:
             w["bfly_mid"] = (2 * R * f * s + 2 * N * Lf * (f // 2) * 4, 2 * 6 * R * (f // 2) * Lf, "hbm")
         w["gemm_down"] = gemm(f, d)
@@ -152,11 +162,13 @@ def kernel_work(cfg):
     if split(Ld):
         w["bfly_out_lo"] = low(d)
         prep_lo += N * (Ld * (d // 2) * 4 + lowfac_bytes(Ld)) if lowfac_bytes(Ld) else 0
-        w["bfly_out_hi"] = part(d, 4, extra=8 * R)
+        w["bfly_out_hi"] = high(d, extra=8 * R)
     else:
         w["bfly_out"] = (2 * R * d * s + ang_d + 8 * R, 6 * R * (d // 2) * Ld, "hbm")
     if prep_lo:
         w["prep_lo"] = (prep_lo, 0, "hbm")
+    if prep_hi:
+        w["prep_hi"] = (prep_hi, 0, "hbm")
     if k > 1:
         w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
     return w
@@ -403,6 +415,7 @@ def bm_kernel_sha(kernel: str, cfg) -> str:
     g = "gemm_fp4.hip" if cfg.act == "bf16" and cfg.d_model >= 256 else "gemm.hip"
     src = {"gemm": g, "gemm_up": g, "gemm_down": g, "combine": "gemm.hip",
            "route": "route.hip", "bucket": "route.hip", "prep": "prep.hip", "prep_lo": "butterfly_split.hip",
+           "prep_hi": "butterfly_split.hip",
            "fused": "fused_mfma.hip"}.get(kernel, "butterfly_split.hip" if kernel.endswith(("_hi", "_lo", "_lo_t"))
                                           else "butterfly.hip")
     p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)

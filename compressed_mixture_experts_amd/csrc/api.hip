@@ -160,7 +160,8 @@ enum LowSet { LF_IN = 0, LF_OUT = 1, LF_UP = 2, LF_DN = 3, LF_SETS = 4 };
 
 struct PrepLayout {
   size_t w_off[2], w_len[2], fac_off, fac_len, total;
-  size_t lf_off[LF_SETS], lf_len[LF_SETS];
+  size_t lf_off[LF_SETS], lf_len[LF_SETS];  // low-part block factors
+  size_t hf_off[LF_SETS], hf_len[LF_SETS];  // high-part block factors (one 16 x 16 block per column)
   bool fp4[2];
 };
 
@@ -204,10 +205,17 @@ PrepLayout prep_layout(const bmoe_layer* L) {
     int ln;
     bool tr;
     low_set(L, k, ang, ln, tr);
-    if (!ln || !use_split(L, ln) || !low_factor_bytes(ln)) continue;
-    q.lf_off[k] = o;
-    q.lf_len[k] = low_factor_bytes(ln) * size_t(L->n_experts);
-    o = align256(o + q.lf_len[k]);
+    if (!ln || !use_split(L, ln)) continue;
+    if (low_factor_bytes(ln)) {
+      q.lf_off[k] = o;
+      q.lf_len[k] = low_factor_bytes(ln) * size_t(L->n_experts);
+      o = align256(o + q.lf_len[k]);
+    }
+    if (high_factor_bytes(ln)) {
+      q.hf_off[k] = o;
+      q.hf_len[k] = high_factor_bytes(ln) * size_t(L->n_experts);
+      o = align256(o + q.hf_len[k]);
+    }
   }
   q.total = o;
   return q;
@@ -383,7 +391,7 @@ bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, 
     int ln;
     bool tr;
     low_set(layer, k, ang, ln, tr);
-    if (q.lf_len[k] && overlap(rp, Range{ang, size_t(layer->n_experts) * ln * (size_t(1) << (ln - 1)) * 4}))
+    if ((q.lf_len[k] || q.hf_len[k]) && overlap(rp, Range{ang, size_t(layer->n_experts) * ln * (size_t(1) << (ln - 1)) * 4}))
       return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
   }
   st = check_device();
@@ -396,6 +404,7 @@ bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, 
     bool tr;
     low_set(layer, k, ang, ln, tr);
     if (q.lf_len[k]) BMOE_HIP(launch_low_factor_prep(ang, buf + q.lf_off[k], layer->n_experts, ln, tr, stream));
+    if (q.hf_len[k]) BMOE_HIP(launch_high_factor_prep(ang, buf + q.hf_off[k], layer->n_experts, ln, tr, stream));
   }
   return ok();
 }
@@ -434,8 +443,10 @@ static int forward_kernel_names(const bmoe_layer* L, const char** names) {
   if (!L->prepared) {
     const PrepLayout q = prep_layout(L);
     if (prep_has_sub(q)) names[n++] = "prep";
-    for (int k = 0; k < LF_SETS; ++k)
+    for (int k = 0; k < LF_SETS; ++k) {
       if (q.lf_len[k]) names[n++] = "prep_lo";
+      if (q.hf_len[k]) names[n++] = "prep_hi";
+    }
   }
   names[n++] = "route";
   names[n++] = "bucket";
@@ -536,10 +547,12 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
       bool tr;
       low_set(layer, k, ang, ln, tr);
       if (q.lf_len[k]) BMOE_LAUNCH(launch_low_factor_prep(ang, buf + q.lf_off[k], N, ln, tr, stream));
+      if (q.hf_len[k]) BMOE_LAUNCH(launch_high_factor_prep(ang, buf + q.hf_off[k], N, ln, tr, stream));
     }
     pbase = buf;
   }
   auto lowfac = [&](int k) -> const unsigned char* { return q.lf_len[k] ? pbase + q.lf_off[k] : nullptr; };
+  auto highfac = [&](int k) -> const unsigned char* { return q.hf_len[k] ? pbase + q.hf_off[k] : nullptr; };
   const unsigned char* wbytes = q.w_len[0] ? pbase + q.w_off[0] : nullptr;
   const unsigned char* wbytes1 = q.w_len[1] ? pbase + q.w_off[1] : nullptr;
   const unsigned char* fac = q.fac_len ? pbase + q.fac_off : nullptr;
@@ -571,7 +584,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   }
   // input rotation: U[q] = B(theta_e)^T x_t
   const bool split_d = use_split(layer, Ld);
-  BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+  BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, highfac(LF_IN)};
   if (split_d) {
     BMOE_LAUNCH(launch_bfly_split(bi, SPLIT_HIGH_IN, Ld, stream));
     BflyArgs bl{bufU, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_IN)};
@@ -590,7 +603,8 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   } else {
     BMOE_LAUNCH(substrate_gemm(0, bufU, bufZ, f, d));
     const int gelu = layer->ffn_act == BMOE_ACT_GELU_ERF ? 1 : 0;
-    BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0, gelu};
+    BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0, gelu,
+                highfac(LF_UP), highfac(LF_DN)};
     if (use_split(layer, ilog2(f))) {
       // B(theta_dn)^T GELU(B(phi_up) h) = low^T(theta) high^T(theta) GELU high(phi) low(phi) h
       BflyArgs b1{bufZ, bufZ, layer->phi[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_UP)};
@@ -607,7 +621,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
     phi_last = layer->phi[1];
   }
   // output rotation, gate, per-slot rows (or y directly when k == 1)
-  BflyArgs bo{zlast, k == 1 ? y : yslot, phi_last, nullptr, offsets, perm, gate, R, N, k, 0, 0};
+  BflyArgs bo{zlast, k == 1 ? y : yslot, phi_last, nullptr, offsets, perm, gate, R, N, k, 0, 0, highfac(LF_OUT)};
   if (split_d) {
     BflyArgs bl{zlast, zlast, phi_last, nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_OUT)};
     BMOE_LAUNCH(launch_bfly_split(bl, SPLIT_LOW, Ld, stream));

@@ -539,6 +539,195 @@ __global__ __launch_bounds__(BF_THREADS) void bsplit_high_kernel(BflyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- matrix-core high part
+// The high part of column v is one 16 x 16 matrix H_v (stages S .. S+3 on the
+// indices v + 2^S j), built once per weight set in bf16 and MFMA operand
+// order: operand row l holds output j = (l >> 2) + 4 (l & 3), contraction slot
+// 4g + i input j = g + 4i (so lane groups 0 and 1 read LDS words 32 banks
+// apart).  The accumulator rows 4g + i then hold output j = g + 4i, the order
+// of the next product's operand, so the FFN middle chains two products with
+// the GELU in between without moving data.
+
+template <int S>
+struct HighMCfg {
+  static constexpr int NV = 1 << S;                       // columns
+  static constexpr size_t per_expert = size_t(NV) * 512;  // one 16 x 16 bf16 block per column
+  static constexpr int RT = 16;                           // rows per sub-tile
+  static constexpr int RSB = 16 * SP_VC * 2 + 8;          // LDS bytes per row: [16 j][64 v] bf16 + pad
+  static constexpr size_t lds_bytes = size_t(RT) * RSB;
+};
+
+// Builder: one workgroup per (expert, 16 columns); thread = (column, output
+// slot).  Operand row j of H is H^T e_j, of H^T it is H e_j.
+template <int S, bool TRANS>
+__global__ __launch_bounds__(BF_THREADS) void hfac_kernel(const float* __restrict__ ang, unsigned char* __restrict__ out) {
+  constexpr int L = S + 4, half = 1 << (L - 1);
+  constexpr int NB = HighMCfg<S>::NV / 16;
+  __shared__ float2 cs[16][32];
+  const int tid = threadIdx.x;
+  const int e = blockIdx.x / NB, v0 = (blockIdx.x % NB) * 16;
+  const float* ae = ang + size_t(e) * L * half;
+  for (int idx = tid; idx < 16 * 32; idx += BF_THREADS) {
+    const int c = idx / 32, t = (idx % 32) / 8, q = idx % 8;
+    cs[c][idx % 32] = sincos_rev(ae[(S + t) * half + (q << S) + v0 + c]);
+  }
+  __syncthreads();
+  const int c = tid / 16, l = tid % 16;
+  const int jo = (l >> 2) + 4 * (l & 3);
+  float x[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) x[q] = q == jo ? 1.0f : 0.0f;
+  rotate_group<4, !TRANS>(x, cs[c]);
+  unsigned char* dst = out + size_t(e) * HighMCfg<S>::per_expert + size_t(v0 + c) * 512;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<uint2*>(dst + (16 * g + l) * 8) =
+        make_uint2(pack_bf16x2(x[g], x[g + 4]), pack_bf16x2(x[g + 8], x[g + 12]));
+}
+
+// High part on the matrix cores.  WG = (tile of <= 64 rows of one expert, 64
+// columns); sub-tiles of 16 rows go through LDS as [row][16 j][64 v] bf16
+// (coalesced 16-byte loads and stores); wave w multiplies columns 16w .. 16w+15
+// in groups of 4, reading each j's 4 columns with one 8-byte LDS read.
+template <int S, int MODE>
+__global__ __launch_bounds__(BF_THREADS, 4) void highm_kernel(BflyArgs a) {
+  using C = HighMCfg<S>;
+  constexpr int L = S + 4, n = 1 << L;
+  constexpr int ncb = C::NV / SP_VC;
+  constexpr int PPT = C::RT * 16 * (SP_VC / 8) / BF_THREADS;  // 16-byte pieces per thread (8)
+  extern __shared__ __attribute__((aligned(16))) unsigned char hl[];
+  __shared__ size_t s_row[SP_RB];
+  __shared__ float s_g[SP_RB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int t = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+  int e, r0, nr;
+  sp_find_tile(a.offsets, a.n_experts, t, e, r0, nr);
+  if (e < 0) return;
+
+  const int vw = cb * SP_VC + 16 * wave;  // this wave's first column
+  uint2 fa0[16], fa1[MODE == SH_MID ? 16 : 1];
+  const unsigned char* f0 = a.fac + size_t(e) * C::per_expert;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) fa0[c] = *reinterpret_cast<const uint2*>(f0 + (size_t(vw + c) * 64 + lane) * 8);
+  if constexpr (MODE == SH_MID) {
+    const unsigned char* f1 = a.fac1 + size_t(e) * C::per_expert;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) fa1[c] = *reinterpret_cast<const uint2*>(f1 + (size_t(vw + c) * 64 + lane) * 8);
+  }
+  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  // row tables of all the tile's rows (source or destination row, gate)
+  if (tid < SP_RB) {
+    const int q = r0 + min(tid, nr - 1);
+    if constexpr (MODE == SH_IN) {
+      s_row[tid] = size_t(a.perm[q] / a.top_k) * n;
+    } else if constexpr (MODE == SH_OUT) {
+      const int slot = a.perm[q];
+      s_row[tid] = size_t(slot) * n;
+      s_g[tid] = a.gate[slot];
+    } else {
+      s_row[tid] = size_t(q) * n;
+    }
+  }
+  __syncthreads();
+  // piece p = (row, j, 8 columns) of a sub-tile; rows past the tile's last repeat it
+  auto load = [&](int rs, uint4 (&v)[PPT]) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = k * BF_THREADS + tid, row = min(rs + p / 128, nr - 1), j = (p / 8) % 16, vc = p % 8;
+      const size_t src = MODE == SH_OUT ? size_t(r0 + row) * n : s_row[row];
+      v[k] = *reinterpret_cast<const uint4*>(in + src + (size_t(j) << S) + cb * SP_VC + 8 * vc);
+    }
+  };
+  for (int rs = 0; rs < nr; rs += C::RT) {
+    const int m = min(C::RT, nr - rs);
+    uint4 v[PPT];
+    load(rs, v);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = k * BF_THREADS + tid, row = p / 128, j = (p / 8) % 16, vc = p % 8;
+      uint16_t* d = reinterpret_cast<uint16_t*>(hl + row * C::RSB) + j * SP_VC + 8 * vc;
+      lm_st64(d, make_uint2(v[k].x, v[k].y));
+      lm_st64(d + 4, make_uint2(v[k].z, v[k].w));
+    }
+    __syncthreads();
+    const float gr = MODE == SH_OUT ? s_g[rs + min(l16, m - 1)] : 1.0f;
+    uint16_t* rp = reinterpret_cast<uint16_t*>(hl + l16 * C::RSB) + 16 * wave;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      uint2 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + (g + 4 * i) * SP_VC + 4 * qd);
+      f32x4_t d[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+        const uint2 bq = (q < 2) ? make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, sel), __builtin_amdgcn_perm(r[3].x, r[2].x, sel))
+                                 : make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, sel), __builtin_amdgcn_perm(r[3].y, r[2].y, sel));
+        d[q] = lm_mfma16(fa0[4 * qd + q], bq);
+        if constexpr (MODE == SH_MID) {
+          if (a.gelu) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[q][i] = gelu_erf(d[q][i]);
+          }
+          d[q] = lm_mfma16(fa1[4 * qd + q], lm_pack4(d[q]));
+        }
+        if constexpr (MODE == SH_OUT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[q][i] *= gr;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lm_st64(rp + (g + 4 * i) * SP_VC + 4 * qd,
+                make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = k * BF_THREADS + tid, row = p / 128, j = (p / 8) % 16, vc = p % 8;
+      if (row < m) {
+        const uint16_t* sp = reinterpret_cast<const uint16_t*>(hl + row * C::RSB) + j * SP_VC + 8 * vc;
+        const uint2 x0 = lm_ld64(sp), x1 = lm_ld64(sp + 4);
+        const size_t dst = MODE == SH_OUT ? s_row[rs + row] : size_t(r0 + rs + row) * n;
+        *reinterpret_cast<uint4*>(out + dst + (size_t(j) << S) + cb * SP_VC + 8 * vc) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      }
+    }
+    __syncthreads();  // stored before the next sub-tile is written
+  }
+}
+
+size_t high_factor_bytes(int log2n) {
+  switch (log2n) {
+    case 10: return HighMCfg<6>::per_expert;
+    case 11: return HighMCfg<7>::per_expert;
+    case 12: return HighMCfg<8>::per_expert;
+    case 13: return HighMCfg<9>::per_expert;
+    default: return 0;
+  }
+}
+
+template <int S>
+static hipError_t launch_hfac_S(const float* ang, unsigned char* out, int n_experts, bool trans, hipStream_t s) {
+  const dim3 grid(n_experts * (HighMCfg<S>::NV / 16)), block(BF_THREADS);
+  if (trans) hipLaunchKernelGGL((hfac_kernel<S, true>), grid, block, 0, s, ang, out);
+  else hipLaunchKernelGGL((hfac_kernel<S, false>), grid, block, 0, s, ang, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_high_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n, bool trans,
+                                   hipStream_t s) {
+  if (n_experts <= 0) return hipSuccess;
+  switch (log2n) {
+    case 10: return launch_hfac_S<6>(ang, out, n_experts, trans, s);
+    case 11: return launch_hfac_S<7>(ang, out, n_experts, trans, s);
+    case 12: return launch_hfac_S<8>(ang, out, n_experts, trans, s);
+    case 13: return launch_hfac_S<9>(ang, out, n_experts, trans, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename K>
 static hipError_t sp_launch(K k, int grid, size_t lds, const BflyArgs& a, hipStream_t s, int* attr_done) {
   if (grid <= 0) return hipSuccess;
@@ -575,6 +764,14 @@ template <int S>
 static hipError_t launch_high_S(const BflyArgs& a, int mode, hipStream_t s) {
   static int done[64] = {0};
   const int grid = sp_tiles(a) * ((1 << S) / SP_VC);
+  if (a.fac && (mode != SH_MID || a.fac1)) {
+    const size_t lds = HighMCfg<S>::lds_bytes;
+    switch (mode) {
+      case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s, done);
+      case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s, done);
+      default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s, done);
+    }
+  }
   switch (mode) {
     case SH_IN: return sp_launch(bsplit_high_kernel<S, SH_IN>, grid, 0, a, s, done);
     case SH_MID: return sp_launch(bsplit_high_kernel<S, SH_MID>, grid, 0, a, s, done);

@@ -159,8 +159,8 @@ struct BflyArgs {
   int32_t top_k;            // IN: token = slot / top_k;  OUT: token when k == 1
   int32_t transpose;        // DBG only
   int32_t gelu;             // MID: apply GELU between the two rotations
-  const unsigned char* fac; // low part of widths 4096 / 8192: prepared block factors
-                            // of ang0 (butterfly_split.hip), or null
+  const unsigned char* fac; // prepared block factors of ang0's part (butterfly_split.hip), or null
+  const unsigned char* fac1; // high part of the FFN middle: those of ang1
 };
 
 // Parts of a wide butterfly run as separate passes (butterfly_split.hip).
@@ -205,6 +205,10 @@ bool bfly_split_supported(int log2n);
 size_t low_factor_bytes(int log2n);
 hipError_t launch_low_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n,
                                   bool trans, hipStream_t s);
+// High-part block factors (one 16 x 16 block per column, widths 1024 .. 8192).
+size_t high_factor_bytes(int log2n);
+hipError_t launch_high_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n,
+                                   bool trans, hipStream_t s);
 hipError_t launch_bfly_split(const BflyArgs& a, int part, int log2n, hipStream_t s);
 bool gemm_fp4_supported(int N, int K);
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s);

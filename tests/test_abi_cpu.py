@@ -229,18 +229,22 @@ def test_prepared_bytes_layout():
     s = make_struct(d_model=128)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 128 * 128
     # wider bf16 layers: each substrate whose product the fp4 GEMM covers
-    # (output width a multiple of 256, contraction a multiple of 128), as fp4
-    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 2
-    # ... and, at FFN width 4096, the low-part block factors of phi_up and theta_dn:
-    # per expert 16 chunks x (16 blocks 16 x 16 + 16 blocks 16 x 16) bf16
+    # (output width a multiple of 256, contraction a multiple of 128), as fp4;
+    # every rotation of width 1024 .. 8192: one 16 x 16 high-part block per column
+    # (width / 16 columns), and at widths 4096 / 8192 the low-part block factors
+    # (16 chunks x (16 blocks 16 x 16 + 16 blocks 16 x 16), or (16 blocks 32 x 32
+    # + 32 blocks 16 x 16))
+    hi = lambda w: (w // 16) * 512
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 2 + 2 * 64 * hi(1024)
     s = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 2 * (4096 * 1024 // 2) + 2 * 64 * 16 * 16384
-    # width 8192: 16 chunks x (16 blocks 32 x 32 + 32 blocks 16 x 16)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (4096 * 1024 // 2) + 2 * 64 * hi(1024)
+                                                      + 2 * 64 * (16 * 16384 + hi(4096)))
     s = make_struct(d_model=2048, d_ff=8192, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 2 * (8192 * 2048 // 2) + 2 * 64 * 16 * (32768 + 16384)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (8192 * 2048 // 2) + 2 * 64 * hi(2048)
+                                                      + 2 * 64 * (16 * (32768 + 16384) + hi(8192)))
     # d_ff = 128: the up product (128 outputs) keeps the 2-bit GEMM, the down one is fp4
     s = make_struct(d_model=1024, d_ff=128, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 2
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 2 + 2 * 64 * hi(1024)
     s = make_struct(d_model=128, d_ff=64, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 0
     # fp32 activations and invalid layers use none
