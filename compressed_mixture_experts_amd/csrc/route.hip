@@ -805,8 +805,10 @@ static hipError_t launch_route_bt(const RouteArgs& a, int act, hipStream_t s) {
 
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  // 64-token tiles once they give every CU a workgroup, 16-token tiles below
+  // the largest token tile (64, 32 or 16 tokens) that still gives every CU a
+  // workgroup: each workgroup reads the whole gate matrix once
   if (a.T >= 64 * 256) return launch_route_bt<64>(a, act, s);
+  if (a.T >= 32 * 256) return launch_route_bt<32>(a, act, s);
   return launch_route_bt<16>(a, act, s);
 }
 
