@@ -87,8 +87,11 @@ def kernel_work(cfg):
                 6 * R * (n // 2) * stages * nbfly, "hbm")
 
     def lowfac_bytes(L):
-        # low-part block factors per expert (widths 4096 / 8192, bf16 layers)
-        return {12: 16 * 16384, 13: 16 * 49152}.get(L, 0) if cfg.act == "bf16" else 0
+        # low-part block factors per expert (widths 1024 .. 8192, bf16 layers)
+        if cfg.act != "bf16" or not 10 <= L <= 13:
+            return 0
+        w = 1 << L
+        return 16 * ((w // 16) * max(16, w // 256) * 2 + (w // 256) * 512)
 
     def highfac_bytes(L):
         # high-part block factors per expert (one 16 x 16 bf16 block per column)
@@ -104,8 +107,8 @@ def kernel_work(cfg):
         fb = lowfac_bytes(L)
         if not fb:
             return part(n, L - 4)
-        P0 = 1 << (L - 8)
-        return (2 * R * n * s + N * fb, 2 * R * n * (P0 + 16), "hbm")
+        B0 = max(16, 1 << (L - 8))
+        return (2 * R * n * s + N * fb, 2 * R * n * (B0 + 16), "hbm")
 
     prep_lo = prep_hi = 0
 

@@ -10,20 +10,14 @@
 //               index of a width-16 butterfly at stage t) uses angle q 2^S + v.
 // B = high * low, so B x runs low then high, B^T x high^T then low^T.
 //
-// Each workgroup owns up to SP_RB rows of ONE expert and one chunk (low) or 64
-// columns (high), so the expert's angles for that part are loaded and turned
-// into (cos, sin) once per workgroup and reused for all its rows; a width that
-// has more angles than a row has elements would otherwise move more angle
-// bytes than activation bytes per row.  Rows are read and written as bf16; the
-// rotations of a part run in fp32.
-//
-// Low part: the chunk rows go through an fp32 LDS tile in passes of three
-// stages (groups and (cos, sin) table as in butterfly_impl.hpp); every pass
-// covers the whole sub-tile with all its LDS reads issued first.
-// High part: thread (column v, row lane) keeps the (cos, sin) of its column in
-// registers and holds the 16 elements of one row's column at a time (stride
-// 2^S; 64 lanes read 64 consecutive bf16), so all four stages, the GELU
-// between the FFN's two butterflies and the gate run in registers.
+// Both parts are products with block-diagonal factors on the matrix cores,
+// built from the angles once per weight set (bf16, MFMA operand order) by the
+// builder kernels below.  Each workgroup owns up to SP_RB rows of ONE expert
+// and a range of chunks (low) or 64 columns (high), so its factor fragments are
+// loaded once and reused for all its rows; a width that has more angles than a
+// row has elements would otherwise move more parameter bytes than activation
+// bytes per row.  Rows are read and written as bf16, products accumulate in
+// fp32.
 #include "butterfly_impl.hpp"
 #include "mfma_factors.hpp"
 
@@ -31,15 +25,6 @@ namespace bmoe {
 
 constexpr int SP_RB = 64;  // rows per workgroup
 constexpr int SP_VC = 64;  // high part: columns per workgroup
-
-template <int S>
-struct LowCfg {
-  static constexpr int n = 1 << S;
-  static constexpr int RT = S >= 8 ? 16 : 32;  // rows per sub-tile
-  static constexpr size_t tile_floats = size_t(RT) * BflyCfg<S>::stride;
-  static constexpr size_t tab_pairs = size_t(S) << (S - 1);
-  static constexpr size_t lds_bytes = tile_floats * 4 + tab_pairs * 8;
-};
 
 // Workgroup tile t -> (expert e, first bucket row r0, rows nr) with tiles of
 // SP_RB rows per expert in expert order; e = -1 past the last tile.
@@ -69,171 +54,48 @@ __device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_exper
   nr = s_info[2];
 }
 
-// One pass (stages 3P .. 3P+M-1) of the chunk butterfly over all RT rows of
-// the sub-tile: each thread owns one group of 2^M elements in RT * G / 256
-// rows, whose reads are all issued before any rotation (rows past the valid
-// ones repeat the last valid row and are not stored).
-template <int S, int P, bool TRANS>
-__device__ __forceinline__ void low_pass(float* __restrict__ tile, const float2* __restrict__ tab) {
-  using C = BflyCfg<S>;
-  constexpr int RT = LowCfg<S>::RT;
-  constexpr int S0 = 3 * P;
-  constexpr int M = (S - S0) < 3 ? (S - S0) : 3;
-  constexpr int E = 1 << M, NCS = M * (E / 2);
-  constexpr int G = C::n >> M;                 // groups per row
-  constexpr int RPT = RT * G / BF_THREADS;     // rows per thread
-  constexpr int TPG = BF_THREADS / G;          // row stride between a thread's rows
-  constexpr int OFF = elem_off<S0>();
-  constexpr bool VEC = (S0 == 0 && M == 3);
-  static_assert(G <= BF_THREADS && RPT >= 1, "tile shape");
-  const int tid = threadIdx.x;
-  const int g = tid & (G - 1), r0 = tid / G;
-  float2 cs[NCS];
-  const float2* t = tab + S0 * C::half + g * NCS;
-#pragma unroll
-  for (int j = 0; j < NCS; ++j) cs[j] = t[j];
-  float* gp = tile + pos(group_base(g, S0, M)) + r0 * C::stride;
-  float v[RPT][E];
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const float* rp = gp + k * TPG * C::stride;
-    if constexpr (VEC) {
-      const float4 x0 = reinterpret_cast<const float4*>(rp)[0];
-      const float4 x1 = reinterpret_cast<const float4*>(rp)[1];
-      v[k][0] = x0.x; v[k][1] = x0.y; v[k][2] = x0.z; v[k][3] = x0.w;
-      v[k][4] = x1.x; v[k][5] = x1.y; v[k][6] = x1.z; v[k][7] = x1.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) v[k][e] = rp[e * OFF];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) rotate_group<M, TRANS>(v[k], cs);
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    float* rp = gp + k * TPG * C::stride;
-    if constexpr (VEC) {
-      reinterpret_cast<float4*>(rp)[0] = make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
-      reinterpret_cast<float4*>(rp)[1] = make_float4(v[k][4], v[k][5], v[k][6], v[k][7]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) rp[e * OFF] = v[k][e];
-    }
-  }
-}
-
-template <int S, bool TRANS, int T = 0>
-__device__ __forceinline__ void low_passes(float* tile, const float2* tab) {
-  constexpr int NP = BflyCfg<S>::NP;
-  if constexpr (T < NP) {
-    low_pass<S, TRANS ? NP - 1 - T : T, TRANS>(tile, tab);
-    __syncthreads();
-    low_passes<S, TRANS, T + 1>(tile, tab);
-  }
-}
-
-// Low part of the butterfly of every row, in place allowed (a.in may equal a.out).
-// Sub-tiles of RT rows: the bf16 rows of sub-tile k + 1 are loaded into
-// registers while sub-tile k runs its passes.
-template <int S, bool TRANS>
-__global__ __launch_bounds__(BF_THREADS) void bsplit_low_kernel(BflyArgs a) {
-  using C = BflyCfg<S>;
-  using LC = LowCfg<S>;
-  constexpr int L = S + 4;
-  constexpr int n = 1 << L, half = n / 2;
-  constexpr int nch = n >> S;
-  constexpr int CPR = C::n / 8;                       // 8-element pieces per row
-  constexpr int PPT = LC::RT * CPR / BF_THREADS;      // pieces per thread
-  static_assert(PPT * BF_THREADS == LC::RT * CPR, "sub-tile shape");
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  float* tile = smem;
-  float2* tab = reinterpret_cast<float2*>(smem + LC::tile_floats);
-  const int tid = threadIdx.x;
-  const int t = blockIdx.x / nch, c = blockIdx.x % nch;
-  int e, r0, nr;
-  sp_find_tile(a.offsets, a.n_experts, t, e, r0, nr);
-  if (e < 0) return;
-
-  // (cos, sin) of the chunk's S stages, group-major as the passes read them
-  const float* ang = a.ang0 + size_t(e) * L * half + size_t(c) * C::half;
-  for (int idx = tid; idx < S * C::half; idx += BF_THREADS) {
-    const int s = idx >> (S - 1), p = idx & (C::half - 1);
-    tab[table_slot(s, p, S, true)] = sincos_rev(ang[s * half + p]);
-  }
-
-  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in) + size_t(r0) * n + c * C::n;
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + size_t(r0) * n + c * C::n;
-  auto load_raw = [&](int rs, uint4 (&raw)[PPT]) {
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int q = k * BF_THREADS + tid, r = q / CPR, j = q % CPR;
-      raw[k] = *reinterpret_cast<const uint4*>(in + size_t(min(rs + r, nr - 1)) * n + 8 * j);
-    }
-  };
-  uint4 raw[PPT];
-  load_raw(0, raw);
-  for (int rs = 0; rs < nr; rs += LC::RT) {
-    __syncthreads();  // table written / previous sub-tile stored
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int q = k * BF_THREADS + tid, r = q / CPR, j = q % CPR;
-      float* d = tile + r * C::stride + pos(8 * j);
-      reinterpret_cast<float4*>(d)[0] = make_float4(bf16lo(raw[k].x), bf16hi(raw[k].x), bf16lo(raw[k].y), bf16hi(raw[k].y));
-      reinterpret_cast<float4*>(d)[1] = make_float4(bf16lo(raw[k].z), bf16hi(raw[k].z), bf16lo(raw[k].w), bf16hi(raw[k].w));
-    }
-    __syncthreads();
-    if (rs + LC::RT < nr) load_raw(rs + LC::RT, raw);
-    low_passes<S, TRANS>(tile, tab);
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int q = k * BF_THREADS + tid, r = q / CPR, j = q % CPR;
-      if (rs + r < nr) {
-        const float* sp = tile + r * C::stride + pos(8 * j);
-        const float4 x0 = reinterpret_cast<const float4*>(sp)[0];
-        const float4 x1 = reinterpret_cast<const float4*>(sp)[1];
-        uint4 o;
-        o.x = pack_bf16x2(x0.x, x0.y);
-        o.y = pack_bf16x2(x0.z, x0.w);
-        o.z = pack_bf16x2(x1.x, x1.y);
-        o.w = pack_bf16x2(x1.z, x1.w);
-        *reinterpret_cast<uint4*>(out + size_t(rs + r) * n + 8 * j) = o;
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- matrix-core low part
-// Widths 4096 (S = 8) and 8192 (S = 9).  The low part of a chunk is G1 G0 with
-//   G0 = stages 0 .. S-5: block-diagonal over runs of P0 = 2^(S-4) consecutive
-//        indices (P0 x P0 blocks: 32 at S = 9, 16 at S = 8),
+// Widths 1024 .. 8192 (S = 6 .. 9).  The low part of a chunk is G1 G0 with
+//   G0 = stages 0 .. S-5: block-diagonal over runs of B0 = max(16, 2^(S-4))
+//        consecutive indices (32 x 32 blocks at S = 9, 16 x 16 below; at
+//        S < 8 a block only mixes its low S-4 bits),
 //   G1 = stages S-4 .. S-1: block-diagonal over the 16 indices u + P0 j (j < 16)
-//        of each u < P0 (16 x 16 blocks),
+//        of each u < P0 = 2^(S-4) (16 x 16 blocks),
 // every block the product of its stages' rotations (the pair structure of each
 // stage stays inside one block).  The blocks depend on the angles only, so they
 // are built once per weight set, in bf16 and in the per-lane order of the MFMA
 // operands; a workgroup then multiplies its 64-row tile (bf16, in LDS) by both
-// factors: B x = G1 (G0 x), B^T x = G0^T (G1^T x).
+// factors: B x = G1 (G0 x), B^T x = G0^T (G1^T x).  A workgroup covers
+// SC = max(1, 256 / 2^S) consecutive chunks, so each wave owns 4 blocks of G0
+// and 4 (S = 9: 8) blocks of G1.
 
 template <int S>
 struct LowMCfg {
-  static constexpr int P0 = 1 << (S - 4);    // G0 block width = number of G1 blocks
-  static constexpr int NB0 = (1 << S) / P0;  // G0 blocks per chunk (16)
-  static constexpr int H0 = P0 / 16;         // 16-row halves of a G0 block
-  static constexpr int RS = (1 << S) + 4;    // LDS row stride in bf16 (8-byte aligned rows)
+  static constexpr int P0 = 1 << (S - 4);        // G1 stride = number of G1 blocks per chunk
+  static constexpr int B0 = P0 > 16 ? P0 : 16;   // G0 block width
+  static constexpr int NB0 = (1 << S) / B0;      // G0 blocks per chunk
+  static constexpr int SC = S >= 8 ? 1 : (256 >> S);   // chunks per workgroup
+  static constexpr int W = SC << S;              // indices per workgroup row
+  static constexpr int RS = W + 4;               // LDS row stride in bf16 (8-byte aligned rows)
   static constexpr int ROWS = SP_RB;
-  static constexpr size_t g0_bytes = size_t(NB0) * P0 * P0 * 2;
+  static constexpr size_t g0_bytes = size_t(NB0) * B0 * B0 * 2;
   static constexpr size_t g1_bytes = size_t(P0) * 256 * 2;
   static constexpr size_t chunk_bytes = g0_bytes + g1_bytes;
   static constexpr size_t per_expert = 16 * chunk_bytes;
   static constexpr size_t lds_bytes = size_t(ROWS) * RS * 2;
-  // G1 contraction slot 4g+i holds j = (g&1) DJ + (g>>1) (6-DJ) + (i&1) + 8 (i>>1):
-  // lane groups 0 and 1 then read LDS words 32 banks apart
-  static constexpr int DJ = S == 9 ? 2 : 4;
+  static constexpr int G0W = W / B0 / 4;         // G0 blocks per wave (4)
+  static constexpr int UQW = W / 16 / 4 / 4;     // G1 groups of 4 blocks per wave (1, or 2 at S = 9)
+  static_assert(G0W == 4 && UQW >= 1, "wave shape");
 };
 
+// G1 contraction slot 4g+i holds j = (g&1) A + (g>>1) B + (i&1) C + (i>>1) D, with
+// A chosen so lane groups 0 and 1 read LDS words 32 banks apart where the
+// stride allows it (any permutation of 0..15 is a valid slot order)
 template <int S>
 __host__ __device__ constexpr int g1_slot(int g, int i) {
-  return (g & 1) * LowMCfg<S>::DJ + (g >> 1) * (6 - LowMCfg<S>::DJ) + (i & 1) + 8 * (i >> 1);
+  return S == 9   ? (g & 1) * 2 + (g >> 1) * 4 + (i & 1) + 8 * (i >> 1)
+         : S == 8 ? (g & 1) * 4 + (g >> 1) * 2 + (i & 1) + 8 * (i >> 1)
+                  : (g & 1) * 8 + (g >> 1) * 4 + (i & 1) + 2 * (i >> 1);
 }
 
 typedef short lm_s16x4_t __attribute__((ext_vector_type(4)));
@@ -252,14 +114,19 @@ __device__ __forceinline__ uint2 lm_pack4(const f32x4_t& d) {
 __device__ __forceinline__ uint2 lm_ld64(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ void lm_st64(uint16_t* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
 
-// Factor fragments one wave keeps: G0 blocks 4w .. 4w+3, G1 blocks (u) P0/4 w ..
-template <int S> struct LowFrag;
-template <> struct LowFrag<9> { uint4 g0[4][2]; uint2 g1[8]; };
-template <> struct LowFrag<8> { uint4 g0_unused; uint2 g0[4][1]; uint2 g1[4]; };
+// Factor fragments one wave keeps: its 4 G0 blocks (two 16-row halves at
+// S = 9) and its 4 UQW G1 blocks.
+template <int S>
+struct LowFrag {
+  uint4 g0w[S == 9 ? 4 : 1][2];
+  uint2 g0[4];
+  uint2 g1[4 * LowMCfg<S>::UQW];
+};
 
-// G0 on the tile: wave w owns blocks 4w .. 4w+3 in all 64 rows.  Operand B of
-// row r: the block's contraction values held by lane group g (S = 9: inputs
-// 8g .. 8g+7; S = 8: 4g .. 4g+3); the products overwrite the same elements.
+// G0 on the tile: wave w owns blocks 4w .. 4w+3 (of B0 consecutive indices) in
+// all 64 rows.  Operand B of row r: the block's contraction values held by
+// lane group g (B0 = 32: inputs 8g .. 8g+7; else 4g .. 4g+3); the products
+// overwrite the same elements.
 template <int S>
 __device__ __forceinline__ void lowm_g0(uint16_t* tile, const LowFrag<S>& F, int wave, int g, int l16) {
   using C = LowMCfg<S>;
@@ -268,34 +135,34 @@ __device__ __forceinline__ void lowm_g0(uint16_t* tile, const LowFrag<S>& F, int
     const int b = 4 * wave + bb;
 #pragma unroll
     for (int rg = 0; rg < C::ROWS / 16; ++rg) {
-      uint16_t* rp = tile + (16 * rg + l16) * C::RS + C::P0 * b;
-      if constexpr (S == 9) {
+      uint16_t* rp = tile + (16 * rg + l16) * C::RS + C::B0 * b;
+      if constexpr (C::B0 == 32) {
         const uint2 x0 = lm_ld64(rp + 8 * g), x1 = lm_ld64(rp + 8 * g + 4);
         const uint4 bx = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        const f32x4_t d0 = lm_mfma32(F.g0[bb][0], bx), d1 = lm_mfma32(F.g0[bb][1], bx);
+        const f32x4_t d0 = lm_mfma32(F.g0w[bb][0], bx), d1 = lm_mfma32(F.g0w[bb][1], bx);
         lm_st64(rp + 4 * g, lm_pack4(d0));
         lm_st64(rp + 16 + 4 * g, lm_pack4(d1));
       } else {
-        const f32x4_t d = lm_mfma16(F.g0[bb][0], lm_ld64(rp + 4 * g));
+        const f32x4_t d = lm_mfma16(F.g0[bb], lm_ld64(rp + 4 * g));
         lm_st64(rp + 4 * g, lm_pack4(d));
       }
     }
   }
 }
 
-// G1 on the tile: wave w owns u = P0/4 w .. in groups of 4 consecutive u; lane
-// group g reads, for each of its 4 slots, the 4 u's of one j at once (8 bytes)
-// and regroups them per u.
+// G1 on the tile: group k of 4 consecutive blocks (chunk 4k / P0, u0 = 4k % P0)
+// belongs to wave k / UQW; lane group g reads, for each of its 4 slots, the 4
+// u's of one j at once (8 bytes) and regroups them per u.
 template <int S>
 __device__ __forceinline__ void lowm_g1(uint16_t* tile, const LowFrag<S>& F, int wave, int g, int l16) {
   using C = LowMCfg<S>;
-  constexpr int UW = C::P0 / 4;  // u per wave
 #pragma unroll
-  for (int uq = 0; uq < UW / 4; ++uq) {
-    const int u0 = UW * wave + 4 * uq;
+  for (int uq = 0; uq < C::UQW; ++uq) {
+    const int k = C::UQW * wave + uq;
+    const int base = ((4 * k) / C::P0 << S) + (4 * k) % C::P0;
 #pragma unroll
     for (int rg = 0; rg < C::ROWS / 16; ++rg) {
-      uint16_t* rp = tile + (16 * rg + l16) * C::RS + u0;
+      uint16_t* rp = tile + (16 * rg + l16) * C::RS + base;
       uint2 r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + C::P0 * g1_slot<S>(g, i));
@@ -316,40 +183,49 @@ __device__ __forceinline__ void lowm_g1(uint16_t* tile, const LowFrag<S>& F, int
 }
 
 // Low part on the matrix cores (in place allowed): WG = (tile of <= 64 rows of
-// one expert, chunk).  Rows past the tile's last repeat it and are not stored.
+// one expert, SC consecutive chunks).  Rows past the tile's last repeat it and
+// are not stored.
 template <int S, bool TRANS>
 __global__ __launch_bounds__(BF_THREADS) void lowm_kernel(BflyArgs a) {
   using C = LowMCfg<S>;
   constexpr int L = S + 4, n = 1 << L;
-  constexpr int PPR = (1 << S) / 8;                 // 16-byte pieces per row
+  constexpr int NWG = 16 / C::SC;                   // workgroups per row
+  constexpr int PPR = C::W / 8;                     // 16-byte pieces per row
   constexpr int PPT = C::ROWS * PPR / BF_THREADS;   // per thread
   constexpr int BATCH = PPT < 8 ? PPT : 8;
   extern __shared__ __attribute__((aligned(16))) uint16_t tile[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int t = blockIdx.x / 16, c = blockIdx.x % 16;
+  const int t = blockIdx.x / NWG, c0 = (blockIdx.x % NWG) * C::SC;
   int e, r0, nr;
   sp_find_tile(a.offsets, a.n_experts, t, e, r0, nr);
   if (e < 0) return;
 
-  const unsigned char* fc = a.fac + (size_t(e) * 16 + c) * C::chunk_bytes;
+  // this wave's fragments; block b of the workgroup lies in chunk c0 + b / NB0
+  const unsigned char* fe = a.fac + (size_t(e) * 16 + c0) * C::chunk_bytes;
   LowFrag<S> F;
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
-    if constexpr (S == 9) {
+    const int b = 4 * wave + bb;
+    const unsigned char* fc = fe + (b / C::NB0) * C::chunk_bytes + size_t(b % C::NB0) * C::B0 * C::B0 * 2;
+    if constexpr (C::B0 == 32) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        F.g0[bb][h] = *reinterpret_cast<const uint4*>(fc + ((size_t(4 * wave + bb) * 2 + h) * 64 + lane) * 16);
+      for (int h = 0; h < 2; ++h) F.g0w[bb][h] = *reinterpret_cast<const uint4*>(fc + (h * 64 + lane) * 16);
     } else {
-      F.g0[bb][0] = *reinterpret_cast<const uint2*>(fc + (size_t(4 * wave + bb) * 64 + lane) * 8);
+      F.g0[bb] = *reinterpret_cast<const uint2*>(fc + lane * 8);
     }
   }
 #pragma unroll
-  for (int q = 0; q < C::P0 / 4; ++q)
-    F.g1[q] = *reinterpret_cast<const uint2*>(fc + C::g0_bytes + (size_t(C::P0 / 4 * wave + q) * 64 + lane) * 8);
+  for (int uq = 0; uq < C::UQW; ++uq) {
+    const int k = C::UQW * wave + uq;
+    const unsigned char* fc = fe + ((4 * k) / C::P0) * C::chunk_bytes + C::g0_bytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      F.g1[4 * uq + q] = *reinterpret_cast<const uint2*>(fc + (size_t((4 * k) % C::P0 + q) * 64 + lane) * 8);
+  }
 
-  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in) + size_t(r0) * n + c * (1 << S);
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + size_t(r0) * n + c * (1 << S);
+  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in) + size_t(r0) * n + (c0 << S);
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + size_t(r0) * n + (c0 << S);
 #pragma unroll
   for (int k0 = 0; k0 < PPT; k0 += BATCH) {
     uint4 v[BATCH];
@@ -396,7 +272,7 @@ template <int S, bool TRANS>
 __global__ __launch_bounds__(BF_THREADS) void lowfac_kernel(const float* __restrict__ ang, unsigned char* __restrict__ out) {
   using C = LowMCfg<S>;
   constexpr int L = S + 4, half = 1 << (L - 1), hc = 1 << (S - 1);
-  constexpr int P0 = C::P0;
+  constexpr int P0 = C::P0, B0 = C::B0;
   __shared__ float2 cs[S * hc];
   const int tid = threadIdx.x;
   const int e = blockIdx.x / 16, c = blockIdx.x % 16;
@@ -404,17 +280,17 @@ __global__ __launch_bounds__(BF_THREADS) void lowfac_kernel(const float* __restr
   for (int idx = tid; idx < S * hc; idx += BF_THREADS) cs[idx] = sincos_rev(ae[(idx / hc) * half + idx % hc]);
   __syncthreads();
   unsigned char* fc = out + (size_t(e) * 16 + c) * C::chunk_bytes;
-  constexpr int J0 = C::NB0 * P0, J1 = P0 * 16;
+  constexpr int J0 = C::NB0 * B0, J1 = P0 * 16;
   for (int job = tid; job < J0 + J1; job += BF_THREADS) {
     if (job < J0) {
-      const int b = job / P0, o = job % P0;
-      float v[P0];
+      const int b = job / B0, o = job % B0;
+      float v[B0];
 #pragma unroll
-      for (int q = 0; q < P0; ++q) v[q] = q == o ? 1.0f : 0.0f;
-      rotate_vec<P0, 0, S - 4, TRANS>(v, cs, hc, P0 * b, 1);
+      for (int q = 0; q < B0; ++q) v[q] = q == o ? 1.0f : 0.0f;
+      rotate_vec<B0, 0, S - 4, TRANS>(v, cs, hc, B0 * b, 1);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        if constexpr (S == 9) {
+        if constexpr (B0 == 32) {
           uint4 w;
           w.x = pack_bf16x2(v[8 * gq + 0], v[8 * gq + 1]);
           w.y = pack_bf16x2(v[8 * gq + 2], v[8 * gq + 3]);
@@ -443,101 +319,36 @@ __global__ __launch_bounds__(BF_THREADS) void lowfac_kernel(const float* __restr
 }
 
 size_t low_factor_bytes(int log2n) {
-  return log2n == 12 ? LowMCfg<8>::per_expert : log2n == 13 ? LowMCfg<9>::per_expert : 0;
+  switch (log2n) {
+    case 10: return LowMCfg<6>::per_expert;
+    case 11: return LowMCfg<7>::per_expert;
+    case 12: return LowMCfg<8>::per_expert;
+    case 13: return LowMCfg<9>::per_expert;
+    default: return 0;
+  }
+}
+
+template <int S>
+static hipError_t launch_lowfac_S(const float* ang, unsigned char* out, int n_experts, bool trans, hipStream_t s) {
+  const dim3 grid(n_experts * 16), block(BF_THREADS);
+  if (trans) hipLaunchKernelGGL((lowfac_kernel<S, true>), grid, block, 0, s, ang, out);
+  else hipLaunchKernelGGL((lowfac_kernel<S, false>), grid, block, 0, s, ang, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_low_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n, bool trans,
                                   hipStream_t s) {
   if (n_experts <= 0) return hipSuccess;
-  const dim3 grid(n_experts * 16), block(BF_THREADS);
   switch (log2n) {
-    case 12:
-      if (trans) hipLaunchKernelGGL((lowfac_kernel<8, true>), grid, block, 0, s, ang, out);
-      else hipLaunchKernelGGL((lowfac_kernel<8, false>), grid, block, 0, s, ang, out);
-      break;
-    case 13:
-      if (trans) hipLaunchKernelGGL((lowfac_kernel<9, true>), grid, block, 0, s, ang, out);
-      else hipLaunchKernelGGL((lowfac_kernel<9, false>), grid, block, 0, s, ang, out);
-      break;
+    case 10: return launch_lowfac_S<6>(ang, out, n_experts, trans, s);
+    case 11: return launch_lowfac_S<7>(ang, out, n_experts, trans, s);
+    case 12: return launch_lowfac_S<8>(ang, out, n_experts, trans, s);
+    case 13: return launch_lowfac_S<9>(ang, out, n_experts, trans, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 enum SplitHigh { SH_IN = 0, SH_MID = 1, SH_OUT = 2 };
-
-// (cos, sin) of the four high stages of column v: cs[t * 8 + q] for stage S+t, local pair q.
-template <int S>
-__device__ __forceinline__ void sp_high_cs(const float* ang_e, int v, float2 cs[32]) {
-  constexpr int half = 1 << (S + 3);
-  float a[32];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int q = 0; q < 8; ++q) a[t * 8 + q] = ang_e[(S + t) * half + (q << S) + v];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) cs[i] = sincos_rev(a[i]);
-}
-
-// High part of every row:
-//   SH_IN   x[token of bucket row q] -> high^T(theta) -> out[q]
-//   SH_MID  in[q] -> high(phi_up) -> GELU (if set) -> high^T(theta_dn) -> out[q]
-//   SH_OUT  in[q] -> high(phi) -> * gate -> out[slot of q]
-template <int S, int MODE>
-__global__ __launch_bounds__(BF_THREADS) void bsplit_high_kernel(BflyArgs a) {
-  constexpr int L = S + 4;
-  constexpr int n = 1 << L, half = n / 2;
-  constexpr int ncb = (1 << S) / SP_VC;
-  const int tid = threadIdx.x;
-  const int t = blockIdx.x / ncb, cb = blockIdx.x % ncb;
-  int e, r0, nr;
-  sp_find_tile(a.offsets, a.n_experts, t, e, r0, nr);
-  if (e < 0) return;
-  const int v = cb * SP_VC + (tid & (SP_VC - 1)), rl = tid / SP_VC;
-  constexpr int RL = BF_THREADS / SP_VC;  // row lanes
-
-  float2 cs0[32], cs1[MODE == SH_MID ? 32 : 1];
-  sp_high_cs<S>(a.ang0 + size_t(e) * L * half, v, cs0);
-  if constexpr (MODE == SH_MID) sp_high_cs<S>(a.ang1 + size_t(e) * L * half, v, cs1);
-
-  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  for (int r = rl; r < nr; r += RL) {
-    const int q = r0 + r;
-    size_t src = size_t(q) * n, dst = size_t(q) * n;
-    float g = 1.0f;
-    if constexpr (MODE == SH_IN) src = size_t(a.perm[q] / a.top_k) * n;
-    if constexpr (MODE == SH_OUT) {
-      const int slot = a.perm[q];
-      dst = size_t(slot) * n;
-      g = a.gate[slot];
-    }
-    float x[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = __uint_as_float(uint32_t(in[src + (j << S) + v]) << 16);
-    if constexpr (MODE == SH_IN) {
-      rotate_group<4, true>(x, cs0);
-    } else {
-      rotate_group<4, false>(x, cs0);
-      if constexpr (MODE == SH_MID) {
-        if (a.gelu) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) x[j] = gelu_erf(x[j]);
-        }
-        rotate_group<4, true>(x, cs1);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] *= g;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const uint32_t w = pack_bf16x2(x[j], x[j + 1]);
-      out[dst + (j << S) + v] = uint16_t(w & 0xFFFFu);
-      out[dst + ((j + 1) << S) + v] = uint16_t(w >> 16);
-    }
-  }
-}
 
 // ---------------------------------------------------------------- matrix-core high part
 // The high part of column v is one 16 x 16 matrix H_v (stages S .. S+3 on the
@@ -745,37 +556,27 @@ static hipError_t sp_launch(K k, int grid, size_t lds, const BflyArgs& a, hipStr
 
 static int sp_tiles(const BflyArgs& a) { return (a.rows + SP_RB - 1) / SP_RB + a.n_experts; }
 
+// Both parts need their prepared block factors (built with the layer's
+// prepared data); a missing buffer is a caller error.
 template <int S>
 static hipError_t launch_low_S(const BflyArgs& a, bool trans, hipStream_t s) {
   static int done[2][64] = {{0}};
-  const int grid = sp_tiles(a) * 16;
-  if constexpr (S == 8 || S == 9) {
-    if (a.fac) {
-      static int mdone[2][64] = {{0}};
-      if (trans) return sp_launch(lowm_kernel<S, true>, grid, LowMCfg<S>::lds_bytes, a, s, mdone[1]);
-      return sp_launch(lowm_kernel<S, false>, grid, LowMCfg<S>::lds_bytes, a, s, mdone[0]);
-    }
-  }
-  if (trans) return sp_launch(bsplit_low_kernel<S, true>, grid, LowCfg<S>::lds_bytes, a, s, done[1]);
-  return sp_launch(bsplit_low_kernel<S, false>, grid, LowCfg<S>::lds_bytes, a, s, done[0]);
+  if (!a.fac) return hipErrorInvalidValue;
+  const int grid = sp_tiles(a) * (16 / LowMCfg<S>::SC);
+  if (trans) return sp_launch(lowm_kernel<S, true>, grid, LowMCfg<S>::lds_bytes, a, s, done[1]);
+  return sp_launch(lowm_kernel<S, false>, grid, LowMCfg<S>::lds_bytes, a, s, done[0]);
 }
 
 template <int S>
 static hipError_t launch_high_S(const BflyArgs& a, int mode, hipStream_t s) {
   static int done[64] = {0};
+  if (!a.fac || (mode == SH_MID && !a.fac1)) return hipErrorInvalidValue;
   const int grid = sp_tiles(a) * ((1 << S) / SP_VC);
-  if (a.fac && (mode != SH_MID || a.fac1)) {
-    const size_t lds = HighMCfg<S>::lds_bytes;
-    switch (mode) {
-      case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s, done);
-      case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s, done);
-      default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s, done);
-    }
-  }
+  const size_t lds = HighMCfg<S>::lds_bytes;
   switch (mode) {
-    case SH_IN: return sp_launch(bsplit_high_kernel<S, SH_IN>, grid, 0, a, s, done);
-    case SH_MID: return sp_launch(bsplit_high_kernel<S, SH_MID>, grid, 0, a, s, done);
-    default: return sp_launch(bsplit_high_kernel<S, SH_OUT>, grid, 0, a, s, done);
+    case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s, done);
+    case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s, done);
+    default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s, done);
   }
 }
 

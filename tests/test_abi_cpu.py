@@ -234,17 +234,22 @@ def test_prepared_bytes_layout():
     # (width / 16 columns), and at widths 4096 / 8192 the low-part block factors
     # (16 chunks x (16 blocks 16 x 16 + 16 blocks 16 x 16), or (16 blocks 32 x 32
     # + 32 blocks 16 x 16))
+    # low part: per chunk of w / 16 indices, G0 blocks (max(16, w / 256) wide) and
+    # w / 256 G1 blocks of 16 x 16, all bf16
     hi = lambda w: (w // 16) * 512
-    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 2 + 2 * 64 * hi(1024)
+    lo = lambda w: 16 * ((w // 16) * max(16, w // 256) * 2 + (w // 256) * 512)
+    rot = lambda w: hi(w) + lo(w)
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 2 + 2 * 64 * rot(1024)
     s = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (4096 * 1024 // 2) + 2 * 64 * hi(1024)
-                                                      + 2 * 64 * (16 * 16384 + hi(4096)))
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (4096 * 1024 // 2) + 2 * 64 * rot(1024)
+                                                      + 2 * 64 * rot(4096))
+    assert lo(4096) == 16 * 16384 and lo(8192) == 16 * (32768 + 16384)
     s = make_struct(d_model=2048, d_ff=8192, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (8192 * 2048 // 2) + 2 * 64 * hi(2048)
-                                                      + 2 * 64 * (16 * (32768 + 16384) + hi(8192)))
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (8192 * 2048 // 2) + 2 * 64 * rot(2048)
+                                                      + 2 * 64 * rot(8192))
     # d_ff = 128: the up product (128 outputs) keeps the 2-bit GEMM, the down one is fp4
     s = make_struct(d_model=1024, d_ff=128, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 2 + 2 * 64 * hi(1024)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 2 + 2 * 64 * rot(1024)
     s = make_struct(d_model=128, d_ff=64, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 0
     # fp32 activations and invalid layers use none
