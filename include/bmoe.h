@@ -125,14 +125,20 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int32_t rows, int32_t cols,
 bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* bytes);
 
 /* Size of the prepared-weights buffer of this layer, 0 when its forward path
- * uses none (or the layer is invalid).  Square bf16 layers of width 64..512
- * use one: the substrate re-encoded for the expert kernel (one byte per weight
- * at widths 64 and 128, one fp4 e2m1 nibble per weight at 256 and 512) and, at
- * widths 256 and 512, every expert's rotations as block-diagonal factors in
- * bf16 (stages below bit 5 at width 512 / bit 4 at width 256 as one block per
- * group of 32 / 16 consecutive indices, the stages above as 16 x 16 blocks).
- * These depend on the weights only (ButterflyMoE zh §2.1-§2.2: ternary
- * substrate, per-expert Givens angles). */
+ * uses none (or the layer is invalid).  Every bf16 layer except narrow FFNs
+ * uses one; fp32 layers use none.  Contents, all depending on the weights only
+ * (ButterflyMoE zh §2.1-§2.2: ternary substrate, per-expert Givens angles):
+ *  - square layers of width 64..512: the substrate re-encoded for the expert
+ *    kernel (one byte per weight at widths 64 and 128, one fp4 e2m1 nibble per
+ *    weight at 256 and 512) and, at widths 256 and 512, every expert's
+ *    rotations as block-diagonal factors in bf16 (stages below bit 5 at width
+ *    512 / bit 4 at width 256 as one block per group of 32 / 16 consecutive
+ *    indices, the stages above as 16 x 16 blocks);
+ *  - other layers: each substrate whose product has an output width that is a
+ *    multiple of 256 and a contraction that is a multiple of 128, as fp4; and
+ *    for every rotation of width n = 2^L in 1024..8192, per expert, its stages
+ *    0..L-5 as block factors per chunk of 2^(L-4) indices and its top four
+ *    stages as one 16 x 16 block per column (bf16). */
 size_t bmoe_prepared_bytes(const bmoe_layer* layer);
 
 /* Fill `prepared` (device, 256-byte aligned, at least bmoe_prepared_bytes) for
@@ -166,11 +172,11 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T,
  *   the workspace or the optional outputs);
  *   topk_idx / topk_gate: optional [T][top_k] outputs as in bmoe_route.
  * Intermediates between the steps are kept in act_dtype; GELU and
- * accumulation run in fp32.  Rotations run in fp32, except in square bf16
- * layers of width 256 and 512, whose rotations are products with the bf16
- * block factors described at bmoe_prepared_bytes (fp32 accumulation, bf16
- * rounding between the two factors).  Without layer->prepared the call
- * builds the prepared data in the workspace first. */
+ * accumulation run in fp32.  Rotations run in fp32, except where they are
+ * products with the bf16 block factors described at bmoe_prepared_bytes
+ * (square bf16 layers of width 256 and 512; bf16 rotations of width
+ * 1024..8192): fp32 accumulation, bf16 rounding between factors.  Without
+ * layer->prepared the call builds the prepared data in the workspace first. */
 bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void* y,
                          int32_t* topk_idx, float* topk_gate,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
