@@ -270,6 +270,9 @@ SMALL_CASES = [
     dict(d_model=2048, n_experts=3, top_k=1, tokens=50, act="bf16"),
     dict(d_model=256, d_ff=4096, n_experts=5, top_k=2, tokens=120, act="bf16"),
     dict(d_model=128, d_ff=8192, n_experts=3, top_k=2, tokens=40, act="bf16"),
+    # top-1: the output rotation's high part writes y directly; one token
+    dict(d_model=1024, d_ff=4096, n_experts=4, top_k=1, tokens=100, act="bf16"),
+    dict(d_model=2048, d_ff=1024, n_experts=8, top_k=2, tokens=1, act="bf16"),
 ]
 
 
@@ -288,6 +291,19 @@ def test_forward_identity_experts_and_skew():
     inp = wl.generate(cfg, angle_mode="zero", gate_mode="skewed")
     log("forward identity experts, skewed routing")
     _, _, (y, idx, gate) = run_layer(inp)
+    check_forward(inp, y, idx, gate)
+
+
+def test_forward_ffn_skewed_routing():
+    # skewed gates at FFN widths: some experts get no rows, others several
+    # 64-row tiles of the split butterflies
+    cfg = wl.small_config(d_model=1024, d_ff=4096, n_experts=16, top_k=2, tokens=600, act="bf16",
+                          seed_index=78)
+    inp = wl.generate(cfg, gate_mode="skewed")
+    log("forward FFN skewed routing")
+    _, _, (y, idx, gate) = run_layer(inp)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=16)
+    assert counts.max() > 64 and counts.min() < counts.mean() / 2
     check_forward(inp, y, idx, gate)
 
 
@@ -335,6 +351,7 @@ PREP_CASES = [
     dict(d_model=512, n_experts=64, top_k=2, tokens=700),   # matrix-core expert kernel
     dict(d_model=256, d_ff=1024, n_experts=6, top_k=2, tokens=300),   # fp4 substrates of both GEMMs
     dict(d_model=128, d_ff=4096, n_experts=4, top_k=2, tokens=150),   # + low-part block factors
+    dict(d_model=1024, n_experts=5, top_k=2, tokens=200),   # square width 1024: low and high factors
     dict(d_model=256, n_experts=9, top_k=3, tokens=333),
     dict(d_model=128, n_experts=5, top_k=2, tokens=200),    # fp32-rotation expert kernel
     dict(d_model=64, n_experts=3, top_k=1, tokens=65),
