@@ -359,23 +359,24 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     uint4 afr0[4][2], afr1[4][2];
     uint4 xr0[XPT], xr1[XPT];
 
+    // loads are unconditional (a branch around loads in the K loop makes every
+    // wait a full drain): experts past N read row N-1, tokens past T row T-1,
+    // chunk indices past the tile chunk XCH-1; none of these is used
     auto load_a = [&](int k0, uint4 (&dst)[4][2]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = 16 * (wave + 4 * i) + (lane & 15);
+        const int e = min(16 * (wave + 4 * i) + (lane & 15), N - 1);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          dst[i][s] = (e < N) ? *reinterpret_cast<const uint4*>(wg + size_t(e) * d + k0 + 32 * s + 8 * (lane >> 4))
-                              : make_uint4(0, 0, 0, 0);
+          dst[i][s] = *reinterpret_cast<const uint4*>(wg + size_t(e) * d + k0 + 32 * s + 8 * (lane >> 4));
       }
     };
     auto load_x = [&](int k0, uint4 (&dst)[XPT]) {
 #pragma unroll
       for (int r = 0; r < XPT; ++r) {
-        const int c = tid + RT_THREADS * r;
-        const int tok = t0 + (c >> 3);
-        dst[r] = (c < XCH && tok < a.T) ? *reinterpret_cast<const uint4*>(xg + size_t(tok) * d + k0 + 8 * (c & 7))
-                                        : make_uint4(0, 0, 0, 0);
+        const int c = min(tid + RT_THREADS * r, XCH - 1);
+        const int tok = min(t0 + (c >> 3), a.T - 1);
+        dst[r] = *reinterpret_cast<const uint4*>(xg + size_t(tok) * d + k0 + 8 * (c & 7));
       }
     };
     auto store_x = [&](int buf, const uint4 (&src)[XPT]) {
@@ -419,21 +420,18 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
         }
       }
       // the gate fragments and token chunks of step kt are consumed: fetch
-      // step kt+2 into their registers, then publish step kt+1 to LDS
-      if (kt + 2 < nk) {
-        load_a((kt + 2) * RT_BK, acur);
-        load_x((kt + 2) * RT_BK, xcur);
-      }
+      // step kt+2 into their registers (past the end: the last step again,
+      // unused), then publish step kt+1 to LDS
+      load_a(min(kt + 2, nk - 1) * RT_BK, acur);
+      load_x(min(kt + 2, nk - 1) * RT_BK, xcur);
       if (kt + 1 < nk) store_x(buf ^ 1, xnext);
       __syncthreads();
     };
 
     load_x(0, xr0);
     load_a(0, afr0);
-    if (nk > 1) {
-      load_x(RT_BK, xr1);
-      load_a(RT_BK, afr1);
-    }
+    load_x(min(1, nk - 1) * RT_BK, xr1);
+    load_a(min(1, nk - 1) * RT_BK, afr1);
     store_x(0, xr0);
     __syncthreads();
     for (int kt = 0; kt < nk; kt += 2) {
