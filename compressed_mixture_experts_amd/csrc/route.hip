@@ -213,37 +213,42 @@ __device__ __forceinline__ void route_recheck_store(const RouteArgs& a, RouteSh<
     int ci[RT_KMAX];
 #pragma unroll
     for (int j = 0; j < RT_KMAX; ++j) { cv[j] = -INFINITY; ci[j] = 0x7fffffff; }
+    // candidates (fp32 logit >= thr) in batches of four: the token's and the
+    // four gate rows' chunks are loaded together (lane owns elements 8 lane ..
+    // 8 lane + 7 of each 512-wide chunk), one fp64 sum per candidate
     for (int u = 0; u < 4; ++u) {
       const int e0 = lane + 64 * u;
-      const bool cand = e0 < N && Lrow[e0] >= thr;
-      uint64_t m = __ballot(cand);
+      uint64_t m = __ballot(e0 < N && Lrow[e0] >= thr);
       while (m) {
-        const int bit = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const int e = 64 * u + bit;
-        // lane owns elements 8*lane .. 8*lane+7 of each 512-wide chunk; the
-        // chunks' loads are issued four at a time before they are used
-        double s = 0.0;
-        for (int i0 = 0; i0 < d; i0 += 4 * 512) {
-          float xv[4][8], wv[4][8];
+        int eb[4];
 #pragma unroll
-          for (int uu = 0; uu < 4; ++uu) {
-            const int i = i0 + 512 * uu + 8 * lane;
-            if (i < d) {
-              load8<ACT>(a.x, xo + i, xv[uu]);
-              load8<ACT>(a.w_gate, size_t(e) * d + i, wv[uu]);
-            }
-          }
-#pragma unroll
-          for (int uu = 0; uu < 4; ++uu) {
-            if (i0 + 512 * uu + 8 * lane < d) {
-#pragma unroll
-              for (int j = 0; j < 8; ++j) s = fma((double)xv[uu][j], (double)wv[uu][j], s);
-            }
+        for (int c = 0; c < 4; ++c) {
+          if (m) {
+            eb[c] = 64 * u + __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+          } else {
+            eb[c] = -1;
           }
         }
-        s = wave_sum(s);
-        topk_insert<RT_KMAX>(cv, ci, s, e);
+        double s4[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int i0 = 0; i0 < d; i0 += 512) {
+          const int i = i0 + 8 * lane;
+          if (i < d) {
+            float xv[8], wv[4][8];
+            load8<ACT>(a.x, xo + i, xv);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) load8<ACT>(a.w_gate, size_t(eb[c] < 0 ? eb[0] : eb[c]) * d + i, wv[c]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) s4[c] = fma((double)xv[j], (double)wv[c][j], s4[c]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const double s = wave_sum(s4[c]);
+          if (eb[c] >= 0) topk_insert<RT_KMAX>(cv, ci, s, eb[c]);
+        }
       }
     }
     if (lane == 0) {
