@@ -74,8 +74,12 @@ def kernel_work(cfg):
     Ld = int(math.log2(d))
     ang_d = N * Ld * (d // 2) * 4
     w = {}
-    w["route"] = (T * d * s + N * d * s + 8 * R, 2 * T * d * N, "hbm")
-    w["bucket"] = (4 * R + 4 * R + 4 * (N + 1), 0, "hbm")
+    # the router also leaves each token tile's slots ordered by expert (R
+    # indices) and the first position of every expert in each tile's list
+    bt = 64 if T >= 64 * 256 else 32 if T >= 32 * 256 else 16
+    G = (T + bt - 1) // bt
+    w["route"] = (T * d * s + N * d * s + 8 * R + 4 * R + 4 * G * N, 2 * T * d * N, "hbm")
+    w["bucket"] = (4 * R + 4 * G * N + 4 * R + 4 * (N + 1), 0, "hbm")
 
     def split(L):
         # bf16 rows of width 1024 .. 8192: butterflies as low / high parts

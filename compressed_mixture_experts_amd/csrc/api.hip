@@ -120,9 +120,10 @@ bmoe_status check_prepared(const bmoe_layer* L, size_t need) {
 
 // Workspace layout (offsets in bytes, each 256-byte aligned).
 struct Plan {
-  size_t offsets, perm, idx, gate, bufU, bufZ, prep, total;
+  size_t offsets, perm, idx, gate, tslots, tstart, bufU, bufZ, prep, total;
   bool fused, mfma;
   int64_t R;
+  int32_t tiles;            // router token tiles
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -263,6 +264,9 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.perm = take(size_t(R) * 4);
   p.idx = take(size_t(R) * 4);
   p.gate = take(size_t(R) * 4);
+  p.tiles = T > 0 ? int32_t((int64_t(T) + route_tile_tokens(T) - 1) / route_tile_tokens(T)) : 0;
+  p.tslots = take(size_t(R) * 4);
+  p.tstart = take(size_t(p.tiles) * L->n_experts * 4);
   p.fused = use_fused(L);
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
   p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
@@ -307,9 +311,11 @@ bmoe_status validate_call(const bmoe_layer* L, const void* x, int32_t T, void* w
 bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* idx, float* gate,
                       void* ws, const Plan& p, hipStream_t s) {
   const int act = L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
-  RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates};
+  RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates,
+               at<int32_t>(ws, p.tslots), at<int32_t>(ws, p.tstart)};
   BMOE_HIP(launch_route(ra, act, s));
-  BucketArgs ba{idx, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R), L->n_experts};
+  BucketArgs ba{ra.tile_slots, ra.tile_start, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R),
+                L->n_experts, route_tile_tokens(T) * L->top_k, p.tiles};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -563,9 +569,10 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
     return launch_gemm(GemmArgs{a_in, layer->w_base[m], z_out, layer->w_scale[m], R, n_out, k_in}, act, stream);
   };
   // router and bucketing
-  RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates};
+  RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates,
+               at<int32_t>(workspace, p.tslots), at<int32_t>(workspace, p.tstart)};
   BMOE_LAUNCH(launch_route(ra, act, stream));
-  BucketArgs ba{idx, offsets, perm, R, N};
+  BucketArgs ba{ra.tile_slots, ra.tile_start, offsets, perm, R, N, route_tile_tokens(T) * k, p.tiles};
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
     void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);

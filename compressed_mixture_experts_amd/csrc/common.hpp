@@ -93,13 +93,17 @@ struct RouteArgs {
   int32_t* topk_idx;        // [T][k]
   float* topk_gate;         // [T][k]
   int32_t T, d, N, k, renorm;
+  // per token tile b (route_tile_tokens(T) tokens, C = that times k slots):
+  int32_t* tile_slots;      // [R] slots b C .. b C + C - 1 ordered by expert, ascending within one
+  int32_t* tile_start;      // [G][N] position of expert e's first slot in tile b's list
 };
 
 struct BucketArgs {
-  const int32_t* topk_idx;  // [R] flat slots
+  const int32_t* tile_slots;  // RouteArgs::tile_slots
+  const int32_t* tile_start;  // RouteArgs::tile_start
   int32_t* offsets;         // [N+1]
   int32_t* perm;            // [R] bucket position -> flat slot
-  int32_t R, N;
+  int32_t R, N, C, G;       // slots, experts, slots per token tile, token tiles
 };
 
 // Weight preparation for the expert kernels (once per weight set,
@@ -194,6 +198,8 @@ struct CombineArgs {
   int32_t T, d, k;
 };
 
+// Tokens per router workgroup for T tokens (the bucketing reads its per-tile lists).
+int route_tile_tokens(int T);
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);

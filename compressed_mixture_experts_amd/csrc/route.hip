@@ -65,6 +65,10 @@ struct RouteSh {
   int Flag[BT];
   int NF;
   float Wmax[8];              // max_e |w_e|^2 seen by each wave (unused entries 0)
+  // the tile's slot sort (routed slots in groups of 64)
+  int Cnt[256];                                         // first list position of each expert
+  __attribute__((aligned(4))) uint8_t Cg[(BT * RT_KMAX + 63) / 64 * 256];  // per-group expert counts
+  uint8_t Sx[BT * RT_KMAX], Sr[BT * RT_KMAX];           // slot's expert, rank in its group
 };
 
 // Per-token decision, 16 lanes per token (four tokens per wave at a time):
@@ -204,6 +208,7 @@ __device__ __forceinline__ void route_recheck_store(const RouteArgs& a, RouteSh<
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N, d = a.d, k = a.k;
   const int nf = sh.NF;
+  for (int i = tid; i < int(sizeof(sh.Cg)) / 4; i += NT) reinterpret_cast<uint32_t*>(sh.Cg)[i] = 0;
   for (int f = wave; f < nf; f += NT / 64) {
     const int tl = sh.Flag[f];
     const float thr = sh.Thr[tl];
@@ -213,42 +218,48 @@ __device__ __forceinline__ void route_recheck_store(const RouteArgs& a, RouteSh<
     int ci[RT_KMAX];
 #pragma unroll
     for (int j = 0; j < RT_KMAX; ++j) { cv[j] = -INFINITY; ci[j] = 0x7fffffff; }
-    // candidates (fp32 logit >= thr) in batches of four: the token's and the
-    // four gate rows' chunks are loaded together (lane owns elements 8 lane ..
-    // 8 lane + 7 of each 512-wide chunk), one fp64 sum per candidate
+    // candidates (fp32 logit >= thr) in batches of four, in expert order over
+    // the whole row: the token's and the four gate rows' chunks are loaded
+    // together (lane owns elements 8 lane .. 8 lane + 7 of each 512-wide
+    // chunk), one fp64 sum per candidate
+    uint64_t m[4];
+#pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e0 = lane + 64 * u;
-      uint64_t m = __ballot(e0 < N && Lrow[e0] >= thr);
-      while (m) {
-        int eb[4];
+      m[u] = __ballot(e0 < N && Lrow[e0] >= thr);
+    }
+    int u = 0;
+    while (true) {
+      int eb[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (m) {
-            eb[c] = 64 * u + __ffsll((unsigned long long)m) - 1;
-            m &= m - 1;
-          } else {
-            eb[c] = -1;
-          }
+      for (int c = 0; c < 4; ++c) {
+        while (u < 4 && !m[u]) ++u;  // uniform
+        if (u < 4) {
+          eb[c] = 64 * u + __ffsll((unsigned long long)m[u]) - 1;
+          m[u] &= m[u] - 1;
+        } else {
+          eb[c] = -1;
         }
-        double s4[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int i0 = 0; i0 < d; i0 += 512) {
-          const int i = i0 + 8 * lane;
-          if (i < d) {
-            float xv[8], wv[4][8];
-            load8<ACT>(a.x, xo + i, xv);
+      }
+      if (eb[0] < 0) break;
+      double s4[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int i0 = 0; i0 < d; i0 += 512) {
+        const int i = i0 + 8 * lane;
+        if (i < d) {
+          float xv[8], wv[4][8];
+          load8<ACT>(a.x, xo + i, xv);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) load8<ACT>(a.w_gate, size_t(eb[c] < 0 ? eb[0] : eb[c]) * d + i, wv[c]);
+          for (int c = 0; c < 4; ++c) load8<ACT>(a.w_gate, size_t(eb[c] < 0 ? eb[0] : eb[c]) * d + i, wv[c]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+          for (int c = 0; c < 4; ++c)
 #pragma unroll
-              for (int j = 0; j < 8; ++j) s4[c] = fma((double)xv[j], (double)wv[c][j], s4[c]);
-          }
+            for (int j = 0; j < 8; ++j) s4[c] = fma((double)xv[j], (double)wv[c][j], s4[c]);
         }
+      }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const double s = wave_sum(s4[c]);
-          if (eb[c] >= 0) topk_insert<RT_KMAX>(cv, ci, s, eb[c]);
-        }
+      for (int c = 0; c < 4; ++c) {
+        const double s = wave_sum(s4[c]);
+        if (eb[c] >= 0) topk_insert<RT_KMAX>(cv, ci, s, eb[c]);
       }
     }
     if (lane == 0) {
@@ -270,13 +281,76 @@ __device__ __forceinline__ void route_recheck_store(const RouteArgs& a, RouteSh<
   }
   __syncthreads();
 
-  for (int p = tid; p < BT * k; p += NT) {
-    const int tl = p / k, j = p - tl * k;
-    const int tok = t0 + tl;
-    if (tok < a.T) {
-      a.topk_idx[size_t(tok) * k + j] = sh.Idx[tl][j];
-      a.topk_gate[size_t(tok) * k + j] = sh.Gate[tl][j];
+  // outputs, and the tile's routed slots ordered by expert (a stable counting
+  // sort; the bucketing kernel concatenates the tiles' lists per expert).
+  // Slots go in groups of 64 (one per wave and round): a slot's rank among
+  // the group's slots of its expert comes from eight ballots over the expert
+  // bits, the groups' per-expert counts from LDS.  The global stores all come
+  // after the last barrier, which would wait for them.
+  const int ns = min(BT, a.T - t0) * k;
+  const int ng = (ns + 63) >> 6;
+  const size_t s0 = size_t(t0) * k;
+  for (int p0 = 0; p0 < ns; p0 += NT) {
+    const int p = p0 + tid;
+    const bool act = p < ns;
+    int e = 0;
+    if (act) {
+      const int tl = p / k, j = p - tl * k;
+      e = sh.Idx[tl][j];
     }
+    uint64_t peers = __ballot(act);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    if (act) {
+      const int r = __popcll(peers & ((1ull << lane) - 1ull));
+      sh.Sx[p] = uint8_t(e);
+      sh.Sr[p] = uint8_t(r);
+      if (r == 0) sh.Cg[(p >> 6) * 256 + e] = uint8_t(__popcll(peers));
+    }
+  }
+  __syncthreads();
+  // first list positions: wave 0, lane l owns experts 4l .. 4l + 3 (N <= 256)
+  int st[4] = {0, 0, 0, 0};
+  if (wave == 0) {
+    int c[4] = {0, 0, 0, 0};
+    for (int g = 0; g < ng; ++g) {
+      const uint32_t q = *reinterpret_cast<const uint32_t*>(&sh.Cg[g * 256 + 4 * lane]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] += (q >> (8 * i)) & 0xFF;
+    }
+    const int own = c[0] + c[1] + c[2] + c[3];
+    int x = own;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    int pre = x - own;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st[i] = pre;
+      sh.Cnt[4 * lane + i] = pre;
+      pre += c[i];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * lane + i < N) a.tile_start[size_t(blockIdx.x) * N + 4 * lane + i] = st[i];
+  }
+  for (int p = tid; p < ns; p += NT) {
+    const int tl = p / k, j = p - tl * k;
+    const int e = sh.Sx[p];
+    int r = sh.Cnt[e] + sh.Sr[p];
+    for (int g = 0; g < (p >> 6); ++g) r += sh.Cg[g * 256 + e];
+    a.topk_idx[s0 + p] = e;
+    a.topk_gate[s0 + p] = sh.Gate[tl][j];
+    a.tile_slots[s0 + r] = int32_t(s0) + p;
   }
 }
 
@@ -806,100 +880,107 @@ static hipError_t launch_route_bt(const RouteArgs& a, int act, hipStream_t s) {
   return route_launch(route_kernel<ACT_F32, BT>, opted_f, grid, RT_THREADS, lds, s, a);
 }
 
+// the largest token tile (64, 32 or 16 tokens) that still gives every CU a
+// workgroup: each workgroup reads the whole gate matrix once
+int route_tile_tokens(int T) { return T >= 64 * 256 ? 64 : T >= 32 * 256 ? 32 : 16; }
+
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  // the largest token tile (64, 32 or 16 tokens) that still gives every CU a
-  // workgroup: each workgroup reads the whole gate matrix once
-  if (a.T >= 64 * 256) return launch_route_bt<64>(a, act, s);
-  if (a.T >= 32 * 256) return launch_route_bt<32>(a, act, s);
-  return launch_route_bt<16>(a, act, s);
+  if (!a.tile_slots || !a.tile_start || a.N > 256) return hipErrorInvalidValue;
+  switch (route_tile_tokens(a.T)) {
+    case 64: return launch_route_bt<64>(a, act, s);
+    case 32: return launch_route_bt<32>(a, act, s);
+    default: return launch_route_bt<16>(a, act, s);
+  }
 }
 
 // ------------------------------------------------------------------ bucketing
-// One workgroup per expert e.  Pass 1 counts the routed slots of experts below
-// e (its first bucket position); pass 2 walks all slots in order and appends
-// the ones routed to e, so within an expert slots ascend.
-constexpr int BK_THREADS = 1024;
+// One workgroup per expert e.  Its first bucket position is the number of
+// slots routed to lower experts, the sum over token tiles of the position of
+// e in the tile's list.  Its slots are the tiles' runs of e, concatenated in
+// tile order (so slots ascend within the expert): tiles are taken BK_THREADS
+// at a time, their run lengths scanned, and the runs copied by all threads.
+constexpr int BK_THREADS = 256;
+constexpr int BK_UNROLL = 4;   // copies in flight per thread
+static_assert(BK_THREADS == 256, "the run search takes 8 halvings");
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   __shared__ int s_w[BK_THREADS / 64];
-  __shared__ int s_off;
-  const int e = blockIdx.x;
+  __shared__ int s_pre[BK_THREADS + 1];  // run starts of the round's tiles in its output
+  __shared__ int s_src[BK_THREADS];      // run starts in the tile lists
+  const int e = blockIdx.x, N = a.N, G = a.G, C = a.C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  auto load4 = [&](int f0) -> int4 {
-    if (f0 + 3 < a.R) return *reinterpret_cast<const int4*>(a.topk_idx + f0);
-    int4 q;
-    q.x = (f0 + 0 < a.R) ? a.topk_idx[f0 + 0] : 0x7fffffff;
-    q.y = (f0 + 1 < a.R) ? a.topk_idx[f0 + 1] : 0x7fffffff;
-    q.z = (f0 + 2 < a.R) ? a.topk_idx[f0 + 2] : 0x7fffffff;
-    q.w = (f0 + 3 < a.R) ? a.topk_idx[f0 + 3] : 0x7fffffff;
-    return q;
-  };
-
-  // The routed slots are read in blocks of BK_BATCH int4 per thread, all
-  // loads of a block issued before any is used.
-  constexpr int BK_BATCH = 8;
-  const int span = 4 * BK_THREADS * BK_BATCH;
-  int lt = 0;
-  for (int b0 = 0; b0 < a.R; b0 += span) {
-    int4 q[BK_BATCH];
-#pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) q[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
-#pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) lt += (q[b].x < e) + (q[b].y < e) + (q[b].z < e) + (q[b].w < e);
-  }
-  lt = wave_sum(lt);
-  if (lane == 0) s_w[wave] = lt;
+  int below = 0;
+  for (int b = tid; b < G; b += BK_THREADS) below += a.tile_start[size_t(b) * N + e];
+  below = wave_sum(below);
+  if (lane == 0) s_w[wave] = below;
   __syncthreads();
+  below = 0;
+#pragma unroll
+  for (int w = 0; w < BK_THREADS / 64; ++w) below += s_w[w];
   if (tid == 0) {
-    int o = 0;
-    for (int w = 0; w < BK_THREADS / 64; ++w) o += s_w[w];
-    s_off = o;
-    a.offsets[e] = o;
-    if (e == a.N - 1) a.offsets[a.N] = a.R;
+    a.offsets[e] = below;
+    if (e == N - 1) a.offsets[N] = a.R;
   }
-  __syncthreads();
-  const int off = s_off;
-  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int running = 0;
-  for (int b0 = 0; b0 < a.R; b0 += span) {
-    int4 qb[BK_BATCH];
-#pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) qb[b] = load4(b0 + 4 * (b * BK_THREADS + tid));
-#pragma unroll
-    for (int b = 0; b < BK_BATCH; ++b) {
-      const int f0 = b0 + 4 * (b * BK_THREADS + tid);
-      if (b0 + 4 * b * BK_THREADS >= a.R) break;  // uniform
-      const int v[4] = {qb[b].x, qb[b].y, qb[b].z, qb[b].w};
-      int c = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c += (v[j] == e);
-      const uint64_t m0 = __ballot(c & 1), m1 = __ballot(c & 2), m2 = __ballot(c & 4);
-      const int lpre = __popcll(m0 & ltmask) + 2 * __popcll(m1 & ltmask) + 4 * __popcll(m2 & ltmask);
-      const int wtot = __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2);
-      __syncthreads();
-      if (lane == 0) s_w[wave] = wtot;
-      __syncthreads();
-      int wpre = 0, tot = 0;
-      for (int w = 0; w < BK_THREADS / 64; ++w) {
-        const int x = s_w[w];
-        wpre += (w < wave) ? x : 0;
-        tot += x;
-      }
-      if (c) {
-        int qq = off + running + wpre + lpre;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (v[j] == e) a.perm[qq++] = f0 + j;
-      }
-      running += tot;
+
+  int base = below;
+  for (int b0 = 0; b0 < G; b0 += BK_THREADS) {
+    const int b = b0 + tid;
+    int st = 0, h = 0;
+    if (b < G) {
+      st = a.tile_start[size_t(b) * N + e];
+      const int en = e + 1 < N ? a.tile_start[size_t(b) * N + e + 1] : min(C, a.R - b * C);
+      h = en - st;
     }
+    int x = h;  // inclusive scan of the run lengths over the round's tiles
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    __syncthreads();  // s_w, s_pre, s_src of the previous round are dead
+    if (lane == 63) s_w[wave] = x;
+    __syncthreads();
+    int pre = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < BK_THREADS / 64; ++w) {
+      pre += w < wave ? s_w[w] : 0;
+      total += s_w[w];
+    }
+    s_pre[tid + 1] = pre + x;
+    if (tid == 0) s_pre[0] = 0;
+    s_src[tid] = b * C + st;
+    __syncthreads();
+    // output position f of the round: the tile i with s_pre[i] <= f < s_pre[i + 1]
+    for (int f0 = 0; f0 < total; f0 += BK_THREADS * BK_UNROLL) {
+      int v[BK_UNROLL];
+#pragma unroll
+      for (int u = 0; u < BK_UNROLL; ++u) {
+        const int f = f0 + u * BK_THREADS + tid;
+        if (f < total) {
+          int lo = 0, hi = BK_THREADS;
+#pragma unroll
+          for (int it = 0; it < 8; ++it) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pre[mid] <= f) lo = mid; else hi = mid;
+          }
+          v[u] = a.tile_slots[s_src[lo] + f - s_pre[lo]];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < BK_UNROLL; ++u) {
+        const int f = f0 + u * BK_THREADS + tid;
+        if (f < total) a.perm[base + f] = v[u];
+      }
+    }
+    base += total;
   }
 }
 
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
+  if (a.G != (a.R / max(a.C, 1) + (a.R % max(a.C, 1) != 0)) || a.N > 256) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bucket_kernel, dim3(a.N), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }
