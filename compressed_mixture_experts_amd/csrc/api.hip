@@ -120,10 +120,11 @@ bmoe_status check_prepared(const bmoe_layer* L, size_t need) {
 
 // Workspace layout (offsets in bytes, each 256-byte aligned).
 struct Plan {
-  size_t offsets, perm, idx, gate, tslots, tstart, bufU, bufZ, prep, total;
+  size_t offsets, perm, idx, gate, tslots, tgates, tstart, rec, bufU, bufZ, prep, total;
   bool fused, mfma;
   int64_t R;
   int32_t tiles;            // router token tiles
+  int32_t n_rec;            // tile records of the square-expert matrix-core kernel (0: none)
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -266,11 +267,14 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.gate = take(size_t(R) * 4);
   p.tiles = T > 0 ? int32_t((int64_t(T) + route_tile_tokens(T) - 1) / route_tile_tokens(T)) : 0;
   p.tslots = take(size_t(R) * 4);
+  p.tgates = take(size_t(R) * 4);
   p.tstart = take(size_t(p.tiles) * L->n_experts * 4);
   p.fused = use_fused(L);
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
   p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
   p.mfma = use_fused_mfma(L);
+  p.n_rec = p.mfma && R > 0 ? int32_t((R + TILE_ROWS - 1) / TILE_ROWS + L->n_experts) : 0;
+  p.rec = take(size_t(p.n_rec) * sizeof(TileRec));
   p.prep = L->prepared ? 0 : take(prep_layout(L).total);  // prepared data built per call
   p.total = o;
   p.R = R;
@@ -312,10 +316,10 @@ bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* id
                       void* ws, const Plan& p, hipStream_t s) {
   const int act = L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
   RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates,
-               at<int32_t>(ws, p.tslots), at<int32_t>(ws, p.tstart)};
+               at<int32_t>(ws, p.tslots), at<float>(ws, p.tgates), at<int32_t>(ws, p.tstart)};
   BMOE_HIP(launch_route(ra, act, s));
-  BucketArgs ba{ra.tile_slots, ra.tile_start, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), int32_t(p.R),
-                L->n_experts, route_tile_tokens(T) * L->top_k, p.tiles};
+  BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm),
+                nullptr, int32_t(p.R), L->n_experts, route_tile_tokens(T) * L->top_k, p.tiles, 0};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -570,14 +574,16 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   };
   // router and bucketing
   RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates,
-               at<int32_t>(workspace, p.tslots), at<int32_t>(workspace, p.tstart)};
+               at<int32_t>(workspace, p.tslots), at<float>(workspace, p.tgates), at<int32_t>(workspace, p.tstart)};
   BMOE_LAUNCH(launch_route(ra, act, stream));
-  BucketArgs ba{ra.tile_slots, ra.tile_start, offsets, perm, R, N, route_tile_tokens(T) * k, p.tiles};
+  TileRec* rec = p.n_rec ? at<TileRec>(workspace, p.rec) : nullptr;
+  BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, offsets, perm, rec, R, N,
+                route_tile_tokens(T) * k, p.tiles, p.n_rec};
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
     void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);
     FusedArgs fa{x, yslot_f, layer->theta[0], layer->phi[0], wbytes, fac, offsets, perm, gate,
-                 layer->w_scale[0], R, N, k};
+                 layer->w_scale[0], R, N, k, rec};
     if (p.mfma) {
       BMOE_LAUNCH(launch_fused_mfma(fa, ilog2(d), stream));
     } else {

@@ -95,15 +95,32 @@ struct RouteArgs {
   int32_t T, d, N, k, renorm;
   // per token tile b (route_tile_tokens(T) tokens, C = that times k slots):
   int32_t* tile_slots;      // [R] slots b C .. b C + C - 1 ordered by expert, ascending within one
+  float* tile_gates;        // [R] their gates, same order
   int32_t* tile_start;      // [G][N] position of expert e's first slot in tile b's list
+};
+
+// Work record of one tile of the square-expert kernel: TILE_ROWS consecutive
+// bucket rows of one expert (e = -1: no tile), with the rows' flat slots and
+// gates.  Expert e's tiles are records floor(off_e / TILE_ROWS) + e + j, j <
+// ceil(cnt_e / TILE_ROWS) (off_e = slots of lower experts); the at most one
+// record between two experts' ranges, and past the last, is empty.  That is
+// ceil(R / TILE_ROWS) + N records.
+constexpr int TILE_ROWS = 32;
+struct TileRec {
+  int32_t e, nr, pad0, pad1;
+  int32_t slot[TILE_ROWS];
+  float gate[TILE_ROWS];
 };
 
 struct BucketArgs {
   const int32_t* tile_slots;  // RouteArgs::tile_slots
+  const float* tile_gates;    // RouteArgs::tile_gates
   const int32_t* tile_start;  // RouteArgs::tile_start
   int32_t* offsets;         // [N+1]
   int32_t* perm;            // [R] bucket position -> flat slot
+  TileRec* rec;             // [n_rec] tile records, or null
   int32_t R, N, C, G;       // slots, experts, slots per token tile, token tiles
+  int32_t n_rec;            // ceil(R / TILE_ROWS) + N when rec is set
 };
 
 // Weight preparation for the expert kernels (once per weight set,
@@ -137,6 +154,7 @@ struct FusedArgs {
   const float* gate;        // [R]
   float alpha;              // substrate scale
   int32_t rows, n_experts, top_k;
+  const TileRec* rec;       // tile records (matrix-core kernel)
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):

@@ -12,13 +12,15 @@
 // then needs 16 + P small dense products per rotation, done on MFMA in bf16
 // with fp32 accumulation, instead of (n/2) L scalar rotations per row.
 //
-// The blocks come from the bucketing kernel (mfma_factors.hpp), in the exact
+// The blocks are built once per weight set (mfma_factors.hpp), in the exact
 // per-lane order of the MFMA operands (bf16): the transposed blocks of theta
 // (input rotation B(theta)^T = G_A^T G_B^T) and the blocks of phi (output
 // rotation G_B G_A).
 //
 // fused_mfma_kernel, one workgroup (4 waves) per tile of 32 bucketed rows of one
-// expert.  Two bf16 LDS buffers of 32 rows alternate:
+// expert, read from the tile record the bucketing kernel wrote (expert, rows,
+// their slots and gates: one load round trip).  Two bf16 LDS buffers of 32
+// rows alternate:
 //   gather   x rows -> buf0 as [row][p][m]                 (transposed per row)
 //   G_B^T    wave (tb, h): token block tb, classes p of half h   -> buf1 [row][m][p]
 //   G_A^T    wave (tb, h): blocks m of half h                    -> buf0 [row][i]  (= U)
@@ -63,23 +65,6 @@ __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
 template <int KA> struct AFragT { using type = uint2; };
 template <> struct AFragT<8> { using type = uint4; };
 
-// exclusive scan over the 256 threads; `total` gets the sum
-__device__ __forceinline__ int fm_block_scan(int v, int* s_tmp, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s_tmp[w] = x;
-  __syncthreads();
-  int pre = 0;
-  for (int i = 0; i < w; ++i) pre += s_tmp[i];
-  total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
-  return pre + x - v;
-}
-
 template <int L>
 __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) {
   using C = MfCfg<L>;
@@ -93,43 +78,24 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* buf0 = lds;
   unsigned char* buf1 = lds + C::buf_bytes;
-  __shared__ int s_info[3];
-  __shared__ int s_tmp[4];
   __shared__ size_t s_src[FM_RT], s_dst[FM_RT];
   __shared__ float s_gate[FM_RT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int tb = wave >> 1, hh = wave & 1;
 
-  // ---- tile of one expert
-  if (tid == 0) s_info[0] = -1;
-  {
-    int nt = 0, cnt = 0, off = 0;
-    if (tid < a.n_experts) {
-      off = a.offsets[tid];
-      cnt = a.offsets[tid + 1] - off;
-      nt = (cnt + FM_RT - 1) / FM_RT;
-    }
-    int total;
-    const int excl = fm_block_scan(nt, s_tmp, total);
-    // tiles of one expert are consecutive: keep them on one XCD
-    const int t = int(blockIdx.x) < total ? xcd_remap(blockIdx.x, total) : -1;
-    if (tid < a.n_experts && t >= excl && t < excl + nt) {
-      const int j = t - excl;
-      s_info[0] = tid;
-      s_info[1] = off + j * FM_RT;
-      s_info[2] = min(FM_RT, cnt - j * FM_RT);
-    }
-  }
-  __syncthreads();
-  const int e = s_info[0];
+  // ---- this workgroup's tile record (one expert's consecutive records stay
+  // on one XCD); the row entries are read with the header, before its test
+  const TileRec* rec = a.rec + xcd_remap(blockIdx.x, gridDim.x);
+  const int32_t rslot = rec->slot[tid & (FM_RT - 1)];
+  const float rgate = rec->gate[tid & (FM_RT - 1)];
+  const int e = rec->e;
   if (e < 0) return;
-  const int r0 = s_info[1], nr = s_info[2];
+  const int nr = rec->nr;
   if (tid < nr) {
-    const int slot = a.perm[r0 + tid];
-    s_src[tid] = size_t(slot / a.top_k) * n;
-    s_dst[tid] = size_t(slot) * n;
-    s_gate[tid] = a.gate[slot] * a.alpha;
+    s_src[tid] = size_t(rslot / a.top_k) * n;
+    s_dst[tid] = size_t(rslot) * n;
+    s_gate[tid] = rgate * a.alpha;
   }
 
   // ---- input-rotation factor fragments of this expert
@@ -273,21 +239,24 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
       }
     }
   };
-  unit(W0, 0);
-  if constexpr (NU == 2) unit(W1, 1);
-  // output-rotation factors
+  // output-rotation factors, loaded once the first unit's substrate registers
+  // are free so that the second unit's products cover their latency
   AF fa[NBW][HA];
-#pragma unroll
-  for (int jm = 0; jm < NBW; ++jm)
-#pragma unroll
-    for (int hq = 0; hq < HA; ++hq)
-      fa[jm][hq] = *reinterpret_cast<const AF*>(
-          fe + C::off_ap + ((size_t(NBW * wave + jm) * HA + hq) * 64 + lane) * sizeof(AF));
-
   uint2 fb[NCW];  // last factor, used after the next barrier
+  auto load_out_factors = [&]() {
 #pragma unroll
-  for (int c = 0; c < NCW; ++c)
-    fb[c] = *reinterpret_cast<const uint2*>(fe + C::off_bp + (size_t(hh * NCW + c) * 64 + lane) * 8);
+    for (int jm = 0; jm < NBW; ++jm)
+#pragma unroll
+      for (int hq = 0; hq < HA; ++hq)
+        fa[jm][hq] = *reinterpret_cast<const AF*>(
+            fe + C::off_ap + ((size_t(NBW * wave + jm) * HA + hq) * 64 + lane) * sizeof(AF));
+#pragma unroll
+    for (int c = 0; c < NCW; ++c)
+      fb[c] = *reinterpret_cast<const uint2*>(fe + C::off_bp + (size_t(hh * NCW + c) * 64 + lane) * 8);
+  };
+  unit(W0, 0);
+  load_out_factors();
+  if constexpr (NU == 2) unit(W1, 1);
 
   // ---- G_A (phi) on the accumulators: blocks NBW*wave .. +3  -> buf1 [row][p][m]
   // (buf1 was last read before the barrier above; buf0 still holds U for the
@@ -357,6 +326,7 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
 template <int L>
 static hipError_t launch_fused_mfma_L(const FusedArgs& a, hipStream_t s) {
   using C = MfCfg<L>;
+  static_assert(FM_RT == TILE_ROWS, "tile records");
   const int grid = (a.rows + FM_RT - 1) / FM_RT + a.n_experts;
   auto k = fused_mfma_kernel<L>;
   static int attr_done[64] = {0};
@@ -378,6 +348,7 @@ size_t factor_bytes_per_expert(int log2n) { return mf_factor_bytes(log2n); }
 
 hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
+  if (!a.rec) return hipErrorInvalidValue;
   switch (log2n) {
     case 8: return launch_fused_mfma_L<8>(a, s);
     case 9: return launch_fused_mfma_L<9>(a, s);

@@ -348,9 +348,11 @@ __device__ __forceinline__ void route_recheck_store(const RouteArgs& a, RouteSh<
     const int e = sh.Sx[p];
     int r = sh.Cnt[e] + sh.Sr[p];
     for (int g = 0; g < (p >> 6); ++g) r += sh.Cg[g * 256 + e];
+    const float gv = sh.Gate[tl][j];
     a.topk_idx[s0 + p] = e;
-    a.topk_gate[s0 + p] = sh.Gate[tl][j];
+    a.topk_gate[s0 + p] = gv;
     a.tile_slots[s0 + r] = int32_t(s0) + p;
+    a.tile_gates[s0 + r] = gv;
   }
 }
 
@@ -886,7 +888,7 @@ int route_tile_tokens(int T) { return T >= 64 * 256 ? 64 : T >= 32 * 256 ? 32 : 
 
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  if (!a.tile_slots || !a.tile_start || a.N > 256) return hipErrorInvalidValue;
+  if (!a.tile_slots || !a.tile_gates || !a.tile_start || a.N > 256) return hipErrorInvalidValue;
   switch (route_tile_tokens(a.T)) {
     case 64: return launch_route_bt<64>(a, act, s);
     case 32: return launch_route_bt<32>(a, act, s);
@@ -900,31 +902,55 @@ hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
 // e in the tile's list.  Its slots are the tiles' runs of e, concatenated in
 // tile order (so slots ascend within the expert): tiles are taken BK_THREADS
 // at a time, their run lengths scanned, and the runs copied by all threads.
+// With `rec` set it also writes the expert's tile records.
 constexpr int BK_THREADS = 256;
 constexpr int BK_UNROLL = 4;   // copies in flight per thread
 static_assert(BK_THREADS == 256, "the run search takes 8 halvings");
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
-  __shared__ int s_w[BK_THREADS / 64];
+  __shared__ int s_w[2][BK_THREADS / 64];
   __shared__ int s_pre[BK_THREADS + 1];  // run starts of the round's tiles in its output
   __shared__ int s_src[BK_THREADS];      // run starts in the tile lists
   const int e = blockIdx.x, N = a.N, G = a.G, C = a.C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  int below = 0;
-  for (int b = tid; b < G; b += BK_THREADS) below += a.tile_start[size_t(b) * N + e];
+  // slots of lower experts and of e
+  int below = 0, cnt = 0;
+  for (int b = tid; b < G; b += BK_THREADS) {
+    const int st = a.tile_start[size_t(b) * N + e];
+    const int en = e + 1 < N ? a.tile_start[size_t(b) * N + e + 1] : min(C, a.R - b * C);
+    below += st;
+    cnt += en - st;
+  }
   below = wave_sum(below);
-  if (lane == 0) s_w[wave] = below;
+  cnt = wave_sum(cnt);
+  if (lane == 0) {
+    s_w[0][wave] = below;
+    s_w[1][wave] = cnt;
+  }
   __syncthreads();
-  below = 0;
+  below = cnt = 0;
 #pragma unroll
-  for (int w = 0; w < BK_THREADS / 64; ++w) below += s_w[w];
+  for (int w = 0; w < BK_THREADS / 64; ++w) {
+    below += s_w[0][w];
+    cnt += s_w[1][w];
+  }
   if (tid == 0) {
     a.offsets[e] = below;
     if (e == N - 1) a.offsets[N] = a.R;
   }
+  const int rbase = below / TILE_ROWS + e;  // first tile record of e
+  if (a.rec) {
+    const int nt = (cnt + TILE_ROWS - 1) / TILE_ROWS;
+    const int next = e + 1 < N ? (below + cnt) / TILE_ROWS + e + 1 : a.n_rec;
+    for (int j = tid; j < next - rbase; j += BK_THREADS) {
+      TileRec* r = a.rec + rbase + j;
+      r->e = j < nt ? e : -1;
+      r->nr = j < nt ? min(TILE_ROWS, cnt - TILE_ROWS * j) : 0;
+    }
+  }
 
-  int base = below;
+  int base = 0;  // position in e's list
   for (int b0 = 0; b0 < G; b0 += BK_THREADS) {
     const int b = b0 + tid;
     int st = 0, h = 0;
@@ -940,13 +966,13 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
       if (lane >= o) x += y;
     }
     __syncthreads();  // s_w, s_pre, s_src of the previous round are dead
-    if (lane == 63) s_w[wave] = x;
+    if (lane == 63) s_w[0][wave] = x;
     __syncthreads();
     int pre = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < BK_THREADS / 64; ++w) {
-      pre += w < wave ? s_w[w] : 0;
-      total += s_w[w];
+      pre += w < wave ? s_w[0][w] : 0;
+      total += s_w[0][w];
     }
     s_pre[tid + 1] = pre + x;
     if (tid == 0) s_pre[0] = 0;
@@ -955,6 +981,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
     // output position f of the round: the tile i with s_pre[i] <= f < s_pre[i + 1]
     for (int f0 = 0; f0 < total; f0 += BK_THREADS * BK_UNROLL) {
       int v[BK_UNROLL];
+      float g[BK_UNROLL];
 #pragma unroll
       for (int u = 0; u < BK_UNROLL; ++u) {
         const int f = f0 + u * BK_THREADS + tid;
@@ -965,13 +992,23 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
             const int mid = (lo + hi) >> 1;
             if (s_pre[mid] <= f) lo = mid; else hi = mid;
           }
-          v[u] = a.tile_slots[s_src[lo] + f - s_pre[lo]];
+          const int src = s_src[lo] + f - s_pre[lo];
+          v[u] = a.tile_slots[src];
+          if (a.rec) g[u] = a.tile_gates[src];
         }
       }
 #pragma unroll
       for (int u = 0; u < BK_UNROLL; ++u) {
         const int f = f0 + u * BK_THREADS + tid;
-        if (f < total) a.perm[base + f] = v[u];
+        if (f < total) {
+          const int q = base + f;
+          a.perm[below + q] = v[u];
+          if (a.rec) {
+            TileRec* r = a.rec + rbase + q / TILE_ROWS;
+            r->slot[q % TILE_ROWS] = v[u];
+            r->gate[q % TILE_ROWS] = g[u];
+          }
+        }
       }
     }
     base += total;
@@ -981,6 +1018,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
   if (a.G != (a.R / max(a.C, 1) + (a.R % max(a.C, 1) != 0)) || a.N > 256) return hipErrorInvalidValue;
+  if (a.rec && (!a.tile_gates || a.n_rec != (a.R + TILE_ROWS - 1) / TILE_ROWS + a.N)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bucket_kernel, dim3(a.N), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }
