@@ -273,7 +273,9 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.bufU = take(size_t(R) * d * s);                  // U, then Z_down (FFN) or per-slot Y (square)
   p.bufZ = take(p.fused ? 0 : size_t(R) * (f > d ? f : d) * s);  // Z / H / A, then per-slot Y (FFN)
   p.mfma = use_fused_mfma(L);
-  p.n_rec = p.mfma && R > 0 ? int32_t((R + TILE_ROWS - 1) / TILE_ROWS + L->n_experts) : 0;
+  // tile records at the smaller tile height (the most records); the call
+  // picks the height when it runs
+  p.n_rec = p.mfma && R > 0 ? int32_t((R + 31) / 32 + L->n_experts) : 0;
   p.rec = take(size_t(p.n_rec) * sizeof(TileRec));
   p.prep = L->prepared ? 0 : take(prep_layout(L).total);  // prepared data built per call
   p.total = o;
@@ -319,7 +321,7 @@ bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* id
                at<int32_t>(ws, p.tslots), at<float>(ws, p.tgates), at<int32_t>(ws, p.tstart)};
   BMOE_HIP(launch_route(ra, act, s));
   BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm),
-                nullptr, int32_t(p.R), L->n_experts, route_tile_tokens(T) * L->top_k, p.tiles, 0};
+                nullptr, int32_t(p.R), L->n_experts, route_tile_tokens(T) * L->top_k, p.tiles, 0, 0};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -577,13 +579,15 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
                at<int32_t>(workspace, p.tslots), at<float>(workspace, p.tgates), at<int32_t>(workspace, p.tstart)};
   BMOE_LAUNCH(launch_route(ra, act, stream));
   TileRec* rec = p.n_rec ? at<TileRec>(workspace, p.rec) : nullptr;
+  const int rec_rows = rec ? fused_tile_rows(R, N) : 0;
   BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, offsets, perm, rec, R, N,
-                route_tile_tokens(T) * k, p.tiles, p.n_rec};
+                route_tile_tokens(T) * k, p.tiles, rec_rows,
+                rec ? int32_t((R + rec_rows - 1) / rec_rows + N) : 0};
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
     void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);
     FusedArgs fa{x, yslot_f, layer->theta[0], layer->phi[0], wbytes, fac, offsets, perm, gate,
-                 layer->w_scale[0], R, N, k, rec};
+                 layer->w_scale[0], R, N, k, rec, rec_rows};
     if (p.mfma) {
       BMOE_LAUNCH(launch_fused_mfma(fa, ilog2(d), stream));
     } else {

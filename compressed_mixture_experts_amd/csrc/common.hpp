@@ -99,17 +99,17 @@ struct RouteArgs {
   int32_t* tile_start;      // [G][N] position of expert e's first slot in tile b's list
 };
 
-// Work record of one tile of the square-expert kernel: TILE_ROWS consecutive
-// bucket rows of one expert (e = -1: no tile), with the rows' flat slots and
-// gates.  Expert e's tiles are records floor(off_e / TILE_ROWS) + e + j, j <
-// ceil(cnt_e / TILE_ROWS) (off_e = slots of lower experts); the at most one
-// record between two experts' ranges, and past the last, is empty.  That is
-// ceil(R / TILE_ROWS) + N records.
-constexpr int TILE_ROWS = 32;
+// Work record of one tile of the square-expert kernel: up to `rows` (32 or
+// TILE_ROWS_MAX) consecutive bucket rows of one expert (e = -1: no tile), with
+// the rows' flat slots and gates.  Expert e's tiles are records
+// floor(off_e / rows) + e + j, j < ceil(cnt_e / rows) (off_e = slots of lower
+// experts); the at most one record between two experts' ranges, and past the
+// last, is empty.  That is ceil(R / rows) + N records.
+constexpr int TILE_ROWS_MAX = 64;
 struct TileRec {
   int32_t e, nr, pad0, pad1;
-  int32_t slot[TILE_ROWS];
-  float gate[TILE_ROWS];
+  int32_t slot[TILE_ROWS_MAX];
+  float gate[TILE_ROWS_MAX];
 };
 
 struct BucketArgs {
@@ -120,7 +120,8 @@ struct BucketArgs {
   int32_t* perm;            // [R] bucket position -> flat slot
   TileRec* rec;             // [n_rec] tile records, or null
   int32_t R, N, C, G;       // slots, experts, slots per token tile, token tiles
-  int32_t n_rec;            // ceil(R / TILE_ROWS) + N when rec is set
+  int32_t rec_rows;         // rows per tile record (32 or 64)
+  int32_t n_rec;            // ceil(R / rec_rows) + N when rec is set
 };
 
 // Weight preparation for the expert kernels (once per weight set,
@@ -155,6 +156,7 @@ struct FusedArgs {
   float alpha;              // substrate scale
   int32_t rows, n_experts, top_k;
   const TileRec* rec;       // tile records (matrix-core kernel)
+  int32_t tile_rows;        // their rows per tile (fused_tile_rows)
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
@@ -241,6 +243,10 @@ hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 bool fused_square_supported(int log2n);
 bool fused_mfma_supported(int log2n);
 size_t factor_bytes_per_expert(int log2n);
+// Rows per tile of the matrix-core square-expert kernel for `rows` routed rows
+// over n_experts experts on the current device (64 while the 32-row tiles
+// would not fill two per CU, else 32).
+int fused_tile_rows(int rows, int n_experts);
 hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s);
 hipError_t launch_fused_square(const FusedArgs& a, int log2n, hipStream_t s);
 

@@ -8,7 +8,7 @@
 // m < 16.  Stages 0 .. LA-1 only mix indices of equal m, stages LA .. L-1 only
 // indices of equal p, so
 //     B = G_B G_A,   G_A = diag over m of A_m (P x P),   G_B = diag over p of B_p (16 x 16),
-// each block the product of its stages' Givens rotations.  A tile of 32 rows
+// each block the product of its stages' Givens rotations.  A tile of 64 rows
 // then needs 16 + P small dense products per rotation, done on MFMA in bf16
 // with fp32 accumulation, instead of (n/2) L scalar rotations per row.
 //
@@ -17,23 +17,27 @@
 // (input rotation B(theta)^T = G_A^T G_B^T) and the blocks of phi (output
 // rotation G_B G_A).
 //
-// fused_mfma_kernel, one workgroup (4 waves) per tile of 32 bucketed rows of one
-// expert, read from the tile record the bucketing kernel wrote (expert, rows,
-// their slots and gates: one load round trip).  Two bf16 LDS buffers of 32
-// rows alternate:
+// fused_mfma_kernel<L, RT>, one workgroup (RT / 8 waves) per tile of RT = 32
+// or 64 bucketed rows of one expert, read from the tile record the bucketing
+// kernel wrote (expert, rows, their slots and gates: one load round trip).
+// Two bf16 LDS buffers of RT rows alternate (wave = 2 tb + h, token block tb
+// of 16 rows; NW waves):
 //   gather   x rows -> buf0 as [row][p][m]                 (transposed per row)
 //   G_B^T    wave (tb, h): token block tb, classes p of half h   -> buf1 [row][m][p]
 //   G_A^T    wave (tb, h): blocks m of half h                    -> buf0 [row][i]  (= U)
-//   W        wave w: outputs [w n/4, (w+1) n/4) of all rows, accumulators kept
+//   W        wave w: outputs [w n/NW, (w+1) n/NW) of all rows, accumulators kept
 //   G_A      on the accumulators of the wave's own blocks        -> buf1 [row][p][m]
 //   G_B      wave (tb, h): classes p of half h, * gate * alpha   -> buf0 [row][i]
 //   store    buf0 rows -> per-slot rows
-// LDS is 2 x 32 rows (~66 KiB), so two workgroups share a CU.
+// LDS is 2 x RT rows: two 32-row workgroups, or one 64-row workgroup, per CU.
+// A CU's loads are bounded by its misses in flight and a tile reads ~224 KiB
+// of substrate and factors at width 512, so while there are too few tiles to
+// give every CU two, 64-row tiles (half the tiles, same bytes each) finish
+// sooner; with more tiles, two 32-row workgroups per CU overlap each other's
+// waits.  Both give every row the same arithmetic in the same order.
 #include "mfma_factors.hpp"
 
 namespace bmoe {
-
-constexpr int FM_THREADS = 256;  // four waves
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -65,21 +69,25 @@ __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
 template <int KA> struct AFragT { using type = uint2; };
 template <> struct AFragT<8> { using type = uint4; };
 
-template <int L>
-__global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) {
+template <int L, int RT>
+__global__ __launch_bounds__(RT * 8, RT == 32 ? 2 : 1) void fused_mfma_kernel(FusedArgs a) {
   using C = MfCfg<L>;
   using AF = typename AFragT<C::KA>::type;
   constexpr int n = C::n, PA = C::PA, NP = C::NP, HA = C::HA, TS = C::TS;
-  constexpr int OB = n / 64;          // substrate: 16-output blocks per wave
+  constexpr int NT = RT * 8;          // threads
+  constexpr int NW = NT / 64;         // waves
+  constexpr int MB = RT / 16;         // 16-row token blocks
+  constexpr int OB = n / (16 * NW);   // substrate: 16-output blocks per wave
   constexpr int NU = n / 256;         // substrate: units of 256 contraction indices
   constexpr int NCW = NP / 2;         // G_B classes per wave
-  constexpr int NBW = (n / 4) / PA;   // G_A blocks inside one wave's substrate outputs
-  static_assert(NBW == 4 && NCW % 4 == 0 && (NU == 1 || NU == 2), "tile shape");
+  constexpr int NBW = (n / NW) / PA;  // G_A blocks inside one wave's substrate outputs
+  static_assert((RT == 32 || RT == 64) && RT <= TILE_ROWS_MAX && NW == 2 * MB, "tile rows");
+  static_assert((NBW == 2 || NBW == 4) && NCW % 4 == 0 && (NU == 1 || NU == 2), "tile shape");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* buf0 = lds;
-  unsigned char* buf1 = lds + C::buf_bytes;
-  __shared__ size_t s_src[FM_RT], s_dst[FM_RT];
-  __shared__ float s_gate[FM_RT];
+  unsigned char* buf1 = lds + size_t(RT) * TS;
+  __shared__ size_t s_src[RT], s_dst[RT];
+  __shared__ float s_gate[RT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int tb = wave >> 1, hh = wave & 1;
@@ -87,8 +95,8 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   // ---- this workgroup's tile record (one expert's consecutive records stay
   // on one XCD); the row entries are read with the header, before its test
   const TileRec* rec = a.rec + xcd_remap(blockIdx.x, gridDim.x);
-  const int32_t rslot = rec->slot[tid & (FM_RT - 1)];
-  const float rgate = rec->gate[tid & (FM_RT - 1)];
+  const int32_t rslot = rec->slot[tid & (RT - 1)];
+  const float rgate = rec->gate[tid & (RT - 1)];
   const int e = rec->e;
   if (e < 0) return;
   const int nr = rec->nr;
@@ -108,19 +116,19 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
 
   // ---- gather x rows into buf0 as [row][p][m]: item (row, m-quad, 8 p's)
   constexpr int PG = PA / 8;
-  constexpr int ITEMS = FM_RT * 4 * PG;
-  constexpr int IPT = ITEMS / FM_THREADS;
-  static_assert(ITEMS % FM_THREADS == 0, "gather items");
+  constexpr int ITEMS = RT * 4 * PG;
+  constexpr int IPT = ITEMS / NT;
+  static_assert(ITEMS % NT == 0, "gather items");
   // substrate rows: n/2 bytes of fp4.  Unit v covers contraction indices
   // [256v, 256v+256) = bytes [128v, 128v+128) of a row; lane group g takes
   // bytes 16g..16g+15 of each 64-byte half (two loads that fill one line).
-  const unsigned char* wrow = a.wb + size_t(wave * (n / 4) + l16) * (n / 2) + 16 * g;
+  const unsigned char* wrow = a.wb + size_t(wave * (n / NW) + l16) * (n / 2) + 16 * g;
   uint4 W0[OB][2];
   {
     uint4 ch[IPT][4];
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int item = it * FM_THREADS + tid;
+      const int item = it * NT + tid;
       const int pg = item % PG, mq = (item / PG) % 4, t = item / (PG * 4);
       if (t < nr) {
         const uint16_t* src = reinterpret_cast<const uint16_t*>(a.x) + s_src[t] + 8 * pg;
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
         W0[i][hf] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * (n / 2) + 64 * hf);
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int item = it * FM_THREADS + tid;
+      const int item = it * NT + tid;
       const int pg = item % PG, mq = (item / PG) % 4, t = item / (PG * 4);
       if (t < nr) {
         unsigned char* dst = buf0 + t * TS + ((8 * pg) * 16 + 4 * mq) * 2;
@@ -216,26 +224,28 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   }
   __syncthreads();
 
-  // ---- Z = U W^T: wave owns outputs [wave n/4, (wave+1) n/4) of all 32 rows.
+  // ---- Z = U W^T: wave owns outputs [wave n/NW, (wave+1) n/NW) of all RT rows.
   // In unit v, MFMA step s (8 contraction indices) of lane group g uses dword
   // s % 4 of half s / 4: indices 256v + 128(s/4) + 32g + 8(s%4) .. +7; the U
   // operand is read in the same order.
-  f32x4_t acc[OB][2];
+  f32x4_t acc[OB][MB];
 #pragma unroll
-  for (int i = 0; i < OB; ++i) acc[i][0] = acc[i][1] = zero4;
+  for (int i = 0; i < OB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = zero4;
   const uint16_t* urow = reinterpret_cast<const uint16_t*>(buf0) + l16 * (TS / 2) + 32 * g;
   auto unit = [&](const uint4 (&Wu)[OB][2], int v) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const int kk = 256 * v + 128 * (st >> 2) + 8 * (st & 3);
-      uint4 uf[2];
+      uint4 uf[MB];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) uf[j] = *reinterpret_cast<const uint4*>(urow + 16 * j * (TS / 2) + kk);
+      for (int j = 0; j < MB; ++j) uf[j] = *reinterpret_cast<const uint4*>(urow + 16 * j * (TS / 2) + kk);
 #pragma unroll
       for (int i = 0; i < OB; ++i) {
         const uint4 wv = fp4x8_to_bf16(u4get(Wu[i][st >> 2], st & 3));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wv, uf[j], acc[i][j]);
+        for (int j = 0; j < MB; ++j) acc[i][j] = mfma32(wv, uf[j], acc[i][j]);
       }
     }
   };
@@ -258,11 +268,11 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   load_out_factors();
   if constexpr (NU == 2) unit(W1, 1);
 
-  // ---- G_A (phi) on the accumulators: blocks NBW*wave .. +3  -> buf1 [row][p][m]
+  // ---- G_A (phi) on the accumulators: blocks NBW*wave .. +NBW-1  -> buf1 [row][p][m]
   // (buf1 was last read before the barrier above; buf0 still holds U for the
   // other waves, so it is not touched here)
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < MB; ++rb) {
     f32x4_t d[NBW][HA];
 #pragma unroll
     for (int jm = 0; jm < NBW; ++jm) {
@@ -284,8 +294,11 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int p = 16 * hq + 4 * g + i;
-        *reinterpret_cast<uint2*>(yr + (p * 16 + NBW * wave) * 2) =
-            make_uint2(pack_bf16x2(d[0][hq][i], d[1][hq][i]), pack_bf16x2(d[2][hq][i], d[3][hq][i]));
+        if constexpr (NBW == 4)
+          *reinterpret_cast<uint2*>(yr + (p * 16 + NBW * wave) * 2) =
+              make_uint2(pack_bf16x2(d[0][hq][i], d[1][hq][i]), pack_bf16x2(d[2][hq][i], d[3][hq][i]));
+        else
+          *reinterpret_cast<uint32_t*>(yr + (p * 16 + NBW * wave) * 2) = pack_bf16x2(d[0][hq][i], d[1][hq][i]);
       }
   }
   __syncthreads();
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   // ---- per-slot rows
   constexpr int CPR = n / 8;
 #pragma unroll
-  for (int c = tid; c < FM_RT * CPR; c += FM_THREADS) {
+  for (int c = tid; c < RT * CPR; c += NT) {
     const int r = c / CPR;
     if (r < nr)
       *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + s_dst[r] + 8 * (c % CPR)) =
@@ -323,23 +336,34 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fused_mfma_kernel(FusedArgs a) 
   }
 }
 
-template <int L>
+template <int L, int RT>
 static hipError_t launch_fused_mfma_L(const FusedArgs& a, hipStream_t s) {
-  using C = MfCfg<L>;
-  static_assert(FM_RT == TILE_ROWS, "tile records");
-  const int grid = (a.rows + FM_RT - 1) / FM_RT + a.n_experts;
-  auto k = fused_mfma_kernel<L>;
+  const size_t lds = size_t(2) * RT * MfCfg<L>::TS;
+  const int grid = (a.rows + RT - 1) / RT + a.n_experts;
+  auto k = fused_mfma_kernel<L, RT>;
   static int attr_done[64] = {0};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  if (C::lds_bytes > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(C::lds_bytes));
+  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
+    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (err != hipSuccess) return err;
     if (dev >= 0 && dev < 64) attr_done[dev] = 1;
   }
-  hipLaunchKernelGGL(k, dim3(grid), dim3(FM_THREADS), C::lds_bytes, s, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(RT * 8), lds, s, a);
   return hipGetLastError();
+}
+
+int fused_tile_rows(int rows, int n_experts) {
+  static int cus[64] = {0};
+  int dev = 0, cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus[dev] = 0;
+    if (cus[dev] > 0) cu = cus[dev];
+  }
+  const long tiles32 = (long(rows) + 31) / 32 + n_experts;
+  return tiles32 <= 2L * cu ? 64 : 32;
 }
 
 bool fused_mfma_supported(int log2n) { return log2n == 8 || log2n == 9; }
@@ -349,9 +373,11 @@ size_t factor_bytes_per_expert(int log2n) { return mf_factor_bytes(log2n); }
 hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (!a.rec) return hipErrorInvalidValue;
+  const bool r64 = a.tile_rows == 64;
+  if (!r64 && a.tile_rows != 32) return hipErrorInvalidValue;
   switch (log2n) {
-    case 8: return launch_fused_mfma_L<8>(a, s);
-    case 9: return launch_fused_mfma_L<9>(a, s);
+    case 8: return r64 ? launch_fused_mfma_L<8, 64>(a, s) : launch_fused_mfma_L<8, 32>(a, s);
+    case 9: return r64 ? launch_fused_mfma_L<9, 64>(a, s) : launch_fused_mfma_L<9, 32>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -15,7 +15,6 @@
 
 namespace bmoe {
 
-constexpr int FM_RT = 32;        // rows per tile of the expert kernel
 
 template <int L>
 struct MfCfg {
@@ -27,8 +26,6 @@ struct MfCfg {
   static constexpr int HA = PA / 16;           // 16-row halves of a G_A block
   static constexpr int KA = PA / 4;            // contraction values per lane in a G_A MFMA
   static constexpr int TS = 2 * n + 16;        // LDS row stride in bytes
-  static constexpr size_t buf_bytes = size_t(FM_RT) * TS;
-  static constexpr size_t lds_bytes = 2 * buf_bytes;
   static constexpr size_t gb_bytes = size_t(NP) * 64 * 4 * 2;        // one G_B set
   static constexpr size_t ga_bytes = size_t(NM) * HA * 64 * KA * 2;  // one G_A set
   // per expert: [G_B^T(theta) | G_A^T(theta) | G_A(phi) | G_B(phi)]

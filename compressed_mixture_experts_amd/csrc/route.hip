@@ -939,14 +939,15 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
     a.offsets[e] = below;
     if (e == N - 1) a.offsets[N] = a.R;
   }
-  const int rbase = below / TILE_ROWS + e;  // first tile record of e
+  const int rrows = a.rec_rows;
+  const int rbase = a.rec ? below / rrows + e : 0;  // first tile record of e
   if (a.rec) {
-    const int nt = (cnt + TILE_ROWS - 1) / TILE_ROWS;
-    const int next = e + 1 < N ? (below + cnt) / TILE_ROWS + e + 1 : a.n_rec;
+    const int nt = (cnt + rrows - 1) / rrows;
+    const int next = e + 1 < N ? (below + cnt) / rrows + e + 1 : a.n_rec;
     for (int j = tid; j < next - rbase; j += BK_THREADS) {
       TileRec* r = a.rec + rbase + j;
       r->e = j < nt ? e : -1;
-      r->nr = j < nt ? min(TILE_ROWS, cnt - TILE_ROWS * j) : 0;
+      r->nr = j < nt ? min(rrows, cnt - rrows * j) : 0;
     }
   }
 
@@ -1004,9 +1005,9 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
           const int q = base + f;
           a.perm[below + q] = v[u];
           if (a.rec) {
-            TileRec* r = a.rec + rbase + q / TILE_ROWS;
-            r->slot[q % TILE_ROWS] = v[u];
-            r->gate[q % TILE_ROWS] = g[u];
+            TileRec* r = a.rec + rbase + q / rrows;
+            r->slot[q % rrows] = v[u];
+            r->gate[q % rrows] = g[u];
           }
         }
       }
@@ -1018,7 +1019,9 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
   if (a.G != (a.R / max(a.C, 1) + (a.R % max(a.C, 1) != 0)) || a.N > 256) return hipErrorInvalidValue;
-  if (a.rec && (!a.tile_gates || a.n_rec != (a.R + TILE_ROWS - 1) / TILE_ROWS + a.N)) return hipErrorInvalidValue;
+  if (a.rec && (!a.tile_gates || (a.rec_rows != 32 && a.rec_rows != TILE_ROWS_MAX) ||
+                a.n_rec != (a.R + a.rec_rows - 1) / a.rec_rows + a.N))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(bucket_kernel, dim3(a.N), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }

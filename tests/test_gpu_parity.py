@@ -332,6 +332,25 @@ def test_forward_deterministic_and_empty():
     assert y0.shape == (0, cfg.d_model)
 
 
+def test_forward_tile_heights_agree():
+    # width-512 square layers run 64-row expert tiles while the 32-row tiles
+    # would not fill two per CU, else 32-row tiles; every row gets the same
+    # arithmetic either way.  4096 tokens take 64-row tiles, the same tokens
+    # repeated four times 32-row tiles: the first 4096 outputs must agree bit
+    # for bit (routing is per token, so it is the same).
+    import torch
+    cfg = wl.CONFIGS[1]
+    inp = wl.generate(cfg)
+    layer = bm.Layer.from_inputs(inp)
+    x = to_dev(inp.x, cfg.act)
+    log("forward tile heights 64 vs 32")
+    y1 = layer.forward(x)
+    y4 = layer.forward(torch.cat([x, x, x, x]).contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y4[: x.shape[0]])
+    assert torch.equal(y4[: x.shape[0]], y4[3 * x.shape[0]:])
+
+
 def test_route_matches_forward_routing():
     import torch
     cfg = wl.CONFIGS[2]
