@@ -99,8 +99,8 @@ struct RouteArgs {
   int32_t* tile_start;      // [G][N] position of expert e's first slot in tile b's list
 };
 
-// Work record of one tile of the square-expert kernel: up to `rows` (32 or
-// TILE_ROWS_MAX) consecutive bucket rows of one expert (e = -1: no tile), with
+// Work record of one tile of the square-expert kernel: up to `rows` (32, 48
+// or TILE_ROWS_MAX) consecutive bucket rows of one expert (e = -1: no tile), with
 // the rows' flat slots and gates.  Expert e's tiles are records
 // floor(off_e / rows) + e + j, j < ceil(cnt_e / rows) (off_e = slots of lower
 // experts); the at most one record between two experts' ranges, and past the
@@ -120,7 +120,7 @@ struct BucketArgs {
   int32_t* perm;            // [R] bucket position -> flat slot
   TileRec* rec;             // [n_rec] tile records, or null
   int32_t R, N, C, G;       // slots, experts, slots per token tile, token tiles
-  int32_t rec_rows;         // rows per tile record (32 or 64)
+  int32_t rec_rows;         // rows per tile record (32, 48 or 64)
   int32_t n_rec;            // ceil(R / rec_rows) + N when rec is set
 };
 
@@ -244,8 +244,8 @@ bool fused_square_supported(int log2n);
 bool fused_mfma_supported(int log2n);
 size_t factor_bytes_per_expert(int log2n);
 // Rows per tile of the matrix-core square-expert kernel for `rows` routed rows
-// over n_experts experts on the current device (64 while the 32-row tiles
-// would not fill two per CU, else 32).
+// over n_experts experts on the current device: 32 when the 32-row tiles would
+// fill two per CU, else 48 when the 48-row tiles fit one per CU, else 64.
 int fused_tile_rows(int rows, int n_experts);
 hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s);
 hipError_t launch_fused_square(const FusedArgs& a, int log2n, hipStream_t s);

@@ -17,11 +17,12 @@
 // (input rotation B(theta)^T = G_A^T G_B^T) and the blocks of phi (output
 // rotation G_B G_A).
 //
-// fused_mfma_kernel<L, RT>, one workgroup (RT / 8 waves) per tile of RT = 32
-// or 64 bucketed rows of one expert, read from the tile record the bucketing
-// kernel wrote (expert, rows, their slots and gates: one load round trip).
-// Two bf16 LDS buffers of RT rows alternate (wave = 2 tb + h, token block tb
-// of 16 rows; NW waves):
+// fused_mfma_kernel<L, RT>, one workgroup per tile of RT = 32, 48 or 64
+// bucketed rows of one expert (4 waves at 32 rows, else 8), read from the tile
+// record the bucketing kernel wrote (expert, rows, their slots and gates: one
+// load round trip).  Two bf16 LDS buffers of RT rows alternate (wave = 2 tb +
+// h, token block tb of 16 rows; NW waves; at 48 rows waves 6 and 7 sit out the
+// rotations):
 //   gather   x rows -> buf0 as [row][p][m]                 (transposed per row)
 //   G_B^T    wave (tb, h): token block tb, classes p of half h   -> buf1 [row][m][p]
 //   G_A^T    wave (tb, h): blocks m of half h                    -> buf0 [row][i]  (= U)
@@ -29,12 +30,13 @@
 //   G_A      on the accumulators of the wave's own blocks        -> buf1 [row][p][m]
 //   G_B      wave (tb, h): classes p of half h, * gate * alpha   -> buf0 [row][i]
 //   store    buf0 rows -> per-slot rows
-// LDS is 2 x RT rows: two 32-row workgroups, or one 64-row workgroup, per CU.
-// A CU's loads are bounded by its misses in flight and a tile reads ~224 KiB
-// of substrate and factors at width 512, so while there are too few tiles to
-// give every CU two, 64-row tiles (half the tiles, same bytes each) finish
-// sooner; with more tiles, two 32-row workgroups per CU overlap each other's
-// waits.  Both give every row the same arithmetic in the same order.
+// LDS is 2 x RT rows: two 32-row workgroups, or one taller one, per CU.  A
+// CU's loads are bounded by its misses in flight and a tile reads ~224 KiB of
+// substrate and factors at width 512, so while there are too few tiles to give
+// every CU two, the shortest tiles that still fit one per CU finish first
+// (fused_tile_rows); with more tiles, two 32-row workgroups per CU overlap
+// each other's waits.  Every height gives every row the same arithmetic in
+// the same order.
 #include "mfma_factors.hpp"
 
 namespace bmoe {
@@ -70,18 +72,18 @@ template <int KA> struct AFragT { using type = uint2; };
 template <> struct AFragT<8> { using type = uint4; };
 
 template <int L, int RT>
-__global__ __launch_bounds__(RT * 8, RT == 32 ? 2 : 1) void fused_mfma_kernel(FusedArgs a) {
+__global__ __launch_bounds__(RT == 32 ? 256 : 512, RT == 32 ? 2 : 1) void fused_mfma_kernel(FusedArgs a) {
   using C = MfCfg<L>;
   using AF = typename AFragT<C::KA>::type;
   constexpr int n = C::n, PA = C::PA, NP = C::NP, HA = C::HA, TS = C::TS;
-  constexpr int NT = RT * 8;          // threads
+  constexpr int NT = RT == 32 ? 256 : 512;  // threads
   constexpr int NW = NT / 64;         // waves
   constexpr int MB = RT / 16;         // 16-row token blocks
   constexpr int OB = n / (16 * NW);   // substrate: 16-output blocks per wave
   constexpr int NU = n / 256;         // substrate: units of 256 contraction indices
   constexpr int NCW = NP / 2;         // G_B classes per wave
   constexpr int NBW = (n / NW) / PA;  // G_A blocks inside one wave's substrate outputs
-  static_assert((RT == 32 || RT == 64) && RT <= TILE_ROWS_MAX && NW == 2 * MB, "tile rows");
+  static_assert((RT == 32 || RT == 48 || RT == 64) && RT <= TILE_ROWS_MAX && NW >= 2 * MB, "tile rows");
   static_assert((NBW == 2 || NBW == 4) && NCW % 4 == 0 && (NU == 1 || NU == 2), "tile shape");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* buf0 = lds;
@@ -91,12 +93,13 @@ __global__ __launch_bounds__(RT * 8, RT == 32 ? 2 : 1) void fused_mfma_kernel(Fu
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int tb = wave >> 1, hh = wave & 1;
+  const bool rot = tb < MB;  // wave takes part in the rotations
 
   // ---- this workgroup's tile record (one expert's consecutive records stay
   // on one XCD); the row entries are read with the header, before its test
   const TileRec* rec = a.rec + xcd_remap(blockIdx.x, gridDim.x);
-  const int32_t rslot = rec->slot[tid & (RT - 1)];
-  const float rgate = rec->gate[tid & (RT - 1)];
+  const int32_t rslot = rec->slot[tid < RT ? tid : 0];
+  const float rgate = rec->gate[tid < RT ? tid : 0];
   const int e = rec->e;
   if (e < 0) return;
   const int nr = rec->nr;
@@ -109,16 +112,17 @@ __global__ __launch_bounds__(RT * 8, RT == 32 ? 2 : 1) void fused_mfma_kernel(Fu
   // ---- input-rotation factor fragments of this expert
   const unsigned char* fe = a.fac + size_t(e) * C::per_expert;
   uint2 fbt[NCW];
+  if (rot) {
 #pragma unroll
-  for (int c = 0; c < NCW; ++c)
-    fbt[c] = *reinterpret_cast<const uint2*>(fe + C::off_bt + (size_t(hh * NCW + c) * 64 + lane) * 8);
+    for (int c = 0; c < NCW; ++c)
+      fbt[c] = *reinterpret_cast<const uint2*>(fe + C::off_bt + (size_t(hh * NCW + c) * 64 + lane) * 8);
+  }
   __syncthreads();
 
   // ---- gather x rows into buf0 as [row][p][m]: item (row, m-quad, 8 p's)
   constexpr int PG = PA / 8;
   constexpr int ITEMS = RT * 4 * PG;
-  constexpr int IPT = ITEMS / NT;
-  static_assert(ITEMS % NT == 0, "gather items");
+  constexpr int IPT = (ITEMS + NT - 1) / NT;  // items past ITEMS have rows t >= RT >= nr
   // substrate rows: n/2 bytes of fp4.  Unit v covers contraction indices
   // [256v, 256v+256) = bytes [128v, 128v+128) of a row; lane group g takes
   // bytes 16g..16g+15 of each 64-byte half (two loads that fill one line).
@@ -160,19 +164,21 @@ __global__ __launch_bounds__(RT * 8, RT == 32 ? 2 : 1) void fused_mfma_kernel(Fu
     }
   }
   AF fat[8][HA];  // second input-rotation factor, used after the next barrier
+  if (rot) {
 #pragma unroll
-  for (int jb = 0; jb < 8; ++jb)
+    for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-    for (int hq = 0; hq < HA; ++hq)
-      fat[jb][hq] = *reinterpret_cast<const AF*>(
-          fe + C::off_at + ((size_t(8 * hh + jb) * HA + hq) * 64 + lane) * sizeof(AF));
+      for (int hq = 0; hq < HA; ++hq)
+        fat[jb][hq] = *reinterpret_cast<const AF*>(
+            fe + C::off_at + ((size_t(8 * hh + jb) * HA + hq) * 64 + lane) * sizeof(AF));
+  }
   __syncthreads();
 
   const int trow = 16 * tb + l16;  // this lane's row in the butterfly phases
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // ---- G_B^T (theta): classes hh*NCW .. +NCW of token block tb  -> buf1 [row][m][p]
-  {
+  if (rot) {
     const unsigned char* xr = buf0 + trow * TS;
     unsigned char* yr = buf1 + trow * TS;
 #pragma unroll
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(RT * 8, RT == 32 ? 2 : 1) void fused_mfma_kernel(Fu
   __syncthreads();
 
   // ---- G_A^T (theta): blocks 8hh .. 8hh+7 of token block tb  -> buf0 [row][i] (U)
-  {
+  if (rot) {
     const unsigned char* yr = buf1 + trow * TS;
     unsigned char* ur = buf0 + trow * TS;
 #pragma unroll
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(RT * 8, RT == 32 ? 2 : 1) void fused_mfma_kernel(Fu
   __syncthreads();
 
   // ---- G_B (phi), * gate * alpha: classes hh*NCW .. of token block tb -> buf0 [row][i]
-  {
+  if (rot) {
     const unsigned char* yr = buf1 + trow * TS;
     unsigned char* orow = buf0 + trow * TS;
     const float gs = s_gate[trow];
@@ -350,7 +356,7 @@ static hipError_t launch_fused_mfma_L(const FusedArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
     if (dev >= 0 && dev < 64) attr_done[dev] = 1;
   }
-  hipLaunchKernelGGL(k, dim3(grid), dim3(RT * 8), lds, s, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(RT == 32 ? 256 : 512), lds, s, a);
   return hipGetLastError();
 }
 
@@ -362,8 +368,9 @@ int fused_tile_rows(int rows, int n_experts) {
       cus[dev] = 0;
     if (cus[dev] > 0) cu = cus[dev];
   }
-  const long tiles32 = (long(rows) + 31) / 32 + n_experts;
-  return tiles32 <= 2L * cu ? 64 : 32;
+  auto tiles = [&](int rt) { return (long(rows) + rt - 1) / rt + n_experts; };  // records, a bound on tiles
+  if (tiles(32) > 2L * cu) return 32;
+  return tiles(48) <= cu ? 48 : 64;
 }
 
 bool fused_mfma_supported(int log2n) { return log2n == 8 || log2n == 9; }
@@ -373,11 +380,13 @@ size_t factor_bytes_per_expert(int log2n) { return mf_factor_bytes(log2n); }
 hipError_t launch_fused_mfma(const FusedArgs& a, int log2n, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (!a.rec) return hipErrorInvalidValue;
-  const bool r64 = a.tile_rows == 64;
-  if (!r64 && a.tile_rows != 32) return hipErrorInvalidValue;
+  const int rt = a.tile_rows;
+  if (rt != 32 && rt != 48 && rt != 64) return hipErrorInvalidValue;
   switch (log2n) {
-    case 8: return r64 ? launch_fused_mfma_L<8, 64>(a, s) : launch_fused_mfma_L<8, 32>(a, s);
-    case 9: return r64 ? launch_fused_mfma_L<9, 64>(a, s) : launch_fused_mfma_L<9, 32>(a, s);
+    case 8: return rt == 64 ? launch_fused_mfma_L<8, 64>(a, s)
+                   : rt == 48 ? launch_fused_mfma_L<8, 48>(a, s) : launch_fused_mfma_L<8, 32>(a, s);
+    case 9: return rt == 64 ? launch_fused_mfma_L<9, 64>(a, s)
+                   : rt == 48 ? launch_fused_mfma_L<9, 48>(a, s) : launch_fused_mfma_L<9, 32>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

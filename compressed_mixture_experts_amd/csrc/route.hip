@@ -1019,7 +1019,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
   if (a.G != (a.R / max(a.C, 1) + (a.R % max(a.C, 1) != 0)) || a.N > 256) return hipErrorInvalidValue;
-  if (a.rec && (!a.tile_gates || (a.rec_rows != 32 && a.rec_rows != TILE_ROWS_MAX) ||
+  if (a.rec && (!a.tile_gates || (a.rec_rows != 32 && a.rec_rows != 48 && a.rec_rows != TILE_ROWS_MAX) ||
                 a.n_rec != (a.R + a.rec_rows - 1) / a.rec_rows + a.N))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(bucket_kernel, dim3(a.N), dim3(BK_THREADS), 0, s, a);

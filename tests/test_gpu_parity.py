@@ -333,22 +333,26 @@ def test_forward_deterministic_and_empty():
 
 
 def test_forward_tile_heights_agree():
-    # width-512 square layers run 64-row expert tiles while the 32-row tiles
-    # would not fill two per CU, else 32-row tiles; every row gets the same
-    # arithmetic either way.  4096 tokens take 64-row tiles, the same tokens
-    # repeated four times 32-row tiles: the first 4096 outputs must agree bit
-    # for bit (routing is per token, so it is the same).
+    # width-512 square layers run 32-row expert tiles when those would fill two
+    # per CU, else 48-row tiles when those fit one per CU, else 64-row tiles;
+    # every row gets the same arithmetic whatever the height.  On 256 CUs the
+    # 4096 tokens take 48-row tiles, 5000 tokens 64-row tiles and 16384 tokens
+    # 32-row tiles: the outputs of shared tokens must agree bit for bit
+    # (routing is per token, so it is the same).
     import torch
     cfg = wl.CONFIGS[1]
     inp = wl.generate(cfg)
     layer = bm.Layer.from_inputs(inp)
     x = to_dev(inp.x, cfg.act)
-    log("forward tile heights 64 vs 32")
+    n = x.shape[0]
+    log("forward tile heights 48 / 64 / 32")
     y1 = layer.forward(x)
+    y5 = layer.forward(torch.cat([x, x[:904]]).contiguous())
     y4 = layer.forward(torch.cat([x, x, x, x]).contiguous())
     torch.cuda.synchronize()
-    assert torch.equal(y1, y4[: x.shape[0]])
-    assert torch.equal(y4[: x.shape[0]], y4[3 * x.shape[0]:])
+    assert torch.equal(y1, y5[:n])
+    assert torch.equal(y1, y4[:n])
+    assert torch.equal(y4[:n], y4[3 * n:])
 
 
 def test_route_matches_forward_routing():
