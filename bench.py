@@ -237,6 +237,9 @@ def main() -> int:
                     help="re-encode the weights inside every forward instead of once")
     ap.add_argument("--eager", action="store_true",
                     help="time launch-by-launch forwards instead of captured-graph replays")
+    ap.add_argument("--skewed", action="store_true",
+                    help="skewed routing: gate row e scaled by 4/(e+1)^0.75, so a few experts take "
+                         "most of the rows and many get few or none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU (asked for --gpus {args.gpus}): the ButterflyMoE forward "
@@ -260,8 +263,9 @@ def main() -> int:
 
     ci = wl.BENCH_CONFIG_INDEX if args.config is None else args.config
     cfg = wl.CONFIGS[ci]
-    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
-    inp = wl.generate(cfg)
+    wname = cfg.name + ("_skewed" if args.skewed else "")
+    print(f"[bench] workload {wname}: generating inputs", file=sys.stderr, flush=True)
+    inp = wl.generate(cfg, gate_mode="skewed" if args.skewed else "normal")
     layer = bm.Layer.from_inputs(inp, device="cuda")
     # weight preparation (substrate re-encoding, rotation block factors): once per
     # weight set, outside the timed steps, unless --per-call-prep
@@ -278,6 +282,11 @@ def main() -> int:
     else:
         x = torch.from_numpy(inp.x).cuda()
     y = torch.empty_like(x)
+    # rows per expert of this batch's routing (load balance of the workload)
+    idx = layer.route(x)[0]
+    counts = torch.bincount(idx.reshape(-1).long(), minlength=cfg.n_experts).cpu().numpy()
+    load = {"rows_max_expert": int(counts.max()), "rows_mean_expert": round(float(counts.mean()), 1),
+            "experts_without_rows": int((counts == 0).sum())}
     names = layer.kernel_names()
     nk = len(names)
     ev = HipEvents()
@@ -367,7 +376,7 @@ def main() -> int:
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         try:
-            tj = json.load(open(tfile)).get(f"{cfg.name}:{dom}")
+            tj = json.load(open(tfile)).get(f"{wname}:{dom}")
             if tj and tj.get("kernel_source_sha") == bm_kernel_sha(dom, cfg):
                 traffic = tj.get("bytes_per_launch")
         except Exception:
@@ -405,9 +414,10 @@ def main() -> int:
                         else {"in_timed_steps": layer.prepared_bytes() > 0}),
         "launch": ({"mode": "graph replay", "eager_ms_per_step": round(eager_ms, 5)} if graphs
                    else {"mode": "eager", "note": graph_note}),
-        "config": {"workload": cfg.name, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+        "config": {"workload": wname, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k, "tokens": cfg.tokens,
-                   "routed_rows": cfg.tokens * cfg.top_k, "parallelism": "single GPU"},
+                   "routed_rows": cfg.tokens * cfg.top_k, "parallelism": "single GPU",
+                   "routing": {"gate_mode": "skewed" if args.skewed else "normal", **load}},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -897,21 +897,24 @@ hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ bucketing
-// One workgroup per expert e.  Its first bucket position is the number of
-// slots routed to lower experts, the sum over token tiles of the position of
-// e in the tile's list.  Its slots are the tiles' runs of e, concatenated in
-// tile order (so slots ascend within the expert): tiles are taken BK_THREADS
-// at a time, their run lengths scanned, and the runs copied by all threads.
-// With `rec` set it also writes the expert's tile records.
+// BK_SPLIT workgroups per expert e (so one popular expert's rows are copied
+// by several CUs).  The expert's first bucket position is the number of slots
+// routed to lower experts, the sum over token tiles of the position of e in
+// the tile's list.  Its slots are the tiles' runs of e, concatenated in tile
+// order (so slots ascend within the expert): tiles are taken BK_THREADS at a
+// time, their run lengths scanned, and the runs copied by all threads; part s
+// of the expert copies its positions [s c, (s + 1) c), c = ceil(count / BK_SPLIT).
+// With `rec` set the expert's tile records are written too (headers by part 0).
 constexpr int BK_THREADS = 256;
 constexpr int BK_UNROLL = 4;   // copies in flight per thread
+constexpr int BK_SPLIT = 4;    // workgroups per expert
 static_assert(BK_THREADS == 256, "the run search takes 8 halvings");
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   __shared__ int s_w[2][BK_THREADS / 64];
   __shared__ int s_pre[BK_THREADS + 1];  // run starts of the round's tiles in its output
   __shared__ int s_src[BK_THREADS];      // run starts in the tile lists
-  const int e = blockIdx.x, N = a.N, G = a.G, C = a.C;
+  const int e = blockIdx.x / BK_SPLIT, part = blockIdx.x % BK_SPLIT, N = a.N, G = a.G, C = a.C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // slots of lower experts and of e
@@ -935,13 +938,15 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
     below += s_w[0][w];
     cnt += s_w[1][w];
   }
-  if (tid == 0) {
+  if (tid == 0 && part == 0) {
     a.offsets[e] = below;
     if (e == N - 1) a.offsets[N] = a.R;
   }
   const int rrows = a.rec_rows;
   const int rbase = a.rec ? below / rrows + e : 0;  // first tile record of e
-  if (a.rec) {
+  const int chunk = (cnt + BK_SPLIT - 1) / BK_SPLIT;
+  const int q_lo = part * chunk, q_hi = min(cnt, q_lo + chunk);  // this part's positions in e's list
+  if (a.rec && part == 0) {
     const int nt = (cnt + rrows - 1) / rrows;
     const int next = e + 1 < N ? (below + cnt) / rrows + e + 1 : a.n_rec;
     for (int j = tid; j < next - rbase; j += BK_THREADS) {
@@ -952,7 +957,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   }
 
   int base = 0;  // position in e's list
-  for (int b0 = 0; b0 < G; b0 += BK_THREADS) {
+  for (int b0 = 0; b0 < G && base < q_hi; b0 += BK_THREADS) {
     const int b = b0 + tid;
     int st = 0, h = 0;
     if (b < G) {
@@ -979,14 +984,16 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
     if (tid == 0) s_pre[0] = 0;
     s_src[tid] = b * C + st;
     __syncthreads();
-    // output position f of the round: the tile i with s_pre[i] <= f < s_pre[i + 1]
-    for (int f0 = 0; f0 < total; f0 += BK_THREADS * BK_UNROLL) {
+    // output position f of the round: the tile i with s_pre[i] <= f < s_pre[i + 1];
+    // this part copies f in [f_lo, f_hi)
+    const int f_lo = max(0, q_lo - base), f_hi = min(total, q_hi - base);
+    for (int f0 = f_lo; f0 < f_hi; f0 += BK_THREADS * BK_UNROLL) {
       int v[BK_UNROLL];
       float g[BK_UNROLL];
 #pragma unroll
       for (int u = 0; u < BK_UNROLL; ++u) {
         const int f = f0 + u * BK_THREADS + tid;
-        if (f < total) {
+        if (f < f_hi) {
           int lo = 0, hi = BK_THREADS;
 #pragma unroll
           for (int it = 0; it < 8; ++it) {
@@ -1001,7 +1008,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
 #pragma unroll
       for (int u = 0; u < BK_UNROLL; ++u) {
         const int f = f0 + u * BK_THREADS + tid;
-        if (f < total) {
+        if (f < f_hi) {
           const int q = base + f;
           a.perm[below + q] = v[u];
           if (a.rec) {
@@ -1022,7 +1029,7 @@ hipError_t launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.rec && (!a.tile_gates || (a.rec_rows != 32 && a.rec_rows != 48 && a.rec_rows != TILE_ROWS_MAX) ||
                 a.n_rec != (a.R + a.rec_rows - 1) / a.rec_rows + a.N))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bucket_kernel, dim3(a.N), dim3(BK_THREADS), 0, s, a);
+  hipLaunchKernelGGL(bucket_kernel, dim3(a.N * BK_SPLIT), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
