@@ -222,6 +222,57 @@ def cpu_baseline(inp, y_gpu, seconds_target: float):
             "max_rel_err_gpu_vs_oracle": err}
 
 
+def spread_stats(v):
+    """Per-row outlier statistics of v [rows][n] (float32 tensor), averaged over rows:
+    peak-to-RMS ratio max|v| / rms(v), and the relative squared error of the
+    ternary code {-a, 0, +a} of each row (threshold 0.7 mean|v|, a = mean of
+    the |v| above it), |v - q|^2 / |v|^2."""
+    import torch
+    a = v.abs()
+    rms = v.pow(2).mean(1).sqrt()
+    peak = a.max(1).values / rms
+    m = a > 0.7 * a.mean(1, keepdim=True)
+    alpha = (a * m).sum(1, keepdim=True) / m.sum(1, keepdim=True).clamp(min=1)
+    q = alpha * torch.sign(v) * m
+    err = (v - q).pow(2).sum(1) / v.pow(2).sum(1)
+    return float(peak.mean()), float(err.mean())
+
+
+def outlier_spread(n_experts: int = 8) -> dict:
+    """Large FFN workload's tokens (1% of channels x50) before and after the
+    input rotation B(theta_e)^T of the up substrate, random angles, for the
+    first n_experts experts: mean peak-to-RMS ratio, ternary-code error and
+    the share of the energy in the outlier channels."""
+    import numpy as np
+    import torch
+    import compressed_mixture_experts_amd as bm
+    from compressed_mixture_experts_amd import workloads as wl
+    cfg = wl.CONFIGS[4]
+    inp = wl.generate(cfg)
+    xb = torch.from_numpy(inp.x.view(np.int16)).view(torch.bfloat16).cuda()
+    x = xb.float()
+    ch = torch.from_numpy(np.asarray(inp.outlier_channels)).cuda()
+
+    def share(v):
+        e = v.pow(2)
+        return float((e[:, ch].sum(1) / e.sum(1)).mean())
+
+    p0, q0 = spread_stats(x)
+    rot = []
+    for e in range(n_experts):
+        th = torch.from_numpy(np.ascontiguousarray(inp.theta[0][e], dtype=np.float32)).cuda()
+        u = bm.dbg_butterfly(th, x, transpose=True)
+        rot.append((*spread_stats(u), share(u)))
+    torch.cuda.synchronize()
+    r = np.array(rot)
+    return {"measurement": "outlier spread by the input rotation (random angles)",
+            "workload": cfg.name, "tokens": cfg.tokens, "width": cfg.d_model,
+            "outlier_channels": int(len(ch)), "experts": n_experts,
+            "x": {"peak_to_rms": round(p0, 3), "ternary_rel_err": round(q0, 4), "outlier_energy_share": round(share(x), 4)},
+            "rotated": {"peak_to_rms": round(float(r[:, 0].mean()), 3), "ternary_rel_err": round(float(r[:, 1].mean()), 4),
+                        "outlier_energy_share": round(float(r[:, 2].mean()), 4)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +288,9 @@ def main() -> int:
                     help="re-encode the weights inside every forward instead of once")
     ap.add_argument("--eager", action="store_true",
                     help="time launch-by-launch forwards instead of captured-graph replays")
+    ap.add_argument("--outlier-spread", action="store_true",
+                    help="only measure how the input rotation spreads the large workload's "
+                         "activation outliers (peak-to-RMS ratio, ternary-code error) and exit")
     ap.add_argument("--skewed", action="store_true",
                     help="skewed routing: gate row e scaled by 4/(e+1)^0.75, so a few experts take "
                          "most of the rows and many get few or none")
@@ -257,6 +311,9 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_mib": args.copy_probe, "copies": 5}))
+        return 0
+    if args.outlier_spread:
+        print(json.dumps(outlier_spread()))
         return 0
     import compressed_mixture_experts_amd as bm
     from compressed_mixture_experts_amd import workloads as wl
