@@ -48,8 +48,8 @@ from scipy.special import erf as _erf
 
 __all__ = [
     "stored_to_f64", "pair_index", "stage_matrix", "butterfly_dense",
-    "butterfly_apply", "expert_matrix", "expert_apply", "gelu", "route",
-    "forward", "forward_tokens", "param_counts", "ternary_product",
+    "butterfly_apply", "butterfly_backward", "expert_matrix", "expert_apply", "gelu",
+    "route", "forward", "forward_tokens", "param_counts", "ternary_product",
 ]
 
 
@@ -134,6 +134,58 @@ def butterfly_apply(angles: np.ndarray, M: np.ndarray, transpose: bool = False) 
             W[:, 1] = -sn * a + c * b
         V = W.reshape(n, -1)
     return V[:, 0] if vec else V
+
+
+def butterfly_backward(angles: np.ndarray, X: np.ndarray, dY: np.ndarray, transpose: bool = False):
+    """Gradients of the rotated columns Y = B(angles) X (or B^T X) for a given dY.
+
+    The rotations are learnable parameters of every expert ([MoE-zh] §2.2: the
+    butterfly angles are the experts' parameters; training them is the
+    adjacent step of the method).  Plain chain rule, one Givens stage at a
+    time: the forward pass keeps every stage's input; walking the stages back,
+    the angle of pair (i, j) of stage s collects, summed over the columns,
+        dY_i * d(out_i)/dt + dY_j * d(out_j)/dt
+    with out = [[c, -s], [s, c]] (a, b) (or its transpose for B^T), and the
+    gradient passes to the stage input through the transposed stage.
+
+    X, dY [n][m] float64-convertible.  Returns (dX [n][m], dAngles [L][n/2]).
+    """
+    ang = np.asarray(angles, dtype=np.float64)
+    L = ang.shape[0]
+    n = 1 << L
+    V = np.array(X, dtype=np.float64, copy=True)
+    G = np.array(dY, dtype=np.float64, copy=True)
+    if V.shape != G.shape or V.shape[0] != n:
+        raise ValueError("X and dY must both be [n][m]")
+    order = list(range(L - 1, -1, -1)) if transpose else list(range(L))
+    kept = []
+    for s in order:
+        kept.append((s, V.copy()))
+        V = butterfly_apply(_one_stage(ang, s), V, transpose=transpose)
+    dang = np.zeros((L, n // 2))
+    for s, Vin in reversed(kept):
+        for i in range(n):
+            if i & (1 << s):
+                continue
+            j = i + (1 << s)
+            p = pair_index(i, s)
+            c, sn = math.cos(ang[s, p]), math.sin(ang[s, p])
+            a, b = Vin[i], Vin[j]
+            if not transpose:      # out_i = c a - s b, out_j = s a + c b
+                da, db = -sn * a - c * b, c * a - sn * b
+            else:                  # out_i = c a + s b, out_j = -s a + c b
+                da, db = -sn * a + c * b, -c * a - sn * b
+            dang[s, p] = float(np.sum(G[i] * da + G[j] * db))
+        # gradient to the stage input: through the transposed stage
+        G = butterfly_apply(_one_stage(ang, s), G, transpose=not transpose)
+    return G, dang
+
+
+def _one_stage(ang: np.ndarray, s: int) -> np.ndarray:
+    """Angle array in which only stage s rotates (every other stage's angles 0)."""
+    one = np.zeros_like(ang)
+    one[s] = ang[s]
+    return one
 
 
 # ---------------------------------------------------------------------------

@@ -130,6 +130,63 @@ def test_orbit_invariants():
     assert np.abs(sv - sv0).max() < 1e-12
 
 
+@pytest.mark.parametrize("n", [2, 8, 16])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_butterfly_backward_finite_differences(n, transpose):
+    # every angle and input gradient against central differences of
+    # L = sum(dY * B X) (or B^T X), evaluated with the forward alone
+    r = np.random.default_rng(7 * n + transpose)
+    ang = rand_angles(n, seed=n + 100 * transpose)
+    X = r.standard_normal((n, 3))
+    dY = r.standard_normal((n, 3))
+    dX, dang = ref.butterfly_backward(ang, X, dY, transpose)
+
+    def loss(a, x):
+        return float(np.sum(dY * ref.butterfly_apply(a, x, transpose)))
+
+    h = 1e-6
+    for s_ in range(ang.shape[0]):
+        for p in range(n // 2):
+            ap, am = ang.copy(), ang.copy()
+            ap[s_, p] += h
+            am[s_, p] -= h
+            fd = (loss(ap, X) - loss(am, X)) / (2 * h)
+            assert abs(fd - dang[s_, p]) < 1e-7 * (1 + abs(fd))
+    for i in range(n):
+        for c in range(3):
+            xp, xm = X.copy(), X.copy()
+            xp[i, c] += h
+            xm[i, c] -= h
+            fd = (loss(ang, xp) - loss(ang, xm)) / (2 * h)
+            assert abs(fd - dX[i, c]) < 1e-7 * (1 + abs(fd))
+
+
+def test_butterfly_backward_d2_by_hand_and_zero_angles():
+    # d = 2: y = (c a - s b, s a + c b), dL/dt = g1 (-s a - c b) + g2 (c a - s b);
+    # for B^T: y = (c a + s b, -s a + c b), dL/dt = g1 (-s a + c b) + g2 (-c a - s b)
+    t, a, b, g1, g2 = 0.3, 1.5, -2.0, 0.7, 0.4
+    c, sn = math.cos(t), math.sin(t)
+    _, d = ref.butterfly_backward(np.array([[t]]), np.array([[a], [b]]), np.array([[g1], [g2]]))
+    assert d[0, 0] == pytest.approx(g1 * (-sn * a - c * b) + g2 * (c * a - sn * b), abs=1e-14)
+    _, d = ref.butterfly_backward(np.array([[t]]), np.array([[a], [b]]), np.array([[g1], [g2]]), True)
+    assert d[0, 0] == pytest.approx(g1 * (-sn * a + c * b) + g2 * (-c * a - sn * b), abs=1e-14)
+    # all angles zero: B = I, so dX = dY, and every angle of pair (i, j)
+    # gathers sum(dY_j X_i - dY_i X_j) (forward) or its negative (transposed)
+    n = 16
+    r = np.random.default_rng(3)
+    X, dY = r.standard_normal((n, 4)), r.standard_normal((n, 4))
+    for tr, sign in ((False, 1.0), (True, -1.0)):
+        dX, dang = ref.butterfly_backward(np.zeros((4, n // 2)), X, dY, tr)
+        assert np.allclose(dX, dY, atol=1e-15)
+        for s_ in range(4):
+            for i in range(n):
+                if i & (1 << s_):
+                    continue
+                j = i + (1 << s_)
+                want = sign * np.sum(dY[j] * X[i] - dY[i] * X[j])
+                assert dang[s_, ref.pair_index(i, s_)] == pytest.approx(want, abs=1e-13)
+
+
 def test_expert_matrix_explicit_products():
     d_out, d_in = 8, 4
     r = np.random.default_rng(9)
