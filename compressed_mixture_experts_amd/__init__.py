@@ -19,7 +19,8 @@ import numpy as np
 
 __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
-    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "STATUS", "EXPORTED_SYMBOLS",
+    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "STATUS",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +39,7 @@ EXPORTED_SYMBOLS = [
     "bmoe_prepare", "bmoe_route", "bmoe_forward", "bmoe_status_string", "bmoe_last_error",
     "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
     "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
+    "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
 ]
 
 
@@ -100,9 +102,13 @@ def lib() -> ctypes.CDLL:
     L.bmoe_dbg_ternary_gemm_fp4.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_f, c_vp, c_vp]
     L.bmoe_dbg_forward_kernels.argtypes = [pL, ctypes.POINTER(c_i32), ctypes.c_char_p, c_sz]
     L.bmoe_dbg_forward_marked.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_i32]
+    L.bmoe_butterfly_backward_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_butterfly_backward.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_sz, c_vp]
     for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
                  "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
-                 "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked"):
+                 "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
+                 "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward"):
         getattr(L, name).restype = c_i32
     _lib = L
     return L
@@ -310,6 +316,27 @@ def dbg_butterfly(angles, x, transpose: bool = False, out=None):
     _check(lib().bmoe_dbg_butterfly(log2n, rows, _ptr(angles), 1 if transpose else 0, dtype,
                                     _ptr(x), _ptr(out), _stream_handle()))
     return out
+
+
+def butterfly_backward(angles, offsets, x, dy, transpose: bool = False, dx=None):
+    """Backward of the bucketed rotation pass y_r = B(angles_e) x_r (or B^T x_r)
+    for rows r of expert e (rows offsets[e] .. offsets[e+1]-1).  angles
+    [N][L][n/2] fp32, offsets [N+1] int32, x and dy [rows][n] (fp32 or bf16).
+    Returns (dx [rows][n] like x, dangles [N][L][n/2] fp32)."""
+    torch = _torch()
+    N, L = int(angles.shape[0]), int(angles.shape[1])
+    rows = int(x.shape[0])
+    dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    if dx is None:
+        dx = torch.empty_like(x)
+    dang = torch.empty_like(angles)
+    nb = ctypes.c_size_t(0)
+    _check(lib().bmoe_butterfly_backward_workspace(L, N, rows, ctypes.byref(nb)))
+    ws = torch.empty(max(int(nb.value), 16), dtype=torch.uint8, device=x.device)
+    _check(lib().bmoe_butterfly_backward(L, N, rows, _ptr(offsets), _ptr(angles), 1 if transpose else 0, dtype,
+                                         _ptr(x), _ptr(dy), _ptr(dx), _ptr(dang), _ptr(ws), int(nb.value),
+                                         _stream_handle()))
+    return dx, dang
 
 
 def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):

@@ -9,6 +9,7 @@
 
 #include "bmoe.h"
 #include "bmoe_debug.h"
+#include "bmoe_grad.h"
 #include "common.hpp"
 
 using namespace bmoe;
@@ -686,6 +687,60 @@ bmoe_status bmoe_dbg_forward_marked(const bmoe_layer* layer, const void* x, int3
   if (n_marks < 0) return fail(BMOE_ERR_SHAPE, "n_marks is negative");
   return forward_impl(layer, x, T, y, nullptr, nullptr, workspace, workspace_bytes, stream, marks,
                       n_marks);
+}
+
+static bmoe_status check_bwd_shape(int32_t log2n, int32_t n_experts, int32_t rows) {
+  if (log2n < 1 || log2n > 13) return fail(BMOE_ERR_SHAPE, "log2n=%d must be in [1, 13]", log2n);
+  if (n_experts < 1 || n_experts > 256) return fail(BMOE_ERR_SHAPE, "n_experts=%d must be in [1, 256]", n_experts);
+  if (rows < 0 || int64_t(rows) << log2n > (int64_t(1) << 31) - 1)
+    return fail(BMOE_ERR_SHAPE, "rows=%d: must be >= 0 with rows * 2^log2n below 2^31", rows);
+  return BMOE_OK;
+}
+
+bmoe_status bmoe_butterfly_backward_workspace(int32_t log2n, int32_t n_experts, int32_t rows, size_t* bytes) {
+  if (!bytes) return fail(BMOE_ERR_NULL, "bytes is NULL");
+  const bmoe_status st = check_bwd_shape(log2n, n_experts, rows);
+  if (st != BMOE_OK) return st;
+  *bytes = bfly_bwd_workspace(log2n, n_experts, rows);
+  return ok();
+}
+
+bmoe_status bmoe_butterfly_backward(int32_t log2n, int32_t n_experts, int32_t rows, const int32_t* offsets,
+                                    const float* angles, int32_t transpose, int32_t dtype, const void* x,
+                                    const void* dy, void* dx, float* dangles, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  bmoe_status st = check_bwd_shape(log2n, n_experts, rows);
+  if (st != BMOE_OK) return st;
+  if (transpose != 0 && transpose != 1) return fail(BMOE_ERR_SHAPE, "transpose must be 0 or 1");
+  if (dtype != BMOE_F32 && dtype != BMOE_BF16) return fail(BMOE_ERR_DTYPE, "dtype=%d is unknown", dtype);
+  if (!offsets || !angles || !dangles) return fail(BMOE_ERR_NULL, "offsets / angles / dangles is NULL");
+  const size_t need = bfly_bwd_workspace(log2n, n_experts, rows);
+  if (rows > 0 && (!x || !dy || !dx)) return fail(BMOE_ERR_NULL, "x / dy / dx is NULL");
+  if (need > 0 && !workspace) return fail(BMOE_ERR_NULL, "workspace is NULL");
+  const size_t es = dtype == BMOE_BF16 ? 2 : 4;
+  if (!aligned(offsets, 4) || !aligned(angles, 4) || !aligned(dangles, 4))
+    return fail(BMOE_ERR_ALIGN, "offsets, angles and dangles must be 4-byte aligned");
+  if (rows > 0 && (!aligned(x, es) || !aligned(dy, es) || !aligned(dx, es)))
+    return fail(BMOE_ERR_ALIGN, "x, dy and dx must be aligned to their element size");
+  if (need > 0 && !aligned(workspace, 16)) return fail(BMOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(BMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t ab = size_t(n_experts) * log2n * (size_t(1) << (log2n - 1)) * 4;
+  const size_t rb = (size_t(rows) << log2n) * es;
+  const Range rx{x, rb}, rdy{dy, rb}, rdx{dx, rb}, rda{dangles, ab}, ran{angles, ab},
+      rof{offsets, size_t(n_experts + 1) * 4}, rws{workspace, need};
+  if (rows > 0 && ((dx != x && overlap(rdx, rx)) || (dx != dy && overlap(rdx, rdy)) || overlap(rdx, ran) ||
+                   overlap(rdx, rof) || overlap(rdx, rws) || overlap(rdx, rda)))
+    return fail(BMOE_ERR_ALIAS, "dx overlaps an input, the workspace or dangles");
+  if (overlap(rda, ran) || overlap(rda, rof) || overlap(rda, rws) || (rows > 0 && (overlap(rda, rx) || overlap(rda, rdy))))
+    return fail(BMOE_ERR_ALIAS, "dangles overlaps an input or the workspace");
+  if (need > 0 && (overlap(rws, ran) || overlap(rws, rof) || (rows > 0 && (overlap(rws, rx) || overlap(rws, rdy)))))
+    return fail(BMOE_ERR_ALIAS, "the workspace overlaps an input");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+  BMOE_HIP(launch_bfly_bwd(x, dy, dx, angles, offsets, static_cast<float*>(workspace), dangles, rows, n_experts,
+                           log2n, transpose, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
+  return ok();
 }
 
 bmoe_status bmoe_dbg_butterfly(int32_t log2n, int32_t rows, const float* angles, int32_t transpose,

@@ -239,6 +239,11 @@ hipError_t launch_bfly_split(const BflyArgs& a, int part, int log2n, hipStream_t
 bool gemm_fp4_supported(int N, int K);
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
+// Backward of a bucketed butterfly pass (butterfly_bwd.hip): workspace bytes and launch.
+size_t bfly_bwd_workspace(int log2n, int n_experts, int rows);
+hipError_t launch_bfly_bwd(const void* x, const void* dy, void* dx, const float* ang, const int32_t* offsets,
+                           float* part, float* dang, int rows, int n_experts, int log2n, int transpose, int act,
+                           hipStream_t s);
 
 bool fused_square_supported(int log2n);
 bool fused_mfma_supported(int log2n);

@@ -1,0 +1,61 @@
+/*
+ * bmoe_grad.h - gradients through the experts' butterfly rotations.
+ *
+ * Training a ButterflyMoE layer learns, per expert, the angles of its
+ * butterflies (ButterflyMoE, gist.science/zh/paper/2601.13563, technical
+ * summary §2.2: the experts are rotations of the shared substrate; their
+ * parameters are the angles of hierarchical Givens rotations).  This header
+ * gives the backward step of one bucketed rotation pass, the building block
+ * of the layer's backward: for rows r of expert e (rows offsets[e] ..
+ * offsets[e+1] - 1, as bmoe_route buckets them)
+ *     forward   y_r = B(angles_e) x_r          (transpose 0)
+ *           or  y_r = B(angles_e)^T x_r        (transpose 1)
+ * and a given dy_r = dL/dy_r it returns dx_r = dL/dx_r and, per expert,
+ *     dangles_e = sum over e's rows of dL/dangles_e.
+ * Butterfly wiring as in bmoe.h.  The forward rotations are recomputed in
+ * fp32 from x; angle gradients are fp32 sums, per expert in a fixed order
+ * (the result does not depend on scheduling).
+ */
+#ifndef BMOE_GRAD_H
+#define BMOE_GRAD_H
+
+#include "bmoe.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Device workspace bytes bmoe_butterfly_backward needs (per-tile partial
+ * angle gradients; 0 when rows is 0).  log2n in [1, 13], n_experts in
+ * [1, 256], rows >= 0. */
+bmoe_status bmoe_butterfly_backward_workspace(int32_t log2n, int32_t n_experts, int32_t rows,
+                                              size_t* bytes);
+
+/* Backward of the bucketed rotation pass described above.
+ *   offsets  [n_experts + 1] int32 (device): expert e owns rows offsets[e] ..
+ *            offsets[e+1] - 1; offsets[0] = 0, nondecreasing, offsets[N] =
+ *            rows (values outside [0, rows] are clamped to it).
+ *   angles   [n_experts][log2n][2^log2n / 2] fp32 (device), read only.
+ *   x, dy    [rows][2^log2n] of dtype (bmoe_dtype, device), read only.
+ *   dx       [rows][2^log2n] of dtype (device), written; may be the same
+ *            buffer as x or dy, must not overlap them otherwise.
+ *   dangles  [n_experts][log2n][2^log2n / 2] fp32 (device), overwritten for
+ *            every expert (zero for an expert without rows).
+ *   workspace at least bmoe_butterfly_backward_workspace bytes (device,
+ *            16-byte aligned), caller-owned scratch, contents undefined after.
+ * Enqueued on `stream`; nothing is allocated or synchronised.  Errors:
+ * BMOE_ERR_SHAPE (sizes), BMOE_ERR_DTYPE, BMOE_ERR_NULL, BMOE_ERR_ALIGN
+ * (x, dy, dx aligned to their element size; angles, dangles, offsets to 4
+ * bytes), BMOE_ERR_ALIAS (an output overlaps an input, the workspace or the
+ * other output), BMOE_ERR_WORKSPACE, BMOE_ERR_HIP; all but the last are
+ * detected before anything is enqueued. */
+bmoe_status bmoe_butterfly_backward(int32_t log2n, int32_t n_experts, int32_t rows,
+                                    const int32_t* offsets, const float* angles, int32_t transpose,
+                                    int32_t dtype, const void* x, const void* dy, void* dx,
+                                    float* dangles, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BMOE_GRAD_H */

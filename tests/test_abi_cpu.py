@@ -294,3 +294,38 @@ def test_forward_checks_prepared_buffer():
     assert call_forward(s) == 6 and ws_size(s, 16)[0] == 6
     s.prepared, s.prepared_bytes = FAKE + 0x10000000 + 64, need
     assert call_forward(s) == 4
+
+
+def test_butterfly_backward_arguments():
+    # workspace: per-tile partial angle gradients, ceil(rows / RT) + N tiles of
+    # L n/2 floats, RT = min(64, 16384 / n); zero without rows
+    L = bm.lib()
+    n = ctypes.c_size_t(0)
+    assert L.bmoe_butterfly_backward_workspace(9, 8, 300, ctypes.byref(n)) == 0
+    assert n.value == ((300 + 31) // 32 + 8) * 9 * 256 * 4
+    assert L.bmoe_butterfly_backward_workspace(13, 2, 5, ctypes.byref(n)) == 0
+    assert n.value == ((5 + 1) // 2 + 2) * 13 * 4096 * 4
+    assert L.bmoe_butterfly_backward_workspace(4, 3, 0, ctypes.byref(n)) == 0 and n.value == 0
+    for args, st in (((0, 4, 10), 2), ((14, 4, 10), 2), ((5, 0, 10), 2), ((5, 257, 10), 2), ((5, 4, -1), 2),
+                     ((13, 4, 1 << 18), 2)):
+        assert L.bmoe_butterfly_backward_workspace(*args, ctypes.byref(n)) == st
+    assert L.bmoe_butterfly_backward_workspace(5, 4, 10, None) == 1
+
+    need = ((10 + 63) // 64 + 4) * 5 * 16 * 4
+    F = FAKE
+    x, dy, dx = F + 0x10000, F + 0x20000, F + 0x30000
+    ang, dang, off, ws = F + 0x40000, F + 0x50000, F + 0x60000, F + 0x70000
+
+    def call(log2n=5, N=4, rows=10, off=off, ang=ang, tr=0, dt=bm.F32, x=x, dy=dy, dx=dx, dang=dang,
+             ws=ws, wsb=need):
+        return L.bmoe_butterfly_backward(log2n, N, rows, off, ang, tr, dt, x, dy, dx, dang, ws, wsb, None)
+
+    assert call(tr=2) == 2
+    assert call(dt=7) == 3
+    assert call(off=None) == 1 and call(dang=None) == 1 and call(x=None) == 1 and call(ws=None) == 1
+    assert call(x=F + 0x10002) == 4            # fp32 rows must be 4-byte aligned
+    assert call(ws=F + 0x70008) == 4           # workspace 16-byte aligned
+    assert call(wsb=need - 1) == 6
+    assert call(dx=x + 64) == 5                # dx partly over x
+    assert call(dang=ang + 4) == 5             # dangles over the angles
+    assert call(ws=x) == 5                     # workspace over an input
