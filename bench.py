@@ -273,6 +273,47 @@ def outlier_spread(n_experts: int = 8) -> dict:
                         "outlier_energy_share": round(float(r[:, 2].mean()), 4)}}
 
 
+def grad_measure(reps: int = 20) -> dict:
+    """Butterfly backward (bmoe_butterfly_backward) at the routed-row shapes of
+    the edge workload (input rotation, width 512) and the large workload
+    (input rotation, width 2048; FFN up rotation, width 8192): bf16 rows
+    bucketed evenly over the experts, fp32 angles.  Per shape: mean time per
+    call (HIP events on torch's stream) and the rate of its algorithmic HBM
+    bytes (rows x, dy in and dx out, angles in, angle gradients out, per-tile
+    partial gradients out and back)."""
+    import math
+    import torch
+    import compressed_mixture_experts_amd as bm
+    out = []
+    for name, rows, n, N, tr in (("edge_d512_n64 input rotation", 8192, 512, 64, True),
+                                 ("large_d2048_n256 input rotation", 65536, 2048, 256, True),
+                                 ("large_d2048_n256 ffn up rotation", 65536, 8192, 256, False)):
+        L = int(math.log2(n))
+        g = torch.Generator(device="cuda").manual_seed(11)
+        x = torch.randn((rows, n), device="cuda", generator=g).to(torch.bfloat16)
+        dy = torch.randn((rows, n), device="cuda", generator=g).to(torch.bfloat16)
+        ang = (torch.rand((N, L, n // 2), device="cuda", generator=g) * 2 - 1) * math.pi
+        off = torch.tensor([(rows * e) // N for e in range(N + 1)], dtype=torch.int32, device="cuda")
+        dx = torch.empty_like(x)
+        for _ in range(3):
+            bm.butterfly_backward(ang, off, x, dy, tr, dx=dx)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(reps):
+            bm.butterfly_backward(ang, off, x, dy, tr, dx=dx)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / reps
+        rt = min(64, 16384 // n)
+        tiles = (rows + rt - 1) // rt + N
+        by = 3 * rows * n * 2 + 2 * N * L * (n // 2) * 4 + 2 * tiles * L * (n // 2) * 4
+        out.append({"shape": name, "rows": rows, "width": n, "experts": N, "ms": round(ms, 4),
+                    "hbm_gbps": round(by / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(by / (ms * 1e-3) / 8e12, 4)})
+    return {"measurement": "butterfly backward (input and angle gradients)", "dtype": "bf16 rows, fp32 angles",
+            "shapes": out}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +329,8 @@ def main() -> int:
                     help="re-encode the weights inside every forward instead of once")
     ap.add_argument("--eager", action="store_true",
                     help="time launch-by-launch forwards instead of captured-graph replays")
+    ap.add_argument("--grad", action="store_true",
+                    help="only time the butterfly backward at the workloads' routed-row shapes and exit")
     ap.add_argument("--outlier-spread", action="store_true",
                     help="only measure how the input rotation spreads the large workload's "
                          "activation outliers (peak-to-RMS ratio, ternary-code error) and exit")
@@ -314,6 +357,9 @@ def main() -> int:
         return 0
     if args.outlier_spread:
         print(json.dumps(outlier_spread()))
+        return 0
+    if args.grad:
+        print(json.dumps(grad_measure()))
         return 0
     import compressed_mixture_experts_amd as bm
     from compressed_mixture_experts_amd import workloads as wl

@@ -161,31 +161,43 @@ def butterfly_backward(angles: np.ndarray, X: np.ndarray, dY: np.ndarray, transp
     kept = []
     for s in order:
         kept.append((s, V.copy()))
-        V = butterfly_apply(_one_stage(ang, s), V, transpose=transpose)
+        V = _apply_stage(ang[s], s, V, transpose)
     dang = np.zeros((L, n // 2))
     for s, Vin in reversed(kept):
-        for i in range(n):
-            if i & (1 << s):
-                continue
-            j = i + (1 << s)
-            p = pair_index(i, s)
-            c, sn = math.cos(ang[s, p]), math.sin(ang[s, p])
-            a, b = Vin[i], Vin[j]
-            if not transpose:      # out_i = c a - s b, out_j = s a + c b
-                da, db = -sn * a - c * b, c * a - sn * b
-            else:                  # out_i = c a + s b, out_j = -s a + c b
-                da, db = -sn * a + c * b, -c * a - sn * b
-            dang[s, p] = float(np.sum(G[i] * da + G[j] * db))
+        # pairs of stage s: lower index i (bit s clear), upper j = i + 2^s; in
+        # the [n / 2^(s+1)][2][2^s] view pair p = (block, offset) is row-major
+        h = 1 << s
+        c = np.cos(ang[s]).reshape(n // (2 * h), h, 1)
+        sn = np.sin(ang[s]).reshape(n // (2 * h), h, 1)
+        Vw = Vin.reshape(n // (2 * h), 2, h, -1)
+        Gw = G.reshape(n // (2 * h), 2, h, -1)
+        a, b = Vw[:, 0], Vw[:, 1]
+        if not transpose:      # out_i = c a - s b, out_j = s a + c b
+            da, db = -sn * a - c * b, c * a - sn * b
+        else:                  # out_i = c a + s b, out_j = -s a + c b
+            da, db = -sn * a + c * b, -c * a - sn * b
+        dang[s] = np.sum(Gw[:, 0] * da + Gw[:, 1] * db, axis=2).reshape(n // 2)
         # gradient to the stage input: through the transposed stage
-        G = butterfly_apply(_one_stage(ang, s), G, transpose=not transpose)
+        G = _apply_stage(ang[s], s, G, not transpose)
     return G, dang
 
 
-def _one_stage(ang: np.ndarray, s: int) -> np.ndarray:
-    """Angle array in which only stage s rotates (every other stage's angles 0)."""
-    one = np.zeros_like(ang)
-    one[s] = ang[s]
-    return one
+def _apply_stage(ang_s: np.ndarray, s: int, V: np.ndarray, transpose: bool) -> np.ndarray:
+    """Stage s alone (or its transpose) applied to the rows of V [n][m]: rows
+    i and i + 2^s rotate by the angle of their pair, as in butterfly_apply."""
+    n = V.shape[0]
+    h = 1 << s
+    c = np.cos(np.asarray(ang_s, dtype=np.float64)).reshape(n // (2 * h), h, 1)
+    sn = np.sin(np.asarray(ang_s, dtype=np.float64)).reshape(n // (2 * h), h, 1)
+    W = np.array(V, dtype=np.float64).reshape(n // (2 * h), 2, h, V.shape[1])
+    a, b = W[:, 0].copy(), W[:, 1].copy()
+    if not transpose:
+        W[:, 0] = c * a - sn * b
+        W[:, 1] = sn * a + c * b
+    else:
+        W[:, 0] = c * a + sn * b
+        W[:, 1] = -sn * a + c * b
+    return W.reshape(n, -1)
 
 
 # ---------------------------------------------------------------------------

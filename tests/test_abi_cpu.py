@@ -297,21 +297,27 @@ def test_forward_checks_prepared_buffer():
 
 
 def test_butterfly_backward_arguments():
-    # workspace: per-tile partial angle gradients, ceil(rows / RT) + N tiles of
-    # L n/2 floats, RT = min(64, 16384 / n); zero without rows
+    # workspace: per-chunk partial angle gradients, ceil(rows / CH) + N chunks
+    # of L n/2 floats, CH = RT * clamp(rows // (RT * 512), 1, 256 // RT) with
+    # RT = min(64, 16384 / n); zero without rows
     L = bm.lib()
     n = ctypes.c_size_t(0)
-    assert L.bmoe_butterfly_backward_workspace(9, 8, 300, ctypes.byref(n)) == 0
-    assert n.value == ((300 + 31) // 32 + 8) * 9 * 256 * 4
-    assert L.bmoe_butterfly_backward_workspace(13, 2, 5, ctypes.byref(n)) == 0
-    assert n.value == ((5 + 1) // 2 + 2) * 13 * 4096 * 4
+
+    def want(log2n, N, rows):
+        rt = min(64, 16384 >> log2n)
+        ch = rt * min(max(rows // (rt * 512), 1), max(256 // rt, 1))
+        return (-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4
+
+    for args in ((9, 8, 300), (13, 2, 5), (11, 256, 65536), (9, 64, 8192), (13, 256, 65536), (2, 3, 100000)):
+        assert L.bmoe_butterfly_backward_workspace(*args, ctypes.byref(n)) == 0
+        assert n.value == want(*args), args
     assert L.bmoe_butterfly_backward_workspace(4, 3, 0, ctypes.byref(n)) == 0 and n.value == 0
     for args, st in (((0, 4, 10), 2), ((14, 4, 10), 2), ((5, 0, 10), 2), ((5, 257, 10), 2), ((5, 4, -1), 2),
                      ((13, 4, 1 << 18), 2)):
         assert L.bmoe_butterfly_backward_workspace(*args, ctypes.byref(n)) == st
     assert L.bmoe_butterfly_backward_workspace(5, 4, 10, None) == 1
 
-    need = ((10 + 63) // 64 + 4) * 5 * 16 * 4
+    need = (1 + 4) * 5 * 16 * 4
     F = FAKE
     x, dy, dx = F + 0x10000, F + 0x20000, F + 0x30000
     ang, dang, off, ws = F + 0x40000, F + 0x50000, F + 0x60000, F + 0x70000

@@ -62,6 +62,8 @@ def check_case(L, N, rows, transpose, act, seed, empty=(), inplace=False):
             assert np.all(dang[e] == 0.0), f"expert {e} has no rows but nonzero angle gradients"
             continue
         dX, dA = ref.butterfly_backward(ang[e].astype(np.float64), x64[r0:r1].T, dy64[r0:r1].T, transpose)
+        if (r1 - r0) << L > (1 << 22):
+            log(f"  expert {e}: {r1 - r0} rows checked")
         err = row_rel_err(dx[r0:r1], dX.T)
         assert err.max() <= tol_x, f"expert {e}: dx row error {err.max():.3g}"
         rel = np.linalg.norm(dang[e] - dA) / max(np.linalg.norm(dA), 1e-30)
@@ -76,7 +78,11 @@ CASES = [
     (9, 8, 300, (3,)),
     (10, 5, 120, ()),
     (11, 3, 40, (1,)),
+    (12, 3, 9, (0,)),
     (13, 2, 5, ()),
+    (7, 4, 1300, ()),    # experts of several chunks
+    (9, 4, 40000, (2,)), # chunks of two 32-row sub-tiles
+    (13, 2, 2100, ()),   # chunks of two 2-row sub-tiles
 ]
 
 
