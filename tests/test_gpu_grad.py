@@ -109,3 +109,66 @@ def test_butterfly_backward_in_place_and_zero_rows():
     dx, dang = bm.butterfly_backward(ang, off, x, x)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dang).item() == 0
+
+
+def test_expert_angle_gradients_compose():
+    # One square expert y = B(phi) (alpha W B(theta)^T x) per bucket of rows:
+    # the output rotation's backward gives d phi and dZ, the substrate's
+    # transposed product (the ternary GEMM with W^T packed) gives dU, the input
+    # rotation's backward gives d theta and dx.  Against the oracle's chain in
+    # fp64, and two angles of each rotation against central differences of
+    # the oracle's expert.
+    import torch
+    r = np.random.default_rng(21)
+    d, N, R, alpha = 256, 4, 300, 0.5
+    L = int(math.log2(d))
+    W = r.integers(-1, 2, size=(d, d)).astype(np.int8)
+    th = r.uniform(-math.pi, math.pi, size=(N, L, d // 2)).astype(np.float32)
+    ph = r.uniform(-math.pi, math.pi, size=(N, L, d // 2)).astype(np.float32)
+    off = np.array([0, 90, 90, 210, R], dtype=np.int32)   # expert 1 has no rows
+    x = r.standard_normal((R, d)).astype(np.float32)
+    dy = r.standard_normal((R, d)).astype(np.float32)
+    log("expert angle gradients through the C ABI")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    xd, dyd, thd, phd, offd = dev(x), dev(dy), dev(th), dev(ph), dev(off)
+    Wp = dev(bm.pack_ternary(W).view(np.int32))
+    WTp = dev(bm.pack_ternary(np.ascontiguousarray(W.T)).view(np.int32))
+    U = torch.empty_like(xd)
+    for e in range(N):
+        if off[e + 1] > off[e]:
+            U[off[e]:off[e + 1]] = bm.dbg_butterfly(thd[e], xd[off[e]:off[e + 1]].contiguous(), transpose=True)
+    Z = bm.dbg_ternary_gemm(U, Wp, d, alpha)
+    dZ, dph = bm.butterfly_backward(phd, offd, Z, dyd, False)
+    dU = bm.dbg_ternary_gemm(dZ, WTp, d, alpha)
+    dx, dth = bm.butterfly_backward(thd, offd, xd, dU, True)
+    torch.cuda.synchronize()
+    dx, dth, dph = (t.cpu().numpy().astype(np.float64) for t in (dx, dth, dph))
+    W64 = W.astype(np.float64)
+    for e in range(N):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            assert not dth[e].any() and not dph[e].any()
+            continue
+        X, DY = x[r0:r1].T.astype(np.float64), dy[r0:r1].T.astype(np.float64)
+        t64, p64 = th[e].astype(np.float64), ph[e].astype(np.float64)
+        Zr = alpha * (W64 @ ref.butterfly_apply(t64, X, transpose=True))
+        dZr, dP = ref.butterfly_backward(p64, Zr, DY, False)
+        dXr, dT = ref.butterfly_backward(t64, X, alpha * (W64.T @ dZr), True)
+        for got, want, what in ((dth[e], dT, "theta"), (dph[e], dP, "phi")):
+            rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+            assert rel <= 1e-4, f"expert {e} d{what}: {rel:.3g}"
+        assert row_rel_err(dx[r0:r1], dXr.T).max() <= 1e-4
+        # the chain itself against central differences of the expert
+        loss = lambda t, p: float(np.sum(DY * ref.expert_apply(t, p, W64, X, alpha)))
+        h = 1e-6
+        for (s_, q) in ((0, 3), (L - 1, 100)):
+            for which, grad in (("t", dT), ("p", dP)):
+                tp, tm, pp, pm = t64.copy(), t64.copy(), p64.copy(), p64.copy()
+                if which == "t":
+                    tp[s_, q] += h
+                    tm[s_, q] -= h
+                else:
+                    pp[s_, q] += h
+                    pm[s_, q] -= h
+                fd = (loss(tp, pp) - loss(tm, pm)) / (2 * h)
+                assert abs(fd - grad[s_, q]) <= 1e-6 * (1 + abs(fd))
