@@ -279,8 +279,9 @@ def grad_measure(reps: int = 20) -> dict:
     (input rotation, width 2048; FFN up rotation, width 8192): bf16 rows
     bucketed evenly over the experts, fp32 angles.  Per shape: mean time per
     call (HIP events on torch's stream) and the rate of its algorithmic HBM
-    bytes (rows x, dy in and dx out, angles in, angle gradients out, per-tile
-    partial gradients out and back)."""
+    bytes (rows x, dy in and dx out, angles in, angle gradients out; per-chunk
+    partial gradients and, at widths of 4096 and more, the fp32 rows between the
+    part passes are the implementation's own traffic and not counted)."""
     import math
     import torch
     import compressed_mixture_experts_amd as bm
@@ -305,9 +306,7 @@ def grad_measure(reps: int = 20) -> dict:
         s1.record()
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / reps
-        rt = min(64, 16384 // n)
-        tiles = (rows + rt - 1) // rt + N
-        by = 3 * rows * n * 2 + 2 * N * L * (n // 2) * 4 + 2 * tiles * L * (n // 2) * 4
+        by = 3 * rows * n * 2 + 2 * N * L * (n // 2) * 4
         out.append({"shape": name, "rows": rows, "width": n, "experts": N, "ms": round(ms, 4),
                     "hbm_gbps": round(by / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(by / (ms * 1e-3) / 8e12, 4)})
     return {"measurement": "butterfly backward (input and angle gradients)", "dtype": "bf16 rows, fp32 angles",

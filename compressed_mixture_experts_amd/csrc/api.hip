@@ -720,8 +720,9 @@ bmoe_status bmoe_butterfly_backward(int32_t log2n, int32_t n_experts, int32_t ro
   const size_t es = dtype == BMOE_BF16 ? 2 : 4;
   if (!aligned(offsets, 4) || !aligned(angles, 4) || !aligned(dangles, 4))
     return fail(BMOE_ERR_ALIGN, "offsets, angles and dangles must be 4-byte aligned");
-  if (rows > 0 && (!aligned(x, es) || !aligned(dy, es) || !aligned(dx, es)))
-    return fail(BMOE_ERR_ALIGN, "x, dy and dx must be aligned to their element size");
+  const size_t ra = log2n >= 3 ? 16 : es;  // rows of 8 or more elements move in 16-byte vectors
+  if (rows > 0 && (!aligned(x, ra) || !aligned(dy, ra) || !aligned(dx, ra)))
+    return fail(BMOE_ERR_ALIGN, "x, dy and dx must be %zu-byte aligned", ra);
   if (need > 0 && !aligned(workspace, 16)) return fail(BMOE_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (workspace_bytes < need)
     return fail(BMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);

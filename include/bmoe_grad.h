@@ -25,8 +25,9 @@
 extern "C" {
 #endif
 
-/* Device workspace bytes bmoe_butterfly_backward needs (per-tile partial
- * angle gradients; 0 when rows is 0).  log2n in [1, 13], n_experts in
+/* Device workspace bytes bmoe_butterfly_backward needs (per-chunk partial
+ * angle gradients, and for log2n >= 12 two fp32 [rows][2^log2n] buffers
+ * between its passes; 0 when rows is 0).  log2n in [1, 13], n_experts in
  * [1, 256], rows >= 0. */
 bmoe_status bmoe_butterfly_backward_workspace(int32_t log2n, int32_t n_experts, int32_t rows,
                                               size_t* bytes);
@@ -45,8 +46,8 @@ bmoe_status bmoe_butterfly_backward_workspace(int32_t log2n, int32_t n_experts, 
  *            16-byte aligned), caller-owned scratch, contents undefined after.
  * Enqueued on `stream`; nothing is allocated or synchronised.  Errors:
  * BMOE_ERR_SHAPE (sizes), BMOE_ERR_DTYPE, BMOE_ERR_NULL, BMOE_ERR_ALIGN
- * (x, dy, dx aligned to their element size; angles, dangles, offsets to 4
- * bytes), BMOE_ERR_ALIAS (an output overlaps an input, the workspace or the
+ * (x, dy, dx aligned to 16 bytes when 2^log2n >= 8, else to their
+ * element size; angles, dangles, offsets to 4 bytes), BMOE_ERR_ALIAS (an output overlaps an input, the workspace or the
  * other output), BMOE_ERR_WORKSPACE, BMOE_ERR_HIP; all but the last are
  * detected before anything is enqueued. */
 bmoe_status bmoe_butterfly_backward(int32_t log2n, int32_t n_experts, int32_t rows,

@@ -304,11 +304,16 @@ def test_butterfly_backward_arguments():
     n = ctypes.c_size_t(0)
 
     def want(log2n, N, rows):
-        rt = min(64, 16384 >> log2n)
+        if log2n >= 12:  # part passes: 32-row chunks, plus two fp32 row buffers
+            ch = 32 * min(max(rows // 8192, 1), 8)
+            up = lambda v: -(-v // 256) * 256
+            return up((-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4) + 2 * up(rows * (4 << log2n))
+        rt = min(64, 8192 >> log2n) if log2n <= 9 else 16384 >> log2n
         ch = rt * min(max(rows // (rt * 512), 1), max(256 // rt, 1))
         return (-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4
 
-    for args in ((9, 8, 300), (13, 2, 5), (11, 256, 65536), (9, 64, 8192), (13, 256, 65536), (2, 3, 100000)):
+    for args in ((9, 8, 300), (9, 8, 500000), (8, 3, 70000), (13, 2, 5), (11, 256, 65536), (9, 64, 8192), (13, 256, 65536), (12, 7, 200000),
+                 (2, 3, 100000)):
         assert L.bmoe_butterfly_backward_workspace(*args, ctypes.byref(n)) == 0
         assert n.value == want(*args), args
     assert L.bmoe_butterfly_backward_workspace(4, 3, 0, ctypes.byref(n)) == 0 and n.value == 0
@@ -329,7 +334,9 @@ def test_butterfly_backward_arguments():
     assert call(tr=2) == 2
     assert call(dt=7) == 3
     assert call(off=None) == 1 and call(dang=None) == 1 and call(x=None) == 1 and call(ws=None) == 1
-    assert call(x=F + 0x10002) == 4            # fp32 rows must be 4-byte aligned
+    assert call(x=F + 0x10002) == 4            # rows of width >= 8 must be 16-byte aligned
+    assert call(dy=F + 0x20008, dt=bm.BF16) == 4
+    assert call(log2n=2, rows=10, x=F + 0x10002, wsb=1 << 20) == 4  # width 4: element alignment
     assert call(ws=F + 0x70008) == 4           # workspace 16-byte aligned
     assert call(wsb=need - 1) == 6
     assert call(dx=x + 64) == 5                # dx partly over x
