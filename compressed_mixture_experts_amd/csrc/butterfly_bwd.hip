@@ -383,8 +383,6 @@ __global__ __launch_bounds__(256) void bfly_bwd_reduce_kernel(BflyBwdArgs a, int
 }
 
 // ---------------------------------------------------------------- parts (L >= 12)
-enum { BP_LOW = 0, BP_HIGH = 1 };
-
 struct BflyPartArgs {
   const void* in0;        // rows the part's forward is recomputed from [R][n]
   const void* in1;        // gradient rows at the part's output [R][n] (backward)
@@ -392,62 +390,16 @@ struct BflyPartArgs {
   const float* ang;       // [N][L][n/2]
   const int32_t* offsets; // [N+1]
   float* part;            // [n_chunks][L][n/2]
-  int32_t rows, n_experts, transpose, chunk, n_chunks;
+  int32_t rows, n_experts, chunk, n_chunks;
 };
 
-// A part as a butterfly over GW local indices of a row: LOW, chunk c: local l
-// is index c 2^S + l, local stage t is stage t (MS = S stages); HIGH, columns
-// v0 .. v0+63: local l = 64 jj + vl is index v0 + vl + 2^S jj, local stage t is
-// stage S + t (MS = 4), with 8 local pairs per column.
-template <int S, int PART>
-struct BpCfg {
-  static constexpr int L = S + 4, n = 1 << L, half = n / 2;
-  static constexpr int GW = PART == BP_LOW ? (1 << S) : 1024;   // local indices per row
-  static constexpr int MS = PART == BP_LOW ? S : 4;             // local stages
-  static constexpr int NG = PART == BP_LOW ? 16 : (1 << S) / 64; // groups per row
-  static constexpr int RT = 8192 / GW;                          // rows per LDS tile (64 KiB for two)
-  static constexpr int NT = GW / 2 < 256 ? GW / 2 : 256;
-  static constexpr int PPT = GW / 2 / NT;                       // local pairs per thread per stage
-};
-
-template <int S, int PART>
-__device__ __forceinline__ int bp_global(int g, int l) {  // local index -> index in the row
-  if constexpr (PART == BP_LOW) return (g << S) + l;
-  else return g * 64 + (l & 63) + ((l >> 6) << S);
-}
-// local pair k of local stage t: its two local indices and its angle's pair number
-template <int S, int PART>
-__device__ __forceinline__ void bp_pair(int g, int t, int k, int& lo, int& hi, int& gp) {
-  if constexpr (PART == BP_LOW) {
-    lo = pair_lo(k, t);
-    hi = lo + (1 << t);
-    gp = (g << (S - 1)) + k;
-  } else {
-    const int q = k >> 6, vl = k & 63;
-    const int jl = pair_lo(q, t);
-    lo = jl * 64 + vl;
-    hi = (jl + (1 << t)) * 64 + vl;
-    gp = (q << S) + g * 64 + vl;
-  }
-}
-
-// One (row chunk, index group) of a part.  BWD = 0: out = part(in0) (or its
-// transpose); BWD = 1: the part's backward, out = gradient at its input.
-template <int S, int PART, int A0, int A1, int AO, int BWD>
-__global__ __launch_bounds__(256, 2) void bfly_part_kernel(BflyPartArgs a) {
-  using C = BpCfg<S, PART>;
-  constexpr int NT = C::NT, GW = C::GW, MS = C::MS, PPT = C::PPT, RT = C::RT, n = C::n, half = C::half;
-  constexpr int s_base = PART == BP_LOW ? 0 : S;
-  extern __shared__ __attribute__((aligned(16))) float tile[];  // V [RT][GW], then G [RT][GW]
-  __shared__ int s_info[3];
+// expert, first row and row count of chunk cb (e = -1 for an unused index),
+// broadcast through LDS to the whole workgroup
+__device__ __forceinline__ void bp_chunk_info(const BflyPartArgs& a, int cb, int* s_info) {
   const int tid = threadIdx.x, CH = a.chunk;
-  const int cb = blockIdx.x / C::NG, g = blockIdx.x % C::NG;
-  float* V = tile;
-  float* G = tile + RT * GW;
-
   if (tid == 0) s_info[0] = -1;
   __syncthreads();
-  for (int e = tid; e < a.n_experts; e += NT) {
+  for (int e = tid; e < a.n_experts; e += blockDim.x) {
     const int off = min(max(a.offsets[e], 0), a.rows);
     const int cnt = min(max(a.offsets[e + 1], off), a.rows) - off;
     const int base = off / CH + e, nt = (cnt + CH - 1) / CH;
@@ -458,142 +410,339 @@ __global__ __launch_bounds__(256, 2) void bfly_part_kernel(BflyPartArgs a) {
     }
   }
   __syncthreads();
-  const int e = s_info[0];
-  if (e < 0) return;
-  const int c0 = s_info[1], ccnt = s_info[2];
-  const float* ang = a.ang + size_t(e) * (S + 4) * half;
-  const bool tr = a.transpose != 0;
-  auto stage_of = [&](int kk) { return tr ? MS - 1 - kk : kk; };  // kk-th local stage applied
+}
 
-  // (cos, sin) of this thread's pairs, once per chunk, sin negated for B^T,
-  // and their angle gradients; both indexed by the order of application kk
-  float2 cs[MS][PPT];
-  float acc[MS][PPT];
-#pragma unroll
-  for (int kk = 0; kk < MS; ++kk)
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      int lo, hi, gp;
-      const int t = stage_of(kk);
-      bp_pair<S, PART>(g, t, tid + k * NT, lo, hi, gp);
-      const float2 v = bb_sincos(ang[(s_base + t) * half + gp]);
-      cs[kk][k] = make_float2(v.x, tr ? -v.y : v.y);
-      acc[kk][k] = 0.f;
-    }
+// number of stage t's pair whose lower index is i
+__device__ __forceinline__ int pair_of(int i, int t) { return ((i >> (t + 1)) << t) | (i & ((1 << t) - 1)); }
 
-  // tile vectors: q -> row q / PR, local index (q % PR) * VEC
-  auto tile_io = [&](auto vec_c, int r0) {
-    constexpr int VEC = decltype(vec_c)::value, PR = GW / VEC;
-    auto gi = [=](int q) { return size_t(r0 + q / PR) * n + bp_global<S, PART>(g, (q % PR) * VEC); };
-    auto li = [=](int q) { return (q / PR) * GW + (q % PR) * VEC; };
-    return std::make_pair(gi, li);
-  };
-
-  for (int t0 = 0; t0 < ccnt; t0 += RT) {
-    const int r0 = c0 + t0, nr = min(RT, ccnt - t0);
-    const int ptid = bb_opaque(tid);
-    {
-      constexpr int V0 = bb_vec<A0>();
-      auto io = tile_io(std::integral_constant<int, V0>(), r0);
-      bb_load_tile<A0, NT, RT * GW / V0 / NT>(a.in0, V, nr * GW / V0, io.first, io.second);
-    }
-    if constexpr (BWD) {
-      constexpr int V1 = bb_vec<A1>();
-      auto io = tile_io(std::integral_constant<int, V1>(), r0);
-      bb_load_tile<A1, NT, RT * GW / V1 / NT>(a.in1, G, nr * GW / V1, io.first, io.second);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < MS; ++kk) {
-      const int t = stage_of(kk);
-#pragma unroll
-      for (int k = 0; k < PPT; ++k) {
-        int lo, hi, gp;
-        bp_pair<S, PART>(g, t, ptid + k * NT, lo, hi, gp);
-        bb_rot_rows(V, GW, nr, lo, hi, cs[kk][k].x, cs[kk][k].y);
-      }
-      __syncthreads();
-    }
-    if constexpr (BWD) {
-#pragma unroll
-      for (int kk = MS - 1; kk >= 0; --kk) {
-        const int t = stage_of(kk);
-#pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-          int lo, hi, gp;
-          bp_pair<S, PART>(g, t, ptid + k * NT, lo, hi, gp);
-          const float gsum = bb_back_rows(V, G, GW, nr, lo, hi, cs[kk][k].x, cs[kk][k].y);
-          acc[kk][k] += tr ? -gsum : gsum;
-        }
-        __syncthreads();
-      }
-    }
-    {
-      constexpr int VO = bb_vec<AO>();
-      auto io = tile_io(std::integral_constant<int, VO>(), r0);
-      bb_store_tile<AO, NT, RT * GW / VO / NT>(a.out, BWD ? G : V, nr * GW / VO, io.first, io.second);
-    }
-    __syncthreads();
-  }
-
-  if constexpr (BWD) {
-    float* part = a.part + size_t(cb) * (S + 4) * half;
-#pragma unroll
-    for (int kk = 0; kk < MS; ++kk)
-#pragma unroll
-      for (int k = 0; k < PPT; ++k) {
-        int lo, hi, gp;
-        const int t = stage_of(kk);
-        bp_pair<S, PART>(g, t, tid + k * NT, lo, hi, gp);
-        part[(s_base + t) * half + gp] = acc[kk][k];
-      }
+template <int A>
+__device__ __forceinline__ void store1(void* p, size_t i, float v) {
+  if constexpr (A == ACT_BF16) {
+    reinterpret_cast<uint16_t*>(p)[i] = uint16_t(pack_bf16x2(v, 0.f) & 0xFFFFu);
+  } else {
+    reinterpret_cast<float*>(p)[i] = v;
   }
 }
 
-template <int S, int PART, int A0, int A1, int AO, int BWD>
-static hipError_t bp_launch(const BflyPartArgs& a, hipStream_t s) {
-  using C = BpCfg<S, PART>;
-  const size_t lds = size_t(BWD ? 2 : 1) * C::RT * C::GW * sizeof(float);
-  static int attr_done[64] = {0};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  auto k = bfly_part_kernel<S, PART, A0, A1, AO, BWD>;
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
+// one rotation of a pair and the backward through it (s already negated for B^T)
+__device__ __forceinline__ void bp_rot(float& x0, float& x1, float c, float s) {
+  const float a = x0, b = x1;
+  x0 = c * a - s * b;
+  x1 = s * a + c * b;
+}
+// returns g_b a' - g_a b' for outputs (o0, o1) with gradients (g0, g1), and
+// turns both pairs back through the rotation
+__device__ __forceinline__ float bp_back(float& o0, float& o1, float& g0, float& g1, float c, float s) {
+  const float a = o0, b = o1, ga = g0, gb = g1;
+  o0 = c * a + s * b;
+  o1 = -s * a + c * b;
+  g0 = c * ga + s * gb;
+  g1 = -s * ga + c * gb;
+  return gb * a - ga * b;
+}
+
+// ---- low part: stages 0 .. S-1 on 2^S consecutive indices.  A wave owns a
+// 512-element slot of the row (one segment for S = 9, two for S = 8) and
+// walks the chunk's rows; a lane holds 8 elements of the slot whose index
+// differs in three bits, so three stages run in registers between exchanges.
+// Layout G (G = 0, 1, 2) puts the 3 bits at base bit BB(G) = 0, 3, and 6
+// (S = 9) or 5 (S = 8; its stages are 6 and 7, the lowest bit is stage 5,
+// already done): element of (lane l, j) = (l mod 2^BB) | j << BB | (l >> BB)
+// << (BB + 3).  Exchanges go through the wave's own 512 floats of LDS (no
+// workgroup barrier), stored at e ^ (((e >> 6) & 7) << 3) so that every
+// layout's accesses spread over the banks.
+template <int S>
+struct BpLow {
+  static constexpr int bb(int G) { return G == 0 ? 0 : G == 1 ? 3 : (S == 9 ? 6 : 5); }
+  static constexpr int first(int G) { return G * 3; }                   // first stage of group G
+  static constexpr int nst(int G) { return G < 2 ? 3 : S - 6; }         // stages in group G
+  static __device__ __forceinline__ int elem(int G, int l, int j) {
+    const int b = bb(G);
+    return (l & ((1 << b) - 1)) | (j << b) | ((l >> b) << (b + 3));
   }
-  hipLaunchKernelGGL(k, dim3(a.n_chunks * C::NG), dim3(C::NT), lds, s, a);
+  static __device__ __forceinline__ int swz(int e) { return e ^ (((e >> 6) & 7) << 3); }
+};
+
+template <int S, int TR, int A0, int A1, int AO, int BWD>
+__global__ __launch_bounds__(256) void bfly_low_kernel(BflyPartArgs a) {
+  using P = BpLow<S>;
+  constexpr int L = S + 4, n = 1 << L, half = n / 2;
+  constexpr int NSLOT = n / 512, BPC = NSLOT / 4;  // slots per row, workgroups per chunk
+  constexpr int G0 = TR ? 2 : 0, G2 = TR ? 0 : 2;   // first and last layout applied
+  __shared__ __attribute__((aligned(16))) float xch[4][2][512];
+  __shared__ int s_info[3];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cb = blockIdx.x / BPC, slot = (blockIdx.x % BPC) * 4 + w;
+  bp_chunk_info(a, cb, s_info);
+  const int e = s_info[0];
+  if (e < 0) return;
+  const int c0 = s_info[1], ccnt = s_info[2];
+  const float* ang = a.ang + size_t(e) * L * half;
+  const int sbase = slot * 512;
+  float* XV = xch[w][0];
+  float* XG = xch[w][1];
+
+  // (cos, sin) and angle gradients of this lane's pairs: [group][stage in group][pair]
+  float cc[3][3][4], ss[3][3][4], acc[3][3][4];
+#pragma unroll
+  for (int G = 0; G < 3; ++G)
+#pragma unroll
+    for (int ti = 0; ti < 3; ++ti)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cc[G][ti][k] = 1.f;
+        ss[G][ti][k] = 0.f;
+        acc[G][ti][k] = 0.f;
+        if (ti < P::nst(G)) {
+          const int t = P::first(G) + ti, p = t - P::bb(G);
+          const int j = pair_lo(k, p);
+          const float2 v = bb_sincos(ang[t * half + pair_of(sbase + P::elem(G, lane, j), t)]);
+          cc[G][ti][k] = v.x;
+          ss[G][ti][k] = TR ? -v.y : v.y;
+        }
+      }
+
+  // the stages of group G in the order of application, forward and backward
+  auto fwd_group = [&](int G, float (&x)[8]) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int ti = TR ? P::nst(G) - 1 - q : q;
+      if (ti < 0 || ti >= P::nst(G)) continue;
+      const int p = P::first(G) + ti - P::bb(G);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = pair_lo(k, p);
+        bp_rot(x[j], x[j + (1 << p)], cc[G][ti][k], ss[G][ti][k]);
+      }
+    }
+  };
+  auto bwd_group = [&](int G, float (&x)[8], float (&g)[8]) {
+#pragma unroll
+    for (int q = 2; q >= 0; --q) {
+      const int ti = TR ? P::nst(G) - 1 - q : q;
+      if (ti < 0 || ti >= P::nst(G)) continue;
+      const int p = P::first(G) + ti - P::bb(G);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = pair_lo(k, p), jh = j + (1 << p);
+        const float d = bp_back(x[j], x[jh], g[j], g[jh], cc[G][ti][k], ss[G][ti][k]);
+        acc[G][ti][k] += TR ? -d : d;
+      }
+    }
+  };
+  // layout change through the wave's LDS (wavefront-scope fences: LDS accesses
+  // of one wave take effect in order; the fences keep the compiler from
+  // moving them across each other)
+  auto exchange = [&](float* X, float (&x)[8], int Gf, int Gt) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) X[P::swz(P::elem(Gf, lane, j))] = x[j];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = X[P::swz(P::elem(Gt, lane, j))];
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // rows <-> registers in layout G (layout 0: 8 consecutive elements)
+  auto load = [&](auto act_c, const void* src, int r, int G, float (&x)[8]) {
+    constexpr int A = decltype(act_c)::value;
+    const size_t base = size_t(r) * n + sbase;
+    if (G == 0) {
+      load8<A>(src, base + P::elem(0, lane, 0), x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = load1<A>(src, base + P::elem(G, lane, j));
+    }
+  };
+  auto store = [&](auto act_c, void* dst, int r, int G, const float (&x)[8]) {
+    constexpr int A = decltype(act_c)::value;
+    const size_t base = size_t(r) * n + sbase;
+    if (G == 0) {
+      store8<A>(dst, base + P::elem(0, lane, 0), x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) store1<A>(dst, base + P::elem(G, lane, j), x[j]);
+    }
+  };
+  using C0 = std::integral_constant<int, A0>;
+  using C1 = std::integral_constant<int, A1>;
+  using CO = std::integral_constant<int, AO>;
+
+  float xn[8], gn[8];  // next row's inputs, loaded while this row is worked on
+  load(C0(), a.in0, c0, G0, xn);
+  if constexpr (BWD) load(C1(), a.in1, c0, G2, gn);
+  for (int r = c0; r < c0 + ccnt; ++r) {
+    float x[8], g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = xn[j];
+      if constexpr (BWD) g[j] = gn[j];
+    }
+    if (r + 1 < c0 + ccnt) {
+      load(C0(), a.in0, r + 1, G0, xn);
+      if constexpr (BWD) load(C1(), a.in1, r + 1, G2, gn);
+    }
+    // forward: groups in the order of application
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int G = TR ? 2 - q : q;
+      if (q > 0) exchange(XV, x, TR ? G + 1 : G - 1, G);
+      fwd_group(G, x);
+    }
+    if constexpr (!BWD) {
+      store(CO(), a.out, r, G2, x);
+    } else {
+#pragma unroll
+      for (int q = 2; q >= 0; --q) {
+        const int G = TR ? 2 - q : q;
+        bwd_group(G, x, g);
+        if (q > 0) {
+          const int Gp = TR ? G + 1 : G - 1;  // the group applied before G
+          exchange(XV, x, G, Gp);
+          exchange(XG, g, G, Gp);
+        }
+      }
+      store(CO(), a.out, r, G0, g);
+    }
+  }
+
+  if constexpr (BWD) {
+    float* part = a.part + size_t(cb) * L * half;
+#pragma unroll
+    for (int G = 0; G < 3; ++G)
+#pragma unroll
+      for (int ti = 0; ti < 3; ++ti)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (ti < P::nst(G)) {
+            const int t = P::first(G) + ti, p = t - P::bb(G);
+            part[t * half + pair_of(sbase + P::elem(G, lane, pair_lo(k, p)), t)] = acc[G][ti][k];
+          }
+  }
+}
+
+// ---- high part: stages S .. S+3, each on pairs (v + 2^S j, v + 2^S (j + 2^t')).
+// A thread owns column v (v < 2^S) and holds its 16 elements j = 0..15 of a
+// row: all four stages run in registers.  256 columns per workgroup.
+template <int S, int TR, int A0, int A1, int AO, int BWD>
+__global__ __launch_bounds__(256) void bfly_high_kernel(BflyPartArgs a) {
+  constexpr int L = S + 4, n = 1 << L, half = n / 2;
+  constexpr int BPC = (1 << S) / 256;  // workgroups per chunk
+  __shared__ int s_info[3];
+  const int cb = blockIdx.x / BPC, v = (blockIdx.x % BPC) * 256 + threadIdx.x;
+  bp_chunk_info(a, cb, s_info);
+  const int e = s_info[0];
+  if (e < 0) return;
+  const int c0 = s_info[1], ccnt = s_info[2];
+  const float* ang = a.ang + size_t(e) * L * half;
+
+  // local stage t (global S + t), local pair q: lower element pair_lo(q, t)
+  float cc[4][8], ss[4][8], acc[4][8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float2 cs = bb_sincos(ang[(S + t) * half + (q << S) + v]);
+      cc[t][q] = cs.x;
+      ss[t][q] = TR ? -cs.y : cs.y;
+      acc[t][q] = 0.f;
+    }
+
+  float xn[16], gn[16];
+  auto load = [&](auto act_c, const void* src, int r, float (&x)[16]) {
+    constexpr int A = decltype(act_c)::value;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = load1<A>(src, size_t(r) * n + v + (j << S));
+  };
+  using C0 = std::integral_constant<int, A0>;
+  using C1 = std::integral_constant<int, A1>;
+  load(C0(), a.in0, c0, xn);
+  if constexpr (BWD) load(C1(), a.in1, c0, gn);
+  for (int r = c0; r < c0 + ccnt; ++r) {
+    float x[16], g[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      x[j] = xn[j];
+      if constexpr (BWD) g[j] = gn[j];
+    }
+    if (r + 1 < c0 + ccnt) {
+      load(C0(), a.in0, r + 1, xn);
+      if constexpr (BWD) load(C1(), a.in1, r + 1, gn);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = TR ? 3 - k : k;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = pair_lo(q, t);
+        bp_rot(x[j], x[j + (1 << t)], cc[t][q], ss[t][q]);
+      }
+    }
+    if constexpr (!BWD) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) store1<AO>(a.out, size_t(r) * n + v + (j << S), x[j]);
+    } else {
+#pragma unroll
+      for (int k = 3; k >= 0; --k) {
+        const int t = TR ? 3 - k : k;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int j = pair_lo(q, t), jh = j + (1 << t);
+          const float d = bp_back(x[j], x[jh], g[j], g[jh], cc[t][q], ss[t][q]);
+          acc[t][q] += TR ? -d : d;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) store1<AO>(a.out, size_t(r) * n + v + (j << S), g[j]);
+    }
+  }
+
+  if constexpr (BWD) {
+    float* part = a.part + size_t(cb) * L * half;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) part[(S + t) * half + (q << S) + v] = acc[t][q];
+  }
+}
+
+template <int S, int HIGH, int TR, int A0, int A1, int AO, int BWD>
+static hipError_t bp_launch(const BflyPartArgs& a, hipStream_t s) {
+  if constexpr (HIGH) {
+    hipLaunchKernelGGL((bfly_high_kernel<S, TR, A0, A1, AO, BWD>), dim3(a.n_chunks * ((1 << S) / 256)), dim3(256),
+                       0, s, a);
+  } else {
+    hipLaunchKernelGGL((bfly_low_kernel<S, TR, A0, A1, AO, BWD>), dim3(a.n_chunks * ((1 << (S + 4)) / 2048)),
+                       dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 // the three part passes of a wide backward (see the header comment)
-template <int S, int ACT>
+template <int S, int TR, int ACT>
 static hipError_t bp_run(BflyPartArgs a, const void* x, const void* dy, void* dx, float* zbuf, float* dzbuf,
                          hipStream_t s) {
-  const bool tr = a.transpose != 0;
+  constexpr int FIRST = TR ? 1 : 0;  // the part applied first: low for B, high^T for B^T
   hipError_t err;
-  // z = first part applied (low for B, high^T for B^T)
+  // z = first part applied to x
   a.in0 = x; a.in1 = nullptr; a.out = zbuf;
-  err = tr ? bp_launch<S, BP_HIGH, ACT, ACT_F32, ACT_F32, 0>(a, s) : bp_launch<S, BP_LOW, ACT, ACT_F32, ACT_F32, 0>(a, s);
+  err = bp_launch<S, FIRST, TR, ACT, ACT_F32, ACT_F32, 0>(a, s);
   if (err != hipSuccess) return err;
   // second part's backward from (z, dy): dz
   a.in0 = zbuf; a.in1 = dy; a.out = dzbuf;
-  err = tr ? bp_launch<S, BP_LOW, ACT_F32, ACT, ACT_F32, 1>(a, s) : bp_launch<S, BP_HIGH, ACT_F32, ACT, ACT_F32, 1>(a, s);
+  err = bp_launch<S, 1 - FIRST, TR, ACT_F32, ACT, ACT_F32, 1>(a, s);
   if (err != hipSuccess) return err;
   // first part's backward from (x, dz): dx
   a.in0 = x; a.in1 = dzbuf; a.out = dx;
-  return tr ? bp_launch<S, BP_HIGH, ACT, ACT_F32, ACT, 1>(a, s) : bp_launch<S, BP_LOW, ACT, ACT_F32, ACT, 1>(a, s);
+  return bp_launch<S, FIRST, TR, ACT, ACT_F32, ACT, 1>(a, s);
 }
 
 static size_t align256z(size_t v) { return (v + 255) & ~size_t(255); }
 
-// rows per chunk of the part passes: a multiple of 32, at most 256, about 256
-// chunks (every part has at least 4 index groups per chunk)
+// rows per chunk of the part passes: a multiple of 32, at most 128, about 256
+// chunks or more
 static int bp_chunk(int rows) {
   int k = rows / (32 * 256);
-  k = k < 1 ? 1 : k > 8 ? 8 : k;
+  k = k < 1 ? 1 : k > 4 ? 4 : k;
   return 32 * k;
 }
 
@@ -654,10 +803,16 @@ hipError_t launch_bfly_bwd(const void* x, const void* dy, void* dx, const float*
     const size_t pbytes = align256z(size_t(a.n_chunks) * L * (n >> 1) * sizeof(float));
     float* zbuf = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + pbytes);
     float* dzbuf = reinterpret_cast<float*>(reinterpret_cast<char*>(zbuf) + align256z((size_t(rows) << L) * 4));
-    BflyPartArgs pa{nullptr, nullptr, nullptr, ang, offsets, part, rows, n_experts, transpose, a.chunk, a.n_chunks};
+    BflyPartArgs pa{nullptr, nullptr, nullptr, ang, offsets, part, rows, n_experts, a.chunk, a.n_chunks};
+    const bool bf = act == ACT_BF16, tr = transpose != 0;
     hipError_t err;
-    if (L == 12) err = act == ACT_BF16 ? bp_run<8, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<8, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s);
-    else err = act == ACT_BF16 ? bp_run<9, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<9, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s);
+    if (L == 12) {
+      err = tr ? (bf ? bp_run<8, 1, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<8, 1, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s))
+               : (bf ? bp_run<8, 0, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<8, 0, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s));
+    } else {
+      err = tr ? (bf ? bp_run<9, 1, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<9, 1, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s))
+               : (bf ? bp_run<9, 0, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<9, 0, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s));
+    }
     if (err != hipSuccess) return err;
   } else if (rows > 0) {
     a.chunk = bfly_bwd_chunk(log2n, rows);

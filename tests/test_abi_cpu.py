@@ -305,7 +305,7 @@ def test_butterfly_backward_arguments():
 
     def want(log2n, N, rows):
         if log2n >= 12:  # part passes: 32-row chunks, plus two fp32 row buffers
-            ch = 32 * min(max(rows // 8192, 1), 8)
+            ch = 32 * min(max(rows // 8192, 1), 4)
             up = lambda v: -(-v // 256) * 256
             return up((-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4) + 2 * up(rows * (4 << log2n))
         rt = min(64, 8192 >> log2n) if log2n <= 9 else 16384 >> log2n
