@@ -705,6 +705,183 @@ __global__ __launch_bounds__(256) void bfly_high_kernel(BflyPartArgs a) {
   }
 }
 
+// ---- width 2048 in one pass: a workgroup's four waves hold one row, wave w
+// its 512-element slot w in the low part's layouts 0..2 (stages 0..8), and
+// a fourth layout, lane l' = 64 w + lane holding the elements l' + 256 j
+// (j = 0..7, index bits 8..10), runs stages 9 and 10.  The change between
+// layouts 2 and 3 crosses waves, through a 2048-float row buffer in LDS and a
+// workgroup barrier; the buffers of the forward and the backward change are
+// distinct, so two barriers per row suffice.
+template <int TR, int ACT>
+__global__ __launch_bounds__(256) void bfly_row11_kernel(BflyPartArgs a) {
+  using P = BpLow<9>;
+  constexpr int L = 11, n = 2048, half = 1024;
+  constexpr int G0 = TR ? 3 : 0, G3 = TR ? 0 : 3;  // first and last layout applied
+  __shared__ __attribute__((aligned(16))) float xw[4][512];   // in-wave layout changes
+  __shared__ __attribute__((aligned(16))) float xf[2048];     // forward 2 <-> 3
+  __shared__ __attribute__((aligned(16))) float xb[2][2048];  // backward 3 <-> 2 (values, gradients)
+  __shared__ int s_info[3];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lp = threadIdx.x;
+  const int cb = blockIdx.x;
+  bp_chunk_info(a, cb, s_info);
+  const int e = s_info[0];
+  if (e < 0) return;
+  const int c0 = s_info[1], ccnt = s_info[2];
+  const float* ang = a.ang + size_t(e) * L * half;
+  const int sbase = w * 512;
+  // row index of element j of this lane in layout G
+  auto elem = [&](int G, int j) { return G < 3 ? sbase + P::elem(G, lane, j) : lp | (j << 8); };
+
+  // groups 0..2: stages 3G .. 3G+2; group 3: stages 9, 10 (j bits 1, 2)
+  float cc[4][3][4], ss[4][3][4], acc[4][3][4];
+#pragma unroll
+  for (int G = 0; G < 4; ++G)
+#pragma unroll
+    for (int ti = 0; ti < 3; ++ti)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cc[G][ti][k] = 1.f;
+        ss[G][ti][k] = 0.f;
+        acc[G][ti][k] = 0.f;
+        if (G < 3 || ti < 2) {
+          const int t = G < 3 ? 3 * G + ti : 9 + ti, p = G < 3 ? ti : ti + 1;
+          const float2 v = bb_sincos(ang[t * half + pair_of(elem(G, pair_lo(k, p)), t)]);
+          cc[G][ti][k] = v.x;
+          ss[G][ti][k] = TR ? -v.y : v.y;
+        }
+      }
+  constexpr int NST[4] = {3, 3, 3, 2};
+  auto jbit = [](int G, int ti) { return G < 3 ? ti : ti + 1; };
+  auto fwd_group = [&](int G, float (&x)[8]) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int ti = TR ? NST[G] - 1 - q : q;
+      if (ti < 0 || ti >= NST[G]) continue;
+      const int p = jbit(G, ti);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = pair_lo(k, p);
+        bp_rot(x[j], x[j + (1 << p)], cc[G][ti][k], ss[G][ti][k]);
+      }
+    }
+  };
+  auto bwd_group = [&](int G, float (&x)[8], float (&g)[8]) {
+#pragma unroll
+    for (int q = 2; q >= 0; --q) {
+      const int ti = TR ? NST[G] - 1 - q : q;
+      if (ti < 0 || ti >= NST[G]) continue;
+      const int p = jbit(G, ti);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = pair_lo(k, p), jh = j + (1 << p);
+        const float d = bp_back(x[j], x[jh], g[j], g[jh], cc[G][ti][k], ss[G][ti][k]);
+        acc[G][ti][k] += TR ? -d : d;
+      }
+    }
+  };
+  // in-wave layout change (groups 0..2) through the wave's slice
+  auto xch_wave = [&](float (&x)[8], int Gf, int Gt) {
+    float* X = xw[w];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) X[P::swz(P::elem(Gf, lane, j))] = x[j];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = X[P::swz(P::elem(Gt, lane, j))];
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto put = [&](float* X, const float (&x)[8], int G) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) X[elem(G, j)] = x[j];
+  };
+  auto get = [&](const float* X, float (&x)[8], int G) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = X[elem(G, j)];
+  };
+  auto load = [&](const void* src, int r, int G, float (&x)[8]) {
+    const size_t base = size_t(r) * n;
+    if (G == 0) {
+      load8<ACT>(src, base + elem(0, 0), x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = load1<ACT>(src, base + elem(G, j));
+    }
+  };
+  auto store = [&](void* dst, int r, int G, const float (&x)[8]) {
+    const size_t base = size_t(r) * n;
+    if (G == 0) {
+      store8<ACT>(dst, base + elem(0, 0), x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) store1<ACT>(dst, base + elem(G, j), x[j]);
+    }
+  };
+
+  float xn[8], gn[8];
+  load(a.in0, c0, G0, xn);
+  load(a.in1, c0, G3, gn);
+  for (int r = c0; r < c0 + ccnt; ++r) {
+    float x[8], g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[j] = xn[j];
+      g[j] = gn[j];
+    }
+    if (r + 1 < c0 + ccnt) {
+      load(a.in0, r + 1, G0, xn);
+      load(a.in1, r + 1, G3, gn);
+    }
+    // forward, layouts in the order of application
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int G = TR ? 3 - q : q;
+      if (q > 0) {
+        const int Gp = TR ? G + 1 : G - 1;
+        if (G == 3 || Gp == 3) {
+          put(xf, x, Gp);
+          __syncthreads();
+          get(xf, x, G);
+        } else {
+          xch_wave(x, Gp, G);
+        }
+      }
+      fwd_group(G, x);
+    }
+    // backward, in the reverse order
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      const int G = TR ? 3 - q : q;
+      bwd_group(G, x, g);
+      if (q > 0) {
+        const int Gp = TR ? G + 1 : G - 1;  // the layout applied before G
+        if (G == 3 || Gp == 3) {
+          put(xb[0], x, G);
+          put(xb[1], g, G);
+          __syncthreads();
+          get(xb[0], x, Gp);
+          get(xb[1], g, Gp);
+        } else {
+          xch_wave(x, G, Gp);
+          xch_wave(g, G, Gp);
+        }
+      }
+    }
+    store(a.out, r, G0, g);
+  }
+
+  float* part = a.part + size_t(cb) * L * half;
+#pragma unroll
+  for (int G = 0; G < 4; ++G)
+#pragma unroll
+    for (int ti = 0; ti < 3; ++ti)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (G < 3 || ti < 2) {
+          const int t = G < 3 ? 3 * G + ti : 9 + ti;
+          part[t * half + pair_of(elem(G, pair_lo(k, jbit(G, ti))), t)] = acc[G][ti][k];
+        }
+}
+
 template <int S, int HIGH, int TR, int A0, int A1, int AO, int BWD>
 static hipError_t bp_launch(const BflyPartArgs& a, hipStream_t s) {
   if constexpr (HIGH) {
@@ -746,7 +923,17 @@ static int bp_chunk(int rows) {
   return 32 * k;
 }
 
-static int bwd_chunk(int log2n, int rows) { return log2n >= 12 ? bp_chunk(rows) : bfly_bwd_chunk(log2n, rows); }
+// rows per chunk at width 2048 (one workgroup per chunk): a multiple of 16, at
+// most 128, about 1024 chunks or more
+static int row11_chunk(int rows) {
+  int k = rows / (16 * 1024);
+  k = k < 1 ? 1 : k > 8 ? 8 : k;
+  return 16 * k;
+}
+
+static int bwd_chunk(int log2n, int rows) {
+  return log2n >= 12 ? bp_chunk(rows) : log2n == 11 ? row11_chunk(rows) : bfly_bwd_chunk(log2n, rows);
+}
 
 size_t bfly_bwd_workspace(int log2n, int n_experts, int rows) {
   if (rows <= 0) return 0;
@@ -787,8 +974,7 @@ static hipError_t bb_launch_act(const BflyBwdArgs& a, int L, hipStream_t s) {
     case 8: return bb_launch<8, ACT>(a, s);
     case 9: return bb_launch<9, ACT>(a, s);
     case 10: return bb_launch<10, ACT>(a, s);
-    case 11: return bb_launch<11, ACT>(a, s);
-    default: return hipErrorInvalidValue;  // widths of 4096 and more take the part passes
+    default: return hipErrorInvalidValue;  // width 2048 and more take the register kernels
   }
 }
 
@@ -813,6 +999,20 @@ hipError_t launch_bfly_bwd(const void* x, const void* dy, void* dx, const float*
       err = tr ? (bf ? bp_run<9, 1, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<9, 1, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s))
                : (bf ? bp_run<9, 0, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<9, 0, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s));
     }
+    if (err != hipSuccess) return err;
+  } else if (rows > 0 && L == 11) {
+    a.chunk = row11_chunk(rows);
+    a.n_chunks = (rows + a.chunk - 1) / a.chunk + n_experts;
+    const BflyPartArgs pa{x, dy, dx, ang, offsets, part, rows, n_experts, a.chunk, a.n_chunks};
+    const bool bf = act == ACT_BF16, tr = transpose != 0;
+    if (tr) {
+      if (bf) hipLaunchKernelGGL((bfly_row11_kernel<1, ACT_BF16>), dim3(a.n_chunks), dim3(256), 0, s, pa);
+      else hipLaunchKernelGGL((bfly_row11_kernel<1, ACT_F32>), dim3(a.n_chunks), dim3(256), 0, s, pa);
+    } else {
+      if (bf) hipLaunchKernelGGL((bfly_row11_kernel<0, ACT_BF16>), dim3(a.n_chunks), dim3(256), 0, s, pa);
+      else hipLaunchKernelGGL((bfly_row11_kernel<0, ACT_F32>), dim3(a.n_chunks), dim3(256), 0, s, pa);
+    }
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   } else if (rows > 0) {
     a.chunk = bfly_bwd_chunk(log2n, rows);

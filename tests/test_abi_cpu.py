@@ -308,11 +308,14 @@ def test_butterfly_backward_arguments():
             ch = 32 * min(max(rows // 8192, 1), 4)
             up = lambda v: -(-v // 256) * 256
             return up((-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4) + 2 * up(rows * (4 << log2n))
+        if log2n == 11:  # one pass, chunks of a multiple of 16 rows
+            ch = 16 * min(max(rows // 16384, 1), 8)
+            return (-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4
         rt = min(64, 8192 >> log2n) if log2n <= 9 else 16384 >> log2n
         ch = rt * min(max(rows // (rt * 512), 1), max(256 // rt, 1))
         return (-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4
 
-    for args in ((9, 8, 300), (9, 8, 500000), (8, 3, 70000), (13, 2, 5), (11, 256, 65536), (9, 64, 8192), (13, 256, 65536), (12, 7, 200000),
+    for args in ((9, 8, 300), (9, 8, 500000), (8, 3, 70000), (11, 9, 300000), (10, 4, 9000), (13, 2, 5), (11, 256, 65536), (9, 64, 8192), (13, 256, 65536), (12, 7, 200000),
                  (2, 3, 100000)):
         assert L.bmoe_butterfly_backward_workspace(*args, ctypes.byref(n)) == 0
         assert n.value == want(*args), args

@@ -82,6 +82,7 @@ CASES = [
     (13, 2, 5, ()),
     (7, 4, 1300, ()),    # experts of several chunks
     (9, 4, 40000, (2,)), # chunks of two 32-row sub-tiles
+    (11, 5, 2500, (2,)), # width 2048 in one pass: 16-row chunks, ragged tails
     (12, 4, 700, (1,)),  # width 4096 in part passes: several 32-row chunks, ragged tails
     (13, 3, 150, ()),    # width 8192 in part passes
 ]
@@ -105,6 +106,7 @@ def test_butterfly_backward_in_place_and_zero_rows():
     import torch
     check_case(9, 4, 130, True, "f32", seed=5, inplace=True)
     check_case(12, 2, 90, False, "bf16", seed=6, inplace=True)  # part passes
+    check_case(11, 3, 150, True, "f32", seed=8, inplace=True)   # one-pass width 2048
     # no rows: every expert's angle gradients are zero, no row buffer touched
     ang = torch.randn(3, 5, 16, device="cuda")
     off = torch.zeros(4, dtype=torch.int32, device="cuda")
