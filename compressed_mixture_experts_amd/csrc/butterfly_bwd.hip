@@ -412,6 +412,32 @@ __device__ __forceinline__ void bp_chunk_info(const BflyPartArgs& a, int cb, int
   __syncthreads();
 }
 
+// the same for the wave's own chunk cb, without LDS or barriers: the lane
+// that finds it broadcasts it (at most one expert owns an index)
+__device__ __forceinline__ void bp_wave_chunk(const BflyPartArgs& a, int cb, int& e, int& c0, int& ccnt) {
+  const int lane = threadIdx.x & 63, CH = a.chunk;
+  int fe = -1, f0 = 0, fc = 0;
+  for (int x = lane; x < a.n_experts; x += 64) {
+    const int off = min(max(a.offsets[x], 0), a.rows);
+    const int cnt = min(max(a.offsets[x + 1], off), a.rows) - off;
+    const int base = off / CH + x, nt = (cnt + CH - 1) / CH;
+    if (cb >= base && cb < base + nt) {
+      fe = x;
+      f0 = off + (cb - base) * CH;
+      fc = min(CH, cnt - (cb - base) * CH);
+    }
+  }
+  const unsigned long long m = __ballot(fe >= 0);
+  if (m == 0) {
+    e = -1;
+    return;
+  }
+  const int src = __ffsll(m) - 1;
+  e = __shfl(fe, src);
+  c0 = __shfl(f0, src);
+  ccnt = __shfl(fc, src);
+}
+
 // number of stage t's pair whose lower index is i
 __device__ __forceinline__ int pair_of(int i, int t) { return ((i >> (t + 1)) << t) | (i & ((1 << t) - 1)); }
 
@@ -441,9 +467,12 @@ __device__ __forceinline__ float bp_back(float& o0, float& o1, float& g0, float&
   return gb * a - ga * b;
 }
 
-// ---- low part: stages 0 .. S-1 on 2^S consecutive indices.  A wave owns a
-// 512-element slot of the row (one segment for S = 9, two for S = 8) and
-// walks the chunk's rows; a lane holds 8 elements of the slot whose index
+// ---- low part: stages 0 .. S-1 on 2^S consecutive indices of rows of 2^LW
+// elements (LW = S + 4 for the split widths; LW = S = 9 for rows of 512, where
+// the low part is the whole butterfly).  A wave owns a 512-element slot of a
+// row (one segment for S = 9, two for S = 8) and walks the chunk's rows
+// (rows of 512: the four waves of a workgroup take every fourth row of one
+// chunk and add their angle gradients in LDS, in wave order, at the end); a lane holds 8 elements of the slot whose index
 // differs in three bits, so three stages run in registers between exchanges.
 // Layout G (G = 0, 1, 2) puts the 3 bits at base bit BB(G) = 0, 3, and 6
 // (S = 9) or 5 (S = 8; its stages are 6 and 7, the lowest bit is stage 5,
@@ -463,20 +492,33 @@ struct BpLow {
   static __device__ __forceinline__ int swz(int e) { return e ^ (((e >> 6) & 7) << 3); }
 };
 
-template <int S, int TR, int A0, int A1, int AO, int BWD>
+template <int S, int LW, int TR, int A0, int A1, int AO, int BWD>
 __global__ __launch_bounds__(256) void bfly_low_kernel(BflyPartArgs a) {
   using P = BpLow<S>;
-  constexpr int L = S + 4, n = 1 << L, half = n / 2;
-  constexpr int NSLOT = n / 512, BPC = NSLOT / 4;  // slots per row, workgroups per chunk
+  constexpr int L = LW, n = 1 << L, half = n / 2;
+  constexpr int NSLOT = n / 512;                   // slots per row
+  constexpr bool SPLIT = NSLOT == 1;               // four waves share a chunk's rows
+  static_assert(SPLIT || NSLOT % 4 == 0, "slots per row");
   constexpr int G0 = TR ? 2 : 0, G2 = TR ? 0 : 2;   // first and last layout applied
   __shared__ __attribute__((aligned(16))) float xch[4][2][512];
   __shared__ int s_info[3];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int cb = blockIdx.x / BPC, slot = (blockIdx.x % BPC) * 4 + w;
-  bp_chunk_info(a, cb, s_info);
-  const int e = s_info[0];
-  if (e < 0) return;
-  const int c0 = s_info[1], ccnt = s_info[2];
+  int cb, slot, e, c0, ccnt;
+  if constexpr (SPLIT) {
+    cb = blockIdx.x;
+    slot = 0;
+    bp_chunk_info(a, cb, s_info);
+    e = s_info[0];
+    if (e < 0) return;
+    c0 = s_info[1];
+    ccnt = s_info[2];
+  } else {
+    const int unit = blockIdx.x * 4 + w;
+    cb = unit / NSLOT;
+    slot = unit % NSLOT;
+    bp_wave_chunk(a, cb, e, c0, ccnt);
+    if (e < 0) return;
+  }
   const float* ang = a.ang + size_t(e) * L * half;
   const int sbase = slot * 512;
   float* XV = xch[w][0];
@@ -567,19 +609,23 @@ __global__ __launch_bounds__(256) void bfly_low_kernel(BflyPartArgs a) {
   using C1 = std::integral_constant<int, A1>;
   using CO = std::integral_constant<int, AO>;
 
+  constexpr int RSTEP = SPLIT ? 4 : 1;
+  const int rend = c0 + ccnt;
   float xn[8], gn[8];  // next row's inputs, loaded while this row is worked on
-  load(C0(), a.in0, c0, G0, xn);
-  if constexpr (BWD) load(C1(), a.in1, c0, G2, gn);
-  for (int r = c0; r < c0 + ccnt; ++r) {
+  if (c0 + (SPLIT ? w : 0) < rend) {
+    load(C0(), a.in0, c0 + (SPLIT ? w : 0), G0, xn);
+    if constexpr (BWD) load(C1(), a.in1, c0 + (SPLIT ? w : 0), G2, gn);
+  }
+  for (int r = c0 + (SPLIT ? w : 0); r < rend; r += RSTEP) {
     float x[8], g[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       x[j] = xn[j];
       if constexpr (BWD) g[j] = gn[j];
     }
-    if (r + 1 < c0 + ccnt) {
-      load(C0(), a.in0, r + 1, G0, xn);
-      if constexpr (BWD) load(C1(), a.in1, r + 1, G2, gn);
+    if (r + RSTEP < rend) {
+      load(C0(), a.in0, r + RSTEP, G0, xn);
+      if constexpr (BWD) load(C1(), a.in1, r + RSTEP, G2, gn);
     }
     // forward: groups in the order of application
 #pragma unroll
@@ -607,16 +653,28 @@ __global__ __launch_bounds__(256) void bfly_low_kernel(BflyPartArgs a) {
 
   if constexpr (BWD) {
     float* part = a.part + size_t(cb) * L * half;
+    float* red = &xch[0][0][0];  // 4 waves x 1024 floats
 #pragma unroll
-    for (int G = 0; G < 3; ++G)
+    for (int G = 0; G < 3; ++G) {
+      if constexpr (SPLIT) {
+        __syncthreads();  // every wave is past its rows (or the previous group)
+#pragma unroll
+        for (int ti = 0; ti < 3; ++ti)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (ti < P::nst(G)) red[w * 1024 + (ti * 4 + k) * 64 + lane] = acc[G][ti][k];
+        __syncthreads();
+      }
 #pragma unroll
       for (int ti = 0; ti < 3; ++ti)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (ti < P::nst(G)) {
-            const int t = P::first(G) + ti, p = t - P::bb(G);
-            part[t * half + pair_of(sbase + P::elem(G, lane, pair_lo(k, p)), t)] = acc[G][ti][k];
+          if (ti < P::nst(G) && (!SPLIT || w == 0)) {
+            const int t = P::first(G) + ti, p = t - P::bb(G), q = (ti * 4 + k) * 64 + lane;
+            const float v = SPLIT ? ((red[q] + red[1024 + q]) + red[2048 + q]) + red[3072 + q] : acc[G][ti][k];
+            part[t * half + pair_of(sbase + P::elem(G, lane, pair_lo(k, p)), t)] = v;
           }
+    }
   }
 }
 
@@ -888,7 +946,7 @@ static hipError_t bp_launch(const BflyPartArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bfly_high_kernel<S, TR, A0, A1, AO, BWD>), dim3(a.n_chunks * ((1 << S) / 256)), dim3(256),
                        0, s, a);
   } else {
-    hipLaunchKernelGGL((bfly_low_kernel<S, TR, A0, A1, AO, BWD>), dim3(a.n_chunks * ((1 << (S + 4)) / 2048)),
+    hipLaunchKernelGGL((bfly_low_kernel<S, S + 4, TR, A0, A1, AO, BWD>), dim3(a.n_chunks * ((1 << (S + 4)) / 2048)),
                        dim3(256), 0, s, a);
   }
   return hipGetLastError();
@@ -931,8 +989,18 @@ static int row11_chunk(int rows) {
   return 16 * k;
 }
 
+// rows per chunk at width 512 (one workgroup per chunk): 8 .. 64, about 512
+// chunks
+static int row9_chunk(int rows) {
+  const int k = rows / 512;
+  return k < 8 ? 8 : k > 64 ? 64 : k;
+}
+
 static int bwd_chunk(int log2n, int rows) {
-  return log2n >= 12 ? bp_chunk(rows) : log2n == 11 ? row11_chunk(rows) : bfly_bwd_chunk(log2n, rows);
+  return log2n >= 12 ? bp_chunk(rows)
+       : log2n == 11 ? row11_chunk(rows)
+       : log2n == 9  ? row9_chunk(rows)
+                     : bfly_bwd_chunk(log2n, rows);
 }
 
 size_t bfly_bwd_workspace(int log2n, int n_experts, int rows) {
@@ -972,7 +1040,6 @@ static hipError_t bb_launch_act(const BflyBwdArgs& a, int L, hipStream_t s) {
     case 6: return bb_launch<6, ACT>(a, s);
     case 7: return bb_launch<7, ACT>(a, s);
     case 8: return bb_launch<8, ACT>(a, s);
-    case 9: return bb_launch<9, ACT>(a, s);
     case 10: return bb_launch<10, ACT>(a, s);
     default: return hipErrorInvalidValue;  // width 2048 and more take the register kernels
   }
@@ -999,6 +1066,20 @@ hipError_t launch_bfly_bwd(const void* x, const void* dy, void* dx, const float*
       err = tr ? (bf ? bp_run<9, 1, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<9, 1, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s))
                : (bf ? bp_run<9, 0, ACT_BF16>(pa, x, dy, dx, zbuf, dzbuf, s) : bp_run<9, 0, ACT_F32>(pa, x, dy, dx, zbuf, dzbuf, s));
     }
+    if (err != hipSuccess) return err;
+  } else if (rows > 0 && L == 9) {
+    a.chunk = row9_chunk(rows);
+    a.n_chunks = (rows + a.chunk - 1) / a.chunk + n_experts;
+    const BflyPartArgs pa{x, dy, dx, ang, offsets, part, rows, n_experts, a.chunk, a.n_chunks};
+    const dim3 grid(a.n_chunks);
+    if (transpose) {
+      if (act == ACT_BF16) hipLaunchKernelGGL((bfly_low_kernel<9, 9, 1, ACT_BF16, ACT_BF16, ACT_BF16, 1>), grid, dim3(256), 0, s, pa);
+      else hipLaunchKernelGGL((bfly_low_kernel<9, 9, 1, ACT_F32, ACT_F32, ACT_F32, 1>), grid, dim3(256), 0, s, pa);
+    } else {
+      if (act == ACT_BF16) hipLaunchKernelGGL((bfly_low_kernel<9, 9, 0, ACT_BF16, ACT_BF16, ACT_BF16, 1>), grid, dim3(256), 0, s, pa);
+      else hipLaunchKernelGGL((bfly_low_kernel<9, 9, 0, ACT_F32, ACT_F32, ACT_F32, 1>), grid, dim3(256), 0, s, pa);
+    }
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   } else if (rows > 0 && L == 11) {
     a.chunk = row11_chunk(rows);

@@ -81,7 +81,8 @@ CASES = [
     (12, 3, 9, (0,)),
     (13, 2, 5, ()),
     (7, 4, 1300, ()),    # experts of several chunks
-    (9, 4, 40000, (2,)), # chunks of two 32-row sub-tiles
+    (9, 4, 40000, (2,)), # width 512, chunks of 64 rows
+    (9, 7, 900, (0, 4)), # width 512, 8-row chunks, ragged tails
     (11, 5, 2500, (2,)), # width 2048 in one pass: 16-row chunks, ragged tails
     (12, 4, 700, (1,)),  # width 4096 in part passes: several 32-row chunks, ragged tails
     (13, 3, 150, ()),    # width 8192 in part passes
