@@ -386,3 +386,20 @@ def ternary_product(U: np.ndarray, w_base: np.ndarray, alpha: float = 1.0) -> np
     routed row goes through ([MoE-zh] §2.1: rotated input times the ternary
     substrate).  U [M][d_in], W_base [d_out][d_in]."""
     return alpha * (np.asarray(U, dtype=np.float64) @ np.asarray(w_base, dtype=np.float64).T)
+
+
+def substrate_weight_grad(U: np.ndarray, dZ: np.ndarray, alpha: float = 1.0) -> np.ndarray:
+    """Gradient of the latent full-precision substrate, fp64.
+
+    The substrate is trained with a straight-through estimator ([MoE-nl] §2
+    "Drie Fasen": ternary quantisation with STE; [MoE-zh] §2.2): the forward
+    uses the ternary codes, and the gradient passes through the quantiser
+    unchanged, so the latent weights receive the gradient of the product
+    Z = alpha U W^T with respect to W.  The substrate is shared by every expert,
+    so the sum runs over all routed rows of all experts:
+        dW[o][i] = alpha * sum_r dZ[r][o] U[r][i]
+    U [R][d_in] (rows after the input rotation), dZ [R][d_out].  Returns
+    dW [d_out][d_in].  The reading takes the estimator as the plain identity
+    (no clipping of the latent weights' gradient): the pages name the
+    estimator and nothing more."""
+    return alpha * (np.asarray(dZ, dtype=np.float64).T @ np.asarray(U, dtype=np.float64))

@@ -343,3 +343,30 @@ def test_generator_stored_values():
     c4 = wl.CONFIGS[4]
     i4 = wl.generate(c4.with_tokens(8))
     assert len(i4.outlier_channels) == round(0.01 * 2048)
+
+
+def test_substrate_weight_grad_finite_differences_and_by_hand():
+    # dW against central differences of L(W) = sum(dZ * ternary_product(U, W))
+    # with W real-valued (the straight-through estimator passes the gradient of
+    # the product unchanged); non-square shapes catch a transposed operand
+    r = np.random.default_rng(41)
+    R, d_in, d_out, alpha = 4, 5, 3, 0.75
+    U = r.standard_normal((R, d_in))
+    dZ = r.standard_normal((R, d_out))
+    W = r.integers(-1, 2, size=(d_out, d_in)).astype(np.float64)
+    dW = ref.substrate_weight_grad(U, dZ, alpha)
+    assert dW.shape == (d_out, d_in)
+    h = 1e-6
+    for o in range(d_out):
+        for i in range(d_in):
+            wp, wm = W.copy(), W.copy()
+            wp[o, i] += h
+            wm[o, i] -= h
+            fd = (np.sum(dZ * ref.ternary_product(U, wp, alpha)) - np.sum(dZ * ref.ternary_product(U, wm, alpha))) / (2 * h)
+            assert abs(fd - dW[o, i]) < 1e-8 * (1 + abs(fd))
+    # two rows by hand: U = [[1, 2], [3, -1]], dZ = [[2], [-1]], alpha = 2
+    #   dW[0][0] = 2 (2*1 + (-1)*3) = -2,  dW[0][1] = 2 (2*2 + (-1)(-1)) = 10
+    got = ref.substrate_weight_grad(np.array([[1.0, 2.0], [3.0, -1.0]]), np.array([[2.0], [-1.0]]), 2.0)
+    assert np.array_equal(got, np.array([[-2.0, 10.0]]))
+    # no rows: zero gradient
+    assert not ref.substrate_weight_grad(np.zeros((0, 4)), np.zeros((0, 2))).any()
