@@ -309,8 +309,32 @@ def grad_measure(reps: int = 20) -> dict:
         by = 3 * rows * n * 2 + 2 * N * L * (n // 2) * 4
         out.append({"shape": name, "rows": rows, "width": n, "experts": N, "ms": round(ms, 4),
                     "hbm_gbps": round(by / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(by / (ms * 1e-3) / 8e12, 4)})
-    return {"measurement": "butterfly backward (input and angle gradients)", "dtype": "bf16 rows, fp32 angles",
-            "shapes": out}
+    # the substrate's latent gradient (straight-through): dW = alpha dZ^T U over
+    # all routed rows; flops 2 rows d_out d_in against the bf16 MFMA peak
+    sg = []
+    for name, rows, d_out, d_in in (("edge_d512_n64 substrate", 16384, 512, 512),
+                                    ("large_d2048_n256 ffn up substrate", 65536, 8192, 2048),
+                                    ("large_d2048_n256 ffn down substrate", 65536, 2048, 8192)):
+        g = torch.Generator(device="cuda").manual_seed(12)
+        dz = torch.randn((rows, d_out), device="cuda", generator=g).to(torch.bfloat16)
+        u = torch.randn((rows, d_in), device="cuda", generator=g).to(torch.bfloat16)
+        dw = torch.empty((d_out, d_in), device="cuda")
+        for _ in range(3):
+            bm.substrate_grad(dz, u, 1.0, dw=dw)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(reps):
+            bm.substrate_grad(dz, u, 1.0, dw=dw)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / reps
+        tf = 2.0 * rows * d_out * d_in / (ms * 1e-3) / 1e12
+        sg.append({"shape": name, "rows": rows, "d_out": d_out, "d_in": d_in, "ms": round(ms, 4),
+                   "tflops": round(tf, 1), "mfma_frac": round(tf / 2500.0, 4)})
+        del dz, u, dw
+    return {"measurement": "butterfly backward (input and angle gradients); substrate weight gradient",
+            "dtype": "bf16 rows, fp32 angles and weight gradients", "shapes": out, "substrate": sg}
 
 
 def main() -> int:

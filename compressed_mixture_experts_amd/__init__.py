@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
-    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "STATUS",
+    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad", "STATUS",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = [
     "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
     "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
     "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
+    "bmoe_substrate_grad_workspace", "bmoe_substrate_grad",
 ]
 
 
@@ -105,10 +106,13 @@ def lib() -> ctypes.CDLL:
     L.bmoe_butterfly_backward_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
     L.bmoe_butterfly_backward.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_sz, c_vp]
+    L.bmoe_substrate_grad_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_substrate_grad.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp, c_sz, c_vp]
     for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
                  "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
                  "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
-                 "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward"):
+                 "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
+                 "bmoe_substrate_grad_workspace", "bmoe_substrate_grad"):
         getattr(L, name).restype = c_i32
     _lib = L
     return L
@@ -337,6 +341,22 @@ def butterfly_backward(angles, offsets, x, dy, transpose: bool = False, dx=None)
                                          _ptr(x), _ptr(dy), _ptr(dx), _ptr(dang), _ptr(ws), int(nb.value),
                                          _stream_handle()))
     return dx, dang
+
+
+def substrate_grad(dz, u, alpha: float = 1.0, dw=None):
+    """Latent substrate gradient through the straight-through estimator:
+    dw [d_out][d_in] fp32 = alpha * dz^T u over all rows; dz [rows][d_out] and
+    u [rows][d_in] bf16."""
+    torch = _torch()
+    rows, d_out, d_in = int(dz.shape[0]), int(dz.shape[1]), int(u.shape[1])
+    if dw is None:
+        dw = torch.empty((d_out, d_in), dtype=torch.float32, device=dz.device)
+    nb = ctypes.c_size_t(0)
+    _check(lib().bmoe_substrate_grad_workspace(d_out, d_in, rows, ctypes.byref(nb)))
+    ws = torch.empty(max(int(nb.value), 16), dtype=torch.uint8, device=dz.device)
+    _check(lib().bmoe_substrate_grad(d_out, d_in, rows, BF16 if dz.dtype == torch.bfloat16 else F32, _ptr(dz),
+                                     _ptr(u), float(alpha), _ptr(dw), _ptr(ws), int(nb.value), _stream_handle()))
+    return dw
 
 
 def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):

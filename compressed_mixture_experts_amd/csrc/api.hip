@@ -830,3 +830,49 @@ const char* bmoe_status_string(bmoe_status s) {
 const char* bmoe_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- substrate weight gradient
+static bmoe_status check_sgrad_shape(int32_t d_out, int32_t d_in, int32_t rows) {
+  if (d_out < 128 || d_out > 16384 || d_in < 128 || d_in > 16384 || !sgrad_shape_ok(d_out, d_in))
+    return fail(BMOE_ERR_SHAPE, "d_out=%d, d_in=%d: each must be a multiple of 128 in [128, 16384]", d_out, d_in);
+  const int32_t d = d_out > d_in ? d_out : d_in;
+  if (rows < 0 || int64_t(rows) * d > (int64_t(1) << 31) - 1)
+    return fail(BMOE_ERR_SHAPE, "rows=%d: must be >= 0 with rows * max(d_out, d_in) below 2^31", rows);
+  return BMOE_OK;
+}
+
+bmoe_status bmoe_substrate_grad_workspace(int32_t d_out, int32_t d_in, int32_t rows, size_t* bytes) {
+  if (!bytes) return fail(BMOE_ERR_NULL, "bytes is NULL");
+  const bmoe_status st = check_sgrad_shape(d_out, d_in, rows);
+  if (st != BMOE_OK) return st;
+  *bytes = sgrad_workspace(d_out, d_in, rows);
+  return ok();
+}
+
+bmoe_status bmoe_substrate_grad(int32_t d_out, int32_t d_in, int32_t rows, int32_t dtype, const void* dz,
+                                const void* u, float alpha, float* dw, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  bmoe_status st = check_sgrad_shape(d_out, d_in, rows);
+  if (st != BMOE_OK) return st;
+  if (dtype != BMOE_BF16)
+    return fail(BMOE_ERR_DTYPE, "dtype=%d: the substrate gradient takes bf16 rows only", dtype);
+  if (!dw) return fail(BMOE_ERR_NULL, "dw is NULL");
+  if (rows > 0 && (!dz || !u)) return fail(BMOE_ERR_NULL, "dz / u is NULL");
+  const size_t need = sgrad_workspace(d_out, d_in, rows);
+  if (need > 0 && !workspace) return fail(BMOE_ERR_NULL, "workspace is NULL");
+  if (!aligned(dw, 16)) return fail(BMOE_ERR_ALIGN, "dw must be 16-byte aligned");
+  if (rows > 0 && (!aligned(dz, 16) || !aligned(u, 16))) return fail(BMOE_ERR_ALIGN, "dz and u must be 16-byte aligned");
+  if (need > 0 && !aligned(workspace, 16)) return fail(BMOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(BMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const Range rw{dw, size_t(d_out) * d_in * 4}, rz{dz, size_t(rows) * d_out * 2}, ru{u, size_t(rows) * d_in * 2},
+      rws{workspace, need};
+  if ((rows > 0 && (overlap(rw, rz) || overlap(rw, ru))) || overlap(rw, rws))
+    return fail(BMOE_ERR_ALIAS, "dw overlaps an input or the workspace");
+  if (need > 0 && rows > 0 && (overlap(rws, rz) || overlap(rws, ru)))
+    return fail(BMOE_ERR_ALIAS, "the workspace overlaps an input");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+  BMOE_HIP(launch_sgrad(dz, u, alpha, dw, static_cast<float*>(workspace), rows, d_out, d_in, stream));
+  return ok();
+}

@@ -241,6 +241,11 @@ hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 // Backward of a bucketed butterfly pass (butterfly_bwd.hip): workspace bytes and launch.
 size_t bfly_bwd_workspace(int log2n, int n_experts, int rows);
+bool sgrad_shape_ok(int M, int N);
+int sgrad_splits(int M, int N, int R, int* kchunk);
+size_t sgrad_workspace(int M, int N, int R);
+hipError_t launch_sgrad(const void* dz, const void* u, float alpha, float* out, float* part, int R, int M, int N,
+                        hipStream_t s);
 hipError_t launch_bfly_bwd(const void* x, const void* dy, void* dx, const float* ang, const int32_t* offsets,
                            float* part, float* dang, int rows, int n_experts, int log2n, int transpose, int act,
                            hipStream_t s);

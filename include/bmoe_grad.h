@@ -56,6 +56,33 @@ bmoe_status bmoe_butterfly_backward(int32_t log2n, int32_t n_experts, int32_t ro
                                     float* dangles, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* Gradient of the latent substrate weights through the straight-through
+ * estimator (ButterflyMoE, gist.science/nl/paper/2601.13563, §2 "Drie
+ * Fasen"; gist.science/zh/paper/2601.13563, technical summary §2.2): the
+ * estimator passes the gradient of Z = alpha U W^T through the ternary
+ * quantiser unchanged, and the substrate is shared by all experts, so
+ *     dw[o][i] = alpha * sum over rows r of dz[r][o] * u[r][i].
+ *   dz   [rows][d_out] bf16 (device, 16-byte aligned): gradient at the
+ *        substrate product's output, read only.
+ *   u    [rows][d_in] bf16 (device, 16-byte aligned): the product's input (rows after the
+ *        input rotation), read only; rows in any order, the same for both.
+ *   dw   [d_out][d_in] fp32 (device, 16-byte aligned), overwritten (zero for
+ *        rows = 0).
+ *   workspace at least bmoe_substrate_grad_workspace bytes (device, 16-byte
+ *        aligned; 0 when the output tiles fill the GPU without splitting the
+ *        rows), caller-owned scratch for per-split partial sums.
+ * d_out and d_in are multiples of 128 in [128, 16384].  The result does not
+ * depend on scheduling (splits are added in order).  Enqueued on `stream`;
+ * nothing is allocated or synchronised.  Errors: BMOE_ERR_SHAPE,
+ * BMOE_ERR_DTYPE (dtype other than BMOE_BF16), BMOE_ERR_NULL, BMOE_ERR_ALIGN,
+ * BMOE_ERR_ALIAS (dw or the workspace overlaps an input, or each other),
+ * BMOE_ERR_WORKSPACE, BMOE_ERR_HIP; all but the last are detected before
+ * anything is enqueued. */
+bmoe_status bmoe_substrate_grad_workspace(int32_t d_out, int32_t d_in, int32_t rows, size_t* bytes);
+bmoe_status bmoe_substrate_grad(int32_t d_out, int32_t d_in, int32_t rows, int32_t dtype, const void* dz,
+                                const void* u, float alpha, float* dw, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -345,3 +345,48 @@ def test_butterfly_backward_arguments():
     assert call(dx=x + 64) == 5                # dx partly over x
     assert call(dang=ang + 4) == 5             # dangles over the angles
     assert call(ws=x) == 5                     # workspace over an input
+
+
+def test_substrate_grad_arguments():
+    L = bm.lib()
+    n = ctypes.c_size_t(0)
+
+    def want(d_out, d_in, rows):
+        # splits of the rows: none when the 128 x 128 output tiles number 256 or more,
+        # else about 512 workgroups with at least 512 rows each (32-row steps)
+        if rows == 0:
+            return 0
+        tiles = (d_out // 128) * (d_in // 128)
+        ns = 1
+        if tiles < 256:
+            ns = max(1, min(-(-512 // tiles), -(-rows // 512)))
+        kc = max(32, -(-(-(-rows // ns)) // 32) * 32)
+        ns = max(1, -(-rows // kc))
+        return ns * d_out * d_in * 4 if ns > 1 else 0
+
+    for args in ((512, 512, 16384), (512, 512, 100), (2048, 8192, 65536), (8192, 2048, 65536), (128, 256, 7),
+                 (1024, 1024, 1 << 20), (128, 128, 0)):
+        assert L.bmoe_substrate_grad_workspace(*args, ctypes.byref(n)) == 0
+        assert n.value == want(*args), args
+    for args in ((100, 512, 10), (512, 0, 10), (512, 32768, 10), (512, 512, -1), (8192, 512, 1 << 20)):
+        assert L.bmoe_substrate_grad_workspace(*args, ctypes.byref(n)) == 2, args
+    assert L.bmoe_substrate_grad_workspace(512, 512, 10, None) == 1
+
+    F = FAKE
+    dz, u, dw, ws = F + 0x100000, F + 0x200000, F + 0x300000, F + 0x400000
+    need = want(512, 512, 1000)
+
+    def call(d_out=512, d_in=512, rows=1000, dt=bm.BF16, dz=dz, u=u, dw=dw, ws=ws, wsb=need):
+        return L.bmoe_substrate_grad(d_out, d_in, rows, dt, dz, u, ctypes.c_float(1.0), dw, ws, wsb, None)
+
+    assert need > 0
+    assert call(d_out=200) == 2
+    assert call(dt=bm.F32) == 3 and call(dt=9) == 3   # bf16 rows only
+    assert call(dz=None) == 1 and call(u=None) == 1 and call(dw=None) == 1 and call(ws=None) == 1
+    assert call(dw=dw + 4) == 4                       # dw 16-byte aligned
+    assert call(dz=dz + 1) == 4 and call(u=u + 8) == 4   # rows 16-byte aligned
+    assert call(ws=ws + 8) == 4
+    assert call(wsb=need - 1) == 6
+    assert call(dw=dz + 64) == 5                      # dw over dz
+    assert call(ws=u) == 5                            # workspace over u
+    assert call(ws=dw + 256) == 5                     # workspace over dw

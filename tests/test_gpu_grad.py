@@ -147,7 +147,13 @@ def test_expert_angle_gradients_compose():
     dZ, dph = bm.butterfly_backward(phd, offd, Z, dyd, False)
     dU = bm.dbg_ternary_gemm(dZ, WTp, d, alpha)
     dx, dth = bm.butterfly_backward(thd, offd, xd, dU, True)
+    # the substrate's latent gradient (straight-through) from bf16 copies of U and dZ
+    U16, dZ16 = U.to(torch.bfloat16), dZ.to(torch.bfloat16)
+    dW = bm.substrate_grad(dZ16, U16, alpha)
     torch.cuda.synchronize()
+    dWr = ref.substrate_weight_grad(U16.float().cpu().numpy().astype(np.float64),
+                                    dZ16.float().cpu().numpy().astype(np.float64), alpha)
+    assert np.linalg.norm(dW.cpu().numpy() - dWr) <= 1e-5 * np.linalg.norm(dWr)
     dx, dth, dph = (t.cpu().numpy().astype(np.float64) for t in (dx, dth, dph))
     W64 = W.astype(np.float64)
     for e in range(N):
@@ -178,3 +184,28 @@ def test_expert_angle_gradients_compose():
                     pm[s_, q] -= h
                 fd = (loss(tp, pp) - loss(tm, pm)) / (2 * h)
                 assert abs(fd - grad[s_, q]) <= 1e-6 * (1 + abs(fd))
+    # the oracle's substrate gradient over all rows (fp64 chain) against central
+    # differences of the summed loss of every expert in one substrate entry
+    Ur = np.zeros((R, d))
+    dZr_all = np.zeros((R, d))
+    for e in range(N):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        X = x[r0:r1].T.astype(np.float64)
+        Ue = ref.butterfly_apply(th[e].astype(np.float64), X, transpose=True)
+        dZe, _ = ref.butterfly_backward(ph[e].astype(np.float64), alpha * (W64 @ Ue), dy[r0:r1].T.astype(np.float64), False)
+        Ur[r0:r1], dZr_all[r0:r1] = Ue.T, dZe.T
+    dW64 = ref.substrate_weight_grad(Ur, dZr_all, alpha)
+
+    def total_loss(Wm):
+        return sum(float(np.sum(dy[off[e]:off[e + 1]].T.astype(np.float64) *
+                                ref.expert_apply(th[e].astype(np.float64), ph[e].astype(np.float64), Wm,
+                                                 x[off[e]:off[e + 1]].T.astype(np.float64), alpha)))
+                   for e in range(N) if off[e + 1] > off[e])
+    for (o, i) in ((0, 0), (17, 200), (255, 3)):
+        wp, wm = W64.copy(), W64.copy()
+        wp[o, i] += 1e-6
+        wm[o, i] -= 1e-6
+        fd = (total_loss(wp) - total_loss(wm)) / 2e-6
+        assert abs(fd - dW64[o, i]) <= 1e-6 * (1 + abs(fd))
