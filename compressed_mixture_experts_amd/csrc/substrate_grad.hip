@@ -12,17 +12,18 @@
 // 8 x 8 block (8 rows of 8 consecutive columns, eight 16-byte loads),
 // transposes it in registers and writes 8 columns of 8 rows as 16-byte runs;
 // the fragments are then 16-byte LDS reads.  Lane l of a wave takes row block
-// l % 8 and column block l / 8 (+ 8 for the odd wave of an operand), so the 16
-// lanes of an LDS write phase cover all banks.  Workgroup tile: 128 x 128
-// outputs, four waves of 64 x 64 (4 x 4 blocks); the next step's loads are in
-// flight while the current step multiplies, two LDS buffers.  Few output tiles
+// l % 8 and column block l / 8 (+ 8 per earlier wave of its operand), so the
+// 16 lanes of an LDS write phase cover all banks.  Workgroup tile: T x T
+// outputs with T = 128 (four waves of 64 x 64) or, where the tiles still fill
+// the GPU, T = 256 (eight waves of 128 x 64, one workgroup per CU: twice the
+// products per loaded byte, the loads being the limit); the next step's loads
+// are in flight while the current step multiplies, two LDS buffers.  Few output tiles
 // (small d) split K: each split writes an fp32 partial tile and a second
 // kernel adds the splits in order (deterministic), times alpha.
 #include "common.hpp"
 
 namespace bmoe {
 
-constexpr int SG_T = 128;   // output tile edge
 constexpr int SG_KT = 64;   // rows per step (two MFMA K)
 constexpr int SG_RS = 72;   // LDS row stride in bf16: 64 rows + 8 (144 bytes)
 
@@ -35,16 +36,21 @@ struct SgradArgs {
   int32_t R, M, N, kchunk, nsplit;
 };
 
-__global__ __launch_bounds__(256, 2) void sgrad_kernel(SgradArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sm[2][2][SG_T * SG_RS];  // [buffer][dZ, U][col][row]
+template <int T>
+__global__ __launch_bounds__(2 * T, T == 128 ? 2 : 1) void sgrad_kernel(SgradArgs a) {
+  constexpr int NW = 2 * T / 64;      // waves
+  constexpr int WM = T / 2;           // rows (of dW) per wave: two waves along M
+  constexpr int IM = WM / 16;         // 16-row blocks per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sm[2][2][T * SG_RS];  // [buffer][dZ, U][col][row]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  const int tM = a.M / SG_T, tN = a.N / SG_T, tiles = tM * tN;
+  const int tM = a.M / T, tN = a.N / T, tiles = tM * tN;
   const int tile = blockIdx.x % tiles, split = blockIdx.x / tiles;
-  const int m0 = (tile % tM) * SG_T, n0 = (tile / tM) * SG_T;
+  const int m0 = (tile % tM) * T, n0 = (tile / tM) * T;
   const int k0 = split * a.kchunk, k1 = min(a.R, k0 + a.kchunk);
-  const int wm = wave & 1, wn = wave >> 1;
-  // loader: operand op (waves 0-1 dZ, 2-3 U), row block rb, column block cb
-  const int op = wave >> 1, rb = lane & 7, cb = (lane >> 3) + 8 * (wave & 1);
+  const int wm = wave & 1, wn = wave >> 1;  // wave's 64 columns: wn of T / 64
+  // loader: operand op (first half of the waves dZ, second U), row block rb,
+  // column block cb
+  const int op = wave / (NW / 2), rb = lane & 7, cb = (lane >> 3) + 8 * (wave % (NW / 2));
   const uint16_t* src = op ? a.u : a.dz;
   const int ld = op ? a.N : a.M, c0 = (op ? n0 : m0) + 8 * cb;
   uint4 blk[8];
@@ -74,9 +80,9 @@ __global__ __launch_bounds__(256, 2) void sgrad_kernel(SgradArgs a) {
     }
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[IM][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < IM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -93,14 +99,15 @@ __global__ __launch_bounds__(256, 2) void sgrad_kernel(SgradArgs a) {
     const uint16_t* B = sm[buf][1];
 #pragma unroll
     for (int ks = 0; ks < SG_KT / 32; ++ks) {
-      bf16x8_t fa[4], fb[4];
+      bf16x8_t fa[IM], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(A + (wm * 64 + 16 * i + l16) * SG_RS + 32 * ks + 8 * g);
-        fb[i] = *reinterpret_cast<const bf16x8_t*>(B + (wn * 64 + 16 * i + l16) * SG_RS + 32 * ks + 8 * g);
-      }
+      for (int i = 0; i < IM; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(A + (wm * WM + 16 * i + l16) * SG_RS + 32 * ks + 8 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        fb[i] = *reinterpret_cast<const bf16x8_t*>(B + (wn * 64 + 16 * i + l16) * SG_RS + 32 * ks + 8 * g);
+#pragma unroll
+      for (int i = 0; i < IM; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -110,16 +117,16 @@ __global__ __launch_bounds__(256, 2) void sgrad_kernel(SgradArgs a) {
     buf ^= 1;
   }
 
-  // acc[i][j][v] = C[m0 + 64 wm + 16 i + 4 g + v][n0 + 64 wn + 16 j + l16]
+  // acc[i][j][v] = C[m0 + WM wm + 16 i + 4 g + v][n0 + 64 wn + 16 j + l16]
   float* dst = a.nsplit > 1 ? a.part + size_t(split) * a.M * a.N : a.out;
   const float sc = a.nsplit > 1 ? 1.f : a.alpha;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < IM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int o = m0 + 64 * wm + 16 * i + 4 * g + v, n = n0 + 64 * wn + 16 * j + l16;
+        const int o = m0 + WM * wm + 16 * i + 4 * g + v, n = n0 + 64 * wn + 16 * j + l16;
         dst[size_t(o) * a.N + n] = sc * acc[i][j][v];
       }
 }
@@ -144,12 +151,18 @@ __global__ __launch_bounds__(256) void sgrad_zero_kernel(float* out, size_t n) {
   if (q < n) out[q] = 0.f;
 }
 
-bool sgrad_shape_ok(int M, int N) { return M % SG_T == 0 && N % SG_T == 0 && M > 0 && N > 0; }
+bool sgrad_shape_ok(int M, int N) { return M % 128 == 0 && N % 128 == 0 && M > 0 && N > 0; }
+
+// output tile edge: 256 where those tiles number at least 256 (one workgroup
+// per CU), else 128
+static int sgrad_tile(int M, int N) {
+  return (M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) >= 256) ? 256 : 128;
+}
 
 // splits of K: none when the output tiles alone fill the chip (>= 256),
 // else enough for about 512 workgroups with at least 512 rows each
 int sgrad_splits(int M, int N, int R, int* kchunk) {
-  const int tiles = (M / SG_T) * (N / SG_T);
+  const int T = sgrad_tile(M, N), tiles = (M / T) * (N / T);
   int ns = 1;
   if (tiles < 256) {
     ns = (512 + tiles - 1) / tiles;
@@ -181,8 +194,12 @@ hipError_t launch_sgrad(const void* dz, const void* u, float alpha, float* out, 
   }
   SgradArgs a{static_cast<const uint16_t*>(dz), static_cast<const uint16_t*>(u), out, part, alpha, R, M, N, 0, 0};
   a.nsplit = sgrad_splits(M, N, R, &a.kchunk);
-  const int tiles = (M / SG_T) * (N / SG_T);
-  hipLaunchKernelGGL(sgrad_kernel, dim3(tiles * a.nsplit), dim3(256), 0, s, a);
+  const int T = sgrad_tile(M, N), tiles = (M / T) * (N / T);
+  if (T == 256) {
+    hipLaunchKernelGGL(sgrad_kernel<256>, dim3(tiles * a.nsplit), dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(sgrad_kernel<128>, dim3(tiles * a.nsplit), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(sgrad_reduce_kernel, dim3((MN / 4 + 255) / 256), dim3(256), 0, s, a);

@@ -356,7 +356,8 @@ def test_substrate_grad_arguments():
         # else about 512 workgroups with at least 512 rows each (32-row steps)
         if rows == 0:
             return 0
-        tiles = (d_out // 128) * (d_in // 128)
+        t = 256 if d_out % 256 == 0 and d_in % 256 == 0 and (d_out // 256) * (d_in // 256) >= 256 else 128
+        tiles = (d_out // t) * (d_in // t)
         ns = 1
         if tiles < 256:
             ns = max(1, min(-(-512 // tiles), -(-rows // 512)))
@@ -365,6 +366,7 @@ def test_substrate_grad_arguments():
         return ns * d_out * d_in * 4 if ns > 1 else 0
 
     for args in ((512, 512, 16384), (512, 512, 100), (2048, 8192, 65536), (8192, 2048, 65536), (128, 256, 7),
+                 (4096, 4096, 300), (4096, 2048, 70000), (3968, 4096, 9000),
                  (1024, 1024, 1 << 20), (128, 128, 0)):
         assert L.bmoe_substrate_grad_workspace(*args, ctypes.byref(n)) == 0
         assert n.value == want(*args), args

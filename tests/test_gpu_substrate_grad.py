@@ -42,6 +42,7 @@ def _f64(t):
     (5000, 1024, 384, -2.0),   # ragged split lengths, non-square
     (33, 256, 128, 1.0),       # fewer rows than one step beyond the first
     (1, 128, 128, 3.0),
+    (300, 4096, 4096, 1.0),    # 256 x 256 output tiles (eight waves), ragged last step
 ])
 def test_substrate_grad_matches_oracle(rows, d_out, d_in, alpha):
     import torch
