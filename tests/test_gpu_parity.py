@@ -195,6 +195,31 @@ def test_route_skewed_and_tied():
     assert counts.max() > 1.5 * counts.mean()  # the load really is skewed
 
 
+def test_route_near_ties_top2():
+    # near ties resolved exactly: experts 9 and 20 carry expert 5's gate row
+    # with one element moved by one bf16 step, and the three rows are three
+    # times larger than the rest, so about a quarter of the tokens have two of
+    # them on top within the fp32 error bound, their order set by one product.
+    # About nine tokens of a 32-token tile are flagged: the first eight are
+    # re-ranked from the gate matrix in LDS, the rest through the global path.
+    import torch
+    cfg = wl.small_config(d_model=512, n_experts=64, top_k=2, tokens=3000, act="bf16", seed_index=9)
+    inp = wl.generate(cfg)
+    wg = ref.stored_to_f64(inp.w_gate, "bf16")
+    inp.w_gate[5] = wl.round_to_bf16_bits(3.0 * wg[5])
+    inp.w_gate[9] = inp.w_gate[5]
+    inp.w_gate[9, 17] ^= 1
+    inp.w_gate[20] = inp.w_gate[5]
+    inp.w_gate[20, 300] ^= 1
+    layer = bm.Layer.from_inputs(inp)
+    log("route near ties, top-2")
+    idx, gate, off, slots = layer.route(to_dev(inp.x, cfg.act), with_buckets=True)
+    torch.cuda.synchronize()
+    R = check_routing(inp, idx.cpu().numpy(), gate.cpu().numpy(), off.cpu().numpy(), slots.cpu().numpy())
+    top = np.isin(R.idx, [5, 9, 20]).all(axis=1)
+    assert top.mean() > 0.15 and not R.ambiguous[top].any()
+
+
 def test_route_buckets_beyond_one_round():
     # more routed slots than one bucketing round (65536): bucket bases must
     # count the slots of lower experts in every round
