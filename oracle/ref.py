@@ -388,6 +388,49 @@ def ternary_product(U: np.ndarray, w_base: np.ndarray, alpha: float = 1.0) -> np
     return alpha * (np.asarray(U, dtype=np.float64) @ np.asarray(w_base, dtype=np.float64).T)
 
 
+def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
+    """Gradients of L = sum(dy * y) through the experts of a square layer,
+    with the routing and the gates held at ``routing`` (they are piecewise
+    constant in the parameters for a fixed choice; the router's own gradient
+    is a separate step).  Follows the forward's definition per routed slot
+    (t, j) with expert e = idx[t][j] and gate g = gates[t][j]:
+        u = B(theta_e)^T x_t,  z = alpha W_base u,  o = B(phi_e) z,  y_t += g o
+    so the slot receives do = g dy_t, and the chain runs back through the
+    output rotation (dphi_e, dz), the substrate (dW_base through the
+    straight-through estimator, du = alpha W_base^T dz) and the input rotation
+    (dtheta_e, dx_t += its input gradient).  Also returns the gates'
+    gradients dgate[t][j] = dy_t . o.
+    Returns dict(theta, phi [N][L][n/2], w_base [d][d], x [T][d], gate [T][k])."""
+    cfg, x, _ = _inputs_f64(inp)
+    if cfg.is_ffn:
+        raise ValueError("square experts only")
+    dy = np.asarray(dy, dtype=np.float64)
+    alpha = cfg.w_scale
+    W = np.asarray(inp.w_base[0], dtype=np.float64)
+    th_all, ph_all = inp.theta[0], inp.phi[0]
+    dth = np.zeros(np.shape(th_all))
+    dph = np.zeros(np.shape(ph_all))
+    dW = np.zeros(W.shape)
+    dx = np.zeros(x.shape)
+    dgate = np.zeros(routing.gates.shape)
+    for e in np.unique(routing.idx):
+        tok, slot = np.nonzero(routing.idx == e)
+        th = np.asarray(th_all[e], dtype=np.float64)
+        ph = np.asarray(ph_all[e], dtype=np.float64)
+        X = x[tok].T                                     # columns = routed slots
+        U = butterfly_apply(th, X, transpose=True)
+        Z = alpha * (W @ U)
+        O = butterfly_apply(ph, Z)
+        dO = dy[tok].T * routing.gates[tok, slot][None, :]
+        dgate[tok, slot] = np.sum(dy[tok].T * O, axis=0)
+        dZ, dph[e] = butterfly_backward(ph, Z, dO, False)
+        dW += substrate_weight_grad(U.T, dZ.T, alpha)
+        dU = alpha * (W.T @ dZ)
+        dX, dth[e] = butterfly_backward(th, X, dU, True)
+        np.add.at(dx, tok, dX.T)
+    return {"theta": dth, "phi": dph, "w_base": dW, "x": dx, "gate": dgate}
+
+
 def substrate_weight_grad(U: np.ndarray, dZ: np.ndarray, alpha: float = 1.0) -> np.ndarray:
     """Gradient of the latent full-precision substrate, fp64.
 

@@ -370,3 +370,46 @@ def test_substrate_weight_grad_finite_differences_and_by_hand():
     assert np.array_equal(got, np.array([[-2.0, 10.0]]))
     # no rows: zero gradient
     assert not ref.substrate_weight_grad(np.zeros((0, 4)), np.zeros((0, 2))).any()
+
+
+def test_layer_backward_experts_finite_differences():
+    # every gradient of L = sum(dy * y) through a routed square layer (routing
+    # and gates held at the router's choice) against central differences of the
+    # oracle's layer forward: angles of both rotations, substrate entries taken
+    # real-valued (straight-through), token inputs and the gates themselves
+    cfg = wl.small_config(d_model=8, n_experts=3, top_k=2, tokens=5, act="f32", w_scale=0.75, seed_index=11)
+    inp = wl.generate(cfg)
+    inp.theta[0] = inp.theta[0].astype(np.float64)
+    inp.phi[0] = inp.phi[0].astype(np.float64)
+    inp.w_base[0] = inp.w_base[0].astype(np.float64)
+    x64 = ref.stored_to_f64(inp.x, "f32")
+    R = ref.route(x64, ref.stored_to_f64(inp.w_gate, "f32"), cfg.top_k)
+    r = np.random.default_rng(3)
+    dy = r.standard_normal((cfg.tokens, cfg.d_model))
+    g = ref.layer_backward_experts(inp, dy, R)
+
+    def loss():
+        return float(np.sum(dy * ref.forward(inp, routing=R)[0]))
+
+    def fd(arr, ix, h):
+        old = arr[ix]
+        arr[ix] = old + h
+        lp = loss()
+        arr[ix] = old - h
+        lm = loss()
+        arr[ix] = old
+        return (lp - lm) / (2 * h)
+
+    used = np.unique(R.idx)
+    for e in used:
+        for (s_, p) in ((0, 0), (1, 2), (2, 3)):
+            assert abs(fd(inp.theta[0], (e, s_, p), 1e-6) - g["theta"][e, s_, p]) < 1e-7 * (1 + abs(g["theta"][e, s_, p]))
+            assert abs(fd(inp.phi[0], (e, s_, p), 1e-6) - g["phi"][e, s_, p]) < 1e-7 * (1 + abs(g["phi"][e, s_, p]))
+    for e in set(range(cfg.n_experts)) - set(used.tolist()):
+        assert not g["theta"][e].any() and not g["phi"][e].any()
+    for (o, i) in ((0, 0), (3, 5), (7, 7)):
+        assert abs(fd(inp.w_base[0], (o, i), 0.25) - g["w_base"][o, i]) < 1e-9 * (1 + abs(g["w_base"][o, i]))
+    for (t, i) in ((0, 1), (4, 6)):   # linear in x with the gates held: exact up to the f32 steps
+        assert abs(fd(inp.x, (t, i), 0.0625) - g["x"][t, i]) < 1e-5 * (1 + abs(g["x"][t, i]))
+    for (t, j) in ((0, 0), (2, 1)):
+        assert abs(fd(R.gates, (t, j), 0.5) - g["gate"][t, j]) < 1e-9 * (1 + abs(g["gate"][t, j]))
