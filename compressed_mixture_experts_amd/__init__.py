@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
-    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad", "STATUS",
+    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad", "combine_backward", "STATUS",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = [
     "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
     "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
     "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
-    "bmoe_substrate_grad_workspace", "bmoe_substrate_grad",
+    "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
 ]
 
 
@@ -108,11 +108,12 @@ def lib() -> ctypes.CDLL:
                                           c_vp, c_vp, c_sz, c_vp]
     L.bmoe_substrate_grad_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
     L.bmoe_substrate_grad.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp, c_sz, c_vp]
+    L.bmoe_combine_backward.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
     for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
                  "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
                  "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
                  "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
-                 "bmoe_substrate_grad_workspace", "bmoe_substrate_grad"):
+                 "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward"):
         getattr(L, name).restype = c_i32
     _lib = L
     return L
@@ -357,6 +358,20 @@ def substrate_grad(dz, u, alpha: float = 1.0, dw=None):
     _check(lib().bmoe_substrate_grad(d_out, d_in, rows, BF16 if dz.dtype == torch.bfloat16 else F32, _ptr(dz),
                                      _ptr(u), float(alpha), _ptr(dw), _ptr(ws), int(nb.value), _stream_handle()))
     return dw
+
+
+def combine_backward(dy, bucket_slots, topk_gate, top_k: int, o=None):
+    """Backward of the gated combine: d_rows [T*k][d] = gate * dy[token] in
+    bucket order, and (with the experts' outputs o in bucket order) d_gate
+    [T*k] by flat slot.  Returns (d_rows, d_gate or None)."""
+    torch = _torch()
+    T, d = int(dy.shape[0]), int(dy.shape[1])
+    d_rows = torch.empty((T * top_k, d), dtype=dy.dtype, device=dy.device)
+    d_gate = torch.empty(T * top_k, dtype=torch.float32, device=dy.device) if o is not None else None
+    _check(lib().bmoe_combine_backward(T, top_k, d, BF16 if dy.dtype == torch.bfloat16 else F32, _ptr(dy),
+                                       _ptr(bucket_slots), _ptr(topk_gate), _ptr(o), _ptr(d_rows), _ptr(d_gate),
+                                       _stream_handle()))
+    return d_rows, d_gate
 
 
 def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):

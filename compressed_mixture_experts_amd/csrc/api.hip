@@ -876,3 +876,33 @@ bmoe_status bmoe_substrate_grad(int32_t d_out, int32_t d_in, int32_t rows, int32
   BMOE_HIP(launch_sgrad(dz, u, alpha, dw, static_cast<float*>(workspace), rows, d_out, d_in, stream));
   return ok();
 }
+
+// ---------------------------------------------------------------- combine backward
+bmoe_status bmoe_combine_backward(int32_t T, int32_t top_k, int32_t d, int32_t dtype, const void* dy,
+                                  const int32_t* bucket_slots, const float* topk_gate, const void* o,
+                                  void* d_rows, float* d_gate, hipStream_t stream) {
+  if (T < 0 || top_k < 1 || top_k > 8 || d < 8 || d > 16384 || d % 8 != 0)
+    return fail(BMOE_ERR_SHAPE, "T=%d, top_k=%d, d=%d: need T >= 0, top_k in [1, 8], d a multiple of 8 in [8, 16384]",
+                T, top_k, d);
+  const int64_t R = int64_t(T) * top_k;
+  if (R * d > (int64_t(1) << 31) - 1) return fail(BMOE_ERR_SHAPE, "T * top_k * d must be below 2^31");
+  if (dtype != BMOE_F32 && dtype != BMOE_BF16) return fail(BMOE_ERR_DTYPE, "dtype=%d is unknown", dtype);
+  if ((o == nullptr) != (d_gate == nullptr)) return fail(BMOE_ERR_NULL, "o and d_gate must be given together");
+  if (R > 0 && (!dy || !bucket_slots || !topk_gate || !d_rows)) return fail(BMOE_ERR_NULL, "an input or d_rows is NULL");
+  if (R > 0 && (!aligned(dy, 16) || !aligned(d_rows, 16) || (o && !aligned(o, 16))))
+    return fail(BMOE_ERR_ALIGN, "dy, o and d_rows must be 16-byte aligned");
+  if (R > 0 && (!aligned(bucket_slots, 4) || !aligned(topk_gate, 4) || (d_gate && !aligned(d_gate, 4))))
+    return fail(BMOE_ERR_ALIGN, "bucket_slots, topk_gate and d_gate must be 4-byte aligned");
+  const size_t es = dtype == BMOE_BF16 ? 2 : 4;
+  const Range rdy{dy, size_t(T) * d * es}, rsl{bucket_slots, size_t(R) * 4}, rg{topk_gate, size_t(R) * 4},
+      ro{o, o ? size_t(R) * d * es : 0}, rr{d_rows, size_t(R) * d * es}, rdg{d_gate, d_gate ? size_t(R) * 4 : 0};
+  if (R > 0 && (overlap(rr, rdy) || overlap(rr, rsl) || overlap(rr, rg) || overlap(rr, ro) || overlap(rr, rdg)))
+    return fail(BMOE_ERR_ALIAS, "d_rows overlaps an input or d_gate");
+  if (R > 0 && d_gate && (overlap(rdg, rdy) || overlap(rdg, rsl) || overlap(rdg, rg) || overlap(rdg, ro)))
+    return fail(BMOE_ERR_ALIAS, "d_gate overlaps an input");
+  const bmoe_status st = check_device();
+  if (st != BMOE_OK) return st;
+  BMOE_HIP(launch_combine_bwd(dy, bucket_slots, topk_gate, o, d_rows, d_gate, int(R), top_k, d,
+                              dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
+  return ok();
+}

@@ -242,6 +242,8 @@ hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 // Backward of a bucketed butterfly pass (butterfly_bwd.hip): workspace bytes and launch.
 size_t bfly_bwd_workspace(int log2n, int n_experts, int rows);
 bool sgrad_shape_ok(int M, int N);
+hipError_t launch_combine_bwd(const void* dy, const int32_t* slots, const float* gate, const void* o, void* d_rows,
+                              float* d_gate, int R, int k, int d, int act, hipStream_t s);
 int sgrad_splits(int M, int N, int R, int* kchunk);
 size_t sgrad_workspace(int M, int N, int R);
 hipError_t launch_sgrad(const void* dz, const void* u, float alpha, float* out, float* part, int R, int M, int N,

@@ -83,6 +83,31 @@ bmoe_status bmoe_substrate_grad(int32_t d_out, int32_t d_in, int32_t rows, int32
                                 const void* u, float alpha, float* dw, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* Backward of the gated combine y_t = sum_j gate_{t,j} o_{t,j} (ButterflyMoE,
+ * gist.science/nl/paper/2601.13563, §2 "Gated Routing"; the forward's combine
+ * in bmoe.h).  For the routed slot s = t*top_k + j at bucket position q
+ * (bucket_slots[q] = s, as bmoe_route writes it):
+ *     d_rows[q] = topk_gate[s] * dy[t]      (gradient at the expert's output)
+ *     d_gate[s] = dy[t] . o[q]              (only when o is given)
+ *   dy           [T][d] of dtype (device, 16-byte aligned), read only.
+ *   bucket_slots [T*top_k] int32 (device): a permutation of the flat slots;
+ *                values outside [0, T*top_k) are clamped to it.
+ *   topk_gate    [T*top_k] fp32 (device), by flat slot, read only.
+ *   o            [T*top_k][d] of dtype (device, 16-byte aligned) or NULL: the
+ *                experts' outputs (before the gate) in bucket order.
+ *   d_rows       [T*top_k][d] of dtype (device, 16-byte aligned), written.
+ *   d_gate       [T*top_k] fp32 (device) by flat slot, written; NULL exactly
+ *                when o is NULL.
+ * d a multiple of 8 in [8, 16384], top_k in [1, 8].  fp32 arithmetic; every
+ * output is written once (no dependence on scheduling).  Enqueued on
+ * `stream`, nothing allocated or synchronised.  Errors: BMOE_ERR_SHAPE,
+ * BMOE_ERR_DTYPE, BMOE_ERR_NULL, BMOE_ERR_ALIGN, BMOE_ERR_ALIAS (an output
+ * overlaps an input or the other output), BMOE_ERR_HIP; all but the last are
+ * detected before anything is enqueued. */
+bmoe_status bmoe_combine_backward(int32_t T, int32_t top_k, int32_t d, int32_t dtype, const void* dy,
+                                  const int32_t* bucket_slots, const float* topk_gate, const void* o,
+                                  void* d_rows, float* d_gate, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

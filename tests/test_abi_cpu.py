@@ -392,3 +392,22 @@ def test_substrate_grad_arguments():
     assert call(dw=dz + 64) == 5                      # dw over dz
     assert call(ws=u) == 5                            # workspace over u
     assert call(ws=dw + 256) == 5                     # workspace over dw
+
+
+def test_combine_backward_arguments():
+    L = bm.lib()
+    F = FAKE
+    dy, sl, g, o, dr, dg = F + 0x100000, F + 0x200000, F + 0x300000, F + 0x400000, F + 0x500000, F + 0x600000
+
+    def call(T=100, k=2, d=512, dt=bm.BF16, dy=dy, sl=sl, g=g, o=o, dr=dr, dg=dg):
+        return L.bmoe_combine_backward(T, k, d, dt, dy, sl, g, o, dr, dg, None)
+
+    assert call(d=100) == 2 and call(k=9) == 2 and call(T=-1) == 2 and call(d=32768) == 2
+    assert call(T=1 << 20, k=8, d=512) == 2       # T * k * d beyond 2^31
+    assert call(dt=5) == 3
+    assert call(o=None) == 1 and call(dg=None) == 1  # o and d_gate together
+    assert call(dy=None) == 1 and call(sl=None) == 1 and call(dr=None) == 1
+    assert call(dy=dy + 8) == 4 and call(dr=dr + 2) == 4 and call(sl=sl + 2) == 4
+    assert call(dr=dy) == 5                        # d_rows over dy
+    assert call(dg=sl) == 5                        # d_gate over the slots
+    assert call(dg=dr + 64) == 5                   # d_gate inside d_rows
