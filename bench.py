@@ -333,8 +333,32 @@ def grad_measure(reps: int = 20) -> dict:
         sg.append({"shape": name, "rows": rows, "d_out": d_out, "d_in": d_in, "ms": round(ms, 4),
                    "tflops": round(tf, 1), "mfma_frac": round(tf / 2500.0, 4)})
         del dz, u, dw
-    return {"measurement": "butterfly backward (input and angle gradients); substrate weight gradient",
-            "dtype": "bf16 rows, fp32 angles and weight gradients", "shapes": out, "substrate": sg}
+    # the gated combine's backward at the edge and large routed-row shapes:
+    # bytes dy rows gathered, expert outputs and row gradients, gates in and out
+    cb = []
+    for name, T, d in (("edge_d512_n64 combine", 4096, 512), ("large_d2048_n256 combine", 32768, 2048)):
+        k = 2
+        g = torch.Generator(device="cuda").manual_seed(13)
+        dy = torch.randn((T, d), device="cuda", generator=g).to(torch.bfloat16)
+        o = torch.randn((T * k, d), device="cuda", generator=g).to(torch.bfloat16)
+        slots = torch.randperm(T * k, device="cuda", generator=g).to(torch.int32)
+        gate = torch.rand(T * k, device="cuda", generator=g)
+        for _ in range(3):
+            bm.combine_backward(dy, slots, gate, k, o)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(reps):
+            bm.combine_backward(dy, slots, gate, k, o)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / reps
+        by = 3 * T * k * d * 2 + T * k * 16
+        cb.append({"shape": name, "rows": T * k, "width": d, "ms": round(ms, 4),
+                   "hbm_gbps": round(by / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(by / (ms * 1e-3) / 8e12, 4)})
+        del dy, o
+    return {"measurement": "butterfly backward (input and angle gradients); substrate weight gradient; combine backward",
+            "dtype": "bf16 rows, fp32 angles and weight gradients", "shapes": out, "substrate": sg, "combine": cb}
 
 
 def main() -> int:
