@@ -388,6 +388,41 @@ def ternary_product(U: np.ndarray, w_base: np.ndarray, alpha: float = 1.0) -> np
     return alpha * (np.asarray(U, dtype=np.float64) @ np.asarray(w_base, dtype=np.float64).T)
 
 
+def router_backward(x64: np.ndarray, wg64: np.ndarray, idx: np.ndarray, dgate: np.ndarray,
+                    renorm: bool = False):
+    """Gradients of L = sum(dgate * gates) through the gating network with the
+    chosen experts held ([MoE-nl] §2 "Gated Routing": standard top-k gating).
+    Logits l = W_g x_t, p = softmax(l) over all N experts, gate_j = p_{e_j}
+    (divided by the sum over the k chosen when ``renorm``).  Chain rule:
+      without renorm  dl_n = p_n (a_n - s), a_n = sum_j dgate_j [n = e_j],
+                      s = sum_j dgate_j p_{e_j};
+      with renorm     dl_{e_j} = g_j (dgate_j - sum_i dgate_i g_i), other n 0;
+    then dW_g = sum_t dl_t x_t^T and dx_t = W_g^T dl_t.
+    x64 [T][d], wg64 [N][d], idx [T][k], dgate [T][k].
+    Returns (dx [T][d], dW_g [N][d], dlogits [T][N])."""
+    x64 = np.asarray(x64, dtype=np.float64)
+    wg64 = np.asarray(wg64, dtype=np.float64)
+    dgate = np.asarray(dgate, dtype=np.float64)
+    T, N = x64.shape[0], wg64.shape[0]
+    logits = x64 @ wg64.T
+    m = logits.max(axis=1, keepdims=True)
+    ex = np.exp(logits - m)
+    p = ex / ex.sum(axis=1, keepdims=True)
+    dl = np.zeros((T, N))
+    rows = np.arange(T)[:, None]
+    pc = p[rows, idx]                                   # [T][k] chosen probabilities
+    if renorm:
+        g = pc / pc.sum(axis=1, keepdims=True)
+        inner = np.sum(dgate * g, axis=1, keepdims=True)
+        np.add.at(dl, (np.repeat(np.arange(T), idx.shape[1]), idx.ravel()), (g * (dgate - inner)).ravel())
+    else:
+        a = np.zeros((T, N))
+        np.add.at(a, (np.repeat(np.arange(T), idx.shape[1]), idx.ravel()), dgate.ravel())
+        s = np.sum(dgate * pc, axis=1, keepdims=True)
+        dl = p * (a - s)
+    return dl @ wg64, dl.T @ x64, dl
+
+
 def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
     """Gradients of L = sum(dy * y) through the experts of a square layer,
     with the routing and the gates held at ``routing`` (they are piecewise

@@ -413,3 +413,41 @@ def test_layer_backward_experts_finite_differences():
         assert abs(fd(inp.x, (t, i), 0.0625) - g["x"][t, i]) < 1e-5 * (1 + abs(g["x"][t, i]))
     for (t, j) in ((0, 0), (2, 1)):
         assert abs(fd(R.gates, (t, j), 0.5) - g["gate"][t, j]) < 1e-9 * (1 + abs(g["gate"][t, j]))
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_router_backward_finite_differences(renorm):
+    # dx and dW_g against central differences of L = sum(dgate * gates) with the
+    # chosen experts held (the perturbations are far too small to change them)
+    r = np.random.default_rng(21 + renorm)
+    T, d, N, k = 4, 6, 5, 2
+    x = r.standard_normal((T, d))
+    wg = r.standard_normal((N, d)) / np.sqrt(d)
+    dgate = r.standard_normal((T, k))
+    R0 = ref.route(x, wg, k, renorm)
+    dx, dwg, dl = ref.router_backward(x, wg, R0.idx, dgate, renorm)
+
+    def loss(xx, ww):
+        R = ref.route(xx, ww, k, renorm)
+        assert np.array_equal(R.idx, R0.idx)
+        return float(np.sum(dgate * R.gates))
+
+    h = 1e-6
+    for (t, i) in ((0, 0), (2, 3), (3, 5)):
+        xp, xm = x.copy(), x.copy()
+        xp[t, i] += h
+        xm[t, i] -= h
+        fd = (loss(xp, wg) - loss(xm, wg)) / (2 * h)
+        assert abs(fd - dx[t, i]) < 1e-7 * (1 + abs(fd))
+    for (n, i) in ((0, 0), (int(R0.idx[1, 0]), 2), (4, 5)):
+        wp, wm = wg.copy(), wg.copy()
+        wp[n, i] += h
+        wm[n, i] -= h
+        fd = (loss(x, wp) - loss(x, wm)) / (2 * h)
+        assert abs(fd - dwg[n, i]) < 1e-7 * (1 + abs(fd))
+    # logits' gradients sum to zero per token (softmax is shift-invariant)
+    assert np.allclose(dl.sum(axis=1), 0.0, atol=1e-12)
+    if renorm:  # only the chosen experts' logits matter
+        mask = np.zeros((T, N), dtype=bool)
+        mask[np.arange(T)[:, None], R0.idx] = True
+        assert not dl[~mask].any()
