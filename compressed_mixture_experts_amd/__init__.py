@@ -19,8 +19,8 @@ import numpy as np
 
 __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
-    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad", "combine_backward", "STATUS",
-    "EXPORTED_SYMBOLS",
+    "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad",
+    "combine_backward", "router_backward", "STATUS", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = [
     "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
     "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
     "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
+    "bmoe_router_backward_workspace", "bmoe_router_backward",
 ]
 
 
@@ -109,11 +110,15 @@ def lib() -> ctypes.CDLL:
     L.bmoe_substrate_grad_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
     L.bmoe_substrate_grad.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp, c_sz, c_vp]
     L.bmoe_combine_backward.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+    L.bmoe_router_backward_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_router_backward.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                       c_vp, c_sz, c_vp]
     for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
                  "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
                  "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
                  "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
-                 "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward"):
+                 "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
+                 "bmoe_router_backward_workspace", "bmoe_router_backward"):
         getattr(L, name).restype = c_i32
     _lib = L
     return L
@@ -372,6 +377,22 @@ def combine_backward(dy, bucket_slots, topk_gate, top_k: int, o=None):
                                        _ptr(bucket_slots), _ptr(topk_gate), _ptr(o), _ptr(d_rows), _ptr(d_gate),
                                        _stream_handle()))
     return d_rows, d_gate
+
+
+def router_backward(x, w_gate, topk_idx, d_gate, renorm: bool = False):
+    """Gating network's backward with the chosen experts held: returns
+    (dx [T][d] fp32, dw_gate [N][d] fp32)."""
+    torch = _torch()
+    T, d, N, k = int(x.shape[0]), int(x.shape[1]), int(w_gate.shape[0]), int(topk_idx.shape[1])
+    dx = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    dwg = torch.empty((N, d), dtype=torch.float32, device=x.device)
+    nb = ctypes.c_size_t(0)
+    _check(lib().bmoe_router_backward_workspace(T, d, N, ctypes.byref(nb)))
+    ws = torch.empty(max(int(nb.value), 16), dtype=torch.uint8, device=x.device)
+    _check(lib().bmoe_router_backward(T, d, N, k, 1 if renorm else 0, BF16 if x.dtype == torch.bfloat16 else F32,
+                                      _ptr(x), _ptr(w_gate), _ptr(topk_idx), _ptr(d_gate), _ptr(dx), _ptr(dwg),
+                                      _ptr(ws), int(nb.value), _stream_handle()))
+    return dx, dwg
 
 
 def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):

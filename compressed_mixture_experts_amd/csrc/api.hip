@@ -906,3 +906,58 @@ bmoe_status bmoe_combine_backward(int32_t T, int32_t top_k, int32_t d, int32_t d
                               dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
   return ok();
 }
+
+// ---------------------------------------------------------------- router backward
+static bmoe_status check_rbwd_shape(int32_t T, int32_t d, int32_t N) {
+  if (T < 0 || d < 8 || d > 2048 || d % 8 != 0 || N < 1 || N > 256)
+    return fail(BMOE_ERR_SHAPE, "T=%d, d=%d, N=%d: need T >= 0, d a multiple of 8 in [8, 2048], N in [1, 256]", T,
+                d, N);
+  if (int64_t(T) * (d > N ? d : N) > (int64_t(1) << 31) - 1) return fail(BMOE_ERR_SHAPE, "T * max(d, N) beyond 2^31");
+  return BMOE_OK;
+}
+
+bmoe_status bmoe_router_backward_workspace(int32_t T, int32_t d, int32_t n_experts, size_t* bytes) {
+  if (!bytes) return fail(BMOE_ERR_NULL, "bytes is NULL");
+  const bmoe_status st = check_rbwd_shape(T, d, n_experts);
+  if (st != BMOE_OK) return st;
+  *bytes = router_bwd_workspace(T, d, n_experts);
+  return ok();
+}
+
+bmoe_status bmoe_router_backward(int32_t T, int32_t d, int32_t n_experts, int32_t top_k, int32_t renorm_gates,
+                                 int32_t dtype, const void* x, const void* w_gate, const int32_t* topk_idx,
+                                 const float* d_gate, float* dx, float* dw_gate, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  bmoe_status st = check_rbwd_shape(T, d, n_experts);
+  if (st != BMOE_OK) return st;
+  if (top_k < 1 || top_k > 8 || top_k > n_experts) return fail(BMOE_ERR_SHAPE, "top_k=%d must be in [1, min(8, N)]", top_k);
+  if (renorm_gates != 0 && renorm_gates != 1) return fail(BMOE_ERR_SHAPE, "renorm_gates must be 0 or 1");
+  if (dtype != BMOE_F32 && dtype != BMOE_BF16) return fail(BMOE_ERR_DTYPE, "dtype=%d is unknown", dtype);
+  if (!w_gate || !dw_gate) return fail(BMOE_ERR_NULL, "w_gate / dw_gate is NULL");
+  if (T > 0 && (!x || !topk_idx || !d_gate || !dx)) return fail(BMOE_ERR_NULL, "x / topk_idx / d_gate / dx is NULL");
+  const size_t need = router_bwd_workspace(T, d, n_experts);
+  if (need > 0 && !workspace) return fail(BMOE_ERR_NULL, "workspace is NULL");
+  if (!aligned(w_gate, 16) || !aligned(dw_gate, 4) || (T > 0 && (!aligned(x, 16) || !aligned(dx, 4))))
+    return fail(BMOE_ERR_ALIGN, "x and w_gate must be 16-byte aligned, dx and dw_gate 4-byte aligned");
+  if (T > 0 && (!aligned(topk_idx, 4) || !aligned(d_gate, 4)))
+    return fail(BMOE_ERR_ALIGN, "topk_idx and d_gate must be 4-byte aligned");
+  if (need > 0 && !aligned(workspace, 16)) return fail(BMOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(BMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t es = dtype == BMOE_BF16 ? 2 : 4;
+  const Range rx{x, size_t(T) * d * es}, rw{w_gate, size_t(n_experts) * d * es}, ri{topk_idx, size_t(T) * top_k * 4},
+      rg{d_gate, size_t(T) * top_k * 4}, rdx{dx, size_t(T) * d * 4}, rdw{dw_gate, size_t(n_experts) * d * 4},
+      rws{workspace, need};
+  if (overlap(rdw, rw) || overlap(rdw, rws) ||
+      (T > 0 && (overlap(rdw, rx) || overlap(rdw, ri) || overlap(rdw, rg) || overlap(rdw, rdx))))
+    return fail(BMOE_ERR_ALIAS, "dw_gate overlaps an input, dx or the workspace");
+  if (T > 0 && (overlap(rdx, rx) || overlap(rdx, rw) || overlap(rdx, ri) || overlap(rdx, rg) || overlap(rdx, rws)))
+    return fail(BMOE_ERR_ALIAS, "dx overlaps an input or the workspace");
+  if (need > 0 && (overlap(rws, rw) || (T > 0 && (overlap(rws, rx) || overlap(rws, ri) || overlap(rws, rg)))))
+    return fail(BMOE_ERR_ALIAS, "the workspace overlaps an input");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+  BMOE_HIP(launch_router_bwd(x, w_gate, topk_idx, d_gate, dx, dw_gate, workspace, T, d, n_experts, top_k,
+                             renorm_gates, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
+  return ok();
+}

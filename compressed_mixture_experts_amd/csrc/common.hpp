@@ -242,6 +242,9 @@ hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 // Backward of a bucketed butterfly pass (butterfly_bwd.hip): workspace bytes and launch.
 size_t bfly_bwd_workspace(int log2n, int n_experts, int rows);
 bool sgrad_shape_ok(int M, int N);
+size_t router_bwd_workspace(int T, int d, int N);
+hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, const float* dgate, float* dx,
+                             float* dwg, void* ws, int T, int d, int N, int k, int renorm, int act, hipStream_t s);
 hipError_t launch_combine_bwd(const void* dy, const int32_t* slots, const float* gate, const void* o, void* d_rows,
                               float* d_gate, int R, int k, int d, int act, hipStream_t s);
 int sgrad_splits(int M, int N, int R, int* kchunk);

@@ -1,0 +1,255 @@
+// Backward of the gating network with the chosen experts held (ButterflyMoE,
+// gist.science/nl/paper/2601.13563, §2 "Gated Routing": a standard top-k
+// gating network).  Logits l = W_g x_t, p = softmax(l) over all N experts,
+// gate_j = p_{e_j} (or renormalised over the k chosen).  Given the gates'
+// gradients:
+//   without renormalisation  dl_n = p_n (a_n - s), a_n = sum_j dgate_j [n = e_j],
+//                            s = sum_j dgate_j p_{e_j}
+//   with renormalisation     dl_{e_j} = g_j (dgate_j - sum_i dgate_i g_i), else 0
+// then dx_t = W_g^T dl_t and dW_g = sum_t dl_t x_t^T.
+//
+// Three passes, fp32 arithmetic, every output written once (no atomics):
+//   router_dl_kernel   16 tokens per workgroup, a thread per expert: the
+//                      logits again (8-element loads of the gate row, the
+//                      token's elements uniform over the wave), softmax over
+//                      the workgroup, dl [T][N] to the workspace;
+//   router_dx_kernel   16 tokens per workgroup, a thread per column of x;
+//   router_dwg_kernel  16 experts x 256 columns per workgroup, the tokens split
+//                      in ranges of at least 256 when the tiles are few; the
+//                      ranges' partial sums added in order by router_red_kernel.
+#include "common.hpp"
+
+namespace bmoe {
+
+constexpr int RB_BT = 16;   // tokens per workgroup (dl, dx)
+constexpr int RB_NB = 16;   // experts per workgroup (dW_g)
+
+struct RouterBwdArgs {
+  const void* x;         // [T][d]
+  const void* wg;        // [N][d]
+  const int32_t* idx;    // [T][k]
+  const float* dgate;    // [T][k]
+  float* dl;             // [T][N] (workspace)
+  float* dx;             // [T][d]
+  float* dwg;            // [N][d]
+  float* part;           // [S][N][d] (workspace) when S > 1
+  int32_t T, d, N, k, renorm, S, tchunk;
+};
+
+template <int A>
+__global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
+  __shared__ float sP[RB_BT][256];      // probabilities
+  __shared__ float sRed[RB_BT][4];
+  __shared__ float sMax[RB_BT], sSum[RB_BT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RB_BT, n = tid;
+  const bool live = n < a.N;
+  float acc[RB_BT];
+#pragma unroll
+  for (int t = 0; t < RB_BT; ++t) acc[t] = 0.f;
+  for (int i = 0; i < a.d; i += 8) {
+    float w[8];
+    if (live) load8<A>(a.wg, size_t(n) * a.d + i, w);
+#pragma unroll
+    for (int t = 0; t < RB_BT; ++t) {
+      if (t0 + t < a.T) {
+        float xv[8];
+        load8<A>(a.x, size_t(t0 + t) * a.d + i, xv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t] = fmaf(live ? w[j] : 0.f, xv[j], acc[t]);
+      }
+    }
+  }
+  // softmax over the experts, per token: max, then sum of exp
+#pragma unroll
+  for (int t = 0; t < RB_BT; ++t) {
+    float m = live ? acc[t] : -INFINITY;
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (lane == 0) sRed[t][wave] = m;
+  }
+  __syncthreads();
+  if (tid < RB_BT) sMax[tid] = fmaxf(fmaxf(sRed[tid][0], sRed[tid][1]), fmaxf(sRed[tid][2], sRed[tid][3]));
+  __syncthreads();
+  float ev[RB_BT];
+#pragma unroll
+  for (int t = 0; t < RB_BT; ++t) {
+    ev[t] = live ? __expf(acc[t] - sMax[t]) : 0.f;
+    float s = ev[t];
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) sRed[t][wave] = s;
+  }
+  __syncthreads();
+  if (tid < RB_BT) sSum[tid] = (sRed[tid][0] + sRed[tid][1]) + (sRed[tid][2] + sRed[tid][3]);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < RB_BT; ++t) sP[t][n] = live ? ev[t] / sSum[t] : 0.f;
+  __syncthreads();
+  // dl of this thread's expert for each token of the tile
+#pragma unroll
+  for (int t = 0; t < RB_BT; ++t) {
+    const int tt = t0 + t;
+    if (tt >= a.T || !live) continue;
+    const int32_t* id = a.idx + size_t(tt) * a.k;
+    const float* dg = a.dgate + size_t(tt) * a.k;
+    float v = 0.f;
+    if (a.renorm) {
+      float ps = 0.f, inner = 0.f, mine = 0.f;
+      bool chosen = false;
+      for (int j = 0; j < a.k; ++j) ps += sP[t][min(max(id[j], 0), a.N - 1)];
+      for (int j = 0; j < a.k; ++j) {
+        const int e = min(max(id[j], 0), a.N - 1);
+        const float g = sP[t][e] / ps;
+        inner = fmaf(dg[j], g, inner);
+        if (e == n) {
+          chosen = true;
+          mine += dg[j];
+        }
+      }
+      if (chosen) {
+        const float g = sP[t][n] / ps;
+        v = g * (mine - inner);
+      }
+    } else {
+      float s = 0.f, an = 0.f;
+      for (int j = 0; j < a.k; ++j) {
+        const int e = min(max(id[j], 0), a.N - 1);
+        s = fmaf(dg[j], sP[t][e], s);
+        if (e == n) an += dg[j];
+      }
+      v = sP[t][n] * (an - s);
+    }
+    a.dl[size_t(tt) * a.N + n] = v;
+  }
+}
+
+// dx[t][i] = sum_n dl[t][n] W_g[n][i]; a thread per column (blockDim = 256,
+// columns tid + 256 c)
+template <int A, int CPT>
+__global__ __launch_bounds__(256) void router_dx_kernel(RouterBwdArgs a) {
+  const int tid = threadIdx.x, t0 = blockIdx.x * RB_BT;
+  float acc[RB_BT][CPT];
+#pragma unroll
+  for (int t = 0; t < RB_BT; ++t)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[t][c] = 0.f;
+  for (int n = 0; n < a.N; ++n) {
+    float w[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int i = tid + 256 * c;
+      w[c] = i < a.d ? load1<A>(a.wg, size_t(n) * a.d + i) : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < RB_BT; ++t) {
+      const float l = t0 + t < a.T ? a.dl[size_t(t0 + t) * a.N + n] : 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[t][c] = fmaf(l, w[c], acc[t][c]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < RB_BT; ++t)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int i = tid + 256 * c;
+      if (t0 + t < a.T && i < a.d) a.dx[size_t(t0 + t) * a.d + i] = acc[t][c];
+    }
+}
+
+// dW_g (or the split's partial) for experts nb .. nb+15, columns cb .. cb+255
+template <int A>
+__global__ __launch_bounds__(256) void router_dwg_kernel(RouterBwdArgs a) {
+  const int nblk = (a.N + RB_NB - 1) / RB_NB, cblk = (a.d + 255) / 256;
+  const int b = blockIdx.x % (nblk * cblk), split = blockIdx.x / (nblk * cblk);
+  const int n0 = (b % nblk) * RB_NB, i = (b / nblk) * 256 + threadIdx.x;
+  const int ta = split * a.tchunk, tb = min(a.T, ta + a.tchunk);
+  float acc[RB_NB];
+#pragma unroll
+  for (int q = 0; q < RB_NB; ++q) acc[q] = 0.f;
+  if (i < a.d) {
+    for (int t = ta; t < tb; ++t) {
+      const float xv = load1<A>(a.x, size_t(t) * a.d + i);
+      const float* l = a.dl + size_t(t) * a.N + n0;
+#pragma unroll
+      for (int q = 0; q < RB_NB; ++q) acc[q] = fmaf(n0 + q < a.N ? l[q < a.N - n0 ? q : 0] : 0.f, xv, acc[q]);
+    }
+  }
+  float* dst = a.S > 1 ? a.part + size_t(split) * a.N * a.d : a.dwg;
+#pragma unroll
+  for (int q = 0; q < RB_NB; ++q)
+    if (n0 + q < a.N && i < a.d) dst[size_t(n0 + q) * a.d + i] = acc[q];
+}
+
+__global__ __launch_bounds__(256) void router_red_kernel(RouterBwdArgs a) {
+  const size_t ND = size_t(a.N) * a.d, q = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (q >= ND) return;
+  float s = a.part[q];
+  for (int k = 1; k < a.S; ++k) s += a.part[size_t(k) * ND + q];
+  a.dwg[q] = s;
+}
+
+__global__ __launch_bounds__(256) void router_zero_kernel(float* p, size_t n) {
+  const size_t q = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (q < n) p[q] = 0.f;
+}
+
+// token ranges of the dW_g pass: none when its tiles reach 512 workgroups, else
+// up to that many with at least 256 tokens each
+int router_bwd_splits(int T, int d, int N, int* tchunk) {
+  const int tiles = ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
+  int S = 1;
+  if (tiles < 512) {
+    S = (512 + tiles - 1) / tiles;
+    const int smax = (T + 255) / 256;
+    S = S < smax ? S : smax;
+    S = S < 1 ? 1 : S;
+  }
+  int tc = (T + S - 1) / S;
+  if (tc < 1) tc = 1;
+  S = (T + tc - 1) / tc;
+  if (S < 1) S = 1;
+  if (tchunk) *tchunk = tc;
+  return S;
+}
+
+static size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t router_bwd_workspace(int T, int d, int N) {
+  if (T <= 0) return 0;
+  const int S = router_bwd_splits(T, d, N, nullptr);
+  return al256(size_t(T) * N * 4) + (S > 1 ? size_t(S) * N * d * 4 : 0);
+}
+
+hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, const float* dgate, float* dx,
+                             float* dwg, void* ws, int T, int d, int N, int k, int renorm, int act, hipStream_t s) {
+  if (T <= 0) {
+    const size_t n = size_t(N) * d;
+    hipLaunchKernelGGL(router_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s, dwg, n);
+    return hipGetLastError();
+  }
+  RouterBwdArgs a{x, wg, idx, dgate, static_cast<float*>(ws), dx, dwg, nullptr, T, d, N, k, renorm, 1, 0};
+  a.S = router_bwd_splits(T, d, N, &a.tchunk);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + al256(size_t(T) * N * 4));
+  const dim3 tgrid((T + RB_BT - 1) / RB_BT);
+  const bool bf = act == ACT_BF16;
+  if (bf) hipLaunchKernelGGL(router_dl_kernel<ACT_BF16>, tgrid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(router_dl_kernel<ACT_F32>, tgrid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int cpt = (d + 255) / 256;
+#define RB_DX(C)                                                                              \
+  if (bf) hipLaunchKernelGGL((router_dx_kernel<ACT_BF16, C>), tgrid, dim3(256), 0, s, a);     \
+  else hipLaunchKernelGGL((router_dx_kernel<ACT_F32, C>), tgrid, dim3(256), 0, s, a);
+  if (cpt <= 1) { RB_DX(1) } else if (cpt <= 2) { RB_DX(2) } else if (cpt <= 4) { RB_DX(4) } else { RB_DX(8) }
+#undef RB_DX
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tiles = ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
+  if (bf) hipLaunchKernelGGL(router_dwg_kernel<ACT_BF16>, dim3(tiles * a.S), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(router_dwg_kernel<ACT_F32>, dim3(tiles * a.S), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.S == 1) return e;
+  hipLaunchKernelGGL(router_red_kernel, dim3((size_t(N) * d + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bmoe

@@ -108,6 +108,39 @@ bmoe_status bmoe_combine_backward(int32_t T, int32_t top_k, int32_t d, int32_t d
                                   const int32_t* bucket_slots, const float* topk_gate, const void* o,
                                   void* d_rows, float* d_gate, hipStream_t stream);
 
+/* Backward of the gating network with the chosen experts held (ButterflyMoE,
+ * gist.science/nl/paper/2601.13563, §2 "Gated Routing"; the router of
+ * bmoe.h: logits l = W_g x_t, p = softmax(l) over all experts, gate_j =
+ * p_{e_j}, renormalised over the k chosen when renorm_gates is 1).  Given the
+ * gates' gradients it returns the router's part of the input gradient and
+ * the gate matrix's gradient:
+ *     without renormalisation  dl_n = p_n (a_n - s), a_n = sum_j d_gate_j [n = e_j],
+ *                              s = sum_j d_gate_j p_{e_j}
+ *     with renormalisation     dl_{e_j} = g_j (d_gate_j - sum_i d_gate_i g_i), else 0
+ *     dx_t = W_g^T dl_t,   dw_gate = sum_t dl_t x_t^T.
+ *   x         [T][d] of dtype (device, 16-byte aligned), read only.
+ *   w_gate    [n_experts][d] of dtype (device, 16-byte aligned), read only.
+ *   topk_idx  [T][top_k] int32 (device): the experts held (for example
+ *             bmoe_route's output); values outside [0, n_experts) are clamped.
+ *   d_gate    [T][top_k] fp32 (device): gradients of the gates.
+ *   dx        [T][d] fp32 (device), written: add it to the input gradient of
+ *             the experts' path.
+ *   dw_gate   [n_experts][d] fp32 (device), written (zero for T = 0).
+ *   workspace at least bmoe_router_backward_workspace bytes (device,
+ *             16-byte aligned): the logits' gradients and per-range sums.
+ * d a multiple of 8 in [8, 2048], n_experts in [1, 256], top_k in [1,
+ * min(8, n_experts)].  fp32 arithmetic (the logits are recomputed); every
+ * output is written once and the token ranges are added in order, so the
+ * result does not depend on scheduling.  Enqueued on `stream`, nothing
+ * allocated or synchronised.  Errors: BMOE_ERR_SHAPE, BMOE_ERR_DTYPE,
+ * BMOE_ERR_NULL, BMOE_ERR_ALIGN, BMOE_ERR_ALIAS, BMOE_ERR_WORKSPACE,
+ * BMOE_ERR_HIP; all but the last are detected before anything is enqueued. */
+bmoe_status bmoe_router_backward_workspace(int32_t T, int32_t d, int32_t n_experts, size_t* bytes);
+bmoe_status bmoe_router_backward(int32_t T, int32_t d, int32_t n_experts, int32_t top_k, int32_t renorm_gates,
+                                 int32_t dtype, const void* x, const void* w_gate, const int32_t* topk_idx,
+                                 const float* d_gate, float* dx, float* dw_gate, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -411,3 +411,39 @@ def test_combine_backward_arguments():
     assert call(dr=dy) == 5                        # d_rows over dy
     assert call(dg=sl) == 5                        # d_gate over the slots
     assert call(dg=dr + 64) == 5                   # d_gate inside d_rows
+
+
+def test_router_backward_arguments():
+    L = bm.lib()
+    n = ctypes.c_size_t(0)
+
+    def want(T, d, N):
+        if T == 0:
+            return 0
+        tiles = -(-N // 16) * -(-d // 256)
+        S = 1
+        if tiles < 512:
+            S = max(1, min(-(-512 // tiles), -(-T // 256)))
+        tc = max(1, -(-T // S))
+        S = max(1, -(-T // tc))
+        return -(-T * N * 4 // 256) * 256 + (S * N * d * 4 if S > 1 else 0)
+
+    for args in ((4096, 512, 64), (16384, 512, 256), (32768, 2048, 256), (777, 128, 16), (10, 8, 3), (0, 64, 4)):
+        assert L.bmoe_router_backward_workspace(*args, ctypes.byref(n)) == 0
+        assert n.value == want(*args), args
+    for args in ((10, 4096, 4), (10, 100, 4), (10, 64, 0), (10, 64, 257), (-1, 64, 4)):
+        assert L.bmoe_router_backward_workspace(*args, ctypes.byref(n)) == 2, args
+
+    F = FAKE
+    x, w, ix, dg, dx, dw, ws = (F + 0x100000 * i for i in range(1, 8))
+    need = want(100, 64, 8)
+
+    def call(T=100, d=64, N=8, k=2, rn=0, dt=bm.BF16, x=x, w=w, ix=ix, dg=dg, dx=dx, dw=dw, ws=ws, wsb=need):
+        return L.bmoe_router_backward(T, d, N, k, rn, dt, x, w, ix, dg, dx, dw, ws, wsb, None)
+
+    assert call(k=9) == 2 and call(k=9, N=8) == 2 and call(rn=2) == 2 and call(N=1, k=2) == 2
+    assert call(dt=4) == 3
+    assert call(w=None) == 1 and call(dw=None) == 1 and call(x=None) == 1 and call(ws=None) == 1
+    assert call(x=x + 8) == 4 and call(w=w + 2) == 4 and call(dg=dg + 2) == 4 and call(ws=ws + 8) == 4
+    assert call(wsb=need - 4) == 6
+    assert call(dx=x) == 5 and call(dw=w + 16) == 5 and call(ws=dx) == 5

@@ -125,3 +125,54 @@ def test_layer_backward_composed_from_the_abi():
     assert np.all(np.abs(dgate - want["gate"]) <= 1e-4 * (1 + ob))
     dWr = want["w_base"]
     assert np.linalg.norm(dW.cpu().numpy() - dWr) <= 1e-2 * np.linalg.norm(dWr)
+    # the router's part, fed with the GPU's gate gradients: the whole layer's
+    # input gradient and the gate matrix's gradient
+    wgd = dev(inp.w_gate)
+    dx_r, dwg = bm.router_backward(x, wgd, idx, d_gate.reshape(cfg.tokens, k).contiguous(), False)
+    torch.cuda.synchronize()
+    rdx, rdwg, _ = ref.router_backward(x64, ref.stored_to_f64(inp.w_gate, "f32"), R.idx, want["gate"])
+    tot = dx.cpu().numpy().astype(np.float64) + dx_r.cpu().numpy()
+    assert row_rel_err(tot, want["x"] + rdx).max() <= 1e-4
+    assert np.linalg.norm(dwg.cpu().numpy() - rdwg) <= 1e-4 * np.linalg.norm(rdwg)
+
+
+@pytest.mark.parametrize("T,d,N,k,renorm,act", [
+    (777, 128, 16, 4, False, "f32"),
+    (777, 128, 16, 4, True, "bf16"),
+    (4096, 512, 64, 2, False, "bf16"),    # edge workload's router
+    (3000, 512, 256, 2, True, "f32"),
+    (300, 2048, 256, 2, False, "bf16"),   # large workload's width, several column blocks
+    (5, 8, 3, 1, False, "f32"),           # fewer tokens than a tile
+])
+def test_router_backward_matches_oracle(T, d, N, k, renorm, act):
+    import torch
+    r = np.random.default_rng(T + d + N)
+    log(f"router backward T={T} d={d} N={N} k={k} renorm={renorm} act={act}")
+    x = wl._store(r.standard_normal((T, d)), act)
+    wg = wl._store(r.standard_normal((N, d)) / math.sqrt(d), act)
+    idx = np.argsort(r.random((T, N)), axis=1)[:, :k].astype(np.int32)   # distinct experts per token
+    dgate = r.standard_normal((T, k)).astype(np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    xd = dev(x) if act == "f32" else dev(x.view(np.int16)).view(torch.bfloat16)
+    wd = dev(wg) if act == "f32" else dev(wg.view(np.int16)).view(torch.bfloat16)
+    dx, dwg = bm.router_backward(xd, wd, dev(idx), dev(dgate), renorm)
+    torch.cuda.synchronize()
+    x64, w64 = ref.stored_to_f64(x, act), ref.stored_to_f64(wg, act)
+    rdx, rdw, _ = ref.router_backward(x64, w64, idx, dgate.astype(np.float64), renorm)
+    got_dx, got_dw = dx.cpu().numpy().astype(np.float64), dwg.cpu().numpy().astype(np.float64)
+    scale_x = np.linalg.norm(rdx, axis=1).max()
+    assert np.abs(got_dx - rdx).max() <= 1e-4 * scale_x
+    assert np.linalg.norm(got_dw - rdw) <= 1e-4 * np.linalg.norm(rdw)
+    assert np.abs(got_dw - rdw).max() <= 1e-4 * np.abs(rdw).max()
+
+
+def test_router_backward_zero_tokens():
+    import torch
+    wd = torch.randn((8, 64), device="cuda")
+    dwg = torch.full((8, 64), 3.0, device="cuda")
+    x = torch.empty((0, 64), device="cuda")
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    dg = torch.empty((0, 2), device="cuda")
+    dx, dwg = bm.router_backward(x, wd, idx, dg)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dwg).item() == 0 and dx.shape == (0, 64)

@@ -451,3 +451,42 @@ def test_router_backward_finite_differences(renorm):
         mask = np.zeros((T, N), dtype=bool)
         mask[np.arange(T)[:, None], R0.idx] = True
         assert not dl[~mask].any()
+
+
+def test_full_layer_gradient_is_experts_plus_router():
+    # with the routing recomputed by the forward (the choice itself stays put
+    # under the small steps), the input and gate-matrix gradients of the whole
+    # layer are the experts' part (gates held) plus the router's part fed with
+    # the gates' gradients
+    cfg = wl.small_config(d_model=8, n_experts=4, top_k=2, tokens=5, act="f32", w_scale=0.5, seed_index=23)
+    inp = wl.generate(cfg)
+    cfg_act = inp.cfg.act
+    x64 = ref.stored_to_f64(inp.x, cfg_act)
+    wg64 = ref.stored_to_f64(inp.w_gate, cfg_act)
+    R = ref.route(x64, wg64, cfg.top_k)
+    dy = np.random.default_rng(8).standard_normal((cfg.tokens, cfg.d_model))
+    ge = ref.layer_backward_experts(inp, dy, R)
+    dxr, dwg, _ = ref.router_backward(x64, wg64, R.idx, ge["gate"])
+
+    def loss():
+        y, Rn = ref.forward(inp)
+        assert np.array_equal(Rn.idx, R.idx)
+        return float(np.sum(dy * y))
+
+    def fd(arr, ix, h):
+        old = arr[ix]
+        arr[ix] = old + h
+        lp = loss()
+        arr[ix] = old - h
+        lm = loss()
+        arr[ix] = old
+        return (lp - lm) / (2 * h)
+
+    # steps of 2^-12: exact in the f32 storage the oracle reads, small enough for
+    # the softmax's curvature
+    h = 2.0 ** -12
+    for (t, i) in ((0, 0), (3, 5), (4, 7)):
+        want = ge["x"][t, i] + dxr[t, i]
+        assert abs(fd(inp.x, (t, i), h) - want) < 1e-5 * (1 + abs(want))
+    for (n, i) in ((int(R.idx[0, 0]), 1), (int(R.idx[2, 1]), 6)):
+        assert abs(fd(inp.w_gate, (n, i), h) - dwg[n, i]) < 1e-5 * (1 + abs(dwg[n, i]))
