@@ -357,8 +357,32 @@ def grad_measure(reps: int = 20) -> dict:
         cb.append({"shape": name, "rows": T * k, "width": d, "ms": round(ms, 4),
                    "hbm_gbps": round(by / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(by / (ms * 1e-3) / 8e12, 4)})
         del dy, o
-    return {"measurement": "butterfly backward (input and angle gradients); substrate weight gradient; combine backward",
-            "dtype": "bf16 rows, fp32 angles and weight gradients", "shapes": out, "substrate": sg, "combine": cb}
+    # the router's backward (softmax at the chosen experts -> logits -> W_g, x):
+    # flops 2 T d N for each of the logits, dx and dW_g
+    rb = []
+    for name, T, d, N in (("edge_d512_n64 router", 4096, 512, 64), ("large_d2048_n256 router", 32768, 2048, 256)):
+        g = torch.Generator(device="cuda").manual_seed(14)
+        x = torch.randn((T, d), device="cuda", generator=g).to(torch.bfloat16)
+        wg = (torch.randn((N, d), device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+        idx = torch.argsort(torch.rand((T, N), device="cuda", generator=g), dim=1)[:, :2].to(torch.int32).contiguous()
+        dg = torch.randn((T, 2), device="cuda", generator=g)
+        for _ in range(3):
+            bm.router_backward(x, wg, idx, dg)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(reps):
+            bm.router_backward(x, wg, idx, dg)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / reps
+        rb.append({"shape": name, "tokens": T, "width": d, "experts": N, "ms": round(ms, 4),
+                   "tflops": round(3 * 2.0 * T * d * N / (ms * 1e-3) / 1e12, 2)})
+        del x, wg, idx
+    return {"measurement": "layer backward pieces: butterfly backward; substrate weight gradient; combine backward; "
+                           "router backward",
+            "dtype": "bf16 rows, fp32 angles and weight gradients", "shapes": out, "substrate": sg, "combine": cb,
+            "router": rb}
 
 
 def main() -> int:

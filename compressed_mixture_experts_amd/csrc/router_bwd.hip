@@ -11,12 +11,15 @@
 // Three passes, fp32 arithmetic, every output written once (no atomics):
 //   router_dl_kernel   16 tokens per workgroup, a thread per expert: the
 //                      logits again (8-element loads of the gate row, the
-//                      token's elements uniform over the wave), softmax over
-//                      the workgroup, dl [T][N] to the workspace;
-//   router_dx_kernel   16 tokens per workgroup, a thread per column of x;
-//   router_dwg_kernel  16 experts x 256 columns per workgroup, the tokens split
-//                      in ranges of at least 256 when the tiles are few; the
-//                      ranges' partial sums added in order by router_red_kernel.
+//                      token tile staged in LDS 512 columns at a time and read
+//                      by broadcast), softmax over the workgroup, dl [T][N] to
+//                      the workspace;
+//   router_dx_kernel   16 tokens per workgroup (their dl rows in LDS), a
+//                      thread per column of x;
+//   router_dwg_kernel  16 experts x 256 columns per workgroup (dl of 256
+//                      tokens at a time in LDS), the tokens split in ranges of
+//                      at least 256 when the tiles are few; the ranges'
+//                      partial sums added in order by router_red_kernel.
 #include "common.hpp"
 
 namespace bmoe {
@@ -36,29 +39,49 @@ struct RouterBwdArgs {
   int32_t T, d, N, k, renorm, S, tchunk;
 };
 
+constexpr int RB_XC = 512;  // columns of the token tile staged in LDS at a time
+
 template <int A>
 __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
   __shared__ float sP[RB_BT][256];      // probabilities
   __shared__ float sRed[RB_BT][4];
   __shared__ float sMax[RB_BT], sSum[RB_BT];
+  __shared__ __attribute__((aligned(16))) float sX[RB_BT][RB_XC];  // token tile, one column chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RB_BT, n = tid;
   const bool live = n < a.N;
   float acc[RB_BT];
 #pragma unroll
   for (int t = 0; t < RB_BT; ++t) acc[t] = 0.f;
-  for (int i = 0; i < a.d; i += 8) {
-    float w[8];
-    if (live) load8<A>(a.wg, size_t(n) * a.d + i, w);
+  for (int c0 = 0; c0 < a.d; c0 += RB_XC) {
+    const int cw = min(RB_XC, a.d - c0);
+    // the tile's columns c0 .. c0+cw-1 (8 per thread and step, rows past T zero)
+    for (int q = tid; q < RB_BT * cw / 8; q += 256) {
+      const int t = q / (cw / 8), i = (q % (cw / 8)) * 8;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (t0 + t < a.T) load8<A>(a.x, size_t(t0 + t) * a.d + c0 + i, v);
+      *reinterpret_cast<float4*>(&sX[t][i]) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(&sX[t][i + 4]) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    __syncthreads();
+    for (int i = 0; i < cw; i += 8) {
+      float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (live) load8<A>(a.wg, size_t(n) * a.d + c0 + i, w);
 #pragma unroll
-    for (int t = 0; t < RB_BT; ++t) {
-      if (t0 + t < a.T) {
-        float xv[8];
-        load8<A>(a.x, size_t(t0 + t) * a.d + i, xv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[t] = fmaf(live ? w[j] : 0.f, xv[j], acc[t]);
+      for (int t = 0; t < RB_BT; ++t) {
+        const float4 x0 = *reinterpret_cast<const float4*>(&sX[t][i]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&sX[t][i + 4]);
+        acc[t] = fmaf(w[0], x0.x, acc[t]);
+        acc[t] = fmaf(w[1], x0.y, acc[t]);
+        acc[t] = fmaf(w[2], x0.z, acc[t]);
+        acc[t] = fmaf(w[3], x0.w, acc[t]);
+        acc[t] = fmaf(w[4], x1.x, acc[t]);
+        acc[t] = fmaf(w[5], x1.y, acc[t]);
+        acc[t] = fmaf(w[6], x1.z, acc[t]);
+        acc[t] = fmaf(w[7], x1.w, acc[t]);
       }
     }
+    __syncthreads();  // the chunk is replaced next
   }
   // softmax over the experts, per token: max, then sum of exp
 #pragma unroll
@@ -126,7 +149,13 @@ __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
 // columns tid + 256 c)
 template <int A, int CPT>
 __global__ __launch_bounds__(256) void router_dx_kernel(RouterBwdArgs a) {
+  __shared__ float sL[RB_BT][256];  // the tile's dl rows
   const int tid = threadIdx.x, t0 = blockIdx.x * RB_BT;
+  for (int q = tid; q < RB_BT * a.N; q += 256) {
+    const int t = q / a.N, n = q % a.N;
+    sL[t][n] = t0 + t < a.T ? a.dl[size_t(t0 + t) * a.N + n] : 0.f;
+  }
+  __syncthreads();
   float acc[RB_BT][CPT];
 #pragma unroll
   for (int t = 0; t < RB_BT; ++t)
@@ -141,7 +170,7 @@ __global__ __launch_bounds__(256) void router_dx_kernel(RouterBwdArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < RB_BT; ++t) {
-      const float l = t0 + t < a.T ? a.dl[size_t(t0 + t) * a.N + n] : 0.f;
+      const float l = sL[t][n];
 #pragma unroll
       for (int c = 0; c < CPT; ++c) acc[t][c] = fmaf(l, w[c], acc[t][c]);
     }
@@ -162,16 +191,31 @@ __global__ __launch_bounds__(256) void router_dwg_kernel(RouterBwdArgs a) {
   const int b = blockIdx.x % (nblk * cblk), split = blockIdx.x / (nblk * cblk);
   const int n0 = (b % nblk) * RB_NB, i = (b / nblk) * 256 + threadIdx.x;
   const int ta = split * a.tchunk, tb = min(a.T, ta + a.tchunk);
+  __shared__ __attribute__((aligned(16))) float sL[256][RB_NB];  // dl of 256 tokens for the block's experts
   float acc[RB_NB];
 #pragma unroll
   for (int q = 0; q < RB_NB; ++q) acc[q] = 0.f;
-  if (i < a.d) {
-    for (int t = ta; t < tb; ++t) {
-      const float xv = load1<A>(a.x, size_t(t) * a.d + i);
-      const float* l = a.dl + size_t(t) * a.N + n0;
-#pragma unroll
-      for (int q = 0; q < RB_NB; ++q) acc[q] = fmaf(n0 + q < a.N ? l[q < a.N - n0 ? q : 0] : 0.f, xv, acc[q]);
+  for (int tc = ta; tc < tb; tc += 256) {
+    const int tn = min(256, tb - tc);
+    for (int q = threadIdx.x; q < tn * RB_NB; q += 256) {
+      const int t = q / RB_NB, e = q % RB_NB;
+      sL[t][e] = n0 + e < a.N ? a.dl[size_t(tc + t) * a.N + n0 + e] : 0.f;
     }
+    __syncthreads();
+    if (i < a.d) {
+      for (int t = 0; t < tn; ++t) {
+        const float xv = load1<A>(a.x, size_t(tc + t) * a.d + i);
+#pragma unroll
+        for (int q = 0; q < RB_NB; q += 4) {
+          const float4 l = *reinterpret_cast<const float4*>(&sL[t][q]);
+          acc[q] = fmaf(l.x, xv, acc[q]);
+          acc[q + 1] = fmaf(l.y, xv, acc[q + 1]);
+          acc[q + 2] = fmaf(l.z, xv, acc[q + 2]);
+          acc[q + 3] = fmaf(l.w, xv, acc[q + 3]);
+        }
+      }
+    }
+    __syncthreads();  // sL is replaced next
   }
   float* dst = a.S > 1 ? a.part + size_t(split) * a.N * a.d : a.dwg;
 #pragma unroll
