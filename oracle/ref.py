@@ -423,6 +423,17 @@ def router_backward(x64: np.ndarray, wg64: np.ndarray, idx: np.ndarray, dgate: n
     return dl @ wg64, dl.T @ x64, dl
 
 
+def gelu_backward(h: np.ndarray, da: np.ndarray) -> np.ndarray:
+    """dh = da * GELU'(h) for the exact (erf) GELU h Phi(h):
+    GELU'(h) = Phi(h) + h phi(h), Phi the standard normal distribution function
+    and phi its density ([ViT-pt] §2: the FFN's activation between its two
+    projections)."""
+    h = np.asarray(h, dtype=np.float64)
+    Phi = 0.5 * (1.0 + _erf(h / math.sqrt(2.0)))
+    phi = np.exp(-0.5 * h * h) / math.sqrt(2.0 * math.pi)
+    return np.asarray(da, dtype=np.float64) * (Phi + h * phi)
+
+
 def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
     """Gradients of L = sum(dy * y) through the experts of a square layer,
     with the routing and the gates held at ``routing`` (they are piecewise
@@ -435,10 +446,14 @@ def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
     straight-through estimator, du = alpha W_base^T dz) and the input rotation
     (dtheta_e, dx_t += its input gradient).  Also returns the gates'
     gradients dgate[t][j] = dy_t . o.
-    Returns dict(theta, phi [N][L][n/2], w_base [d][d], x [T][d], gate [T][k])."""
+    Returns dict(theta, phi [N][L][n/2], w_base [d][d], x [T][d], gate [T][k]).
+
+    FFN layers (two substrates, a GELU or the identity between) go through
+    ``_ffn_backward``: the same chain twice with the activation's derivative
+    between; their dict holds lists (up, down) for theta, phi and w_base."""
     cfg, x, _ = _inputs_f64(inp)
     if cfg.is_ffn:
-        raise ValueError("square experts only")
+        return _ffn_backward(inp, cfg, x, np.asarray(dy, dtype=np.float64), routing)
     dy = np.asarray(dy, dtype=np.float64)
     alpha = cfg.w_scale
     W = np.asarray(inp.w_base[0], dtype=np.float64)
@@ -464,6 +479,46 @@ def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
         dX, dth[e] = butterfly_backward(th, X, dU, True)
         np.add.at(dx, tok, dX.T)
     return {"theta": dth, "phi": dph, "w_base": dW, "x": dx, "gate": dgate}
+
+
+def _ffn_backward(inp, cfg, x, dy, routing):
+    """The FFN form of ``layer_backward_experts``: per routed slot
+        u = B(th_up)^T x, h1 = alpha W_up u, h = B(ph_up) h1, a = act(h),
+        v = B(th_dn)^T a, z = alpha W_dn v, o = B(ph_dn) z, y_t += g o
+    walked back one step at a time ([ViT-pt] §2: rotations before and after
+    each shared substrate of the FFN)."""
+    alpha = cfg.w_scale
+    Wu = np.asarray(inp.w_base[0], dtype=np.float64)
+    Wd = np.asarray(inp.w_base[1], dtype=np.float64)
+    out = {"theta": [np.zeros(np.shape(inp.theta[0])), np.zeros(np.shape(inp.theta[1]))],
+           "phi": [np.zeros(np.shape(inp.phi[0])), np.zeros(np.shape(inp.phi[1]))],
+           "w_base": [np.zeros(Wu.shape), np.zeros(Wd.shape)],
+           "x": np.zeros(x.shape), "gate": np.zeros(routing.gates.shape)}
+    use_gelu = cfg.ffn_act == "gelu"
+    for e in np.unique(routing.idx):
+        tok, slot = np.nonzero(routing.idx == e)
+        thu, phu = (np.asarray(a[e], dtype=np.float64) for a in (inp.theta[0], inp.phi[0]))
+        thd, phd = (np.asarray(a[e], dtype=np.float64) for a in (inp.theta[1], inp.phi[1]))
+        X = x[tok].T
+        U = butterfly_apply(thu, X, transpose=True)
+        H1 = alpha * (Wu @ U)
+        H = butterfly_apply(phu, H1)
+        A = gelu(H) if use_gelu else H
+        V = butterfly_apply(thd, A, transpose=True)
+        Z = alpha * (Wd @ V)
+        O = butterfly_apply(phd, Z)
+        dO = dy[tok].T * routing.gates[tok, slot][None, :]
+        out["gate"][tok, slot] = np.sum(dy[tok].T * O, axis=0)
+        dZ, dphd = butterfly_backward(phd, Z, dO, False)
+        out["w_base"][1] += substrate_weight_grad(V.T, dZ.T, alpha)
+        dA, dthd = butterfly_backward(thd, A, alpha * (Wd.T @ dZ), True)
+        dH = gelu_backward(H, dA) if use_gelu else dA
+        dH1, dphu = butterfly_backward(phu, H1, dH, False)
+        out["w_base"][0] += substrate_weight_grad(U.T, dH1.T, alpha)
+        dX, dthu = butterfly_backward(thu, X, alpha * (Wu.T @ dH1), True)
+        np.add.at(out["x"], tok, dX.T)
+        out["theta"][0][e], out["phi"][0][e], out["theta"][1][e], out["phi"][1][e] = dthu, dphu, dthd, dphd
+    return out
 
 
 def substrate_weight_grad(U: np.ndarray, dZ: np.ndarray, alpha: float = 1.0) -> np.ndarray:

@@ -490,3 +490,58 @@ def test_full_layer_gradient_is_experts_plus_router():
         assert abs(fd(inp.x, (t, i), h) - want) < 1e-5 * (1 + abs(want))
     for (n, i) in ((int(R.idx[0, 0]), 1), (int(R.idx[2, 1]), 6)):
         assert abs(fd(inp.w_gate, (n, i), h) - dwg[n, i]) < 1e-5 * (1 + abs(dwg[n, i]))
+
+
+def test_gelu_backward_closed_forms_and_differences():
+    h = np.array([-6.0, -1.5, -0.3, 0.0, 0.2, 1.0, 2.5, 8.0])
+    da = np.linspace(0.5, 2.0, h.size)
+    d = ref.gelu_backward(h, da)
+    # at 0 the slope is 1/2; far left 0, far right 1
+    assert abs(d[3] / da[3] - 0.5) < 1e-15
+    assert abs(d[0] / da[0]) < 1e-7 and abs(d[-1] / da[-1] - 1.0) < 1e-12
+    # central differences of the oracle's GELU
+    eps = 1e-6
+    fd = (ref.gelu(h + eps) - ref.gelu(h - eps)) / (2 * eps)
+    assert np.allclose(d, da * fd, rtol=1e-8, atol=1e-10)
+
+
+@pytest.mark.parametrize("act", ["gelu", "none"])
+def test_ffn_layer_backward_finite_differences(act):
+    # the FFN form: angles of all four rotations, both substrates' entries
+    # (real-valued), inputs and gates, against central differences of the
+    # oracle's layer forward with the routing held
+    cfg = wl.small_config(d_model=8, d_ff=16, n_experts=3, top_k=2, tokens=4, act="f32", ffn_act=act,
+                          w_scale=0.5, seed_index=31)
+    inp = wl.generate(cfg)
+    for lst in (inp.theta, inp.phi, inp.w_base):
+        for i in range(2):
+            lst[i] = lst[i].astype(np.float64)
+    R = ref.route(ref.stored_to_f64(inp.x, "f32"), ref.stored_to_f64(inp.w_gate, "f32"), cfg.top_k)
+    dy = np.random.default_rng(4).standard_normal((cfg.tokens, cfg.d_model))
+    g = ref.layer_backward_experts(inp, dy, R)
+
+    def loss():
+        return float(np.sum(dy * ref.forward(inp, routing=R)[0]))
+
+    def fd(arr, ix, h):
+        old = arr[ix]
+        arr[ix] = old + h
+        lp = loss()
+        arr[ix] = old - h
+        lm = loss()
+        arr[ix] = old
+        return (lp - lm) / (2 * h)
+
+    e = int(R.idx[0, 0])
+    for side in (0, 1):
+        for arr, grad in ((inp.theta[side], g["theta"][side]), (inp.phi[side], g["phi"][side])):
+            L = arr.shape[1]   # the input and output rotations act on different widths
+            for (s_, p) in ((0, 0), (L - 1, 1)):
+                want = grad[e, s_, p]
+                assert abs(fd(arr, (e, s_, p), 1e-6) - want) < 1e-6 * (1 + abs(want))
+        want = g["w_base"][side][1, 2]
+        assert abs(fd(inp.w_base[side], (1, 2), 1e-6) - want) < 1e-6 * (1 + abs(want))
+    want = g["x"][1, 3]
+    assert abs(fd(inp.x, (1, 3), 2.0 ** -12) - want) < 1e-5 * (1 + abs(want))
+    want = g["gate"][2, 1]
+    assert abs(fd(R.gates, (2, 1), 1e-3) - want) < 1e-8 * (1 + abs(want))
