@@ -20,7 +20,7 @@ import numpy as np
 __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
     "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad",
-    "combine_backward", "router_backward", "STATUS", "EXPORTED_SYMBOLS",
+    "combine_backward", "router_backward", "gelu_backward", "STATUS", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = [
     "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
     "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
     "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
-    "bmoe_router_backward_workspace", "bmoe_router_backward",
+    "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward",
 ]
 
 
@@ -113,12 +113,13 @@ def lib() -> ctypes.CDLL:
     L.bmoe_router_backward_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
     L.bmoe_router_backward.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                        c_vp, c_sz, c_vp]
+    L.bmoe_gelu_backward.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
     for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
                  "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
                  "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
                  "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
                  "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
-                 "bmoe_router_backward_workspace", "bmoe_router_backward"):
+                 "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward"):
         getattr(L, name).restype = c_i32
     _lib = L
     return L
@@ -393,6 +394,17 @@ def router_backward(x, w_gate, topk_idx, d_gate, renorm: bool = False):
                                       _ptr(x), _ptr(w_gate), _ptr(topk_idx), _ptr(d_gate), _ptr(dx), _ptr(dwg),
                                       _ptr(ws), int(nb.value), _stream_handle()))
     return dx, dwg
+
+
+def gelu_backward(h, da, dh=None):
+    """dh = da * GELU'(h) (exact erf GELU), elementwise; h, da [rows][width]."""
+    torch = _torch()
+    rows, width = int(h.shape[0]), int(h.shape[1])
+    if dh is None:
+        dh = torch.empty_like(h)
+    _check(lib().bmoe_gelu_backward(rows, width, BF16 if h.dtype == torch.bfloat16 else F32, _ptr(h), _ptr(da),
+                                    _ptr(dh), _stream_handle()))
+    return dh
 
 
 def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):

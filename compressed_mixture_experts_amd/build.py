@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbmoe.so")
 SOURCES = ["api.hip", "route.hip", "gemm.hip", "butterfly.hip", "butterfly_dbg.hip",
            "butterfly_in.hip", "butterfly_mid.hip", "butterfly_out.hip", "fused.hip", "fused_mfma.hip", "prep.hip", "gemm_fp4.hip",
-           "butterfly_split.hip", "butterfly_bwd.hip", "substrate_grad.hip", "combine_bwd.hip", "router_bwd.hip"]
+           "butterfly_split.hip", "butterfly_bwd.hip", "substrate_grad.hip", "combine_bwd.hip", "router_bwd.hip", "gelu_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -961,3 +961,23 @@ bmoe_status bmoe_router_backward(int32_t T, int32_t d, int32_t n_experts, int32_
                              renorm_gates, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
   return ok();
 }
+
+// ---------------------------------------------------------------- GELU derivative
+bmoe_status bmoe_gelu_backward(int32_t rows, int32_t width, int32_t dtype, const void* h, const void* da, void* dh,
+                               hipStream_t stream) {
+  if (rows < 0 || width < 8 || width % 8 != 0 || int64_t(rows) * width > (int64_t(1) << 31) - 1)
+    return fail(BMOE_ERR_SHAPE, "rows=%d, width=%d: need rows >= 0, width a multiple of 8, rows * width below 2^31",
+                rows, width);
+  if (dtype != BMOE_F32 && dtype != BMOE_BF16) return fail(BMOE_ERR_DTYPE, "dtype=%d is unknown", dtype);
+  if (rows == 0) return ok();
+  if (!h || !da || !dh) return fail(BMOE_ERR_NULL, "h / da / dh is NULL");
+  if (!aligned(h, 16) || !aligned(da, 16) || !aligned(dh, 16)) return fail(BMOE_ERR_ALIGN, "h, da and dh must be 16-byte aligned");
+  const size_t bytes = size_t(rows) * width * (dtype == BMOE_BF16 ? 2 : 4);
+  const Range rh{h, bytes}, rd{da, bytes}, ro{dh, bytes};
+  if ((dh != h && overlap(ro, rh)) || (dh != da && overlap(ro, rd)))
+    return fail(BMOE_ERR_ALIAS, "dh overlaps h or da without being the same buffer");
+  const bmoe_status st = check_device();
+  if (st != BMOE_OK) return st;
+  BMOE_HIP(launch_gelu_bwd(h, da, dh, size_t(rows) * width, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
+  return ok();
+}

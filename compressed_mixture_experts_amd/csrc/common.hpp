@@ -243,6 +243,7 @@ hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
 size_t bfly_bwd_workspace(int log2n, int n_experts, int rows);
 bool sgrad_shape_ok(int M, int N);
 size_t router_bwd_workspace(int T, int d, int N);
+hipError_t launch_gelu_bwd(const void* h, const void* da, void* dh, size_t n, int act, hipStream_t s);
 hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, const float* dgate, float* dx,
                              float* dwg, void* ws, int T, int d, int N, int k, int renorm, int act, hipStream_t s);
 hipError_t launch_combine_bwd(const void* dy, const int32_t* slots, const float* gate, const void* o, void* d_rows,

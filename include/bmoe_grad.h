@@ -141,6 +141,24 @@ bmoe_status bmoe_router_backward(int32_t T, int32_t d, int32_t n_experts, int32_
                                  const float* d_gate, float* dx, float* dw_gate, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
+/* Derivative of the FFN experts' activation (ButterflyViT,
+ * gist.science/pt/paper/2603.06746, §2; the exact (erf) GELU of bmoe.h's FFN
+ * layers, with the same erf approximation, |error| <= 1.5e-7):
+ *     dh = da * (Phi(h) + h phi(h))  elementwise,
+ * Phi / phi the standard normal distribution function / density.
+ *   h   [rows][width] of dtype (device, 16-byte aligned): the activation's
+ *       input (the FFN middle's first rotation output), read only.
+ *   da  [rows][width] of dtype (device, 16-byte aligned): gradient at the
+ *       activation's output, read only.
+ *   dh  [rows][width] of dtype (device, 16-byte aligned), written; may be the
+ *       same buffer as h or da, must not overlap them otherwise.
+ * width a multiple of 8.  Enqueued on `stream`, nothing allocated or
+ * synchronised.  Errors: BMOE_ERR_SHAPE, BMOE_ERR_DTYPE, BMOE_ERR_NULL,
+ * BMOE_ERR_ALIGN, BMOE_ERR_ALIAS, BMOE_ERR_HIP; all but the last are detected
+ * before anything is enqueued. */
+bmoe_status bmoe_gelu_backward(int32_t rows, int32_t width, int32_t dtype, const void* h, const void* da, void* dh,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -447,3 +447,18 @@ def test_router_backward_arguments():
     assert call(x=x + 8) == 4 and call(w=w + 2) == 4 and call(dg=dg + 2) == 4 and call(ws=ws + 8) == 4
     assert call(wsb=need - 4) == 6
     assert call(dx=x) == 5 and call(dw=w + 16) == 5 and call(ws=dx) == 5
+
+
+def test_gelu_backward_arguments():
+    L = bm.lib()
+    F = FAKE
+    h, da, dh = F + 0x100000, F + 0x200000, F + 0x300000
+
+    def call(rows=10, w=64, dt=bm.F32, h=h, da=da, dh=dh):
+        return L.bmoe_gelu_backward(rows, w, dt, h, da, dh, None)
+
+    assert call(w=12) == 2 and call(rows=-1) == 2 and call(rows=1 << 20, w=4096) == 2
+    assert call(dt=3) == 3
+    assert call(h=None) == 1 and call(dh=None) == 1
+    assert call(h=h + 4) == 4 and call(dh=dh + 8) == 4
+    assert call(dh=h + 16) == 5 and call(dh=da + 256) == 5   # partial overlaps

@@ -176,3 +176,102 @@ def test_router_backward_zero_tokens():
     dx, dwg = bm.router_backward(x, wd, idx, dg)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dwg).item() == 0 and dx.shape == (0, 64)
+
+
+def test_gelu_backward_matches_oracle():
+    import torch
+    r = np.random.default_rng(12)
+    for act in ("f32", "bf16"):
+        h = wl._store(3.0 * r.standard_normal((300, 256)), act)
+        da = wl._store(r.standard_normal((300, 256)), act)
+        dev = lambda a: (torch.from_numpy(np.ascontiguousarray(a)).cuda() if act == "f32"
+                         else torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16))
+        hd, dad = dev(h), dev(da)
+        dh = bm.gelu_backward(hd, dad)
+        dh2 = bm.gelu_backward(hd, dad.clone(), dh=None)
+        inplace = dad.clone()
+        bm.gelu_backward(hd, inplace, dh=inplace)
+        torch.cuda.synchronize()
+        want = ref.gelu_backward(ref.stored_to_f64(h, act), ref.stored_to_f64(da, act))
+        got = dh.float().cpu().numpy().astype(np.float64)
+        # fp32 arithmetic (the erf approximation within 1.5e-7), then for bf16
+        # the output's rounding: half a step, 2^-8 of the result at most
+        rnd = 2.0 ** -8 if act == "bf16" else 0.0
+        assert np.all(np.abs(got - want) <= rnd * np.abs(want) + 2e-6 * np.abs(ref.stored_to_f64(da, act)) + 1e-30)
+        assert torch.equal(dh, dh2) and torch.equal(dh, inplace)
+
+
+def test_ffn_layer_backward_composed_from_the_abi():
+    # the FFN form: route -> (input rotation, up substrate, up rotation, GELU,
+    # down input rotation, down substrate, output rotation) forward values ->
+    # combine backward -> each piece's backward in reverse, GELU's derivative
+    # between the two substrates; against the oracle's FFN backward
+    import torch
+    cfg = wl.small_config(d_model=128, d_ff=256, n_experts=4, top_k=2, tokens=300, act="f32", w_scale=0.5,
+                          seed_index=19)
+    inp = wl.generate(cfg)
+    x64 = ref.stored_to_f64(inp.x, "f32")
+    R = ref.route(x64, ref.stored_to_f64(inp.w_gate, "f32"), cfg.top_k)
+    layer = bm.Layer.from_inputs(inp)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = dev(inp.x)
+    log("ffn layer backward: route")
+    idx, gate, off, slots = layer.route(x, with_buckets=True)
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == R.idx).all(), "routing differs from the oracle (pick a seed without near ties)"
+    k, d, f, N, alpha = cfg.top_k, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.w_scale
+    offs = off.cpu().numpy()
+    thu, phu = dev(inp.theta[0].astype(np.float32)), dev(inp.phi[0].astype(np.float32))
+    thd, phd = dev(inp.theta[1].astype(np.float32)), dev(inp.phi[1].astype(np.float32))
+    Wu, Wd = inp.w_base[0], inp.w_base[1]          # [f][d], [d][f]
+    pk = lambda W: dev(bm.pack_ternary(np.ascontiguousarray(W)).view(np.int32))
+    Wup, WupT, Wdp, WdpT = pk(Wu), pk(Wu.T), pk(Wd), pk(Wd.T)
+    tok = (slots // k).long()
+    xb = x[tok].contiguous()
+
+    def per_expert(ang, rows, transpose):
+        out = torch.empty_like(rows)
+        for e in range(N):
+            if offs[e + 1] > offs[e]:
+                out[offs[e]:offs[e + 1]] = bm.dbg_butterfly(ang[e], rows[offs[e]:offs[e + 1]].contiguous(),
+                                                            transpose=transpose)
+        return out
+
+    U = per_expert(thu, xb, True)
+    H1 = bm.dbg_ternary_gemm(U, Wup, f, alpha)
+    H = per_expert(phu, H1, False)
+    A = torch.nn.functional.gelu(H, approximate="none")
+    V = per_expert(thd, A, True)
+    Z = bm.dbg_ternary_gemm(V, Wdp, d, alpha)
+    O = per_expert(phd, Z, False)
+    dy64 = np.random.default_rng(6).standard_normal((cfg.tokens, d))
+    dy = dev(dy64.astype(np.float32))
+    log("ffn layer backward: pieces")
+    d_rows, d_gate = bm.combine_backward(dy, slots, gate.reshape(-1).contiguous(), k, O)
+    dZ, dphd = bm.butterfly_backward(phd, off, Z, d_rows, False)
+    dV = bm.dbg_ternary_gemm(dZ, WdpT, f, alpha)
+    dA, dthd = bm.butterfly_backward(thd, off, A, dV, True)
+    dH = bm.gelu_backward(H, dA)
+    dH1, dphu = bm.butterfly_backward(phu, off, H1, dH, False)
+    dU = bm.dbg_ternary_gemm(dH1, WupT, d, alpha)
+    dxb, dthu = bm.butterfly_backward(thu, off, xb, dU, True)
+    dWu = bm.substrate_grad(dH1.to(torch.bfloat16), U.to(torch.bfloat16), alpha)
+    dWd = bm.substrate_grad(dZ.to(torch.bfloat16), V.to(torch.bfloat16), alpha)
+    dx = torch.zeros_like(x).index_add_(0, tok, dxb)
+    torch.cuda.synchronize()
+
+    want = ref.layer_backward_experts(inp, dy64.astype(np.float32).astype(np.float64), R)
+    for got, ref_, what in ((dthu, want["theta"][0], "theta_up"), (dphu, want["phi"][0], "phi_up"),
+                            (dthd, want["theta"][1], "theta_dn"), (dphd, want["phi"][1], "phi_dn")):
+        g_ = got.cpu().numpy()
+        for e in range(N):
+            nr = np.linalg.norm(ref_[e])
+            if nr == 0:
+                assert not g_[e].any(), f"expert {e} d{what} should be zero"
+            else:
+                assert np.linalg.norm(g_[e] - ref_[e]) <= 1e-4 * nr, f"expert {e} d{what}"
+    assert row_rel_err(dx.cpu().numpy().astype(np.float64), want["x"]).max() <= 1e-4
+    dg = d_gate.cpu().numpy().reshape(cfg.tokens, k)
+    assert np.abs(dg - want["gate"]).max() <= 1e-4 * np.abs(want["gate"]).max()
+    for got, ref_ in ((dWu, want["w_base"][0]), (dWd, want["w_base"][1])):
+        assert np.linalg.norm(got.cpu().numpy() - ref_) <= 1e-2 * np.linalg.norm(ref_)
