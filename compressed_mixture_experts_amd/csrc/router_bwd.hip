@@ -15,10 +15,11 @@
 //                      by broadcast), softmax over the workgroup, dl [T][N] to
 //                      the workspace;
 //   router_dx_kernel   16 tokens per workgroup (their dl rows in LDS), a
-//                      thread per column of x;
+//                      thread per column of x, four experts' gate rows loaded
+//                      ahead;
 //   router_dwg_kernel  16 experts x 256 columns per workgroup (dl of 256
 //                      tokens at a time in LDS), the tokens split in ranges of
-//                      at least 256 when the tiles are few; the ranges'
+//                      at least 256 for about 2048 workgroups; the ranges'
 //                      partial sums added in order by router_red_kernel.
 #include "common.hpp"
 
@@ -161,18 +162,25 @@ __global__ __launch_bounds__(256) void router_dx_kernel(RouterBwdArgs a) {
   for (int t = 0; t < RB_BT; ++t)
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[t][c] = 0.f;
-  for (int n = 0; n < a.N; ++n) {
-    float w[CPT];
+  // four experts' gate rows in flight at a time
+  for (int n0 = 0; n0 < a.N; n0 += 4) {
+    float w[4][CPT];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int i = tid + 256 * c;
-      w[c] = i < a.d ? load1<A>(a.wg, size_t(n) * a.d + i) : 0.f;
-    }
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int t = 0; t < RB_BT; ++t) {
-      const float l = sL[t][n];
+      for (int c = 0; c < CPT; ++c) {
+        const int i = tid + 256 * c, n = n0 + u;
+        w[u][c] = (i < a.d && n < a.N) ? load1<A>(a.wg, size_t(n) * a.d + i) : 0.f;
+      }
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[t][c] = fmaf(l, w[c], acc[t][c]);
+    for (int u = 0; u < 4; ++u) {
+      const int n = n0 + u < a.N ? n0 + u : a.N - 1;  // w is zero past N
+#pragma unroll
+      for (int t = 0; t < RB_BT; ++t) {
+        const float l = sL[t][n];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[t][c] = fmaf(l, w[u][c], acc[t][c]);
+      }
     }
   }
 #pragma unroll
@@ -236,13 +244,13 @@ __global__ __launch_bounds__(256) void router_zero_kernel(float* p, size_t n) {
   if (q < n) p[q] = 0.f;
 }
 
-// token ranges of the dW_g pass: none when its tiles reach 512 workgroups, else
-// up to that many with at least 256 tokens each
+// token ranges of the dW_g pass: none when its tiles reach 2048 workgroups,
+// else up to that many with at least 256 tokens each
 int router_bwd_splits(int T, int d, int N, int* tchunk) {
   const int tiles = ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
   int S = 1;
-  if (tiles < 512) {
-    S = (512 + tiles - 1) / tiles;
+  if (tiles < 2048) {
+    S = (2048 + tiles - 1) / tiles;
     const int smax = (T + 255) / 256;
     S = S < smax ? S : smax;
     S = S < 1 ? 1 : S;

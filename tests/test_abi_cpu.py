@@ -422,8 +422,8 @@ def test_router_backward_arguments():
             return 0
         tiles = -(-N // 16) * -(-d // 256)
         S = 1
-        if tiles < 512:
-            S = max(1, min(-(-512 // tiles), -(-T // 256)))
+        if tiles < 2048:
+            S = max(1, min(-(-2048 // tiles), -(-T // 256)))
         tc = max(1, -(-T // S))
         S = max(1, -(-T // tc))
         return -(-T * N * 4 // 256) * 256 + (S * N * d * 4 if S > 1 else 0)
