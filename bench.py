@@ -275,7 +275,8 @@ def outlier_spread(n_experts: int = 8) -> dict:
 
 def grad_measure(reps: int = 20) -> dict:
     """Butterfly backward (bmoe_butterfly_backward) at the routed-row shapes of
-    the edge workload (input rotation, width 512) and the large workload
+    the edge workload (input rotation, width 512), the ViT FFN workload (input
+    rotation, width 1024) and the large workload
     (input rotation, width 2048; FFN up rotation, width 8192): bf16 rows
     bucketed evenly over the experts, fp32 angles.  Per shape: mean time per
     call (HIP events on torch's stream) and the rate of its algorithmic HBM
@@ -287,6 +288,7 @@ def grad_measure(reps: int = 20) -> dict:
     import compressed_mixture_experts_amd as bm
     out = []
     for name, rows, n, N, tr in (("edge_d512_n64 input rotation", 8192, 512, 64, True),
+                                 ("vit_ffn_d1024_n64 input rotation", 16384, 1024, 64, True),
                                  ("large_d2048_n256 input rotation", 65536, 2048, 256, True),
                                  ("large_d2048_n256 ffn up rotation", 65536, 8192, 256, False)):
         L = int(math.log2(n))

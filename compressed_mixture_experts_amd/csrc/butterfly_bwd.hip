@@ -763,34 +763,42 @@ __global__ __launch_bounds__(256) void bfly_high_kernel(BflyPartArgs a) {
   }
 }
 
-// ---- width 2048 in one pass: a workgroup's four waves hold one row, wave w
-// its 512-element slot w in the low part's layouts 0..2 (stages 0..8), and
-// a fourth layout, lane l' = 64 w + lane holding the elements l' + 256 j
-// (j = 0..7, index bits 8..10), runs stages 9 and 10.  The change between
-// layouts 2 and 3 crosses waves, through a 2048-float row buffer in LDS and a
-// workgroup barrier; the buffers of the forward and the backward change are
-// distinct, so two barriers per row suffice.
-template <int TR, int ACT>
-__global__ __launch_bounds__(256) void bfly_row11_kernel(BflyPartArgs a) {
+// ---- widths 1024 and 2048 in one pass: NW = n / 512 waves hold a row (the
+// workgroup's four waves work on 4 / NW rows at a time), wave w its
+// 512-element slot w % NW in the low part's layouts 0..2 (stages 0..8), and a
+// fourth layout, lane l' = 64 (w % NW) + lane holding the elements
+// l' + 2^(L-3) j (j = 0..7, index bits L-3 .. L-1), runs stages 9 .. L-1.  The
+// change between layouts 2 and 3 crosses waves, through a row buffer in LDS
+// and a workgroup barrier; the buffers of the forward and the backward change
+// are distinct, so two barriers per row step suffice.  Every wave takes the
+// same number of row steps (a step past the chunk's end loads and stores
+// nothing), and at width 1024 the two rows' waves of a slot add their angle
+// gradients in LDS at the end.
+template <int L, int TR, int ACT>
+__global__ __launch_bounds__(256) void bfly_row_kernel(BflyPartArgs a) {
   using P = BpLow<9>;
-  constexpr int L = 11, n = 2048, half = 1024;
+  constexpr int n = 1 << L, half = n / 2;
+  constexpr int NW = n / 512, RPW = 4 / NW;        // waves per row, rows per step
+  constexpr int B3 = L - 3, NST3 = L - 9;          // layout 3: base bit, stages
+  static_assert(L == 10 || L == 11, "widths 1024 and 2048");
   constexpr int G0 = TR ? 3 : 0, G3 = TR ? 0 : 3;  // first and last layout applied
   __shared__ __attribute__((aligned(16))) float xw[4][512];   // in-wave layout changes
-  __shared__ __attribute__((aligned(16))) float xf[2048];     // forward 2 <-> 3
+  __shared__ __attribute__((aligned(16))) float xf[2048];     // forward 2 <-> 3 (RPW rows)
   __shared__ __attribute__((aligned(16))) float xb[2][2048];  // backward 3 <-> 2 (values, gradients)
   __shared__ int s_info[3];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lp = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rs = w / NW, slot = w % NW, lp = slot * 64 + lane;
   const int cb = blockIdx.x;
   bp_chunk_info(a, cb, s_info);
   const int e = s_info[0];
   if (e < 0) return;
   const int c0 = s_info[1], ccnt = s_info[2];
   const float* ang = a.ang + size_t(e) * L * half;
-  const int sbase = w * 512;
-  // row index of element j of this lane in layout G
-  auto elem = [&](int G, int j) { return G < 3 ? sbase + P::elem(G, lane, j) : lp | (j << 8); };
+  const int sbase = slot * 512;
+  // index in the row of element j of this lane in layout G
+  auto elem = [&](int G, int j) { return G < 3 ? sbase + P::elem(G, lane, j) : lp | (j << B3); };
 
-  // groups 0..2: stages 3G .. 3G+2; group 3: stages 9, 10 (j bits 1, 2)
+  // groups 0..2: stages 3G .. 3G+2; group 3: stages 9 .. L-1 (j bits 12-L ..)
   float cc[4][3][4], ss[4][3][4], acc[4][3][4];
 #pragma unroll
   for (int G = 0; G < 4; ++G)
@@ -801,15 +809,15 @@ __global__ __launch_bounds__(256) void bfly_row11_kernel(BflyPartArgs a) {
         cc[G][ti][k] = 1.f;
         ss[G][ti][k] = 0.f;
         acc[G][ti][k] = 0.f;
-        if (G < 3 || ti < 2) {
-          const int t = G < 3 ? 3 * G + ti : 9 + ti, p = G < 3 ? ti : ti + 1;
+        if (G < 3 || ti < NST3) {
+          const int t = G < 3 ? 3 * G + ti : 9 + ti, p = G < 3 ? ti : 12 - L + ti;
           const float2 v = bb_sincos(ang[t * half + pair_of(elem(G, pair_lo(k, p)), t)]);
           cc[G][ti][k] = v.x;
           ss[G][ti][k] = TR ? -v.y : v.y;
         }
       }
-  constexpr int NST[4] = {3, 3, 3, 2};
-  auto jbit = [](int G, int ti) { return G < 3 ? ti : ti + 1; };
+  constexpr int NST[4] = {3, 3, 3, NST3};
+  auto jbit = [](int G, int ti) { return G < 3 ? ti : 12 - L + ti; };
   auto fwd_group = [&](int G, float (&x)[8]) {
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
@@ -875,19 +883,29 @@ __global__ __launch_bounds__(256) void bfly_row11_kernel(BflyPartArgs a) {
     }
   };
 
+  float* XF = xf + rs * n;
+  float* XB0 = xb[0] + rs * n;
+  float* XB1 = xb[1] + rs * n;
+  const int rend = c0 + ccnt, steps = (ccnt + RPW - 1) / RPW;
   float xn[8], gn[8];
-  load(a.in0, c0, G0, xn);
-  load(a.in1, c0, G3, gn);
-  for (int r = c0; r < c0 + ccnt; ++r) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) xn[j] = gn[j] = 0.f;
+  if (c0 + rs < rend) {
+    load(a.in0, c0 + rs, G0, xn);
+    load(a.in1, c0 + rs, G3, gn);
+  }
+  for (int it = 0; it < steps; ++it) {
+    const int r = c0 + it * RPW + rs;
+    const bool act = r < rend;  // a step past the end works on zeros: no gradient, no store
     float x[8], g[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      x[j] = xn[j];
-      g[j] = gn[j];
+      x[j] = act ? xn[j] : 0.f;
+      g[j] = act ? gn[j] : 0.f;
     }
-    if (r + 1 < c0 + ccnt) {
-      load(a.in0, r + 1, G0, xn);
-      load(a.in1, r + 1, G3, gn);
+    if (r + RPW < rend) {
+      load(a.in0, r + RPW, G0, xn);
+      load(a.in1, r + RPW, G3, gn);
     }
     // forward, layouts in the order of application
 #pragma unroll
@@ -896,9 +914,9 @@ __global__ __launch_bounds__(256) void bfly_row11_kernel(BflyPartArgs a) {
       if (q > 0) {
         const int Gp = TR ? G + 1 : G - 1;
         if (G == 3 || Gp == 3) {
-          put(xf, x, Gp);
+          put(XF, x, Gp);
           __syncthreads();
-          get(xf, x, G);
+          get(XF, x, G);
         } else {
           xch_wave(x, Gp, G);
         }
@@ -913,31 +931,48 @@ __global__ __launch_bounds__(256) void bfly_row11_kernel(BflyPartArgs a) {
       if (q > 0) {
         const int Gp = TR ? G + 1 : G - 1;  // the layout applied before G
         if (G == 3 || Gp == 3) {
-          put(xb[0], x, G);
-          put(xb[1], g, G);
+          put(XB0, x, G);
+          put(XB1, g, G);
           __syncthreads();
-          get(xb[0], x, Gp);
-          get(xb[1], g, Gp);
+          get(XB0, x, Gp);
+          get(XB1, g, Gp);
         } else {
           xch_wave(x, G, Gp);
           xch_wave(g, G, Gp);
         }
       }
     }
-    store(a.out, r, G0, g);
+    if (act) store(a.out, r, G0, g);
   }
 
   float* part = a.part + size_t(cb) * L * half;
+  float* red = xb[0];  // 4 waves x 1024 floats (free after the last row step)
 #pragma unroll
-  for (int G = 0; G < 4; ++G)
+  for (int G = 0; G < 4; ++G) {
+    if constexpr (RPW > 1) {
+      __syncthreads();  // every wave is past its rows (or the previous group)
+#pragma unroll
+      for (int ti = 0; ti < 3; ++ti)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (G < 3 || ti < NST3) red[w * 1024 + (ti * 4 + k) * 64 + lane] = acc[G][ti][k];
+      __syncthreads();
+    }
 #pragma unroll
     for (int ti = 0; ti < 3; ++ti)
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (G < 3 || ti < 2) {
-          const int t = G < 3 ? 3 * G + ti : 9 + ti;
-          part[t * half + pair_of(elem(G, pair_lo(k, jbit(G, ti))), t)] = acc[G][ti][k];
+        if ((G < 3 || ti < NST3) && rs == 0) {
+          const int t = G < 3 ? 3 * G + ti : 9 + ti, q = (ti * 4 + k) * 64 + lane;
+          float v = acc[G][ti][k];
+          if constexpr (RPW > 1) {
+            v = red[w * 1024 + q];
+#pragma unroll
+            for (int o = 1; o < RPW; ++o) v += red[(w + o * NW) * 1024 + q];
+          }
+          part[t * half + pair_of(elem(G, pair_lo(k, jbit(G, ti))), t)] = v;
         }
+  }
 }
 
 template <int S, int HIGH, int TR, int A0, int A1, int AO, int BWD>
@@ -981,8 +1016,8 @@ static int bp_chunk(int rows) {
   return 32 * k;
 }
 
-// rows per chunk at width 2048 (one workgroup per chunk): a multiple of 16, at
-// most 128, about 1024 chunks or more
+// rows per chunk at widths 1024 and 2048 (one workgroup per chunk): a multiple
+// of 16, at most 128, about 1024 chunks or more
 static int row11_chunk(int rows) {
   int k = rows / (16 * 1024);
   k = k < 1 ? 1 : k > 8 ? 8 : k;
@@ -998,7 +1033,7 @@ static int row9_chunk(int rows) {
 
 static int bwd_chunk(int log2n, int rows) {
   return log2n >= 12 ? bp_chunk(rows)
-       : log2n == 11 ? row11_chunk(rows)
+       : log2n == 11 || log2n == 10 ? row11_chunk(rows)
        : log2n == 9  ? row9_chunk(rows)
                      : bfly_bwd_chunk(log2n, rows);
 }
@@ -1040,7 +1075,6 @@ static hipError_t bb_launch_act(const BflyBwdArgs& a, int L, hipStream_t s) {
     case 6: return bb_launch<6, ACT>(a, s);
     case 7: return bb_launch<7, ACT>(a, s);
     case 8: return bb_launch<8, ACT>(a, s);
-    case 10: return bb_launch<10, ACT>(a, s);
     default: return hipErrorInvalidValue;  // width 2048 and more take the register kernels
   }
 }
@@ -1081,18 +1115,21 @@ hipError_t launch_bfly_bwd(const void* x, const void* dy, void* dx, const float*
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-  } else if (rows > 0 && L == 11) {
+  } else if (rows > 0 && (L == 10 || L == 11)) {
     a.chunk = row11_chunk(rows);
     a.n_chunks = (rows + a.chunk - 1) / a.chunk + n_experts;
     const BflyPartArgs pa{x, dy, dx, ang, offsets, part, rows, n_experts, a.chunk, a.n_chunks};
     const bool bf = act == ACT_BF16, tr = transpose != 0;
-    if (tr) {
-      if (bf) hipLaunchKernelGGL((bfly_row11_kernel<1, ACT_BF16>), dim3(a.n_chunks), dim3(256), 0, s, pa);
-      else hipLaunchKernelGGL((bfly_row11_kernel<1, ACT_F32>), dim3(a.n_chunks), dim3(256), 0, s, pa);
-    } else {
-      if (bf) hipLaunchKernelGGL((bfly_row11_kernel<0, ACT_BF16>), dim3(a.n_chunks), dim3(256), 0, s, pa);
-      else hipLaunchKernelGGL((bfly_row11_kernel<0, ACT_F32>), dim3(a.n_chunks), dim3(256), 0, s, pa);
+#define BB_ROW(LL)                                                                                      \
+    if (tr) {                                                                                           \
+      if (bf) hipLaunchKernelGGL((bfly_row_kernel<LL, 1, ACT_BF16>), dim3(a.n_chunks), dim3(256), 0, s, pa); \
+      else hipLaunchKernelGGL((bfly_row_kernel<LL, 1, ACT_F32>), dim3(a.n_chunks), dim3(256), 0, s, pa);    \
+    } else {                                                                                            \
+      if (bf) hipLaunchKernelGGL((bfly_row_kernel<LL, 0, ACT_BF16>), dim3(a.n_chunks), dim3(256), 0, s, pa); \
+      else hipLaunchKernelGGL((bfly_row_kernel<LL, 0, ACT_F32>), dim3(a.n_chunks), dim3(256), 0, s, pa);    \
     }
+    if (L == 10) { BB_ROW(10) } else { BB_ROW(11) }
+#undef BB_ROW
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   } else if (rows > 0) {

@@ -308,7 +308,7 @@ def test_butterfly_backward_arguments():
             ch = 32 * min(max(rows // 8192, 1), 4)
             up = lambda v: -(-v // 256) * 256
             return up((-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4) + 2 * up(rows * (4 << log2n))
-        if log2n in (9, 11):  # one register pass: a wave (9) or a workgroup (11) per chunk
+        if log2n in (9, 10, 11):  # one register pass, a workgroup per chunk
             ch = min(max(rows // 512, 8), 64) if log2n == 9 else 16 * min(max(rows // 16384, 1), 8)
             return (-(-rows // ch) + N) * log2n * (1 << (log2n - 1)) * 4
         rt = min(64, 8192 >> log2n) if log2n <= 9 else 16384 >> log2n

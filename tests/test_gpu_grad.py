@@ -83,6 +83,7 @@ CASES = [
     (7, 4, 1300, ()),    # experts of several chunks
     (9, 4, 40000, (2,)), # width 512, chunks of 64 rows
     (9, 7, 900, (0, 4)), # width 512, 8-row chunks, ragged tails
+    (10, 4, 2001, (1,)), # width 1024 in one pass, two rows per step: odd row counts
     (11, 5, 2500, (2,)), # width 2048 in one pass: 16-row chunks, ragged tails
     (12, 4, 700, (1,)),  # width 4096 in part passes: several 32-row chunks, ragged tails
     (13, 3, 150, ()),    # width 8192 in part passes
@@ -108,6 +109,7 @@ def test_butterfly_backward_in_place_and_zero_rows():
     check_case(9, 4, 130, True, "f32", seed=5, inplace=True)
     check_case(12, 2, 90, False, "bf16", seed=6, inplace=True)  # part passes
     check_case(11, 3, 150, True, "f32", seed=8, inplace=True)   # one-pass width 2048
+    check_case(10, 3, 77, False, "bf16", seed=9, inplace=True)  # one-pass width 1024
     # no rows: every expert's angle gradients are zero, no row buffer touched
     ang = torch.randn(3, 5, 16, device="cuda")
     off = torch.zeros(4, dtype=torch.int32, device="cuda")
