@@ -888,15 +888,17 @@ __global__ __launch_bounds__(256) void bfly_row_kernel(BflyPartArgs a) {
   float* XB1 = xb[1] + rs * n;
   const int rend = c0 + ccnt, steps = (ccnt + RPW - 1) / RPW;
   float xn[8], gn[8];
+  if constexpr (RPW > 1) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) xn[j] = gn[j] = 0.f;
-  if (c0 + rs < rend) {
+    for (int j = 0; j < 8; ++j) xn[j] = gn[j] = 0.f;
+  }
+  if (RPW == 1 || c0 + rs < rend) {
     load(a.in0, c0 + rs, G0, xn);
     load(a.in1, c0 + rs, G3, gn);
   }
   for (int it = 0; it < steps; ++it) {
     const int r = c0 + it * RPW + rs;
-    const bool act = r < rend;  // a step past the end works on zeros: no gradient, no store
+    const bool act = RPW == 1 || r < rend;  // a step past the end works on zeros: no gradient, no store
     float x[8], g[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
