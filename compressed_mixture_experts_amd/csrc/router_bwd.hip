@@ -14,9 +14,9 @@
 //                      token tile staged in LDS 512 columns at a time and read
 //                      by broadcast), softmax over the workgroup, dl [T][N] to
 //                      the workspace;
-//   router_dx_kernel   16 tokens per workgroup (their dl rows in LDS), a
-//                      thread per column of x, four experts' gate rows loaded
-//                      ahead;
+//   router_dx_kernel   16 tokens per workgroup (64 when the tokens are many,
+//                      512 columns each), their dl in LDS, a thread per
+//                      column of x, four experts' gate rows loaded ahead;
 //   router_dwg_kernel  16 experts x 256 columns per workgroup (dl of 256
 //                      tokens at a time in LDS), the tokens split in ranges of
 //                      at least 256 for about 2048 workgroups; the ranges'
@@ -146,48 +146,56 @@ __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
   }
 }
 
-// dx[t][i] = sum_n dl[t][n] W_g[n][i]; a thread per column (blockDim = 256,
-// columns tid + 256 c)
-template <int A, int CPT>
+// dx[t][i] = sum_n dl[t][n] W_g[n][i] for BT tokens and 256 CW columns per
+// workgroup (a thread per column, CW columns 256 apart); the tile's dl in LDS
+// as [n][t] so that a thread reads four tokens' values in one 16-byte
+// broadcast; four experts' gate rows loaded ahead.
+template <int A, int BT, int CW>
 __global__ __launch_bounds__(256) void router_dx_kernel(RouterBwdArgs a) {
-  __shared__ float sL[RB_BT][256];  // the tile's dl rows
-  const int tid = threadIdx.x, t0 = blockIdx.x * RB_BT;
-  for (int q = tid; q < RB_BT * a.N; q += 256) {
+  __shared__ __attribute__((aligned(16))) float sLT[256][BT];
+  const int tid = threadIdx.x;
+  const int ncb = (a.d + 256 * CW - 1) / (256 * CW);
+  const int t0 = (blockIdx.x / ncb) * BT, c0 = (blockIdx.x % ncb) * 256 * CW;
+  for (int q = tid; q < BT * a.N; q += 256) {
     const int t = q / a.N, n = q % a.N;
-    sL[t][n] = t0 + t < a.T ? a.dl[size_t(t0 + t) * a.N + n] : 0.f;
+    sLT[n][t] = t0 + t < a.T ? a.dl[size_t(t0 + t) * a.N + n] : 0.f;
   }
   __syncthreads();
-  float acc[RB_BT][CPT];
+  float acc[BT][CW];
 #pragma unroll
-  for (int t = 0; t < RB_BT; ++t)
+  for (int t = 0; t < BT; ++t)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[t][c] = 0.f;
-  // four experts' gate rows in flight at a time
+    for (int c = 0; c < CW; ++c) acc[t][c] = 0.f;
   for (int n0 = 0; n0 < a.N; n0 += 4) {
-    float w[4][CPT];
+    float w[4][CW];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int i = tid + 256 * c, n = n0 + u;
+      for (int c = 0; c < CW; ++c) {
+        const int i = c0 + tid + 256 * c, n = n0 + u;
         w[u][c] = (i < a.d && n < a.N) ? load1<A>(a.wg, size_t(n) * a.d + i) : 0.f;
       }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int n = n0 + u < a.N ? n0 + u : a.N - 1;  // w is zero past N
 #pragma unroll
-      for (int t = 0; t < RB_BT; ++t) {
-        const float l = sL[t][n];
+      for (int t = 0; t < BT; t += 4) {
+        const float4 l = *reinterpret_cast<const float4*>(&sLT[n][t]);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[t][c] = fmaf(l, w[u][c], acc[t][c]);
+        for (int c = 0; c < CW; ++c) {
+          acc[t][c] = fmaf(l.x, w[u][c], acc[t][c]);
+          acc[t + 1][c] = fmaf(l.y, w[u][c], acc[t + 1][c]);
+          acc[t + 2][c] = fmaf(l.z, w[u][c], acc[t + 2][c]);
+          acc[t + 3][c] = fmaf(l.w, w[u][c], acc[t + 3][c]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < RB_BT; ++t)
+  for (int t = 0; t < BT; ++t)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int i = tid + 256 * c;
+    for (int c = 0; c < CW; ++c) {
+      const int i = c0 + tid + 256 * c;
       if (t0 + t < a.T && i < a.d) a.dx[size_t(t0 + t) * a.d + i] = acc[t][c];
     }
 }
@@ -287,11 +295,20 @@ hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, 
   else hipLaunchKernelGGL(router_dl_kernel<ACT_F32>, tgrid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // dx: 64-token tiles of 512 columns when the tokens are many (the gate
+  // matrix is read once per tile), else 16-token tiles of all columns
   const int cpt = (d + 255) / 256;
-#define RB_DX(C)                                                                              \
-  if (bf) hipLaunchKernelGGL((router_dx_kernel<ACT_BF16, C>), tgrid, dim3(256), 0, s, a);     \
-  else hipLaunchKernelGGL((router_dx_kernel<ACT_F32, C>), tgrid, dim3(256), 0, s, a);
-  if (cpt <= 1) { RB_DX(1) } else if (cpt <= 2) { RB_DX(2) } else if (cpt <= 4) { RB_DX(4) } else { RB_DX(8) }
+#define RB_DX(BT, C)                                                                                          \
+  {                                                                                                            \
+    const dim3 g(unsigned(((T + BT - 1) / BT) * ((d + 256 * C - 1) / (256 * C))));                             \
+    if (bf) hipLaunchKernelGGL((router_dx_kernel<ACT_BF16, BT, C>), g, dim3(256), 0, s, a);                    \
+    else hipLaunchKernelGGL((router_dx_kernel<ACT_F32, BT, C>), g, dim3(256), 0, s, a);                        \
+  }
+  if (T >= 16384) RB_DX(64, 2)
+  else if (cpt <= 1) RB_DX(16, 1)
+  else if (cpt <= 2) RB_DX(16, 2)
+  else if (cpt <= 4) RB_DX(16, 4)
+  else RB_DX(16, 8)
 #undef RB_DX
   e = hipGetLastError();
   if (e != hipSuccess) return e;
