@@ -10,10 +10,10 @@
 //
 // Three passes, fp32 arithmetic, every output written once (no atomics):
 //   router_dl_kernel   16 tokens per workgroup, a thread per expert: the
-//                      logits again (8-element loads of the gate row, the
-//                      token tile staged in LDS 512 columns at a time and read
-//                      by broadcast), softmax over the workgroup, dl [T][N] to
-//                      the workspace;
+//                      logits again (bf16 rows on the matrix cores, the token
+//                      tile in LDS 512 columns at a time; fp32 rows on the
+//                      VALU with the tile read by broadcast), softmax over the
+//                      workgroup, dl [T][N] to the workspace;
 //   router_dx_kernel   16 tokens per workgroup (64 when the tokens are many,
 //                      512 columns each), their dl in LDS, a thread per
 //                      column of x, four experts' gate rows loaded ahead;
@@ -54,6 +54,59 @@ __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
   float acc[RB_BT];
 #pragma unroll
   for (int t = 0; t < RB_BT; ++t) acc[t] = 0.f;
+  if (A == ACT_BF16 && a.d % 32 == 0) {  // uniform
+    // bf16 rows: the logits on the matrix cores (exact products, fp32 sums).
+    // The tile's columns in LDS as bf16 rows; wave w takes the 16-expert
+    // blocks w, w+4, ... with its gate-row fragments straight from memory;
+    // then the logits go through sP to the thread of each expert.
+    constexpr int XS = RB_XC + 8;
+    uint16_t* sXb = reinterpret_cast<uint16_t*>(&sX[0][0]);  // [RB_BT][XS] bf16
+    const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+    const uint16_t* wgp = static_cast<const uint16_t*>(a.wg);
+    const int NB = (a.N + 15) >> 4, l16 = lane & 15, g = lane >> 4;
+    f32x4_t am[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) am[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < a.d; c0 += RB_XC) {
+      const int cw = min(RB_XC, a.d - c0);
+      for (int q = tid; q < RB_BT * (cw / 8); q += 256) {
+        const int t = q / (cw / 8), i = (q % (cw / 8)) * 8;
+        const uint4 v = t0 + t < a.T ? *reinterpret_cast<const uint4*>(xg + size_t(t0 + t) * a.d + c0 + i)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(sXb + t * XS + i) = v;
+      }
+      __syncthreads();
+      for (int st = 0; st < cw / 32; ++st) {
+        const bf16x8_t bx = *reinterpret_cast<const bf16x8_t*>(sXb + l16 * XS + 32 * st + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = wave + 4 * i, e = 16 * b + l16;
+          if (b < NB) {  // uniform per wave
+            const uint4 wv = e < a.N ? *reinterpret_cast<const uint4*>(wgp + size_t(e) * a.d + c0 + 32 * st + 8 * g)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+            am[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv), bx, am[i], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();  // the chunk is replaced next
+    }
+    // am[i][v] = logit of expert 16 (w + 4 i) + 4 g + v for token l16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave + 4 * i;
+      if (b < NB) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int e = 16 * b + 4 * g + v;
+          if (e < a.N) sP[l16][e] = am[i][v];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < RB_BT; ++t) acc[t] = live ? sP[t][n] : 0.f;
+    __syncthreads();  // sP is rewritten with the probabilities below
+  } else
   for (int c0 = 0; c0 < a.d; c0 += RB_XC) {
     const int cw = min(RB_XC, a.d - c0);
     // the tile's columns c0 .. c0+cw-1 (8 per thread and step, rows past T zero)
