@@ -17,6 +17,8 @@
 //   router_dx_kernel   16 tokens per workgroup (64 when the tokens are many,
 //                      512 columns each), their dl in LDS, a thread per
 //                      column of x, four experts' gate rows loaded ahead;
+//                      bf16 rows of width a multiple of 256 take
+//                      router_dx_mfma_kernel instead;
 //   router_dwg_kernel  16 experts x 256 columns per workgroup (dl of 256
 //                      tokens at a time in LDS), the tokens split in ranges of
 //                      at least 256 for about 2048 workgroups; the ranges'
@@ -253,6 +255,96 @@ __global__ __launch_bounds__(256) void router_dx_kernel(RouterBwdArgs a) {
     }
 }
 
+// dx on the matrix cores (bf16 gate matrix, width a multiple of 256): a
+// workgroup takes 64 tokens x 256 columns, wave w the columns 64 w .. 64 w + 63
+// of all 64 tokens.  K runs over the experts 32 at a time: the gate matrix's
+// 32 x 256 tile is loaded as 8 x 8 blocks, transposed in registers and
+// stored with the experts innermost (so a fragment is one 16-byte LDS read);
+// dl comes from the workspace as fp32 and is split into two bf16 terms
+// hi + lo (|dl - hi - lo| <= 2^-18 |dl|), each multiplied exactly.
+constexpr int RX_RS = 40;  // LDS row stride (bf16) of the transposed tile: 32 experts + 8
+
+__device__ __forceinline__ void rx_split(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)v[j];
+    hi[j] = h;
+    lo[j] = (__bf16)(v[j] - (float)h);
+  }
+}
+
+__global__ __launch_bounds__(256) void router_dx_mfma_kernel(RouterBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sW[256 * RX_RS];  // [column][expert]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int ncb = a.d / 256;
+  const int t0 = (blockIdx.x / ncb) * 64, c0 = (blockIdx.x % ncb) * 256;
+  const uint16_t* wg = static_cast<const uint16_t*>(a.wg);
+  f32x4_t acc[4][4];  // [column block][token block]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // loader (threads 0..127): expert block rb (8 experts), column block cb (8 columns)
+  const int rb = tid & 3, cbk = tid >> 2;
+  for (int k0 = 0; k0 < a.N; k0 += 32) {
+    if (tid < 128) {
+      uint4 blk[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int e = k0 + 8 * rb + r;
+        blk[r] = e < a.N ? *reinterpret_cast<const uint4*>(wg + size_t(e) * a.d + c0 + 8 * cbk)
+                         : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint4& x0 = blk[2 * p];
+          const uint4& x1 = blk[2 * p + 1];
+          const uint32_t v0 = (c >> 1) == 0 ? x0.x : (c >> 1) == 1 ? x0.y : (c >> 1) == 2 ? x0.z : x0.w;
+          const uint32_t v1 = (c >> 1) == 0 ? x1.x : (c >> 1) == 1 ? x1.y : (c >> 1) == 2 ? x1.z : x1.w;
+          w4[p] = (c & 1) ? ((v0 >> 16) | (v1 & 0xFFFF0000u)) : ((v0 & 0xFFFFu) | (v1 << 16));
+        }
+        *reinterpret_cast<uint4*>(sW + (8 * cbk + c) * RX_RS + 8 * rb) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+    }
+    __syncthreads();
+    bf16x8_t wf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const bf16x8_t*>(sW + (64 * wave + 16 * i + l16) * RX_RS + 8 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + 16 * j + l16, e0 = k0 + 8 * g;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = (t < a.T && e0 + q < a.N) ? a.dl[size_t(t) * a.N + e0 + q] : 0.f;
+      bf16x8_t hi, lo;
+      rx_split(v, hi, lo);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], hi, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], lo, acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // sW is rewritten next
+  }
+  // acc[i][j][v] = dx[token t0 + 16 j + l16][column c0 + 64 wave + 16 i + 4 g + v]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 16 * j + l16;
+    if (t < a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + 64 * wave + 16 * i + 4 * g;
+        float* o = a.dx + size_t(t) * a.d + c;  // dx is only 4-byte aligned
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = acc[i][j][v];
+      }
+    }
+  }
+}
+
 // dW_g (or the split's partial) for experts nb .. nb+15, columns cb .. cb+255
 template <int A>
 __global__ __launch_bounds__(256) void router_dwg_kernel(RouterBwdArgs a) {
@@ -357,7 +449,9 @@ hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, 
     if (bf) hipLaunchKernelGGL((router_dx_kernel<ACT_BF16, BT, C>), g, dim3(256), 0, s, a);                    \
     else hipLaunchKernelGGL((router_dx_kernel<ACT_F32, BT, C>), g, dim3(256), 0, s, a);                        \
   }
-  if (T >= 16384) RB_DX(64, 2)
+  if (bf && d % 256 == 0) {
+    hipLaunchKernelGGL(router_dx_mfma_kernel, dim3(unsigned(((T + 63) / 64) * (d / 256))), dim3(256), 0, s, a);
+  } else if (T >= 16384) RB_DX(64, 2)
   else if (cpt <= 1) RB_DX(16, 1)
   else if (cpt <= 2) RB_DX(16, 2)
   else if (cpt <= 4) RB_DX(16, 4)
