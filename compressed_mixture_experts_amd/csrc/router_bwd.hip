@@ -345,6 +345,98 @@ __global__ __launch_bounds__(256) void router_dx_mfma_kernel(RouterBwdArgs a) {
   }
 }
 
+// dW_g on the matrix cores (bf16 x, width a multiple of 256): a workgroup
+// takes 64 experts x 256 columns over one token range, wave w the columns
+// 64 w .. 64 w + 63 of all 64 experts; K runs over the range's tokens 32 at a
+// time.  Both operands have the token outermost, so each step goes through
+// LDS with the token innermost: dl (fp32) split into hi + lo bf16 terms, a
+// thread writing 8 experts of one token; x as 8 x 8 blocks transposed in
+// registers.  The ranges' partial sums are added in order by router_red_kernel.
+constexpr int RW2_RS = 40;  // LDS row stride (bf16): 32 tokens + 8
+
+__global__ __launch_bounds__(256) void router_dwg_mfma_kernel(RouterBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sDh[64 * RW2_RS];   // [expert][token] hi
+  __shared__ __attribute__((aligned(16))) uint16_t sDl[64 * RW2_RS];   // [expert][token] lo
+  __shared__ __attribute__((aligned(16))) uint16_t sXt[256 * RW2_RS];  // [column][token]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int neb = (a.N + 63) / 64, ncb = a.d / 256, tiles = neb * ncb;
+  const int b = blockIdx.x % tiles, split = blockIdx.x / tiles;
+  const int e0 = (b % neb) * 64, c0 = (b / neb) * 256;
+  const int ta = split * a.tchunk, tb = min(a.T, ta + a.tchunk);
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+  f32x4_t acc[4][4];  // [expert block][column block]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // dl loader: token tl = tid / 8, experts 8 (tid % 8) .. + 7;
+  // x loader (threads 0..127): token block rb (8 tokens), column block cbk (8 columns)
+  const int tl = tid >> 3, eg = tid & 7, rb = tid & 3, cbk = tid >> 2;
+  for (int k0 = ta; k0 < tb; k0 += 32) {
+    {
+      const int t = k0 + tl;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = e0 + 8 * eg + q;
+        const float v = (t < tb && e < a.N) ? a.dl[size_t(t) * a.N + e] : 0.f;
+        const __bf16 h = (__bf16)v;
+        const __bf16 l = (__bf16)(v - (float)h);
+        sDh[(8 * eg + q) * RW2_RS + tl] = __builtin_bit_cast(uint16_t, h);
+        sDl[(8 * eg + q) * RW2_RS + tl] = __builtin_bit_cast(uint16_t, l);
+      }
+    }
+    if (tid < 128) {
+      uint4 blk[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int t = k0 + 8 * rb + r;
+        blk[r] = t < tb ? *reinterpret_cast<const uint4*>(xg + size_t(t) * a.d + c0 + 8 * cbk)
+                        : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint4& x0 = blk[2 * p];
+          const uint4& x1 = blk[2 * p + 1];
+          const uint32_t v0 = (c >> 1) == 0 ? x0.x : (c >> 1) == 1 ? x0.y : (c >> 1) == 2 ? x0.z : x0.w;
+          const uint32_t v1 = (c >> 1) == 0 ? x1.x : (c >> 1) == 1 ? x1.y : (c >> 1) == 2 ? x1.z : x1.w;
+          w4[p] = (c & 1) ? ((v0 >> 16) | (v1 & 0xFFFF0000u)) : ((v0 & 0xFFFFu) | (v1 << 16));
+        }
+        *reinterpret_cast<uint4*>(sXt + (8 * cbk + c) * RW2_RS + 8 * rb) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+    }
+    __syncthreads();
+    bf16x8_t xf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const bf16x8_t*>(sXt + (64 * wave + 16 * j + l16) * RW2_RS + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8_t hi = *reinterpret_cast<const bf16x8_t*>(sDh + (16 * i + l16) * RW2_RS + 8 * g);
+      const bf16x8_t lo = *reinterpret_cast<const bf16x8_t*>(sDl + (16 * i + l16) * RW2_RS + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xf[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the tiles are rewritten next
+  }
+  // acc[i][j][v] = dW_g[e0 + 16 i + 4 g + v][c0 + 64 wave + 16 j + l16]
+  float* dst = a.S > 1 ? a.part + size_t(split) * a.N * a.d : a.dwg;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = e0 + 16 * i + 4 * g + v;
+      if (e < a.N) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[size_t(e) * a.d + c0 + 64 * wave + 16 * j + l16] = acc[i][j][v];
+      }
+    }
+}
+
 // dW_g (or the split's partial) for experts nb .. nb+15, columns cb .. cb+255
 template <int A>
 __global__ __launch_bounds__(256) void router_dwg_kernel(RouterBwdArgs a) {
@@ -399,11 +491,13 @@ __global__ __launch_bounds__(256) void router_zero_kernel(float* p, size_t n) {
 
 // token ranges of the dW_g pass: none when its tiles reach 2048 workgroups,
 // else up to that many with at least 256 tokens each
-int router_bwd_splits(int T, int d, int N, int* tchunk) {
-  const int tiles = ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
+int router_bwd_splits(int T, int d, int N, int bf16, int* tchunk) {
+  const bool mf = bf16 && d % 256 == 0;  // matrix-core pass: 64 x 256 tiles, about 512 workgroups
+  const int tiles = mf ? ((N + 63) / 64) * (d / 256) : ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
+  const int target = mf ? 512 : 2048;
   int S = 1;
-  if (tiles < 2048) {
-    S = (2048 + tiles - 1) / tiles;
+  if (tiles < target) {
+    S = (target + tiles - 1) / tiles;
     const int smax = (T + 255) / 256;
     S = S < smax ? S : smax;
     S = S < 1 ? 1 : S;
@@ -418,9 +512,11 @@ int router_bwd_splits(int T, int d, int N, int* tchunk) {
 
 static size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// the larger of the two dW_g passes' needs (the query does not know the dtype)
 size_t router_bwd_workspace(int T, int d, int N) {
   if (T <= 0) return 0;
-  const int S = router_bwd_splits(T, d, N, nullptr);
+  const int S0 = router_bwd_splits(T, d, N, 0, nullptr), S1 = router_bwd_splits(T, d, N, 1, nullptr);
+  const int S = S0 > S1 ? S0 : S1;
   return al256(size_t(T) * N * 4) + (S > 1 ? size_t(S) * N * d * 4 : 0);
 }
 
@@ -432,7 +528,7 @@ hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, 
     return hipGetLastError();
   }
   RouterBwdArgs a{x, wg, idx, dgate, static_cast<float*>(ws), dx, dwg, nullptr, T, d, N, k, renorm, 1, 0};
-  a.S = router_bwd_splits(T, d, N, &a.tchunk);
+  a.S = router_bwd_splits(T, d, N, act == ACT_BF16, &a.tchunk);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + al256(size_t(T) * N * 4));
   const dim3 tgrid((T + RB_BT - 1) / RB_BT);
   const bool bf = act == ACT_BF16;
@@ -459,9 +555,14 @@ hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, 
 #undef RB_DX
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int tiles = ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
-  if (bf) hipLaunchKernelGGL(router_dwg_kernel<ACT_BF16>, dim3(tiles * a.S), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(router_dwg_kernel<ACT_F32>, dim3(tiles * a.S), dim3(256), 0, s, a);
+  if (bf && d % 256 == 0) {
+    const int tiles = ((N + 63) / 64) * (d / 256);
+    hipLaunchKernelGGL(router_dwg_mfma_kernel, dim3(tiles * a.S), dim3(256), 0, s, a);
+  } else {
+    const int tiles = ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
+    if (bf) hipLaunchKernelGGL(router_dwg_kernel<ACT_BF16>, dim3(tiles * a.S), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(router_dwg_kernel<ACT_F32>, dim3(tiles * a.S), dim3(256), 0, s, a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess || a.S == 1) return e;
   hipLaunchKernelGGL(router_red_kernel, dim3((size_t(N) * d + 255) / 256), dim3(256), 0, s, a);

@@ -417,15 +417,20 @@ def test_router_backward_arguments():
     L = bm.lib()
     n = ctypes.c_size_t(0)
 
+    def splits(T, d, N, mf):
+        tiles = (-(-N // 64) * (d // 256)) if mf else (-(-N // 16) * -(-d // 256))
+        target = 512 if mf else 2048
+        S = 1
+        if tiles < target:
+            S = max(1, min(-(-target // tiles), -(-T // 256)))
+        tc = max(1, -(-T // S))
+        return max(1, -(-T // tc))
+
     def want(T, d, N):
+        # the larger of the VALU and matrix-core dW_g passes' token splits
         if T == 0:
             return 0
-        tiles = -(-N // 16) * -(-d // 256)
-        S = 1
-        if tiles < 2048:
-            S = max(1, min(-(-2048 // tiles), -(-T // 256)))
-        tc = max(1, -(-T // S))
-        S = max(1, -(-T // tc))
+        S = max(splits(T, d, N, False), splits(T, d, N, d % 256 == 0))
         return -(-T * N * 4 // 256) * 256 + (S * N * d * 4 if S > 1 else 0)
 
     for args in ((4096, 512, 64), (16384, 512, 256), (32768, 2048, 256), (777, 128, 16), (10, 8, 3), (0, 64, 4)):
