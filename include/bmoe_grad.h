@@ -129,9 +129,12 @@ bmoe_status bmoe_combine_backward(int32_t T, int32_t top_k, int32_t d, int32_t d
  *   workspace at least bmoe_router_backward_workspace bytes (device,
  *             16-byte aligned): the logits' gradients and per-range sums.
  * d a multiple of 8 in [8, 2048], n_experts in [1, 256], top_k in [1,
- * min(8, n_experts)].  fp32 arithmetic (the logits are recomputed); every
- * output is written once and the token ranges are added in order, so the
- * result does not depend on scheduling.  Enqueued on `stream`, nothing
+ * min(8, n_experts)].  The logits are recomputed; sums are fp32 throughout.
+ * With bf16 rows the logits (d a multiple of 32), dx and dw_gate (d a
+ * multiple of 256) run on the matrix cores: bf16 products are exact, and dl
+ * enters as two bf16 terms whose sum is within 2^-18 of it; other shapes use
+ * fp32 products.  Every output is written once and the token ranges are
+ * added in order, so the result does not depend on scheduling.  Enqueued on `stream`, nothing
  * allocated or synchronised.  Errors: BMOE_ERR_SHAPE, BMOE_ERR_DTYPE,
  * BMOE_ERR_NULL, BMOE_ERR_ALIGN, BMOE_ERR_ALIAS, BMOE_ERR_WORKSPACE,
  * BMOE_ERR_HIP; all but the last are detected before anything is enqueued. */
