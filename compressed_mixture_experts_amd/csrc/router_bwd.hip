@@ -260,8 +260,9 @@ __global__ __launch_bounds__(256) void router_dx_kernel(RouterBwdArgs a) {
 // of all 64 tokens.  K runs over the experts 32 at a time: the gate matrix's
 // 32 x 256 tile is loaded as 8 x 8 blocks, transposed in registers and
 // stored with the experts innermost (so a fragment is one 16-byte LDS read);
-// dl comes from the workspace as fp32 and is split into two bf16 terms
-// hi + lo (|dl - hi - lo| <= 2^-18 |dl|), each multiplied exactly.
+// dl comes from the workspace as fp32, is split into two bf16 terms hi + lo
+// (|dl - hi - lo| <= 2^-18 |dl|) once per workgroup and staged in LDS, and
+// each term is multiplied exactly.
 constexpr int RX_RS = 40;  // LDS row stride (bf16) of the transposed tile: 32 experts + 8
 
 __device__ __forceinline__ void rx_split(const float (&v)[8], bf16x8_t& hi, bf16x8_t& lo) {
@@ -275,6 +276,8 @@ __device__ __forceinline__ void rx_split(const float (&v)[8], bf16x8_t& hi, bf16
 
 __global__ __launch_bounds__(256) void router_dx_mfma_kernel(RouterBwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sW[256 * RX_RS];  // [column][expert]
+  __shared__ __attribute__((aligned(16))) uint16_t sLh[64 * RX_RS];  // [token][expert], dl hi
+  __shared__ __attribute__((aligned(16))) uint16_t sLl[64 * RX_RS];  // [token][expert], dl lo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int ncb = a.d / 256;
   const int t0 = (blockIdx.x / ncb) * 64, c0 = (blockIdx.x % ncb) * 256;
@@ -287,6 +290,16 @@ __global__ __launch_bounds__(256) void router_dx_mfma_kernel(RouterBwdArgs a) {
   // loader (threads 0..127): expert block rb (8 experts), column block cb (8 columns)
   const int rb = tid & 3, cbk = tid >> 2;
   for (int k0 = 0; k0 < a.N; k0 += 32) {
+    {  // the step's dl: token tid / 4, experts 8 (tid % 4) .. + 7, split once for all waves
+      const int t = t0 + (tid >> 2), ee = k0 + 8 * (tid & 3);
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = (t < a.T && ee + q < a.N) ? a.dl[size_t(t) * a.N + ee + q] : 0.f;
+      bf16x8_t hi, lo;
+      rx_split(v, hi, lo);
+      *reinterpret_cast<bf16x8_t*>(sLh + (tid >> 2) * RX_RS + 8 * (tid & 3)) = hi;
+      *reinterpret_cast<bf16x8_t*>(sLl + (tid >> 2) * RX_RS + 8 * (tid & 3)) = lo;
+    }
     if (tid < 128) {
       uint4 blk[8];
 #pragma unroll
@@ -315,12 +328,8 @@ __global__ __launch_bounds__(256) void router_dx_mfma_kernel(RouterBwdArgs a) {
     for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const bf16x8_t*>(sW + (64 * wave + 16 * i + l16) * RX_RS + 8 * g);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 16 * j + l16, e0 = k0 + 8 * g;
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = (t < a.T && e0 + q < a.N) ? a.dl[size_t(t) * a.N + e0 + q] : 0.f;
-      bf16x8_t hi, lo;
-      rx_split(v, hi, lo);
+      const bf16x8_t hi = *reinterpret_cast<const bf16x8_t*>(sLh + (16 * j + l16) * RX_RS + 8 * g);
+      const bf16x8_t lo = *reinterpret_cast<const bf16x8_t*>(sLl + (16 * j + l16) * RX_RS + 8 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], hi, acc[i][j], 0, 0, 0);
