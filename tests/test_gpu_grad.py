@@ -74,7 +74,9 @@ CASES = [
     # (L, N, rows, empty experts)
     (1, 3, 20, (1,)),
     (3, 4, 50, ()),
+    (4, 3, 90, ()),
     (6, 16, 500, (0, 7)),
+    (8, 6, 700, (2,)),   # width 256: 32-row LDS tiles, several chunks
     (9, 8, 300, (3,)),
     (10, 5, 120, ()),
     (11, 3, 40, (1,)),
