@@ -20,7 +20,8 @@ import numpy as np
 __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
     "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad",
-    "combine_backward", "router_backward", "gelu_backward", "STATUS", "EXPORTED_SYMBOLS",
+    "combine_backward", "router_backward", "gelu_backward", "substrate_input_grad", "STATUS",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = [
     "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
     "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
     "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward",
+    "bmoe_substrate_input_grad",
 ]
 
 
@@ -114,12 +116,14 @@ def lib() -> ctypes.CDLL:
     L.bmoe_router_backward.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                        c_vp, c_sz, c_vp]
     L.bmoe_gelu_backward.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
+    L.bmoe_substrate_input_grad.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
     for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
                  "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
                  "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
                  "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
                  "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
-                 "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward"):
+                 "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward",
+                 "bmoe_substrate_input_grad"):
         getattr(L, name).restype = c_i32
     _lib = L
     return L
@@ -405,6 +409,17 @@ def gelu_backward(h, da, dh=None):
     _check(lib().bmoe_gelu_backward(rows, width, BF16 if h.dtype == torch.bfloat16 else F32, _ptr(h), _ptr(da),
                                     _ptr(dh), _stream_handle()))
     return dh
+
+
+def substrate_input_grad(dz, wt_packed, d_in: int, alpha: float = 1.0):
+    """du [rows][d_in] = alpha * dz [rows][d_out] * W_base, with W_base^T packed
+    ([d_in][d_out/16] words)."""
+    torch = _torch()
+    rows, d_out = int(dz.shape[0]), int(dz.shape[1])
+    du = torch.empty((rows, d_in), dtype=dz.dtype, device=dz.device)
+    _check(lib().bmoe_substrate_input_grad(rows, d_out, d_in, BF16 if dz.dtype == torch.bfloat16 else F32, _ptr(dz),
+                                           _ptr(wt_packed), float(alpha), _ptr(du), _stream_handle()))
+    return du
 
 
 def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):

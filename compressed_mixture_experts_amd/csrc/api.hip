@@ -981,3 +981,28 @@ bmoe_status bmoe_gelu_backward(int32_t rows, int32_t width, int32_t dtype, const
   BMOE_HIP(launch_gelu_bwd(h, da, dh, size_t(rows) * width, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
   return ok();
 }
+
+// ---------------------------------------------------------------- substrate input gradient
+bmoe_status bmoe_substrate_input_grad(int32_t rows, int32_t d_out, int32_t d_in, int32_t dtype, const void* dz,
+                                      const uint32_t* wt_packed, float alpha, void* du, hipStream_t stream) {
+  if (dtype != BMOE_F32 && dtype != BMOE_BF16) return fail(BMOE_ERR_DTYPE, "dtype=%d is unknown", dtype);
+  const int q = dtype == BMOE_BF16 ? 64 : 16;
+  if (rows < 0 || d_out < q || d_in < q || d_out % q || d_in % q)
+    return fail(BMOE_ERR_SHAPE, "rows=%d d_out=%d d_in=%d: d_out and d_in must be positive multiples of %d", rows,
+                d_out, d_in, q);
+  if (int64_t(rows) * (d_out > d_in ? d_out : d_in) > (int64_t(1) << 31) - 1)
+    return fail(BMOE_ERR_SHAPE, "rows * max(d_out, d_in) must be below 2^31");
+  if (rows == 0) return ok();
+  if (!dz || !wt_packed || !du) return fail(BMOE_ERR_NULL, "dz / wt_packed / du is NULL");
+  if (!aligned(dz, 16) || !aligned(wt_packed, 16) || !aligned(du, 16))
+    return fail(BMOE_ERR_ALIGN, "dz, wt_packed and du must be 16-byte aligned");
+  const size_t s = dtype == BMOE_BF16 ? 2 : 4;
+  const Range rz{dz, size_t(rows) * d_out * s}, ru{du, size_t(rows) * d_in * s},
+      rw{wt_packed, size_t(d_in) * (d_out / 16) * 4};
+  if (overlap(ru, rz) || overlap(ru, rw)) return fail(BMOE_ERR_ALIAS, "du overlaps dz or the packed substrate");
+  const bmoe_status st = check_device();
+  if (st != BMOE_OK) return st;
+  GemmArgs g{dz, wt_packed, du, alpha, rows, d_in, d_out};
+  BMOE_HIP(launch_gemm(g, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
+  return ok();
+}

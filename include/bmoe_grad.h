@@ -162,6 +162,24 @@ bmoe_status bmoe_router_backward(int32_t T, int32_t d, int32_t n_experts, int32_
 bmoe_status bmoe_gelu_backward(int32_t rows, int32_t width, int32_t dtype, const void* h, const void* da, void* dh,
                                hipStream_t stream);
 
+/* Input gradient of the substrate product Z = alpha U W_base^T through the
+ * straight-through estimator (ButterflyMoE, gist.science/nl/paper/2601.13563,
+ * §2 "Drie Fasen"; gist.science/zh/paper/2601.13563, technical summary §2.2):
+ * the forward's ternary codes are used as values, so
+ *     du = alpha * dz * W_base         ([rows][d_in] = [rows][d_out] x [d_out][d_in]).
+ *   dz         [rows][d_out] of dtype (device, 16-byte aligned), read only.
+ *   wt_packed  W_base^T packed: [d_in][d_out / 16] words (bmoe_pack_ternary of
+ *              the transposed substrate, device, 16-byte aligned), read only.
+ *   du         [rows][d_in] of dtype (device, 16-byte aligned), written; must
+ *              not overlap dz or wt_packed.
+ * d_out and d_in multiples of 64 (bf16) or 16 (fp32); fp32 accumulation; the
+ * forward's substrate GEMM.  Enqueued on `stream`, nothing allocated or
+ * synchronised.  Errors: BMOE_ERR_SHAPE, BMOE_ERR_DTYPE, BMOE_ERR_NULL,
+ * BMOE_ERR_ALIGN, BMOE_ERR_ALIAS, BMOE_ERR_HIP; all but the last are detected
+ * before anything is enqueued. */
+bmoe_status bmoe_substrate_input_grad(int32_t rows, int32_t d_out, int32_t d_in, int32_t dtype, const void* dz,
+                                      const uint32_t* wt_packed, float alpha, void* du, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -467,3 +467,20 @@ def test_gelu_backward_arguments():
     assert call(h=None) == 1 and call(dh=None) == 1
     assert call(h=h + 4) == 4 and call(dh=dh + 8) == 4
     assert call(dh=h + 16) == 5 and call(dh=da + 256) == 5   # partial overlaps
+
+
+def test_substrate_input_grad_arguments():
+    L = bm.lib()
+    F = FAKE
+    dz, wt, du = F + 0x100000, F + 0x200000, F + 0x300000
+
+    def call(rows=100, d_out=256, d_in=128, dt=bm.BF16, dz=dz, wt=wt, du=du):
+        return L.bmoe_substrate_input_grad(rows, d_out, d_in, dt, dz, wt, ctypes.c_float(1.0), du, None)
+
+    assert call(d_out=100) == 2 and call(d_in=32) == 2 and call(rows=-1) == 2
+    assert call(dt=bm.F32, d_in=40) == 2               # fp32: multiples of 16
+    assert call(dt=9) == 3
+    assert call(dz=None) == 1 and call(wt=None) == 1 and call(du=None) == 1
+    assert call(dz=dz + 8) == 4 and call(du=du + 2) == 4
+    assert call(du=dz + 64) == 5 and call(du=wt) == 5
+    assert call(rows=0, dz=None) == 0                    # nothing to do, nothing launched

@@ -104,7 +104,7 @@ def test_layer_backward_composed_from_the_abi():
     gate_flat = gate.reshape(-1).contiguous()
     d_rows, d_gate = bm.combine_backward(dy, slots, gate_flat, k, O)
     dZ, dph = bm.butterfly_backward(ph, off, Z, d_rows, False)
-    dU = bm.dbg_ternary_gemm(dZ, WTp, d, alpha)
+    dU = bm.substrate_input_grad(dZ, WTp, d, alpha)
     dxb, dth = bm.butterfly_backward(th, off, xb, dU, True)
     dW = bm.substrate_grad(dZ.to(torch.bfloat16), U.to(torch.bfloat16), alpha)
     dx = torch.zeros_like(x).index_add_(0, tok, dxb)
@@ -251,11 +251,11 @@ def test_ffn_layer_backward_composed_from_the_abi():
     log("ffn layer backward: pieces")
     d_rows, d_gate = bm.combine_backward(dy, slots, gate.reshape(-1).contiguous(), k, O)
     dZ, dphd = bm.butterfly_backward(phd, off, Z, d_rows, False)
-    dV = bm.dbg_ternary_gemm(dZ, WdpT, f, alpha)
+    dV = bm.substrate_input_grad(dZ, WdpT, f, alpha)
     dA, dthd = bm.butterfly_backward(thd, off, A, dV, True)
     dH = bm.gelu_backward(H, dA)
     dH1, dphu = bm.butterfly_backward(phu, off, H1, dH, False)
-    dU = bm.dbg_ternary_gemm(dH1, WupT, d, alpha)
+    dU = bm.substrate_input_grad(dH1, WupT, d, alpha)
     dxb, dthu = bm.butterfly_backward(thu, off, xb, dU, True)
     dWu = bm.substrate_grad(dH1.to(torch.bfloat16), U.to(torch.bfloat16), alpha)
     dWd = bm.substrate_grad(dZ.to(torch.bfloat16), V.to(torch.bfloat16), alpha)
