@@ -498,16 +498,17 @@ __global__ __launch_bounds__(256) void router_zero_kernel(float* p, size_t n) {
   if (q < n) p[q] = 0.f;
 }
 
-// token ranges of the dW_g pass: none when its tiles reach 2048 workgroups,
-// else up to that many with at least 256 tokens each
+// token ranges of the dW_g pass: none when its tiles reach 2048 workgroups
+// (512 for the matrix-core pass), else up to that many with at least 256
+// tokens each (64 for the matrix-core pass)
 int router_bwd_splits(int T, int d, int N, int bf16, int* tchunk) {
   const bool mf = bf16 && d % 256 == 0;  // matrix-core pass: 64 x 256 tiles, about 512 workgroups
   const int tiles = mf ? ((N + 63) / 64) * (d / 256) : ((N + RB_NB - 1) / RB_NB) * ((d + 255) / 256);
-  const int target = mf ? 512 : 2048;
+  const int target = mf ? 512 : 2048, tmin = mf ? 64 : 256;  // workgroups, tokens per range
   int S = 1;
   if (tiles < target) {
     S = (target + tiles - 1) / tiles;
-    const int smax = (T + 255) / 256;
+    const int smax = (T + tmin - 1) / tmin;
     S = S < smax ? S : smax;
     S = S < 1 ? 1 : S;
   }

@@ -419,10 +419,10 @@ def test_router_backward_arguments():
 
     def splits(T, d, N, mf):
         tiles = (-(-N // 64) * (d // 256)) if mf else (-(-N // 16) * -(-d // 256))
-        target = 512 if mf else 2048
+        target, tmin = (512, 64) if mf else (2048, 256)
         S = 1
         if tiles < target:
-            S = max(1, min(-(-target // tiles), -(-T // 256)))
+            S = max(1, min(-(-target // tiles), -(-T // tmin)))
         tc = max(1, -(-T // S))
         return max(1, -(-T // tc))
 
