@@ -9,7 +9,8 @@
 // then dx_t = W_g^T dl_t and dW_g = sum_t dl_t x_t^T.
 //
 // Three passes, fp32 arithmetic, every output written once (no atomics):
-//   router_dl_kernel   16 tokens per workgroup, a thread per expert: the
+//   router_dl_kernel   16 tokens per workgroup (32 or 64 on the matrix cores
+//                      when the tokens are many), a thread per expert: the
 //                      logits again (bf16 rows on the matrix cores, the token
 //                      tile in LDS 512 columns at a time; fp32 rows on the
 //                      VALU with the tile read by broadcast), softmax over the
@@ -44,160 +45,186 @@ struct RouterBwdArgs {
 
 constexpr int RB_XC = 512;  // columns of the token tile staged in LDS at a time
 
-template <int A>
+// TB blocks of 16 tokens per workgroup; TB > 1 only for bf16 rows of width a
+// multiple of 32 (the matrix-core path), where each gate-row fragment read
+// from memory then serves TB token blocks.
+template <int A, int TB>
 __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
+  constexpr int XC = TB == 1 ? RB_XC : 256;  // bf16 columns of the token tile staged at a time
+  constexpr int XS = XC + 8;
+  constexpr int SXF = TB == 1 ? RB_BT * RB_XC : TB * RB_BT * XS / 2;  // floats of the staging area
   __shared__ float sP[RB_BT][256];      // probabilities
   __shared__ float sRed[RB_BT][4];
   __shared__ float sMax[RB_BT], sSum[RB_BT];
-  __shared__ __attribute__((aligned(16))) float sX[RB_BT][RB_XC];  // token tile, one column chunk
+  __shared__ __attribute__((aligned(16))) float sXf[SXF];  // token tile, one column chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RB_BT, n = tid;
+  const int tw0 = blockIdx.x * RB_BT * TB, n = tid;
   const bool live = n < a.N;
   float acc[RB_BT];
 #pragma unroll
   for (int t = 0; t < RB_BT; ++t) acc[t] = 0.f;
+  f32x4_t am[4][TB];
+  const int l16 = lane & 15, g = lane >> 4, NB = (a.N + 15) >> 4;
   if (A == ACT_BF16 && a.d % 32 == 0) {  // uniform
     // bf16 rows: the logits on the matrix cores (exact products, fp32 sums).
     // The tile's columns in LDS as bf16 rows; wave w takes the 16-expert
     // blocks w, w+4, ... with its gate-row fragments straight from memory;
     // then the logits go through sP to the thread of each expert.
-    constexpr int XS = RB_XC + 8;
-    uint16_t* sXb = reinterpret_cast<uint16_t*>(&sX[0][0]);  // [RB_BT][XS] bf16
+    uint16_t* sXb = reinterpret_cast<uint16_t*>(sXf);  // [TB RB_BT][XS] bf16
     const uint16_t* xg = static_cast<const uint16_t*>(a.x);
     const uint16_t* wgp = static_cast<const uint16_t*>(a.wg);
-    const int NB = (a.N + 15) >> 4, l16 = lane & 15, g = lane >> 4;
-    f32x4_t am[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) am[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < a.d; c0 += RB_XC) {
-      const int cw = min(RB_XC, a.d - c0);
-      for (int q = tid; q < RB_BT * (cw / 8); q += 256) {
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int b = 0; b < TB; ++b) am[i][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < a.d; c0 += XC) {
+      const int cw = min(XC, a.d - c0);
+      for (int q = tid; q < TB * RB_BT * (cw / 8); q += 256) {
         const int t = q / (cw / 8), i = (q % (cw / 8)) * 8;
-        const uint4 v = t0 + t < a.T ? *reinterpret_cast<const uint4*>(xg + size_t(t0 + t) * a.d + c0 + i)
-                                     : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 v = tw0 + t < a.T ? *reinterpret_cast<const uint4*>(xg + size_t(tw0 + t) * a.d + c0 + i)
+                                      : make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4*>(sXb + t * XS + i) = v;
       }
       __syncthreads();
       for (int st = 0; st < cw / 32; ++st) {
-        const bf16x8_t bx = *reinterpret_cast<const bf16x8_t*>(sXb + l16 * XS + 32 * st + 8 * g);
+        bf16x8_t bx[TB];
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+          bx[b] = *reinterpret_cast<const bf16x8_t*>(sXb + (RB_BT * b + l16) * XS + 32 * st + 8 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int b = wave + 4 * i, e = 16 * b + l16;
           if (b < NB) {  // uniform per wave
             const uint4 wv = e < a.N ? *reinterpret_cast<const uint4*>(wgp + size_t(e) * a.d + c0 + 32 * st + 8 * g)
                                      : make_uint4(0u, 0u, 0u, 0u);
-            am[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv), bx, am[i], 0, 0, 0);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+              am[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv), bx[tb], am[i][tb], 0, 0, 0);
           }
         }
       }
       __syncthreads();  // the chunk is replaced next
     }
-    // am[i][v] = logit of expert 16 (w + 4 i) + 4 g + v for token l16
+  } else if constexpr (TB == 1) {
+    float (*sX)[RB_XC] = reinterpret_cast<float (*)[RB_XC]>(sXf);
+    for (int c0 = 0; c0 < a.d; c0 += RB_XC) {
+      const int cw = min(RB_XC, a.d - c0);
+      // the tile's columns c0 .. c0+cw-1 (8 per thread and step, rows past T zero)
+      for (int q = tid; q < RB_BT * cw / 8; q += 256) {
+        const int t = q / (cw / 8), i = (q % (cw / 8)) * 8;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (tw0 + t < a.T) load8<A>(a.x, size_t(tw0 + t) * a.d + c0 + i, v);
+        *reinterpret_cast<float4*>(&sX[t][i]) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(&sX[t][i + 4]) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+      __syncthreads();
+      for (int i = 0; i < cw; i += 8) {
+        float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (live) load8<A>(a.wg, size_t(n) * a.d + c0 + i, w);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = wave + 4 * i;
-      if (b < NB) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int e = 16 * b + 4 * g + v;
-          if (e < a.N) sP[l16][e] = am[i][v];
+        for (int t = 0; t < RB_BT; ++t) {
+          const float4 x0 = *reinterpret_cast<const float4*>(&sX[t][i]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&sX[t][i + 4]);
+          acc[t] = fmaf(w[0], x0.x, acc[t]);
+          acc[t] = fmaf(w[1], x0.y, acc[t]);
+          acc[t] = fmaf(w[2], x0.z, acc[t]);
+          acc[t] = fmaf(w[3], x0.w, acc[t]);
+          acc[t] = fmaf(w[4], x1.x, acc[t]);
+          acc[t] = fmaf(w[5], x1.y, acc[t]);
+          acc[t] = fmaf(w[6], x1.z, acc[t]);
+          acc[t] = fmaf(w[7], x1.w, acc[t]);
         }
       }
+      __syncthreads();  // the chunk is replaced next
     }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < RB_BT; ++t) acc[t] = live ? sP[t][n] : 0.f;
-    __syncthreads();  // sP is rewritten with the probabilities below
-  } else
-  for (int c0 = 0; c0 < a.d; c0 += RB_XC) {
-    const int cw = min(RB_XC, a.d - c0);
-    // the tile's columns c0 .. c0+cw-1 (8 per thread and step, rows past T zero)
-    for (int q = tid; q < RB_BT * cw / 8; q += 256) {
-      const int t = q / (cw / 8), i = (q % (cw / 8)) * 8;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (t0 + t < a.T) load8<A>(a.x, size_t(t0 + t) * a.d + c0 + i, v);
-      *reinterpret_cast<float4*>(&sX[t][i]) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4*>(&sX[t][i + 4]) = make_float4(v[4], v[5], v[6], v[7]);
-    }
-    __syncthreads();
-    for (int i = 0; i < cw; i += 8) {
-      float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (live) load8<A>(a.wg, size_t(n) * a.d + c0 + i, w);
-#pragma unroll
-      for (int t = 0; t < RB_BT; ++t) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&sX[t][i]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&sX[t][i + 4]);
-        acc[t] = fmaf(w[0], x0.x, acc[t]);
-        acc[t] = fmaf(w[1], x0.y, acc[t]);
-        acc[t] = fmaf(w[2], x0.z, acc[t]);
-        acc[t] = fmaf(w[3], x0.w, acc[t]);
-        acc[t] = fmaf(w[4], x1.x, acc[t]);
-        acc[t] = fmaf(w[5], x1.y, acc[t]);
-        acc[t] = fmaf(w[6], x1.z, acc[t]);
-        acc[t] = fmaf(w[7], x1.w, acc[t]);
-      }
-    }
-    __syncthreads();  // the chunk is replaced next
   }
-  // softmax over the experts, per token: max, then sum of exp
+  const bool mf = A == ACT_BF16 && a.d % 32 == 0;
+#pragma unroll 1
+  for (int tb = 0; tb < TB; ++tb) {
+    const int t0 = tw0 + RB_BT * tb;
+    if (mf) {
+      // am[i][tb][v] = logit of expert 16 (w + 4 i) + 4 g + v for token t0 + l16
 #pragma unroll
-  for (int t = 0; t < RB_BT; ++t) {
-    float m = live ? acc[t] : -INFINITY;
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    if (lane == 0) sRed[t][wave] = m;
-  }
-  __syncthreads();
-  if (tid < RB_BT) sMax[tid] = fmaxf(fmaxf(sRed[tid][0], sRed[tid][1]), fmaxf(sRed[tid][2], sRed[tid][3]));
-  __syncthreads();
-  float ev[RB_BT];
+      for (int i = 0; i < 4; ++i) {
+        const int b = wave + 4 * i;
+        if (b < NB) {
 #pragma unroll
-  for (int t = 0; t < RB_BT; ++t) {
-    ev[t] = live ? __expf(acc[t] - sMax[t]) : 0.f;
-    float s = ev[t];
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0) sRed[t][wave] = s;
-  }
-  __syncthreads();
-  if (tid < RB_BT) sSum[tid] = (sRed[tid][0] + sRed[tid][1]) + (sRed[tid][2] + sRed[tid][3]);
-  __syncthreads();
+          for (int v = 0; v < 4; ++v) {
+            const int e = 16 * b + 4 * g + v;
+            f32x4_t m = am[i][0];
 #pragma unroll
-  for (int t = 0; t < RB_BT; ++t) sP[t][n] = live ? ev[t] / sSum[t] : 0.f;
-  __syncthreads();
-  // dl of this thread's expert for each token of the tile
-#pragma unroll
-  for (int t = 0; t < RB_BT; ++t) {
-    const int tt = t0 + t;
-    if (tt >= a.T || !live) continue;
-    const int32_t* id = a.idx + size_t(tt) * a.k;
-    const float* dg = a.dgate + size_t(tt) * a.k;
-    float v = 0.f;
-    if (a.renorm) {
-      float ps = 0.f, inner = 0.f, mine = 0.f;
-      bool chosen = false;
-      for (int j = 0; j < a.k; ++j) ps += sP[t][min(max(id[j], 0), a.N - 1)];
-      for (int j = 0; j < a.k; ++j) {
-        const int e = min(max(id[j], 0), a.N - 1);
-        const float g = sP[t][e] / ps;
-        inner = fmaf(dg[j], g, inner);
-        if (e == n) {
-          chosen = true;
-          mine += dg[j];
+            for (int q = 1; q < TB; ++q)
+              if (q == tb) m = am[i][q];
+            if (e < a.N) sP[l16][e] = m[v];
+          }
         }
       }
-      if (chosen) {
-        const float g = sP[t][n] / ps;
-        v = g * (mine - inner);
-      }
-    } else {
-      float s = 0.f, an = 0.f;
-      for (int j = 0; j < a.k; ++j) {
-        const int e = min(max(id[j], 0), a.N - 1);
-        s = fmaf(dg[j], sP[t][e], s);
-        if (e == n) an += dg[j];
-      }
-      v = sP[t][n] * (an - s);
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < RB_BT; ++t) acc[t] = live ? sP[t][n] : 0.f;
+      __syncthreads();  // sP is rewritten with the probabilities below
     }
-    a.dl[size_t(tt) * a.N + n] = v;
+    // softmax over the experts, per token: max, then sum of exp
+#pragma unroll
+    for (int t = 0; t < RB_BT; ++t) {
+      float m = live ? acc[t] : -INFINITY;
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) sRed[t][wave] = m;
+    }
+    __syncthreads();
+    if (tid < RB_BT) sMax[tid] = fmaxf(fmaxf(sRed[tid][0], sRed[tid][1]), fmaxf(sRed[tid][2], sRed[tid][3]));
+    __syncthreads();
+    float ev[RB_BT];
+#pragma unroll
+    for (int t = 0; t < RB_BT; ++t) {
+      ev[t] = live ? __expf(acc[t] - sMax[t]) : 0.f;
+      float s = ev[t];
+      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+      if (lane == 0) sRed[t][wave] = s;
+    }
+    __syncthreads();
+    if (tid < RB_BT) sSum[tid] = (sRed[tid][0] + sRed[tid][1]) + (sRed[tid][2] + sRed[tid][3]);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < RB_BT; ++t) sP[t][n] = live ? ev[t] / sSum[t] : 0.f;
+    __syncthreads();
+    // dl of this thread's expert for each token of the tile
+#pragma unroll
+    for (int t = 0; t < RB_BT; ++t) {
+      const int tt = t0 + t;
+      if (tt >= a.T || !live) continue;
+      const int32_t* id = a.idx + size_t(tt) * a.k;
+      const float* dg = a.dgate + size_t(tt) * a.k;
+      float v = 0.f;
+      if (a.renorm) {
+        float ps = 0.f, inner = 0.f, mine = 0.f;
+        bool chosen = false;
+        for (int j = 0; j < a.k; ++j) ps += sP[t][min(max(id[j], 0), a.N - 1)];
+        for (int j = 0; j < a.k; ++j) {
+          const int e = min(max(id[j], 0), a.N - 1);
+          const float g = sP[t][e] / ps;
+          inner = fmaf(dg[j], g, inner);
+          if (e == n) {
+            chosen = true;
+            mine += dg[j];
+          }
+        }
+        if (chosen) {
+          const float g = sP[t][n] / ps;
+          v = g * (mine - inner);
+        }
+      } else {
+        float s = 0.f, an = 0.f;
+        for (int j = 0; j < a.k; ++j) {
+          const int e = min(max(id[j], 0), a.N - 1);
+          s = fmaf(dg[j], sP[t][e], s);
+          if (e == n) an += dg[j];
+        }
+        v = sP[t][n] * (an - s);
+      }
+      a.dl[size_t(tt) * a.N + n] = v;
+    }
+    if (TB > 1) __syncthreads();  // sP is rewritten for the next token block
   }
 }
 
@@ -540,10 +567,17 @@ hipError_t launch_router_bwd(const void* x, const void* wg, const int32_t* idx, 
   RouterBwdArgs a{x, wg, idx, dgate, static_cast<float*>(ws), dx, dwg, nullptr, T, d, N, k, renorm, 1, 0};
   a.S = router_bwd_splits(T, d, N, act == ACT_BF16, &a.tchunk);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + al256(size_t(T) * N * 4));
-  const dim3 tgrid((T + RB_BT - 1) / RB_BT);
   const bool bf = act == ACT_BF16;
-  if (bf) hipLaunchKernelGGL(router_dl_kernel<ACT_BF16>, tgrid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(router_dl_kernel<ACT_F32>, tgrid, dim3(256), 0, s, a);
+  // logits and dl: 16-token blocks, 4 or 2 per workgroup on the matrix cores
+  // while that leaves at least 512 workgroups (the gate matrix is read once
+  // per workgroup)
+  const int tiles = (T + RB_BT - 1) / RB_BT;
+  const int tb = bf && d % 32 == 0 ? (tiles / 4 >= 512 ? 4 : tiles / 2 >= 512 ? 2 : 1) : 1;
+  const dim3 tgrid((tiles + tb - 1) / tb);
+  if (tb == 4) hipLaunchKernelGGL((router_dl_kernel<ACT_BF16, 4>), tgrid, dim3(256), 0, s, a);
+  else if (tb == 2) hipLaunchKernelGGL((router_dl_kernel<ACT_BF16, 2>), tgrid, dim3(256), 0, s, a);
+  else if (bf) hipLaunchKernelGGL((router_dl_kernel<ACT_BF16, 1>), tgrid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((router_dl_kernel<ACT_F32, 1>), tgrid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dx: 64-token tiles of 512 columns when the tokens are many (the gate

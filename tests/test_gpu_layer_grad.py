@@ -143,7 +143,8 @@ def test_layer_backward_composed_from_the_abi():
     (3000, 512, 256, 2, True, "f32"),
     (300, 2048, 256, 2, False, "bf16"),   # large workload's width, several column blocks
     (5, 8, 3, 1, False, "f32"),           # fewer tokens than a tile
-    (16500, 256, 64, 2, False, "bf16"),   # 64-token tiles of the dx pass, ragged last tile
+    (16500, 256, 64, 2, False, "bf16"),   # 64-token tiles of the dx pass, ragged last tile; 32-token logits tiles
+    (33000, 64, 16, 2, True, "bf16"),     # 64-token logits tiles, ragged last tile, one expert block
     (50, 40, 5, 2, False, "bf16"),        # width not a multiple of 32: logits on the VALU
 ])
 def test_router_backward_matches_oracle(T, d, N, k, renorm, act):
