@@ -57,8 +57,17 @@ __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
   __shared__ float sRed[RB_BT][4];
   __shared__ float sMax[RB_BT], sSum[RB_BT];
   __shared__ __attribute__((aligned(16))) float sXf[SXF];  // token tile, one column chunk
+  __shared__ int sId[TB * RB_BT][8];     // the tile's chosen experts (top_k <= 8) ...
+  __shared__ float sDg[TB * RB_BT][8];   // ... and their gate gradients
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tw0 = blockIdx.x * RB_BT * TB, n = tid;
+  for (int q = tid; q < TB * RB_BT * a.k; q += 256) {  // read before the first barrier below
+    const int t = q / a.k, j = q % a.k;
+    if (tw0 + t < a.T) {
+      sId[t][j] = min(max(a.idx[size_t(tw0 + t) * a.k + j], 0), a.N - 1);
+      sDg[t][j] = a.dgate[size_t(tw0 + t) * a.k + j];
+    }
+  }
   const bool live = n < a.N;
   float acc[RB_BT];
 #pragma unroll
@@ -193,15 +202,15 @@ __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
     for (int t = 0; t < RB_BT; ++t) {
       const int tt = t0 + t;
       if (tt >= a.T || !live) continue;
-      const int32_t* id = a.idx + size_t(tt) * a.k;
-      const float* dg = a.dgate + size_t(tt) * a.k;
+      const int* id = sId[RB_BT * tb + t];
+      const float* dg = sDg[RB_BT * tb + t];
       float v = 0.f;
       if (a.renorm) {
         float ps = 0.f, inner = 0.f, mine = 0.f;
         bool chosen = false;
-        for (int j = 0; j < a.k; ++j) ps += sP[t][min(max(id[j], 0), a.N - 1)];
+        for (int j = 0; j < a.k; ++j) ps += sP[t][id[j]];
         for (int j = 0; j < a.k; ++j) {
-          const int e = min(max(id[j], 0), a.N - 1);
+          const int e = id[j];
           const float g = sP[t][e] / ps;
           inner = fmaf(dg[j], g, inner);
           if (e == n) {
@@ -216,7 +225,7 @@ __global__ __launch_bounds__(256) void router_dl_kernel(RouterBwdArgs a) {
       } else {
         float s = 0.f, an = 0.f;
         for (int j = 0; j < a.k; ++j) {
-          const int e = min(max(id[j], 0), a.N - 1);
+          const int e = id[j];
           s = fmaf(dg[j], sP[t][e], s);
           if (e == n) an += dg[j];
         }
