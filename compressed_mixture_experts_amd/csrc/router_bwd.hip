@@ -417,27 +417,36 @@ __global__ __launch_bounds__(256) void router_dwg_mfma_kernel(RouterBwdArgs a) {
   // dl loader: token tl = tid / 8, experts 8 (tid % 8) .. + 7;
   // x loader (threads 0..127): token block rb (8 tokens), column block cbk (8 columns)
   const int tl = tid >> 3, eg = tid & 7, rb = tid & 3, cbk = tid >> 2;
-  for (int k0 = ta; k0 < tb; k0 += 32) {
-    {
-      const int t = k0 + tl;
+  // the next 32 tokens' dl and x are loaded into registers while the current
+  // ones are multiplied from LDS
+  float dv[8];
+  uint4 blk[8];
+  auto load_step = [&](int k0) {
+    const int t = k0 + tl;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int e = e0 + 8 * eg + q;
-        const float v = (t < tb && e < a.N) ? a.dl[size_t(t) * a.N + e] : 0.f;
-        const __bf16 h = (__bf16)v;
-        const __bf16 l = (__bf16)(v - (float)h);
-        sDh[(8 * eg + q) * RW2_RS + tl] = __builtin_bit_cast(uint16_t, h);
-        sDl[(8 * eg + q) * RW2_RS + tl] = __builtin_bit_cast(uint16_t, l);
-      }
+    for (int q = 0; q < 8; ++q) {
+      const int e = e0 + 8 * eg + q;
+      dv[q] = (t < tb && e < a.N) ? a.dl[size_t(t) * a.N + e] : 0.f;
     }
     if (tid < 128) {
-      uint4 blk[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int t = k0 + 8 * rb + r;
-        blk[r] = t < tb ? *reinterpret_cast<const uint4*>(xg + size_t(t) * a.d + c0 + 8 * cbk)
-                        : make_uint4(0u, 0u, 0u, 0u);
+        const int tr = k0 + 8 * rb + r;
+        blk[r] = tr < tb ? *reinterpret_cast<const uint4*>(xg + size_t(tr) * a.d + c0 + 8 * cbk)
+                         : make_uint4(0u, 0u, 0u, 0u);
       }
+    }
+  };
+  load_step(ta);
+  for (int k0 = ta; k0 < tb; k0 += 32) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const __bf16 h = (__bf16)dv[q];
+      const __bf16 l = (__bf16)(dv[q] - (float)h);
+      sDh[(8 * eg + q) * RW2_RS + tl] = __builtin_bit_cast(uint16_t, h);
+      sDl[(8 * eg + q) * RW2_RS + tl] = __builtin_bit_cast(uint16_t, l);
+    }
+    if (tid < 128) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         uint32_t w4[4];
@@ -453,6 +462,7 @@ __global__ __launch_bounds__(256) void router_dwg_mfma_kernel(RouterBwdArgs a) {
       }
     }
     __syncthreads();
+    if (k0 + 32 < tb) load_step(k0 + 32);  // uniform
     bf16x8_t xf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const bf16x8_t*>(sXt + (64 * wave + 16 * j + l16) * RW2_RS + 8 * g);
