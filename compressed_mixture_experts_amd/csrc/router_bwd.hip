@@ -325,25 +325,33 @@ __global__ __launch_bounds__(256) void router_dx_mfma_kernel(RouterBwdArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // loader (threads 0..127): expert block rb (8 experts), column block cb (8 columns)
   const int rb = tid & 3, cbk = tid >> 2;
-  for (int k0 = 0; k0 < a.N; k0 += 32) {
-    {  // the step's dl: token tid / 4, experts 8 (tid % 4) .. + 7, split once for all waves
-      const int t = t0 + (tid >> 2), ee = k0 + 8 * (tid & 3);
-      float v[8];
+  // the next 32 experts' dl and gate rows are loaded into registers while the
+  // current ones are multiplied from LDS
+  float dv[8];
+  uint4 blk[8];
+  auto load_step = [&](int k0) {
+    // dl: token tid / 4, experts 8 (tid % 4) .. + 7 (split once for all waves)
+    const int t = t0 + (tid >> 2), ee = k0 + 8 * (tid & 3);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = (t < a.T && ee + q < a.N) ? a.dl[size_t(t) * a.N + ee + q] : 0.f;
-      bf16x8_t hi, lo;
-      rx_split(v, hi, lo);
-      *reinterpret_cast<bf16x8_t*>(sLh + (tid >> 2) * RX_RS + 8 * (tid & 3)) = hi;
-      *reinterpret_cast<bf16x8_t*>(sLl + (tid >> 2) * RX_RS + 8 * (tid & 3)) = lo;
-    }
+    for (int q = 0; q < 8; ++q) dv[q] = (t < a.T && ee + q < a.N) ? a.dl[size_t(t) * a.N + ee + q] : 0.f;
     if (tid < 128) {
-      uint4 blk[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int e = k0 + 8 * rb + r;
         blk[r] = e < a.N ? *reinterpret_cast<const uint4*>(wg + size_t(e) * a.d + c0 + 8 * cbk)
                          : make_uint4(0u, 0u, 0u, 0u);
       }
+    }
+  };
+  load_step(0);
+  for (int k0 = 0; k0 < a.N; k0 += 32) {
+    {
+      bf16x8_t hi, lo;
+      rx_split(dv, hi, lo);
+      *reinterpret_cast<bf16x8_t*>(sLh + (tid >> 2) * RX_RS + 8 * (tid & 3)) = hi;
+      *reinterpret_cast<bf16x8_t*>(sLl + (tid >> 2) * RX_RS + 8 * (tid & 3)) = lo;
+    }
+    if (tid < 128) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         uint32_t w4[4];
@@ -359,6 +367,7 @@ __global__ __launch_bounds__(256) void router_dx_mfma_kernel(RouterBwdArgs a) {
       }
     }
     __syncthreads();
+    if (k0 + 32 < a.N) load_step(k0 + 32);  // uniform
     bf16x8_t wf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const bf16x8_t*>(sW + (64 * wave + 16 * i + l16) * RX_RS + 8 * g);
