@@ -322,10 +322,14 @@ def forward(inp, routing: Optional[Routing] = None, idx_override: Optional[np.nd
 
 def forward_tokens(inp, tokens: Sequence[int], routing: Optional[Routing] = None,
                    idx_override: Optional[np.ndarray] = None):
-    """Layer output for a subset of tokens, one token at a time, without
-    materialising experts (right-to-left evaluation of the same products).
+    """Layer output for a subset of tokens without materialising experts: the
+    same products as ``forward`` evaluated right to left, B(phi) (W (B(theta)^T x))
+    ([MoE-zh] §2.1: the expert is applied as input rotation, substrate product and
+    output rotation; the nl page, §2 "Drie Fasen", has it never formed during
+    inference).  The chosen tokens of one expert are stacked as the columns of
+    one matrix, which changes nothing but the rounding order of the fp64 sums.
 
-    Used for sampled checks of layers too large to materialise.  Routing is
+    Used for the checks of layers too large to materialise.  Routing is
     computed for the requested tokens only unless ``routing`` is given.
     Returns (y float64 [len(tokens)][d], idx [len][k], gates [len][k]).
     """
@@ -343,18 +347,18 @@ def forward_tokens(inp, tokens: Sequence[int], routing: Optional[Routing] = None
         gates = np.take_along_axis(probs, idx, axis=1)
         if cfg.renorm_gates:
             gates = gates / gates.sum(axis=1, keepdims=True)
+    w64 = [np.asarray(w, dtype=np.float64) for w in inp.w_base]
     y = np.zeros((len(tokens), cfg.d_model))
-    for t in range(len(tokens)):
-        for j in range(idx.shape[1]):
-            e = int(idx[t, j])
-            v = x[t][:, None]
-            if cfg.is_ffn:
-                h = expert_apply(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], v, cfg.w_scale)
-                a = gelu(h) if cfg.ffn_act == "gelu" else h
-                z = expert_apply(inp.theta[1][e], inp.phi[1][e], inp.w_base[1], a, cfg.w_scale)
-            else:
-                z = expert_apply(inp.theta[0][e], inp.phi[0][e], inp.w_base[0], v, cfg.w_scale)
-            y[t] += gates[t, j] * z[:, 0]
+    for e in np.unique(idx):
+        t, j = np.nonzero(idx == e)                 # the tokens that chose expert e
+        V = x[t].T                                  # [d][m], one column per token
+        if cfg.is_ffn:
+            h = expert_apply(inp.theta[0][e], inp.phi[0][e], w64[0], V, cfg.w_scale)
+            a = gelu(h) if cfg.ffn_act == "gelu" else h
+            z = expert_apply(inp.theta[1][e], inp.phi[1][e], w64[1], a, cfg.w_scale)
+        else:
+            z = expert_apply(inp.theta[0][e], inp.phi[0][e], w64[0], V, cfg.w_scale)
+        np.add.at(y, t, gates[t, j][:, None] * z.T)
     return y, idx, gates
 
 

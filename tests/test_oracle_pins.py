@@ -307,10 +307,12 @@ def test_forward_tokens_equals_materialised(ffn):
                           act="bf16", seed_index=33)
     inp = wl.generate(cfg)
     y, r = ref.forward(inp)
-    toks = [0, 4, 17, 22]
-    ys, idx, g = ref.forward_tokens(inp, toks)
-    assert np.array_equal(idx, r.idx[toks])
-    assert np.abs(ys - y[toks]).max() < 1e-11 * np.abs(y).max()
+    # a few tokens (about one per expert), then every token and a repeated one
+    # (several columns per expert in the stacked right-to-left products)
+    for toks in ([0, 4, 17, 22], list(range(23)), [5, 3, 5, 22, 0, 5]):
+        ys, idx, g = ref.forward_tokens(inp, toks)
+        assert np.array_equal(idx, r.idx[toks])
+        assert np.abs(ys - y[toks]).max() < 1e-11 * np.abs(y).max()
 
 
 # ---------------------------------------------------------------- page figures
