@@ -48,3 +48,26 @@ def run_layer(inp, return_routing=True, prepared=False):
     out = layer.forward(x, return_routing=return_routing)
     torch.cuda.synchronize()
     return layer, x, out
+
+
+def abs_butterfly_apply(angles, M, transpose=False):
+    """|S_{L-1}| ... |S_0| M (or the transposed order for B^T): the butterfly of
+    the given angles applied stage by stage with |cos| and |sin| in place of
+    cos and sin, M [n][m] non-negative.  Elementwise it bounds |B| |M|, since
+    each Givens block of B = S_{L-1} ... S_0 is a product of the stages' blocks
+    (triangle inequality); used for forward error bounds of rotations computed
+    in steps with rounding."""
+    ang = np.asarray(angles, dtype=np.float64)
+    L = ang.shape[0]
+    n = 1 << L
+    V = np.array(M, dtype=np.float64, copy=True)
+    for s in (range(L - 1, -1, -1) if transpose else range(L)):
+        h = 1 << s
+        c = np.abs(np.cos(ang[s])).reshape(n // (2 * h), h, 1)
+        sn = np.abs(np.sin(ang[s])).reshape(n // (2 * h), h, 1)
+        W = V.reshape(n // (2 * h), 2, h, V.shape[1])
+        a, b = W[:, 0].copy(), W[:, 1].copy()
+        W[:, 0] = c * a + sn * b
+        W[:, 1] = sn * a + c * b
+        V = W.reshape(n, -1)
+    return V

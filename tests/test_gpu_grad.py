@@ -51,7 +51,9 @@ def check_case(L, N, rows, transpose, act, seed, empty=(), inplace=False):
     xd, dyd = to_dev(x, act), to_dev(dy, act)
     angd = torch.from_numpy(ang).cuda()
     offd = torch.from_numpy(off).cuda()
-    dx, dang = bm.butterfly_backward(angd, offd, xd, dyd, transpose, dx=dyd if inplace else None)
+    # inplace: dx written over dy (True or "dy") or over x ("x")
+    out = xd if inplace == "x" else dyd if inplace else None
+    dx, dang = bm.butterfly_backward(angd, offd, xd, dyd, transpose, dx=out)
     torch.cuda.synchronize()
     dx, dang = to_f64(dx), dang.cpu().numpy().astype(np.float64)
     x64, dy64 = ref.stored_to_f64(x, act), ref.stored_to_f64(dy, act)
@@ -112,6 +114,11 @@ def test_butterfly_backward_in_place_and_zero_rows():
     check_case(12, 2, 90, False, "bf16", seed=6, inplace=True)  # part passes
     check_case(11, 3, 150, True, "f32", seed=8, inplace=True)   # one-pass width 2048
     check_case(10, 3, 77, False, "bf16", seed=9, inplace=True)  # one-pass width 1024
+    # dx over x: the one-pass kernels where two or four waves share a row
+    # (widths 1024, 2048) and the part passes, whose last pass re-reads x (4096)
+    for L, tr, seed in ((10, False, 41), (11, True, 42), (12, False, 43), (13, True, 44)):
+        for act in ("f32", "bf16"):
+            check_case(L, 3, 130, tr, act, seed=seed + (act == "bf16"), inplace="x")
     # no rows: every expert's angle gradients are zero, no row buffer touched
     ang = torch.randn(3, 5, 16, device="cuda")
     off = torch.zeros(4, dtype=torch.int32, device="cuda")
