@@ -64,93 +64,66 @@ class HipEvents:
 def kernel_work(cfg):
     """Algorithmic bytes and flops of each kernel of one forward.
 
-    Bytes count what the step must move at least once (activations in and out
-    of each kernel, the packed substrate, the angles of every expert, the
-    router weights); flops count multiply-adds as 2.  Returns
+    Bytes count what the method must move at least once per kernel: the
+    activations in and out, the router weights, the angles of the stages the
+    kernel applies (fp32, (n/2) per stage per expert), the ternary substrate at
+    2 bits per weight, and the routing indices and gates it reads or writes.
+    Re-encodings that the implementation builds once per weight set (fp4
+    substrate, bf16 block factors) and its own scratch (the router's per-tile
+    lists) are not counted.  Flops count multiply-adds as 2.  Returns
     {name: (bytes, flops, bound)}."""
     s = 2 if cfg.act == "bf16" else 4
     T, d, f, N, k = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k
     R = T * k
     Ld = int(math.log2(d))
-    ang_d = N * Ld * (d // 2) * 4
+    ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+
+    def ang(n, stages=None, nbfly=1):
+        # fp32 angles of `stages` stages of width-n butterflies, every expert
+        L = int(math.log2(n))
+        return nbfly * N * (L if stages is None else stages) * (n // 2) * 4
+
+    def bound(by, fl):
+        return "mfma" if fl / by > ridge else "hbm"
+
     w = {}
-    # the router also leaves each token tile's slots ordered by expert (R
-    # indices) and the first position of every expert in each tile's list
-    bt = 64 if T >= 64 * 256 else 32 if T >= 32 * 256 else 16
-    G = (T + bt - 1) // bt
-    w["route"] = (T * d * s + N * d * s + 8 * R + 4 * R + 4 * G * N, 2 * T * d * N, "hbm")
-    w["bucket"] = (4 * R + 4 * G * N + 4 * R + 4 * (N + 1), 0, "hbm")
+    w["route"] = (T * d * s + N * d * s + 8 * R, 2 * T * d * N, "hbm")
+    w["bucket"] = (8 * R + 4 * (N + 1), 0, "hbm")
 
     def split(L):
         # bf16 rows of width 1024 .. 8192: butterflies as low / high parts
         return cfg.act == "bf16" and 10 <= L <= 13
 
-    def part(n, stages, nbfly=1, extra=0):
-        # one pass over R rows of width n applying `stages` stages of nbfly butterflies
-        return (2 * R * n * s + nbfly * N * stages * (n // 2) * 4 + extra,
-                6 * R * (n // 2) * stages * nbfly, "hbm")
-
-    def lowfac_bytes(L):
-        # low-part block factors per expert (widths 1024 .. 8192, bf16 layers)
-        if cfg.act != "bf16" or not 10 <= L <= 13:
-            return 0
-        w = 1 << L
-        return 16 * ((w // 16) * max(16, w // 256) * 2 + (w // 256) * 512)
-
-    def highfac_bytes(L):
-        # high-part block factors per expert (one 16 x 16 bf16 block per column)
-        return (1 << (L - 4)) * 512 if cfg.act == "bf16" and 10 <= L <= 13 else 0
+    def low(n, extra=0):
+        # stages 0 .. L-5 of one butterfly over R rows (flops: 3 per element per stage)
+        L = int(math.log2(n))
+        return (2 * R * n * s + ang(n, L - 4) + extra, 3 * R * n * (L - 4), "hbm")
 
     def high(n, nbfly=1, extra=0):
-        L = int(math.log2(n))
-        return (2 * R * n * s + nbfly * N * highfac_bytes(L) + extra, 2 * R * n * 16 * nbfly, "hbm")
-
-    def low(n):
-        # low part of width n: block factors on the matrix cores where prepared
-        L = int(math.log2(n))
-        fb = lowfac_bytes(L)
-        if not fb:
-            return part(n, L - 4)
-        B0 = max(16, 1 << (L - 8))
-        return (2 * R * n * s + N * fb, 2 * R * n * (B0 + 16), "hbm")
-
-    prep_lo = prep_hi = 0
-
-    if split(Ld):
-        w["bfly_in_hi"] = high(d, extra=4 * R)
-        w["bfly_in_lo"] = low(d)
-        prep_lo += N * (Ld * (d // 2) * 4 + lowfac_bytes(Ld)) if lowfac_bytes(Ld) else 0
-        prep_hi += 2 * N * (4 * (d // 2) * 4 + highfac_bytes(Ld))
-    else:
-        w["bfly_in"] = (2 * R * d * s + ang_d + 4 * R, 6 * R * (d // 2) * Ld, "hbm")
-
-    def fp4_gemm(din, dout):
-        # bf16 products whose shape the fp4 matrix-core GEMM covers read the
-        # substrate prepared as fp4 (half a byte per weight)
-        return cfg.act == "bf16" and dout % 256 == 0 and din % 128 == 0
+        # the top four stages of nbfly butterflies over R rows
+        return (2 * R * n * s + ang(n, 4, nbfly) + extra, 3 * R * n * 4 * nbfly, "hbm")
 
     def gemm(din, dout):
         fl = 2 * R * din * dout
-        by = R * din * s + R * dout * s + dout * din // (2 if fp4_gemm(din, dout) else 4)
-        return (by, fl, "mfma" if fl / by > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm")
+        by = R * din * s + R * dout * s + dout * din // 4
+        return (by, fl, bound(by, fl))
 
+    if f == 0 and cfg.act == "bf16" and Ld <= 9:
+        # one kernel per expert tile: gathered x rows, per-slot rows (or y at
+        # k = 1), both rotations' angles, the substrate, slots and gates
+        fb = 2 * R * d * s + 2 * ang(d) + d * d // 4 + 8 * R
+        ff = 2 * R * d * d + 2 * 3 * R * d * Ld
+        w["fused"] = (fb, ff, bound(fb, ff))
+        if k > 1:
+            w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
+        return w
+    if split(Ld):
+        w["bfly_in_hi"] = high(d, extra=4 * R)
+        w["bfly_in_lo"] = low(d)
+    else:
+        w["bfly_in"] = (2 * R * d * s + ang(d) + 4 * R, 3 * R * d * Ld, "hbm")
     if f == 0:
         w["gemm"] = gemm(d, d)
-        if fp4_gemm(d, d) and Ld > 9:
-            w["prep"] = (d * d // 4 + d * d // 2, 0, "hbm")
-        if cfg.act == "bf16" and Ld in (8, 9):
-            # rotations as block factors on the matrix cores: per rotation one
-            # P x P and one 16 x 16 product per 32-wide / 16-wide block of a row
-            P = 32 if Ld == 9 else 16
-            fac = N * 2 * (P * 64 * 4 * 2 + 16 * (P // 16) * 64 * (P // 4) * 2)
-            w["prep"] = (d * d // 4 + d * d // 2 + 2 * ang_d + fac, 0, "hbm")
-            fb = 2 * R * d * s + fac + d * d // 2 + 8 * R
-            ff = 2 * R * d * d + 2 * 2 * R * d * (P + 16)
-        else:
-            fb = 2 * R * d * s + 2 * ang_d + d * d // 4 + 8 * R
-            ff = 2 * R * d * d + 2 * 6 * R * (d // 2) * Ld
-            w["prep"] = (d * d // 4 + d * d, 0, "hbm")
-        w["fused"] = (fb, ff, "mfma" if ff / fb > MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "hbm")
     else:
         Lf = int(math.log2(f))
         w["gemm_up"] = gemm(d, f)
@@ -158,24 +131,14 @@ def kernel_work(cfg):
             w["bfly_mid_lo"] = low(f)
             w["bfly_mid_hi"] = high(f, nbfly=2)
             w["bfly_mid_lo_t"] = low(f)
-            prep_lo += 2 * N * (Lf * (f // 2) * 4 + lowfac_bytes(Lf)) if lowfac_bytes(Lf) else 0
-            prep_hi += 2 * N * (4 * (f // 2) * 4 + highfac_bytes(Lf))
         else:
-            w["bfly_mid"] = (2 * R * f * s + 2 * N * Lf * (f // 2) * 4, 2 * 6 * R * (f // 2) * Lf, "hbm")
+            w["bfly_mid"] = (2 * R * f * s + ang(f, nbfly=2), 2 * 3 * R * f * Lf, "hbm")
         w["gemm_down"] = gemm(f, d)
-        pw = sum(a * b // 4 + a * b // 2 for a, b in ((d, f), (f, d)) if fp4_gemm(a, b))
-        if pw:
-            w["prep"] = (pw, 0, "hbm")
     if split(Ld):
         w["bfly_out_lo"] = low(d)
-        prep_lo += N * (Ld * (d // 2) * 4 + lowfac_bytes(Ld)) if lowfac_bytes(Ld) else 0
         w["bfly_out_hi"] = high(d, extra=8 * R)
     else:
-        w["bfly_out"] = (2 * R * d * s + ang_d + 8 * R, 6 * R * (d // 2) * Ld, "hbm")
-    if prep_lo:
-        w["prep_lo"] = (prep_lo, 0, "hbm")
-    if prep_hi:
-        w["prep_hi"] = (prep_hi, 0, "hbm")
+        w["bfly_out"] = (2 * R * d * s + ang(d) + 8 * R, 3 * R * d * Ld, "hbm")
     if k > 1:
         w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
     return w
@@ -191,35 +154,64 @@ def roofline_entry(by, fl, bound, seconds, traffic=None):
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
-def cpu_baseline(inp, y_gpu, seconds_target: float):
-    """fp64 oracle on this host: full-batch forwards until ~seconds_target."""
-    import numpy as np
-    from oracle import ref
+def _cores():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, y_gpu, seconds_target: float):
+    """fp64 oracle on this host.  Layers the oracle materialises in seconds:
+    full-batch forwards (every used expert materialised) until ~seconds_target.
+    The large FFN layer: fp64 routing of every token, then the oracle's
+    right-to-left products on seeded disjoint 64-token subsets until
+    ~seconds_target; tokens/s = subset tokens / their wall time."""
+    import numpy as np
+    from oracle import ref
+    cores = _cores()
     cfg = inp.cfg
-    t0 = time.perf_counter()
-    reps = 0
-    y_ref = None
-    while True:
-        y_ref, _ = ref.forward(inp)
-        reps += 1
+    err = None
+    if cfg.d_model * max(cfg.d_ff, cfg.d_model) <= 1 << 20:
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            y_ref, _ = ref.forward(inp)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds_target:
+                break
+        dt = time.perf_counter() - t0
+        if y_gpu is not None:
+            num = np.linalg.norm(y_gpu - y_ref, axis=1)
+            err = float((num / np.maximum(np.linalg.norm(y_ref, axis=1), 1e-30)).max())
+        return {"value": round(cfg.tokens * reps / dt, 1), "unit": "tokens/s", "cores": int(cores),
+                "kind": "oracle",
+                "sample": f"{reps} full-batch forward(s) of {cfg.tokens} tokens ({cfg.name}), "
+                          f"materialising every used expert in fp64, {dt:.1f} s",
+                "max_rel_err_gpu_vs_oracle": err}
+    tr = time.perf_counter()
+    x = ref.stored_to_f64(inp.x, cfg.act)
+    R = ref.route(x, ref.stored_to_f64(inp.w_gate, cfg.act), cfg.top_k, cfg.renorm_gates)
+    route_s = time.perf_counter() - tr
+    order = np.random.default_rng(0xB7F1).permutation(cfg.tokens)
+    done, t0 = 0, time.perf_counter()
+    errs = []
+    while done + 64 <= cfg.tokens:
+        toks = np.sort(order[done:done + 64])
+        y_ref, _, _ = ref.forward_tokens(inp, toks, routing=R)
+        done += 64
+        if y_gpu is not None:
+            num = np.linalg.norm(y_gpu[toks] - y_ref, axis=1)
+            errs.append(float((num / np.maximum(np.linalg.norm(y_ref, axis=1), 1e-30)).max()))
         if time.perf_counter() - t0 >= seconds_target:
             break
     dt = time.perf_counter() - t0
-    err = None
-    if y_gpu is not None:
-        num = np.linalg.norm(y_gpu - y_ref, axis=1)
-        den = np.maximum(np.linalg.norm(y_ref, axis=1), 1e-30)
-        err = float((num / den).max())
-    return {"value": round(cfg.tokens * reps / dt, 1), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{reps} full-batch forward(s) of {cfg.tokens} tokens ({cfg.name}), "
-                      f"materialising every used expert in fp64, {dt:.1f} s",
-            "max_rel_err_gpu_vs_oracle": err}
+    return {"value": round(done / dt, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 routing of all {cfg.tokens} tokens ({route_s:.1f} s), then {done // 64} seeded "
+                      f"64-token subsets through the oracle's right-to-left expert products "
+                      f"({cfg.name}), {dt:.1f} s for {done} tokens",
+            "max_rel_err_gpu_vs_oracle": max(errs) if errs else None}
 
 
 def spread_stats(v):
@@ -390,11 +382,14 @@ def grad_measure(reps: int = 20) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=None,
-                    help="workload index (default: the d=512, 64-expert layer)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+                    help="workload index (default: the large d=2048 FFN layer, with the other "
+                         "bf16 layers measured after it under by_config)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="measure only the headline workload")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 5 times (HBM counter calibration) and exit")
@@ -434,11 +429,60 @@ def main() -> int:
     if args.grad:
         print(json.dumps(grad_measure()))
         return 0
-    import compressed_mixture_experts_amd as bm
     from compressed_mixture_experts_amd import workloads as wl
 
     ci = wl.BENCH_CONFIG_INDEX if args.config is None else args.config
-    cfg = wl.CONFIGS[ci]
+    head = measure_workload(wl.CONFIGS[ci], args, args.steps, args.warmup, cpu=not args.no_cpu_baseline)
+    out = {
+        "metric": "routed tokens/sec per ButterflyMoE layer",
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.CONFIGS[ci].act,
+        "data": "synthetic (seeded Gaussian activations, uniform ternary substrate, uniform angles)",
+        **{k: v for k, v in head.items() if k not in ("value", "ms_per_step")},
+    }
+    if args.config is None and not args.headline_only:
+        # the other bf16 layer settings, same protocol, fewer steps, no CPU leg
+        out["by_config"] = {}
+        for cj in range(1, len(wl.CONFIGS)):
+            if cj == ci:
+                continue
+            r = measure_workload(wl.CONFIGS[cj], args, min(args.steps, 50), min(args.warmup, 10), cpu=False)
+            out["by_config"][r["config"]["workload"]] = {
+                "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+                "warm_ms_per_step": r["timing"]["warm_ms_per_step"], "roofline": r["roofline"],
+                "kernels": r["kernels"]}
+    print(json.dumps(out))
+    return 0
+
+
+def _flush_buffer():
+    """A 1 GiB device buffer; writing it evicts the 256 MB memory-side cache
+    and the L2s, so each timed step starts with its inputs in HBM only."""
+    import torch
+    return torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+
+def measure_workload(cfg, args, K, W, cpu=True):
+    """Time K forwards of one layer setting after W warm-up forwards.
+
+    Each timed step is one replay of a captured HIP graph of bmoe_forward,
+    bracketed by HIP events on the replay stream; before each step an eager
+    kernel writes a 1 GiB buffer (outside the events), so every step reads
+    its inputs from HBM.  The dominant kernel's duration comes from events
+    recorded around its launch inside the captured forward."""
+    import numpy as np
+    import torch
+    import compressed_mixture_experts_amd as bm
+    from compressed_mixture_experts_amd import workloads as wl
+
     wname = cfg.name + ("_skewed" if args.skewed else "")
     print(f"[bench] workload {wname}: generating inputs", file=sys.stderr, flush=True)
     inp = wl.generate(cfg, gate_mode="skewed" if args.skewed else "normal")
@@ -466,16 +510,19 @@ def main() -> int:
     names = layer.kernel_names()
     nk = len(names)
     ev = HipEvents()
+    flush = _flush_buffer()
 
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for _ in range(W):
         layer.forward(x, y)
     torch.cuda.synchronize()
 
-    # calibration (outside the timed region): every kernel bracketed
+    # calibration (outside the timed region): eager forwards with an event
+    # after every launch, cold caches; picks the dominant kernel
     cal_steps = 10
     marks = [ev.create(nk + 1) for _ in range(cal_steps)]
     for i in range(cal_steps):
+        flush.fill_(i & 0xFF)
         layer.forward_marked(x, y, marks[i])
     torch.cuda.synchronize()
     per_kernel = {n: 0.0 for n in names}
@@ -487,31 +534,27 @@ def main() -> int:
     dom = max(per_kernel, key=per_kernel.get)
     dj = names.index(dom)
 
-    # timed region: K steps, HIP events around the dominant kernel's launch
-    K = args.steps
+    # K captured forwards, each with events around the dominant kernel's launch
     starts, stops = ev.create(K), ev.create(K)
     step_marks = []
     for i in range(K):
         m = [None] * (nk + 1)
         m[dj], m[dj + 1] = starts[i], stops[i]
         step_marks.append(m)
-    # eager reference result and eager step time (launch by launch from the host)
     y_eager = layer.forward(x).clone()
     torch.cuda.synchronize()
+    # eager step time (launch by launch from the host, back to back)
     te0 = time.perf_counter()
     for i in range(K):
         layer.forward_marked(x, y, step_marks[i])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - te0) / K * 1e3
 
-    # each timed step replays a captured HIP graph of one forward (the same kernel
-    # launches and event records, replayed without host launch gaps); eager
-    # launches when capture is unavailable
     graphs = []
     graph_note = None
+    cs = torch.cuda.Stream()
     if not args.eager:
         try:
-            cs = torch.cuda.Stream()
             for i in range(K):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cs):
@@ -527,66 +570,84 @@ def main() -> int:
                     raise RuntimeError("graph replay differs from the eager forward")
         except Exception as ex:  # pragma: no cover - depends on the runtime
             graphs, graph_note = [], f"graph capture unavailable: {ex}"[:200]
+
+    def run_step(i):
+        if graphs:
+            graphs[i].replay()
+        else:
+            layer.forward_marked(x, y, step_marks[i])
+
+    # warm figure: the K steps back to back (caches hold what the previous step left)
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    for i in range(K):
+        run_step(i)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - tw0) / K * 1e3
+
+    # timed region: K steps, each after a 1 GiB eviction write, events around each step
     print(f"[bench] timing {K} steps (dominant kernel {dom}, "
-          f"{'graph replay' if graphs else 'eager'})", file=sys.stderr, flush=True)
+          f"{'graph replay' if graphs else 'eager'}, cold caches)", file=sys.stderr, flush=True)
+    s0, s1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)], \
+        [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if graphs:
-        for g in graphs:
-            g.replay()
-    else:
-        for i in range(K):
-            layer.forward_marked(x, y, step_marks[i])
+    for i in range(K):
+        flush.fill_((i + 1) & 0xFF)
+        s0[i].record()
+        run_step(i)
+        s1[i].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    wall = time.perf_counter() - t0
+    step_ms = [s0[i].elapsed_time(s1[i]) for i in range(K)]
+    ms_per_step = sum(step_ms) / K
     dom_ms = sum(ev.elapsed_ms(starts[i], stops[i]) for i in range(K)) / K
     ev.destroy(starts)
     ev.destroy(stops)
-    elapsed = t1 - t0
-    ms_per_step = elapsed / K * 1e3
-    value = cfg.tokens * K / elapsed
+    value = cfg.tokens / (ms_per_step * 1e-3)
 
     work = kernel_work(cfg)
-    by, fl, bound = work[dom]
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tfile):
+    if os.path.exists(tfile) and dom in work:
         try:
             tj = json.load(open(tfile)).get(f"{wname}:{dom}")
             if tj and tj.get("kernel_source_sha") == bm_kernel_sha(dom, cfg):
                 traffic = tj.get("bytes_per_launch")
         except Exception:
             traffic = None
-    roof = roofline_entry(by, fl, bound, dom_ms / 1e3, traffic)
-    roof["kernel"] = dom
-    roof["avg_us"] = round(dom_ms * 1e3, 2)
+    roof = None
+    if dom in work:
+        by, fl, bound = work[dom]
+        roof = roofline_entry(by, fl, bound, dom_ms / 1e3, traffic)
+        roof["kernel"] = dom
+        roof["avg_us"] = round(dom_ms * 1e3, 2)
+        roof["algorithmic_bytes"] = by
+        roof["algorithmic_flop"] = fl
 
     kernels = {}
     for n in names:
-        b_, f_, bd_ = work[n]
-        e = roofline_entry(b_, f_, bd_, per_kernel[n] / 1e3)
-        kernels[n] = {"us": round(per_kernel[n] * 1e3, 2), "bound": bd_, "frac": e["frac"]}
+        kernels[n] = {"us": round(per_kernel[n] * 1e3, 2)}
+        if n in work:
+            b_, f_, bd_ = work[n]
+            e = roofline_entry(b_, f_, bd_, per_kernel[n] / 1e3)
+            kernels[n].update({"bound": bd_, "frac": e["frac"]})
 
-    cpu = None
-    if not args.no_cpu_baseline:
+    cpu_res = None
+    if cpu:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         y64 = y.float().cpu().numpy().astype(np.float64)
-        cpu = cpu_baseline(inp, y64, args.cpu_seconds)
-
-    out = {
-        "metric": "routed tokens/sec per ButterflyMoE layer",
+        cpu_res = cpu_baseline(inp, y64, args.cpu_seconds)
+    res = {
         "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.act,
-        "data": "synthetic (seeded Gaussian activations, uniform ternary substrate, uniform angles)",
-        "weight_prep": ({"once_ms": round(prep_ms, 3), "in_timed_steps": False} if prep_ms is not None
+        "timing": {"protocol": "per-step HIP events around one graph replay, 1 GiB eviction write before "
+                               "each step (outside the events)",
+                   "cold_ms_per_step": round(ms_per_step, 5), "warm_ms_per_step": round(warm_ms, 5),
+                   "min_step_ms": round(min(step_ms), 5), "max_step_ms": round(max(step_ms), 5),
+                   "timed_region_wall_s": round(wall, 4)},
+        "weight_prep": ({"once_ms": round(prep_ms, 3), "in_timed_steps": False,
+                         "prepared_bytes": int(layer.prepared_bytes())} if prep_ms is not None
                         else {"in_timed_steps": layer.prepared_bytes() > 0}),
         "launch": ({"mode": "graph replay", "eager_ms_per_step": round(eager_ms, 5)} if graphs
                    else {"mode": "eager", "note": graph_note}),
@@ -595,11 +656,13 @@ def main() -> int:
                    "routed_rows": cfg.tokens * cfg.top_k, "parallelism": "single GPU",
                    "routing": {"gate_mode": "skewed" if args.skewed else "normal", **load}},
         "roofline": roof,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_res,
         "kernels": kernels,
     }
-    print(json.dumps(out))
-    return 0
+    del graphs, flush, layer, x, y, y_eager
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def bm_kernel_sha(kernel: str, cfg) -> str:

@@ -75,7 +75,7 @@ CONFIGS: List[LayerConfig] = [
                 outlier_scale=50.0, seed_index=4),
 ]
 
-BENCH_CONFIG_INDEX = 1
+BENCH_CONFIG_INDEX = 4
 
 
 @dataclasses.dataclass
