@@ -1,9 +1,14 @@
 """ButterflyMoE expert layer on AMD MI355X (gfx950): Python binding.
 
 The computation runs in ``libbmoe.so`` (hand-written HIP kernels behind the C
-ABI of ``include/bmoe.h``).  This module only marshals arguments: torch
-tensors provide device memory and the current HIP stream.  There is no
-fallback path; if the library is missing, loading it raises.
+ABI of ``include/bmoe.h``, ``bmoe_trace.h`` and ``bmoe_grad.h``).  The test
+hooks of ``include/bmoe_debug.h`` live only in ``libbmoe_debug.so`` (the same
+kernels, built with -DBMOE_DEBUG_EXPORTS), loaded on first use of a
+``dbg_*`` function.  This module only marshals arguments: torch tensors
+provide device memory and the current HIP stream.  There is no fallback path;
+if a library is missing, loading it raises.  The environment variable
+BMOE_LIBRARY names another build of the debug library to load for both (the
+CPU ABI tests use it for the sanitized host build).
 
     import compressed_mixture_experts_amd as bmoe
     layer = bmoe.Layer.from_inputs(inputs, device="cuda")   # uploads + packs
@@ -21,11 +26,12 @@ __all__ = [
     "BmoeError", "lib", "library_path", "pack_ternary", "packed_words", "Layer",
     "dbg_butterfly", "dbg_ternary_gemm", "dbg_ternary_gemm_fp4", "butterfly_backward", "substrate_grad",
     "combine_backward", "router_backward", "gelu_backward", "substrate_input_grad", "STATUS",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "DEBUG_SYMBOLS", "debug_lib",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libbmoe.so")
+_DEBUG_LIB_PATH = os.path.join(_PKG, "libbmoe_debug.so")
 
 STATUS = {
     0: "BMOE_OK", 1: "BMOE_ERR_NULL", 2: "BMOE_ERR_SHAPE", 3: "BMOE_ERR_DTYPE",
@@ -35,16 +41,18 @@ STATUS = {
 F32, BF16 = 0, 1
 ACT_NONE, ACT_GELU_ERF = 0, 1
 
+# exports of libbmoe.so (include/bmoe.h, bmoe_trace.h, bmoe_grad.h)
 EXPORTED_SYMBOLS = [
     "bmoe_packed_words", "bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepared_bytes",
     "bmoe_prepare", "bmoe_route", "bmoe_forward", "bmoe_status_string", "bmoe_last_error",
-    "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
-    "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
+    "bmoe_forward_kernels", "bmoe_forward_marked",
     "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
     "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
     "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward",
     "bmoe_substrate_input_grad",
 ]
+# exported by libbmoe_debug.so only (include/bmoe_debug.h)
+DEBUG_SYMBOLS = ["bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4"]
 
 
 class BmoeError(RuntimeError):
@@ -71,21 +79,18 @@ class LayerStruct(ctypes.Structure):
 
 
 _lib = None
+_debug_lib = None
 
 
 def library_path() -> str:
-    return _LIB_PATH
+    return os.environ.get("BMOE_LIBRARY") or _LIB_PATH
 
 
-def lib() -> ctypes.CDLL:
-    """Load libbmoe.so (built in-tree by compressed_mixture_experts_amd.build)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+def _load(path: str, debug: bool) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m compressed_mixture_experts_amd.build`")
-    L = ctypes.CDLL(_LIB_PATH)
+    L = ctypes.CDLL(path)
     c_i32, c_sz, c_vp, c_f = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
     pL = ctypes.POINTER(LayerStruct)
     L.bmoe_packed_words.argtypes = [c_i32, c_i32]
@@ -101,11 +106,8 @@ def lib() -> ctypes.CDLL:
     L.bmoe_status_string.restype = ctypes.c_char_p
     L.bmoe_last_error.argtypes = []
     L.bmoe_last_error.restype = ctypes.c_char_p
-    L.bmoe_dbg_butterfly.argtypes = [c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
-    L.bmoe_dbg_ternary_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
-    L.bmoe_dbg_ternary_gemm_fp4.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_f, c_vp, c_vp]
-    L.bmoe_dbg_forward_kernels.argtypes = [pL, ctypes.POINTER(c_i32), ctypes.c_char_p, c_sz]
-    L.bmoe_dbg_forward_marked.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_i32]
+    L.bmoe_forward_kernels.argtypes = [pL, ctypes.POINTER(c_i32), ctypes.c_char_p, c_sz]
+    L.bmoe_forward_marked.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_vp, c_i32]
     L.bmoe_butterfly_backward_workspace.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]
     L.bmoe_butterfly_backward.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_sz, c_vp]
@@ -117,21 +119,41 @@ def lib() -> ctypes.CDLL:
                                        c_vp, c_sz, c_vp]
     L.bmoe_gelu_backward.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
     L.bmoe_substrate_input_grad.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
-    for name in ("bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepare", "bmoe_route", "bmoe_forward",
-                 "bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4",
-                 "bmoe_dbg_forward_kernels", "bmoe_dbg_forward_marked",
-                 "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
-                 "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
-                 "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward",
-                 "bmoe_substrate_input_grad"):
+    ret = [n for n in EXPORTED_SYMBOLS if n not in ("bmoe_packed_words", "bmoe_prepared_bytes",
+                                                    "bmoe_status_string", "bmoe_last_error")]
+    if debug:
+        L.bmoe_dbg_butterfly.argtypes = [c_i32, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]
+        L.bmoe_dbg_ternary_gemm.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
+        L.bmoe_dbg_ternary_gemm_fp4.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_f, c_vp, c_vp]
+        ret += DEBUG_SYMBOLS
+    for name in ret:
         getattr(L, name).restype = c_i32
-    _lib = L
     return L
 
 
-def _check(status: int) -> None:
+def lib() -> ctypes.CDLL:
+    """Load libbmoe.so (built in-tree by compressed_mixture_experts_amd.build)."""
+    global _lib
+    if _lib is None:
+        alt = os.environ.get("BMOE_LIBRARY")
+        _lib = debug_lib() if alt else _load(_LIB_PATH, debug=False)
+    return _lib
+
+
+def debug_lib() -> ctypes.CDLL:
+    """Load libbmoe_debug.so: the product exports plus the test hooks of
+    include/bmoe_debug.h (or the library BMOE_LIBRARY names)."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(os.environ.get("BMOE_LIBRARY") or _DEBUG_LIB_PATH, debug=True)
+    return _debug_lib
+
+
+def _check(status: int, L: Optional[ctypes.CDLL] = None) -> None:
+    """Raise BmoeError for a nonzero status; the detail comes from the
+    thread-local error string of the library that returned it."""
     if status != 0:
-        detail = lib().bmoe_last_error().decode(errors="replace")
+        detail = (L or lib()).bmoe_last_error().decode(errors="replace")
         raise BmoeError(status, detail)
 
 
@@ -306,7 +328,7 @@ class Layer:
         """Names of the kernel launches of one forward, in order."""
         n = ctypes.c_int32(0)
         buf = ctypes.create_string_buffer(512)
-        _check(lib().bmoe_dbg_forward_kernels(ctypes.byref(self.struct), ctypes.byref(n), buf, 512))
+        _check(lib().bmoe_forward_kernels(ctypes.byref(self.struct), ctypes.byref(n), buf, 512))
         return buf.value.decode().split(",")[: n.value]
 
     def forward_marked(self, x, y, marks):
@@ -315,7 +337,7 @@ class Layer:
         T = int(x.shape[0])
         ws, nbytes = self.workspace(T, x.device)
         arr = (ctypes.c_void_p * max(len(marks), 1))(*[m if m else None for m in marks])
-        _check(lib().bmoe_dbg_forward_marked(ctypes.byref(self.struct), _ptr(x), T, _ptr(y),
+        _check(lib().bmoe_forward_marked(ctypes.byref(self.struct), _ptr(x), T, _ptr(y),
                                              _ptr(ws), nbytes, _stream_handle(), arr, len(marks)))
         return y
 
@@ -328,8 +350,9 @@ def dbg_butterfly(angles, x, transpose: bool = False, out=None):
     dtype = BF16 if x.dtype == torch.bfloat16 else F32
     if out is None:
         out = torch.empty_like(x)
-    _check(lib().bmoe_dbg_butterfly(log2n, rows, _ptr(angles), 1 if transpose else 0, dtype,
-                                    _ptr(x), _ptr(out), _stream_handle()))
+    D = debug_lib()
+    _check(D.bmoe_dbg_butterfly(log2n, rows, _ptr(angles), 1 if transpose else 0, dtype,
+                                _ptr(x), _ptr(out), _stream_handle()), D)
     return out
 
 
@@ -428,8 +451,9 @@ def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):
     M, K = int(a.shape[0]), int(a.shape[1])
     dtype = BF16 if a.dtype == torch.bfloat16 else F32
     z = torch.empty((M, n_out), dtype=a.dtype, device=a.device)
-    _check(lib().bmoe_dbg_ternary_gemm(M, n_out, K, dtype, _ptr(a), _ptr(w_packed), float(alpha),
-                                       _ptr(z), _stream_handle()))
+    D = debug_lib()
+    _check(D.bmoe_dbg_ternary_gemm(M, n_out, K, dtype, _ptr(a), _ptr(w_packed), float(alpha),
+                                   _ptr(z), _stream_handle()), D)
     return z
 
 
@@ -439,6 +463,7 @@ def dbg_ternary_gemm_fp4(a, w_packed, n_out: int, alpha: float = 1.0):
     M, K = int(a.shape[0]), int(a.shape[1])
     z = torch.empty((M, n_out), dtype=a.dtype, device=a.device)
     scratch = torch.empty((n_out * K // 2,), dtype=torch.uint8, device=a.device)
-    _check(lib().bmoe_dbg_ternary_gemm_fp4(M, n_out, K, _ptr(a), _ptr(w_packed), _ptr(scratch),
-                                           float(alpha), _ptr(z), _stream_handle()))
+    D = debug_lib()
+    _check(D.bmoe_dbg_ternary_gemm_fp4(M, n_out, K, _ptr(a), _ptr(w_packed), _ptr(scratch),
+                                       float(alpha), _ptr(z), _stream_handle()), D)
     return z

@@ -1,6 +1,8 @@
-// Host side of the C ABI declared in include/bmoe.h and include/bmoe_debug.h:
-// argument validation (all before any enqueue), workspace planning, and the
-// launch sequence of the forward pass on the caller's stream.
+// Host side of the C ABI declared in include/bmoe.h, include/bmoe_trace.h,
+// include/bmoe_grad.h and (built with -DBMOE_DEBUG_EXPORTS only)
+// include/bmoe_debug.h: argument validation (all before any enqueue),
+// workspace planning, and the launch sequence of the forward pass on the
+// caller's stream.
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -10,6 +12,7 @@
 #include "bmoe.h"
 #include "bmoe_debug.h"
 #include "bmoe_grad.h"
+#include "bmoe_trace.h"
 #include "common.hpp"
 
 using namespace bmoe;
@@ -450,8 +453,11 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T, int32_
   return ok();
 }
 
-// Kernel launches of one forward, in order (marks[i] follows launch i-1).
-static int forward_kernel_names(const bmoe_layer* L, const char** names) {
+// Kernel launches of one forward, in order (marks[i] follows launch i-1): at
+// most 1 + 2 LF_SETS preparation launches, route and bucket, and 12 for the
+// widest FFN layer.
+constexpr int kMaxForwardKernels = 1 + 2 * LF_SETS + 2 + 12;
+static int forward_kernel_names(const bmoe_layer* L, const char* (&names)[kMaxForwardKernels]) {
   int n = 0;
   if (!L->prepared) {
     const PrepLayout q = prep_layout(L);
@@ -662,12 +668,12 @@ bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void
                       nullptr, 0);
 }
 
-bmoe_status bmoe_dbg_forward_kernels(const bmoe_layer* layer, int32_t* n_kernels, char* names,
+bmoe_status bmoe_forward_kernels(const bmoe_layer* layer, int32_t* n_kernels, char* names,
                                      size_t names_len) {
   bmoe_status st = check_layer(layer);
   if (st != BMOE_OK) return st;
   if (!n_kernels) return fail(BMOE_ERR_NULL, "n_kernels is NULL");
-  const char* nm[16];
+  const char* nm[kMaxForwardKernels];
   const int n = forward_kernel_names(layer, nm);
   *n_kernels = n;
   if (names && names_len) {
@@ -681,7 +687,7 @@ bmoe_status bmoe_dbg_forward_kernels(const bmoe_layer* layer, int32_t* n_kernels
   return ok();
 }
 
-bmoe_status bmoe_dbg_forward_marked(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+bmoe_status bmoe_forward_marked(const bmoe_layer* layer, const void* x, int32_t T, void* y,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* marks, int32_t n_marks) {
   if (n_marks < 0) return fail(BMOE_ERR_SHAPE, "n_marks is negative");
@@ -744,6 +750,7 @@ bmoe_status bmoe_butterfly_backward(int32_t log2n, int32_t n_experts, int32_t ro
   return ok();
 }
 
+#ifdef BMOE_DEBUG_EXPORTS
 bmoe_status bmoe_dbg_butterfly(int32_t log2n, int32_t rows, const float* angles, int32_t transpose,
                                int32_t dtype, const void* in, void* out, hipStream_t stream) {
   if (log2n < 3 || log2n > 13) return fail(BMOE_ERR_SHAPE, "log2n=%d must be in [3, 13]", log2n);
@@ -761,7 +768,7 @@ bmoe_status bmoe_dbg_butterfly(int32_t log2n, int32_t rows, const float* angles,
   bmoe_status st = check_device();
   if (st != BMOE_OK) return st;
   BflyArgs a{in, out, angles, nullptr, nullptr, nullptr, nullptr, rows, 1, 1, transpose, 0};
-  BMOE_HIP(launch_butterfly(a, BFLY_DBG, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, log2n, stream));
+  BMOE_HIP(launch_bfly_dbg(a, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, log2n, stream));
   return ok();
 }
 
@@ -810,6 +817,8 @@ bmoe_status bmoe_dbg_ternary_gemm_fp4(int32_t M, int32_t N, int32_t K, const voi
   BMOE_HIP(launch_gemm_fp4(g, stream));
   return ok();
 }
+
+#endif  // BMOE_DEBUG_EXPORTS
 
 const char* bmoe_status_string(bmoe_status s) {
   switch (s) {

@@ -1052,16 +1052,8 @@ size_t bfly_bwd_workspace(int log2n, int n_experts, int rows) {
 template <int L, int ACT>
 static hipError_t bb_launch(const BflyBwdArgs& a, hipStream_t s) {
   const size_t lds = size_t(2) * a.rt * (1 << L) * sizeof(float);
-  static int attr_done[64] = {0};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  const hipError_t err = allow_dynamic_lds((const void*)bfly_bwd_kernel<L, ACT>, lds);
   if (err != hipSuccess) return err;
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    err = hipFuncSetAttribute((const void*)bfly_bwd_kernel<L, ACT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              int(lds));
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
-  }
   hipLaunchKernelGGL((bfly_bwd_kernel<L, ACT>), dim3(a.n_chunks), dim3(bb_threads(L)), lds, s, a);
   return hipGetLastError();
 }

@@ -540,16 +540,10 @@ hipError_t launch_high_factor_prep(const float* ang, unsigned char* out, int n_e
 }
 
 template <typename K>
-static hipError_t sp_launch(K k, int grid, size_t lds, const BflyArgs& a, hipStream_t s, int* attr_done) {
+static hipError_t sp_launch(K k, int grid, size_t lds, const BflyArgs& a, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  const hipError_t err = allow_dynamic_lds((const void*)k, lds);
   if (err != hipSuccess) return err;
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
-  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(BF_THREADS), lds, s, a);
   return hipGetLastError();
 }
@@ -560,23 +554,21 @@ static int sp_tiles(const BflyArgs& a) { return (a.rows + SP_RB - 1) / SP_RB + a
 // prepared data); a missing buffer is a caller error.
 template <int S>
 static hipError_t launch_low_S(const BflyArgs& a, bool trans, hipStream_t s) {
-  static int done[2][64] = {{0}};
   if (!a.fac) return hipErrorInvalidValue;
   const int grid = sp_tiles(a) * (16 / LowMCfg<S>::SC);
-  if (trans) return sp_launch(lowm_kernel<S, true>, grid, LowMCfg<S>::lds_bytes, a, s, done[1]);
-  return sp_launch(lowm_kernel<S, false>, grid, LowMCfg<S>::lds_bytes, a, s, done[0]);
+  if (trans) return sp_launch(lowm_kernel<S, true>, grid, LowMCfg<S>::lds_bytes, a, s);
+  return sp_launch(lowm_kernel<S, false>, grid, LowMCfg<S>::lds_bytes, a, s);
 }
 
 template <int S>
 static hipError_t launch_high_S(const BflyArgs& a, int mode, hipStream_t s) {
-  static int done[64] = {0};
   if (!a.fac || (mode == SH_MID && !a.fac1)) return hipErrorInvalidValue;
   const int grid = sp_tiles(a) * ((1 << S) / SP_VC);
   const size_t lds = HighMCfg<S>::lds_bytes;
   switch (mode) {
-    case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s, done);
-    case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s, done);
-    default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s, done);
+    case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s);
+    case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s);
+    default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s);
   }
 }
 

@@ -224,6 +224,17 @@ hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
+// one angle set for all rows (the test hook of bmoe_debug.h)
+hipError_t launch_bfly_dbg(const BflyArgs& a, int act, int log2n, hipStream_t s);
+
+// A kernel launched with more than the default 64 KiB of dynamic LDS needs its
+// limit raised first.  Done before every such launch (host work of the order
+// of a microsecond) instead of remembered, so the library keeps no mutable
+// state between calls.
+inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 bool bfly_split_supported(int log2n);
 // Low-part block factors (matrix-core low part, widths 4096 and 8192): bytes per

@@ -266,15 +266,8 @@ static hipError_t launch_fused_L(const FusedArgs& a, hipStream_t s) {
   using F = FusedCfg<L>;
   const int grid = (a.rows + FZ_RT - 1) / FZ_RT + a.n_experts;
   auto k = fused_square_kernel<L>;
-  static int attr_done[64] = {0};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  const hipError_t err = allow_dynamic_lds((const void*)k, F::lds_bytes);
   if (err != hipSuccess) return err;
-  if (F::lds_bytes > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(F::lds_bytes));
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
-  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(BF_THREADS), F::lds_bytes, s, a);
   return hipGetLastError();
 }

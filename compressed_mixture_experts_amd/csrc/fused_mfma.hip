@@ -347,27 +347,18 @@ static hipError_t launch_fused_mfma_L(const FusedArgs& a, hipStream_t s) {
   const size_t lds = size_t(2) * RT * MfCfg<L>::TS;
   const int grid = (a.rows + RT - 1) / RT + a.n_experts;
   auto k = fused_mfma_kernel<L, RT>;
-  static int attr_done[64] = {0};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  const hipError_t err = allow_dynamic_lds((const void*)k, lds);
   if (err != hipSuccess) return err;
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
-  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(RT == 32 ? 256 : 512), lds, s, a);
   return hipGetLastError();
 }
 
 int fused_tile_rows(int rows, int n_experts) {
-  static int cus[64] = {0};
-  int dev = 0, cu = 256;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus[dev] = 0;
-    if (cus[dev] > 0) cu = cus[dev];
-  }
+  // compute units of the current device, asked on every call (no cached state)
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+    cu = 256;
   auto tiles = [&](int rt) { return (long(rows) + rt - 1) / rt + n_experts; };  // records, a bound on tiles
   if (tiles(32) > 2L * cu) return 32;
   return tiles(48) <= cu ? 48 : 64;

@@ -170,16 +170,8 @@ template <int TM, int TN, int NS>
 static hipError_t launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
   const int ntn = (a.N + TN - 1) / TN, ntm = (a.M + TM - 1) / TM;
   const size_t lds = size_t(2) * (TN + TM) * GLDK * sizeof(uint16_t);
-  static int attr_done[64] = {0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  const hipError_t e = allow_dynamic_lds((const void*)gemm_bf16_kernel<TM, TN, NS>, lds);
   if (e != hipSuccess) return e;
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<TM, TN, NS>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
-  }
   auto kern = gemm_bf16_kernel<TM, TN, NS>;
   hipLaunchKernelGGL(kern, dim3(ntn * ntm), dim3(GM_THREADS), lds, s, a);
   return hipGetLastError();

@@ -169,15 +169,8 @@ static hipError_t launch_gemm_fp4_tn(const GemmFp4Args& a, hipStream_t s) {
   const int ntn = a.N / TN, ntm = (a.M + GF_TM - 1) / GF_TM;
   const int ngrp = (ntm + GF_GRP - 1) / GF_GRP;
   const size_t lds = size_t(2) * GF_TILE * sizeof(uint16_t);
-  static int attr_done[64] = {0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  const hipError_t e = allow_dynamic_lds((const void*)gemm_fp4_kernel<TN>, lds);
   if (e != hipSuccess) return e;
-  if (lds > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    e = hipFuncSetAttribute((const void*)gemm_fp4_kernel<TN>, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
-  }
   hipLaunchKernelGGL(gemm_fp4_kernel<TN>, dim3(ngrp * GF_GRP * ntn), dim3(GF_THREADS), lds, s, a);
   return hipGetLastError();
 }

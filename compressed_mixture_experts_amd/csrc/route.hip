@@ -828,27 +828,18 @@ static size_t route_lds_bytes(int N, size_t tiles) {
 
 constexpr size_t RT_WHOLE_MAX = 72 * 1024;  // whole token tile in LDS up to this size
 
-// `opted`: per-device flags of one kernel (dynamic LDS above 64 KiB allowed once)
 template <typename K>
-static hipError_t route_launch(K kern, int* opted, int grid, int threads, size_t lds, hipStream_t s,
-                               const RouteArgs& a) {
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+static hipError_t route_launch(K kern, int grid, int threads, size_t lds, hipStream_t s, const RouteArgs& a) {
+  const hipError_t err = allow_dynamic_lds((const void*)kern, lds);
   if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= 64 || !opted[dev]) {
-    err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) opted[dev] = 1;
-  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
 template <int BT, int NK, int NI>
 static hipError_t launch_whole(const RouteArgs& a, hipStream_t s) {
-  static int opted[64] = {0};
   const size_t lds = route_lds_bytes<BT>(a.N, size_t(BT) * (NK * RT_BK + 8) * sizeof(uint16_t));
-  return route_launch(route_whole_kernel<BT, NK, NI>, opted, (a.T + BT - 1) / BT, RW_THREADS, lds, s, a);
+  return route_launch(route_whole_kernel<BT, NK, NI>, (a.T + BT - 1) / BT, RW_THREADS, lds, s, a);
 }
 
 // whole-tile kernel when the tile fits LDS and a wave's gate rows fit 128
@@ -875,11 +866,10 @@ static hipError_t launch_route_bt(const RouteArgs& a, int act, hipStream_t s) {
       }
     }
   }
-  static int opted_b[64] = {0}, opted_f[64] = {0};
   const size_t lds = route_lds_bytes<BT>(a.N, size_t(2) * BT * RT_XLD * sizeof(uint16_t));
   const int grid = (a.T + BT - 1) / BT;
-  if (act == ACT_BF16) return route_launch(route_kernel<ACT_BF16, BT>, opted_b, grid, RT_THREADS, lds, s, a);
-  return route_launch(route_kernel<ACT_F32, BT>, opted_f, grid, RT_THREADS, lds, s, a);
+  if (act == ACT_BF16) return route_launch(route_kernel<ACT_BF16, BT>, grid, RT_THREADS, lds, s, a);
+  return route_launch(route_kernel<ACT_F32, BT>, grid, RT_THREADS, lds, s, a);
 }
 
 // the largest token tile (64, 32 or 16 tokens) that still gives every CU a

@@ -43,6 +43,21 @@
  *
  * Limits.  d_model and d_ff (when nonzero) are powers of two in [64, 8192];
  * 1 <= n_experts <= 256; 1 <= top_k <= min(8, n_experts); 0 <= T.
+ *
+ * Layout choices (the pages fix no interface; these are this library's):
+ *   - The gate matrix is stored expert-major, [n_experts][d_model]: expert e's
+ *     gate vector is one contiguous row, which is the operand layout the
+ *     router's matrix-core tiles load (16 experts x 32 columns per fragment).
+ *     A caller holding W_g as [d_model][n_experts] passes its transpose.
+ *   - Angles come as one array per rotation (theta[m], phi[m]), each
+ *     [n_experts][log2 n][n/2], rather than one array holding every rotation
+ *     of an expert: a kernel applies one rotation to the rows of many
+ *     experts, so each rotation's angles of all experts are one contiguous
+ *     block.  The four rotations of an FFN expert are theta[0] (B(theta_up),
+ *     width d_model), phi[0] (B(phi_up), d_ff), theta[1] (B(theta_dn), d_ff)
+ *     and phi[1] (B(phi_dn), d_model).
+ *   - The library keeps no state between calls except the per-thread error
+ *     string; every call re-derives what it needs from its arguments.
  */
 #ifndef BMOE_H
 #define BMOE_H

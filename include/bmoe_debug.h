@@ -3,6 +3,10 @@
  * that each kernel can be checked on its own against a reference.  They run
  * the same kernels bmoe_forward runs, on caller-given device buffers, enqueued
  * on `stream`, with the same validation rules and error codes as bmoe.h.
+ *
+ * Test-only: these functions exist only in a library compiled with
+ * -DBMOE_DEBUG_EXPORTS (libbmoe_debug.so, built beside libbmoe.so); the
+ * product library libbmoe.so does not export them.
  */
 #ifndef BMOE_DEBUG_H
 #define BMOE_DEBUG_H
@@ -41,21 +45,6 @@ bmoe_status bmoe_dbg_ternary_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype
 bmoe_status bmoe_dbg_ternary_gemm_fp4(int32_t M, int32_t N, int32_t K, const void* a,
                                       const uint32_t* w_packed, void* w_fp4, float alpha,
                                       void* z, hipStream_t stream);
-
-/* Names of the kernel launches one bmoe_forward makes for this layer, in
- * launch order, comma-separated into `names` (truncated to names_len), and
- * their number in *n_kernels. */
-bmoe_status bmoe_dbg_forward_kernels(const bmoe_layer* layer, int32_t* n_kernels, char* names,
-                                     size_t names_len);
-
-/* bmoe_forward (without the optional routing outputs) that also records
- * marks[0] on `stream` before its first kernel launch and marks[i] after its
- * i-th launch (i = 1 .. n_kernels); NULL entries and entries at or beyond
- * n_marks are skipped.  The events are created and owned by the caller; the
- * call never synchronises.  Used to time single kernels of a live forward. */
-bmoe_status bmoe_dbg_forward_marked(const bmoe_layer* layer, const void* x, int32_t T, void* y,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                    hipEvent_t* marks, int32_t n_marks);
 
 #ifdef __cplusplus
 }

@@ -12,10 +12,11 @@ import compressed_mixture_experts_amd as bm
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def header_functions():
+def header_functions(debug=False):
+    """Functions declared by the product headers (or by bmoe_debug.h alone)."""
     names = set()
-    for h in os.listdir(os.path.join(ROOT, "include")):
-        if h.endswith(".h"):
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h") and (h == "bmoe_debug.h") == debug:
             src = open(os.path.join(ROOT, "include", h)).read()
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
             names |= set(re.findall(r"\b(bmoe_\w+)\s*\(", src))
@@ -28,6 +29,15 @@ def test_library_exports_every_declared_function():
     assert declared == set(bm.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
+    # the test hooks are in the debug build only
+    dbg = header_functions(debug=True)
+    assert dbg == set(bm.DEBUG_SYMBOLS)
+    D = bm.debug_lib()
+    for name in declared | dbg:
+        assert hasattr(D, name), name
+    if not os.environ.get("BMOE_LIBRARY"):
+        for name in dbg:
+            assert not hasattr(L, name), f"{name} exported by the product library"
 
 
 def decode_packed(words: np.ndarray, cols: int) -> np.ndarray:
@@ -188,7 +198,7 @@ def test_route_argument_errors():
 
 
 def test_debug_hook_argument_errors():
-    L = bm.lib()
+    L = bm.debug_lib()
     assert L.bmoe_dbg_butterfly(2, 4, FAKE, 0, 0, FAKE, FAKE, None) == 2
     assert L.bmoe_dbg_butterfly(14, 4, FAKE, 0, 0, FAKE, FAKE, None) == 2
     assert L.bmoe_dbg_butterfly(8, 4, FAKE, 3, 0, FAKE, FAKE, None) == 2
@@ -484,3 +494,23 @@ def test_substrate_input_grad_arguments():
     assert call(dz=dz + 8) == 4 and call(du=du + 2) == 4
     assert call(du=dz + 64) == 5 and call(du=wt) == 5
     assert call(rows=0, dz=None) == 0                    # nothing to do, nothing launched
+
+
+def test_forward_kernel_names_of_the_widest_layer():
+    # per-call preparation of an FFN layer whose both widths use the split
+    # rotations: the most launches one forward makes
+    L = bm.lib()
+    s = make_struct(d_model=2048, d_ff=8192, n_experts=256, ffn_act=bm.ACT_GELU_ERF)
+    n = ctypes.c_int32(0)
+    buf = ctypes.create_string_buffer(1024)
+    assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), buf, 1024) == 0
+    names = buf.value.decode().split(",")
+    assert len(names) == n.value == 21
+    assert names[:1] == ["prep"] and names.count("prep_lo") == 4 and names.count("prep_hi") == 4
+    assert names[9:] == ["route", "bucket", "bfly_in_hi", "bfly_in_lo", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+                         "bfly_mid_lo_t", "gemm_down", "bfly_out_lo", "bfly_out_hi", "combine"]
+    # truncation keeps the string terminated
+    small = ctypes.create_string_buffer(8)
+    assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), small, 8) == 0
+    assert small.value == b"prep,pr"
+    assert L.bmoe_forward_kernels(ctypes.byref(s), None, small, 8) == 1
