@@ -39,13 +39,14 @@ STATUS = {
     7: "BMOE_ERR_TERNARY", 8: "BMOE_ERR_HIP", 9: "BMOE_ERR_DEVICE",
 }
 F32, BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20   # BMOE_NOALLOC_SCRATCH_BYTES of include/bmoe.h
 ACT_NONE, ACT_GELU_ERF = 0, 1
 
 # exports of libbmoe.so (include/bmoe.h, bmoe_trace.h, bmoe_grad.h)
 EXPORTED_SYMBOLS = [
     "bmoe_packed_words", "bmoe_pack_ternary", "bmoe_workspace_size", "bmoe_prepared_bytes",
-    "bmoe_prepare", "bmoe_route", "bmoe_forward", "bmoe_status_string", "bmoe_last_error",
-    "bmoe_forward_kernels", "bmoe_forward_marked",
+    "bmoe_prepare", "bmoe_route", "bmoe_forward", "bmoe_forward_noalloc", "bmoe_status_string",
+    "bmoe_last_error", "bmoe_forward_kernels", "bmoe_forward_marked",
     "bmoe_butterfly_backward_workspace", "bmoe_butterfly_backward",
     "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
     "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward",
@@ -102,6 +103,7 @@ def _load(path: str, debug: bool) -> ctypes.CDLL:
     L.bmoe_prepare.argtypes = [pL, c_vp, c_sz, c_vp]
     L.bmoe_route.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
     L.bmoe_forward.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+    L.bmoe_forward_noalloc.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]
     L.bmoe_status_string.argtypes = [c_i32]
     L.bmoe_status_string.restype = ctypes.c_char_p
     L.bmoe_last_error.argtypes = []
@@ -323,6 +325,14 @@ class Layer:
             return y, idx, gate
         return y
 
+    def forward_noalloc(self, x, y, idx=None, gate=None):
+        """bmoe_forward_noalloc: the forward into caller-given y (and optional
+        idx / gate [T][top_k]) with the library's fixed device scratch as the
+        workspace; nothing is allocated by the call."""
+        T = int(x.shape[0])
+        _check(lib().bmoe_forward_noalloc(ctypes.byref(self.struct), _ptr(x), T, _ptr(y), _ptr(idx),
+                                          _ptr(gate), _stream_handle()))
+        return y
 
     def kernel_names(self) -> List[str]:
         """Names of the kernel launches of one forward, in order."""

@@ -668,6 +668,53 @@ bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void
                       nullptr, 0);
 }
 
+// ---- allocation-free forward -------------------------------------------
+// The workspace of bmoe_forward_noalloc: a fixed array in device memory, one
+// copy per GPU the library runs on, alive until the process ends.  Host code
+// never uses the array's name as an address: each device's copy is looked up
+// once with hipGetSymbolAddress and that pointer is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[BMOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+// per-device address of `scratch` (set on the device's first call; the one
+// piece of state the library keeps besides the error string)
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+bmoe_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  BMOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BMOE_ERR_DEVICE, "device %d is beyond the %d this build serves", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    BMOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || !aligned(p, 256)) return fail(BMOE_ERR_HIP, "scratch of device %d has no usable address", dev);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return BMOE_OK;
+}
+}  // namespace
+
+bmoe_status bmoe_forward_noalloc(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+                                 int32_t* topk_idx, float* topk_gate, hipStream_t stream) {
+  size_t need = 0;
+  bmoe_status st = bmoe_workspace_size(layer, T, &need);
+  if (st != BMOE_OK) return st;
+  if (need > BMOE_NOALLOC_SCRATCH_BYTES)
+    return fail(BMOE_ERR_WORKSPACE,
+                "this layer at T=%d needs %zu bytes of workspace; the allocation-free forward has a fixed "
+                "scratch of %zu bytes (use bmoe_forward with a caller workspace, or fewer tokens per call)",
+                T, need, size_t(BMOE_NOALLOC_SCRATCH_BYTES));
+  if (T == 0) return ok();
+  st = check_device();
+  if (st != BMOE_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != BMOE_OK) return st;
+  return forward_impl(layer, x, T, y, topk_idx, topk_gate, ws, BMOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
+}
+
 bmoe_status bmoe_forward_kernels(const bmoe_layer* layer, int32_t* n_kernels, char* names,
                                      size_t names_len) {
   bmoe_status st = check_layer(layer);

@@ -196,6 +196,29 @@ bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void
                          int32_t* topk_idx, float* topk_gate,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Size of the fixed device scratch that bmoe_forward_noalloc uses as its
+ * workspace (64 MiB; one copy per GPU the library runs on, held until the
+ * process ends). */
+#define BMOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* bmoe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as bmoe_forward, but no workspace argument:
+ * the library's own scratch array on the current device serves as the
+ * workspace, so the call allocates nothing (no hipMalloc / hipFree; its first
+ * call on a device looks up that device's scratch address once).
+ *   - Layers and T whose bmoe_workspace_size exceeds
+ *     BMOE_NOALLOC_SCRATCH_BYTES are rejected with BMOE_ERR_WORKSPACE before
+ *     anything is enqueued (e.g. the d=512, 64-expert, top-2 layer fits up to
+ *     about 30000 tokens with prepared weights).
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *     time on one device (different streams, or different host threads
+ *     without ordering) race and give undefined results.  Calls ordered on
+ *     one stream are safe; nothing in the scratch carries over between calls.
+ *   - y must not overlap x or the optional routing outputs (BMOE_ERR_ALIAS). */
+bmoe_status bmoe_forward_noalloc(const bmoe_layer* layer, const void* x, int32_t T, void* y,
+                                 int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* bmoe_status_string(bmoe_status status);
 

@@ -514,3 +514,19 @@ def test_forward_kernel_names_of_the_widest_layer():
     assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), small, 8) == 0
     assert small.value == b"prep,pr"
     assert L.bmoe_forward_kernels(ctypes.byref(s), None, small, 8) == 1
+
+
+def test_forward_noalloc_argument_errors():
+    # rejected on the host before any device call: a workspace beyond the fixed
+    # scratch, a bad layer; T = 0 is a no-op
+    L = bm.lib()
+    s = make_struct()                       # d=512, 64 experts, top-2, no prepared buffer
+    st, need = ws_size(s, 40000)
+    assert st == 0 and need > bm.NOALLOC_SCRATCH_BYTES
+    assert L.bmoe_forward_noalloc(ctypes.byref(s), FAKE, 40000, FAKE + 0x10000000, None, None, None) == 6
+    msg = L.bmoe_last_error()
+    assert b"scratch" in msg and str(bm.NOALLOC_SCRATCH_BYTES).encode() in msg
+    assert L.bmoe_forward_noalloc(ctypes.byref(make_struct(d_model=500)), FAKE, 16, FAKE, None, None, None) == 2
+    assert L.bmoe_forward_noalloc(None, FAKE, 16, FAKE, None, None, None) == 1
+    assert L.bmoe_forward_noalloc(ctypes.byref(s), None, 0, None, None, None, None) == 0
+    assert L.bmoe_forward_noalloc(ctypes.byref(s), FAKE, -1, FAKE, None, None, None) == 2
