@@ -468,11 +468,12 @@ def dbg_ternary_gemm(a, w_packed, n_out: int, alpha: float = 1.0):
 
 
 def dbg_ternary_gemm_fp4(a, w_packed, n_out: int, alpha: float = 1.0):
-    """Matrix-core form of dbg_ternary_gemm for bf16 `a` (substrate re-encoded as fp4)."""
+    """Matrix-core form of dbg_ternary_gemm for bf16 `a` (substrate re-encoded as
+    paired 2-bit codes in a scratch buffer first)."""
     torch = _torch()
     M, K = int(a.shape[0]), int(a.shape[1])
     z = torch.empty((M, n_out), dtype=a.dtype, device=a.device)
-    scratch = torch.empty((n_out * K // 2,), dtype=torch.uint8, device=a.device)
+    scratch = torch.empty((n_out * K // 4,), dtype=torch.uint8, device=a.device)
     D = debug_lib()
     _check(D.bmoe_dbg_ternary_gemm_fp4(M, n_out, K, _ptr(a), _ptr(w_packed), _ptr(scratch),
                                        float(alpha), _ptr(z), _stream_handle()), D)

@@ -156,9 +156,9 @@ bool use_split(const bmoe_layer* L, int log2n) {
 
 // Prepared-weights buffer, 256-aligned sections: [substrate 0 re-encoded |
 // substrate 1 re-encoded (FFN) | rotation factors].  Fused square layers: the
-// substrate as bytes (widths 64, 128) or fp4 (256, 512) plus block factors
-// (256, 512).  Other bf16 layers: each substrate whose product the fp4 GEMM
-// covers, as fp4.  fp32 layers: nothing.
+// substrate as bytes (widths 64, 128) or paired 2-bit codes (256, 512) plus
+// block factors (256, 512).  Other bf16 layers: each substrate whose product
+// the matrix-core GEMM covers, as paired 2-bit codes.  fp32 layers: nothing.
 // Low-part block factors of the butterflies of width 4096 / 8192 (bf16 layers):
 // input rotation theta (transposed), output rotation phi, FFN phi_up, FFN
 // theta_dn (transposed).
@@ -188,7 +188,7 @@ PrepLayout prep_layout(const bmoe_layer* L) {
   if (use_fused(L)) {
     const size_t d = size_t(L->d_model);
     q.fp4[0] = use_fused_mfma(L);
-    q.w_len[0] = d * d / (q.fp4[0] ? 2 : 1);
+    q.w_len[0] = d * d / (q.fp4[0] ? 4 : 1);
     o = align256(q.w_len[0]);
     q.fac_off = o;
     q.fac_len = q.fp4[0] ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(L->d_model)) : 0;
@@ -202,7 +202,7 @@ PrepLayout prep_layout(const bmoe_layer* L) {
     if (!gemm_fp4_supported(n_out, k_in)) continue;
     q.fp4[m] = true;
     q.w_off[m] = o;
-    q.w_len[m] = size_t(n_out) * size_t(k_in) / 2;
+    q.w_len[m] = size_t(n_out) * size_t(k_in) / 4;
     o = align256(o + q.w_len[m]);
   }
   q.fac_off = o;
@@ -575,7 +575,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   const unsigned char* wbytes = q.w_len[0] ? pbase + q.w_off[0] : nullptr;
   const unsigned char* wbytes1 = q.w_len[1] ? pbase + q.w_off[1] : nullptr;
   const unsigned char* fac = q.fac_len ? pbase + q.fac_off : nullptr;
-  // substrate product: fp4 matrix-core GEMM on a prepared substrate, else the 2-bit one
+  // substrate product: matrix-core GEMM on a prepared substrate, else the 2-bit LDS-decoding one
   auto substrate_gemm = [&](int m, const void* a_in, void* z_out, int32_t n_out, int32_t k_in) -> hipError_t {
     const unsigned char* wq = m == 0 ? wbytes : wbytes1;
     if (wq) return launch_gemm_fp4(GemmFp4Args{a_in, wq, z_out, layer->w_scale[m], R, n_out, k_in}, stream);
@@ -848,7 +848,7 @@ bmoe_status bmoe_dbg_ternary_gemm_fp4(int32_t M, int32_t N, int32_t K, const voi
   if (!a || !w_packed || !w_fp4 || !z) return fail(BMOE_ERR_NULL, "a / w_packed / w_fp4 / z is NULL");
   if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_fp4, 16) || !aligned(z, 16))
     return fail(BMOE_ERR_ALIGN, "a, w_packed, w_fp4 and z must be 16-byte aligned");
-  const Range ra{a, size_t(M) * K * 2}, rz{z, size_t(M) * N * 2}, rq{w_fp4, size_t(N) * K / 2},
+  const Range ra{a, size_t(M) * K * 2}, rz{z, size_t(M) * N * 2}, rq{w_fp4, size_t(N) * K / 4},
       rw{w_packed, size_t(N) * K / 4};
   if (overlap(ra, rz) || overlap(rq, ra) || overlap(rq, rz) || overlap(rq, rw))
     return fail(BMOE_ERR_ALIAS, "z / w_fp4 overlap an operand");

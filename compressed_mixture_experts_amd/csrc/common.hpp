@@ -25,6 +25,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Paired 2-bit substrate code: one 32-bit word holds 16 consecutive ternary
+// weights, weight c < 8 as bit 4c+1 (nonzero) and bit 4c+3 (negative), weight
+// 8 + c as bits 4c and 4c+2.  Masking the word, or the word shifted left by
+// one, leaves eight fp4 e2m1 nibbles (weight c in nibble c): +1 -> 0x2,
+// -1 -> 0xA, 0 -> 0x0, which v_cvt_scalef32_pk_bf16_fp4 turns into exact bf16.
+__device__ __forceinline__ uint32_t pair2_to_fp4(uint32_t w, bool upper) {
+  return (upper ? (w << 1) : w) & 0xAAAAAAAAu;
+}
+
 // Load 8 consecutive activations starting at element `i` of `p` as floats.
 template <int ACT>
 __device__ __forceinline__ void load8(const void* p, size_t i, float v[8]) {
@@ -129,7 +138,9 @@ struct BucketArgs {
 struct PrepArgs {
   const uint32_t* w_packed; // substrate 0, 2-bit packed, w_words words (16 weights each)
   unsigned char* w_out;     // w_fp4 == 0: one byte per weight (bf16 high byte of +-0.5 / 0);
-                            // w_fp4 == 1: fp4 e2m1 nibbles, two per byte, low nibble first
+                            // w_fp4 == 1: paired 2-bit codes, one 32-bit word per 16
+                            // consecutive weights (pair2_to_fp4 turns a word into two words
+                            // of fp4 e2m1 nibbles)
   int32_t w_words;
   int32_t w_fp4;
   const uint32_t* w_packed1; // substrate 1 (FFN down), always fp4; w_words1 may be 0
@@ -206,7 +217,7 @@ struct GemmArgs {
 
 struct GemmFp4Args {
   const void* a;            // [M][K] bf16
-  const unsigned char* w;   // [N][K/2] fp4 e2m1 substrate (weight 2b in the low nibble of byte b)
+  const unsigned char* w;   // [N][K/4] substrate as paired 2-bit codes (pair2_to_fp4)
   void* z;                  // [M][N] bf16
   float alpha;
   int32_t M, N, K;

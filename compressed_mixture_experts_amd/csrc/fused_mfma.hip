@@ -27,6 +27,7 @@
 //   G_B^T    wave (tb, h): token block tb, classes p of half h   -> buf1 [row][m][p]
 //   G_A^T    wave (tb, h): blocks m of half h                    -> buf0 [row][i]  (= U)
 //   W        wave w: outputs [w n/NW, (w+1) n/NW) of all rows, accumulators kept
+//            (substrate as paired 2-bit codes, expanded to exact bf16 in registers)
 //   G_A      on the accumulators of the wave's own blocks        -> buf1 [row][p][m]
 //   G_B      wave (tb, h): classes p of half h, * gate * alpha   -> buf0 [row][i]
 //   store    buf0 rows -> per-slot rows
@@ -123,11 +124,12 @@ __global__ __launch_bounds__(RT == 32 ? 256 : 512, RT == 32 ? 2 : 1) void fused_
   constexpr int PG = PA / 8;
   constexpr int ITEMS = RT * 4 * PG;
   constexpr int IPT = (ITEMS + NT - 1) / NT;  // items past ITEMS have rows t >= RT >= nr
-  // substrate rows: n/2 bytes of fp4.  Unit v covers contraction indices
-  // [256v, 256v+256) = bytes [128v, 128v+128) of a row; lane group g takes
-  // bytes 16g..16g+15 of each 64-byte half (two loads that fill one line).
-  const unsigned char* wrow = a.wb + size_t(wave * (n / NW) + l16) * (n / 2) + 16 * g;
-  uint4 W0[OB][2];
+  // substrate rows: n/4 bytes of paired 2-bit codes (16 weights per word).
+  // Unit v covers contraction indices [256v, 256v+256) = bytes [64v, 64v+64)
+  // of a row; lane group g takes bytes 8g..8g+7 of each 32-byte half, the
+  // words of indices 256v + 128h + 32g .. +31.
+  const unsigned char* wrow = a.wb + size_t(wave * (n / NW) + l16) * (n / 4) + 8 * g;
+  uint2 W0[OB][2];
   {
     uint4 ch[IPT][4];
 #pragma unroll
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(RT == 32 ? 256 : 512, RT == 32 ? 2 : 1) void fused_
     for (int i = 0; i < OB; ++i)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        W0[i][hf] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * (n / 2) + 64 * hf);
+        W0[i][hf] = *reinterpret_cast<const uint2*>(wrow + size_t(16 * i) * (n / 4) + 32 * hf);
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int item = it * NT + tid;
@@ -220,27 +222,27 @@ __global__ __launch_bounds__(RT == 32 ? 256 : 512, RT == 32 ? 2 : 1) void fused_
       }
     }
   }
-  uint4 W1[OB][2];  // second substrate unit (width 512)
+  uint2 W1[OB][2];  // second substrate unit (width 512)
   if constexpr (NU == 2) {
 #pragma unroll
     for (int i = 0; i < OB; ++i)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        W1[i][hf] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * (n / 2) + 128 + 64 * hf);
+        W1[i][hf] = *reinterpret_cast<const uint2*>(wrow + size_t(16 * i) * (n / 4) + 64 + 32 * hf);
   }
   __syncthreads();
 
   // ---- Z = U W^T: wave owns outputs [wave n/NW, (wave+1) n/NW) of all RT rows.
-  // In unit v, MFMA step s (8 contraction indices) of lane group g uses dword
-  // s % 4 of half s / 4: indices 256v + 128(s/4) + 32g + 8(s%4) .. +7; the U
-  // operand is read in the same order.
+  // In unit v, MFMA step s (8 contraction indices) of lane group g uses
+  // indices 256v + 128(s/4) + 32g + 8(s%4) .. +7: word (s%4)/2 of half s/4,
+  // its lower or upper eight weights; the U operand is read in the same order.
   f32x4_t acc[OB][MB];
 #pragma unroll
   for (int i = 0; i < OB; ++i)
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = zero4;
   const uint16_t* urow = reinterpret_cast<const uint16_t*>(buf0) + l16 * (TS / 2) + 32 * g;
-  auto unit = [&](const uint4 (&Wu)[OB][2], int v) {
+  auto unit = [&](const uint2 (&Wu)[OB][2], int v) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const int kk = 256 * v + 128 * (st >> 2) + 8 * (st & 3);
@@ -249,7 +251,8 @@ __global__ __launch_bounds__(RT == 32 ? 256 : 512, RT == 32 ? 2 : 1) void fused_
       for (int j = 0; j < MB; ++j) uf[j] = *reinterpret_cast<const uint4*>(urow + 16 * j * (TS / 2) + kk);
 #pragma unroll
       for (int i = 0; i < OB; ++i) {
-        const uint4 wv = fp4x8_to_bf16(u4get(Wu[i][st >> 2], st & 3));
+        const uint2 wd = Wu[i][st >> 2];
+        const uint4 wv = fp4x8_to_bf16(pair2_to_fp4((st & 2) ? wd.y : wd.x, st & 1));
 #pragma unroll
         for (int j = 0; j < MB; ++j) acc[i][j] = mfma32(wv, uf[j], acc[i][j]);
       }

@@ -1,13 +1,14 @@
 // Shared ternary substrate product Z = alpha * U * W^T for wide layers, with the
-// substrate pre-encoded as fp4 e2m1 (ButterflyMoE, gist.science/zh/paper/2601.13563,
+// substrate prepared as paired 2-bit codes (ButterflyMoE, gist.science/zh/paper/2601.13563,
 // technical summary §2.1-§2.2: one ternary substrate shared by every expert, so
 // all routed rows form one dense contraction: M = rows, N = d_out, K = d_in).
 //
 // Workgroup tile: 128 rows x TN output columns, four waves; wave w owns output
 // columns [w TN/4, (w+1) TN/4) for all 128 rows, so no two waves read the same
 // substrate rows.  Its substrate fragments come straight from global memory
-// (16 bytes = 32 fp4 weights per lane per 128-wide K step; four lanes fill a
-// 64-byte half line of a row) and become exact bf16 +-1/0 with one
+// (8 bytes = 32 weights per lane per 128-wide K step, two words of 16; four
+// lanes fill 32 contiguous bytes of a row), each word becomes two words of
+// fp4 nibbles by a mask (pair2_to_fp4) and exact bf16 +-1/0 with one
 // v_cvt_scalef32_pk_bf16_fp4 per two weights.  The activation tile (128 rows x
 // 128 K, bf16) goes through two LDS buffers and is read by all four waves.
 // In a K step, lanes 16g .. 16g+15 supply contraction indices 32g .. 32g+31 of
@@ -65,8 +66,8 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
   const int m0 = tm * GF_TM, n0 = tn * TN + wave * WN;
   const int K = a.K, nk = K / GF_KS;
   const uint16_t* U = reinterpret_cast<const uint16_t*>(a.a);
-  // this lane's substrate rows n0 + 16 i + l16, bytes 16 g .. 16 g + 15 of each 64-byte step
-  const unsigned char* wrow = a.w + size_t(n0 + l16) * (K / 2) + 16 * g;
+  // this lane's substrate rows n0 + 16 i + l16, bytes 8 g .. 8 g + 7 of each 32-byte step
+  const unsigned char* wrow = a.w + size_t(n0 + l16) * (K / 4) + 8 * g;
   // this lane's source of direct load j: row 4 (DPW wave + j) + lane / 16 (clamped to
   // M - 1: rows past M are never stored), chunk (lane % 16) ^ (row % 16)
   auto usrc = [&](int j) {
@@ -75,10 +76,10 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
     return U + size_t(min(m0 + row, a.M - 1)) * K + 8 * ch;
   };
 
-  auto load_w = [&](int kt, uint4 (&w)[OB]) {
+  auto load_w = [&](int kt, uint2 (&w)[OB]) {
 #pragma unroll
     for (int i = 0; i < OB; ++i)
-      w[i] = *reinterpret_cast<const uint4*>(wrow + size_t(16 * i) * (K / 2) + 64 * kt);
+      w[i] = *reinterpret_cast<const uint2*>(wrow + size_t(16 * i) * (K / 4) + 32 * kt);
   };
   auto load_u = [&](int kt, int buf) {
 #pragma unroll
@@ -101,14 +102,15 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
     for (int j = 0; j < MB; ++j)
       uf[j] = *reinterpret_cast<const bf16x8_t*>(ub + (16 * j + l16) * GF_KS + 8 * p);
   };
-  // products of one sub-step with dword 0 of each substrate fragment, which
-  // then rotates so that the next sub-step's dword is dword 0 (the sub-step
-  // loop stays rolled, which bounds the live operand registers)
-  auto substep = [&](const bf16x8_t (&uf)[MB], uint4 (&Wc)[OB]) {
+  // products of one sub-step with the lower (upper) eight weights of word 0
+  // of each substrate fragment; after the upper half the words swap, so that
+  // the next two sub-steps use word 0 again (the sub-step loop stays rolled,
+  // which bounds the live operand registers)
+  auto substep = [&](const bf16x8_t (&uf)[MB], uint2 (&Wc)[OB], bool upper) {
 #pragma unroll
     for (int i = 0; i < OB; ++i) {
-      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, gf_fp4x8_to_bf16(Wc[i].x));
-      Wc[i] = make_uint4(Wc[i].y, Wc[i].z, Wc[i].w, Wc[i].x);
+      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, gf_fp4x8_to_bf16(pair2_to_fp4(Wc[i].x, upper)));
+      if (upper) Wc[i] = make_uint2(Wc[i].y, Wc[i].x);
 #pragma unroll
       for (int j = 0; j < MB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, uf[j], acc[i][j], 0, 0, 0);
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
   // wait for the loads and for every wave.  The operand fragments of sub-step
   // s + 1 are read while sub-step s multiplies (the read past sub-step 3 is of
   // chunk 4 g + 4 ^ l16 < 16 of the same rows, unused).
-  auto step = [&](int kt, uint4 (&Wc)[OB], uint4 (&Wn)[OB]) {
+  auto step = [&](int kt, uint2 (&Wc)[OB], uint2 (&Wn)[OB]) {
     const int buf = kt & 1;
     if (kt + 1 < nk) {
       load_u(kt + 1, buf ^ 1);
@@ -131,14 +133,14 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
       load_uf(ub, 2 * h + 1, ubf);
-      substep(ua, Wc);
+      substep(ua, Wc, false);
       load_uf(ub, (2 * h + 2) & 3, ua);
-      substep(ubf, Wc);
+      substep(ubf, Wc, true);
     }
     __syncthreads();  // waits for this wave's loads, then for every wave
   };
 
-  uint4 W0[OB], W1[OB];
+  uint2 W0[OB], W1[OB];
   load_u(0, 0);
   load_w(0, W0);
   __syncthreads();

@@ -22,7 +22,8 @@ __global__ __launch_bounds__(PR_THREADS) void prep_kernel(PrepArgs a) {
   const int tid = threadIdx.x;
   // substrate: 16 weights per word, column 2j+h of the word's 16: nonzero bit
   // 16h+j, sign bit 16h+8+j.  Bytes: +1 -> 0x3F, -1 -> 0xBF, 0 -> 0 (bf16 high
-  // byte of +-0.5); fp4 e2m1: +1 -> 0x2, -1 -> 0xA, 0 -> 0
+  // byte of +-0.5); paired 2-bit code (pair2_to_fp4): column c < 8 at bits
+  // 4c+1 (nonzero) and 4c+3 (sign), column 8+c at bits 4c and 4c+2
   const int nw = a.w_words + a.w_words1;
   for (int i = blockIdx.x * PR_THREADS + tid; i < nw; i += gridDim.x * PR_THREADS) {
     const bool s1 = i >= a.w_words;
@@ -30,19 +31,24 @@ __global__ __launch_bounds__(PR_THREADS) void prep_kernel(PrepArgs a) {
     const bool fp4 = s1 || a.w_fp4;
     const uint32_t P = s1 ? a.w_packed1[w] : a.w_packed[w];
     unsigned char* out = s1 ? a.w_out1 : a.w_out;
-    uint32_t code[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int j = c >> 1, h = c & 1;
-      const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = (P >> (16 * h + 8 + j)) & 1u;
-      code[c] = fp4 ? nz * (0x2u | (sg << 3)) : nz * (0x3Fu | (sg << 7));
-    }
     if (fp4) {
-      uint32_t o[2] = {0u, 0u};
+      uint32_t o = 0u;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) o[c >> 3] |= code[c] << (4 * (c & 7));
-      reinterpret_cast<uint2*>(out)[w] = make_uint2(o[0], o[1]);
+      for (int c = 0; c < 16; ++c) {
+        const int j = c >> 1, h = c & 1;
+        const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = nz & (P >> (16 * h + 8 + j));
+        const int at = c < 8 ? 4 * c + 1 : 4 * (c - 8);
+        o |= (nz << at) | (sg << (at + 2));
+      }
+      reinterpret_cast<uint32_t*>(out)[w] = o;
     } else {
+      uint32_t code[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int j = c >> 1, h = c & 1;
+        const uint32_t nz = (P >> (16 * h + j)) & 1u, sg = (P >> (16 * h + 8 + j)) & 1u;
+        code[c] = nz * (0x3Fu | (sg << 7));
+      }
       uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int c = 0; c < 16; ++c) o[c >> 2] |= code[c] << (8 * (c & 3));

@@ -144,13 +144,17 @@ bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* byte
  * uses one; fp32 layers use none.  Contents, all depending on the weights only
  * (ButterflyMoE zh §2.1-§2.2: ternary substrate, per-expert Givens angles):
  *  - square layers of width 64..512: the substrate re-encoded for the expert
- *    kernel (one byte per weight at widths 64 and 128, one fp4 e2m1 nibble per
- *    weight at 256 and 512) and, at widths 256 and 512, every expert's
+ *    kernel (one byte per weight at widths 64 and 128; at 256 and 512 two bits
+ *    per weight, each 32-bit word holding 16 consecutive weights with the
+ *    nonzero and sign bits of weight c < 8 at bits 4c+1 and 4c+3 and of
+ *    weight 8+c at bits 4c and 4c+2, so that a mask gives fp4 e2m1 nibbles)
+ *    and, at widths 256 and 512, every expert's
  *    rotations as block-diagonal factors in bf16 (stages below bit 5 at width
  *    512 / bit 4 at width 256 as one block per group of 32 / 16 consecutive
  *    indices, the stages above as 16 x 16 blocks);
  *  - other layers: each substrate whose product has an output width that is a
- *    multiple of 256 and a contraction that is a multiple of 128, as fp4; and
+ *    multiple of 256 and a contraction that is a multiple of 128, in the same
+ *    two-bit code; and
  *    for every rotation of width n = 2^L in 1024..8192, per expert, its stages
  *    0..L-5 as block factors per chunk of 2^(L-4) indices and its top four
  *    stages as one 16 x 16 block per column (bf16). */

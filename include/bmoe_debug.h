@@ -37,11 +37,13 @@ bmoe_status bmoe_dbg_ternary_gemm(int32_t M, int32_t N, int32_t K, int32_t dtype
                                   void* z, hipStream_t stream);
 
 /* The same product on the matrix-core path of bf16 layers: W is re-encoded as
- * fp4 e2m1 nibbles into `w_fp4` (N * K / 2 bytes, device, 16-byte aligned,
- * caller-owned scratch, overwritten), then multiplied with bf16 operands and
- * fp32 accumulation (ButterflyMoE zh §2.2: ternary substrate; +-1 and 0 are
- * exact in e2m1).  a [M][K] bf16, z [M][N] bf16; N a multiple of 256, K a
- * multiple of 128, M >= 0.  w_fp4 must overlap none of a, w_packed, z. */
+ * paired 2-bit codes into `w_fp4` (N * K / 4 bytes, device, 16-byte aligned,
+ * caller-owned scratch, overwritten; each 32-bit word holds 16 consecutive
+ * weights and masks turn it into fp4 e2m1 nibbles, in which +-1 and 0 are
+ * exact), then multiplied with bf16 operands and fp32 accumulation
+ * (ButterflyMoE zh §2.2: ternary substrate).  a [M][K] bf16, z [M][N] bf16; N
+ * a multiple of 256, K a multiple of 128, M >= 0.  w_fp4 must overlap none of
+ * a, w_packed, z. */
 bmoe_status bmoe_dbg_ternary_gemm_fp4(int32_t M, int32_t N, int32_t K, const void* a,
                                       const uint32_t* w_packed, void* w_fp4, float alpha,
                                       void* z, hipStream_t stream);

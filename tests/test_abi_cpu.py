@@ -230,16 +230,16 @@ def test_status_strings():
 
 def test_prepared_bytes_layout():
     L = bm.lib()
-    # square bf16 width 512: fp4 substrate d*d/2 plus 98304 factor bytes per expert
+    # square bf16 width 512: 2-bit substrate d*d/4 plus 98304 factor bytes per expert
     s = make_struct()
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 512 * 512 // 2 + 64 * 98304
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 512 * 512 // 4 + 64 * 98304
     s = make_struct(d_model=256)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 256 * 256 // 2 + 64 * 32768
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 256 * 256 // 4 + 64 * 32768
     # widths 64 / 128: one byte per weight, no factors (rounded up to 256 bytes)
     s = make_struct(d_model=128)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 128 * 128
-    # wider bf16 layers: each substrate whose product the fp4 GEMM covers
-    # (output width a multiple of 256, contraction a multiple of 128), as fp4;
+    # wider bf16 layers: each substrate whose product the matrix-core GEMM covers
+    # (output width a multiple of 256, contraction a multiple of 128), 2 bits per weight;
     # every rotation of width 1024 .. 8192: one 16 x 16 high-part block per column
     # (width / 16 columns), and at widths 4096 / 8192 the low-part block factors
     # (16 chunks x (16 blocks 16 x 16 + 16 blocks 16 x 16), or (16 blocks 32 x 32
@@ -249,17 +249,18 @@ def test_prepared_bytes_layout():
     hi = lambda w: (w // 16) * 512
     lo = lambda w: 16 * ((w // 16) * max(16, w // 256) * 2 + (w // 256) * 512)
     rot = lambda w: hi(w) + lo(w)
-    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 2 + 2 * 64 * rot(1024)
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 4 + 2 * 64 * rot(1024)
     s = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (4096 * 1024 // 2) + 2 * 64 * rot(1024)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (4096 * 1024 // 4) + 2 * 64 * rot(1024)
                                                       + 2 * 64 * rot(4096))
     assert lo(4096) == 16 * 16384 and lo(8192) == 16 * (32768 + 16384)
     s = make_struct(d_model=2048, d_ff=8192, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (8192 * 2048 // 2) + 2 * 64 * rot(2048)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (8192 * 2048 // 4) + 2 * 64 * rot(2048)
                                                       + 2 * 64 * rot(8192))
-    # d_ff = 128: the up product (128 outputs) keeps the 2-bit GEMM, the down one is fp4
+    # d_ff = 128: the up product (128 outputs) keeps the LDS-decoding GEMM, the down
+    # one runs on the prepared codes
     s = make_struct(d_model=1024, d_ff=128, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 2 + 2 * 64 * rot(1024)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 4 + 2 * 64 * rot(1024)
     s = make_struct(d_model=128, d_ff=64, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 0
     # fp32 activations and invalid layers use none
