@@ -51,6 +51,8 @@ EXPORTED_SYMBOLS = [
     "bmoe_substrate_grad_workspace", "bmoe_substrate_grad", "bmoe_combine_backward",
     "bmoe_router_backward_workspace", "bmoe_router_backward", "bmoe_gelu_backward",
     "bmoe_substrate_input_grad",
+    "bmoe_train_state_size", "bmoe_forward_train_workspace", "bmoe_forward_train",
+    "bmoe_layer_backward_workspace", "bmoe_layer_backward",
 ]
 # exported by libbmoe_debug.so only (include/bmoe_debug.h)
 DEBUG_SYMBOLS = ["bmoe_dbg_butterfly", "bmoe_dbg_ternary_gemm", "bmoe_dbg_ternary_gemm_fp4"]
@@ -61,6 +63,14 @@ class BmoeError(RuntimeError):
         self.status = status
         self.name = STATUS.get(status, str(status))
         super().__init__(f"{self.name}: {detail}")
+
+
+class LayerGrads(ctypes.Structure):
+    """bmoe_layer_grads of include/bmoe_train.h (device pointers)."""
+    _fields_ = [
+        ("dx", ctypes.c_void_p), ("d_w_gate", ctypes.c_void_p),
+        ("d_theta", ctypes.c_void_p * 2), ("d_phi", ctypes.c_void_p * 2), ("d_w_base", ctypes.c_void_p * 2),
+    ]
 
 
 class LayerStruct(ctypes.Structure):
@@ -121,6 +131,12 @@ def _load(path: str, debug: bool) -> ctypes.CDLL:
                                        c_vp, c_sz, c_vp]
     L.bmoe_gelu_backward.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
     L.bmoe_substrate_input_grad.argtypes = [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f, c_vp, c_vp]
+    L.bmoe_train_state_size.argtypes = [pL, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_forward_train_workspace.argtypes = [pL, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_forward_train.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp, c_sz, c_vp]
+    L.bmoe_layer_backward_workspace.argtypes = [pL, c_i32, ctypes.POINTER(c_sz)]
+    L.bmoe_layer_backward.argtypes = [pL, c_vp, c_i32, c_vp, c_vp, c_sz, ctypes.POINTER(LayerGrads), c_vp, c_sz,
+                                      c_vp]
     ret = [n for n in EXPORTED_SYMBOLS if n not in ("bmoe_packed_words", "bmoe_prepared_bytes",
                                                     "bmoe_status_string", "bmoe_last_error")]
     if debug:
@@ -333,6 +349,55 @@ class Layer:
         _check(lib().bmoe_forward_noalloc(ctypes.byref(self.struct), _ptr(x), T, _ptr(y), _ptr(idx),
                                           _ptr(gate), _stream_handle()))
         return y
+
+    def _sized(self, fn, T: int, device) -> Tuple[object, int]:
+        torch = _torch()
+        n = ctypes.c_size_t(0)
+        _check(fn(ctypes.byref(self.struct), T, ctypes.byref(n)))
+        return torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device), int(n.value)
+
+    def forward_train(self, x, y=None):
+        """bmoe_forward_train: y = layer(x) and the state the layer backward
+        reads (an opaque device buffer).  Returns (y, state)."""
+        torch = _torch()
+        T = int(x.shape[0])
+        if y is None:
+            y = torch.empty_like(x)
+        state, ns = self._sized(lib().bmoe_train_state_size, T, x.device)
+        ws, nw = self._sized(lib().bmoe_forward_train_workspace, T, x.device)
+        _check(lib().bmoe_forward_train(ctypes.byref(self.struct), _ptr(x), T, _ptr(y), _ptr(state), ns, _ptr(ws), nw,
+                                        _stream_handle()))
+        return y, state
+
+    def backward(self, x, dy, state) -> dict:
+        """bmoe_layer_backward: fp32 gradients of sum(dy * y) in x, the gate
+        matrix, every rotation's angles and the latent substrates, at the
+        state of forward_train(x).  Returns dict(x, w_gate, theta [list],
+        phi [list], w_base [list]) of device tensors."""
+        torch = _torch()
+        T = int(x.shape[0])
+        dev = x.device
+        nm = 2 if self.struct.d_ff else 1
+        out = {"x": torch.empty((T, self.d_model), dtype=torch.float32, device=dev),
+               "w_gate": torch.empty((self.n_experts, self.d_model), dtype=torch.float32, device=dev),
+               "theta": [], "phi": [], "w_base": []}
+        g = LayerGrads()
+        g.dx = _ptr(out["x"])
+        g.d_w_gate = _ptr(out["w_gate"])
+        for m in range(nm):
+            th, ph = self.theta[m], self.phi[m]
+            out["theta"].append(torch.empty_like(th, dtype=torch.float32))
+            out["phi"].append(torch.empty_like(ph, dtype=torch.float32))
+            d_out = 1 << (ph.shape[1])
+            d_in = 1 << (th.shape[1])
+            out["w_base"].append(torch.empty((d_out, d_in), dtype=torch.float32, device=dev))
+            g.d_theta[m] = _ptr(out["theta"][m])
+            g.d_phi[m] = _ptr(out["phi"][m])
+            g.d_w_base[m] = _ptr(out["w_base"][m])
+        ws, nw = self._sized(lib().bmoe_layer_backward_workspace, T, dev)
+        _check(lib().bmoe_layer_backward(ctypes.byref(self.struct), _ptr(x), T, _ptr(dy), _ptr(state),
+                                         int(state.numel()), ctypes.byref(g), _ptr(ws), nw, _stream_handle()))
+        return out
 
     def kernel_names(self) -> List[str]:
         """Names of the kernel launches of one forward, in order."""

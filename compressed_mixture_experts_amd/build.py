@@ -3,7 +3,8 @@
     python -m compressed_mixture_experts_amd.build [--jobs N] [--no-host-sanitize]
 
 Outputs, next to this file:
-  libbmoe.so          the product library (include/bmoe.h, bmoe_trace.h, bmoe_grad.h)
+  libbmoe.so          the product library (include/bmoe.h, bmoe_trace.h, bmoe_grad.h,
+                      bmoe_train.h)
   libbmoe_debug.so    the same plus the test hooks of include/bmoe_debug.h
                       (api.hip compiled with -DBMOE_DEBUG_EXPORTS)
   libbmoe_hostsan.so  the debug library with its host code (argument checks,
@@ -32,7 +33,7 @@ LIB_HOSTSAN = os.path.join(PKG, "libbmoe_hostsan.so")
 KERNEL_SOURCES = ["route.hip", "gemm.hip", "butterfly.hip", "butterfly_in.hip", "butterfly_mid.hip",
                   "butterfly_out.hip", "fused.hip", "fused_mfma.hip", "prep.hip", "gemm_fp4.hip",
                   "butterfly_split.hip", "butterfly_bwd.hip", "substrate_grad.hip", "combine_bwd.hip",
-                  "router_bwd.hip", "gelu_bwd.hip"]
+                  "router_bwd.hip", "gelu_bwd.hip", "butterfly_rot.hip", "train.hip"]
 DEBUG_SOURCES = ["butterfly_dbg.hip"]   # kernels reached only from the test hooks
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -8,11 +8,13 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "bmoe.h"
 #include "bmoe_debug.h"
 #include "bmoe_grad.h"
 #include "bmoe_trace.h"
+#include "bmoe_train.h"
 #include "common.hpp"
 
 using namespace bmoe;
@@ -1062,3 +1064,367 @@ bmoe_status bmoe_substrate_input_grad(int32_t rows, int32_t d_out, int32_t d_in,
   BMOE_HIP(launch_gemm(g, dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32, stream));
   return ok();
 }
+
+// ---------------------------------------------------------------- training path
+namespace {
+
+// State of a training forward (slices 256-byte aligned): routing, then the rows
+// the backward reads, in bucket order and the activation dtype.
+struct TrainLayout {
+  size_t idx, gate, offsets, perm, qpos, U, H1, H, V, Z, O, total;
+};
+
+TrainLayout train_layout(const bmoe_layer* L, int32_t T) {
+  TrainLayout t{};
+  const size_t R = size_t(T) * L->top_k, s = act_size(L->act_dtype);
+  const size_t d = size_t(L->d_model), f = size_t(L->d_ff);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  t.idx = take(R * 4);
+  t.gate = take(R * 4);
+  t.offsets = take(size_t(L->n_experts + 1) * 4);
+  t.perm = take(R * 4);
+  t.qpos = take(R * 4);
+  t.U = take(R * d * s);
+  if (f) {
+    t.H1 = take(R * f * s);
+    t.H = take(R * f * s);
+    t.V = take(R * f * s);
+  }
+  t.Z = take(R * d * s);
+  t.O = take(R * d * s);
+  t.total = o;
+  return t;
+}
+
+// Workspace of the training forward: the router's tile lists, and at FFN
+// layers the GELU output between the two middle rotations.
+struct TrainFwdWs {
+  size_t tslots, tgates, tstart, A, total;
+  int32_t tiles;
+};
+
+TrainFwdWs train_fwd_ws(const bmoe_layer* L, int32_t T) {
+  TrainFwdWs w{};
+  const size_t R = size_t(T) * L->top_k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  w.tiles = T > 0 ? int32_t((int64_t(T) + route_tile_tokens(T) - 1) / route_tile_tokens(T)) : 0;
+  w.tslots = take(R * 4);
+  w.tgates = take(R * 4);
+  w.tstart = take(size_t(w.tiles) * L->n_experts * 4);
+  w.A = take(L->d_ff ? R * size_t(L->d_ff) * act_size(L->act_dtype) : 0);
+  w.total = o;
+  return w;
+}
+
+// Workspace of the layer backward (see bmoe_layer_backward for the data flow).
+struct TrainBwdWs {
+  size_t G1, G2, A, xb, c1, c2, dgate, dxr, wt0, wt1, bb, sg, rb, total;
+};
+
+TrainBwdWs train_bwd_ws(const bmoe_layer* L, int32_t T) {
+  TrainBwdWs w{};
+  const int32_t R = T * L->top_k;
+  const size_t s = act_size(L->act_dtype);
+  const size_t d = size_t(L->d_model), f = size_t(L->d_ff), wide = f > d ? f : d;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  w.G1 = take(size_t(R) * wide * s);
+  w.G2 = take(size_t(R) * wide * s);
+  w.A = take(f ? size_t(R) * f * s : 0);
+  w.xb = take(size_t(R) * d * s);
+  const bool cast = L->act_dtype != BMOE_BF16;  // the substrate gradient takes bf16 rows
+  w.c1 = take(cast ? size_t(R) * wide * 2 : 0);
+  w.c2 = take(cast ? size_t(R) * wide * 2 : 0);
+  w.dgate = take(size_t(R) * 4);
+  w.dxr = take(size_t(T) * d * 4);
+  int32_t n0, k0, n1 = 0, k1 = 0;
+  sub_shape(L, 0, n0, k0);
+  if (f) sub_shape(L, 1, n1, k1);
+  w.wt0 = take(size_t(n0) * k0 / 4);
+  w.wt1 = take(f ? size_t(n1) * k1 / 4 : 0);
+  size_t bb = bfly_bwd_workspace(ilog2(L->d_model), L->n_experts, R);
+  if (f) {
+    const size_t bf = bfly_bwd_workspace(ilog2(L->d_ff), L->n_experts, R);
+    bb = bf > bb ? bf : bb;
+  }
+  w.bb = take(bb);
+  size_t sg = sgrad_workspace(n0, k0, R);
+  if (f) {
+    const size_t s1 = sgrad_workspace(n1, k1, R);
+    sg = s1 > sg ? s1 : sg;
+  }
+  w.sg = take(sg);
+  w.rb = take(router_bwd_workspace(T, L->d_model, L->n_experts));
+  w.total = o;
+  return w;
+}
+
+bmoe_status check_train_layer(const bmoe_layer* L, int32_t T) {
+  bmoe_status st = check_layer(L);
+  if (st != BMOE_OK) return st;
+  if (T < 0 || T > kMaxTokens) return fail(BMOE_ERR_SHAPE, "T=%d must be in [0, %d]", T, kMaxTokens);
+  if (L->d_model < 128 || (L->d_ff && L->d_ff < 128))
+    return fail(BMOE_ERR_SHAPE, "the training path needs d_model and d_ff of at least 128 (d_model=%d, d_ff=%d)",
+                L->d_model, L->d_ff);
+  if (L->d_model > 2048) return fail(BMOE_ERR_SHAPE, "the training path's router backward takes d_model <= 2048");
+  const int64_t R = int64_t(T) * L->top_k, wide = L->d_ff > L->d_model ? L->d_ff : L->d_model;
+  if (R * wide > (int64_t(1) << 31) - 1) return fail(BMOE_ERR_SHAPE, "T * top_k * max(d_model, d_ff) beyond 2^31");
+  return BMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bmoe_status bmoe_train_state_size(const bmoe_layer* layer, int32_t T, size_t* bytes) {
+  if (!bytes) return fail(BMOE_ERR_NULL, "bytes is NULL");
+  const bmoe_status st = check_train_layer(layer, T);
+  if (st != BMOE_OK) return st;
+  *bytes = train_layout(layer, T).total;
+  return ok();
+}
+
+bmoe_status bmoe_forward_train_workspace(const bmoe_layer* layer, int32_t T, size_t* bytes) {
+  if (!bytes) return fail(BMOE_ERR_NULL, "bytes is NULL");
+  const bmoe_status st = check_train_layer(layer, T);
+  if (st != BMOE_OK) return st;
+  *bytes = train_fwd_ws(layer, T).total;
+  return ok();
+}
+
+bmoe_status bmoe_layer_backward_workspace(const bmoe_layer* layer, int32_t T, size_t* bytes) {
+  if (!bytes) return fail(BMOE_ERR_NULL, "bytes is NULL");
+  const bmoe_status st = check_train_layer(layer, T);
+  if (st != BMOE_OK) return st;
+  *bytes = train_bwd_ws(layer, T).total;
+  return ok();
+}
+
+// Training forward: route and bucket as bmoe_forward; then, per routed row in
+// bucket order, U = B(theta_0)^T x_t (gathered), square: Z = alpha U W^T;
+// FFN: H1 = alpha U W_up^T, H = B(phi_up) H1, A = act(H) (workspace),
+// V = B(theta_dn)^T A, Z = alpha V W_dn^T; O = B(phi_last) Z; y_t = sum_j of
+// the gated rows in slot order.
+bmoe_status bmoe_forward_train(const bmoe_layer* layer, const void* x, int32_t T, void* y, void* state,
+                               size_t state_bytes, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bmoe_status st = check_train_layer(layer, T);
+  if (st != BMOE_OK) return st;
+  const TrainLayout tl = train_layout(layer, T);
+  const TrainFwdWs fw = train_fwd_ws(layer, T);
+  if (T == 0) return ok();
+  if (!x || !y || !state || !workspace) return fail(BMOE_ERR_NULL, "x / y / state / workspace is NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(state, 256) || !aligned(workspace, 256))
+    return fail(BMOE_ERR_ALIGN, "x and y must be 16-byte aligned, state and workspace 256-byte aligned");
+  if (state_bytes < tl.total) return fail(BMOE_ERR_WORKSPACE, "state has %zu bytes, %zu needed", state_bytes, tl.total);
+  if (workspace_bytes < fw.total)
+    return fail(BMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, fw.total);
+  const size_t s = act_size(layer->act_dtype);
+  const Range rx{x, size_t(T) * layer->d_model * s}, ry{y, size_t(T) * layer->d_model * s},
+      rs{state, tl.total}, rw{workspace, fw.total};
+  if (overlap(ry, rx) || overlap(ry, rs) || overlap(ry, rw)) return fail(BMOE_ERR_ALIAS, "y overlaps x, the state or the workspace");
+  if (overlap(rs, rx) || overlap(rs, rw) || overlap(rw, rx))
+    return fail(BMOE_ERR_ALIAS, "the state, the workspace and x must not overlap");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+
+  const int act = layer->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
+  const int32_t N = layer->n_experts, k = layer->top_k, d = layer->d_model, f = layer->d_ff;
+  const int32_t R = T * k;
+  int32_t* idx = at<int32_t>(state, tl.idx);
+  float* gate = at<float>(state, tl.gate);
+  int32_t* offsets = at<int32_t>(state, tl.offsets);
+  int32_t* perm = at<int32_t>(state, tl.perm);
+  int32_t* qpos = at<int32_t>(state, tl.qpos);
+  void* U = at<char>(state, tl.U);
+  void* Z = at<char>(state, tl.Z);
+  void* O = at<char>(state, tl.O);
+  RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates,
+               at<int32_t>(workspace, fw.tslots), at<float>(workspace, fw.tgates), at<int32_t>(workspace, fw.tstart)};
+  BMOE_HIP(launch_route(ra, act, stream));
+  BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, offsets, perm, nullptr, R, N,
+                route_tile_tokens(T) * k, fw.tiles, 0, 0};
+  BMOE_HIP(launch_bucket(ba, stream));
+  BMOE_HIP(launch_invert_perm(perm, qpos, R, stream));
+  BflyArgs bi{x, U, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+  BMOE_HIP(launch_butterfly(bi, BFLY_IN, act, ilog2(d), stream));
+  const void* zin = U;
+  if (f) {
+    void* H1 = at<char>(state, tl.H1);
+    void* H = at<char>(state, tl.H);
+    void* V = at<char>(state, tl.V);
+    void* A = at<char>(workspace, fw.A);
+    BMOE_HIP(launch_gemm(GemmArgs{U, layer->w_base[0], H1, layer->w_scale[0], R, f, d}, act, stream));
+    BflyArgs bu{H1, H, layer->phi[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+    BMOE_HIP(launch_bfly_rot(bu, act, ilog2(f), false, stream));
+    const void* a_in = H;  // no activation: the rotation reads H itself
+    if (layer->ffn_act == BMOE_ACT_GELU_ERF) {
+      BMOE_HIP(launch_gelu_fwd(H, A, size_t(R) * f, act, stream));
+      a_in = A;
+    }
+    BflyArgs bd{a_in, V, layer->theta[1], nullptr, offsets, perm, nullptr, R, N, k, 1, 0};
+    BMOE_HIP(launch_bfly_rot(bd, act, ilog2(f), true, stream));
+    zin = V;
+  }
+  const int m = f ? 1 : 0;
+  int32_t n_out, k_in;
+  sub_shape(layer, m, n_out, k_in);
+  BMOE_HIP(launch_gemm(GemmArgs{zin, layer->w_base[m], Z, layer->w_scale[m], R, n_out, k_in}, act, stream));
+  BflyArgs bo{Z, O, layer->phi[m], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};
+  BMOE_HIP(launch_bfly_rot(bo, act, ilog2(d), false, stream));
+  BMOE_HIP(launch_token_sum(O, qpos, gate, nullptr, y, false, T, d, k, act, stream));
+  return ok();
+}
+
+// Layer backward.  Rows in bucket order; G1 / G2 are row-gradient buffers of
+// the activation dtype.  With l the last substrate (0 square, 1 FFN):
+//   G1 = gate * dy_t (combine backward, with dgate = dy_t . O)
+//   G1 = dZ, dphi_l           (output rotation backward, in place)
+//   square: G2 = dU = alpha dZ W;  dW_0 = alpha sum dZ^T U
+//   FFN:    G2 = dV = alpha dZ W_dn;  dW_1 = alpha sum dZ^T V;  A = act(H)
+//           G2 = dA, dtheta_dn (rotation backward, in place);  G2 = dH = act'(H) dA
+//           G2 = dH1, dphi_up (in place);  G1 = dU = alpha dH1 W_up;  dW_0 = alpha sum dH1^T U
+//   xb = x_t gathered;  dU's buffer = dxb, dtheta_0 (in place)
+//   dx_r, dW_g = router backward (x, W_g, idx, dgate);  dx_t = dx_r + sum_j dxb (slot order)
+bmoe_status bmoe_layer_backward(const bmoe_layer* layer, const void* x, int32_t T, const void* dy,
+                                const void* state, size_t state_bytes, const bmoe_layer_grads* g, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  bmoe_status st = check_train_layer(layer, T);
+  if (st != BMOE_OK) return st;
+  if (!g) return fail(BMOE_ERR_NULL, "grads is NULL");
+  const bool ffn = layer->d_ff != 0;
+  const int nm = ffn ? 2 : 1;
+  if (!g->d_w_gate) return fail(BMOE_ERR_NULL, "grads->d_w_gate is NULL");
+  for (int m = 0; m < nm; ++m)
+    if (!g->d_theta[m] || !g->d_phi[m] || !g->d_w_base[m])
+      return fail(BMOE_ERR_NULL, "grads->d_theta / d_phi / d_w_base [%d] is NULL", m);
+  const TrainLayout tl = train_layout(layer, T);
+  const TrainBwdWs bw = train_bwd_ws(layer, T);
+  const int32_t N = layer->n_experts, k = layer->top_k, d = layer->d_model, f = layer->d_ff;
+  const size_t s = act_size(layer->act_dtype);
+  // outputs: ranges, alignment, no overlap with each other or the inputs
+  std::vector<Range> outs;
+  outs.push_back(Range{g->d_w_gate, size_t(N) * d * 4});
+  for (int m = 0; m < nm; ++m) {
+    int32_t n_out, k_in;
+    sub_shape(layer, m, n_out, k_in);
+    outs.push_back(Range{g->d_theta[m], size_t(N) * ilog2(k_in) * (k_in / 2) * 4});
+    outs.push_back(Range{g->d_phi[m], size_t(N) * ilog2(n_out) * (n_out / 2) * 4});
+    outs.push_back(Range{g->d_w_base[m], size_t(n_out) * k_in * 4});
+  }
+  if (T > 0) outs.push_back(Range{g->dx, size_t(T) * d * 4});
+  for (const Range& r : outs)
+    if (!aligned(r.p, 16)) return fail(BMOE_ERR_ALIGN, "gradient outputs must be 16-byte aligned");
+  if (T > 0) {
+    if (!x || !dy || !state || !workspace || !g->dx) return fail(BMOE_ERR_NULL, "x / dy / state / workspace / dx is NULL");
+    if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(state, 256) || !aligned(workspace, 256))
+      return fail(BMOE_ERR_ALIGN, "x and dy must be 16-byte aligned, state and workspace 256-byte aligned");
+    if (state_bytes < tl.total) return fail(BMOE_ERR_WORKSPACE, "state has %zu bytes, %zu needed", state_bytes, tl.total);
+    if (workspace_bytes < bw.total)
+      return fail(BMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, bw.total);
+    const Range ins[] = {Range{x, size_t(T) * d * s}, Range{dy, size_t(T) * d * s}, Range{state, tl.total},
+                         Range{workspace, bw.total}};
+    for (const Range& a : ins)
+      for (const Range& b : outs)
+        if (overlap(a, b)) return fail(BMOE_ERR_ALIAS, "a gradient output overlaps an input, the state or the workspace");
+    if (overlap(ins[3], ins[0]) || overlap(ins[3], ins[1]) || overlap(ins[3], ins[2]))
+      return fail(BMOE_ERR_ALIAS, "the workspace overlaps x, dy or the state");
+  }
+  for (size_t i = 0; i < outs.size(); ++i)
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j])) return fail(BMOE_ERR_ALIAS, "two gradient outputs overlap");
+  st = check_device();
+  if (st != BMOE_OK) return st;
+  const int act = layer->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
+  const int32_t R = T * k;
+  if (T == 0) {
+    // no rows: every parameter gradient is zero
+    for (const Range& r : outs) BMOE_HIP(launch_zero(const_cast<void*>(r.p), r.bytes, stream));
+    return ok();
+  }
+  const int32_t* idx = at<const int32_t>(const_cast<void*>(state), tl.idx);
+  const float* gate = at<const float>(const_cast<void*>(state), tl.gate);
+  const int32_t* offsets = at<const int32_t>(const_cast<void*>(state), tl.offsets);
+  const int32_t* perm = at<const int32_t>(const_cast<void*>(state), tl.perm);
+  const int32_t* qpos = at<const int32_t>(const_cast<void*>(state), tl.qpos);
+  auto srow = [&](size_t off) { return at<char>(const_cast<void*>(state), off); };
+  void* G1 = at<char>(workspace, bw.G1);
+  void* G2 = at<char>(workspace, bw.G2);
+  float* dgate = at<float>(workspace, bw.dgate);
+  float* bbws = at<float>(workspace, bw.bb);
+  float* sgws = at<float>(workspace, bw.sg);
+  // the substrate gradient takes bf16 rows: fp32 layers cast both operands first
+  auto substrate_grad = [&](const void* dz, const void* u, int32_t d_out, int32_t d_in, float alpha,
+                            float* out) -> hipError_t {
+    const void *a = dz, *b = u;
+    if (act != ACT_BF16) {
+      uint16_t* c1 = at<uint16_t>(workspace, bw.c1);
+      uint16_t* c2 = at<uint16_t>(workspace, bw.c2);
+      hipError_t e = launch_cast_bf16(static_cast<const float*>(dz), c1, size_t(R) * d_out, stream);
+      if (e != hipSuccess) return e;
+      e = launch_cast_bf16(static_cast<const float*>(u), c2, size_t(R) * d_in, stream);
+      if (e != hipSuccess) return e;
+      a = c1;
+      b = c2;
+    }
+    return launch_sgrad(a, b, alpha, out, sgws, R, d_out, d_in, stream);
+  };
+  const int m = ffn ? 1 : 0;
+  BMOE_HIP(launch_combine_bwd(dy, perm, gate, srow(tl.O), G1, dgate, R, k, d, act, stream));
+  BMOE_HIP(launch_bfly_bwd(srow(tl.Z), G1, G1, layer->phi[m], offsets, bbws, g->d_phi[m], R, N, ilog2(d), 0, act,
+                           stream));
+  void* dU;
+  if (!ffn) {
+    uint32_t* wt = at<uint32_t>(workspace, bw.wt0);
+    BMOE_HIP(launch_transpose_packed(layer->w_base[0], wt, d, d, stream));
+    BMOE_HIP(launch_gemm(GemmArgs{G1, wt, G2, layer->w_scale[0], R, d, d}, act, stream));
+    BMOE_HIP(substrate_grad(G1, srow(tl.U), d, d, layer->w_scale[0], g->d_w_base[0]));
+    dU = G2;
+  } else {
+    uint32_t* wt1 = at<uint32_t>(workspace, bw.wt1);
+    uint32_t* wt0 = at<uint32_t>(workspace, bw.wt0);
+    void* A = at<char>(workspace, bw.A);
+    BMOE_HIP(launch_transpose_packed(layer->w_base[1], wt1, d, f, stream));    // W_dn [d][f] -> [f][d]
+    BMOE_HIP(launch_gemm(GemmArgs{G1, wt1, G2, layer->w_scale[1], R, f, d}, act, stream));  // dV [R][f]
+    BMOE_HIP(substrate_grad(G1, srow(tl.V), d, f, layer->w_scale[1], g->d_w_base[1]));
+    const bool gelu = layer->ffn_act == BMOE_ACT_GELU_ERF;
+    const void* a_in = srow(tl.H);  // no activation: the rotation's input is H itself
+    if (gelu) {
+      BMOE_HIP(launch_gelu_fwd(srow(tl.H), A, size_t(R) * f, act, stream));
+      a_in = A;
+    }
+    BMOE_HIP(launch_bfly_bwd(a_in, G2, G2, layer->theta[1], offsets, bbws, g->d_theta[1], R, N, ilog2(f), 1, act,
+                             stream));
+    if (gelu) BMOE_HIP(launch_gelu_bwd(srow(tl.H), G2, G2, size_t(R) * f, act, stream));
+    BMOE_HIP(launch_bfly_bwd(srow(tl.H1), G2, G2, layer->phi[0], offsets, bbws, g->d_phi[0], R, N, ilog2(f), 0,
+                             act, stream));
+    BMOE_HIP(launch_transpose_packed(layer->w_base[0], wt0, f, d, stream));    // W_up [f][d] -> [d][f]
+    BMOE_HIP(launch_gemm(GemmArgs{G2, wt0, G1, layer->w_scale[0], R, d, f}, act, stream));  // dU [R][d]
+    BMOE_HIP(substrate_grad(G2, srow(tl.U), f, d, layer->w_scale[0], g->d_w_base[0]));
+    dU = G1;
+  }
+  void* xb = at<char>(workspace, bw.xb);
+  BMOE_HIP(launch_gather_rows(x, perm, xb, R, d, k, act, stream));
+  BMOE_HIP(launch_bfly_bwd(xb, dU, dU, layer->theta[0], offsets, bbws, g->d_theta[0], R, N, ilog2(d), 1, act,
+                           stream));
+  float* dxr = at<float>(workspace, bw.dxr);
+  BMOE_HIP(launch_router_bwd(x, layer->w_gate, idx, dgate, dxr, g->d_w_gate, at<char>(workspace, bw.rb), T, d, N, k,
+                             layer->renorm_gates, act, stream));
+  BMOE_HIP(launch_token_sum(dU, qpos, nullptr, dxr, g->dx, true, T, d, k, act, stream));
+  return ok();
+}
+
+}  // extern "C"

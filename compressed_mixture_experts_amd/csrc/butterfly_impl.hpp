@@ -397,7 +397,7 @@ __global__ __launch_bounds__(BF_THREADS) void bfly_kernel(BflyArgs a) {
   __syncthreads();
 
   // ---- rotations
-  if constexpr (MODE == BFLY_DBG) {
+  if constexpr (MODE == BFLY_DBG || MODE == BFLY_ROT) {
     run_passes<L, DBG_TRANS, false>(tile, nr, tab, ang0, R);
   } else if constexpr (MODE == BFLY_IN) {
     run_passes<L, true, false>(tile, nr, tab, ang0, R);
@@ -449,15 +449,8 @@ hipError_t launch_bfly_L(const BflyArgs& a, hipStream_t s) {
   if (MODE != BFLY_DBG) grid += a.n_experts;
   if (grid == 0) return hipSuccess;
   auto k = bfly_kernel<MODE, ACT, TR, L>;
-  static int attr_done[64] = {0};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  const hipError_t err = allow_dynamic_lds((const void*)k, C::lds_bytes);
   if (err != hipSuccess) return err;
-  if (C::lds_bytes > 64 * 1024 && (dev < 0 || dev >= 64 || !attr_done[dev])) {
-    err = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, int(C::lds_bytes));
-    if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64) attr_done[dev] = 1;
-  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(BF_THREADS), C::lds_bytes, s, a);
   return hipGetLastError();
 }
@@ -481,6 +474,7 @@ hipError_t launch_bfly_width(const BflyArgs& a, int log2n, hipStream_t s) {
 
 hipError_t launch_bfly_dbg(const BflyArgs& a, int act, int log2n, hipStream_t s);
 hipError_t launch_bfly_in(const BflyArgs& a, int act, int log2n, hipStream_t s);
+hipError_t launch_bfly_rot(const BflyArgs& a, int act, int log2n, bool transpose, hipStream_t s);
 hipError_t launch_bfly_mid(const BflyArgs& a, int act, int log2n, hipStream_t s);
 hipError_t launch_bfly_out(const BflyArgs& a, int act, int log2n, hipStream_t s);
 

@@ -179,7 +179,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
-enum BflyMode { BFLY_DBG = 0, BFLY_IN = 1, BFLY_MID = 2, BFLY_OUT = 3 };
+// DBG: one angle set for all rows; IN: gather token rows into bucket order, B^T;
+// MID: FFN middle; OUT: bucket rows to gated slot rows, B; ROT: bucket rows to
+// bucket rows, B or B^T (the training path)
+enum BflyMode { BFLY_DBG = 0, BFLY_IN = 1, BFLY_MID = 2, BFLY_OUT = 3, BFLY_ROT = 4 };
 
 struct BflyArgs {
   const void* in;           // source rows
@@ -237,6 +240,19 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 // one angle set for all rows (the test hook of bmoe_debug.h)
 hipError_t launch_bfly_dbg(const BflyArgs& a, int act, int log2n, hipStream_t s);
+// bucket rows to bucket rows, each expert's B (or B^T when transpose), fp32 stages
+hipError_t launch_bfly_rot(const BflyArgs& a, int act, int log2n, bool transpose, hipStream_t s);
+
+// Training-path helpers (train.hip).
+hipError_t launch_invert_perm(const int32_t* perm, int32_t* qpos, int R, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, void* out, int R, int d, int k, int act,
+                              hipStream_t s);
+hipError_t launch_token_sum(const void* rows, const int32_t* qpos, const float* gate, const float* base, void* out,
+                            bool out_f32, int T, int d, int k, int act, hipStream_t s);
+hipError_t launch_transpose_packed(const uint32_t* w, uint32_t* wt, int rows, int cols, hipStream_t s);
+hipError_t launch_gelu_fwd(const void* h, void* a, size_t n, int act, hipStream_t s);
+hipError_t launch_cast_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);  // bytes a multiple of 4
 
 // A kernel launched with more than the default 64 KiB of dynamic LDS needs its
 // limit raised first.  Done before every such launch (host work of the order

@@ -450,7 +450,9 @@ def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
     straight-through estimator, du = alpha W_base^T dz) and the input rotation
     (dtheta_e, dx_t += its input gradient).  Also returns the gates'
     gradients dgate[t][j] = dy_t . o.
-    Returns dict(theta, phi [N][L][n/2], w_base [d][d], x [T][d], gate [T][k]).
+    Returns dict(theta, phi [N][L][n/2], w_base [d][d], x [T][d], gate [T][k],
+    w_base_abs): w_base_abs = alpha sum_r |dZ_r|^T |U_r|, the same sum as dW
+    over magnitudes, a scale for the error of dW computed from rounded rows.
 
     FFN layers (two substrates, a GELU or the identity between) go through
     ``_ffn_backward``: the same chain twice with the activation's derivative
@@ -465,6 +467,7 @@ def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
     dth = np.zeros(np.shape(th_all))
     dph = np.zeros(np.shape(ph_all))
     dW = np.zeros(W.shape)
+    dWa = np.zeros(W.shape)
     dx = np.zeros(x.shape)
     dgate = np.zeros(routing.gates.shape)
     for e in np.unique(routing.idx):
@@ -479,10 +482,11 @@ def layer_backward_experts(inp, dy: np.ndarray, routing: "Routing"):
         dgate[tok, slot] = np.sum(dy[tok].T * O, axis=0)
         dZ, dph[e] = butterfly_backward(ph, Z, dO, False)
         dW += substrate_weight_grad(U.T, dZ.T, alpha)
+        dWa += substrate_weight_grad(np.abs(U.T), np.abs(dZ.T), abs(alpha))
         dU = alpha * (W.T @ dZ)
         dX, dth[e] = butterfly_backward(th, X, dU, True)
         np.add.at(dx, tok, dX.T)
-    return {"theta": dth, "phi": dph, "w_base": dW, "x": dx, "gate": dgate}
+    return {"theta": dth, "phi": dph, "w_base": dW, "x": dx, "gate": dgate, "w_base_abs": dWa}
 
 
 def _ffn_backward(inp, cfg, x, dy, routing):
@@ -497,6 +501,7 @@ def _ffn_backward(inp, cfg, x, dy, routing):
     out = {"theta": [np.zeros(np.shape(inp.theta[0])), np.zeros(np.shape(inp.theta[1]))],
            "phi": [np.zeros(np.shape(inp.phi[0])), np.zeros(np.shape(inp.phi[1]))],
            "w_base": [np.zeros(Wu.shape), np.zeros(Wd.shape)],
+           "w_base_abs": [np.zeros(Wu.shape), np.zeros(Wd.shape)],
            "x": np.zeros(x.shape), "gate": np.zeros(routing.gates.shape)}
     use_gelu = cfg.ffn_act == "gelu"
     for e in np.unique(routing.idx):
@@ -515,10 +520,12 @@ def _ffn_backward(inp, cfg, x, dy, routing):
         out["gate"][tok, slot] = np.sum(dy[tok].T * O, axis=0)
         dZ, dphd = butterfly_backward(phd, Z, dO, False)
         out["w_base"][1] += substrate_weight_grad(V.T, dZ.T, alpha)
+        out["w_base_abs"][1] += substrate_weight_grad(np.abs(V.T), np.abs(dZ.T), abs(alpha))
         dA, dthd = butterfly_backward(thd, A, alpha * (Wd.T @ dZ), True)
         dH = gelu_backward(H, dA) if use_gelu else dA
         dH1, dphu = butterfly_backward(phu, H1, dH, False)
         out["w_base"][0] += substrate_weight_grad(U.T, dH1.T, alpha)
+        out["w_base_abs"][0] += substrate_weight_grad(np.abs(U.T), np.abs(dH1.T), abs(alpha))
         dX, dthu = butterfly_backward(thu, X, alpha * (Wu.T @ dH1), True)
         np.add.at(out["x"], tok, dX.T)
         out["theta"][0][e], out["phi"][0][e], out["theta"][1][e], out["phi"][1][e] = dthu, dphu, dthd, dphd

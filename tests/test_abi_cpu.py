@@ -531,3 +531,46 @@ def test_forward_noalloc_argument_errors():
     assert L.bmoe_forward_noalloc(None, FAKE, 16, FAKE, None, None, None) == 1
     assert L.bmoe_forward_noalloc(ctypes.byref(s), None, 0, None, None, None, None) == 0
     assert L.bmoe_forward_noalloc(ctypes.byref(s), FAKE, -1, FAKE, None, None, None) == 2
+
+
+def test_training_path_argument_errors():
+    # include/bmoe_train.h: every error found on the host before a device call
+    L = bm.lib()
+    n = ctypes.c_size_t(0)
+    s = make_struct(d_model=256)
+    assert L.bmoe_train_state_size(ctypes.byref(s), 100, ctypes.byref(n)) == 0 and n.value > 0
+    state_need = n.value
+    assert L.bmoe_train_state_size(ctypes.byref(make_struct(d_model=64)), 100, ctypes.byref(n)) == 2
+    assert L.bmoe_train_state_size(ctypes.byref(s), -1, ctypes.byref(n)) == 2
+    assert L.bmoe_train_state_size(ctypes.byref(s), 100, None) == 1
+    assert L.bmoe_forward_train_workspace(ctypes.byref(s), 100, ctypes.byref(n)) == 0
+    fw_need = n.value
+    assert L.bmoe_layer_backward_workspace(ctypes.byref(s), 100, ctypes.byref(n)) == 0
+    bw_need = n.value
+    f = L.bmoe_forward_train
+    big = 1 << 34
+    assert f(ctypes.byref(s), None, 100, FAKE, FAKE + big, state_need, FAKE + 2 * big, fw_need, None) == 1
+    assert f(ctypes.byref(s), FAKE + 8, 100, FAKE + big // 2, FAKE + big, state_need, FAKE + 2 * big, fw_need, None) == 4
+    assert f(ctypes.byref(s), FAKE, 100, FAKE + big // 2, FAKE + big, state_need - 1, FAKE + 2 * big, fw_need,
+             None) == 6
+    assert f(ctypes.byref(s), FAKE, 100, FAKE, FAKE + big, state_need, FAKE + 2 * big, fw_need, None) == 5
+    assert f(ctypes.byref(s), FAKE, 0, None, None, 0, None, 0, None) == 0
+    g = bm.LayerGrads()
+    g.dx, g.d_w_gate = FAKE + 3 * big, FAKE + 3 * big + (1 << 24)
+    g.d_theta[0], g.d_phi[0], g.d_w_base[0] = (FAKE + 3 * big + (2 << 24), FAKE + 3 * big + (3 << 24),
+                                               FAKE + 3 * big + (4 << 24))
+    b = L.bmoe_layer_backward
+    assert b(ctypes.byref(s), FAKE, 100, FAKE + big // 2, FAKE + big, state_need, None, FAKE + 2 * big, bw_need,
+             None) == 1
+    assert b(ctypes.byref(s), FAKE, 100, FAKE + big // 2, FAKE + big, state_need, ctypes.byref(g), FAKE + 2 * big,
+             bw_need - 1, None) == 6
+    g.d_phi[0] = g.d_theta[0]  # two outputs on one buffer
+    assert b(ctypes.byref(s), FAKE, 100, FAKE + big // 2, FAKE + big, state_need, ctypes.byref(g), FAKE + 2 * big,
+             bw_need, None) == 5
+    g.d_phi[0] = FAKE + 3 * big + (3 << 24) + 4
+    assert b(ctypes.byref(s), FAKE, 100, FAKE + big // 2, FAKE + big, state_need, ctypes.byref(g), FAKE + 2 * big,
+             bw_need, None) == 4
+    ffn = make_struct(d_model=256, d_ff=512, ffn_act=bm.ACT_GELU_ERF)
+    g.d_phi[0] = FAKE + 3 * big + (3 << 24)
+    assert b(ctypes.byref(ffn), FAKE, 100, FAKE + big // 2, FAKE + big, 1 << 30, ctypes.byref(g), FAKE + 2 * big,
+             1 << 30, None) == 1  # the down substrate's gradient pointers are missing

@@ -9,9 +9,10 @@ routed row, gate gradients); bmoe_butterfly_backward through the output
 rotation (dphi, dZ); the substrate product with W^T packed (dU);
 bmoe_butterfly_backward through the input rotation (dtheta, per-row dx);
 bmoe_substrate_grad (dW, bf16 copies of U and dZ).  Per-row input gradients
-are added into tokens by the test itself.  Bars: fp32 rows; angle gradients
-and dx within 1e-4 relative, gate gradients within 1e-4 of |dy||o|, dW within
-1e-2 relative (its inputs rounded to bf16: half a bf16 step per element).
+are added into tokens by the test itself.  Bars, elementwise: fp32 rows;
+angle gradients and dx within 3e-5 of (|ref| + the expert's or token's RMS),
+gate gradients within 1e-4 of |dy||o|, dW within 2^-7 alpha sum |dZ|^T |U|
+(its inputs rounded to bf16: one rounding each).
 """
 import math
 
@@ -112,19 +113,19 @@ def test_layer_backward_composed_from_the_abi():
 
     want = ref.layer_backward_experts(inp, dy64.astype(np.float32).astype(np.float64), R)
     got_th, got_ph = dth.cpu().numpy(), dph.cpu().numpy()
-    for e in range(N):
-        for got, ref_, what in ((got_th[e], want["theta"][e], "theta"), (got_ph[e], want["phi"][e], "phi")):
-            nr = np.linalg.norm(ref_)
-            if nr == 0:
-                assert not got.any(), f"expert {e} d{what} should be zero"
-            else:
-                assert np.linalg.norm(got - ref_) <= 1e-4 * nr, f"expert {e} d{what}"
-    assert row_rel_err(dx.cpu().numpy().astype(np.float64), want["x"]).max() <= 1e-4
+    # elementwise: within 3e-5 of |ref| + the expert's RMS (fp32 chain rule)
+    for got, ref_, what in ((got_th, want["theta"], "theta"), (got_ph, want["phi"], "phi")):
+        rms = np.sqrt(np.mean(ref_ ** 2, axis=(1, 2), keepdims=True))
+        assert np.all(np.abs(got - ref_) <= 3e-5 * (np.abs(ref_) + rms)), f"d{what}"
+    dxw = want["x"]
+    dxg = dx.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(dxg - dxw) <= 3e-5 * (np.abs(dxw) + np.sqrt(np.mean(dxw ** 2, axis=1, keepdims=True))))
     dgate = d_gate.cpu().numpy().reshape(cfg.tokens, k)
     ob = np.linalg.norm(dy64, axis=1)[:, None] * np.abs(want["gate"]).max()
     assert np.all(np.abs(dgate - want["gate"]) <= 1e-4 * (1 + ob))
+    # dW from bf16 copies of dZ and U: one rounding each, 2^-8 relative per product term
     dWr = want["w_base"]
-    assert np.linalg.norm(dW.cpu().numpy() - dWr) <= 1e-2 * np.linalg.norm(dWr)
+    assert np.all(np.abs(dW.cpu().numpy() - dWr) <= 2.0 ** -7 * want["w_base_abs"] + 1e-6 * np.abs(dWr).max())
     # the router's part, fed with the GPU's gate gradients: the whole layer's
     # input gradient and the gate matrix's gradient
     wgd = dev(inp.w_gate)
@@ -165,8 +166,9 @@ def test_router_backward_matches_oracle(T, d, N, k, renorm, act):
     got_dx, got_dw = dx.cpu().numpy().astype(np.float64), dwg.cpu().numpy().astype(np.float64)
     scale_x = np.linalg.norm(rdx, axis=1).max()
     assert np.abs(got_dx - rdx).max() <= 1e-4 * scale_x
-    assert np.linalg.norm(got_dw - rdw) <= 1e-4 * np.linalg.norm(rdw)
-    assert np.abs(got_dw - rdw).max() <= 1e-4 * np.abs(rdw).max()
+    # elementwise, against |ref| + the expert row's RMS
+    rms = np.sqrt(np.mean(rdw ** 2, axis=1, keepdims=True))
+    assert np.all(np.abs(got_dw - rdw) <= 1e-4 * (np.abs(rdw) + rms))
 
 
 def test_router_backward_zero_tokens():
@@ -264,17 +266,18 @@ def test_ffn_layer_backward_composed_from_the_abi():
     torch.cuda.synchronize()
 
     want = ref.layer_backward_experts(inp, dy64.astype(np.float32).astype(np.float64), R)
+    # elementwise: within 3e-5 of |ref| + the expert's (token's) RMS
     for got, ref_, what in ((dthu, want["theta"][0], "theta_up"), (dphu, want["phi"][0], "phi_up"),
                             (dthd, want["theta"][1], "theta_dn"), (dphd, want["phi"][1], "phi_dn")):
         g_ = got.cpu().numpy()
-        for e in range(N):
-            nr = np.linalg.norm(ref_[e])
-            if nr == 0:
-                assert not g_[e].any(), f"expert {e} d{what} should be zero"
-            else:
-                assert np.linalg.norm(g_[e] - ref_[e]) <= 1e-4 * nr, f"expert {e} d{what}"
-    assert row_rel_err(dx.cpu().numpy().astype(np.float64), want["x"]).max() <= 1e-4
+        rms = np.sqrt(np.mean(ref_ ** 2, axis=(1, 2), keepdims=True))
+        assert np.all(np.abs(g_ - ref_) <= 3e-5 * (np.abs(ref_) + rms)), f"d{what}"
+    dxg = dx.cpu().numpy().astype(np.float64)
+    dxw = want["x"]
+    assert np.all(np.abs(dxg - dxw) <= 3e-5 * (np.abs(dxw) + np.sqrt(np.mean(dxw ** 2, axis=1, keepdims=True))))
     dg = d_gate.cpu().numpy().reshape(cfg.tokens, k)
     assert np.abs(dg - want["gate"]).max() <= 1e-4 * np.abs(want["gate"]).max()
-    for got, ref_ in ((dWu, want["w_base"][0]), (dWd, want["w_base"][1])):
-        assert np.linalg.norm(got.cpu().numpy() - ref_) <= 1e-2 * np.linalg.norm(ref_)
+    # substrate gradients from bf16 copies of both operands: one rounding each
+    for got, ref_, mag in ((dWu, want["w_base"][0], want["w_base_abs"][0]),
+                           (dWd, want["w_base"][1], want["w_base_abs"][1])):
+        assert np.all(np.abs(got.cpu().numpy() - ref_) <= 2.0 ** -7 * mag + 1e-6 * np.abs(ref_).max())

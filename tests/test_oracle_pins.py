@@ -547,3 +547,26 @@ def test_ffn_layer_backward_finite_differences(act):
     assert abs(fd(inp.x, (1, 3), 2.0 ** -12) - want) < 1e-5 * (1 + abs(want))
     want = g["gate"][2, 1]
     assert abs(fd(R.gates, (2, 1), 1e-3) - want) < 1e-8 * (1 + abs(want))
+
+
+@pytest.mark.parametrize("ffn", [False, True])
+def test_layer_backward_magnitude_sums_bound_the_substrate_gradient(ffn):
+    # w_base_abs = alpha sum |dZ|^T |U| bounds |dW| entrywise (triangle
+    # inequality), with equality where every term has one sign
+    cfg = wl.small_config(d_model=16, d_ff=32 if ffn else 0, n_experts=3, top_k=2, tokens=9,
+                          act="f32", w_scale=0.75, seed_index=61)
+    inp = wl.generate(cfg)
+    x = ref.stored_to_f64(inp.x, "f32")
+    R = ref.route(x, ref.stored_to_f64(inp.w_gate, "f32"), cfg.top_k)
+    dy = np.random.default_rng(3).standard_normal((cfg.tokens, cfg.d_model))
+    out = ref.layer_backward_experts(inp, dy, R)
+    dws = out["w_base"] if ffn else [out["w_base"]]
+    mags = out["w_base_abs"] if ffn else [out["w_base_abs"]]
+    for dw, mag in zip(dws, mags):
+        assert np.all(np.abs(dw) <= mag * (1 + 1e-12) + 1e-300)
+        assert np.all(mag >= 0) and mag.max() > 0
+    # one token, one expert, all-positive factors: |U| = U and |dZ| = dZ up to sign
+    # per entry, so the bound is attained where both have one sign
+    out1 = ref.layer_backward_experts(inp, np.abs(dy), R)
+    assert np.all(np.abs((out1["w_base"][0] if ffn else out1["w_base"])) <=
+                  (out1["w_base_abs"][0] if ffn else out1["w_base_abs"]) * (1 + 1e-12))
