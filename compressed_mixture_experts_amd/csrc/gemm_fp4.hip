@@ -13,7 +13,12 @@
 // 128 K, bf16) goes through two LDS buffers and is read by all four waves.
 // In a K step, lanes 16g .. 16g+15 supply contraction indices 32g .. 32g+31 of
 // the step (8 per MFMA); the activation operand follows the same order.  The
-// loads of step k+1 are issued before the products of step k.
+// loads of step k+1 are issued before the products of step k, and within a
+// step the LDS reads of each sub-step's operand fragments are interleaved with
+// the first products of the sub-step before it (scheduling barriers and an
+// explicit LDS wait at each sub-step boundary fix that order; left to itself
+// the compiler issued each sub-step's reads just before their first use and
+// waited for them there).
 // TN = 256: 64 columns per wave, 128 accumulators per lane, two workgroups
 // per CU (LDS 64 KiB each), so one workgroup's products cover the other's
 // load waits.
@@ -44,10 +49,15 @@ __device__ __forceinline__ uint4 gf_fp4x8_to_bf16(uint32_t w) {
 }
 
 // Activation tile in LDS: 128 rows of 128 bf16 (256 bytes, no padding); the
-// 16-byte chunk ch of row r sits at position ch ^ (r & 15) of the row, so the
-// 16 rows one MFMA operand read touches hit 16 different bank groups.  The
-// tile is filled by direct global->LDS loads: one 16-byte load per lane, each
-// wave-wide load filling 4 consecutive rows.
+// 16-byte chunk ch of row r sits at position ch ^ gf_swz(r & 15) of the row,
+// gf_swz swapping the two 2-bit halves of its argument.  With that map a
+// wave's 16-byte operand read (lane l: row 16 j + l % 16, chunk 4 (l / 16) + s)
+// has no LDS bank conflicts on gfx950 (measured: 0 conflict cycles per read;
+// the plain map ch ^ (r & 15) took 4), as the linear read of a 1 KiB block
+// does.  The tile is filled by direct global->LDS loads: one 16-byte load per
+// lane, each wave-wide load filling 4 consecutive rows.
+__device__ __forceinline__ int gf_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 template <int TN>
 __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) {
   constexpr int WN = TN / 4;                  // output columns per wave
@@ -69,10 +79,10 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
   // this lane's substrate rows n0 + 16 i + l16, bytes 8 g .. 8 g + 7 of each 32-byte step
   const unsigned char* wrow = a.w + size_t(n0 + l16) * (K / 4) + 8 * g;
   // this lane's source of direct load j: row 4 (DPW wave + j) + lane / 16 (clamped to
-  // M - 1: rows past M are never stored), chunk (lane % 16) ^ (row % 16)
+  // M - 1: rows past M are never stored), chunk (lane % 16) ^ gf_swz(row % 16)
   auto usrc = [&](int j) {
     const int row = 4 * (DPW * wave + j) + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
+    const int ch = (lane & 15) ^ gf_swz(row & 15);
     return U + size_t(min(m0 + row, a.M - 1)) * K + 8 * ch;
   };
 
@@ -95,33 +105,30 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // operand reads: row 16 jb + l16, chunk 4 g + s at position (4 g + s) ^ l16
+  // operand reads: row 16 jb + l16, chunk 4 g + s at position (4 g + s) ^ gf_swz(l16)
   auto load_uf = [&](const uint16_t* ub, int s, bf16x8_t (&uf)[MB]) {
-    const int p = (4 * g + s) ^ l16;
+    const int p = (4 * g + s) ^ gf_swz(l16);
 #pragma unroll
     for (int j = 0; j < MB; ++j)
       uf[j] = *reinterpret_cast<const bf16x8_t*>(ub + (16 * j + l16) * GF_KS + 8 * p);
   };
-  // products of one sub-step with the lower (upper) eight weights of word 0
-  // of each substrate fragment; after the upper half the words swap, so that
-  // the next two sub-steps use word 0 again (the sub-step loop stays rolled,
-  // which bounds the live operand registers)
-  auto substep = [&](const bf16x8_t (&uf)[MB], uint2 (&Wc)[OB], bool upper) {
+  // products of sub-step q (0 .. 3): weights 8 (q & 1) .. 8 (q & 1) + 7 of word
+  // q >> 1 of each substrate fragment
+  auto substep = [&](const bf16x8_t (&uf)[MB], const uint2 (&Wc)[OB], int q) {
 #pragma unroll
     for (int i = 0; i < OB; ++i) {
-      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, gf_fp4x8_to_bf16(pair2_to_fp4(Wc[i].x, upper)));
-      if (upper) Wc[i] = make_uint2(Wc[i].y, Wc[i].x);
+      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, gf_fp4x8_to_bf16(pair2_to_fp4((q >> 1) ? Wc[i].y : Wc[i].x, q & 1)));
 #pragma unroll
       for (int j = 0; j < MB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, uf[j], acc[i][j], 0, 0, 0);
     }
   };
   // step kt: start the loads of step kt + 1 (activation tile into the other LDS
-  // buffer, substrate fragments into Wn), multiply buffer kt & 1 with Wc, then
-  // wait for the loads and for every wave.  The operand fragments of sub-step
-  // s + 1 are read while sub-step s multiplies (the read past sub-step 3 is of
-  // chunk 4 g + 4 ^ l16 < 16 of the same rows, unused).
-  auto step = [&](int kt, uint2 (&Wc)[OB], uint2 (&Wn)[OB]) {
+  // buffer, substrate fragments into Wn), then four sub-steps, the operand
+  // fragments of sub-step q + 1 read from LDS before the products of sub-step q
+  // (scheduling barriers keep that order), then wait for the loads and for
+  // every wave.
+  auto step = [&](int kt, const uint2 (&Wc)[OB], uint2 (&Wn)[OB]) {
     const int buf = kt & 1;
     if (kt + 1 < nk) {
       load_u(kt + 1, buf ^ 1);
@@ -129,14 +136,36 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
     }
     const uint16_t* ub = smem + buf * GF_TILE;
     bf16x8_t ua[MB], ubf[MB];
+    // each region: the LDS reads of sub-step q + 1 issued one per product at
+    // the start of the products of sub-step q
+    auto early_reads = [&]() {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, OB * MB - MB, 0);
+    };
     load_uf(ub, 0, ua);
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-      load_uf(ub, 2 * h + 1, ubf);
-      substep(ua, Wc, false);
-      load_uf(ub, (2 * h + 2) & 3, ua);
-      substep(ubf, Wc, true);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this sub-step's fragments are in
+    load_uf(ub, 1, ubf);
+    substep(ua, Wc, 0);
+    early_reads();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    load_uf(ub, 2, ua);
+    substep(ubf, Wc, 1);
+    early_reads();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    load_uf(ub, 3, ubf);
+    substep(ua, Wc, 2);
+    early_reads();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    substep(ubf, Wc, 3);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // waits for this wave's loads, then for every wave
   };
 
