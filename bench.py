@@ -458,6 +458,7 @@ def main() -> int:
             out["by_config"][r["config"]["workload"]] = {
                 "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
                 "warm_ms_per_step": r["timing"]["warm_ms_per_step"], "roofline": r["roofline"],
+                "weight_prep": r["weight_prep"], "per_call_prep": r.get("per_call_prep"),
                 "kernels": r["kernels"]}
     print(json.dumps(out))
     return 0
@@ -659,10 +660,43 @@ def measure_workload(cfg, args, K, W, cpu=True):
         "cpu_baseline": cpu_res,
         "kernels": kernels,
     }
+    if prep_ms is not None:
+        # the compact form: no prepared buffer kept between calls, every forward
+        # rebuilds the re-encoded substrate and the block factors from the
+        # packed codes and the angles inside its own launches
+        res["per_call_prep"] = compact_steps(layer, x, y, flush, min(K, 10))
     del graphs, flush, layer, x, y, y_eager
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def compact_steps(layer, x, y, flush, K):
+    """ms per step of the layer without its prepared buffer (graph replay of
+    one forward, eviction write before each step outside the events)."""
+    import torch
+    layer.unprepare()
+    for _ in range(2):
+        layer.forward(x, y)
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        layer.forward(x, y)
+    torch.cuda.synchronize()
+    s0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    s1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        flush.fill_((i + 7) & 0xFF)
+        s0[i].record()
+        g.replay()
+        s1[i].record()
+    torch.cuda.synchronize()
+    ms = sum(s0[i].elapsed_time(s1[i]) for i in range(K)) / K
+    ang = sum(int(t.numel()) * 4 for t in list(layer.theta) + list(layer.phi))
+    del g
+    return {"ms_per_step": round(ms, 5), "steps": K, "resident_bytes_beyond_weights": 0,
+            "angle_bytes": ang, "note": "no prepared buffer: substrate code and block factors rebuilt in every forward"}
 
 
 def bm_kernel_sha(kernel: str, cfg) -> str:
