@@ -13,7 +13,7 @@
 // Both parts are products with block-diagonal factors on the matrix cores,
 // built from the angles once per weight set (bf16, MFMA operand order) by the
 // builder kernels below.  Each workgroup owns up to SP_RB rows of ONE expert
-// and a range of chunks (low) or 64 columns (high), so its factor fragments are
+// and a range of chunks (low) or 64 / 128 columns (high), so its factor fragments are
 // loaded once and reused for all its rows; a width that has more angles than a
 // row has elements would otherwise move more parameter bytes than activation
 // bytes per row.  Rows are read and written as bf16, products accumulate in
@@ -24,14 +24,13 @@
 namespace bmoe {
 
 constexpr int SP_RB = 64;  // rows per workgroup
-constexpr int SP_VC = 64;  // high part: columns per workgroup
 
 // Workgroup tile t -> (expert e, first bucket row r0, rows nr) with tiles of
 // SP_RB rows per expert in expert order; e = -1 past the last tile.
 __device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_experts, int t, int& e, int& r0,
                                              int& nr) {
   __shared__ int s_info[3];
-  __shared__ int s_tmp[4];
+  __shared__ int s_tmp[16];  // one entry per wave (up to 1024 threads); only experts < 256 count
   const int tid = threadIdx.x;
   if (tid == 0) s_info[0] = -1;
   int nt = 0, cnt = 0, off = 0;
@@ -364,7 +363,14 @@ struct HighMCfg {
   static constexpr int NV = 1 << S;                       // columns
   static constexpr size_t per_expert = size_t(NV) * 512;  // one 16 x 16 bf16 block per column
   static constexpr int RT = 16;                           // rows per sub-tile
-  static constexpr int RSB = 16 * SP_VC * 2 + 8;          // LDS bytes per row: [16 j][64 v] bf16 + pad
+  // columns per workgroup (16 per wave): 128 at width 8192, whose 16 indices
+  // of a column lie 1 KiB apart, so that a workgroup reads 256-byte runs
+  // (566 -> 533 us for the FFN middle's pass over 65536 rows of 8192); 64
+  // below (128 columns at width 4096 gave half the workgroups and took 90
+  // instead of 76 us over 16384 rows)
+  static constexpr int VC = S == 9 ? 128 : 64;
+  static constexpr int NTH = 4 * VC;                      // threads
+  static constexpr int RSB = 16 * VC * 2 + 8;             // LDS bytes per row: [16 j][VC v] bf16 + pad
   static constexpr size_t lds_bytes = size_t(RT) * RSB;
 };
 
@@ -396,16 +402,19 @@ __global__ __launch_bounds__(BF_THREADS) void hfac_kernel(const float* __restric
         make_uint2(pack_bf16x2(x[g], x[g + 4]), pack_bf16x2(x[g + 8], x[g + 12]));
 }
 
-// High part on the matrix cores.  WG = (tile of <= 64 rows of one expert, 64
-// columns); sub-tiles of 16 rows go through LDS as [row][16 j][64 v] bf16
-// (coalesced 16-byte loads and stores); wave w multiplies columns 16w .. 16w+15
-// in groups of 4, reading each j's 4 columns with one 8-byte LDS read.
+// High part on the matrix cores.  WG = (tile of <= 64 rows of one expert, VC
+// columns, VC / 16 waves); sub-tiles of 16 rows go through LDS as
+// [row][16 j][VC v] bf16 (coalesced 16-byte loads and stores); wave w
+// multiplies columns 16w .. 16w+15 in groups of 4, reading each j's 4 columns
+// with one 8-byte LDS read.
 template <int S, int MODE>
-__global__ __launch_bounds__(BF_THREADS, 4) void highm_kernel(BflyArgs a) {
+__global__ __launch_bounds__(HighMCfg<S>::NTH, 1024 / HighMCfg<S>::NTH) void highm_kernel(BflyArgs a) {
   using C = HighMCfg<S>;
   constexpr int L = S + 4, n = 1 << L;
-  constexpr int ncb = C::NV / SP_VC;
-  constexpr int PPT = C::RT * 16 * (SP_VC / 8) / BF_THREADS;  // 16-byte pieces per thread (8)
+  constexpr int VC = C::VC, NTH = C::NTH;
+  constexpr int VPC = VC / 8, PR = 16 * VPC;  // 16-byte pieces per (row, j) and per row
+  constexpr int ncb = C::NV / VC;
+  constexpr int PPT = C::RT * PR / NTH;  // 16-byte pieces per thread (8)
   extern __shared__ __attribute__((aligned(16))) unsigned char hl[];
   __shared__ size_t s_row[SP_RB];
   __shared__ float s_g[SP_RB];
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(BF_THREADS, 4) void highm_kernel(BflyArgs a) {
   sp_find_tile(a.offsets, a.n_experts, t, e, r0, nr);
   if (e < 0) return;
 
-  const int vw = cb * SP_VC + 16 * wave;  // this wave's first column
+  const int vw = cb * VC + 16 * wave;  // this wave's first column
   uint2 fa0[16], fa1[MODE == SH_MID ? 16 : 1];
   const unsigned char* f0 = a.fac + size_t(e) * C::per_expert;
 #pragma unroll
@@ -446,9 +455,9 @@ __global__ __launch_bounds__(BF_THREADS, 4) void highm_kernel(BflyArgs a) {
   auto load = [&](int rs, uint4 (&v)[PPT]) {
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-      const int p = k * BF_THREADS + tid, row = min(rs + p / 128, nr - 1), j = (p / 8) % 16, vc = p % 8;
+      const int p = k * NTH + tid, row = min(rs + p / PR, nr - 1), j = (p / VPC) % 16, vc = p % VPC;
       const size_t src = MODE == SH_OUT ? size_t(r0 + row) * n : s_row[row];
-      v[k] = *reinterpret_cast<const uint4*>(in + src + (size_t(j) << S) + cb * SP_VC + 8 * vc);
+      v[k] = *reinterpret_cast<const uint4*>(in + src + (size_t(j) << S) + cb * VC + 8 * vc);
     }
   };
   for (int rs = 0; rs < nr; rs += C::RT) {
@@ -457,8 +466,8 @@ __global__ __launch_bounds__(BF_THREADS, 4) void highm_kernel(BflyArgs a) {
     load(rs, v);
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-      const int p = k * BF_THREADS + tid, row = p / 128, j = (p / 8) % 16, vc = p % 8;
-      uint16_t* d = reinterpret_cast<uint16_t*>(hl + row * C::RSB) + j * SP_VC + 8 * vc;
+      const int p = k * NTH + tid, row = p / PR, j = (p / VPC) % 16, vc = p % VPC;
+      uint16_t* d = reinterpret_cast<uint16_t*>(hl + row * C::RSB) + j * VC + 8 * vc;
       lm_st64(d, make_uint2(v[k].x, v[k].y));
       lm_st64(d + 4, make_uint2(v[k].z, v[k].w));
     }
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(BF_THREADS, 4) void highm_kernel(BflyArgs a) {
     for (int qd = 0; qd < 4; ++qd) {
       uint2 r[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + (g + 4 * i) * SP_VC + 4 * qd);
+      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + (g + 4 * i) * VC + 4 * qd);
       f32x4_t d[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -491,18 +500,18 @@ __global__ __launch_bounds__(BF_THREADS, 4) void highm_kernel(BflyArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        lm_st64(rp + (g + 4 * i) * SP_VC + 4 * qd,
+        lm_st64(rp + (g + 4 * i) * VC + 4 * qd,
                 make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-      const int p = k * BF_THREADS + tid, row = p / 128, j = (p / 8) % 16, vc = p % 8;
+      const int p = k * NTH + tid, row = p / PR, j = (p / VPC) % 16, vc = p % VPC;
       if (row < m) {
-        const uint16_t* sp = reinterpret_cast<const uint16_t*>(hl + row * C::RSB) + j * SP_VC + 8 * vc;
+        const uint16_t* sp = reinterpret_cast<const uint16_t*>(hl + row * C::RSB) + j * VC + 8 * vc;
         const uint2 x0 = lm_ld64(sp), x1 = lm_ld64(sp + 4);
         const size_t dst = MODE == SH_OUT ? s_row[rs + row] : size_t(r0 + rs + row) * n;
-        *reinterpret_cast<uint4*>(out + dst + (size_t(j) << S) + cb * SP_VC + 8 * vc) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        *reinterpret_cast<uint4*>(out + dst + (size_t(j) << S) + cb * VC + 8 * vc) = make_uint4(x0.x, x0.y, x1.x, x1.y);
       }
     }
     __syncthreads();  // stored before the next sub-tile is written
@@ -540,11 +549,11 @@ hipError_t launch_high_factor_prep(const float* ang, unsigned char* out, int n_e
 }
 
 template <typename K>
-static hipError_t sp_launch(K k, int grid, size_t lds, const BflyArgs& a, hipStream_t s) {
+static hipError_t sp_launch(K k, int grid, size_t lds, const BflyArgs& a, hipStream_t s, int threads = BF_THREADS) {
   if (grid <= 0) return hipSuccess;
   const hipError_t err = allow_dynamic_lds((const void*)k, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k, dim3(grid), dim3(BF_THREADS), lds, s, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -563,12 +572,13 @@ static hipError_t launch_low_S(const BflyArgs& a, bool trans, hipStream_t s) {
 template <int S>
 static hipError_t launch_high_S(const BflyArgs& a, int mode, hipStream_t s) {
   if (!a.fac || (mode == SH_MID && !a.fac1)) return hipErrorInvalidValue;
-  const int grid = sp_tiles(a) * ((1 << S) / SP_VC);
-  const size_t lds = HighMCfg<S>::lds_bytes;
+  using C = HighMCfg<S>;
+  const int grid = sp_tiles(a) * (C::NV / C::VC);
+  const size_t lds = C::lds_bytes;
   switch (mode) {
-    case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s);
-    case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s);
-    default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s);
+    case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s, C::NTH);
+    case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s, C::NTH);
+    default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s, C::NTH);
   }
 }
 
