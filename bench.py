@@ -94,6 +94,11 @@ def kernel_work(cfg):
         # bf16 rows of width 1024 .. 8192: butterflies as low / high parts
         return cfg.act == "bf16" and 10 <= L <= 13
 
+    def split_io(L):
+        # input / output rotations in two passes (widths 4096, 8192); widths
+        # 1024 and 2048 apply both parts in one pass
+        return split(L) and L >= 12
+
     def low(n, extra=0):
         # stages 0 .. L-5 of one butterfly over R rows (flops: 3 per element per stage)
         L = int(math.log2(n))
@@ -117,7 +122,7 @@ def kernel_work(cfg):
         if k > 1:
             w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
         return w
-    if split(Ld):
+    if split_io(Ld):
         w["bfly_in_hi"] = high(d, extra=4 * R)
         w["bfly_in_lo"] = low(d)
     else:
@@ -134,7 +139,7 @@ def kernel_work(cfg):
         else:
             w["bfly_mid"] = (2 * R * f * s + ang(f, nbfly=2), 2 * 3 * R * f * Lf, "hbm")
         w["gemm_down"] = gemm(f, d)
-    if split(Ld):
+    if split_io(Ld):
         w["bfly_out_lo"] = low(d)
         w["bfly_out_hi"] = high(d, extra=8 * R)
     else:
@@ -703,11 +708,18 @@ def bm_kernel_sha(kernel: str, cfg) -> str:
     """Hash of the HIP source that holds `kernel` (to invalidate stale counters)."""
     import hashlib
     g = "gemm_fp4.hip" if cfg.act == "bf16" and cfg.d_model >= 256 else "gemm.hip"
+    if kernel in ("bfly_in", "bfly_out") and cfg.act == "bf16" and cfg.d_model in (1024, 2048):
+        return _sha("butterfly_split.hip")
     src = {"gemm": g, "gemm_up": g, "gemm_down": g, "combine": "gemm.hip",
            "route": "route.hip", "bucket": "route.hip", "prep": "prep.hip", "prep_lo": "butterfly_split.hip",
            "prep_hi": "butterfly_split.hip",
            "fused": "fused_mfma.hip"}.get(kernel, "butterfly_split.hip" if kernel.endswith(("_hi", "_lo", "_lo_t"))
                                           else "butterfly.hip")
+    return _sha(src)
+
+
+def _sha(src: str) -> str:
+    import hashlib
     p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 

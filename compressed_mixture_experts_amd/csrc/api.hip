@@ -476,7 +476,8 @@ static int forward_kernel_names(const bmoe_layer* L, const char* (&names)[kMaxFo
     if (L->top_k > 1) names[n++] = "combine";
     return n;
   }
-  const bool split_d = use_split(L, ilog2(L->d_model));
+  // widths 4096 / 8192 run the input and output rotations as two passes each
+  const bool split_d = use_split(L, ilog2(L->d_model)) && !bfly_full_supported(ilog2(L->d_model));
   if (split_d) {
     names[n++] = "bfly_in_hi";
     names[n++] = "bfly_in_lo";
@@ -611,7 +612,11 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   // input rotation: U[q] = B(theta_e)^T x_t
   const bool split_d = use_split(layer, Ld);
   BflyArgs bi{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, highfac(LF_IN)};
-  if (split_d) {
+  if (split_d && bfly_full_supported(Ld)) {
+    BflyArgs bf{x, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_IN),
+                highfac(LF_IN)};
+    BMOE_LAUNCH(launch_bfly_full(bf, false, Ld, stream));
+  } else if (split_d) {
     BMOE_LAUNCH(launch_bfly_split(bi, SPLIT_HIGH_IN, Ld, stream));
     BflyArgs bl{bufU, bufU, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_IN)};
     BMOE_LAUNCH(launch_bfly_split(bl, SPLIT_LOW_T, Ld, stream));
@@ -648,7 +653,11 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   }
   // output rotation, gate, per-slot rows (or y directly when k == 1)
   BflyArgs bo{zlast, k == 1 ? y : yslot, phi_last, nullptr, offsets, perm, gate, R, N, k, 0, 0, highfac(LF_OUT)};
-  if (split_d) {
+  if (split_d && bfly_full_supported(Ld)) {
+    BflyArgs bf{zlast, k == 1 ? y : yslot, phi_last, nullptr, offsets, perm, gate, R, N, k, 0, 0, lowfac(LF_OUT),
+                highfac(LF_OUT)};
+    BMOE_LAUNCH(launch_bfly_full(bf, true, Ld, stream));
+  } else if (split_d) {
     BflyArgs bl{zlast, zlast, phi_last, nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_OUT)};
     BMOE_LAUNCH(launch_bfly_split(bl, SPLIT_LOW, Ld, stream));
     BMOE_LAUNCH(launch_bfly_split(bo, SPLIT_HIGH_OUT, Ld, stream));

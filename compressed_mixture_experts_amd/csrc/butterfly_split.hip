@@ -26,7 +26,8 @@ namespace bmoe {
 constexpr int SP_RB = 64;  // rows per workgroup
 
 // Workgroup tile t -> (expert e, first bucket row r0, rows nr) with tiles of
-// SP_RB rows per expert in expert order; e = -1 past the last tile.
+// RB rows per expert in expert order; e = -1 past the last tile.
+template <int RB = SP_RB>
 __device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_experts, int t, int& e, int& r0,
                                              int& nr) {
   __shared__ int s_info[3];
@@ -37,15 +38,15 @@ __device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_exper
   if (tid < n_experts) {
     off = offsets[tid];
     cnt = offsets[tid + 1] - off;
-    nt = (cnt + SP_RB - 1) / SP_RB;
+    nt = (cnt + RB - 1) / RB;
   }
   int total;
   const int excl = block_excl_scan(nt, s_tmp, total);
   if (tid < n_experts && t >= excl && t < excl + nt) {
     const int j = t - excl;
     s_info[0] = tid;
-    s_info[1] = off + j * SP_RB;
-    s_info[2] = min(SP_RB, cnt - j * SP_RB);
+    s_info[1] = off + j * RB;
+    s_info[2] = min(RB, cnt - j * RB);
   }
   __syncthreads();
   e = s_info[0];
@@ -518,6 +519,212 @@ __global__ __launch_bounds__(HighMCfg<S>::NTH, 1024 / HighMCfg<S>::NTH) void hig
   }
 }
 
+// ---------------------------------------------------------------- whole butterfly, one pass
+// Widths 1024 and 2048 (S = 6, 7): a row is 2 or 4 KiB, so a workgroup holds
+// FM_RB = 16 whole rows of one expert in LDS (row-major, row stride n + 8)
+// and applies both parts there, with the same prepared block factors as the
+// split passes: input rotation B^T = low^T high^T (gather the token rows,
+// high^T, then G1^T, G0^T), output rotation B = high low (G0, G1, then high,
+// times the gate, scattered to the slot rows).  One read and one write of
+// the rows instead of two of each.  In the row-major tile the high part's
+// column v, index j is element j 2^S + v, and the low part's chunks are
+// consecutive, so both parts use the split kernels' MFMA steps with those
+// strides.  Each wave keeps one pass's factor fragments in registers and
+// loads the next pass's before the barrier between them.
+constexpr int FM_RB = 16;      // rows per workgroup
+constexpr int FM_THREADS = 256;
+
+template <int S>
+struct FullCfg {
+  static constexpr int NV = 1 << S;          // high part: columns; low part: chunk width
+  static constexpr int n = 16 * NV;
+  static constexpr int RS = n + 8;           // LDS row stride (bf16)
+  static constexpr int NB0 = NV / 16;        // G0 blocks (16 x 16) per chunk
+  static constexpr int P0 = NV / 16;         // G1 blocks per chunk
+  static constexpr int HC = NV / 4;          // high-part columns per wave
+  static constexpr int G0W = 16 * NB0 / 4;   // G0 blocks per wave
+  static constexpr int G1W = 16 * P0 / 16;   // G1 groups of 4 blocks per wave
+  static constexpr int PPT = FM_RB * n / 8 / FM_THREADS;  // 16-byte pieces per thread
+  static constexpr size_t lds_bytes = size_t(FM_RB) * RS * 2;
+  static_assert(S == 6 || S == 7, "widths 1024 and 2048");
+  static_assert(LowMCfg<S>::B0 == 16 && LowMCfg<S>::P0 == P0, "low factor layout");
+};
+
+enum FullMode { FM_IN = 0, FM_OUT = 1 };
+
+template <int S, int MODE>
+__global__ __launch_bounds__(FM_THREADS, 2) void fullm_kernel(BflyArgs a) {
+  using C = FullCfg<S>;
+  using LC = LowMCfg<S>;
+  using HC = HighMCfg<S>;
+  constexpr int n = C::n, NV = C::NV, RS = C::RS;
+  extern __shared__ __attribute__((aligned(16))) uint16_t tile[];  // [FM_RB][RS]
+  __shared__ size_t s_row[FM_RB];
+  __shared__ float s_g[FM_RB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  int e, r0, nr;
+  sp_find_tile<FM_RB>(a.offsets, a.n_experts, blockIdx.x, e, r0, nr);
+  if (e < 0) return;
+  const unsigned char* lowf = a.fac + size_t(e) * LC::per_expert;
+  const unsigned char* highf = a.fac1 + size_t(e) * HC::per_expert;
+  if (tid < FM_RB) {
+    const int q = r0 + min(tid, nr - 1);
+    if constexpr (MODE == FM_IN) {
+      s_row[tid] = size_t(a.perm[q] / a.top_k) * n;  // token row of x
+    } else {
+      const int slot = a.perm[q];
+      s_row[tid] = size_t(slot) * n;                 // per-slot output row
+      s_g[tid] = a.gate[slot];
+    }
+  }
+
+  // factor fragments of one pass; a wave's blocks are w + 4 t
+  uint2 fh[C::HC];          // high part: columns 16 (w + 4 gi) + c
+  uint2 f0[C::G0W];         // G0: blocks w + 4 t (16 consecutive indices each)
+  uint2 f1[4 * C::G1W];     // G1: groups k = w + 4 t of 4 blocks (u0 .. u0 + 3 of one chunk)
+  auto load_high = [&]() {
+#pragma unroll
+    for (int gi = 0; gi < C::HC / 16; ++gi)
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        fh[16 * gi + c] = *reinterpret_cast<const uint2*>(highf + (size_t(16 * (wave + 4 * gi) + c) * 64 + lane) * 8);
+  };
+  auto load_g0 = [&]() {
+#pragma unroll
+    for (int t = 0; t < C::G0W; ++t) {
+      const int b = wave + 4 * t;
+      f0[t] = *reinterpret_cast<const uint2*>(lowf + size_t(b / C::NB0) * LC::chunk_bytes +
+                                              size_t(b % C::NB0) * 512 + lane * 8);
+    }
+  };
+  auto load_g1 = [&]() {
+#pragma unroll
+    for (int t = 0; t < C::G1W; ++t) {
+      const int k = wave + 4 * t, ch = (4 * k) / C::P0, u0 = (4 * k) % C::P0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        f1[4 * t + q] = *reinterpret_cast<const uint2*>(lowf + size_t(ch) * LC::chunk_bytes + LC::g0_bytes +
+                                                        (size_t(u0 + q) * 64 + lane) * 8);
+    }
+  };
+  uint16_t* rowp = tile + l16 * RS;  // this lane's row in the MFMA steps
+  auto high_pass = [&]() {
+    const float gr = MODE == FM_OUT ? s_g[min(l16, nr - 1)] : 1.0f;
+#pragma unroll
+    for (int gi = 0; gi < C::HC / 16; ++gi) {
+      uint16_t* rp = rowp + 16 * (wave + 4 * gi);
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        uint2 r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + (g + 4 * i) * NV + 4 * qd);
+        f32x4_t d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+          const uint2 bq = (q < 2) ? make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, sel), __builtin_amdgcn_perm(r[3].x, r[2].x, sel))
+                                   : make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, sel), __builtin_amdgcn_perm(r[3].y, r[2].y, sel));
+          d[q] = lm_mfma16(fh[16 * gi + 4 * qd + q], bq);
+          if constexpr (MODE == FM_OUT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[q][i] *= gr;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          lm_st64(rp + (g + 4 * i) * NV + 4 * qd,
+                  make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
+      }
+    }
+  };
+  auto g0_pass = [&]() {
+#pragma unroll
+    for (int t = 0; t < C::G0W; ++t) {
+      uint16_t* rp = rowp + 16 * (wave + 4 * t) + 4 * g;
+      lm_st64(rp, lm_pack4(lm_mfma16(f0[t], lm_ld64(rp))));
+    }
+  };
+  auto g1_pass = [&]() {
+#pragma unroll
+    for (int t = 0; t < C::G1W; ++t) {
+      const int k = wave + 4 * t;
+      uint16_t* rp = rowp + ((4 * k) / C::P0) * NV + (4 * k) % C::P0;
+      uint2 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + C::P0 * g1_slot<S>(g, i));
+      f32x4_t d[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+        const uint2 bq = (q < 2) ? make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, sel), __builtin_amdgcn_perm(r[3].x, r[2].x, sel))
+                                 : make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, sel), __builtin_amdgcn_perm(r[3].y, r[2].y, sel));
+        d[q] = lm_mfma16(f1[4 * t + q], bq);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lm_st64(rp + C::P0 * g1_slot<S>(g, i), make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
+    }
+  };
+
+  // first pass's fragments, then the rows (rows past the tile's last repeat it)
+  if constexpr (MODE == FM_IN) load_high(); else load_g0();
+  __syncthreads();  // row table
+  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
+  {
+    constexpr int CPR = n / 8;  // 16-byte pieces per row
+#pragma unroll
+    for (int k0 = 0; k0 < C::PPT; k0 += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int p = (k0 + k) * FM_THREADS + tid, row = min(p / CPR, nr - 1), c = p % CPR;
+        const size_t src = MODE == FM_IN ? s_row[row] : size_t(r0 + row) * n;
+        v[k] = *reinterpret_cast<const uint4*>(in + src + 8 * c);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int p = (k0 + k) * FM_THREADS + tid, row = p / CPR, c = p % CPR;
+        uint16_t* d = tile + row * RS + 8 * c;
+        lm_st64(d, make_uint2(v[k].x, v[k].y));
+        lm_st64(d + 4, make_uint2(v[k].z, v[k].w));
+      }
+    }
+  }
+  if constexpr (MODE == FM_IN) load_g1(); else load_g1();
+  __syncthreads();
+  if constexpr (MODE == FM_IN) {
+    high_pass();   // high^T (transposed blocks)
+    load_g0();
+    __syncthreads();
+    g1_pass();     // G1^T
+    __syncthreads();
+    g0_pass();     // G0^T
+  } else {
+    g0_pass();
+    load_high();
+    __syncthreads();
+    g1_pass();
+    __syncthreads();
+    high_pass();   // high, times the gate
+  }
+  __syncthreads();
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  {
+    constexpr int CPR = n / 8;
+#pragma unroll
+    for (int k = 0; k < C::PPT; ++k) {
+      const int p = k * FM_THREADS + tid, row = p / CPR, c = p % CPR;
+      if (row < nr) {
+        const uint16_t* sp = tile + row * RS + 8 * c;
+        const uint2 x0 = lm_ld64(sp), x1 = lm_ld64(sp + 4);
+        const size_t dst = MODE == FM_IN ? size_t(r0 + row) * n : s_row[row];
+        *reinterpret_cast<uint4*>(out + dst + 8 * c) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      }
+    }
+  }
+}
+
 size_t high_factor_bytes(int log2n) {
   switch (log2n) {
     case 10: return HighMCfg<6>::per_expert;
@@ -579,6 +786,26 @@ static hipError_t launch_high_S(const BflyArgs& a, int mode, hipStream_t s) {
     case SH_IN: return sp_launch(highm_kernel<S, SH_IN>, grid, lds, a, s, C::NTH);
     case SH_MID: return sp_launch(highm_kernel<S, SH_MID>, grid, lds, a, s, C::NTH);
     default: return sp_launch(highm_kernel<S, SH_OUT>, grid, lds, a, s, C::NTH);
+  }
+}
+
+template <int S>
+static hipError_t launch_full_S(const BflyArgs& a, bool out_mode, hipStream_t s) {
+  if (!a.fac || !a.fac1) return hipErrorInvalidValue;
+  const int grid = (a.rows + FM_RB - 1) / FM_RB + a.n_experts;
+  const size_t lds = FullCfg<S>::lds_bytes;
+  if (out_mode) return sp_launch(fullm_kernel<S, FM_OUT>, grid, lds, a, s, FM_THREADS);
+  return sp_launch(fullm_kernel<S, FM_IN>, grid, lds, a, s, FM_THREADS);
+}
+
+bool bfly_full_supported(int log2n) { return log2n == 10 || log2n == 11; }
+
+hipError_t launch_bfly_full(const BflyArgs& a, bool out_mode, int log2n, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  switch (log2n) {
+    case 10: return launch_full_S<6>(a, out_mode, s);
+    case 11: return launch_full_S<7>(a, out_mode, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -274,6 +274,12 @@ size_t high_factor_bytes(int log2n);
 hipError_t launch_high_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n,
                                    bool trans, hipStream_t s);
 hipError_t launch_bfly_split(const BflyArgs& a, int part, int log2n, hipStream_t s);
+// Whole butterfly of width 1024 or 2048 in one pass (butterfly_split.hip):
+// input rotation (out_mode false: gather token rows, high^T, low^T, rows in
+// bucket order) or output rotation (true: low, high, times the gate, per-slot
+// rows); fac = the rotation's low-part factors, fac1 = its high-part factors.
+bool bfly_full_supported(int log2n);
+hipError_t launch_bfly_full(const BflyArgs& a, bool out_mode, int log2n, hipStream_t s);
 bool gemm_fp4_supported(int N, int K);
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);

@@ -499,9 +499,10 @@ def test_substrate_input_grad_arguments():
 
 def test_forward_kernel_names_of_the_widest_layer():
     # per-call preparation of an FFN layer whose both widths use the split
-    # rotations: the most launches one forward makes
+    # rotations in two passes each (widths 4096 and 8192): the most launches
+    # one forward makes
     L = bm.lib()
-    s = make_struct(d_model=2048, d_ff=8192, n_experts=256, ffn_act=bm.ACT_GELU_ERF)
+    s = make_struct(d_model=4096, d_ff=8192, n_experts=256, ffn_act=bm.ACT_GELU_ERF)
     n = ctypes.c_int32(0)
     buf = ctypes.create_string_buffer(1024)
     assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), buf, 1024) == 0
@@ -515,6 +516,13 @@ def test_forward_kernel_names_of_the_widest_layer():
     assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), small, 8) == 0
     assert small.value == b"prep,pr"
     assert L.bmoe_forward_kernels(ctypes.byref(s), None, small, 8) == 1
+    # widths 1024 and 2048: the input and output rotations in one pass each
+    s = make_struct(d_model=2048, d_ff=8192, n_experts=256, ffn_act=bm.ACT_GELU_ERF)
+    assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), buf, 1024) == 0
+    names = buf.value.decode().split(",")
+    assert len(names) == n.value == 19
+    assert names[9:] == ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+                         "bfly_mid_lo_t", "gemm_down", "bfly_out", "combine"]
 
 
 def test_forward_noalloc_argument_errors():

@@ -63,12 +63,14 @@ def test_large_ffn_kernel_bytes_and_flops():
     assert w["bfly_mid_lo"][0] == 2 * R * f * 2 + N * 9 * (f // 2) * 4
     # high part of the FFN middle: the top four stages of two butterflies
     assert w["bfly_mid_hi"][0] == 2 * R * f * 2 + 2 * N * 4 * (f // 2) * 4
-    # output high part: rows in and out, its angles, slots and gates
-    assert w["bfly_out_hi"][0] == 2 * R * d * 2 + N * 4 * (d // 2) * 4 + 8 * R
+    # output rotation (width 2048, one pass): rows in and out, all 11 stages'
+    # angles, slots and gates
+    assert w["bfly_out"][0] == 2 * R * d * 2 + N * 11 * (d // 2) * 4 + 8 * R
+    assert w["bfly_in"][0] == 2 * R * d * 2 + N * 11 * (d // 2) * 4 + 4 * R
     assert w["combine"][0] == R * d * 2 + T * d * 2 == 402_653_184
     assert w["route"][0] == T * d * 2 + N * d * 2 + 8 * R
-    names = ["route", "bucket", "bfly_in_hi", "bfly_in_lo", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
-             "bfly_mid_lo_t", "gemm_down", "bfly_out_lo", "bfly_out_hi", "combine"]
+    names = ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+             "bfly_mid_lo_t", "gemm_down", "bfly_out", "combine"]
     assert set(w) == set(names)
 
 
