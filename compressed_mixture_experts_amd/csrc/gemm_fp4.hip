@@ -178,20 +178,34 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
     if (kt + 1 < nk) step(kt + 1, W1, W0);
   }
 
-  uint16_t* Z = reinterpret_cast<uint16_t*>(a.z);
+  // Output tile through LDS (both activation buffers are free after the last
+  // step's barrier): row r, 8-byte unit u (4 columns) at unit u ^ 2 (r mod 16)
+  // of the row, so the 32 lanes of one write pass (16 rows, 2 units each) and
+  // the 16 lanes of one 16-byte read (one row) hit distinct banks; each row's
+  // TN columns then go out as whole 16-byte pieces, one row per 32 lanes.
+  static_assert(TN == 256, "one 512-byte row of output per 32 lanes");
+  uint2* st = reinterpret_cast<uint2*>(smem);
 #pragma unroll
   for (int i = 0; i < OB; ++i) {
-    const int n = n0 + 16 * i + 4 * g;
+    const int u = wave * (WN / 4) + 4 * i + g;
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-      const int m = m0 + 16 * j + l16;
-      if (m < a.M) {
-        uint2 o;
-        o.x = pack_bf16x2(a.alpha * acc[i][j][0], a.alpha * acc[i][j][1]);
-        o.y = pack_bf16x2(a.alpha * acc[i][j][2], a.alpha * acc[i][j][3]);
-        *reinterpret_cast<uint2*>(Z + size_t(m) * a.N + n) = o;
-      }
+      const int r = 16 * j + l16;
+      uint2 o;
+      o.x = pack_bf16x2(a.alpha * acc[i][j][0], a.alpha * acc[i][j][1]);
+      o.y = pack_bf16x2(a.alpha * acc[i][j][2], a.alpha * acc[i][j][3]);
+      st[r * (TN / 4) + (u ^ ((r & 15) << 1))] = o;
     }
+  }
+  __syncthreads();
+  uint16_t* Z = reinterpret_cast<uint16_t*>(a.z);
+  constexpr int CPR = TN / 8;  // 16-byte pieces per output row
+#pragma unroll
+  for (int p = 0; p < GF_TM * CPR / GF_THREADS; ++p) {
+    const int idx = p * GF_THREADS + tid, r = idx / CPR, c = idx % CPR;
+    if (m0 + r < a.M)
+      *reinterpret_cast<uint4*>(Z + size_t(m0 + r) * a.N + tn * TN + 8 * c) =
+          *reinterpret_cast<const uint4*>(smem + r * TN + 8 * (c ^ (r & 15)));
   }
 }
 
