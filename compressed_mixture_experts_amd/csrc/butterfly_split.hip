@@ -25,11 +25,12 @@ namespace bmoe {
 
 constexpr int SP_RB = 64;  // rows per workgroup
 
-// Workgroup tile t -> (expert e, first bucket row r0, rows nr) with tiles of
-// RB rows per expert in expert order; e = -1 past the last tile.
-template <int RB = SP_RB>
-__device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_experts, int t, int& e, int& r0,
-                                             int& nr) {
+// Tiles of RB rows per expert in expert order.  The workgroup's tile index
+// is pick(total) for `total` real tiles; it is turned into (expert e, first
+// bucket row r0, rows nr), e = -1 for an index outside [0, total).
+template <int RB, typename Pick>
+__device__ __forceinline__ void sp_lookup(const int32_t* offsets, int n_experts, Pick pick, int& e, int& r0,
+                                          int& nr) {
   __shared__ int s_info[3];
   __shared__ int s_tmp[16];  // one entry per wave (up to 1024 threads); only experts < 256 count
   const int tid = threadIdx.x;
@@ -42,6 +43,7 @@ __device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_exper
   }
   int total;
   const int excl = block_excl_scan(nt, s_tmp, total);
+  const int t = pick(total);
   if (tid < n_experts && t >= excl && t < excl + nt) {
     const int j = t - excl;
     s_info[0] = tid;
@@ -52,6 +54,32 @@ __device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_exper
   e = s_info[0];
   r0 = s_info[1];
   nr = s_info[2];
+}
+
+// Workgroup tile t, in grid order.
+template <int RB = SP_RB>
+__device__ __forceinline__ void sp_find_tile(const int32_t* offsets, int n_experts, int t, int& e, int& r0,
+                                             int& nr) {
+  sp_lookup<RB>(offsets, n_experts, [=](int) { return t; }, e, r0, nr);
+}
+
+// Each tile split into `units` workgroups (sub = 0 .. units-1).  Workgroup b
+// runs on XCD b mod 8 (round-robin dispatch); the mapping gives every XCD one
+// contiguous run of the real units, the runs balanced to within one, so
+// consecutive tiles of one expert share an XCD's L2 and the expert's factors
+// are fetched from beyond it about once rather than once per XCD.  The grid
+// must hold at least as many workgroups as real units.
+template <int RB = SP_RB>
+__device__ __forceinline__ void sp_find_tile_xcd(const int32_t* offsets, int n_experts, int units, int& e, int& r0,
+                                                 int& nr, int& sub) {
+  int u = -1;
+  sp_lookup<RB>(offsets, n_experts, [&](int total) {
+    const int b = blockIdx.x, x = b & 7, slot = b >> 3;
+    const int nu = total * units, per = nu >> 3, rem = nu & 7;
+    u = slot < per + (x < rem) ? x * per + min(x, rem) + slot : -1;
+    return u < 0 ? -1 : u / units;
+  }, e, r0, nr);
+  sub = u < 0 ? 0 : u % units;
 }
 
 // ---------------------------------------------------------------- matrix-core low part
@@ -421,9 +449,8 @@ __global__ __launch_bounds__(HighMCfg<S>::NTH, 1024 / HighMCfg<S>::NTH) void hig
   __shared__ float s_g[SP_RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int t = blockIdx.x / ncb, cb = blockIdx.x % ncb;
-  int e, r0, nr;
-  sp_find_tile(a.offsets, a.n_experts, t, e, r0, nr);
+  int e, r0, nr, cb;
+  sp_find_tile_xcd(a.offsets, a.n_experts, ncb, e, r0, nr, cb);
   if (e < 0) return;
 
   const int vw = cb * VC + 16 * wave;  // this wave's first column
@@ -563,8 +590,8 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fullm_kernel(BflyArgs a) {
   __shared__ float s_g[FM_RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  int e, r0, nr;
-  sp_find_tile<FM_RB>(a.offsets, a.n_experts, blockIdx.x, e, r0, nr);
+  int e, r0, nr, sub;
+  sp_find_tile_xcd<FM_RB>(a.offsets, a.n_experts, 1, e, r0, nr, sub);
   if (e < 0) return;
   const unsigned char* lowf = a.fac + size_t(e) * LC::per_expert;
   const unsigned char* highf = a.fac1 + size_t(e) * HC::per_expert;

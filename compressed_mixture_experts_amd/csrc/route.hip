@@ -627,27 +627,29 @@ __global__ __launch_bounds__(RW_THREADS) void route_whole_kernel(RouteArgs a) {
   if (tid == 0) sh.NF = 0;
   if (tid < BT) sh.X2[tid] = 0.f;
 
-  // token tile: all loads first
+  // token tile and this wave's gate rows (block b = wave + 8 i, k-step st, 8
+  // values per lane), all loads issued before any wait.  The loads are
+  // unconditional (a branch around a load makes the wait at its join a full
+  // drain): chunks past the tile read its last chunk, tokens past T row T-1,
+  // experts past N row N-1; none of these values reaches an output (tokens
+  // past T are never stored, experts past N never ranked, and a repeated row
+  // leaves max_e |w_e| unchanged).
   uint4 xv[CPT];
 #pragma unroll
   for (int r = 0; r < CPT; ++r) {
-    const int c = r * RW_THREADS + tid;
-    const int tl = c / CPR;
-    xv[r] = (c < NCH && t0 + tl < a.T) ? *reinterpret_cast<const uint4*>(xg + size_t(t0 + tl) * D + 8 * (c % CPR))
-                                       : make_uint4(0, 0, 0, 0);
+    const int c = min(r * RW_THREADS + tid, NCH - 1);
+    const int tok = min(t0 + c / CPR, a.T - 1);
+    xv[r] = *reinterpret_cast<const uint4*>(xg + size_t(tok) * D + 8 * (c % CPR));
   }
-  // this wave's gate rows: block b = wave + 8 i, k-step s, 8 values per lane
   bool bval[NI];
   uint4 A[NI][KS];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int b = wave + RW_WAVES * i;
-    const int e = 16 * b + l16;
+    const int e = min(16 * b + l16, N - 1);
     bval[i] = b < NB;
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
-      A[i][st] = (bval[i] && e < N) ? *reinterpret_cast<const uint4*>(wg + size_t(e) * D + 32 * st + 8 * g)
-                                    : make_uint4(0, 0, 0, 0);
+    for (int st = 0; st < KS; ++st) A[i][st] = *reinterpret_cast<const uint4*>(wg + size_t(e) * D + 32 * st + 8 * g);
   }
   // tile -> LDS; |x|^2 partial sums reduced over the lanes sharing a row
   float xs[CPT];
