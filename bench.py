@@ -713,7 +713,7 @@ def bm_kernel_sha(kernel: str, cfg) -> str:
     src = {"gemm": g, "gemm_up": g, "gemm_down": g, "combine": "gemm.hip",
            "route": "route.hip", "bucket": "route.hip", "prep": "prep.hip", "prep_lo": "butterfly_split.hip",
            "prep_hi": "butterfly_split.hip",
-           "fused": "fused_mfma.hip"}.get(kernel, "butterfly_split.hip" if kernel.endswith(("_hi", "_lo", "_lo_t"))
+           "prep_gate": "route.hip", "fused": "fused_mfma.hip"}.get(kernel, "butterfly_split.hip" if kernel.endswith(("_hi", "_lo", "_lo_t"))
                                           else "butterfly.hip")
     return _sha(src)
 

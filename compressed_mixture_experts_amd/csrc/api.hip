@@ -170,6 +170,7 @@ struct PrepLayout {
   size_t w_off[2], w_len[2], fac_off, fac_len, total;
   size_t lf_off[LF_SETS], lf_len[LF_SETS];  // low-part block factors
   size_t hf_off[LF_SETS], hf_len[LF_SETS];  // high-part block factors (one 16 x 16 block per column)
+  size_t gf_off, gf_len;                     // gate matrix as MFMA fragments (last)
   bool fp4[2];
 };
 
@@ -184,6 +185,14 @@ void low_set(const bmoe_layer* L, int k, const float*& ang, int& log2n, bool& tr
   }
 }
 
+// The gate matrix in MFMA fragment order, after everything else (bf16 layers).
+void add_gate_frags(const bmoe_layer* L, PrepLayout& q) {
+  q.gf_len = gate_frag_bytes(L->n_experts, L->d_model);
+  if (!q.gf_len) return;
+  q.gf_off = align256(q.total);
+  q.total = align256(q.gf_off + q.gf_len);
+}
+
 PrepLayout prep_layout(const bmoe_layer* L) {
   PrepLayout q{};
   size_t o = 0;
@@ -195,6 +204,7 @@ PrepLayout prep_layout(const bmoe_layer* L) {
     q.fac_off = o;
     q.fac_len = q.fp4[0] ? size_t(L->n_experts) * factor_bytes_per_expert(ilog2(L->d_model)) : 0;
     q.total = align256(o + q.fac_len);
+    if (L->act_dtype == BMOE_BF16) add_gate_frags(L, q);
     return q;
   }
   if (L->act_dtype != BMOE_BF16) return q;
@@ -226,6 +236,7 @@ PrepLayout prep_layout(const bmoe_layer* L) {
     }
   }
   q.total = o;
+  add_gate_frags(L, q);
   return q;
 }
 
@@ -320,11 +331,18 @@ bmoe_status validate_call(const bmoe_layer* L, const void* x, int32_t T, void* w
   return BMOE_OK;
 }
 
+// The caller's prepared gate fragments, or none (the router then reads W_g).
+const void* gate_frags(const bmoe_layer* L) {
+  const PrepLayout q = prep_layout(L);
+  return L->prepared && q.gf_len ? static_cast<const unsigned char*>(L->prepared) + q.gf_off : nullptr;
+}
+
 bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* idx, float* gate,
                       void* ws, const Plan& p, hipStream_t s) {
   const int act = L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32;
   RouteArgs ra{x, L->w_gate, idx, gate, T, L->d_model, L->n_experts, L->top_k, L->renorm_gates,
                at<int32_t>(ws, p.tslots), at<float>(ws, p.tgates), at<int32_t>(ws, p.tstart)};
+  ra.w_frag = gate_frags(L);
   BMOE_HIP(launch_route(ra, act, s));
   BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm),
                 nullptr, int32_t(p.R), L->n_experts, route_tile_tokens(T) * L->top_k, p.tiles, 0, 0};
@@ -412,10 +430,13 @@ bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, 
     if ((q.lf_len[k] || q.hf_len[k]) && overlap(rp, Range{ang, size_t(layer->n_experts) * ln * (size_t(1) << (ln - 1)) * 4}))
       return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
   }
+  if (q.gf_len && overlap(rp, Range{layer->w_gate, size_t(layer->n_experts) * layer->d_model * 2}))
+    return fail(BMOE_ERR_ALIAS, "prepared buffer overlaps a weight array");
   st = check_device();
   if (st != BMOE_OK) return st;
   unsigned char* buf = static_cast<unsigned char*>(prepared);
   if (prep_has_sub(q)) BMOE_HIP(launch_prep(prep_args(layer, q, buf), stream));
+  if (q.gf_len) BMOE_HIP(launch_gate_frag(layer->w_gate, buf + q.gf_off, layer->n_experts, layer->d_model, stream));
   for (int k = 0; k < LF_SETS; ++k) {
     const float* ang;
     int ln;
@@ -456,9 +477,9 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T, int32_
 }
 
 // Kernel launches of one forward, in order (marks[i] follows launch i-1): at
-// most 1 + 2 LF_SETS preparation launches, route and bucket, and 12 for the
+// most 2 + 2 LF_SETS preparation launches, route and bucket, and 12 for the
 // widest FFN layer.
-constexpr int kMaxForwardKernels = 1 + 2 * LF_SETS + 2 + 12;
+constexpr int kMaxForwardKernels = 2 + 2 * LF_SETS + 2 + 12;
 static int forward_kernel_names(const bmoe_layer* L, const char* (&names)[kMaxForwardKernels]) {
   int n = 0;
   if (!L->prepared) {
@@ -468,6 +489,7 @@ static int forward_kernel_names(const bmoe_layer* L, const char* (&names)[kMaxFo
       if (q.lf_len[k]) names[n++] = "prep_lo";
       if (q.hf_len[k]) names[n++] = "prep_hi";
     }
+    if (q.gf_len) names[n++] = "prep_gate";
   }
   names[n++] = "route";
   names[n++] = "bucket";
@@ -571,6 +593,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
       if (q.lf_len[k]) BMOE_LAUNCH(launch_low_factor_prep(ang, buf + q.lf_off[k], N, ln, tr, stream));
       if (q.hf_len[k]) BMOE_LAUNCH(launch_high_factor_prep(ang, buf + q.hf_off[k], N, ln, tr, stream));
     }
+    if (q.gf_len) BMOE_LAUNCH(launch_gate_frag(layer->w_gate, buf + q.gf_off, N, d, stream));
     pbase = buf;
   }
   auto lowfac = [&](int k) -> const unsigned char* { return q.lf_len[k] ? pbase + q.lf_off[k] : nullptr; };
@@ -587,6 +610,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   // router and bucketing
   RouteArgs ra{x, layer->w_gate, idx, gate, T, d, N, k, layer->renorm_gates,
                at<int32_t>(workspace, p.tslots), at<float>(workspace, p.tgates), at<int32_t>(workspace, p.tstart)};
+  ra.w_frag = q.gf_len ? pbase + q.gf_off : nullptr;
   BMOE_LAUNCH(launch_route(ra, act, stream));
   TileRec* rec = p.n_rec ? at<TileRec>(workspace, p.rec) : nullptr;
   const int rec_rows = rec ? fused_tile_rows(R, N) : 0;

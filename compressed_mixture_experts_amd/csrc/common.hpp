@@ -106,6 +106,9 @@ struct RouteArgs {
   int32_t* tile_slots;      // [R] slots b C .. b C + C - 1 ordered by expert, ascending within one
   float* tile_gates;        // [R] their gates, same order
   int32_t* tile_start;      // [G][N] position of expert e's first slot in tile b's list
+  // optional (bf16): W_g as MFMA operand fragments (gate_frag_bytes), read in
+  // place of w_gate when set
+  const void* w_frag;
 };
 
 // Work record of one tile of the square-expert kernel: up to `rows` (32, 48
@@ -237,6 +240,12 @@ int route_tile_tokens(int T);
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
+// Gate matrix as MFMA operand fragments: for 16-expert block b, contraction
+// step st of 32 and lane l (expert 16 b + l % 16, indices 32 st + 8 (l / 16)
+// .. +7), 16 bytes at ((b (d / 32) + st) 64 + l) 16; experts past N are zero.
+size_t gate_frag_bytes(int N, int d);
+bool gate_frag_supported(int d);
+hipError_t launch_gate_frag(const void* w_gate, void* out, int N, int d, hipStream_t s);
 hipError_t launch_butterfly(const BflyArgs& a, int mode, int act, int log2n, hipStream_t s);
 // one angle set for all rows (the test hook of bmoe_debug.h)
 hipError_t launch_bfly_dbg(const BflyArgs& a, int act, int log2n, hipStream_t s);

@@ -443,14 +443,23 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     // loads are unconditional (a branch around loads in the K loop makes every
     // wait a full drain): experts past N read row N-1, tokens past T row T-1,
     // chunk indices past the tile chunk XCH-1; none of these is used
+    // gate fragments of block wave + 4 i, k-step st at abase[i] + st * astep:
+    // one contiguous 1 KiB per wave from the fragment copy, else 16 rows of 64
+    // bytes from W_g (blocks past the last read the last one)
+    const uint16_t* abase[4];
+    const int astep = a.w_frag ? 512 : 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = min(wave + 4 * i, NB - 1);
+      abase[i] = a.w_frag ? reinterpret_cast<const uint16_t*>(a.w_frag) + (size_t(b) * (d / 32) * 64 + lane) * 8
+                          : wg + size_t(min(16 * b + (lane & 15), N - 1)) * d + 8 * (lane >> 4);
+    }
     auto load_a = [&](int k0, uint4 (&dst)[4][2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = min(16 * (wave + 4 * i) + (lane & 15), N - 1);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          dst[i][s] = *reinterpret_cast<const uint4*>(wg + size_t(e) * d + k0 + 32 * s + 8 * (lane >> 4));
-      }
+          dst[i][s] = *reinterpret_cast<const uint4*>(abase[i] + (k0 / 32 + s) * astep);
     };
     auto load_x = [&](int k0, uint4 (&dst)[XPT]) {
 #pragma unroll
@@ -631,9 +640,10 @@ __global__ __launch_bounds__(RW_THREADS) void route_whole_kernel(RouteArgs a) {
   // values per lane), all loads issued before any wait.  The loads are
   // unconditional (a branch around a load makes the wait at its join a full
   // drain): chunks past the tile read its last chunk, tokens past T row T-1,
-  // experts past N row N-1; none of these values reaches an output (tokens
-  // past T are never stored, experts past N never ranked, and a repeated row
-  // leaves max_e |w_e| unchanged).
+  // experts past N row N-1 (or zeros in the fragment copy), blocks past the
+  // last the last one; none of these values reaches an output (tokens past T
+  // are never stored, experts past N never ranked, blocks past the last never
+  // multiplied, and a repeated row leaves max_e |w_e| unchanged).
   uint4 xv[CPT];
 #pragma unroll
   for (int r = 0; r < CPT; ++r) {
@@ -643,13 +653,15 @@ __global__ __launch_bounds__(RW_THREADS) void route_whole_kernel(RouteArgs a) {
   }
   bool bval[NI];
   uint4 A[NI][KS];
+  const int astep = a.w_frag ? 512 : 32;  // fragment copy: 1 KiB per wave per k-step
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int b = wave + RW_WAVES * i;
-    const int e = min(16 * b + l16, N - 1);
+    const int b = wave + RW_WAVES * i, bc = min(b, NB - 1);
     bval[i] = b < NB;
+    const uint16_t* ab = a.w_frag ? reinterpret_cast<const uint16_t*>(a.w_frag) + (size_t(bc) * KS * 64 + lane) * 8
+                                  : wg + size_t(min(16 * bc + l16, N - 1)) * D + 8 * g;
 #pragma unroll
-    for (int st = 0; st < KS; ++st) A[i][st] = *reinterpret_cast<const uint4*>(wg + size_t(e) * D + 32 * st + 8 * g);
+    for (int st = 0; st < KS; ++st) A[i][st] = *reinterpret_cast<const uint4*>(ab + st * astep);
   }
   // tile -> LDS; |x|^2 partial sums reduced over the lanes sharing a row
   float xs[CPT];
@@ -886,6 +898,33 @@ hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
     case 32: return launch_route_bt<32>(a, act, s);
     default: return launch_route_bt<16>(a, act, s);
   }
+}
+
+// ------------------------------------------------------------------ gate fragments
+// One thread per 16-byte fragment: copies W_g's 8 values of (expert, k-step,
+// lane) to fragment order (zeros for experts past N).
+__global__ __launch_bounds__(256) void gate_frag_kernel(const uint16_t* __restrict__ w, uint4* __restrict__ out,
+                                                        int N, int d, int units) {
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int ks = d / 32, lane = u & 63, st = (u >> 6) % ks, b = (u >> 6) / ks;
+  const int e = 16 * b + (lane & 15);
+  out[u] = e < N ? *reinterpret_cast<const uint4*>(w + size_t(e) * d + 32 * st + 8 * (lane >> 4))
+                 : make_uint4(0, 0, 0, 0);
+}
+
+bool gate_frag_supported(int d) { return d > 0 && d % 32 == 0; }
+
+size_t gate_frag_bytes(int N, int d) {
+  return gate_frag_supported(d) ? size_t((N + 15) / 16) * 16 * size_t(d) * 2 : 0;
+}
+
+hipError_t launch_gate_frag(const void* w_gate, void* out, int N, int d, hipStream_t s) {
+  if (N <= 0 || !gate_frag_supported(d)) return hipErrorInvalidValue;
+  const int units = int(gate_frag_bytes(N, d) / 16);
+  hipLaunchKernelGGL(gate_frag_kernel, dim3((units + 255) / 256), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(w_gate), reinterpret_cast<uint4*>(out), N, d, units);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ bucketing

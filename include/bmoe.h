@@ -140,9 +140,10 @@ bmoe_status bmoe_pack_ternary(const int8_t* w, int32_t rows, int32_t cols,
 bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* bytes);
 
 /* Size of the prepared-weights buffer of this layer, 0 when its forward path
- * uses none (or the layer is invalid).  Every bf16 layer except narrow FFNs
- * uses one; fp32 layers use none.  Contents, all depending on the weights only
- * (ButterflyMoE zh §2.1-§2.2: ternary substrate, per-expert Givens angles):
+ * uses none (or the layer is invalid).  Every bf16 layer uses one; fp32
+ * layers use none.  Contents, all depending on the weights only
+ * (ButterflyMoE zh §2.1-§2.2: ternary substrate, per-expert Givens angles;
+ * nl §2: the gating network):
  *  - square layers of width 64..512: the substrate re-encoded for the expert
  *    kernel (one byte per weight at widths 64 and 128; at 256 and 512 two bits
  *    per weight, each 32-bit word holding 16 consecutive weights with the
@@ -157,7 +158,11 @@ bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* byte
  *    two-bit code; and
  *    for every rotation of width n = 2^L in 1024..8192, per expert, its stages
  *    0..L-5 as block factors per chunk of 2^(L-4) indices and its top four
- *    stages as one 16 x 16 block per column (bf16). */
+ *    stages as one 16 x 16 block per column (bf16);
+ *  - every bf16 layer, last: the gate matrix W_g reordered for the router's
+ *    matrix-core products, ceil(n_experts / 16) * 16 * d_model * 2 bytes
+ *    (per block of 16 experts and contraction step of 32, the 16-byte pieces
+ *    in operand-lane order; experts past n_experts zero). */
 size_t bmoe_prepared_bytes(const bmoe_layer* layer);
 
 /* Fill `prepared` (device, 256-byte aligned, at least bmoe_prepared_bytes) for

@@ -231,13 +231,18 @@ def test_status_strings():
 def test_prepared_bytes_layout():
     L = bm.lib()
     # square bf16 width 512: 2-bit substrate d*d/4 plus 98304 factor bytes per expert
+    # every bf16 layer ends with the gate matrix in fragment order: 16-expert
+    # blocks (64 experts here) of d_model bf16 each
+    gate = lambda n_exp, d: (n_exp + 15) // 16 * 16 * d * 2
     s = make_struct()
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 512 * 512 // 4 + 64 * 98304
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 512 * 512 // 4 + 64 * 98304 + gate(64, 512)
     s = make_struct(d_model=256)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 256 * 256 // 4 + 64 * 32768
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 256 * 256 // 4 + 64 * 32768 + gate(64, 256)
+    s = make_struct(d_model=512, n_experts=40)       # padded to 48 experts
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 512 * 512 // 4 + 40 * 98304 + 48 * 512 * 2
     # widths 64 / 128: one byte per weight, no factors (rounded up to 256 bytes)
     s = make_struct(d_model=128)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 128 * 128
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 128 * 128 + gate(64, 128)
     # wider bf16 layers: each substrate whose product the matrix-core GEMM covers
     # (output width a multiple of 256, contraction a multiple of 128), 2 bits per weight;
     # every rotation of width 1024 .. 8192: one 16 x 16 high-part block per column
@@ -249,20 +254,22 @@ def test_prepared_bytes_layout():
     hi = lambda w: (w // 16) * 512
     lo = lambda w: 16 * ((w // 16) * max(16, w // 256) * 2 + (w // 256) * 512)
     rot = lambda w: hi(w) + lo(w)
-    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == 1024 * 1024 // 4 + 2 * 64 * rot(1024)
+    assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(d_model=1024))) == (1024 * 1024 // 4 + 2 * 64 * rot(1024)
+                                                                          + gate(64, 1024))
     s = make_struct(d_model=1024, d_ff=4096, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (4096 * 1024 // 4) + 2 * 64 * rot(1024)
-                                                      + 2 * 64 * rot(4096))
+                                                      + 2 * 64 * rot(4096) + gate(64, 1024))
     assert lo(4096) == 16 * 16384 and lo(8192) == 16 * (32768 + 16384)
     s = make_struct(d_model=2048, d_ff=8192, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (8192 * 2048 // 4) + 2 * 64 * rot(2048)
-                                                      + 2 * 64 * rot(8192))
+                                                      + 2 * 64 * rot(8192) + gate(64, 2048))
     # d_ff = 128: the up product (128 outputs) keeps the LDS-decoding GEMM, the down
     # one runs on the prepared codes
     s = make_struct(d_model=1024, d_ff=128, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 4 + 2 * 64 * rot(1024)
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 1024 * 128 // 4 + 2 * 64 * rot(1024) + gate(64, 1024)
+    # a narrow FFN: only the gate fragments
     s = make_struct(d_model=128, d_ff=64, ffn_act=bm.ACT_GELU_ERF)
-    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == 0
+    assert L.bmoe_prepared_bytes(ctypes.byref(s)) == gate(64, 128)
     # fp32 activations and invalid layers use none
     assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(act_dtype=bm.F32))) == 0
     assert L.bmoe_prepared_bytes(ctypes.byref(make_struct(act_dtype=bm.F32, d_model=1024, d_ff=4096,
@@ -507,9 +514,10 @@ def test_forward_kernel_names_of_the_widest_layer():
     buf = ctypes.create_string_buffer(1024)
     assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), buf, 1024) == 0
     names = buf.value.decode().split(",")
-    assert len(names) == n.value == 21
+    assert len(names) == n.value == 22
     assert names[:1] == ["prep"] and names.count("prep_lo") == 4 and names.count("prep_hi") == 4
-    assert names[9:] == ["route", "bucket", "bfly_in_hi", "bfly_in_lo", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+    assert names[9] == "prep_gate"
+    assert names[10:] == ["route", "bucket", "bfly_in_hi", "bfly_in_lo", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
                          "bfly_mid_lo_t", "gemm_down", "bfly_out_lo", "bfly_out_hi", "combine"]
     # truncation keeps the string terminated
     small = ctypes.create_string_buffer(8)
@@ -520,8 +528,8 @@ def test_forward_kernel_names_of_the_widest_layer():
     s = make_struct(d_model=2048, d_ff=8192, n_experts=256, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), buf, 1024) == 0
     names = buf.value.decode().split(",")
-    assert len(names) == n.value == 19
-    assert names[9:] == ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+    assert len(names) == n.value == 20
+    assert names[10:] == ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
                          "bfly_mid_lo_t", "gemm_down", "bfly_out", "combine"]
 
 
