@@ -108,6 +108,11 @@ def kernel_work(cfg):
         # the top four stages of nbfly butterflies over R rows
         return (2 * R * n * s + ang(n, 4, nbfly) + extra, 3 * R * n * 4 * nbfly, "hbm")
 
+    def gemm_tiles(din, dout):
+        # the matrix-core GEMM (prepared 2-bit code): output width a multiple
+        # of 256, contraction a multiple of 128
+        return cfg.act == "bf16" and dout % 256 == 0 and din % 128 == 0
+
     def gemm(din, dout):
         fl = 2 * R * din * dout
         by = R * din * s + R * dout * s + dout * din // 4
@@ -132,7 +137,15 @@ def kernel_work(cfg):
     else:
         Lf = int(math.log2(f))
         w["gemm_up"] = gemm(d, f)
-        if split(Lf):
+        if split(Lf) and Lf == 12 and gemm_tiles(d, f):
+            # width 4096: the up product's epilogue applies phi_up's low part
+            # (stages 0..7 of each row's expert, angles and flops added)
+            by, fl, _ = w["gemm_up"]
+            by, fl = by + ang(f, Lf - 4), fl + 3 * R * f * (Lf - 4)
+            w["gemm_up"] = (by, fl, bound(by, fl))
+            w["bfly_mid_hi"] = high(f, nbfly=2)
+            w["bfly_mid_lo_t"] = low(f)
+        elif split(Lf):
             w["bfly_mid_lo"] = low(f)
             w["bfly_mid_hi"] = high(f, nbfly=2)
             w["bfly_mid_lo_t"] = low(f)

@@ -240,6 +240,13 @@ PrepLayout prep_layout(const bmoe_layer* L) {
   return q;
 }
 
+// FFN layers of width d_ff = 4096 with a prepared up substrate: the up
+// product's epilogue applies the low part of phi_up (one pass fewer).
+bool up_low_in_gemm(const bmoe_layer* L, const PrepLayout& q) {
+  return L->d_ff && q.fp4[0] && q.lf_len[LF_UP] && gemm_fp4_low_epilogue_supported(L->d_ff) &&
+         use_split(L, ilog2(L->d_ff));
+}
+
 // Launches of the preparation: the substrate / fused-factor kernel when it has
 // work, then one builder per low-factor set.
 bool prep_has_sub(const PrepLayout& q) { return q.w_len[0] || q.w_len[1] || q.fac_len; }
@@ -511,7 +518,7 @@ static int forward_kernel_names(const bmoe_layer* L, const char* (&names)[kMaxFo
   } else {
     names[n++] = "gemm_up";
     if (use_split(L, ilog2(L->d_ff))) {
-      names[n++] = "bfly_mid_lo";
+      if (!up_low_in_gemm(L, prep_layout(L))) names[n++] = "bfly_mid_lo";
       names[n++] = "bfly_mid_hi";
       names[n++] = "bfly_mid_lo_t";
     } else {
@@ -656,14 +663,19 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
     yslot = bufU;
     phi_last = layer->phi[0];
   } else {
-    BMOE_LAUNCH(substrate_gemm(0, bufU, bufZ, f, d));
+    const bool up_low = up_low_in_gemm(layer, q);
+    if (up_low)
+      BMOE_LAUNCH(launch_gemm_fp4(GemmFp4Args{bufU, wbytes, bufZ, layer->w_scale[0], R, f, d, lowfac(LF_UP), offsets, N},
+                                  stream));
+    else
+      BMOE_LAUNCH(substrate_gemm(0, bufU, bufZ, f, d));
     const int gelu = layer->ffn_act == BMOE_ACT_GELU_ERF ? 1 : 0;
     BflyArgs bm{bufZ, bufZ, layer->phi[0], layer->theta[1], offsets, perm, nullptr, R, N, k, 0, gelu,
                 highfac(LF_UP), highfac(LF_DN)};
     if (use_split(layer, ilog2(f))) {
       // B(theta_dn)^T GELU(B(phi_up) h) = low^T(theta) high^T(theta) GELU high(phi) low(phi) h
       BflyArgs b1{bufZ, bufZ, layer->phi[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_UP)};
-      BMOE_LAUNCH(launch_bfly_split(b1, SPLIT_LOW, ilog2(f), stream));
+      if (!up_low) BMOE_LAUNCH(launch_bfly_split(b1, SPLIT_LOW, ilog2(f), stream));
       BMOE_LAUNCH(launch_bfly_split(bm, SPLIT_HIGH_MID, ilog2(f), stream));
       BflyArgs b3{bufZ, bufZ, layer->theta[1], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_DN)};
       BMOE_LAUNCH(launch_bfly_split(b3, SPLIT_LOW_T, ilog2(f), stream));

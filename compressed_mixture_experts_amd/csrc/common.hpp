@@ -227,7 +227,14 @@ struct GemmFp4Args {
   void* z;                  // [M][N] bf16
   float alpha;
   int32_t M, N, K;
+  // optional epilogue (N = 4096): the low part (stages 0..7) of each row's
+  // expert rotation applied to Z, rows bucketed by expert (offsets [E+1]),
+  // lowfac the prepared low-part factors of the rotation (width 4096)
+  const unsigned char* lowfac;
+  const int32_t* offsets;
+  int32_t n_experts;
 };
+bool gemm_fp4_low_epilogue_supported(int N);
 
 struct CombineArgs {
   const void* yp;           // [T*k][d] per-slot gated outputs

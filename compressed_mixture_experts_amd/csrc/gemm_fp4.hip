@@ -27,6 +27,7 @@
 // slice is reused by 4 row tiles and an activation tile by every column tile
 // while both sit in one XCD's L2 (contiguous logical tiles per XCD).
 #include "common.hpp"
+#include "lowpart.hpp"
 
 namespace bmoe {
 
@@ -58,7 +59,7 @@ __device__ __forceinline__ uint4 gf_fp4x8_to_bf16(uint32_t w) {
 // lane, each wave-wide load filling 4 consecutive rows.
 __device__ __forceinline__ int gf_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-template <int TN>
+template <int TN, bool EPI>
 __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) {
   constexpr int WN = TN / 4;                  // output columns per wave
   constexpr int OB = WN / 16;                 // 16-column blocks per wave
@@ -184,6 +185,11 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
   // the 16 lanes of one 16-byte read (one row) hit distinct banks; each row's
   // TN columns then go out as whole 16-byte pieces, one row per 32 lanes.
   static_assert(TN == 256, "one 512-byte row of output per 32 lanes");
+  // epilogue: bucket offsets of the experts (for each row's expert)
+  __shared__ int s_off[EPI ? 257 : 1];
+  __shared__ int s_exp[EPI ? GF_TM : 1];
+  if constexpr (EPI)
+    for (int i = tid; i <= a.n_experts; i += GF_THREADS) s_off[i] = a.offsets[i];
   uint2* st = reinterpret_cast<uint2*>(smem);
 #pragma unroll
   for (int i = 0; i < OB; ++i) {
@@ -198,6 +204,81 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
     }
   }
   __syncthreads();
+  if constexpr (EPI) {
+    // Low part (stages 0..7) of each row's expert rotation on the tile: the
+    // tile's 256 columns are chunk tn of width 4096, so G0 (16 x 16 blocks of
+    // consecutive columns) then G1 (16 x 16 blocks over u + 16 j) act inside
+    // it, each product rounded to bf16 as the separate low-part pass does.
+    // Wave w owns G0 blocks 4w .. 4w+3 and G1 blocks 4w .. 4w+3 for every
+    // 16-row block; a row block spanning several experts is multiplied once
+    // per expert and each row keeps its own expert's result.
+    using LC = LowMCfg<8>;
+    if (tid < GF_TM) {
+      // the expert of row m: s_off[e] <= m < s_off[e + 1] (s_off[n_experts] = M)
+      const int m = min(m0 + tid, a.M - 1);
+      int lo = 0, hi = a.n_experts;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= m) lo = mid; else hi = mid;
+      }
+      s_exp[tid] = lo;
+    }
+    __syncthreads();
+    // 8-byte unit u (columns 4u .. 4u+3) of tile row r
+    auto unit = [&](int r, int u) { return smem + r * TN + 4 * (u ^ ((r & 15) << 1)); };
+    const unsigned char* lfc = a.lowfac + size_t(tn) * LC::chunk_bytes;
+    uint2 f0[4], f1[4];
+    int cur = -1;
+    auto frags = [&](int e) {
+      if (e == cur) return;
+      const unsigned char* fc = lfc + size_t(e) * LC::per_expert;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) f0[bb] = *reinterpret_cast<const uint2*>(fc + (4 * wave + bb) * 512 + lane * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        f1[q] = *reinterpret_cast<const uint2*>(fc + LC::g0_bytes + (size_t(4 * wave + q) * 64 + lane) * 8);
+      cur = e;
+    };
+    for (int jb = 0; jb < MB; ++jb) {
+      const int r = 16 * jb + l16, er = s_exp[r];
+      const int e1 = __builtin_amdgcn_readfirstlane(s_exp[16 * jb + 15]);
+      for (int e = __builtin_amdgcn_readfirstlane(s_exp[16 * jb]); e <= e1; ++e) {
+        frags(e);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          uint16_t* p = unit(r, 4 * (4 * wave + bb) + g);
+          const f32x4_t d = lm_mfma16(f0[bb], lm_ld64(p));
+          if (er == e) lm_st64(p, lm_pack4(d));
+        }
+      }
+    }
+    __syncthreads();
+    for (int jb = 0; jb < MB; ++jb) {
+      const int r = 16 * jb + l16, er = s_exp[r];
+      const int e1 = __builtin_amdgcn_readfirstlane(s_exp[16 * jb + 15]);
+      for (int e = __builtin_amdgcn_readfirstlane(s_exp[16 * jb]); e <= e1; ++e) {
+        frags(e);
+        uint2 x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = lm_ld64(unit(r, wave + 4 * g1_slot<8>(g, i)));
+        f32x4_t d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+          const uint2 bq = (q < 2) ? make_uint2(__builtin_amdgcn_perm(x[1].x, x[0].x, sel), __builtin_amdgcn_perm(x[3].x, x[2].x, sel))
+                                   : make_uint2(__builtin_amdgcn_perm(x[1].y, x[0].y, sel), __builtin_amdgcn_perm(x[3].y, x[2].y, sel));
+          d[q] = lm_mfma16(f1[q], bq);
+        }
+        if (er == e) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            lm_st64(unit(r, wave + 4 * g1_slot<8>(g, i)),
+                    make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
+        }
+      }
+    }
+    __syncthreads();
+  }
   uint16_t* Z = reinterpret_cast<uint16_t*>(a.z);
   constexpr int CPR = TN / 8;  // 16-byte pieces per output row
 #pragma unroll
@@ -209,23 +290,31 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
   }
 }
 
-template <int TN>
+template <int TN, bool EPI>
 static hipError_t launch_gemm_fp4_tn(const GemmFp4Args& a, hipStream_t s) {
   const int ntn = a.N / TN, ntm = (a.M + GF_TM - 1) / GF_TM;
   const int ngrp = (ntm + GF_GRP - 1) / GF_GRP;
   const size_t lds = size_t(2) * GF_TILE * sizeof(uint16_t);
-  const hipError_t e = allow_dynamic_lds((const void*)gemm_fp4_kernel<TN>, lds);
+  const hipError_t e = allow_dynamic_lds((const void*)gemm_fp4_kernel<TN, EPI>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_fp4_kernel<TN>, dim3(ngrp * GF_GRP * ntn), dim3(GF_THREADS), lds, s, a);
+  hipLaunchKernelGGL((gemm_fp4_kernel<TN, EPI>), dim3(ngrp * GF_GRP * ntn), dim3(GF_THREADS), lds, s, a);
   return hipGetLastError();
 }
 
 bool gemm_fp4_supported(int N, int K) { return N % 256 == 0 && K % GF_KS == 0; }
 
+// the epilogue's low part covers chunks of 256 = one column tile: width 4096
+bool gemm_fp4_low_epilogue_supported(int N) { return N == 4096; }
+
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (!gemm_fp4_supported(a.N, a.K)) return hipErrorInvalidValue;
-  return launch_gemm_fp4_tn<256>(a, s);
+  if (a.lowfac) {
+    if (!gemm_fp4_low_epilogue_supported(a.N) || !a.offsets || a.n_experts < 1 || a.n_experts > 256)
+      return hipErrorInvalidValue;
+    return launch_gemm_fp4_tn<256, true>(a, s);
+  }
+  return launch_gemm_fp4_tn<256, false>(a, s);
 }
 
 }  // namespace bmoe

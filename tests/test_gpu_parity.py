@@ -346,6 +346,12 @@ SMALL_CASES = [
     # top-1: the output rotation's high part writes y directly; one token
     dict(d_model=1024, d_ff=4096, n_experts=4, top_k=1, tokens=100, act="bf16"),
     dict(d_model=2048, d_ff=1024, n_experts=8, top_k=2, tokens=1, act="bf16"),
+    # d_ff 4096: the up product's epilogue applies phi_up's low part; 64 experts
+    # with about 3 rows each, so most 16-row blocks hold several experts, and a
+    # ragged last row tile
+    dict(d_model=256, d_ff=4096, n_experts=64, top_k=2, tokens=101, act="bf16"),
+    # the same with a few long experts (row tiles inside one expert) and k = 1
+    dict(d_model=256, d_ff=4096, n_experts=3, top_k=1, tokens=700, act="bf16"),
 ]
 
 
