@@ -124,6 +124,11 @@ bmoe_status check_prepared(const bmoe_layer* L, size_t need) {
   return BMOE_OK;
 }
 
+// Tokens per router tile (and bucketing's slots per tile / k) for this layer.
+int32_t router_tile(int32_t T, const bmoe_layer* L) {
+  return route_tile_tokens(T, L->d_model, L->act_dtype == BMOE_BF16 ? ACT_BF16 : ACT_F32);
+}
+
 // Workspace layout (offsets in bytes, each 256-byte aligned).
 struct Plan {
   size_t offsets, perm, idx, gate, tslots, tgates, tstart, rec, bufU, bufZ, prep, total;
@@ -289,7 +294,7 @@ Plan make_plan(const bmoe_layer* L, int32_t T) {
   p.perm = take(size_t(R) * 4);
   p.idx = take(size_t(R) * 4);
   p.gate = take(size_t(R) * 4);
-  p.tiles = T > 0 ? int32_t((int64_t(T) + route_tile_tokens(T) - 1) / route_tile_tokens(T)) : 0;
+  p.tiles = T > 0 ? int32_t((int64_t(T) + router_tile(T, L) - 1) / router_tile(T, L)) : 0;
   p.tslots = take(size_t(R) * 4);
   p.tgates = take(size_t(R) * 4);
   p.tstart = take(size_t(p.tiles) * L->n_experts * 4);
@@ -352,7 +357,7 @@ bmoe_status run_route(const bmoe_layer* L, const void* x, int32_t T, int32_t* id
   ra.w_frag = gate_frags(L);
   BMOE_HIP(launch_route(ra, act, s));
   BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm),
-                nullptr, int32_t(p.R), L->n_experts, route_tile_tokens(T) * L->top_k, p.tiles, 0, 0};
+                nullptr, int32_t(p.R), L->n_experts, router_tile(T, L) * L->top_k, p.tiles, 0, 0};
   BMOE_HIP(launch_bucket(ba, s));
   return BMOE_OK;
 }
@@ -622,7 +627,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   TileRec* rec = p.n_rec ? at<TileRec>(workspace, p.rec) : nullptr;
   const int rec_rows = rec ? fused_tile_rows(R, N) : 0;
   BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, offsets, perm, rec, R, N,
-                route_tile_tokens(T) * k, p.tiles, rec_rows,
+                router_tile(T, layer) * k, p.tiles, rec_rows,
                 rec ? int32_t((R + rec_rows - 1) / rec_rows + N) : 0};
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
@@ -1162,7 +1167,7 @@ TrainFwdWs train_fwd_ws(const bmoe_layer* L, int32_t T) {
     o = align256(o + bytes);
     return at;
   };
-  w.tiles = T > 0 ? int32_t((int64_t(T) + route_tile_tokens(T) - 1) / route_tile_tokens(T)) : 0;
+  w.tiles = T > 0 ? int32_t((int64_t(T) + router_tile(T, L) - 1) / router_tile(T, L)) : 0;
   w.tslots = take(R * 4);
   w.tgates = take(R * 4);
   w.tstart = take(size_t(w.tiles) * L->n_experts * 4);
@@ -1301,7 +1306,7 @@ bmoe_status bmoe_forward_train(const bmoe_layer* layer, const void* x, int32_t T
                at<int32_t>(workspace, fw.tslots), at<float>(workspace, fw.tgates), at<int32_t>(workspace, fw.tstart)};
   BMOE_HIP(launch_route(ra, act, stream));
   BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, offsets, perm, nullptr, R, N,
-                route_tile_tokens(T) * k, fw.tiles, 0, 0};
+                router_tile(T, layer) * k, fw.tiles, 0, 0};
   BMOE_HIP(launch_bucket(ba, stream));
   BMOE_HIP(launch_invert_perm(perm, qpos, R, stream));
   BflyArgs bi{x, U, layer->theta[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0};

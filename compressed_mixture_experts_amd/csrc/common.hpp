@@ -102,7 +102,7 @@ struct RouteArgs {
   int32_t* topk_idx;        // [T][k]
   float* topk_gate;         // [T][k]
   int32_t T, d, N, k, renorm;
-  // per token tile b (route_tile_tokens(T) tokens, C = that times k slots):
+  // per token tile b (route_tile_tokens(T, d, act) tokens, C = that times k slots):
   int32_t* tile_slots;      // [R] slots b C .. b C + C - 1 ordered by expert, ascending within one
   float* tile_gates;        // [R] their gates, same order
   int32_t* tile_start;      // [G][N] position of expert e's first slot in tile b's list
@@ -243,7 +243,7 @@ struct CombineArgs {
 };
 
 // Tokens per router workgroup for T tokens (the bucketing reads its per-tile lists).
-int route_tile_tokens(int T);
+int route_tile_tokens(int T, int d, int act);
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s);
 hipError_t launch_bucket(const BucketArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);

@@ -404,11 +404,13 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
 // ----------------------------------------------------------------------------
 // Any width: bf16 tokens stream through two LDS steps of 64 contraction
 // indices (pipelined), fp32 tokens use one FMA chain per logit.
-template <int ACT, int BT>
-__global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
+template <int ACT, int BT, int NW>
+__global__ __launch_bounds__(64 * NW) void route_kernel(RouteArgs a) {
+  constexpr int NT = 64 * NW;                 // threads
+  constexpr int NI = 16 / NW;                 // expert blocks per wave (256 experts at most)
   constexpr int TB = BT / 16;                 // token blocks of 16
   constexpr int XCH = BT * (RT_BK / 8);       // 16-byte chunks of the token tile per step
-  constexpr int XPT = (XCH + RT_THREADS - 1) / RT_THREADS;
+  constexpr int XPT = (XCH + NT - 1) / NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sx = reinterpret_cast<uint16_t*>(smem);  // [2][BT][RT_XLD] token tile (bf16)
   float* sL = reinterpret_cast<float*>(smem);         // [BT][LS] logits (after the K loop)
@@ -425,19 +427,21 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   if constexpr (ACT == ACT_BF16) {
     const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
     const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w_gate);
-    // wave w owns expert blocks b = w + 4 i (i < 4) and all token blocks
-    f32x4_t acc[4][TB];
+    // wave w owns expert blocks b = w + NW i (i < NI) and all token blocks
+    f32x4_t acc[NI][TB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float wsq[4] = {0.f, 0.f, 0.f, 0.f};
+    float wsq[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wsq[i] = 0.f;
     float xsq[XPT];
 #pragma unroll
     for (int r = 0; r < XPT; ++r) xsq[r] = 0.f;
     // two register sets (compile-time indexed): gate-weight fragments and
     // token chunks two steps ahead
-    uint4 afr0[4][2], afr1[4][2];
+    uint4 afr0[NI][2], afr1[NI][2];
     uint4 xr0[XPT], xr1[XPT];
 
     // loads are unconditional (a branch around loads in the K loop makes every
@@ -446,17 +450,17 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     // gate fragments of block wave + 4 i, k-step st at abase[i] + st * astep:
     // one contiguous 1 KiB per wave from the fragment copy, else 16 rows of 64
     // bytes from W_g (blocks past the last read the last one)
-    const uint16_t* abase[4];
+    const uint16_t* abase[NI];
     const int astep = a.w_frag ? 512 : 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = min(wave + 4 * i, NB - 1);
+    for (int i = 0; i < NI; ++i) {
+      const int b = min(wave + NW * i, NB - 1);
       abase[i] = a.w_frag ? reinterpret_cast<const uint16_t*>(a.w_frag) + (size_t(b) * (d / 32) * 64 + lane) * 8
                           : wg + size_t(min(16 * b + (lane & 15), N - 1)) * d + 8 * (lane >> 4);
     }
-    auto load_a = [&](int k0, uint4 (&dst)[4][2]) {
+    auto load_a = [&](int k0, uint4 (&dst)[NI][2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           dst[i][s] = *reinterpret_cast<const uint4*>(abase[i] + (k0 / 32 + s) * astep);
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     auto load_x = [&](int k0, uint4 (&dst)[XPT]) {
 #pragma unroll
       for (int r = 0; r < XPT; ++r) {
-        const int c = min(tid + RT_THREADS * r, XCH - 1);
+        const int c = min(tid + NT * r, XCH - 1);
         const int tok = min(t0 + (c >> 3), a.T - 1);
         dst[r] = *reinterpret_cast<const uint4*>(xg + size_t(tok) * d + k0 + 8 * (c & 7));
       }
@@ -472,7 +476,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     auto store_x = [&](int buf, const uint4 (&src)[XPT]) {
 #pragma unroll
       for (int r = 0; r < XPT; ++r) {
-        const int c = tid + RT_THREADS * r;
+        const int c = tid + NT * r;
         if (c < XCH) {
           const uint4 v = src[r];
           const float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
@@ -485,7 +489,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     };
 
     const int nk = d / RT_BK;
-    auto step = [&](auto bufc, int kt, uint4 (&acur)[4][2], uint4 (&xcur)[XPT], uint4 (&xnext)[XPT]) {
+    auto step = [&](auto bufc, int kt, uint4 (&acur)[NI][2], uint4 (&xcur)[XPT], uint4 (&xnext)[XPT]) {
       constexpr int buf = decltype(bufc)::value;
       const uint16_t* xb = sx + buf * BT * RT_XLD;
 #pragma unroll
@@ -495,8 +499,8 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
         for (int j = 0; j < TB; ++j)
           bx[j] = *reinterpret_cast<const bf16x8_t*>(xb + (16 * j + (lane & 15)) * RT_XLD + 32 * s + 8 * (lane >> 4));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (wave + 4 * i < NB) {
+        for (int i = 0; i < NI; ++i) {
+          if (wave + NW * i < NB) {
             const uint4 av = acur[i][s];
             const float f[8] = {bf16lo(av.x), bf16hi(av.x), bf16lo(av.y), bf16hi(av.y),
                                 bf16lo(av.z), bf16hi(av.z), bf16lo(av.w), bf16hi(av.w)};
@@ -535,14 +539,14 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       v += __shfl_xor(v, 1, 64);
       v += __shfl_xor(v, 2, 64);
       v += __shfl_xor(v, 4, 64);
-      const int c = tid + RT_THREADS * r;
+      const int c = tid + NT * r;
       if ((tid & 7) == 0 && c < XCH) sh.X2[c >> 3] = v;
     }
     publish_wmax(wsq, sh.Wmax);
     // logits -> LDS (the token tile is dead after the last barrier)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = wave + 4 * i;
+    for (int i = 0; i < NI; ++i) {
+      const int b = wave + NW * i;
       if (b < NB) {
 #pragma unroll
         for (int j = 0; j < TB; ++j)
@@ -556,7 +560,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     // fp32 activations: one sequential FMA chain per (token, expert)
     const float* xf = reinterpret_cast<const float*>(a.x);
     const float* wf = reinterpret_cast<const float*>(a.w_gate);
-    for (int p = tid; p < BT * N; p += RT_THREADS) {
+    for (int p = tid; p < BT * N; p += NT) {
       const int tl = p / N, e = p - tl * N;
       const int tok = t0 + tl;
       float s = 0.f;
@@ -567,7 +571,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       }
       sL[tl * LS + e] = s;
     }
-    for (int tl = tid; tl < BT; tl += RT_THREADS) {
+    for (int tl = tid; tl < BT; tl += NT) {
       const int tok = t0 + tl;
       float s = 0.f;
       if (tok < a.T) {
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       sh.X2[tl] = s;
     }
     float wm = 0.f;
-    for (int e = tid; e < N; e += RT_THREADS) {
+    for (int e = tid; e < N; e += NT) {
       const float* wrow = wf + size_t(e) * d;
       float s = 0.f;
       for (int i = 0; i < d; ++i) s = fmaf(wrow[i], wrow[i], s);
@@ -588,9 +592,9 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     if (lane == 0) sh.Wmax[wave] = wm;
     depth = d;
   }
-  if (tid < 4) sh.Wmax[4 + tid] = 0.f;
-  route_decide<BT, RT_THREADS>(a, sh, sL, LS, depth, t0);
-  route_recheck_store<ACT, BT, RT_THREADS>(a, sh, sL, LS, t0);
+  if (tid < 8 - NW) sh.Wmax[NW + tid] = 0.f;  // entries of waves this workgroup does not have
+  route_decide<BT, NT>(a, sh, sL, LS, depth, t0);
+  route_recheck_store<ACT, BT, NT>(a, sh, sL, LS, t0);
 }
 
 // ----------------------------------------------------------------------------
@@ -856,6 +860,15 @@ static hipError_t launch_whole(const RouteArgs& a, hipStream_t s) {
   return route_launch(route_whole_kernel<BT, NK, NI>, (a.T + BT - 1) / BT, RW_THREADS, lds, s, a);
 }
 
+// the pipelined kernel with NW waves per workgroup of BT tokens
+template <int BT, int NW>
+static hipError_t launch_pipelined(const RouteArgs& a, int act, hipStream_t s) {
+  const size_t lds = route_lds_bytes<BT>(a.N, size_t(2) * BT * RT_XLD * sizeof(uint16_t));
+  const int grid = (a.T + BT - 1) / BT;
+  if (act == ACT_BF16) return route_launch(route_kernel<ACT_BF16, BT, NW>, grid, 64 * NW, lds, s, a);
+  return route_launch(route_kernel<ACT_F32, BT, NW>, grid, 64 * NW, lds, s, a);
+}
+
 // whole-tile kernel when the tile fits LDS and a wave's gate rows fit 128
 // registers per lane (width <= 1024 with one 16-expert block per wave, <= 512 with two)
 template <int BT>
@@ -880,20 +893,23 @@ static hipError_t launch_route_bt(const RouteArgs& a, int act, hipStream_t s) {
       }
     }
   }
-  const size_t lds = route_lds_bytes<BT>(a.N, size_t(2) * BT * RT_XLD * sizeof(uint16_t));
-  const int grid = (a.T + BT - 1) / BT;
-  if (act == ACT_BF16) return route_launch(route_kernel<ACT_BF16, BT>, grid, RT_THREADS, lds, s, a);
-  return route_launch(route_kernel<ACT_F32, BT>, grid, RT_THREADS, lds, s, a);
+  return launch_pipelined<BT, 4>(a, act, s);
 }
 
-// the largest token tile (64, 32 or 16 tokens) that still gives every CU a
-// workgroup: each workgroup reads the whole gate matrix once
-int route_tile_tokens(int T) { return T >= 64 * 256 ? 64 : T >= 32 * 256 ? 32 : 16; }
+// the largest token tile that still gives every CU a workgroup (each
+// workgroup reads the whole gate matrix once): 64, 32 or 16 tokens, or 128
+// (one eight-wave workgroup per CU, half the gate traffic) for bf16 tokens
+// too wide for the whole-tile kernel
+int route_tile_tokens(int T, int d, int act) {
+  if (act == ACT_BF16 && T >= 128 * 256 && size_t(64) * (d + 8) * sizeof(uint16_t) > RT_WHOLE_MAX) return 128;
+  return T >= 64 * 256 ? 64 : T >= 32 * 256 ? 32 : 16;
+}
 
 hipError_t launch_route(const RouteArgs& a, int act, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (!a.tile_slots || !a.tile_gates || !a.tile_start || a.N > 256) return hipErrorInvalidValue;
-  switch (route_tile_tokens(a.T)) {
+  switch (route_tile_tokens(a.T, a.d, act)) {
+    case 128: return launch_pipelined<128, 8>(a, act, s);
     case 64: return launch_route_bt<64>(a, act, s);
     case 32: return launch_route_bt<32>(a, act, s);
     default: return launch_route_bt<16>(a, act, s);

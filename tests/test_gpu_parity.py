@@ -237,6 +237,24 @@ def test_route_buckets_beyond_one_round():
     check_routing(inp, idx.cpu().numpy(), gate.cpu().numpy(), off.cpu().numpy(), slots.cpu().numpy())
 
 
+def test_route_wide_tokens_128_token_tiles():
+    # bf16 tokens too wide for the whole-tile router and at least 32768 of
+    # them: 128-token tiles of eight waves.  A ragged last tile, 100 experts
+    # (a partial last block of 16) and k = 3 (the decision over the logits in
+    # LDS); the gate matrix read from the prepared fragment copy and from W_g.
+    import torch
+    cfg = wl.small_config(d_model=1024, n_experts=100, top_k=3, tokens=32768 + 77, act="bf16", seed_index=13)
+    inp = wl.generate(cfg)
+    for prepared in (True, False):
+        layer = bm.Layer.from_inputs(inp)
+        if prepared:
+            layer.prepare()
+        log(f"route 128-token tiles, prepared={prepared}")
+        idx, gate, off, slots = layer.route(to_dev(inp.x, cfg.act), with_buckets=True)
+        torch.cuda.synchronize()
+        check_routing(inp, idx.cpu().numpy(), gate.cpu().numpy(), off.cpu().numpy(), slots.cpu().numpy())
+
+
 # ------------------------------------------------------------------ layer forward
 def check_forward(inp, y, idx, gate, tokens=None):
     """Compare the GPU layer output with the oracle on every token (the
