@@ -26,6 +26,12 @@
 // Tile order: groups of 4 row tiles sweep all column tiles, so a substrate
 // slice is reused by 4 row tiles and an activation tile by every column tile
 // while both sit in one XCD's L2 (contiguous logical tiles per XCD).
+//
+// The output tile leaves through LDS as whole 512-byte row runs.  With EPI
+// (N = 4096, rows bucketed by expert) it is first multiplied there by the low
+// part of each row's expert rotation: 256 columns are one chunk of that
+// rotation's low part (ButterflyMoE zh, technical summary §2.2: the stages
+// below bit 8 act within runs of 256 consecutive indices).
 #include "common.hpp"
 #include "lowpart.hpp"
 
