@@ -137,13 +137,18 @@ def kernel_work(cfg):
     else:
         Lf = int(math.log2(f))
         w["gemm_up"] = gemm(d, f)
-        if split(Lf) and Lf == 12 and gemm_tiles(d, f):
-            # width 4096: the up product's epilogue applies phi_up's low part
-            # (stages 0..7 of each row's expert, angles and flops added)
+        if split(Lf) and Lf in (12, 13) and gemm_tiles(d, f):
+            # widths 4096 / 8192: the up product's epilogue applies stages
+            # 0..7 of phi_up (each row's expert; angles and flops added); at
+            # 8192 the middle pass starts with stage 8
             by, fl, _ = w["gemm_up"]
-            by, fl = by + ang(f, Lf - 4), fl + 3 * R * f * (Lf - 4)
+            by, fl = by + ang(f, 8), fl + 3 * R * f * 8
             w["gemm_up"] = (by, fl, bound(by, fl))
-            w["bfly_mid_hi"] = high(f, nbfly=2)
+            if Lf == 12:
+                w["bfly_mid_hi"] = high(f, nbfly=2)
+            else:
+                by, fl, _ = high(f, nbfly=2, extra=ang(f, 1))
+                w["bfly_mid_hi"] = (by, fl + 3 * R * f, "hbm")
             w["bfly_mid_lo_t"] = low(f)
         elif split(Lf):
             w["bfly_mid_lo"] = low(f)

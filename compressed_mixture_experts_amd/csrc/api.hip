@@ -174,6 +174,7 @@ enum LowSet { LF_IN = 0, LF_OUT = 1, LF_UP = 2, LF_DN = 3, LF_SETS = 4 };
 struct PrepLayout {
   size_t w_off[2], w_len[2], fac_off, fac_len, total;
   size_t lf_off[LF_SETS], lf_len[LF_SETS];  // low-part block factors
+  bool lf_c256[LF_SETS];                     // ... for stages 0..7 on chunks of 256 (the up product's epilogue)
   size_t hf_off[LF_SETS], hf_len[LF_SETS];  // high-part block factors (one 16 x 16 block per column)
   size_t gf_off, gf_len;                     // gate matrix as MFMA fragments (last)
   bool fp4[2];
@@ -223,15 +224,19 @@ PrepLayout prep_layout(const bmoe_layer* L) {
     o = align256(o + q.w_len[m]);
   }
   q.fac_off = o;
+  // FFN layers of width d_ff = 4096 / 8192 with a prepared up substrate: the up
+  // product's epilogue applies stages 0..7 of phi_up (one pass fewer)
+  const bool up_epi = L->d_ff && q.fp4[0] && gemm_fp4_low_epilogue_supported(L->d_ff);
   for (int k = 0; k < LF_SETS; ++k) {
     const float* ang;
     int ln;
     bool tr;
     low_set(L, k, ang, ln, tr);
     if (!ln || !use_split(L, ln)) continue;
-    if (low_factor_bytes(ln)) {
+    q.lf_c256[k] = k == LF_UP && up_epi;
+    if (low_factor_bytes(ln, q.lf_c256[k])) {
       q.lf_off[k] = o;
-      q.lf_len[k] = low_factor_bytes(ln) * size_t(L->n_experts);
+      q.lf_len[k] = low_factor_bytes(ln, q.lf_c256[k]) * size_t(L->n_experts);
       o = align256(o + q.lf_len[k]);
     }
     if (high_factor_bytes(ln)) {
@@ -245,11 +250,10 @@ PrepLayout prep_layout(const bmoe_layer* L) {
   return q;
 }
 
-// FFN layers of width d_ff = 4096 with a prepared up substrate: the up
-// product's epilogue applies the low part of phi_up (one pass fewer).
+// The up product's epilogue applies stages 0..7 of phi_up (width 4096: its
+// whole low part; 8192: the FFN middle then starts with stage 8).
 bool up_low_in_gemm(const bmoe_layer* L, const PrepLayout& q) {
-  return L->d_ff && q.fp4[0] && q.lf_len[LF_UP] && gemm_fp4_low_epilogue_supported(L->d_ff) &&
-         use_split(L, ilog2(L->d_ff));
+  return L->d_ff && q.lf_len[LF_UP] && q.lf_c256[LF_UP];
 }
 
 // Launches of the preparation: the substrate / fused-factor kernel when it has
@@ -454,7 +458,8 @@ bmoe_status bmoe_prepare(const bmoe_layer* layer, void* prepared, size_t bytes, 
     int ln;
     bool tr;
     low_set(layer, k, ang, ln, tr);
-    if (q.lf_len[k]) BMOE_HIP(launch_low_factor_prep(ang, buf + q.lf_off[k], layer->n_experts, ln, tr, stream));
+    if (q.lf_len[k])
+      BMOE_HIP(launch_low_factor_prep(ang, buf + q.lf_off[k], layer->n_experts, ln, tr, q.lf_c256[k], stream));
     if (q.hf_len[k]) BMOE_HIP(launch_high_factor_prep(ang, buf + q.hf_off[k], layer->n_experts, ln, tr, stream));
   }
   return ok();
@@ -602,7 +607,7 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
       int ln;
       bool tr;
       low_set(layer, k, ang, ln, tr);
-      if (q.lf_len[k]) BMOE_LAUNCH(launch_low_factor_prep(ang, buf + q.lf_off[k], N, ln, tr, stream));
+      if (q.lf_len[k]) BMOE_LAUNCH(launch_low_factor_prep(ang, buf + q.lf_off[k], N, ln, tr, q.lf_c256[k], stream));
       if (q.hf_len[k]) BMOE_LAUNCH(launch_high_factor_prep(ang, buf + q.hf_off[k], N, ln, tr, stream));
     }
     if (q.gf_len) BMOE_LAUNCH(launch_gate_frag(layer->w_gate, buf + q.gf_off, N, d, stream));
@@ -681,7 +686,8 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
       // B(theta_dn)^T GELU(B(phi_up) h) = low^T(theta) high^T(theta) GELU high(phi) low(phi) h
       BflyArgs b1{bufZ, bufZ, layer->phi[0], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_UP)};
       if (!up_low) BMOE_LAUNCH(launch_bfly_split(b1, SPLIT_LOW, ilog2(f), stream));
-      BMOE_LAUNCH(launch_bfly_split(bm, SPLIT_HIGH_MID, ilog2(f), stream));
+      if (up_low && ilog2(f) == 13) BMOE_LAUNCH(launch_bfly_mid_pair(bm, stream));  // stage 8 first
+      else BMOE_LAUNCH(launch_bfly_split(bm, SPLIT_HIGH_MID, ilog2(f), stream));
       BflyArgs b3{bufZ, bufZ, layer->theta[1], nullptr, offsets, perm, nullptr, R, N, k, 0, 0, lowfac(LF_DN)};
       BMOE_LAUNCH(launch_bfly_split(b3, SPLIT_LOW_T, ilog2(f), stream));
     } else {

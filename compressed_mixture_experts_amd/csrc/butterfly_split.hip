@@ -235,19 +235,21 @@ __global__ __launch_bounds__(BF_THREADS) void lowm_kernel(BflyArgs a) {
 // Builder: one workgroup per (expert, chunk).  (cos, sin) of the chunk's S
 // stages into LDS, then one job per operand row: G0 (block b, output o), G1
 // (u, output slot).  Operand row o of M is M^T e_o (stages in decreasing order,
-// transposed rotations); of M^T it is M e_o.
-template <int S, bool TRANS>
+// transposed rotations); of M^T it is M e_o.  Width 2^L holds 2^(L-S) chunks:
+// 16 for the split passes (L = S + 4), 32 for the low part of width 8192 that
+// the up product's epilogue applies (S = 8).
+template <int S, bool TRANS, int L = S + 4>
 __global__ __launch_bounds__(BF_THREADS) void lowfac_kernel(const float* __restrict__ ang, unsigned char* __restrict__ out) {
   using C = LowMCfg<S>;
-  constexpr int L = S + 4, half = 1 << (L - 1), hc = 1 << (S - 1);
+  constexpr int half = 1 << (L - 1), hc = 1 << (S - 1), NCH = 1 << (L - S);
   constexpr int P0 = C::P0, B0 = C::B0;
   __shared__ float2 cs[S * hc];
   const int tid = threadIdx.x;
-  const int e = blockIdx.x / 16, c = blockIdx.x % 16;
+  const int e = blockIdx.x / NCH, c = blockIdx.x % NCH;
   const float* ae = ang + size_t(e) * L * half + size_t(c) * hc;
   for (int idx = tid; idx < S * hc; idx += BF_THREADS) cs[idx] = sincos_rev(ae[(idx / hc) * half + idx % hc]);
   __syncthreads();
-  unsigned char* fc = out + (size_t(e) * 16 + c) * C::chunk_bytes;
+  unsigned char* fc = out + (size_t(e) * NCH + c) * C::chunk_bytes;
   constexpr int J0 = C::NB0 * B0, J1 = P0 * 16;
   for (int job = tid; job < J0 + J1; job += BF_THREADS) {
     if (job < J0) {
@@ -286,7 +288,8 @@ __global__ __launch_bounds__(BF_THREADS) void lowfac_kernel(const float* __restr
   }
 }
 
-size_t low_factor_bytes(int log2n) {
+size_t low_factor_bytes(int log2n, bool chunks256) {
+  if (chunks256) return log2n == 13 ? 32 * LowMCfg<8>::chunk_bytes : log2n == 12 ? LowMCfg<8>::per_expert : 0;
   switch (log2n) {
     case 10: return LowMCfg<6>::per_expert;
     case 11: return LowMCfg<7>::per_expert;
@@ -296,17 +299,19 @@ size_t low_factor_bytes(int log2n) {
   }
 }
 
-template <int S>
+template <int S, int L = S + 4>
 static hipError_t launch_lowfac_S(const float* ang, unsigned char* out, int n_experts, bool trans, hipStream_t s) {
-  const dim3 grid(n_experts * 16), block(BF_THREADS);
-  if (trans) hipLaunchKernelGGL((lowfac_kernel<S, true>), grid, block, 0, s, ang, out);
-  else hipLaunchKernelGGL((lowfac_kernel<S, false>), grid, block, 0, s, ang, out);
+  const dim3 grid(n_experts << (L - S)), block(BF_THREADS);
+  if (trans) hipLaunchKernelGGL((lowfac_kernel<S, true, L>), grid, block, 0, s, ang, out);
+  else hipLaunchKernelGGL((lowfac_kernel<S, false, L>), grid, block, 0, s, ang, out);
   return hipGetLastError();
 }
 
 hipError_t launch_low_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n, bool trans,
-                                  hipStream_t s) {
+                                  bool chunks256, hipStream_t s) {
   if (n_experts <= 0) return hipSuccess;
+  if (chunks256 && log2n == 13) return launch_lowfac_S<8, 13>(ang, out, n_experts, trans, s);
+  if (chunks256 && log2n != 12) return hipErrorInvalidValue;
   switch (log2n) {
     case 10: return launch_lowfac_S<6>(ang, out, n_experts, trans, s);
     case 11: return launch_lowfac_S<7>(ang, out, n_experts, trans, s);
@@ -483,6 +488,143 @@ __global__ __launch_bounds__(HighMCfg<S>::NTH, 1024 / HighMCfg<S>::NTH) void hig
       }
     }
     __syncthreads();  // stored before the next sub-tile is written
+  }
+}
+
+// ---------------------------------------------------------------- FFN middle at width 8192, pair stage
+// After the up product's epilogue has applied stages 0..7 of B(phi_up) (its
+// 256-column tiles are the chunks of those stages), B(phi_up) still needs
+// stage 8 and stages 9..12.  Stage 8 rotates the pairs (v + 512 j, v + 256 +
+// 512 j) for v < 256, j < 16 (pair index 256 j + v), i.e. column v of the
+// S = 9 high part against column v + 256 at the same j; stages 9..12 are the
+// S = 9 high part's H_v' (v' < 512).  A workgroup takes 64 column pairs
+// (v0 + p, p < 64, and their partners) and keeps them interleaved in LDS, tile
+// column 2p + b holding column v' = 256 b + v0 + p, so a pair's stage-8
+// rotation acts on two neighbouring bf16 values of one lane (fp32 cos and sin
+// from a per-workgroup table).  The rest is the S = 9 middle: H(phi_up),
+// GELU, H(theta_dn)^T; the low part of B(theta_dn)^T follows as its own pass.
+struct HighPCfg {
+  static constexpr int PW = 64;                                 // column pairs per workgroup
+  static constexpr int VC = 2 * PW;                             // tile columns
+  static constexpr int NTH = 4 * VC;                            // 16 tile columns per wave
+  static constexpr int RT = 16;                                 // rows per sub-tile
+  static constexpr int RSB = 16 * VC * 2 + 8;                   // LDS bytes per row
+  static constexpr int CSP = PW + 2;                            // cos/sin table row stride (float2)
+  static constexpr size_t cs_off = size_t(RT) * RSB;            // table after the sub-tile (16-aligned)
+  static constexpr size_t lds_bytes = cs_off + size_t(16) * CSP * sizeof(float2);
+  static_assert(cs_off % 16 == 0, "table alignment");
+};
+
+__global__ __launch_bounds__(HighPCfg::NTH, 2) void highp_kernel(BflyArgs a) {
+  using C = HighPCfg;
+  constexpr int S = 9, L = 13, n = 1 << L, half = n / 2;
+  constexpr int VC = C::VC, NTH = C::NTH;
+  constexpr int ncb = 256 / C::PW;                 // workgroups per row tile
+  constexpr int JPR = 16 * (C::PW / 8);            // load jobs per row: (j, 8 pairs)
+  constexpr int JPT = C::RT * JPR / NTH;           // per thread
+  static_assert(C::RT * JPR % NTH == 0, "jobs per thread");
+  extern __shared__ __attribute__((aligned(16))) unsigned char hl[];
+  float2* cs = reinterpret_cast<float2*>(hl + C::cs_off);  // [16 j][CSP] stage-8 (cos, sin)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  int e, r0, nr, cb;
+  sp_find_tile_xcd(a.offsets, a.n_experts, ncb, e, r0, nr, cb);
+  if (e < 0) return;
+  const int v0 = cb * C::PW;
+
+  // factor fragments of tile column 16 w + c: v' = 256 (c & 1) + v0 + 8 w + (c >> 1)
+  uint2 fa0[16], fa1[16];
+  const unsigned char* f0 = a.fac + size_t(e) * HighMCfg<S>::per_expert;
+  const unsigned char* f1 = a.fac1 + size_t(e) * HighMCfg<S>::per_expert;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const size_t vc = size_t(256 * (c & 1) + v0 + 8 * wave + (c >> 1));
+    fa0[c] = *reinterpret_cast<const uint2*>(f0 + (vc * 64 + lane) * 8);
+    fa1[c] = *reinterpret_cast<const uint2*>(f1 + (vc * 64 + lane) * 8);
+  }
+  {
+    const float* a8 = a.ang0 + size_t(e) * L * half + size_t(8) * half;
+    for (int idx = tid; idx < 16 * C::PW; idx += NTH) {
+      const int j = idx / C::PW, p = idx % C::PW;
+      cs[j * C::CSP + p] = sincos_rev(a8[256 * j + v0 + p]);
+    }
+  }
+  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  for (int rs = 0; rs < nr; rs += C::RT) {
+    const int m = min(C::RT, nr - rs);
+    // job = (row, j, pairs 8 pg .. 8 pg + 7): the two 16-byte pieces of
+    // columns v0 + 8 pg .. and their partners; rows past the tile's last repeat it
+    uint4 v[2 * JPT];
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+      const int q = k * NTH + tid, row = min(rs + q / JPR, nr - 1), j = (q / 8) % 16, pg = q % 8;
+      const uint16_t* src = in + size_t(r0 + row) * n + (size_t(j) << S) + v0 + 8 * pg;
+      v[2 * k] = *reinterpret_cast<const uint4*>(src);
+      v[2 * k + 1] = *reinterpret_cast<const uint4*>(src + 256);
+    }
+    if (rs > 0) __syncthreads();  // the previous sub-tile has left LDS
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+      const int q = k * NTH + tid, row = q / JPR, j = (q / 8) % 16, pg = q % 8;
+      const uint4 x0 = v[2 * k], x1 = v[2 * k + 1];
+      uint16_t* d = reinterpret_cast<uint16_t*>(hl + row * C::RSB) + j * VC + 16 * pg;
+      lm_st64(d, make_uint2(__builtin_amdgcn_perm(x1.x, x0.x, 0x05040100u), __builtin_amdgcn_perm(x1.x, x0.x, 0x07060302u)));
+      lm_st64(d + 4, make_uint2(__builtin_amdgcn_perm(x1.y, x0.y, 0x05040100u), __builtin_amdgcn_perm(x1.y, x0.y, 0x07060302u)));
+      lm_st64(d + 8, make_uint2(__builtin_amdgcn_perm(x1.z, x0.z, 0x05040100u), __builtin_amdgcn_perm(x1.z, x0.z, 0x07060302u)));
+      lm_st64(d + 12, make_uint2(__builtin_amdgcn_perm(x1.w, x0.w, 0x05040100u), __builtin_amdgcn_perm(x1.w, x0.w, 0x07060302u)));
+    }
+    __syncthreads();
+    uint16_t* rp = reinterpret_cast<uint16_t*>(hl + l16 * C::RSB) + 16 * wave;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      // tile columns 16 w + 4 qd .. + 3: pairs 8 w + 2 qd and 8 w + 2 qd + 1, (b = 0, 1) each
+      uint2 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + (g + 4 * i) * VC + 4 * qd);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // stage 8: (lo, hi) -> (c lo - s hi, s lo + c hi)
+        const float4 t = *reinterpret_cast<const float4*>(cs + (g + 4 * i) * C::CSP + 8 * wave + 2 * qd);
+        const float a0 = __uint_as_float(r[i].x << 16), b0 = __uint_as_float(r[i].x & 0xffff0000u);
+        const float a1 = __uint_as_float(r[i].y << 16), b1 = __uint_as_float(r[i].y & 0xffff0000u);
+        r[i] = make_uint2(pack_bf16x2(t.x * a0 - t.y * b0, t.y * a0 + t.x * b0),
+                          pack_bf16x2(t.z * a1 - t.w * b1, t.w * a1 + t.z * b1));
+      }
+      f32x4_t d[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+        const uint2 bq = (q < 2) ? make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, sel), __builtin_amdgcn_perm(r[3].x, r[2].x, sel))
+                                 : make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, sel), __builtin_amdgcn_perm(r[3].y, r[2].y, sel));
+        d[q] = lm_mfma16(fa0[4 * qd + q], bq);
+        if (a.gelu) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[q][i] = gelu_erf(d[q][i]);
+        }
+        d[q] = lm_mfma16(fa1[4 * qd + q], lm_pack4(d[q]));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lm_st64(rp + (g + 4 * i) * VC + 4 * qd,
+                make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+      const int q = k * NTH + tid, row = q / JPR, j = (q / 8) % 16, pg = q % 8;
+      if (row < m) {
+        const uint16_t* sp = reinterpret_cast<const uint16_t*>(hl + row * C::RSB) + j * VC + 16 * pg;
+        const uint2 w0 = lm_ld64(sp), w1 = lm_ld64(sp + 4), w2 = lm_ld64(sp + 8), w3 = lm_ld64(sp + 12);
+        uint16_t* dst = out + size_t(r0 + rs + row) * n + (size_t(j) << S) + v0 + 8 * pg;
+        *reinterpret_cast<uint4*>(dst) =
+            make_uint4(__builtin_amdgcn_perm(w0.y, w0.x, 0x05040100u), __builtin_amdgcn_perm(w1.y, w1.x, 0x05040100u),
+                       __builtin_amdgcn_perm(w2.y, w2.x, 0x05040100u), __builtin_amdgcn_perm(w3.y, w3.x, 0x05040100u));
+        *reinterpret_cast<uint4*>(dst + 256) =
+            make_uint4(__builtin_amdgcn_perm(w0.y, w0.x, 0x07060302u), __builtin_amdgcn_perm(w1.y, w1.x, 0x07060302u),
+                       __builtin_amdgcn_perm(w2.y, w2.x, 0x07060302u), __builtin_amdgcn_perm(w3.y, w3.x, 0x07060302u));
+      }
+    }
   }
 }
 
@@ -774,6 +916,12 @@ hipError_t launch_bfly_full(const BflyArgs& a, bool out_mode, int log2n, hipStre
     case 11: return launch_full_S<7>(a, out_mode, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_bfly_mid_pair(const BflyArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (!a.fac || !a.fac1 || !a.ang0) return hipErrorInvalidValue;
+  return sp_launch(highp_kernel, sp_tiles(a) * (256 / HighPCfg::PW), HighPCfg::lds_bytes, a, s, HighPCfg::NTH);
 }
 
 bool bfly_split_supported(int log2n) { return log2n >= 10 && log2n <= 13; }

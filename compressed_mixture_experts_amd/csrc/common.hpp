@@ -227,9 +227,9 @@ struct GemmFp4Args {
   void* z;                  // [M][N] bf16
   float alpha;
   int32_t M, N, K;
-  // optional epilogue (N = 4096): the low part (stages 0..7) of each row's
-  // expert rotation applied to Z, rows bucketed by expert (offsets [E+1]),
-  // lowfac the prepared low-part factors of the rotation (width 4096)
+  // optional epilogue (N = 4096 or 8192): stages 0..7 of each row's expert
+  // rotation (on chunks of 256 columns) applied to Z, rows bucketed by expert
+  // (offsets [E+1]), lowfac the rotation's prepared factors for those chunks
   const unsigned char* lowfac;
   const int32_t* offsets;
   int32_t n_experts;
@@ -280,16 +280,22 @@ inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
 }
 hipError_t launch_gemm(const GemmArgs& a, int act, hipStream_t s);
 bool bfly_split_supported(int log2n);
-// Low-part block factors (matrix-core low part, widths 4096 and 8192): bytes per
-// expert, and the launch that builds them from one butterfly's angles.
-size_t low_factor_bytes(int log2n);
+// Low-part block factors (matrix-core low part, widths 1024 .. 8192): bytes per
+// expert, and the launch that builds them from one butterfly's angles.  The
+// low part is stages 0 .. L-5 on chunks of 2^(L-4), or with chunks256 (widths
+// 4096 and 8192, for the up product's epilogue) stages 0 .. 7 on chunks of 256.
+size_t low_factor_bytes(int log2n, bool chunks256 = false);
 hipError_t launch_low_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n,
-                                  bool trans, hipStream_t s);
+                                  bool trans, bool chunks256, hipStream_t s);
 // High-part block factors (one 16 x 16 block per column, widths 1024 .. 8192).
 size_t high_factor_bytes(int log2n);
 hipError_t launch_high_factor_prep(const float* ang, unsigned char* out, int n_experts, int log2n,
                                    bool trans, hipStream_t s);
 hipError_t launch_bfly_split(const BflyArgs& a, int part, int log2n, hipStream_t s);
+// FFN middle of width 8192 after the up product's epilogue (which applied
+// stages 0 .. 7 of ang0): stage 8 and the high part of ang0, GELU, the high
+// part of ang1 transposed (in place; fac / fac1 the two high parts' factors).
+hipError_t launch_bfly_mid_pair(const BflyArgs& a, hipStream_t s);
 // Whole butterfly of width 1024 or 2048 in one pass (butterfly_split.hip):
 // input rotation (out_mode false: gather token rows, high^T, low^T, rows in
 // bucket order) or output rotation (true: low, high, times the gate, per-slot

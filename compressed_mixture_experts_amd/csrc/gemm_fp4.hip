@@ -28,10 +28,10 @@
 // while both sit in one XCD's L2 (contiguous logical tiles per XCD).
 //
 // The output tile leaves through LDS as whole 512-byte row runs.  With EPI
-// (N = 4096, rows bucketed by expert) it is first multiplied there by the low
-// part of each row's expert rotation: 256 columns are one chunk of that
-// rotation's low part (ButterflyMoE zh, technical summary §2.2: the stages
-// below bit 8 act within runs of 256 consecutive indices).
+// (N = 4096 or 8192, rows bucketed by expert) it is first multiplied there by
+// stages 0..7 of each row's expert rotation: 256 columns are one chunk of
+// them (ButterflyMoE zh, technical summary §2.2: the stages below bit 8 act
+// within runs of 256 consecutive indices).
 #include "common.hpp"
 #include "lowpart.hpp"
 
@@ -211,8 +211,8 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
   }
   __syncthreads();
   if constexpr (EPI) {
-    // Low part (stages 0..7) of each row's expert rotation on the tile: the
-    // tile's 256 columns are chunk tn of width 4096, so G0 (16 x 16 blocks of
+    // Stages 0..7 of each row's expert rotation on the tile: the tile's 256
+    // columns are chunk tn of the width (4096 or 8192), so G0 (16 x 16 blocks of
     // consecutive columns) then G1 (16 x 16 blocks over u + 16 j) act inside
     // it, each product rounded to bf16 as the separate low-part pass does.
     // Wave w owns G0 blocks 4w .. 4w+3 and G1 blocks 4w .. 4w+3 for every
@@ -233,11 +233,12 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
     // 8-byte unit u (columns 4u .. 4u+3) of tile row r
     auto unit = [&](int r, int u) { return smem + r * TN + 4 * (u ^ ((r & 15) << 1)); };
     const unsigned char* lfc = a.lowfac + size_t(tn) * LC::chunk_bytes;
+    const size_t lf_expert = size_t(a.N / TN) * LC::chunk_bytes;  // one expert's chunks
     uint2 f0[4], f1[4];
     int cur = -1;
     auto frags = [&](int e) {
       if (e == cur) return;
-      const unsigned char* fc = lfc + size_t(e) * LC::per_expert;
+      const unsigned char* fc = lfc + size_t(e) * lf_expert;
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) f0[bb] = *reinterpret_cast<const uint2*>(fc + (4 * wave + bb) * 512 + lane * 8);
 #pragma unroll
@@ -309,8 +310,9 @@ static hipError_t launch_gemm_fp4_tn(const GemmFp4Args& a, hipStream_t s) {
 
 bool gemm_fp4_supported(int N, int K) { return N % 256 == 0 && K % GF_KS == 0; }
 
-// the epilogue's low part covers chunks of 256 = one column tile: width 4096
-bool gemm_fp4_low_epilogue_supported(int N) { return N == 4096; }
+// the epilogue's low part covers chunks of 256 = one column tile: stages 0..7
+// of widths 4096 and 8192
+bool gemm_fp4_low_epilogue_supported(int N) { return N == 4096 || N == 8192; }
 
 hipError_t launch_gemm_fp4(const GemmFp4Args& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;

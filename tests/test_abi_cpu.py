@@ -260,9 +260,13 @@ def test_prepared_bytes_layout():
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (4096 * 1024 // 4) + 2 * 64 * rot(1024)
                                                       + 2 * 64 * rot(4096) + gate(64, 1024))
     assert lo(4096) == 16 * 16384 and lo(8192) == 16 * (32768 + 16384)
+    # phi_up of width 8192, whose stages 0..7 the up product's epilogue applies:
+    # 32 chunks of 256 (16 blocks 16 x 16 of G0 + 16 of G1 each) instead
+    lo256 = 32 * (16 * 512 + 16 * 512)
     s = make_struct(d_model=2048, d_ff=8192, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_prepared_bytes(ctypes.byref(s)) == (2 * (8192 * 2048 // 4) + 2 * 64 * rot(2048)
-                                                      + 2 * 64 * rot(8192) + gate(64, 2048))
+                                                      + 64 * (hi(8192) + lo256) + 64 * rot(8192)
+                                                      + gate(64, 2048))
     # d_ff = 128: the up product (128 outputs) keeps the LDS-decoding GEMM, the down
     # one runs on the prepared codes
     s = make_struct(d_model=1024, d_ff=128, ffn_act=bm.ACT_GELU_ERF)
@@ -514,10 +518,12 @@ def test_forward_kernel_names_of_the_widest_layer():
     buf = ctypes.create_string_buffer(1024)
     assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), buf, 1024) == 0
     names = buf.value.decode().split(",")
-    assert len(names) == n.value == 22
+    # (the up product's epilogue applies stages 0..7 of phi_up, the middle
+    # pass stage 8 onwards: no separate low pass of phi_up)
+    assert len(names) == n.value == 21
     assert names[:1] == ["prep"] and names.count("prep_lo") == 4 and names.count("prep_hi") == 4
     assert names[9] == "prep_gate"
-    assert names[10:] == ["route", "bucket", "bfly_in_hi", "bfly_in_lo", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+    assert names[10:] == ["route", "bucket", "bfly_in_hi", "bfly_in_lo", "gemm_up", "bfly_mid_hi",
                          "bfly_mid_lo_t", "gemm_down", "bfly_out_lo", "bfly_out_hi", "combine"]
     # truncation keeps the string terminated
     small = ctypes.create_string_buffer(8)
@@ -528,8 +534,8 @@ def test_forward_kernel_names_of_the_widest_layer():
     s = make_struct(d_model=2048, d_ff=8192, n_experts=256, ffn_act=bm.ACT_GELU_ERF)
     assert L.bmoe_forward_kernels(ctypes.byref(s), ctypes.byref(n), buf, 1024) == 0
     names = buf.value.decode().split(",")
-    assert len(names) == n.value == 20
-    assert names[10:] == ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+    assert len(names) == n.value == 19
+    assert names[10:] == ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_hi",
                          "bfly_mid_lo_t", "gemm_down", "bfly_out", "combine"]
 
 

@@ -55,21 +55,27 @@ def test_large_ffn_kernel_bytes_and_flops():
     w = bench.kernel_work(_cfg("large_ffn_d2048_f8192_n256_top2_outliers"))
     T, d, f, N, k = 32768, 2048, 8192, 256, 2
     R = T * k
-    # each substrate product: rows in and out once, the shared 2-bit substrate once
+    # each substrate product: rows in and out once, the shared 2-bit substrate
+    # once; the up product's epilogue also applies stages 0..7 of phi_up (their
+    # angles, 3 flops per element per stage)
     up = (R * d * 2 + R * f * 2 + f * d // 4, 2 * R * d * f)
-    assert w["gemm_up"][:2] == up and w["gemm_down"][:2] == (R * f * 2 + R * d * 2 + d * f // 4, 2 * R * f * d)
+    epi = (N * 8 * (f // 2) * 4, 3 * R * f * 8)
+    assert w["gemm_up"][:2] == (up[0] + epi[0], up[1] + epi[1])
+    assert w["gemm_down"][:2] == (R * f * 2 + R * d * 2 + d * f // 4, 2 * R * f * d)
     assert up[1] == 2_199_023_255_552 and w["gemm_up"][2] == "mfma"
-    # low part of width 8192: one pass over the rows, angles of stages 0..8
-    assert w["bfly_mid_lo"][0] == 2 * R * f * 2 + N * 9 * (f // 2) * 4
-    # high part of the FFN middle: the top four stages of two butterflies
-    assert w["bfly_mid_hi"][0] == 2 * R * f * 2 + 2 * N * 4 * (f // 2) * 4
+    # low part of theta_dn (width 8192): one pass over the rows, angles of stages 0..8
+    assert w["bfly_mid_lo_t"][0] == 2 * R * f * 2 + N * 9 * (f // 2) * 4
+    # the FFN middle's pass: stage 8 of phi_up, then the top four stages of
+    # both butterflies
+    assert w["bfly_mid_hi"][0] == 2 * R * f * 2 + 2 * N * 4 * (f // 2) * 4 + N * (f // 2) * 4
+    assert w["bfly_mid_hi"][1] == 3 * R * f * 9
     # output rotation (width 2048, one pass): rows in and out, all 11 stages'
     # angles, slots and gates
     assert w["bfly_out"][0] == 2 * R * d * 2 + N * 11 * (d // 2) * 4 + 8 * R
     assert w["bfly_in"][0] == 2 * R * d * 2 + N * 11 * (d // 2) * 4 + 4 * R
     assert w["combine"][0] == R * d * 2 + T * d * 2 == 402_653_184
     assert w["route"][0] == T * d * 2 + N * d * 2 + 8 * R
-    names = ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_lo", "bfly_mid_hi",
+    names = ["route", "bucket", "bfly_in", "gemm_up", "bfly_mid_hi",
              "bfly_mid_lo_t", "gemm_down", "bfly_out", "combine"]
     assert set(w) == set(names)
 

@@ -361,6 +361,9 @@ SMALL_CASES = [
     dict(d_model=2048, n_experts=3, top_k=1, tokens=50, act="bf16"),
     dict(d_model=256, d_ff=4096, n_experts=5, top_k=2, tokens=120, act="bf16"),
     dict(d_model=128, d_ff=8192, n_experts=3, top_k=2, tokens=40, act="bf16"),
+    # width 8192 with the up product's epilogue: several 128-row product tiles
+    # spanning two experts, 64-row middle tiles with ragged tails
+    dict(d_model=256, d_ff=8192, n_experts=5, top_k=2, tokens=301, act="bf16"),
     # top-1: the output rotation's high part writes y directly; one token
     dict(d_model=1024, d_ff=4096, n_experts=4, top_k=1, tokens=100, act="bf16"),
     dict(d_model=2048, d_ff=1024, n_experts=8, top_k=2, tokens=1, act="bf16"),
