@@ -639,8 +639,12 @@ __global__ __launch_bounds__(HighPCfg::NTH, 2) void highp_kernel(BflyArgs a) {
 // column v, index j is element j 2^S + v, and the low part's chunks are
 // consecutive, so both parts use the split kernels' MFMA steps with those
 // strides.  Each wave keeps one pass's factor fragments in registers and
-// loads the next pass's before the barrier between them.
-constexpr int FM_RB = 16;      // rows per workgroup
+// loads the next pass's before the barrier between them; with many rows a
+// workgroup instead takes a tall tile of 64 rows of one expert, keeps all
+// three passes' fragments and runs the rows as four 16-row sub-tiles.
+constexpr int FM_RB = 16;      // rows per workgroup (per sub-tile of a tall tile)
+constexpr int FM_TALL = 64;    // rows per tall tile
+constexpr int FM_TALL_ROWS = 32768;  // tall tiles from this many rows: two 64-row workgroups per CU
 constexpr int FM_THREADS = 256;
 
 template <int S>
@@ -661,23 +665,24 @@ struct FullCfg {
 
 enum FullMode { FM_IN = 0, FM_OUT = 1 };
 
-template <int S, int MODE>
+template <int S, int MODE, int TR>
 __global__ __launch_bounds__(FM_THREADS, 2) void fullm_kernel(BflyArgs a) {
   using C = FullCfg<S>;
   using LC = LowMCfg<S>;
   using HC = HighMCfg<S>;
   constexpr int n = C::n, NV = C::NV, RS = C::RS;
   extern __shared__ __attribute__((aligned(16))) uint16_t tile[];  // [FM_RB][RS]
-  __shared__ size_t s_row[FM_RB];
-  __shared__ float s_g[FM_RB];
+  static_assert(TR % FM_RB == 0, "tile of whole sub-tiles");
+  __shared__ size_t s_row[TR];
+  __shared__ float s_g[TR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   int e, r0, nr, sub;
-  sp_find_tile_xcd<FM_RB>(a.offsets, a.n_experts, 1, e, r0, nr, sub);
+  sp_find_tile_xcd<TR>(a.offsets, a.n_experts, 1, e, r0, nr, sub);
   if (e < 0) return;
   const unsigned char* lowf = a.fac + size_t(e) * LC::per_expert;
   const unsigned char* highf = a.fac1 + size_t(e) * HC::per_expert;
-  if (tid < FM_RB) {
+  if (tid < TR) {
     const int q = r0 + min(tid, nr - 1);
     if constexpr (MODE == FM_IN) {
       s_row[tid] = size_t(a.perm[q] / a.top_k) * n;  // token row of x
@@ -718,8 +723,8 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fullm_kernel(BflyArgs a) {
     }
   };
   uint16_t* rowp = tile + l16 * RS;  // this lane's row in the MFMA steps
-  auto high_pass = [&]() {
-    const float gr = MODE == FM_OUT ? s_g[min(l16, nr - 1)] : 1.0f;
+  auto high_pass = [&](int rs, int m) {  // sub-tile rows rs .. rs + m - 1
+    const float gr = MODE == FM_OUT ? s_g[rs + min(l16, m - 1)] : 1.0f;
 #pragma unroll
     for (int gi = 0; gi < C::HC / 16; ++gi) {
       uint16_t* rp = rowp + 16 * (wave + 4 * gi);
@@ -776,59 +781,120 @@ __global__ __launch_bounds__(FM_THREADS, 2) void fullm_kernel(BflyArgs a) {
     }
   };
 
-  // first pass's fragments, then the rows (rows past the tile's last repeat it)
-  if constexpr (MODE == FM_IN) load_high(); else load_g0();
-  __syncthreads();  // row table
-  const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
-  {
-    constexpr int CPR = n / 8;  // 16-byte pieces per row
-#pragma unroll
-    for (int k0 = 0; k0 < C::PPT; k0 += 8) {
-      uint4 v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int p = (k0 + k) * FM_THREADS + tid, row = min(p / CPR, nr - 1), c = p % CPR;
-        const size_t src = MODE == FM_IN ? s_row[row] : size_t(r0 + row) * n;
-        v[k] = *reinterpret_cast<const uint4*>(in + src + 8 * c);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int p = (k0 + k) * FM_THREADS + tid, row = p / CPR, c = p % CPR;
-        uint16_t* d = tile + row * RS + 8 * c;
-        lm_st64(d, make_uint2(v[k].x, v[k].y));
-        lm_st64(d + 4, make_uint2(v[k].z, v[k].w));
+  if constexpr (TR == FM_RB) {
+    // first pass's fragments, then the rows (rows past the tile's last repeat it)
+    if constexpr (MODE == FM_IN) load_high(); else load_g0();
+    __syncthreads();  // row table
+    const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
+    {
+      constexpr int CPR = n / 8;  // 16-byte pieces per row
+  #pragma unroll
+      for (int k0 = 0; k0 < C::PPT; k0 += 8) {
+        uint4 v[8];
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int p = (k0 + k) * FM_THREADS + tid, row = min(p / CPR, nr - 1), c = p % CPR;
+          const size_t src = MODE == FM_IN ? s_row[row] : size_t(r0 + row) * n;
+          v[k] = *reinterpret_cast<const uint4*>(in + src + 8 * c);
+        }
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int p = (k0 + k) * FM_THREADS + tid, row = p / CPR, c = p % CPR;
+          uint16_t* d = tile + row * RS + 8 * c;
+          lm_st64(d, make_uint2(v[k].x, v[k].y));
+          lm_st64(d + 4, make_uint2(v[k].z, v[k].w));
+        }
       }
     }
-  }
-  if constexpr (MODE == FM_IN) load_g1(); else load_g1();
-  __syncthreads();
-  if constexpr (MODE == FM_IN) {
-    high_pass();   // high^T (transposed blocks)
-    load_g0();
+    if constexpr (MODE == FM_IN) load_g1(); else load_g1();
     __syncthreads();
-    g1_pass();     // G1^T
+    if constexpr (MODE == FM_IN) {
+      high_pass(0, nr);   // high^T (transposed blocks)
+      load_g0();
+      __syncthreads();
+      g1_pass();     // G1^T
+      __syncthreads();
+      g0_pass();     // G0^T
+    } else {
+      g0_pass();
+      load_high();
+      __syncthreads();
+      g1_pass();
+      __syncthreads();
+      high_pass(0, nr);   // high, times the gate
+    }
     __syncthreads();
-    g0_pass();     // G0^T
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    {
+      constexpr int CPR = n / 8;
+  #pragma unroll
+      for (int k = 0; k < C::PPT; ++k) {
+        const int p = k * FM_THREADS + tid, row = p / CPR, c = p % CPR;
+        if (row < nr) {
+          const uint16_t* sp = tile + row * RS + 8 * c;
+          const uint2 x0 = lm_ld64(sp), x1 = lm_ld64(sp + 4);
+          const size_t dst = MODE == FM_IN ? size_t(r0 + row) * n : s_row[row];
+          *reinterpret_cast<uint4*>(out + dst + 8 * c) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        }
+      }
+    }
   } else {
-    g0_pass();
+    // tall tiles (many rows): every pass's fragments stay in registers (192
+    // per lane at width 2048) while the workgroup runs its TR rows as
+    // sub-tiles of FM_RB, so each expert's factors cross from L2 once per TR
+    // rows instead of once per FM_RB
     load_high();
-    __syncthreads();
-    g1_pass();
-    __syncthreads();
-    high_pass();   // high, times the gate
-  }
-  __syncthreads();
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  {
-    constexpr int CPR = n / 8;
+    load_g0();
+    load_g1();
+    __syncthreads();  // row table
+    const uint16_t* in = reinterpret_cast<const uint16_t*>(a.in);
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    constexpr int CPR = n / 8;  // 16-byte pieces per row
+    for (int rs = 0; rs < nr; rs += FM_RB) {
+      const int m = min(FM_RB, nr - rs);
+      // the sub-tile's rows (rows past the tile's last repeat it)
 #pragma unroll
-    for (int k = 0; k < C::PPT; ++k) {
-      const int p = k * FM_THREADS + tid, row = p / CPR, c = p % CPR;
-      if (row < nr) {
-        const uint16_t* sp = tile + row * RS + 8 * c;
-        const uint2 x0 = lm_ld64(sp), x1 = lm_ld64(sp + 4);
-        const size_t dst = MODE == FM_IN ? size_t(r0 + row) * n : s_row[row];
-        *reinterpret_cast<uint4*>(out + dst + 8 * c) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      for (int k0 = 0; k0 < C::PPT; k0 += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int p = (k0 + k) * FM_THREADS + tid, row = min(rs + p / CPR, nr - 1), c = p % CPR;
+          const size_t src = MODE == FM_IN ? s_row[row] : size_t(r0 + row) * n;
+          v[k] = *reinterpret_cast<const uint4*>(in + src + 8 * c);
+        }
+        if (k0 == 0 && rs > 0) __syncthreads();  // the previous sub-tile has left LDS
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int p = (k0 + k) * FM_THREADS + tid, row = p / CPR, c = p % CPR;
+          uint16_t* d = tile + row * RS + 8 * c;
+          lm_st64(d, make_uint2(v[k].x, v[k].y));
+          lm_st64(d + 4, make_uint2(v[k].z, v[k].w));
+        }
+      }
+      __syncthreads();
+      if constexpr (MODE == FM_IN) {
+        high_pass(rs, m);  // high^T (transposed blocks)
+        __syncthreads();
+        g1_pass();         // G1^T
+        __syncthreads();
+        g0_pass();         // G0^T
+      } else {
+        g0_pass();
+        __syncthreads();
+        g1_pass();
+        __syncthreads();
+        high_pass(rs, m);  // high, times the gate
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < C::PPT; ++k) {
+        const int p = k * FM_THREADS + tid, row = p / CPR, c = p % CPR;
+        if (row < m) {
+          const uint16_t* sp = tile + row * RS + 8 * c;
+          const uint2 x0 = lm_ld64(sp), x1 = lm_ld64(sp + 4);
+          const size_t dst = MODE == FM_IN ? size_t(r0 + rs + row) * n : s_row[rs + row];
+          *reinterpret_cast<uint4*>(out + dst + 8 * c) = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        }
       }
     }
   }
@@ -898,13 +964,23 @@ static hipError_t launch_high_S(const BflyArgs& a, int mode, hipStream_t s) {
   }
 }
 
+template <int S, int TR>
+static hipError_t launch_full_ST(const BflyArgs& a, bool out_mode, hipStream_t s) {
+  const int grid = (a.rows + TR - 1) / TR + a.n_experts;
+  const size_t lds = FullCfg<S>::lds_bytes;
+  if (out_mode) return sp_launch(fullm_kernel<S, FM_OUT, TR>, grid, lds, a, s, FM_THREADS);
+  return sp_launch(fullm_kernel<S, FM_IN, TR>, grid, lds, a, s, FM_THREADS);
+}
+
+// Fewer rows keep 16-row workgroups, which overlap each pass's factor loads
+// with the previous pass (64-row tiles at 16384 rows of width 1024 leave too
+// few workgroups: 21.6 -> 28-31 us); many rows take tall tiles (65536 rows of
+// width 2048: 152-155 -> 141-143 us)
 template <int S>
 static hipError_t launch_full_S(const BflyArgs& a, bool out_mode, hipStream_t s) {
   if (!a.fac || !a.fac1) return hipErrorInvalidValue;
-  const int grid = (a.rows + FM_RB - 1) / FM_RB + a.n_experts;
-  const size_t lds = FullCfg<S>::lds_bytes;
-  if (out_mode) return sp_launch(fullm_kernel<S, FM_OUT>, grid, lds, a, s, FM_THREADS);
-  return sp_launch(fullm_kernel<S, FM_IN>, grid, lds, a, s, FM_THREADS);
+  if (a.rows >= FM_TALL_ROWS) return launch_full_ST<S, FM_TALL>(a, out_mode, s);
+  return launch_full_ST<S, FM_RB>(a, out_mode, s);
 }
 
 bool bfly_full_supported(int log2n) { return log2n == 10 || log2n == 11; }

@@ -106,6 +106,38 @@ def test_square_layer_single_rotation(n, T, part, side):
     _check(to_f64(y), want, chain, np.linalg.norm(x, axis=1), g, 8.0)
 
 
+@pytest.mark.parametrize("side", ["phi", "theta"])
+def test_square_layer_single_rotation_tall_tiles(side):
+    # 33000 routed rows at width 1024: the one-pass rotations take 64-row
+    # workgroups that keep every factor in registers over four 16-row
+    # sub-tiles (three experts: tiles of 64 with ragged ends)
+    n, T, N = 1024, 33000, 3
+    cfg = wl.small_config(d_model=n, n_experts=N, top_k=1, tokens=T, act="bf16", seed_index=640)
+    inp = wl.generate(cfg)
+    rng = np.random.default_rng(1024 + (7 if side == "theta" else 0))
+    ang = _angle_pattern(rng, N, n, "all", 0)
+    zero = np.zeros_like(ang)
+    inp.w_base[0] = np.eye(n, dtype=np.int8)
+    inp.theta[0], inp.phi[0] = (ang, zero) if side == "theta" else (zero, ang)
+    log(f"single rotation, tall tiles: square n={n} T={T} {side}")
+    _, _, (y, idx, gate) = run_layer(inp, prepared=True)
+    idx = idx.cpu().numpy()[:, 0]
+    g = gate.cpu().numpy().astype(np.float64)[:, 0]
+    x = ref.stored_to_f64(inp.x, "bf16")
+    R = ref.route(x, ref.stored_to_f64(inp.w_gate, "bf16"), 1)
+    assert np.array_equal(idx, R.idx[:, 0])
+    want = np.empty_like(x)
+    chain = np.empty_like(x)
+    for e in range(N):
+        t = np.nonzero(idx == e)[0]
+        if not len(t):
+            continue
+        tr = side == "theta"
+        want[t] = ref.butterfly_apply(ang[e], x[t].T, transpose=tr).T * R.gates[t, :1]
+        chain[t] = abs_butterfly_apply(ang[e], np.abs(x[t]).T, transpose=tr).T
+    _check(to_f64(y), want, chain, np.linalg.norm(x, axis=1), g, 8.0)
+
+
 # FFN middle: W_up = [I; 0] (d_ff x d), W_dn = [I 0] (d x d_ff), theta_up = phi_dn = 0,
 # no activation: y_t = g_t [I 0] B(theta_dn)^T B(phi_up) [x_t; 0]
 FFN = [(256, 1024, 200), (256, 4096, 120), (256, 8192, 80)]
