@@ -158,7 +158,10 @@ bmoe_status bmoe_workspace_size(const bmoe_layer* layer, int32_t T, size_t* byte
  *    two-bit code; and
  *    for every rotation of width n = 2^L in 1024..8192, per expert, its stages
  *    0..L-5 as block factors per chunk of 2^(L-4) indices and its top four
- *    stages as one 16 x 16 block per column (bf16);
+ *    stages as one 16 x 16 block per column (bf16) -- except the FFN's
+ *    phi_up of width 8192 when the up product runs on the two-bit code: its
+ *    stages 0..7 per chunk of 256 indices (the up product applies them to
+ *    its output; stage 8 is taken from the angles);
  *  - every bf16 layer, last: the gate matrix W_g reordered for the router's
  *    matrix-core products, ceil(n_experts / 16) * 16 * d_model * 2 bytes
  *    (per block of 16 experts and contraction step of 32, the 16-byte pieces

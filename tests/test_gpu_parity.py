@@ -364,6 +364,7 @@ SMALL_CASES = [
     # width 8192 with the up product's epilogue: several 128-row product tiles
     # spanning two experts, 64-row middle tiles with ragged tails
     dict(d_model=256, d_ff=8192, n_experts=5, top_k=2, tokens=301, act="bf16"),
+    dict(d_model=256, d_ff=8192, n_experts=1, top_k=1, tokens=1, act="bf16"),
     # top-1: the output rotation's high part writes y directly; one token
     dict(d_model=1024, d_ff=4096, n_experts=4, top_k=1, tokens=100, act="bf16"),
     dict(d_model=2048, d_ff=1024, n_experts=8, top_k=2, tokens=1, act="bf16"),

@@ -106,15 +106,15 @@ def test_square_layer_single_rotation(n, T, part, side):
     _check(to_f64(y), want, chain, np.linalg.norm(x, axis=1), g, 8.0)
 
 
-@pytest.mark.parametrize("side", ["phi", "theta"])
-def test_square_layer_single_rotation_tall_tiles(side):
-    # 33000 routed rows at width 1024: the one-pass rotations take 64-row
-    # workgroups that keep every factor in registers over four 16-row
+@pytest.mark.parametrize("n,side", [(1024, "phi"), (1024, "theta"), (2048, "phi"), (2048, "theta")])
+def test_square_layer_single_rotation_tall_tiles(n, side):
+    # 33000 routed rows at widths 1024 / 2048: the one-pass rotations take
+    # 64-row workgroups that keep every factor in registers over four 16-row
     # sub-tiles (three experts: tiles of 64 with ragged ends)
-    n, T, N = 1024, 33000, 3
+    T, N = 33000, 3
     cfg = wl.small_config(d_model=n, n_experts=N, top_k=1, tokens=T, act="bf16", seed_index=640)
     inp = wl.generate(cfg)
-    rng = np.random.default_rng(1024 + (7 if side == "theta" else 0))
+    rng = np.random.default_rng(n + (7 if side == "theta" else 0))
     ang = _angle_pattern(rng, N, n, "all", 0)
     zero = np.zeros_like(ang)
     inp.w_base[0] = np.eye(n, dtype=np.int8)
