@@ -164,6 +164,10 @@ def test_expert_angle_gradients_compose():
     torch.cuda.synchronize()
     dWr = ref.substrate_weight_grad(U16.float().cpu().numpy().astype(np.float64),
                                     dZ16.float().cpu().numpy().astype(np.float64), alpha)
+    # elementwise against the sum's magnitude |alpha| sqrt(sum_r dZ^2 U^2) (fp32 accumulation)
+    u64, dz64 = (t.float().cpu().numpy().astype(np.float64) for t in (U16, dZ16))
+    wscale = abs(alpha) * np.sqrt((dz64 ** 2).T @ (u64 ** 2))
+    assert np.all(np.abs(dW.cpu().numpy() - dWr) <= 1e-5 * wscale + 1e-30)
     assert np.linalg.norm(dW.cpu().numpy() - dWr) <= 1e-5 * np.linalg.norm(dWr)
     dx, dth, dph = (t.cpu().numpy().astype(np.float64) for t in (dx, dth, dph))
     W64 = W.astype(np.float64)

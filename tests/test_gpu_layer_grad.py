@@ -135,6 +135,13 @@ def test_layer_backward_composed_from_the_abi():
     tot = dx.cpu().numpy().astype(np.float64) + dx_r.cpu().numpy()
     assert row_rel_err(tot, want["x"] + rdx).max() <= 1e-4
     assert np.linalg.norm(dwg.cpu().numpy() - rdwg) <= 1e-4 * np.linalg.norm(rdwg)
+    # elementwise, against |ref| + the expert row's RMS (the gate gradients fed
+    # in carry their own 1e-4 relative error)
+    gw = dwg.cpu().numpy().astype(np.float64)
+    rms = np.sqrt(np.mean(rdwg ** 2, axis=1, keepdims=True))
+    err = np.abs(gw - rdwg) / (np.abs(rdwg) + rms)
+    log(f"  dW_g elementwise: max {err.max():.2e}")
+    assert err.max() <= 3e-4
 
 
 @pytest.mark.parametrize("T,d,N,k,renorm,act", [
