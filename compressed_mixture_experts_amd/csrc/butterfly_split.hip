@@ -508,7 +508,13 @@ struct HighPCfg {
   static constexpr int VC = 2 * PW;                             // tile columns
   static constexpr int NTH = 4 * VC;                            // 16 tile columns per wave
   static constexpr int RT = 16;                                 // rows per sub-tile
-  static constexpr int RSB = 16 * VC * 2 + 8;                   // LDS bytes per row
+  // LDS layout of a tile row: the 16 j's at a stride of JS bf16 (264 bytes,
+  // two banks apart modulo 64 banks), rows RSB bytes apart (4 banks apart), so
+  // the 8-byte accesses of the load, product and store phases are free of bank
+  // conflicts (lanes of a 32-lane pass: 8 column groups x 4 j's, or 16 rows x 2 j's)
+  static constexpr int JS = VC + 4;
+  static constexpr int RSB = 16 * JS * 2 + 144;
+  static_assert(JS * 2 % 256 == 8 && RSB % 256 == 16, "bank spread");
   static constexpr int CSP = PW + 2;                            // cos/sin table row stride (float2)
   static constexpr size_t cs_off = size_t(RT) * RSB;            // table after the sub-tile (16-aligned)
   static constexpr size_t lds_bytes = cs_off + size_t(16) * CSP * sizeof(float2);
@@ -520,7 +526,8 @@ __global__ __launch_bounds__(HighPCfg::NTH, 2) void highp_kernel(BflyArgs a) {
   constexpr int S = 9, L = 13, n = 1 << L, half = n / 2;
   constexpr int VC = C::VC, NTH = C::NTH;
   constexpr int ncb = 256 / C::PW;                 // workgroups per row tile
-  constexpr int JPR = 16 * (C::PW / 8);            // load jobs per row: (j, 8 pairs)
+  constexpr int PGN = C::PW / 8;                    // groups of 8 pairs per (row, j)
+  constexpr int JPR = 16 * PGN;                     // load jobs per row: (j, 8 pairs)
   constexpr int JPT = C::RT * JPR / NTH;           // per thread
   static_assert(C::RT * JPR % NTH == 0, "jobs per thread");
   extern __shared__ __attribute__((aligned(16))) unsigned char hl[];
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(HighPCfg::NTH, 2) void highp_kernel(BflyArgs a) {
     uint4 v[2 * JPT];
 #pragma unroll
     for (int k = 0; k < JPT; ++k) {
-      const int q = k * NTH + tid, row = min(rs + q / JPR, nr - 1), j = (q / 8) % 16, pg = q % 8;
+      const int q = k * NTH + tid, row = min(rs + q / JPR, nr - 1), j = (q / PGN) % 16, pg = q % PGN;
       const uint16_t* src = in + size_t(r0 + row) * n + (size_t(j) << S) + v0 + 8 * pg;
       v[2 * k] = *reinterpret_cast<const uint4*>(src);
       v[2 * k + 1] = *reinterpret_cast<const uint4*>(src + 256);
@@ -566,9 +573,9 @@ __global__ __launch_bounds__(HighPCfg::NTH, 2) void highp_kernel(BflyArgs a) {
     if (rs > 0) __syncthreads();  // the previous sub-tile has left LDS
 #pragma unroll
     for (int k = 0; k < JPT; ++k) {
-      const int q = k * NTH + tid, row = q / JPR, j = (q / 8) % 16, pg = q % 8;
+      const int q = k * NTH + tid, row = q / JPR, j = (q / PGN) % 16, pg = q % PGN;
       const uint4 x0 = v[2 * k], x1 = v[2 * k + 1];
-      uint16_t* d = reinterpret_cast<uint16_t*>(hl + row * C::RSB) + j * VC + 16 * pg;
+      uint16_t* d = reinterpret_cast<uint16_t*>(hl + row * C::RSB) + j * C::JS + 16 * pg;
       lm_st64(d, make_uint2(__builtin_amdgcn_perm(x1.x, x0.x, 0x05040100u), __builtin_amdgcn_perm(x1.x, x0.x, 0x07060302u)));
       lm_st64(d + 4, make_uint2(__builtin_amdgcn_perm(x1.y, x0.y, 0x05040100u), __builtin_amdgcn_perm(x1.y, x0.y, 0x07060302u)));
       lm_st64(d + 8, make_uint2(__builtin_amdgcn_perm(x1.z, x0.z, 0x05040100u), __builtin_amdgcn_perm(x1.z, x0.z, 0x07060302u)));
@@ -581,7 +588,7 @@ __global__ __launch_bounds__(HighPCfg::NTH, 2) void highp_kernel(BflyArgs a) {
       // tile columns 16 w + 4 qd .. + 3: pairs 8 w + 2 qd and 8 w + 2 qd + 1, (b = 0, 1) each
       uint2 r[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + (g + 4 * i) * VC + 4 * qd);
+      for (int i = 0; i < 4; ++i) r[i] = lm_ld64(rp + (g + 4 * i) * C::JS + 4 * qd);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // stage 8: (lo, hi) -> (c lo - s hi, s lo + c hi)
@@ -606,15 +613,15 @@ __global__ __launch_bounds__(HighPCfg::NTH, 2) void highp_kernel(BflyArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        lm_st64(rp + (g + 4 * i) * VC + 4 * qd,
+        lm_st64(rp + (g + 4 * i) * C::JS + 4 * qd,
                 make_uint2(pack_bf16x2(d[0][i], d[1][i]), pack_bf16x2(d[2][i], d[3][i])));
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < JPT; ++k) {
-      const int q = k * NTH + tid, row = q / JPR, j = (q / 8) % 16, pg = q % 8;
+      const int q = k * NTH + tid, row = q / JPR, j = (q / PGN) % 16, pg = q % PGN;
       if (row < m) {
-        const uint16_t* sp = reinterpret_cast<const uint16_t*>(hl + row * C::RSB) + j * VC + 16 * pg;
+        const uint16_t* sp = reinterpret_cast<const uint16_t*>(hl + row * C::RSB) + j * C::JS + 16 * pg;
         const uint2 w0 = lm_ld64(sp), w1 = lm_ld64(sp + 4), w2 = lm_ld64(sp + 8), w3 = lm_ld64(sp + 12);
         uint16_t* dst = out + size_t(r0 + rs + row) * n + (size_t(j) << S) + v0 + 8 * pg;
         *reinterpret_cast<uint4*>(dst) =
