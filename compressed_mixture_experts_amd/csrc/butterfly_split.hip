@@ -510,8 +510,9 @@ struct HighPCfg {
   static constexpr int RT = 16;                                 // rows per sub-tile
   // LDS layout of a tile row: the 16 j's at a stride of JS bf16 (264 bytes,
   // two banks apart modulo 64 banks), rows RSB bytes apart (4 banks apart), so
-  // the 8-byte accesses of the load, product and store phases are free of bank
-  // conflicts (lanes of a 32-lane pass: 8 column groups x 4 j's, or 16 rows x 2 j's)
+  // that the 32 lanes of one pass of an 8-byte access (8 column groups x 4 j's
+  // in the load and store phases, 16 rows x 2 j's in the product phase) fall
+  // on distinct banks; with 256-byte j-runs they all shared one bank pair
   static constexpr int JS = VC + 4;
   static constexpr int RSB = 16 * JS * 2 + 144;
   static_assert(JS * 2 % 256 == 8 && RSB % 256 == 16, "bank spread");
