@@ -69,9 +69,27 @@ __device__ __forceinline__ float erf_as(float z) {
   return copysignf(fmaf(-q * t, e, 1.0f), z);
 }
 
-// GELU with the exact (erf) form: h * (1 + erf(h / sqrt 2)) / 2
+// GELU with the exact (erf) form, h Phi(h) = h (1 + erf(h / sqrt 2)) / 2,
+// written as relu(h) - |h| Q(|h|) with Q(a) = Phi(-a) the upper normal tail
+// (no cancellation on either side).  log2 Q is smooth, so it is a degree-7
+// polynomial in a = min(|h|, 5.75) (a minimax fit of log2 Q on [0, 5.75],
+// printed by gelu_tail_fit.py beside this file; Q's relative error is below
+// 6e-6 in fp32, GELU's absolute error below 1e-6 |h| + 1e-6).  Past 5.75 the
+// tail term is under 3e-8 and is kept at Q(5.75) * 5.75.  One exp2 and seven
+// FMAs instead of a reciprocal, an exp2 and the A&S polynomial; the FFN middle
+// passes are bound by this arithmetic.  NaN and +inf pass through.
 __device__ __forceinline__ float gelu_erf(float h) {
-  return h * 0.5f * (1.0f + erf_as(h * 0.70710678118654752f));
+  const float a = fminf(fabsf(h), 5.75f);
+  float p = -1.825512868e-06f;
+  p = fmaf(p, a, 6.144048530e-05f);
+  p = fmaf(p, a, -9.294924675e-04f);
+  p = fmaf(p, a, 8.504617028e-03f);
+  p = fmaf(p, a, -5.395488441e-02f);
+  p = fmaf(p, a, -4.584681690e-01f);
+  p = fmaf(p, a, -1.151250005e+00f);
+  p = fmaf(p, a, -9.999953508e-01f);
+  const float q = __builtin_amdgcn_exp2f(p);
+  return fmaf(0.5f, h + fabsf(h), -a * q);
 }
 
 // cos and sin with the hardware transcendental unit (angle in revolutions)
