@@ -79,7 +79,7 @@ __device__ __forceinline__ float erf_as(float z) {
 // FMAs instead of a reciprocal, an exp2 and the A&S polynomial; the FFN middle
 // passes are bound by this arithmetic.  NaN and +inf pass through.
 __device__ __forceinline__ float gelu_erf(float h) {
-  const float a = fminf(fabsf(h), 5.75f);
+  const float a = __builtin_amdgcn_fmed3f(fabsf(h), 0.0f, 5.75f);  // min(|h|, 5.75), one instruction
   float p = -1.825512868e-06f;
   p = fmaf(p, a, 6.144048530e-05f);
   p = fmaf(p, a, -9.294924675e-04f);

@@ -3,7 +3,7 @@
 GELU(h) = h Phi(h) = relu(h) - |h| Q(|h|), with Q(a) = Phi(-a) = erfc(a / sqrt 2) / 2
 the upper normal tail.  log2 Q(a) is smooth on [0, A] (A = 5.75, where Q is about
 4.5e-9), so the kernels evaluate a polynomial P(a) of degree 7 there and take
-Q = exp2(P(min(|h|, A))): one hardware exp2, seven FMAs, no reciprocal.
+Q = exp2(P(min(|h|, A))): one hardware exp2, seven FMAs, no reciprocal (the clamp is one med3).
 
 The polynomial is a minimax fit of log2 Q in the absolute sense (relative error
 of Q), by Lawson's iteratively reweighted least squares over Chebyshev nodes,

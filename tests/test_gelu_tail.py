@@ -20,7 +20,7 @@ def header_constants():
     src = open(os.path.join(CSRC, "butterfly_impl.hpp")).read()
     body = src[src.index("float gelu_erf(float h)"):]
     body = body[:body.index("\n}")]
-    clamp = float(re.search(r"fminf\(fabsf\(h\), ([0-9.eE+-]+)f\)", body).group(1))
+    clamp = float(re.search(r"fmed3f\(fabsf\(h\), 0\.0f, ([0-9.eE+-]+)f\)", body).group(1))
     lead = float(re.search(r"float p = ([0-9.eE+-]+)f;", body).group(1))
     rest = [float(v) for v in re.findall(r"p = fmaf\(p, a, ([0-9.eE+-]+)f\);", body)]
     return clamp, np.array([lead] + rest, dtype=np.float32)[::-1]   # ascending powers
