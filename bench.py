@@ -737,9 +737,20 @@ def bm_kernel_sha(kernel: str, cfg) -> str:
 
 
 def _sha(src: str) -> str:
+    """Hash of a kernel source and the local headers it includes, transitively."""
     import hashlib
-    p = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc", src)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    import re
+    csrc = os.path.join(ROOT, "compressed_mixture_experts_amd", "csrc")
+    seen, todo, h = set(), [src], hashlib.sha256()
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.add(f)
+        text = open(os.path.join(csrc, f), "rb").read()
+        h.update(f.encode() + b"\0" + text)
+        todo += [m.decode() for m in re.findall(rb'#include "([^"]+)"', text)]
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

@@ -194,31 +194,43 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
   // epilogue: bucket offsets of the experts (for each row's expert)
   __shared__ int s_off[EPI ? 257 : 1];
   __shared__ int s_exp[EPI ? GF_TM : 1];
-  if constexpr (EPI)
-    for (int i = tid; i <= a.n_experts; i += GF_THREADS) s_off[i] = a.offsets[i];
   uint2* st = reinterpret_cast<uint2*>(smem);
+  // the lane's 4 consecutive output columns of row 16 j + l16 in its column
+  // block i, as bf16, and their place in the staged tile
+  uint2 ob[OB][MB];
 #pragma unroll
-  for (int i = 0; i < OB; ++i) {
-    const int u = wave * (WN / 4) + 4 * i + g;
+  for (int i = 0; i < OB; ++i)
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-      const int r = 16 * j + l16;
-      uint2 o;
-      o.x = pack_bf16x2(a.alpha * acc[i][j][0], a.alpha * acc[i][j][1]);
-      o.y = pack_bf16x2(a.alpha * acc[i][j][2], a.alpha * acc[i][j][3]);
-      st[r * (TN / 4) + (u ^ ((r & 15) << 1))] = o;
+      ob[i][j].x = pack_bf16x2(a.alpha * acc[i][j][0], a.alpha * acc[i][j][1]);
+      ob[i][j].y = pack_bf16x2(a.alpha * acc[i][j][2], a.alpha * acc[i][j][3]);
     }
-  }
-  __syncthreads();
-  if constexpr (EPI) {
+  auto stage = [&](int i, int j, uint2 o) {
+    const int r = 16 * j + l16, u = wave * (WN / 4) + 4 * i + g;
+    st[r * (TN / 4) + (u ^ ((r & 15) << 1))] = o;
+  };
+  if constexpr (!EPI) {
+#pragma unroll
+    for (int i = 0; i < OB; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j) stage(i, j, ob[i][j]);
+    __syncthreads();
+  } else {
     // Stages 0..7 of each row's expert rotation on the tile: the tile's 256
     // columns are chunk tn of the width (4096 or 8192), so G0 (16 x 16 blocks of
     // consecutive columns) then G1 (16 x 16 blocks over u + 16 j) act inside
     // it, each product rounded to bf16 as the separate low-part pass does.
     // Wave w owns G0 blocks 4w .. 4w+3 and G1 blocks 4w .. 4w+3 for every
     // 16-row block; a row block spanning several experts is multiplied once
-    // per expert and each row keeps its own expert's result.
+    // per expert and each row keeps its own expert's result.  G0 acts on the
+    // accumulators before the tile is staged: a lane's 4 consecutive columns
+    // of one row are the B operand of a 16 x 16 x 16 product over its block,
+    // so only G1 makes a pass over the staged tile (the epilogue is bound by
+    // those LDS passes); operands and roundings are those of a staged G0.
     using LC = LowMCfg<8>;
+    static_assert(OB == 4, "a wave's four G0 blocks");
+    for (int i = tid; i <= a.n_experts; i += GF_THREADS) s_off[i] = a.offsets[i];
+    __syncthreads();
     if (tid < GF_TM) {
       // the expert of row m: s_off[e] <= m < s_off[e + 1] (s_off[n_experts] = M)
       const int m = min(m0 + tid, a.M - 1);
@@ -246,18 +258,23 @@ __global__ __launch_bounds__(GF_THREADS, 2) void gemm_fp4_kernel(GemmFp4Args a) 
         f1[q] = *reinterpret_cast<const uint2*>(fc + LC::g0_bytes + (size_t(4 * wave + q) * 64 + lane) * 8);
       cur = e;
     };
-    for (int jb = 0; jb < MB; ++jb) {
-      const int r = 16 * jb + l16, er = s_exp[r];
-      const int e1 = __builtin_amdgcn_readfirstlane(s_exp[16 * jb + 15]);
-      for (int e = __builtin_amdgcn_readfirstlane(s_exp[16 * jb]); e <= e1; ++e) {
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      uint2 y[OB];
+#pragma unroll
+      for (int i = 0; i < OB; ++i) y[i] = ob[i][j];
+      const int er = s_exp[16 * j + l16];
+      const int e1 = __builtin_amdgcn_readfirstlane(s_exp[16 * j + 15]);
+      for (int e = __builtin_amdgcn_readfirstlane(s_exp[16 * j]); e <= e1; ++e) {
         frags(e);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          uint16_t* p = unit(r, 4 * (4 * wave + bb) + g);
-          const f32x4_t d = lm_mfma16(f0[bb], lm_ld64(p));
-          if (er == e) lm_st64(p, lm_pack4(d));
+        for (int i = 0; i < OB; ++i) {
+          const f32x4_t d = lm_mfma16(f0[i], ob[i][j]);
+          if (er == e) y[i] = lm_pack4(d);
         }
       }
+#pragma unroll
+      for (int i = 0; i < OB; ++i) stage(i, j, y[i]);
     }
     __syncthreads();
     for (int jb = 0; jb < MB; ++jb) {
