@@ -28,10 +28,11 @@
 // while both sit in one XCD's L2 (contiguous logical tiles per XCD).
 //
 // The output tile leaves through LDS as whole 512-byte row runs.  With EPI
-// (N = 4096 or 8192, rows bucketed by expert) it is first multiplied there by
-// stages 0..7 of each row's expert rotation: 256 columns are one chunk of
-// them (ButterflyMoE zh, technical summary §2.2: the stages below bit 8 act
-// within runs of 256 consecutive indices).
+// (N = 4096 or 8192, rows bucketed by expert) it is first multiplied by
+// stages 0..7 of each row's expert rotation: G0 on the accumulators, G1 on
+// the staged tile; 256 columns are one chunk of them (ButterflyMoE zh,
+// technical summary §2.2: the stages below bit 8 act within runs of 256
+// consecutive indices).
 #include "common.hpp"
 #include "lowpart.hpp"
 
