@@ -121,10 +121,15 @@ def kernel_work(cfg):
     if f == 0 and cfg.act == "bf16" and Ld <= 9:
         # one kernel per expert tile: gathered x rows, per-slot rows (or y at
         # k = 1), both rotations' angles, the substrate, slots and gates
+        # (at k = 2 on the matrix-core kernel, widths 256 / 512, the k rows are
+        # added into y there: the same bytes, no combine, and the bucketing
+        # kernel zeroes y first)
         fb = 2 * R * d * s + 2 * ang(d) + d * d // 4 + 8 * R
         ff = 2 * R * d * d + 2 * 3 * R * d * Ld
         w["fused"] = (fb, ff, bound(fb, ff))
-        if k > 1:
+        if k == 2 and Ld in (8, 9):
+            w["bucket"] = (w["bucket"][0] + T * d * s, 0, "hbm")
+        elif k > 1:
             w["combine"] = (R * d * s + T * d * s, R * d, "hbm")
         return w
     if split_io(Ld):

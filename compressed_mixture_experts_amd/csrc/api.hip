@@ -147,6 +147,12 @@ bool use_fused(const bmoe_layer* L) {
 }
 // ... with the rotations as block factors on the matrix cores (widths 256, 512)
 bool use_fused_mfma(const bmoe_layer* L) { return use_fused(L) && fused_mfma_supported(ilog2(L->d_model)); }
+// Top-2 square layers on the matrix-core expert kernel add their gated rows
+// straight into y (zeroed by the bucketing kernel) with packed bf16 atomic
+// adds: 0 + a + b rounds the same in either order, so the result is
+// deterministic and equals the separate combine's, and no per-slot rows
+// round-trip HBM.  Other top-k keep the per-slot rows and the combine.
+bool fused_adds_into_y(const bmoe_layer* L) { return use_fused_mfma(L) && L->top_k == 2; }
 
 // Substrate m's product as a GEMM Z = U W_m^T: output columns and contraction length.
 void sub_shape(const bmoe_layer* L, int m, int32_t& n_out, int32_t& k_in) {
@@ -512,7 +518,7 @@ static int forward_kernel_names(const bmoe_layer* L, const char* (&names)[kMaxFo
   names[n++] = "bucket";
   if (use_fused(L)) {
     names[n++] = "fused";
-    if (L->top_k > 1) names[n++] = "combine";
+    if (L->top_k > 1 && !fused_adds_into_y(L)) names[n++] = "combine";
     return n;
   }
   // widths 4096 / 8192 run the input and output rotations as two passes each
@@ -634,17 +640,23 @@ static bmoe_status forward_impl(const bmoe_layer* layer, const void* x, int32_t 
   BucketArgs ba{ra.tile_slots, ra.tile_gates, ra.tile_start, offsets, perm, rec, R, N,
                 router_tile(T, layer) * k, p.tiles, rec_rows,
                 rec ? int32_t((R + rec_rows - 1) / rec_rows + N) : 0};
+  const bool yatom = fused && fused_adds_into_y(layer);
+  if (yatom) {
+    ba.zero = reinterpret_cast<uint4*>(y);
+    ba.zero16 = size_t(T) * d * 2 / 16;
+  }
   BMOE_LAUNCH(launch_bucket(ba, stream));
   if (fused) {
     void* yslot_f = k == 1 ? y : at<char>(workspace, p.bufU);
     FusedArgs fa{x, yslot_f, layer->theta[0], layer->phi[0], wbytes, fac, offsets, perm, gate,
                  layer->w_scale[0], R, N, k, rec, rec_rows};
+    if (yatom) fa.yatom = y;
     if (p.mfma) {
       BMOE_LAUNCH(launch_fused_mfma(fa, ilog2(d), stream));
     } else {
       BMOE_LAUNCH(launch_fused_square(fa, ilog2(d), stream));
     }
-    if (k > 1) {
+    if (k > 1 && !yatom) {
       CombineArgs c{yslot_f, y, T, d, k};
       BMOE_LAUNCH(launch_combine(c, act, stream));
     }

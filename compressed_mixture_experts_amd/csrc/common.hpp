@@ -134,6 +134,8 @@ struct BucketArgs {
   int32_t R, N, C, G;       // slots, experts, slots per token tile, token tiles
   int32_t rec_rows;         // rows per tile record (32, 48 or 64)
   int32_t n_rec;            // ceil(R / rec_rows) + N when rec is set
+  uint4* zero;              // cleared by the bucketing workgroups when set
+  size_t zero16;            // its 16-byte words
 };
 
 // Weight preparation for the expert kernels (once per weight set,
@@ -158,7 +160,7 @@ struct PrepArgs {
 
 struct FusedArgs {
   const void* x;            // [T][d] bf16
-  void* out;                // per-slot rows [R][d] (or y when k == 1)
+  void* out;                // per-slot rows [R][d] (or y when k == 1; unused with yatom)
   const float* theta;       // [N][L][d/2]
   const float* phi;         // [N][L][d/2]
   const unsigned char* wb;  // substrate: [d][d] bytes (bf16 high byte of +-0.5 / 0) for the
@@ -171,6 +173,7 @@ struct FusedArgs {
   int32_t rows, n_experts, top_k;
   const TileRec* rec;       // tile records (matrix-core kernel)
   int32_t tile_rows;        // their rows per tile (fused_tile_rows)
+  void* yatom;              // bf16 [T][d], zeroed: rows added into it (k = 2) instead of per-slot rows
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):

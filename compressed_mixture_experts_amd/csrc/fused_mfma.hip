@@ -30,7 +30,10 @@
 //            (substrate as paired 2-bit codes, expanded to exact bf16 in registers)
 //   G_A      on the accumulators of the wave's own blocks        -> buf1 [row][p][m]
 //   G_B      wave (tb, h): classes p of half h, * gate * alpha   -> buf0 [row][i]
-//   store    buf0 rows -> per-slot rows
+//   store    buf0 rows -> per-slot rows; at top-2 they are added into y
+//            instead (packed bf16 atomic adds into y, which the bucketing
+//            kernel zeroed: 0 + a + b rounds the same in either order, so the
+//            result is deterministic and equals a separate combine's)
 // LDS is 2 x RT rows: two 32-row workgroups, or one taller one, per CU.  A
 // CU's loads are bounded by its misses in flight and a tile reads ~224 KiB of
 // substrate and factors at width 512, so while there are too few tiles to give
@@ -336,6 +339,19 @@ __global__ __launch_bounds__(RT == 32 ? 256 : 512, RT == 32 ? 2 : 1) void fused_
 
   // ---- per-slot rows
   constexpr int CPR = n / 8;
+  if (a.yatom) {
+    // each row's gated values added into its token's row of y, two bf16 per
+    // lane, consecutive lanes on consecutive words
+    typedef __bf16 bf2v_t __attribute__((ext_vector_type(2)));
+    for (int w = tid; w < RT * (n / 2); w += NT) {
+      const int r = w / (n / 2), c = w % (n / 2);
+      if (r < nr)
+        __builtin_amdgcn_global_atomic_fadd_v2bf16(
+            (__attribute__((address_space(1))) bf2v_t*)(reinterpret_cast<uint16_t*>(a.yatom) + s_src[r] + 2 * c),
+            __builtin_bit_cast(bf2v_t, *reinterpret_cast<const uint32_t*>(buf0 + r * TS + 4 * c)));
+    }
+    return;
+  }
 #pragma unroll
   for (int c = tid; c < RT * CPR; c += NT) {
     const int r = c / CPR;

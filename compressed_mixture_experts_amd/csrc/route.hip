@@ -961,6 +961,9 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(BucketArgs a) {
   __shared__ int s_w[2][BK_THREADS / 64];
   __shared__ int s_pre[BK_THREADS + 1];  // run starts of the round's tiles in its output
   __shared__ int s_src[BK_THREADS];      // run starts in the tile lists
+  if (a.zero)
+    for (size_t i = size_t(blockIdx.x) * BK_THREADS + threadIdx.x; i < a.zero16; i += size_t(gridDim.x) * BK_THREADS)
+      a.zero[i] = make_uint4(0u, 0u, 0u, 0u);
   const int e = blockIdx.x / BK_SPLIT, part = blockIdx.x % BK_SPLIT, N = a.N, G = a.G, C = a.C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 

@@ -37,7 +37,7 @@ def test_edge_fused_kernel_bytes_and_flops():
     T, d, N, k = 4096, 512, 64, 2
     R = T * k
     gathered_x = R * d * 2            # 8,388,608
-    per_slot_rows = R * d * 2         # 8,388,608
+    per_slot_rows = R * d * 2         # 8,388,608 (the k rows added into y)
     angles = 2 * N * 9 * (d // 2) * 4  # both rotations, 9 stages of 256 pairs: 1,179,648
     substrate = d * d // 4            # 2 bits per weight: 65,536
     slots_gates = 8 * R               # 65,536
@@ -45,10 +45,11 @@ def test_edge_fused_kernel_bytes_and_flops():
     # substrate product 2 R d^2 plus 3 flops per element per Givens stage, both rotations
     assert w["fused"][1] == 2 * R * d * d + 2 * 3 * R * d * 9
     assert w["fused"][2] == "hbm"     # 250 flop/byte, below the 312.5 ridge
-    assert w["combine"][0] == R * d * 2 + T * d * 2
+    # top-2: no combine; the bucketing kernel also zeroes y
+    assert w["bucket"][0] == 8 * R + 4 * (N + 1) + T * d * 2
     assert w["route"][0] == T * d * 2 + N * d * 2 + 8 * R
     assert w["route"][1] == 2 * T * d * N
-    assert set(w) == {"route", "bucket", "fused", "combine"}
+    assert set(w) == {"route", "bucket", "fused"}
 
 
 def test_large_ffn_kernel_bytes_and_flops():
