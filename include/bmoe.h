@@ -202,8 +202,13 @@ bmoe_status bmoe_route(const bmoe_layer* layer, const void* x, int32_t T,
  * accumulation run in fp32.  Rotations run in fp32, except where they are
  * products with the bf16 block factors described at bmoe_prepared_bytes
  * (square bf16 layers of width 256 and 512; bf16 rotations of width
- * 1024..8192): fp32 accumulation, bf16 rounding between factors.  Without
- * layer->prepared the call builds the prepared data in the workspace first. */
+ * 1024..8192): fp32 accumulation, bf16 rounding between factors.  Square
+ * bf16 layers of width 256 / 512 with top_k = 2 combine inside the expert
+ * kernel: y is first zeroed, then each routed row is added into it with
+ * packed bf16 atomic adds; two adds onto zero round the same in either order,
+ * so y is deterministic and equal to a separate fp32 combine rounded once.
+ * Without layer->prepared the call builds the prepared data in the
+ * workspace first. */
 bmoe_status bmoe_forward(const bmoe_layer* layer, const void* x, int32_t T, void* y,
                          int32_t* topk_idx, float* topk_gate,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
